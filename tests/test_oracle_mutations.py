@@ -1,0 +1,61 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case below plants one mistake in a copy of the oracle's C source (on the
+CPU, in a temporary directory), builds it, and runs the pin suite against the
+copy in a child process. The suite must fail for every planted mistake. This
+checks the pins, not the oracle: the real oracle is never modified.
+"""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+
+MUTANTS = {
+    "weights_lx_ly_swapped": ("double wy = i ? c->ly : 1.0 - c->ly;",
+                              "double wy = i ? c->lx : 1.0 - c->lx;"),
+    "loc_x_grad_missing_W": ("grad_loc[2 * p] = (double)W * a * dot_x;",
+                             "grad_loc[2 * p] = a * dot_x;"),
+    "loc_y_grad_uses_W": ("grad_loc[2 * p + 1] = (double)H * a * dot_y;",
+                          "grad_loc[2 * p + 1] = (double)W * a * dot_y;"),
+    "x_slope_sign_flipped": ("double sx = (1.0 - c.ly) * (a01 - a00) + c.ly * (a11 - a10);",
+                             "double sx = (1.0 - c.ly) * (a00 - a01) + c.ly * (a11 - a10);"),
+    "corner_transposed": ("int64_t row = start + (c->y0 + i) * W + (c->x0 + j);",
+                          "int64_t row = start + (c->y0 + j) * W + (c->x0 + i);"),
+    "flat_index_bounds_check": ("return yy >= 0 && yy < H && xx >= 0 && xx < W;",
+                                "return yy * W + xx >= 0 && yy * W + xx < H * W;"),
+    "no_half_pixel_shift": ("float xf = fmaf((float)loc_x, (float)W, -0.5f);",
+                            "float xf = fmaf((float)loc_x, (float)W, 0.0f);"),
+    "level_start_ignored": ("starts[l] = level_start ? level_start[l] : acc;",
+                            "starts[l] = acc;"),
+    "grad_value_missing_A": ("double coef = a * corner_weight(&c, i, j);",
+                             "double coef = corner_weight(&c, i, j);"),
+    "two_roundings_in_mapping": ("float xf = fmaf((float)loc_x, (float)W, -0.5f);",
+                                 "volatile float xw = (float)loc_x * (float)W; float xf = xw - 0.5f;"),
+    "grad_attn_scaled_by_A": ("grad_attn[p] = dot_s;", "grad_attn[p] = a * dot_s;"),
+    "batch_offset_dropped": ("return value + ((b * S + row) * M + m) * D;",
+                             "return value + ((0 * b * S + row) * M + m) * D;"),
+    "forward_missing_A": ("o[d] += a * sample[d];", "o[d] += sample[d];"),
+    "y_weight_from_wrong_corner": ("double sy = (1.0 - c.lx) * (a10 - a00) + c.lx * (a11 - a01);",
+                                   "double sy = (1.0 - c.lx) * (a10 - a00) + c.lx * (a11 - a10);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    src = open(os.path.join(ROOT, "oracle", "msda_oracle.c")).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle.build(src=str(mutant_src), out=str(tmp_path / "libmutant.so"))
+    env = dict(os.environ, MSDA_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        PINS], cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
