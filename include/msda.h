@@ -1,0 +1,172 @@
+/*
+ * msda.h - C ABI of the multi-scale deformable attention (MSDA) sampling and
+ * aggregation core for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the bracketed core of the MSDA operator (msda-triton
+ * README, section "The operator"): for every batch b, query q and head m,
+ *
+ *   out[b,q,m,:] = sum_l sum_k A[b,q,m,l,k] * bilinear_l(value[b,:,m,:], loc[b,q,m,l,k])
+ *
+ * where bilinear_l samples level l of the multi-level value map at the pixel
+ * x = loc_x * W_l - 0.5, y = loc_y * H_l - 0.5 with zero padding outside the
+ * level (README, section "Kernel design"; course page "4. The forward kernel,
+ * line by line", sections "Bilinear sampling" and "Accumulate and store").
+ * The x mapping is computed as one fused multiply-add rounded once to fp32,
+ * then floor; every in/out-of-bounds decision is taken per dimension on the
+ * integer cell coordinates, so a column past an edge never aliases a
+ * neighbouring row or level.
+ *
+ * The backward gives the three gradients of course page "5. The backward
+ * kernel: gradients, atomics, and a precision switch", section "What the
+ * backward pass must produce": grad_attention_weights (g . sample),
+ * grad_sampling_locations (corner slopes x A x W_l, and x H_l for y) and
+ * grad_value (A * w_ij * g scattered onto every in-bounds corner with relaxed
+ * atomics; out-of-bounds corners receive nothing, section "Scatter needs
+ * atomics").
+ *
+ * Tensor layouts (all dense, row-major, on the device, one dtype for every
+ * floating tensor of a call):
+ *   value                    (B, S, M, D)       S = rows of all levels
+ *   sampling_locations       (B, Q, M, L, K, 2) normalised (x, y), not clamped
+ *   attention_weights        (B, Q, M, L, K)    used as given (no softmax)
+ *   output / grad_output     (B, Q, M, D)       == (B, Q, M*D)
+ *   grad_value               (B, S, M, D)
+ *   grad_sampling_locations  (B, Q, M, L, K, 2)
+ *   grad_attention_weights   (B, Q, M, L, K)
+ * Level tables are HOST arrays:
+ *   spatial_shapes     L x 2 int64, rows (H_l, W_l), each >= 1
+ *   level_start_index  L int64, or NULL for the exclusive prefix sum of
+ *                      H_l * W_l (README, section "Quickstart"); a given index
+ *                      is used as given and only checked for memory safety:
+ *                      0 <= start_l and start_l + H_l * W_l <= S.
+ *
+ * Ownership and threading: the caller owns every buffer. The library keeps no
+ * global state apart from a thread-local error string, allocates no device
+ * memory, never synchronises, and enqueues all work on the caller's stream
+ * (a hipStream_t passed as void*; NULL is the default stream). Calls are
+ * reentrant. Device pointers must be aligned to their element size; wider
+ * vector accesses are used automatically when every pointer allows them.
+ *
+ * Errors: every entry point returns an msda_status_t. All argument checks run
+ * before any HIP call, so a rejected call has no side effect and needs no GPU.
+ * A failed kernel launch returns MSDA_ERR_HIP; faults during execution
+ * surface at the caller's next synchronisation. msda_last_error() gives a
+ * thread-local message for the last non-OK status.
+ */
+#ifndef MSDA_H
+#define MSDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSDA_ABI_VERSION 1
+#define MSDA_MAX_LEVELS 16
+
+typedef enum msda_dtype {
+    MSDA_F32 = 0,
+    MSDA_F16 = 1,
+    MSDA_BF16 = 2
+} msda_dtype_t;
+
+/* Where the backward accumulates grad_value (course page "5. The backward
+ * kernel", section "The fix: accumulate in FP32, downcast at the end").
+ *   NATIVE        atomics of the value dtype straight into grad_value
+ *                 (fp32 atomics, or packed two-wide fp16 / bf16 atomics);
+ *   FP32_SCRATCH  fp32 atomics into the caller's workspace, then one
+ *                 downcast pass into grad_value (identical to NATIVE for fp32);
+ *   AUTO          the library's measured choice for this dtype and shape. */
+typedef enum msda_accum {
+    MSDA_ACCUM_AUTO = -1,
+    MSDA_ACCUM_NATIVE = 0,
+    MSDA_ACCUM_FP32_SCRATCH = 1
+} msda_accum_t;
+
+typedef enum msda_status {
+    MSDA_OK = 0,
+    MSDA_ERR_NULL_ARG = 1,    /* a required pointer is NULL              */
+    MSDA_ERR_SHAPE = 2,       /* a size is negative, zero or too large   */
+    MSDA_ERR_LEVELS = 3,      /* bad spatial_shapes / level_start_index  */
+    MSDA_ERR_DTYPE = 4,       /* unknown dtype or accumulation mode      */
+    MSDA_ERR_ALIGN = 5,       /* pointer not aligned to its element size */
+    MSDA_ERR_WORKSPACE = 6,   /* workspace missing or too small          */
+    MSDA_ERR_HIP = 7,         /* a HIP launch failed                     */
+    MSDA_ERR_UNSUPPORTED = 8  /* valid but outside this build's limits   */
+} msda_status_t;
+
+/* Add into grad_value instead of overwriting it (training-style gradient
+ * accumulation); without it the library zero-fills grad_value first. */
+#define MSDA_FLAG_ACCUMULATE_GRAD_VALUE 1u
+
+/*
+ * Forward. Writes every element of `output` (B, Q, M, D).
+ * B == 0 or Q == 0: returns MSDA_OK without touching the device.
+ * Limits (MSDA_ERR_UNSUPPORTED): L <= MSDA_MAX_LEVELS, H_l and W_l < 2^24,
+ * D <= 64 * v where v is the widest channel vector that divides D.
+ */
+int msda_forward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
+                 int64_t head_dim, int64_t num_levels,
+                 const int64_t *spatial_shapes, const int64_t *level_start_index,
+                 int64_t num_queries, int64_t num_points,
+                 const void *value, const void *sampling_locations,
+                 const void *attention_weights, void *output, void *stream);
+
+/*
+ * Bytes of device workspace msda_backward needs for `accum` on this problem
+ * (0 for NATIVE, and for fp32 data). Returns 0 and sets the last error for
+ * invalid arguments; host-only, needs no GPU.
+ */
+size_t msda_backward_workspace_size(int dtype, int64_t batch, int64_t num_keys,
+                                    int64_t num_heads, int64_t head_dim,
+                                    int64_t num_levels, const int64_t *spatial_shapes,
+                                    const int64_t *level_start_index,
+                                    int64_t num_queries, int64_t num_points,
+                                    int accum);
+
+/*
+ * The accumulation mode msda_backward will use for `accum` on this problem
+ * (AUTO resolved to NATIVE or FP32_SCRATCH), or -1 on invalid arguments.
+ */
+int msda_backward_resolve_accum(int dtype, int64_t batch, int64_t num_keys,
+                                int64_t num_heads, int64_t head_dim,
+                                int64_t num_levels, const int64_t *spatial_shapes,
+                                const int64_t *level_start_index,
+                                int64_t num_queries, int64_t num_points, int accum);
+
+/*
+ * Backward, given grad_output (B, Q, M, D). Writes every element of
+ * grad_sampling_locations and grad_attention_weights; grad_value is
+ * zero-filled and then accumulated into (or only accumulated into, with
+ * MSDA_FLAG_ACCUMULATE_GRAD_VALUE). `workspace` must hold at least
+ * msda_backward_workspace_size(...) bytes, 16-byte aligned (NULL if 0).
+ * grad_value is bitwise nondeterministic run to run (atomic order); the two
+ * other gradients are deterministic.
+ * B == 0: returns MSDA_OK. Q == 0: only the grad_value zero-fill runs.
+ */
+int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
+                  int64_t head_dim, int64_t num_levels,
+                  const int64_t *spatial_shapes, const int64_t *level_start_index,
+                  int64_t num_queries, int64_t num_points,
+                  const void *value, const void *sampling_locations,
+                  const void *attention_weights, const void *grad_output,
+                  void *grad_value, void *grad_sampling_locations,
+                  void *grad_attention_weights, int accum, unsigned flags,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *msda_status_string(int status);
+
+/* Thread-local detail for the last non-OK status of this thread ("" if none). */
+const char *msda_last_error(void);
+
+/* MSDA_ABI_VERSION of the built library. */
+int msda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSDA_H */

@@ -1,0 +1,305 @@
+"""Python binding of the C ABI in include/msda.h: argument marshalling only.
+
+Every step of the computation runs in the HIP library (libmsda_amd.so). This
+module checks tensor shapes, dtypes and devices, makes inputs contiguous
+(course page "4. The forward kernel", section "The wrapper": the wrapper owns
+the layout contract), allocates outputs and the optional fp32 workspace with
+the PyTorch caching allocator, and passes raw pointers plus the current HIP
+stream. There is no CPU fallback: if the library is missing, every call
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmsda_amd.so")
+
+MSDA_F32, MSDA_F16, MSDA_BF16 = 0, 1, 2
+ACCUM_AUTO, ACCUM_NATIVE, ACCUM_FP32_SCRATCH = -1, 0, 1
+FLAG_ACCUMULATE_GRAD_VALUE = 1
+MAX_LEVELS = 16
+
+_DTYPE_CODES = {torch.float32: MSDA_F32, torch.float16: MSDA_F16, torch.bfloat16: MSDA_BF16}
+_ACCUM_CODES = {"auto": ACCUM_AUTO, None: ACCUM_AUTO, "native": ACCUM_NATIVE, False: ACCUM_NATIVE,
+                "fp32_scratch": ACCUM_FP32_SCRATCH, True: ACCUM_FP32_SCRATCH}
+
+# every symbol include/msda.h declares
+EXPORTED_SYMBOLS = ("msda_forward", "msda_backward", "msda_backward_workspace_size",
+                    "msda_backward_resolve_accum", "msda_status_string", "msda_last_error",
+                    "msda_abi_version")
+
+_lib = None
+
+
+class MSDAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library {path} is not built; run `python -m scale_deformable_attention_amd.build`"
+            " or __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    i64, vp, i32, u32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+    prob = [i32, i64, i64, i64, i64, i64, vp, vp, i64, i64]
+    lib.msda_forward.argtypes = prob + [vp, vp, vp, vp, vp]
+    lib.msda_forward.restype = i32
+    lib.msda_backward.argtypes = prob + [vp, vp, vp, vp, vp, vp, vp, i32, u32, vp, sz, vp]
+    lib.msda_backward.restype = i32
+    lib.msda_backward_workspace_size.argtypes = prob + [i32]
+    lib.msda_backward_workspace_size.restype = sz
+    lib.msda_backward_resolve_accum.argtypes = prob + [i32]
+    lib.msda_backward_resolve_accum.restype = i32
+    lib.msda_status_string.argtypes = [i32]
+    lib.msda_status_string.restype = ctypes.c_char_p
+    lib.msda_last_error.argtypes = []
+    lib.msda_last_error.restype = ctypes.c_char_p
+    lib.msda_abi_version.argtypes = []
+    lib.msda_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        msg = lib.msda_last_error().decode() or lib.msda_status_string(status).decode()
+        raise MSDAError(status, msg)
+
+
+class _Levels:
+    """Host copies of spatial_shapes / level_start_index (the ABI takes host arrays)."""
+
+    def __init__(self, spatial_shapes, level_start_index):
+        shp = torch.as_tensor(spatial_shapes).detach().to("cpu", torch.int64).contiguous()
+        if shp.dim() != 2 or shp.shape[1] != 2:
+            raise ValueError(f"spatial_shapes must be (L, 2), got {tuple(shp.shape)}")
+        self.shapes = shp
+        self.L = shp.shape[0]
+        if level_start_index is None:
+            self.starts = None
+        else:
+            st = torch.as_tensor(level_start_index).detach().to("cpu", torch.int64).contiguous()
+            if st.shape != (self.L,):
+                raise ValueError(f"level_start_index must be ({self.L},), got {tuple(st.shape)}")
+            self.starts = st
+
+    def ptrs(self):
+        return (ctypes.c_void_p(self.shapes.data_ptr()),
+                None if self.starts is None else ctypes.c_void_p(self.starts.data_ptr()))
+
+
+def _dims(value: torch.Tensor, levels: _Levels, loc: torch.Tensor, attn: torch.Tensor):
+    if value.dim() != 4:
+        raise ValueError(f"value must be (B, S, M, D), got {tuple(value.shape)}")
+    B, S, M, D = value.shape
+    if loc.dim() != 6 or loc.shape[0] != B or loc.shape[2] != M or loc.shape[3] != levels.L \
+            or loc.shape[5] != 2:
+        raise ValueError(f"sampling_locations must be (B, Q, M, L, K, 2) = ({B}, Q, {M}, "
+                         f"{levels.L}, K, 2), got {tuple(loc.shape)}")
+    Q, K = loc.shape[1], loc.shape[4]
+    if tuple(attn.shape) != (B, Q, M, levels.L, K):
+        raise ValueError(f"attention_weights must be {(B, Q, M, levels.L, K)}, got {tuple(attn.shape)}")
+    return B, S, M, D, Q, K
+
+
+def _dtype_code(*tensors: torch.Tensor) -> int:
+    dt = tensors[0].dtype
+    if dt not in _DTYPE_CODES:
+        raise TypeError(f"unsupported dtype {dt}; use float32, float16 or bfloat16")
+    dev = tensors[0].device
+    for t in tensors:
+        if t.dtype != dt:
+            raise TypeError(f"all floating tensors must share one dtype, got {dt} and {t.dtype}")
+        if t.device != dev:
+            raise ValueError(f"all tensors must be on one device, got {dev} and {t.device}")
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU (cuda/hip device), got {dev}")
+    return _DTYPE_CODES[dt]
+
+
+def _stream(device: torch.device, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return ctypes.c_void_p(handle)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _problem(code, B, S, M, D, levels, Q, K):
+    shp, st = levels.ptrs()
+    return (code, B, S, M, D, levels.L, shp, st, Q, K)
+
+
+def msda_forward(value: torch.Tensor, spatial_shapes, level_start_index,
+                 sampling_locations: torch.Tensor, attention_weights: torch.Tensor,
+                 output: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Forward of the MSDA core; returns (B, Q, M*D) in the input dtype."""
+    lib = load_library()
+    levels = _Levels(spatial_shapes, level_start_index)
+    code = _dtype_code(value, sampling_locations, attention_weights)
+    value = value.contiguous()
+    loc = sampling_locations.contiguous()
+    attn = attention_weights.contiguous()
+    B, S, M, D, Q, K = _dims(value, levels, loc, attn)
+    if output is None:
+        output = torch.empty((B, Q, M * D), dtype=value.dtype, device=value.device)
+    elif output.shape != (B, Q, M * D) or output.dtype != value.dtype or not output.is_contiguous():
+        raise ValueError("output must be a contiguous (B, Q, M*D) tensor of the input dtype")
+    _check(lib.msda_forward(*_problem(code, B, S, M, D, levels, Q, K), _ptr(value), _ptr(loc),
+                            _ptr(attn), _ptr(output), _stream(value.device, stream)))
+    return output
+
+
+def msda_backward_workspace_size(value: torch.Tensor, spatial_shapes, level_start_index,
+                                 sampling_locations: torch.Tensor,
+                                 attention_weights: torch.Tensor, accum="auto") -> int:
+    lib = load_library()
+    levels = _Levels(spatial_shapes, level_start_index)
+    code = _DTYPE_CODES[value.dtype]
+    B, S, M, D, Q, K = _dims(value, levels, sampling_locations, attention_weights)
+    return int(lib.msda_backward_workspace_size(*_problem(code, B, S, M, D, levels, Q, K),
+                                                _ACCUM_CODES[accum]))
+
+
+def msda_backward_resolve_accum(value: torch.Tensor, spatial_shapes, level_start_index,
+                                sampling_locations: torch.Tensor,
+                                attention_weights: torch.Tensor, accum="auto") -> str:
+    lib = load_library()
+    levels = _Levels(spatial_shapes, level_start_index)
+    code = _DTYPE_CODES[value.dtype]
+    B, S, M, D, Q, K = _dims(value, levels, sampling_locations, attention_weights)
+    r = int(lib.msda_backward_resolve_accum(*_problem(code, B, S, M, D, levels, Q, K),
+                                            _ACCUM_CODES[accum]))
+    if r < 0:
+        _check(int(MSDAErrorCodes.DTYPE))
+    return {ACCUM_NATIVE: "native", ACCUM_FP32_SCRATCH: "fp32_scratch"}[r]
+
+
+class MSDAErrorCodes:
+    NULL_ARG, SHAPE, LEVELS, DTYPE, ALIGN, WORKSPACE, HIP, UNSUPPORTED = range(1, 9)
+
+
+def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index,
+                  sampling_locations: torch.Tensor, attention_weights: torch.Tensor,
+                  grad_output: torch.Tensor, grad_value: Optional[torch.Tensor] = None,
+                  grad_sampling_locations: Optional[torch.Tensor] = None,
+                  grad_attention_weights: Optional[torch.Tensor] = None,
+                  accum: Union[str, bool, None] = "auto", accumulate: bool = False,
+                  workspace: Optional[torch.Tensor] = None, stream=None
+                  ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of the MSDA core: (grad_value, grad_sampling_locations,
+    grad_attention_weights). `accum` is "auto", "native" or "fp32_scratch"
+    (True/False/None are accepted as in the pages' fp32_grad_accum switch).
+    With `accumulate`, grad_value (given) is added into instead of overwritten."""
+    lib = load_library()
+    levels = _Levels(spatial_shapes, level_start_index)
+    code = _dtype_code(value, sampling_locations, attention_weights, grad_output)
+    value = value.contiguous()
+    loc = sampling_locations.contiguous()
+    attn = attention_weights.contiguous()
+    gout = grad_output.contiguous()
+    B, S, M, D, Q, K = _dims(value, levels, loc, attn)
+    if gout.numel() != B * Q * M * D:
+        raise ValueError(f"grad_output must hold B*Q*M*D = {B * Q * M * D} elements, got {gout.numel()}")
+    if accum not in _ACCUM_CODES:
+        raise ValueError(f"accum must be one of {list(_ACCUM_CODES)}, got {accum!r}")
+
+    def out_like(t, ref, name):
+        if t is None:
+            return torch.empty_like(ref)
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like {tuple(ref.shape)} {ref.dtype}")
+        return t
+
+    if accumulate and grad_value is None:
+        raise ValueError("accumulate=True needs the grad_value to add into")
+    grad_value = out_like(grad_value, value, "grad_value")
+    grad_loc = out_like(grad_sampling_locations, loc, "grad_sampling_locations")
+    grad_attn = out_like(grad_attention_weights, attn, "grad_attention_weights")
+    prob = _problem(code, B, S, M, D, levels, Q, K)
+    acode = _ACCUM_CODES[accum]
+    need = int(lib.msda_backward_workspace_size(*prob, acode))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=value.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.msda_backward(*prob, _ptr(value), _ptr(loc), _ptr(attn), _ptr(gout),
+                             _ptr(grad_value), _ptr(grad_loc), _ptr(grad_attn), acode,
+                             FLAG_ACCUMULATE_GRAD_VALUE if accumulate else 0, _ptr(workspace),
+                             ws_bytes, _stream(value.device, stream)))
+    return grad_value, grad_loc, grad_attn
+
+
+class PreparedCall:
+    """Pre-marshalled forward/backward calls on fixed tensors.
+
+    Holds the ctypes argument tuples for one problem so that repeated calls
+    (training loops, benchmarks, graph capture) cost one foreign call each.
+    The tensors must stay alive and keep their storage while this object is
+    used; outputs are written in place.
+    """
+
+    def __init__(self, value, spatial_shapes, level_start_index, sampling_locations,
+                 attention_weights, grad_output=None, accum="auto", stream=None):
+        self.lib = load_library()
+        levels = _Levels(spatial_shapes, level_start_index)
+        code = _dtype_code(value, sampling_locations, attention_weights)
+        for t in (value, sampling_locations, attention_weights):
+            if not t.is_contiguous():
+                raise ValueError("PreparedCall needs contiguous tensors")
+        B, S, M, D, Q, K = _dims(value, levels, sampling_locations, attention_weights)
+        self.levels = levels  # keeps the host arrays alive
+        self.value, self.loc, self.attn = value, sampling_locations, attention_weights
+        self.output = torch.empty((B, Q, M * D), dtype=value.dtype, device=value.device)
+        self.prob = _problem(code, B, S, M, D, levels, Q, K)
+        self.device = value.device
+        self._stream_arg = stream  # None: torch's current stream at each call (graph capture)
+        self._fwd_args = self.prob + (_ptr(value), _ptr(sampling_locations),
+                                      _ptr(attention_weights), _ptr(self.output))
+        self.accum_code = _ACCUM_CODES[accum]
+        self.grad_output = grad_output
+        if grad_output is not None:
+            if grad_output.numel() != B * Q * M * D or not grad_output.is_contiguous() \
+                    or grad_output.dtype != value.dtype:
+                raise ValueError("grad_output must be a contiguous (B, Q, M*D) tensor of the input dtype")
+            self.grad_value = torch.empty_like(value)
+            self.grad_loc = torch.empty_like(sampling_locations)
+            self.grad_attn = torch.empty_like(attention_weights)
+            need = int(self.lib.msda_backward_workspace_size(*self.prob, self.accum_code))
+            self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=value.device) \
+                if need else None
+            self._bwd_head = self.prob + (_ptr(value), _ptr(sampling_locations),
+                                          _ptr(attention_weights), _ptr(grad_output),
+                                          _ptr(self.grad_value), _ptr(self.grad_loc),
+                                          _ptr(self.grad_attn))
+            self._ws = (_ptr(self.workspace), need)
+        self.resolved_accum = {ACCUM_NATIVE: "native", ACCUM_FP32_SCRATCH: "fp32_scratch"}.get(
+            int(self.lib.msda_backward_resolve_accum(*self.prob, self.accum_code)))
+
+    def forward(self) -> torch.Tensor:
+        _check(self.lib.msda_forward(*self._fwd_args, _stream(self.device, self._stream_arg)))
+        return self.output
+
+    def backward(self, accumulate: bool = False, accum=None):
+        code = self.accum_code if accum is None else _ACCUM_CODES[accum]
+        ws = self._ws if accum is None else (self._ws if code == self.accum_code else (None, 0))
+        _check(self.lib.msda_backward(*self._bwd_head, code,
+                                      FLAG_ACCUMULATE_GRAD_VALUE if accumulate else 0, ws[0], ws[1],
+                                      _stream(self.device, self._stream_arg)))
+        return self.grad_value, self.grad_loc, self.grad_attn

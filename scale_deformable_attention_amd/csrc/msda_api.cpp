@@ -1,0 +1,350 @@
+// Host side of the C ABI declared in include/msda.h: argument validation, the
+// level table, the lane mapping, the accumulation policy and the launches.
+//
+// Every check runs before the first HIP call, so a rejected call has no side
+// effect and works on a host without a GPU. The default level_start_index is
+// the exclusive prefix sum of H_l * W_l (msda-triton README, section
+// "Quickstart"; course page "4. The forward kernel", section "The wrapper").
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "msda_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return MSDA_OK;
+}
+
+size_t elem_size(int dtype) { return dtype == MSDA_F32 ? 4 : 2; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+    __int128 r = (__int128)a * (__int128)b;
+    if (r > (__int128)INT64_MAX) return false;
+    *out = (int64_t)r;
+    return true;
+}
+
+// Validate sizes and build the level table.
+int make_problem(int dtype, int64_t B, int64_t S, int64_t M, int64_t D, int64_t L,
+                 const int64_t *shapes, const int64_t *starts, int64_t Q, int64_t K,
+                 msda::Problem *p) {
+    if (dtype != MSDA_F32 && dtype != MSDA_F16 && dtype != MSDA_BF16)
+        return fail(MSDA_ERR_DTYPE, "unknown dtype %d (0=f32, 1=f16, 2=bf16)", dtype);
+    if (B < 0 || Q < 0) return fail(MSDA_ERR_SHAPE, "batch (%lld) and num_queries (%lld) must be >= 0",
+                                    (long long)B, (long long)Q);
+    if (S < 1 || M < 1 || D < 1 || K < 1)
+        return fail(MSDA_ERR_SHAPE,
+                    "num_keys (%lld), num_heads (%lld), head_dim (%lld) and num_points (%lld) "
+                    "must be >= 1",
+                    (long long)S, (long long)M, (long long)D, (long long)K);
+    if (L < 1) return fail(MSDA_ERR_SHAPE, "num_levels must be >= 1, got %lld", (long long)L);
+    if (L > MSDA_MAX_LEVELS)
+        return fail(MSDA_ERR_UNSUPPORTED, "num_levels %lld exceeds the limit of %d", (long long)L,
+                    MSDA_MAX_LEVELS);
+    if (!shapes) return fail(MSDA_ERR_NULL_ARG, "spatial_shapes is NULL");
+    // Products used for indexing must fit comfortably in int64 / int32.
+    int64_t t, bsmd, bqmlk;
+    if (!mul_ok(B, S, &t) || !mul_ok(t, M, &t) || !mul_ok(t, D, &bsmd) ||
+        bsmd > ((int64_t)1 << 62))
+        return fail(MSDA_ERR_SHAPE, "value tensor B*S*M*D overflows");
+    if (!mul_ok(B, Q, &t) || !mul_ok(t, M, &t) || !mul_ok(t, L, &t) || !mul_ok(t, K, &bqmlk) ||
+        bqmlk > ((int64_t)1 << 61))
+        return fail(MSDA_ERR_SHAPE, "sampling tensor B*Q*M*L*K overflows");
+    if (M > INT32_MAX || D > INT32_MAX || L * K > (1 << 20) || Q > INT32_MAX)
+        return fail(MSDA_ERR_UNSUPPORTED,
+                    "num_heads, head_dim, num_queries or num_levels*num_points too large");
+    p->dtype = dtype;
+    p->B = B;
+    p->S = S;
+    p->M = M;
+    p->D = D;
+    p->L = L;
+    p->Q = Q;
+    p->K = K;
+    memset(&p->levels, 0, sizeof(p->levels));
+    int64_t acc = 0;
+    for (int64_t l = 0; l < L; ++l) {
+        const int64_t H = shapes[2 * l], W = shapes[2 * l + 1];
+        if (H < 1 || W < 1)
+            return fail(MSDA_ERR_LEVELS, "level %lld has shape (%lld, %lld); both must be >= 1",
+                        (long long)l, (long long)H, (long long)W);
+        if (H >= (1 << 24) || W >= (1 << 24))
+            return fail(MSDA_ERR_UNSUPPORTED, "level %lld shape (%lld, %lld) exceeds 2^24",
+                        (long long)l, (long long)H, (long long)W);
+        const int64_t st = starts ? starts[l] : acc;
+        acc += H * W;
+        if (st < 0 || st > S || H * W > S - st)
+            return fail(MSDA_ERR_LEVELS,
+                        "level %lld (start %lld, %lld x %lld) does not fit in num_keys = %lld",
+                        (long long)l, (long long)st, (long long)H, (long long)W, (long long)S);
+        p->levels.H[l] = (int32_t)H;
+        p->levels.W[l] = (int32_t)W;
+        p->levels.start[l] = st;
+    }
+    return MSDA_OK;
+}
+
+bool aligned(const void *ptr, size_t a) { return reinterpret_cast<uintptr_t>(ptr) % a == 0; }
+
+int log2_ceil(int64_t x) {
+    int r = 0;
+    while (((int64_t)1 << r) < x) ++r;
+    return r;
+}
+
+// Pick the channel vector width and the lane mapping. `vec_ptrs` are the
+// pointers accessed VEC channels at a time (value, output, grad_output,
+// grad_value); `need4` asks for 4-byte aligned channel pairs (packed atomics).
+int choose_mapping(const msda::Problem &p, const void *const *vec_ptrs, int nptrs,
+                   msda::Mapping *mp) {
+    const size_t e = elem_size(p.dtype);
+    static const int cand32[] = {4, 3, 2, 1};
+    static const int cand16[] = {8, 4, 2, 1};
+    const int *cand = e == 4 ? cand32 : cand16;
+    int best = 0;
+    double best_eff = -1.0;
+    for (int i = 0; i < 4; ++i) {
+        const int v = cand[i];
+        if (p.D % v) continue;
+        const size_t need = (v == 3) ? e : (size_t)v * e;
+        bool ok_align = true;
+        for (int j = 0; j < nptrs; ++j) ok_align = ok_align && aligned(vec_ptrs[j], need);
+        if (!ok_align) continue;
+        const int64_t lanes = p.D / v;
+        const int lg = log2_ceil(lanes);
+        if (lg > 6) continue;
+        const double eff = (double)lanes / (double)((int64_t)1 << lg);
+        if (eff > best_eff + 1e-9) {
+            best_eff = eff;
+            best = v;
+        }
+    }
+    if (!best)
+        return fail(MSDA_ERR_UNSUPPORTED,
+                    "head_dim %lld needs more than 64 lanes at every supported vector width",
+                    (long long)p.D);
+    mp->vec = best;
+    mp->log2_group = log2_ceil(p.D / best);
+    // Few queries: let up to 4 lane groups split one query's points so that
+    // enough waves are in flight (about 8 per CU on 256 CUs).
+    const int64_t target_lanes = (int64_t)256 * 8 * 64;
+    const int64_t lanes = p.B * p.M * p.Q * ((int64_t)1 << mp->log2_group);
+    int ls = 0;
+    // The lanes of one query (group x split) must stay inside one 64-lane wave.
+    while (ls < 2 && p.K % ((int64_t)2 << ls) == 0 && lanes * ((int64_t)1 << ls) < target_lanes &&
+           mp->log2_group + ls + 1 <= 6)
+        ++ls;
+    mp->log2_split = ls;
+    // Workgroups: 2^(8 - group - split) queries each, B*M*ceil(Q/that) of them.
+    const int64_t qpb = (int64_t)256 >> (mp->log2_group + mp->log2_split);
+    const int64_t qblocks = (p.Q + qpb - 1) / qpb;
+    if (qblocks > INT32_MAX || p.B * p.M * qblocks > (int64_t)INT32_MAX - 8)
+        return fail(MSDA_ERR_UNSUPPORTED, "too many workgroups for one launch");
+    return MSDA_OK;
+}
+
+int check_ptr(const void *ptr, const char *name, int dtype) {
+    if (!ptr) return fail(MSDA_ERR_NULL_ARG, "%s is NULL", name);
+    if (!aligned(ptr, elem_size(dtype)))
+        return fail(MSDA_ERR_ALIGN, "%s is not aligned to its element size", name);
+    return MSDA_OK;
+}
+
+int hip_fail(hipError_t err, const char *what) {
+    return fail(MSDA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+// Accumulation policy for AUTO. fp32 data: fp32 atomics into grad_value.
+// fp16: packed fp16 atomics. bf16: fp32 scratch (packed bf16 atomics round
+// every add to 8 bits and drift on heavily shared pixels).
+int resolve_accum(const msda::Problem &p, int accum) {
+    if (p.dtype == MSDA_F32) return MSDA_ACCUM_NATIVE;
+    if (accum == MSDA_ACCUM_AUTO) {
+        if ((p.B * p.S * p.M * p.D) % 2 != 0) return MSDA_ACCUM_FP32_SCRATCH;
+        return p.dtype == MSDA_F16 ? MSDA_ACCUM_NATIVE : MSDA_ACCUM_FP32_SCRATCH;
+    }
+    return accum;
+}
+
+size_t scratch_bytes(const msda::Problem &p, int resolved) {
+    if (p.dtype == MSDA_F32 || resolved != MSDA_ACCUM_FP32_SCRATCH) return 0;
+    return (size_t)(p.B * p.S * p.M * p.D) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int msda_abi_version(void) { return MSDA_ABI_VERSION; }
+
+const char *msda_last_error(void) { return g_last_error.c_str(); }
+
+const char *msda_status_string(int status) {
+    switch (status) {
+        case MSDA_OK: return "ok";
+        case MSDA_ERR_NULL_ARG: return "null argument";
+        case MSDA_ERR_SHAPE: return "bad shape";
+        case MSDA_ERR_LEVELS: return "bad level table";
+        case MSDA_ERR_DTYPE: return "bad dtype or accumulation mode";
+        case MSDA_ERR_ALIGN: return "misaligned pointer";
+        case MSDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case MSDA_ERR_HIP: return "HIP error";
+        case MSDA_ERR_UNSUPPORTED: return "unsupported size";
+        default: return "unknown status";
+    }
+}
+
+int msda_forward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, int64_t head_dim,
+                 int64_t num_levels, const int64_t *spatial_shapes,
+                 const int64_t *level_start_index, int64_t num_queries, int64_t num_points,
+                 const void *value, const void *sampling_locations, const void *attention_weights,
+                 void *output, void *stream) {
+    msda::Problem p;
+    int st = make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
+                          level_start_index, num_queries, num_points, &p);
+    if (st) return st;
+    if (p.B == 0 || p.Q == 0) return ok();  // empty tensors may carry NULL pointers
+    if ((st = check_ptr(value, "value", dtype))) return st;
+    if ((st = check_ptr(sampling_locations, "sampling_locations", dtype))) return st;
+    if ((st = check_ptr(attention_weights, "attention_weights", dtype))) return st;
+    if ((st = check_ptr(output, "output", dtype))) return st;
+    const void *vec_ptrs[] = {value, output};
+    msda::Mapping mp;
+    if ((st = choose_mapping(p, vec_ptrs, 2, &mp))) return st;
+    hipError_t err = msda::launch_forward(p, mp, value, sampling_locations, attention_weights,
+                                          output, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "forward launch");
+    return ok();
+}
+
+int msda_backward_resolve_accum(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
+                                int64_t head_dim, int64_t num_levels,
+                                const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                int64_t num_queries, int64_t num_points, int accum) {
+    msda::Problem p;
+    if (make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
+                     level_start_index, num_queries, num_points, &p))
+        return -1;
+    if (accum != MSDA_ACCUM_AUTO && accum != MSDA_ACCUM_NATIVE && accum != MSDA_ACCUM_FP32_SCRATCH) {
+        fail(MSDA_ERR_DTYPE, "unknown accumulation mode %d", accum);
+        return -1;
+    }
+    return resolve_accum(p, accum);
+}
+
+size_t msda_backward_workspace_size(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
+                                    int64_t head_dim, int64_t num_levels,
+                                    const int64_t *spatial_shapes,
+                                    const int64_t *level_start_index, int64_t num_queries,
+                                    int64_t num_points, int accum) {
+    msda::Problem p;
+    if (make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
+                     level_start_index, num_queries, num_points, &p))
+        return 0;
+    if (accum != MSDA_ACCUM_AUTO && accum != MSDA_ACCUM_NATIVE && accum != MSDA_ACCUM_FP32_SCRATCH) {
+        fail(MSDA_ERR_DTYPE, "unknown accumulation mode %d", accum);
+        return 0;
+    }
+    return scratch_bytes(p, resolve_accum(p, accum));
+}
+
+int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, int64_t head_dim,
+                  int64_t num_levels, const int64_t *spatial_shapes,
+                  const int64_t *level_start_index, int64_t num_queries, int64_t num_points,
+                  const void *value, const void *sampling_locations, const void *attention_weights,
+                  const void *grad_output, void *grad_value, void *grad_sampling_locations,
+                  void *grad_attention_weights, int accum, unsigned flags, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    msda::Problem p;
+    int st = make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
+                          level_start_index, num_queries, num_points, &p);
+    if (st) return st;
+    if (accum != MSDA_ACCUM_AUTO && accum != MSDA_ACCUM_NATIVE && accum != MSDA_ACCUM_FP32_SCRATCH)
+        return fail(MSDA_ERR_DTYPE, "unknown accumulation mode %d", accum);
+    if (flags & ~MSDA_FLAG_ACCUMULATE_GRAD_VALUE)
+        return fail(MSDA_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~MSDA_FLAG_ACCUMULATE_GRAD_VALUE);
+    if (p.B == 0) return ok();
+    const bool accumulate = (flags & MSDA_FLAG_ACCUMULATE_GRAD_VALUE) != 0;
+    const int resolved = resolve_accum(p, accum);
+    const size_t need = scratch_bytes(p, resolved);
+    const bool use_scratch = need > 0;
+    if ((st = check_ptr(value, "value", dtype))) return st;
+    if ((st = check_ptr(grad_value, "grad_value", dtype))) return st;
+    if (use_scratch) {
+        if (!workspace) return fail(MSDA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+        if (workspace_bytes < need)
+            return fail(MSDA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+        if (!aligned(workspace, 16)) return fail(MSDA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
+    if (p.Q > 0) {
+        if ((st = check_ptr(sampling_locations, "sampling_locations", dtype))) return st;
+        if ((st = check_ptr(attention_weights, "attention_weights", dtype))) return st;
+        if ((st = check_ptr(grad_output, "grad_output", dtype))) return st;
+        if ((st = check_ptr(grad_sampling_locations, "grad_sampling_locations", dtype))) return st;
+        if ((st = check_ptr(grad_attention_weights, "grad_attention_weights", dtype))) return st;
+    }
+    // Native half-precision atomics update aligned 4-byte pairs; every pair
+    // must lie inside grad_value.
+    if (!use_scratch && dtype != MSDA_F32 &&
+        (!aligned(grad_value, 4) || (p.B * p.S * p.M * p.D) % 2 != 0))
+        return fail(MSDA_ERR_ALIGN,
+                    "native half-precision atomics need a 4-byte aligned grad_value with an even "
+                    "element count; use MSDA_ACCUM_FP32_SCRATCH");
+    msda::Mapping mp = {1, 0, 0};
+    if (p.Q > 0) {
+        // Packed half-precision atomics need 4-byte aligned channel pairs;
+        // an unaligned grad_value falls back to single-element packed adds
+        // through choose_mapping's alignment test on the vector width.
+        const void *vec_ptrs[] = {value, grad_output, grad_value, workspace ? workspace : value};
+        if ((st = choose_mapping(p, vec_ptrs, 4, &mp))) return st;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t gv_bytes = (size_t)(p.B * p.S * p.M * p.D) * elem_size(dtype);
+    hipError_t err;
+    if (use_scratch) {
+        if (p.Q == 0) {
+            if (!accumulate && (err = msda::launch_zero(grad_value, gv_bytes, s)) != hipSuccess)
+                return hip_fail(err, "grad_value zero fill");
+            return ok();
+        }
+        if ((err = msda::launch_zero(workspace, need, s)) != hipSuccess)
+            return hip_fail(err, "scratch zero fill");
+        if ((err = msda::launch_backward(p, mp, value, sampling_locations, attention_weights,
+                                         grad_output, workspace, true, grad_sampling_locations,
+                                         grad_attention_weights, s)) != hipSuccess)
+            return hip_fail(err, "backward launch");
+        if ((err = msda::launch_downcast(dtype, static_cast<const float *>(workspace), grad_value,
+                                         p.B * p.S * p.M * p.D, accumulate, s)) != hipSuccess)
+            return hip_fail(err, "downcast launch");
+        return ok();
+    }
+    if (!accumulate && (err = msda::launch_zero(grad_value, gv_bytes, s)) != hipSuccess)
+        return hip_fail(err, "grad_value zero fill");
+    if (p.Q == 0) return ok();
+    if ((err = msda::launch_backward(p, mp, value, sampling_locations, attention_weights,
+                                     grad_output, grad_value, dtype == MSDA_F32,
+                                     grad_sampling_locations, grad_attention_weights, s)) !=
+        hipSuccess)
+        return hip_fail(err, "backward launch");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+"""Parity rule between the HIP path and the CPU oracle.
+
+A slice passes when every element satisfies
+    |gpu - oracle| <= tol * (|oracle| + rms(oracle slice)),
+with slices = the whole tensor for output and grad_attention_weights, and one
+slice per level for grad_value (rows of that level) and
+grad_sampling_locations (entries of that level), because magnitudes scale
+with W_l, H_l and with how many points share a pixel.
+
+Tolerances (relative): fp32 1e-5 everywhere; fp16 / bf16 2e-2 on output,
+grad_sampling_locations and grad_attention_weights, 5e-2 on grad_value.
+
+Exact parts: a grad_value row no in-bounds corner lands on, and an output
+row none of whose points has an in-bounds corner, must be exactly zero.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+TOL = {
+    torch.float32: {"output": 1e-5, "grad_value": 1e-5, "grad_sampling_locations": 1e-5,
+                    "grad_attention_weights": 1e-5},
+    torch.float16: {"output": 2e-2, "grad_value": 5e-2, "grad_sampling_locations": 2e-2,
+                    "grad_attention_weights": 2e-2},
+    torch.bfloat16: {"output": 2e-2, "grad_value": 5e-2, "grad_sampling_locations": 2e-2,
+                     "grad_attention_weights": 2e-2},
+}
+
+
+def to_np(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        return t.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def check_slice(name: str, got: np.ndarray, ref: np.ndarray, tol: float) -> dict:
+    got = got.astype(np.float64).ravel()
+    ref = ref.astype(np.float64).ravel()
+    if ref.size == 0:
+        return {"name": name, "n": 0}
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    diff = np.abs(got - ref)
+    bound = tol * (np.abs(ref) + rms)
+    bad = ~(diff <= bound)  # NaN counts as bad
+    scaled = diff / np.maximum(np.abs(ref) + rms, 1e-300)
+    denom = float(np.linalg.norm(ref))
+    stats = {
+        "name": name, "n": int(ref.size), "max_abs": float(np.nanmax(diff)),
+        "max_scaled": float(np.nanmax(scaled)), "rms_ref": rms,
+        "normwise": float(np.linalg.norm(got - ref) / denom) if denom > 0 else 0.0,
+        "cos": float(np.dot(got, ref) / (np.linalg.norm(got) * denom))
+        if denom > 0 and np.linalg.norm(got) > 0 else 1.0,
+    }
+    if bad.any():
+        i = int(np.argmax(np.where(np.isnan(scaled), np.inf, scaled)))
+        raise AssertionError(
+            f"{name}: {int(bad.sum())}/{ref.size} elements outside tol {tol:g}; worst #{i}: "
+            f"gpu={got[i]!r} oracle={ref[i]!r} (max abs {stats['max_abs']:.3e}, "
+            f"max scaled {stats['max_scaled']:.3e}, normwise {stats['normwise']:.3e}, "
+            f"cos {stats['cos']:.6f})")
+    return stats
+
+
+def level_row_ranges(spatial_shapes, level_start_index=None):
+    shp = [tuple(map(int, r)) for r in torch.as_tensor(spatial_shapes).tolist()]
+    out, acc = [], 0
+    for i, (h, w) in enumerate(shp):
+        s = acc if level_start_index is None else int(level_start_index[i])
+        out.append((s, s + h * w))
+        acc += h * w
+    return out
+
+
+def check_forward(dtype, out_gpu, out_ref, touched=None) -> list:
+    got, ref = to_np(out_gpu), np.asarray(out_ref)
+    stats = [check_slice("output", got, ref, TOL[dtype]["output"])]
+    if touched is not None:
+        B, Q, M = touched.shape
+        g = got.reshape(B, Q, M, -1)
+        untouched = ~touched
+        assert np.all(g[untouched] == 0), "output of a query with no in-bounds corner is not exactly 0"
+    return stats
+
+
+def check_backward(dtype, gpu, ref, spatial_shapes, level_start_index=None,
+                   touched_rows=None) -> list:
+    gv, gl, ga = (to_np(t) for t in gpu)
+    rgv, rgl, rga = ref
+    tol = TOL[dtype]
+    stats = [check_slice("grad_attention_weights", ga, rga, tol["grad_attention_weights"])]
+    for l, (r0, r1) in enumerate(level_row_ranges(spatial_shapes, level_start_index)):
+        stats.append(check_slice(f"grad_value[level {l}]", gv[:, r0:r1], rgv[:, r0:r1],
+                                 tol["grad_value"]))
+        stats.append(check_slice(f"grad_sampling_locations[level {l}]", gl[:, :, :, l],
+                                 rgl[:, :, :, l], tol["grad_sampling_locations"]))
+    if touched_rows is not None:
+        assert np.all(gv[~touched_rows] == 0), \
+            "grad_value row with no in-bounds corner is not exactly 0"
+    return stats

@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/msda.h declares, and
+reject every bad argument with its status code before any HIP call. No call
+here reaches a kernel launch: each one either fails validation or has an
+empty batch / query set.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msda.h")
+
+from scale_deformable_attention_amd import _binding as bind  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bind.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return bind.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding_list():
+    assert _declared_functions() == sorted(bind.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+    assert lib.msda_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        assert lib.msda_status_string(code).decode()
+    assert lib.msda_status_string(99).decode() == "unknown status"
+
+
+# A valid small problem: two levels (8,10), (4,5) -> S = 100.
+SHAPES = (ctypes.c_int64 * 4)(8, 10, 4, 5)
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below stops before a launch
+
+
+def fwd(lib, dtype=0, B=1, S=100, M=2, D=8, L=2, shapes=SHAPES, starts=None, Q=16, K=2,
+        value=FAKE, loc=FAKE, attn=FAKE, out=FAKE):
+    return lib.msda_forward(dtype, B, S, M, D, L, shapes, starts, Q, K, value, loc, attn, out, None)
+
+
+def bwd(lib, dtype=0, B=1, S=100, M=2, D=8, L=2, shapes=SHAPES, starts=None, Q=16, K=2,
+        accum=-1, flags=0, ws=None, ws_bytes=0, gv=FAKE, gout=FAKE):
+    return lib.msda_backward(dtype, B, S, M, D, L, shapes, starts, Q, K, FAKE, FAKE, FAKE, gout,
+                             gv, FAKE, FAKE, accum, flags, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), 4),
+    (dict(B=-1), 2),
+    (dict(Q=-1), 2),
+    (dict(M=0), 2),
+    (dict(D=0), 2),
+    (dict(K=0), 2),
+    (dict(L=0), 2),
+    (dict(L=17), 8),
+    (dict(shapes=None), 1),
+    (dict(S=99), 3),  # levels need 100 rows
+    (dict(shapes=(ctypes.c_int64 * 4)(8, 10, 0, 5)), 3),
+    (dict(shapes=(ctypes.c_int64 * 4)(1 << 24, 1, 4, 5), S=(1 << 24) + 20), 8),
+    (dict(starts=(ctypes.c_int64 * 2)(0, 90)), 3),
+    (dict(starts=(ctypes.c_int64 * 2)(-1, 80)), 3),
+    (dict(value=None), 1),
+    (dict(loc=None), 1),
+    (dict(attn=None), 1),
+    (dict(out=None), 1),
+    (dict(value=ctypes.c_void_p(0x10002)), 5),
+    (dict(dtype=2, out=ctypes.c_void_p(0x10001)), 5),
+    (dict(D=(1 << 20)), 8),  # more than 64 lanes at every vector width
+])
+def test_forward_rejects(lib, kw, status):
+    assert fwd(lib, **kw) == status
+    assert lib.msda_last_error().decode() != ""
+
+
+def test_forward_empty_batch_or_queries_is_ok_without_launch(lib):
+    assert fwd(lib, B=0) == 0
+    assert fwd(lib, Q=0) == 0
+    assert lib.msda_last_error().decode() == ""
+
+
+def test_forward_given_start_index_may_differ_from_prefix(lib):
+    # valid but non-prefix start index with an empty query set: accepted
+    assert fwd(lib, Q=0, starts=(ctypes.c_int64 * 2)(20, 0)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(accum=2), 4),
+    (dict(flags=2), 2),
+    (dict(gv=None), 1),
+    (dict(gout=None), 1),
+    (dict(dtype=2, accum=1), 6),  # scratch needed, no workspace
+    (dict(dtype=2, accum=1, ws=ctypes.c_void_p(0x10000), ws_bytes=100), 6),
+    (dict(dtype=2, accum=1, ws=ctypes.c_void_p(0x10008), ws_bytes=1 << 20), 5),
+])
+def test_backward_rejects(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_backward_empty_batch_is_ok(lib):
+    assert bwd(lib, B=0) == 0
+
+
+def test_workspace_size_and_accum_resolution(lib):
+    prob = (1, 100, 2, 8, 2, SHAPES, None, 16, 2)
+    # fp32 never needs scratch; bf16 fp32-scratch needs B*S*M*D*4 bytes
+    assert lib.msda_backward_workspace_size(0, *prob, 1) == 0
+    assert lib.msda_backward_workspace_size(2, *prob, 1) == 1 * 100 * 2 * 8 * 4
+    assert lib.msda_backward_workspace_size(2, *prob, 0) == 0
+    assert lib.msda_backward_workspace_size(1, *prob, 1) == 1 * 100 * 2 * 8 * 4
+    assert lib.msda_backward_resolve_accum(0, *prob, -1) == 0
+    assert lib.msda_backward_resolve_accum(2, *prob, 0) == 0
+    assert lib.msda_backward_resolve_accum(2, *prob, 1) == 1
+    assert lib.msda_backward_resolve_accum(2, *prob, -1) in (0, 1)
+    assert lib.msda_backward_resolve_accum(2, *prob, 7) == -1
+    assert lib.msda_backward_workspace_size(9, *prob, 1) == 0 and lib.msda_last_error()
+
+
+def test_python_binding_rejects_bad_tensors_on_cpu():
+    import torch
+    from scale_deformable_attention_amd import msda_forward
+    v = torch.zeros(1, 100, 2, 8)
+    loc = torch.zeros(1, 16, 2, 2, 2, 2)
+    a = torch.zeros(1, 16, 2, 2, 2)
+    with pytest.raises(ValueError, match="GPU"):
+        msda_forward(v, [[8, 10], [4, 5]], None, loc, a)
+    with pytest.raises(TypeError):
+        msda_forward(v, [[8, 10], [4, 5]], None, loc.double(), a)
+    with pytest.raises(ValueError):
+        msda_forward(v, [[8, 10], [4, 5], [2, 2]], None, loc, a)

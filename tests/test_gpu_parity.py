@@ -1,0 +1,359 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every workload runs forward + backward on the GPU and is compared element by
+element with the oracle on the same seeded inputs (tests/_parity.py holds the
+tolerance rule), at the workloads' full sizes. Edge cases cover ragged query blocks,
+channel widths that need masking, misaligned pointers, custom level tables,
+empty inputs, out-of-bounds points, integer-aligned points, accumulation,
+determinism and 64-bit indexing.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from scale_deformable_attention_amd import MSDAError, msda_backward, msda_forward
+from scale_deformable_attention_amd.workloads import Workload, make_inputs, workload
+
+from _parity import check_backward, check_forward, level_row_ranges, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _library():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from scale_deformable_attention_amd import _binding
+    import os
+    if not os.path.exists(_binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    _binding.load_library()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def to_dev(inp):
+    return {k: (v.to(DEV) if k != "spatial_shapes" else v) for k, v in inp.items()}
+
+
+def gpu_run(inp, accum="auto", starts=None):
+    g = to_dev(inp)
+    out = msda_forward(g["value"], g["spatial_shapes"], starts, g["sampling_locations"],
+                       g["attention_weights"])
+    grads = msda_backward(g["value"], g["spatial_shapes"], starts, g["sampling_locations"],
+                          g["attention_weights"], g["grad_output"], accum=accum)
+    torch.cuda.synchronize()
+    return out.cpu(), tuple(t.cpu() for t in grads)
+
+
+def oracle_run(inp, starts=None):
+    args = (inp["value"], inp["spatial_shapes"], starts, inp["sampling_locations"],
+            inp["attention_weights"])
+    out, touched = oracle.forward(*args, return_touched=True)
+    gv, gl, ga, trows = oracle.backward(*args, inp["grad_output"], return_touched=True)
+    return out, touched, (gv, gl, ga), trows
+
+
+def full_check(inp, dtype, accum="auto", starts=None, ref=None):
+    out, grads = gpu_run(inp, accum, starts)
+    ref_out, touched, ref_grads, trows = ref if ref is not None else oracle_run(inp, starts)
+    stats = check_forward(dtype, out, ref_out, touched)
+    stats += check_backward(dtype, grads, ref_grads, inp["spatial_shapes"], starts, trows)
+    for s in stats:
+        if s.get("n"):
+            say(f"  {s['name']:34s} max_scaled={s['max_scaled']:.2e} normwise={s['normwise']:.2e}")
+    return out, grads
+
+
+# ------------------------------------------------------------- workloads
+
+_REF_CACHE = {}
+
+
+def _cached(name):
+    if name not in _REF_CACHE:
+        inp = make_inputs(workload(name))
+        _REF_CACHE[name] = (inp, oracle_run(inp))
+    return _REF_CACHE[name]
+
+
+@pytest.mark.parametrize("name,accum", [
+    ("tiny_fp32", "auto"),
+    ("decoder_bf16", "auto"), ("decoder_bf16", "native"), ("decoder_bf16", "fp32_scratch"),
+    ("encoder_fp16", "native"), ("encoder_fp16", "fp32_scratch"),
+    ("oddhead_fp32", "auto"),
+])
+def test_workload_parity(name, accum):
+    wl = workload(name)
+    say(f"case {name} accum={accum}: B={wl.B} Q={wl.num_queries} M={wl.M} D={wl.D} "
+        f"L={wl.L} K={wl.K} {wl.dtype}")
+    inp, ref = _cached(name)
+    full_check(inp, wl.dtype, accum, ref=ref)
+
+
+def test_large_encoder_parity():
+    name = "large_encoder_bf16"
+    wl = workload(name)
+    say(f"case {name} accum=auto: B={wl.B} Q={wl.num_queries} M={wl.M} D={wl.D} "
+        f"L={wl.L} K={wl.K} {wl.dtype}")
+    inp, ref = _cached(name)
+    full_check(inp, wl.dtype, "auto", ref=ref)
+
+
+def test_native_bf16_atomics_error_profile():
+    """Packed bf16 atomics round the running sum to 8 significant bits on every
+    add (course page "5. The backward kernel", section "Atomics make gradients
+    nondeterministic"). On the large encoder a few elements per million drift
+    past the elementwise 5e-2 bar, which is why AUTO accumulates bf16 in fp32
+    scratch; the opt-in native path stays close in norm and direction."""
+    name = "large_encoder_bf16"
+    wl = workload(name)
+    say(f"case {name} accum=native (normwise bound)")
+    inp, (ref_out, touched, ref_grads, trows) = _cached(name)
+    _, grads = gpu_run(inp, "native")
+    gv = to_np(grads[0])
+    assert np.all(gv[~trows] == 0)
+    for l, (r0, r1) in enumerate(level_row_ranges(inp["spatial_shapes"])):
+        got, want = gv[:, r0:r1].ravel(), ref_grads[0][:, r0:r1].ravel()
+        normwise = np.linalg.norm(got - want) / np.linalg.norm(want)
+        cos = np.dot(got, want) / (np.linalg.norm(got) * np.linalg.norm(want))
+        say(f"  grad_value[level {l}] native bf16: normwise {normwise:.2e} cos {cos:.6f}")
+        assert normwise < 2e-2 and cos > 0.9998
+
+
+# ------------------------------------------------------------ edge cases
+
+def _small(dtype, D=8, Q=37, M=3, K=3, levels=((6, 9), (3, 5), (2, 2)), B=2, lo=-0.15, hi=1.15,
+           seed=77):
+    wl = Workload(name="edge", dtype=dtype, B=B, Q=Q, M=M, D=D, K=K, levels=levels,
+                  loc_kind="uniform", loc_lo=lo, loc_hi=hi, seed=seed)
+    return wl, make_inputs(wl)
+
+
+DTYPES = [torch.float32, torch.float16, torch.bfloat16]
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+@pytest.mark.parametrize("D", [1, 3, 8, 24, 32, 48, 64, 128, 256])
+def test_head_dims_and_ragged_queries(dtype, D):
+    wl, inp = _small(dtype, D=D)
+    say(f"case head_dim D={D} {dtype} Q={wl.Q}")
+    full_check(inp, dtype, "native")
+    if dtype != torch.float32:
+        full_check(inp, dtype, "fp32_scratch")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+def test_widest_head_dim(dtype):
+    D = 512 if dtype != torch.float32 else 256  # 64 lanes x widest vector
+    wl, inp = _small(dtype, D=D, Q=9, M=2)
+    say(f"case widest head_dim D={D} {dtype}")
+    full_check(inp, dtype, "native")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+@pytest.mark.parametrize("K,L", [(1, 1), (8, 2), (5, 3), (2, 16)])
+def test_points_and_levels(dtype, K, L):
+    levels = tuple((3 + (i % 4), 2 + (i % 5)) for i in range(L))
+    wl, inp = _small(dtype, K=K, levels=levels, Q=300, B=1, M=2, D=16)
+    say(f"case K={K} L={L} {dtype}")
+    # tiny levels: up to 1600 contributions per pixel, so bf16 goes through
+    # the default (fp32 scratch) accumulation
+    full_check(inp, dtype, "auto")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+def test_custom_level_start_and_padding_rows(dtype):
+    levels = ((6, 9), (3, 5), (2, 2))
+    wl, inp = _small(dtype, levels=levels)
+    # levels stored in another order along S, with 11 unused rows (19..29)
+    starts = torch.tensor([30, 4, 0])
+    S = 30 + 54
+    g = torch.Generator().manual_seed(3)
+    B, _, M, D = inp["value"].shape
+    inp["value"] = torch.randn(B, S, M, D, generator=g).to(dtype)
+    say(f"case custom level_start_index {starts.tolist()} S={S} {dtype}")
+    full_check(inp, dtype, "native", starts=starts)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+def test_misaligned_pointers_fall_back_to_narrow_access(dtype):
+    wl, inp = _small(dtype, D=32, Q=20)
+    g = to_dev(inp)
+    say(f"case misaligned value/output pointers {dtype}")
+    ref_out, touched, ref_grads, trows = oracle_run(inp)
+    # views starting one element into a larger buffer: element-aligned only
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+    v, loc, a, go = (shifted(g[k]) for k in ("value", "sampling_locations", "attention_weights",
+                                              "grad_output"))
+    out = shifted(torch.empty(wl.B, wl.Q, wl.M * wl.D, dtype=dtype, device=DEV))
+    msda_forward(v, g["spatial_shapes"], None, loc, a, output=out)
+    gv = shifted(torch.empty_like(g["value"]))
+    gl = shifted(torch.empty_like(g["sampling_locations"]))
+    ga = shifted(torch.empty_like(g["attention_weights"]))
+    kw = dict(grad_value=gv, grad_sampling_locations=gl, grad_attention_weights=ga)
+    if dtype != torch.float32:
+        # packed atomics would straddle the tensor's edge: refused, scratch works
+        with pytest.raises(MSDAError, match="4-byte aligned"):
+            msda_backward(v, g["spatial_shapes"], None, loc, a, go, accum="native", **kw)
+    msda_backward(v, g["spatial_shapes"], None, loc, a, go,
+                  accum="native" if dtype == torch.float32 else "fp32_scratch", **kw)
+    torch.cuda.synchronize()
+    check_forward(dtype, out.cpu(), ref_out, touched)
+    check_backward(dtype, (gv.cpu(), gl.cpu(), ga.cpu()), ref_grads, inp["spatial_shapes"], None,
+                   trows)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+def test_non_contiguous_inputs(dtype):
+    wl, inp = _small(dtype, D=16)
+    g = to_dev(inp)
+    say(f"case non-contiguous inputs {dtype}")
+    # same values, non-contiguous storage
+    v = g["value"].transpose(1, 2).contiguous().transpose(1, 2)
+    loc = g["sampling_locations"].permute(5, 0, 1, 2, 3, 4).contiguous().permute(1, 2, 3, 4, 5, 0)
+    assert not v.is_contiguous() and not loc.is_contiguous()
+    out = msda_forward(v, g["spatial_shapes"], None, loc, g["attention_weights"])
+    torch.cuda.synchronize()
+    ref_out = oracle.forward(inp["value"], inp["spatial_shapes"], None, inp["sampling_locations"],
+                             inp["attention_weights"])
+    check_forward(dtype, out.cpu(), ref_out)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+def test_empty_batch_and_queries(dtype):
+    say(f"case empty B/Q {dtype}")
+    wl, inp = _small(dtype, Q=0)
+    g = to_dev(inp)
+    out = msda_forward(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                       g["attention_weights"])
+    assert out.shape == (wl.B, 0, wl.M * wl.D)
+    for accum in ("native", "fp32_scratch"):
+        gv = torch.full_like(g["value"], 7.0)
+        gv, gl, ga = msda_backward(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                                   g["attention_weights"], g["grad_output"], grad_value=gv,
+                                   accum=accum)
+        torch.cuda.synchronize()
+        assert torch.all(gv == 0) and gl.numel() == 0 and ga.numel() == 0
+    wl, inp = _small(dtype, B=0)
+    g = to_dev(inp)
+    out = msda_forward(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                       g["attention_weights"])
+    assert out.shape[0] == 0
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+def test_all_points_out_of_bounds(dtype):
+    wl, inp = _small(dtype)
+    loc = inp["sampling_locations"].float()
+    sel = torch.rand(loc.shape[:-1], generator=torch.Generator().manual_seed(1)) < 0.5
+    loc[..., 0] = torch.where(sel, torch.tensor(1.6), torch.tensor(-0.8))
+    inp["sampling_locations"] = loc.to(dtype)
+    say(f"case all points out of bounds {dtype}")
+    out, (gv, gl, ga) = gpu_run(inp, "native")
+    assert torch.all(out == 0) and torch.all(gv == 0) and torch.all(gl == 0) and torch.all(ga == 0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+def test_integer_aligned_points_reproduce_rows_exactly(dtype):
+    levels = ((8, 16), (4, 8))
+    B, Q, M, D, K, L = 2, 50, 2, 16, 2, 2
+    g = torch.Generator().manual_seed(12)
+    S = sum(h * w for h, w in levels)
+    value = torch.randn(B, S, M, D, generator=g).to(dtype)
+    loc = torch.empty(B, Q, M, L, K, 2)
+    for l, (H, W) in enumerate(levels):
+        ix = torch.randint(W, (B, Q, M, K), generator=g)
+        iy = torch.randint(H, (B, Q, M, K), generator=g)
+        loc[:, :, :, l, :, 0] = (ix + 0.5) / W
+        loc[:, :, :, l, :, 1] = (iy + 0.5) / H
+    hot = torch.randint(L * K, (B, Q, M), generator=g)
+    attn = torch.nn.functional.one_hot(hot, L * K).float().reshape(B, Q, M, L, K)
+    inp = {"value": value, "spatial_shapes": torch.tensor(levels),
+           "sampling_locations": loc.to(dtype), "attention_weights": attn.to(dtype),
+           "grad_output": torch.randn(B, Q, M * D, generator=g).to(dtype)}
+    say(f"case integer-aligned one-hot points {dtype}")
+    out, _ = gpu_run(inp, "native")
+    ref = oracle.forward(inp["value"], inp["spatial_shapes"], None, inp["sampling_locations"],
+                         inp["attention_weights"])
+    # each output row is exactly one value row: bit-exact in every dtype
+    assert torch.equal(out.double(), torch.from_numpy(ref).to(dtype).double())
+    assert np.array_equal(to_np(out), ref)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+@pytest.mark.parametrize("accum", ["native", "fp32_scratch"])
+def test_accumulate_flag_doubles_grad_value(dtype, accum):
+    if dtype == torch.float32 and accum == "fp32_scratch":
+        pytest.skip("identical to native for fp32")
+    wl, inp = _small(dtype, D=16)
+    g = to_dev(inp)
+    say(f"case accumulate twice {dtype} {accum}")
+    args = (g["value"], g["spatial_shapes"], None, g["sampling_locations"], g["attention_weights"],
+            g["grad_output"])
+    gv1, _, _ = msda_backward(*args, accum=accum)
+    once = gv1.clone()
+    msda_backward(*args, grad_value=gv1, accum=accum, accumulate=True)
+    torch.cuda.synchronize()
+    ref = oracle.backward(inp["value"], inp["spatial_shapes"], None, inp["sampling_locations"],
+                          inp["attention_weights"], inp["grad_output"])[0]
+    tol = 1e-5 if dtype == torch.float32 else 5e-2
+    from _parity import check_slice
+    check_slice("grad_value once", to_np(once), ref, tol)
+    check_slice("grad_value twice", to_np(gv1), 2 * ref, tol)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+def test_deterministic_outputs(dtype):
+    wl, inp = _small(dtype, D=32, Q=200)
+    say(f"case determinism {dtype}")
+    out1, (gv1, gl1, ga1) = gpu_run(inp, "fp32_scratch" if dtype != torch.float32 else "native")
+    out2, (gv2, gl2, ga2) = gpu_run(inp, "fp32_scratch" if dtype != torch.float32 else "native")
+    assert torch.equal(out1, out2) and torch.equal(gl1, gl2) and torch.equal(ga1, ga2)
+    # grad_value: atomic order may differ; fp32 accumulation keeps runs within rounding
+    d = (gv1.double() - gv2.double()).abs().max().item()
+    scale = gv1.double().abs().max().item()
+    assert d <= 1e-6 * scale + (2.0 ** -8 if dtype != torch.float32 else 0.0) * scale
+
+
+def test_int64_indexing_beyond_2_pow_31_elements():
+    """B*S*M*D above 2^31 elements: the last batch's value rows sit past
+    element 2^31; every other batch holds a constant sentinel."""
+    levels = ((512, 896), (256, 448), (128, 224), (64, 112))
+    S = sum(h * w for h, w in levels)
+    B, M, D, K, Q = 16, 8, 32, 4, 512
+    assert B * S * M * D > 2 ** 31
+    dtype = torch.bfloat16
+    say(f"case int64 indexing: B={B} S={S} M={M} D={D} bf16 ({B * S * M * D / 2**30:.2f} Gi elements)")
+    wl = Workload(name="int64", dtype=dtype, B=1, Q=Q, M=M, D=D, K=K, levels=levels,
+                  loc_kind="uniform", seed=99)
+    last = make_inputs(wl)  # batch B-1's inputs
+    value = torch.full((B, S, M, D), 1000.0, dtype=dtype, device=DEV)
+    value[B - 1].copy_(last["value"][0].to(DEV))
+    def rep(t):
+        return t.to(DEV).expand(B, *t.shape[1:]).contiguous()
+    loc, attn, gout = rep(last["sampling_locations"]), rep(last["attention_weights"]), \
+        rep(last["grad_output"])
+    shapes = last["spatial_shapes"]
+    out = msda_forward(value, shapes, None, loc, attn)
+    gv, gl, ga = msda_backward(value, shapes, None, loc, attn, gout, accum="native")
+    torch.cuda.synchronize()
+    out_last = out[B - 1:].cpu()
+    gv_last = gv[B - 1:].cpu()
+    gl_last, ga_last = gl[B - 1:].cpu(), ga[B - 1:].cpu()
+    del value, gv, out
+    torch.cuda.empty_cache()
+    ref_out, touched, ref_grads, trows = oracle_run(last)
+    check_forward(dtype, out_last, ref_out, touched)
+    check_backward(dtype, (gv_last, gl_last, ga_last), ref_grads, shapes, None, trows)
