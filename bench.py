@@ -19,9 +19,10 @@ Algorithmic bytes per launch (e = element size, P = B*Q*M*L*K points,
 U = distinct (b, row, m) value rows with at least one in-bounds corner):
   forward       3*P*e (locations + weights) + B*Q*M*D*e (output) + U*D*e
   scatter       3*P*e (params) + B*Q*M*D*e (grad_output) + U*D*e (value)
-                + 2*U*D*e_acc (read-modify-write of touched grad rows)
+                + 2*U*D*e_acc (read-modify-write of touched grad rows; e_acc = 4
+                  for rows of levels accumulated in fp32 scratch)
                 + 3*P*e (grad locations + grad weights)
-  zero fill     B*S*M*D*e_acc;   downcast   B*S*M*D*(4 + e)
+  zero fill     B*S*M*D*e (+ scratch rows * 4);  scratch add  rows * D * (4 + 2e)
 """
 
 from __future__ import annotations
@@ -53,7 +54,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def touched_rows(inp) -> int:
+def touched_rows(inp, only_levels=None) -> int:
     """U: distinct (b, row, m) value rows that at least one in-bounds corner
     lands on. Host-side accounting of compulsory bytes (single-rounding
     pixel mapping as in the kernels; products of an fp32 location and an
@@ -67,6 +68,9 @@ def touched_rows(inp) -> int:
     m_idx = np.arange(M).reshape(1, 1, M, 1)
     start = 0
     for l, (H, W) in enumerate(shapes):
+        if only_levels is not None and l not in only_levels:
+            start += H * W
+            continue
         x = (loc[:, :, :, l, :, 0] * W - 0.5).astype(np.float32)
         y = (loc[:, :, :, l, :, 1] * H - 0.5).astype(np.float32)
         x0 = np.floor(x).astype(np.int64)
@@ -226,27 +230,36 @@ def main():
     # Per-kernel device time, host overhead removed by graph replay.
     reps, inner = 20, 20
     fwd_kernel_us = time_graph(call.forward, reps, inner)
-    # the scatter kernel alone: native accumulation adding into grad_value
+    # the scatter kernel alone, as the default accumulation runs it: add into
+    # grad_value and keep adding into the scratch levels (no fill, no final add)
+    from scale_deformable_attention_amd._binding import FLAG_CONTINUE_SCRATCH, FLAG_DEFER_SCRATCH
+    call.backward()
+    scatter_us = time_graph(lambda: call.backward(
+        accumulate=True, flags=FLAG_CONTINUE_SCRATCH | FLAG_DEFER_SCRATCH), reps, inner)
     scatter_native_us = time_graph(lambda: call.backward(accumulate=True, accum="native"), reps,
                                    inner)
     graph_step_us = time_graph(step, reps, 5)
-    log(f"graph replay: forward kernel {fwd_kernel_us:.2f} us, native scatter kernel "
-        f"{scatter_native_us:.2f} us, full step {graph_step_us:.2f} us")
+    log(f"graph replay: forward kernel {fwd_kernel_us:.2f} us, scatter kernel ({call.resolved_accum}) "
+        f"{scatter_us:.2f} us, all-native scatter kernel {scatter_native_us:.2f} us, "
+        f"full step {graph_step_us:.2f} us")
 
     # Algorithmic bytes.
     e = torch.finfo(wl.dtype).bits // 8
     B, S, M, D, L, Kp, Q = wl.B, wl.S, wl.M, wl.D, wl.L, wl.K, wl.num_queries
     P = B * Q * M * L * Kp
     U = touched_rows(inp)
-    e_native_acc = e
+    U_scr = touched_rows(inp, only_levels=call.scratch_levels()) if call.scratch_levels() else 0
     fwd_bytes = 3 * P * e + B * Q * M * D * e + U * D * e
-    scatter_bytes = 3 * P * e + B * Q * M * D * e + U * D * e + 2 * U * D * e_native_acc + 3 * P * e
+    # grad rows: read + write once each, 2 bytes per element in bf16/fp16 levels
+    # and 4 in fp32 ones (fp32 data, or the scratch levels of 16-bit data)
+    grad_rows = 2 * ((U - U_scr) * D * e + U_scr * D * 4)
+    scatter_bytes = 3 * P * e + B * Q * M * D * e + U * D * e + grad_rows + 3 * P * e
     fwd_gbps = fwd_bytes / (fwd_kernel_us * 1e-6) / 1e9
-    scatter_gbps = scatter_bytes / (scatter_native_us * 1e-6) / 1e9
+    scatter_gbps = scatter_bytes / (scatter_us * 1e-6) / 1e9
     # Dominant kernel: the longer of the two hot kernels.
     src_hash = kernel_source_hash()
-    if scatter_native_us >= fwd_kernel_us:
-        kname, kus, kbytes = "msda_bwd_kernel", scatter_native_us, scatter_bytes
+    if scatter_us >= fwd_kernel_us:
+        kname, kus, kbytes = "msda_bwd_kernel", scatter_us, scatter_bytes
     else:
         kname, kus, kbytes = "msda_fwd_kernel", fwd_kernel_us, fwd_bytes
     achieved = kbytes / (kus * 1e-6) / 1e9
@@ -270,8 +283,8 @@ def main():
         "fwd_us": round(fwd_us, 3), "bwd_us": round(bwd_us, 3), "host_enqueue_us": round(host_us, 3),
         "graph_step_us": round(graph_step_us, 3),
         "fwd_kernel_us": round(fwd_kernel_us, 3), "fwd_kernel_GBps": round(fwd_gbps, 1),
-        "scatter_native_kernel_us": round(scatter_native_us, 3),
-        "scatter_native_kernel_GBps": round(scatter_gbps, 1),
+        "scatter_kernel_us": round(scatter_us, 3), "scatter_kernel_GBps": round(scatter_gbps, 1),
+        "scatter_all_native_kernel_us": round(scatter_native_us, 3),
         "touched_rows_U": U, "points_P": P,
         "roofline": roofline,
     }

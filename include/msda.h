@@ -78,11 +78,19 @@ typedef enum msda_dtype {
  *                 (fp32 atomics, or packed two-wide fp16 / bf16 atomics);
  *   FP32_SCRATCH  fp32 atomics into the caller's workspace, then one
  *                 downcast pass into grad_value (identical to NATIVE for fp32);
- *   AUTO          the library's measured choice for this dtype and shape. */
+ *   AUTO          the library's measured choice: fp32 data -> fp32 atomics;
+ *                 fp16 -> packed fp16 atomics; bf16 -> per level: fp32 scratch
+ *                 for levels whose pixels receive more than 4 contributions on
+ *                 average (Q*K*4 / (H_l*W_l) > 4), packed bf16 atomics for the
+ *                 others (bf16 keeps 8 significant bits, so long chains of
+ *                 rounded adds drift; see msda_backward).
+ * The scratch for a level is laid out (B, H_l*W_l, M, D) in fp32; its rows are
+ * added into grad_value once at the end. */
 typedef enum msda_accum {
     MSDA_ACCUM_AUTO = -1,
     MSDA_ACCUM_NATIVE = 0,
-    MSDA_ACCUM_FP32_SCRATCH = 1
+    MSDA_ACCUM_FP32_SCRATCH = 1,
+    MSDA_ACCUM_PER_LEVEL = 2  /* resolution only: scratch for some levels */
 } msda_accum_t;
 
 typedef enum msda_status {
@@ -100,6 +108,15 @@ typedef enum msda_status {
 /* Add into grad_value instead of overwriting it (training-style gradient
  * accumulation); without it the library zero-fills grad_value first. */
 #define MSDA_FLAG_ACCUMULATE_GRAD_VALUE 1u
+/* The workspace already holds this problem's fp32 partial sums from an earlier
+ * call made with MSDA_FLAG_DEFER_SCRATCH: keep adding to them instead of
+ * zero-filling the workspace first. */
+#define MSDA_FLAG_CONTINUE_SCRATCH 2u
+/* Leave the fp32 sums of the scratch levels in the workspace instead of
+ * adding them into grad_value at the end. With CONTINUE_SCRATCH this lets
+ * several backward calls (micro-batches) accumulate in fp32 and round into
+ * grad_value once, by a last call without DEFER_SCRATCH. */
+#define MSDA_FLAG_DEFER_SCRATCH 4u
 
 /*
  * Forward. Writes every element of `output` (B, Q, M, D).
@@ -127,8 +144,10 @@ size_t msda_backward_workspace_size(int dtype, int64_t batch, int64_t num_keys,
                                     int accum);
 
 /*
- * The accumulation mode msda_backward will use for `accum` on this problem
- * (AUTO resolved to NATIVE or FP32_SCRATCH), or -1 on invalid arguments.
+ * The accumulation msda_backward will use for `accum` on this problem:
+ * NATIVE (no level uses scratch; always the case for fp32 data),
+ * FP32_SCRATCH (every level does), PER_LEVEL (some levels do), or -1 on
+ * invalid arguments.
  */
 int msda_backward_resolve_accum(int dtype, int64_t batch, int64_t num_keys,
                                 int64_t num_heads, int64_t head_dim,

@@ -21,8 +21,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmsda_amd.so")
 
 MSDA_F32, MSDA_F16, MSDA_BF16 = 0, 1, 2
-ACCUM_AUTO, ACCUM_NATIVE, ACCUM_FP32_SCRATCH = -1, 0, 1
+ACCUM_AUTO, ACCUM_NATIVE, ACCUM_FP32_SCRATCH, ACCUM_PER_LEVEL = -1, 0, 1, 2
+_RESOLVED = {ACCUM_NATIVE: "native", ACCUM_FP32_SCRATCH: "fp32_scratch", ACCUM_PER_LEVEL: "per_level"}
 FLAG_ACCUMULATE_GRAD_VALUE = 1
+FLAG_CONTINUE_SCRATCH = 2
+FLAG_DEFER_SCRATCH = 4
 MAX_LEVELS = 16
 
 _DTYPE_CODES = {torch.float32: MSDA_F32, torch.float16: MSDA_F16, torch.bfloat16: MSDA_BF16}
@@ -189,7 +192,7 @@ def msda_backward_resolve_accum(value: torch.Tensor, spatial_shapes, level_start
                                             _ACCUM_CODES[accum]))
     if r < 0:
         _check(int(MSDAErrorCodes.DTYPE))
-    return {ACCUM_NATIVE: "native", ACCUM_FP32_SCRATCH: "fp32_scratch"}[r]
+    return _RESOLVED[r]
 
 
 class MSDAErrorCodes:
@@ -202,12 +205,15 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index,
                   grad_sampling_locations: Optional[torch.Tensor] = None,
                   grad_attention_weights: Optional[torch.Tensor] = None,
                   accum: Union[str, bool, None] = "auto", accumulate: bool = False,
-                  workspace: Optional[torch.Tensor] = None, stream=None
+                  workspace: Optional[torch.Tensor] = None, stream=None,
+                  continue_scratch: bool = False, defer_scratch: bool = False
                   ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Backward of the MSDA core: (grad_value, grad_sampling_locations,
     grad_attention_weights). `accum` is "auto", "native" or "fp32_scratch"
     (True/False/None are accepted as in the pages' fp32_grad_accum switch).
-    With `accumulate`, grad_value (given) is added into instead of overwritten."""
+    With `accumulate`, grad_value (given) is added into instead of overwritten.
+    `continue_scratch` / `defer_scratch` map to MSDA_FLAG_CONTINUE_SCRATCH /
+    MSDA_FLAG_DEFER_SCRATCH (fp32 accumulation across calls in `workspace`)."""
     lib = load_library()
     levels = _Levels(spatial_shapes, level_start_index)
     code = _dtype_code(value, sampling_locations, attention_weights, grad_output)
@@ -237,12 +243,15 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index,
     acode = _ACCUM_CODES[accum]
     need = int(lib.msda_backward_workspace_size(*prob, acode))
     if need and workspace is None:
+        if continue_scratch or defer_scratch:
+            raise ValueError("continue_scratch / defer_scratch need the caller's workspace")
         workspace = torch.empty(need, dtype=torch.uint8, device=value.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    flags = (FLAG_ACCUMULATE_GRAD_VALUE if accumulate else 0) | \
+        (FLAG_CONTINUE_SCRATCH if continue_scratch else 0) | (FLAG_DEFER_SCRATCH if defer_scratch else 0)
     _check(lib.msda_backward(*prob, _ptr(value), _ptr(loc), _ptr(attn), _ptr(gout),
-                             _ptr(grad_value), _ptr(grad_loc), _ptr(grad_attn), acode,
-                             FLAG_ACCUMULATE_GRAD_VALUE if accumulate else 0, _ptr(workspace),
-                             ws_bytes, _stream(value.device, stream)))
+                             _ptr(grad_value), _ptr(grad_loc), _ptr(grad_attn), acode, flags,
+                             _ptr(workspace), ws_bytes, _stream(value.device, stream)))
     return grad_value, grad_loc, grad_attn
 
 
@@ -289,17 +298,29 @@ class PreparedCall:
                                           _ptr(self.grad_value), _ptr(self.grad_loc),
                                           _ptr(self.grad_attn))
             self._ws = (_ptr(self.workspace), need)
-        self.resolved_accum = {ACCUM_NATIVE: "native", ACCUM_FP32_SCRATCH: "fp32_scratch"}.get(
+        self.resolved_accum = _RESOLVED.get(
             int(self.lib.msda_backward_resolve_accum(*self.prob, self.accum_code)))
+
+    def scratch_levels(self):
+        """Levels whose grad_value rows the backward accumulates in fp32 scratch
+        under this call's accumulation mode (same rule as the library)."""
+        if self.value.dtype == torch.float32 or self.resolved_accum == "native":
+            return []
+        L = self.levels.L
+        if self.resolved_accum == "fp32_scratch":
+            return list(range(L))
+        B, Q, M, _, K, _ = self.loc.shape
+        return [l for l, (h, w) in enumerate(self.levels.shapes.tolist()) if Q * K * 4 / (h * w) > 4.0]
 
     def forward(self) -> torch.Tensor:
         _check(self.lib.msda_forward(*self._fwd_args, _stream(self.device, self._stream_arg)))
         return self.output
 
-    def backward(self, accumulate: bool = False, accum=None):
+    def backward(self, accumulate: bool = False, accum=None, flags: int = 0):
+        """One backward call; `flags` adds MSDA_FLAG_* bits (CONTINUE / DEFER scratch)."""
         code = self.accum_code if accum is None else _ACCUM_CODES[accum]
         ws = self._ws if accum is None else (self._ws if code == self.accum_code else (None, 0))
-        _check(self.lib.msda_backward(*self._bwd_head, code,
-                                      FLAG_ACCUMULATE_GRAD_VALUE if accumulate else 0, ws[0], ws[1],
+        fl = (FLAG_ACCUMULATE_GRAD_VALUE if accumulate else 0) | flags
+        _check(self.lib.msda_backward(*self._bwd_head, code, fl, ws[0], ws[1],
                                       _stream(self.device, self._stream_arg)))
         return self.grad_value, self.grad_loc, self.grad_attn

@@ -80,6 +80,7 @@ int make_problem(int dtype, int64_t B, int64_t S, int64_t M, int64_t D, int64_t 
     p->Q = Q;
     p->K = K;
     memset(&p->levels, 0, sizeof(p->levels));
+    for (int l = 0; l < MSDA_MAX_LEVELS; ++l) p->levels.scratch_off[l] = -1;
     int64_t acc = 0;
     for (int64_t l = 0; l < L; ++l) {
         const int64_t H = shapes[2 * l], W = shapes[2 * l + 1];
@@ -172,21 +173,84 @@ int hip_fail(hipError_t err, const char *what) {
     return fail(MSDA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
 }
 
-// Accumulation policy for AUTO. fp32 data: fp32 atomics into grad_value.
-// fp16: packed fp16 atomics. bf16: fp32 scratch (packed bf16 atomics round
-// every add to 8 bits and drift on heavily shared pixels).
-int resolve_accum(const msda::Problem &p, int accum) {
-    if (p.dtype == MSDA_F32) return MSDA_ACCUM_NATIVE;
-    if (accum == MSDA_ACCUM_AUTO) {
-        if ((p.B * p.S * p.M * p.D) % 2 != 0) return MSDA_ACCUM_FP32_SCRATCH;
-        return p.dtype == MSDA_F16 ? MSDA_ACCUM_NATIVE : MSDA_ACCUM_FP32_SCRATCH;
-    }
-    return accum;
+// Average number of contributions a pixel of level l receives: every query
+// samples K points per level, each touching 4 corners.
+double contributions_per_pixel(const msda::Problem &p, int l) {
+    return (double)p.Q * (double)p.K * 4.0 /
+           ((double)p.levels.H[l] * (double)p.levels.W[l]);
 }
 
-size_t scratch_bytes(const msda::Problem &p, int resolved) {
-    if (p.dtype == MSDA_F32 || resolved != MSDA_ACCUM_FP32_SCRATCH) return 0;
-    return (size_t)(p.B * p.S * p.M * p.D) * sizeof(float);
+// Decide, per level, whether the backward accumulates in fp32 scratch, and
+// lay the scratch blocks out back to back. Returns the workspace bytes.
+// AUTO: fp32 data never needs scratch; fp16 keeps packed fp16 atomics (11
+// significant bits held parity on every tested shape, including ~1300
+// contributions per pixel); bf16 (8 significant bits) uses fp32 scratch for
+// levels above 4 contributions per pixel, where chains of rounded adds drift
+// beyond the 5e-2 parity bar in the tails.
+size_t plan_scratch(msda::Problem *p, int accum) {
+    size_t total = 0;
+    for (int l = 0; l < (int)p->L; ++l) {
+        bool scratch = false;
+        if (p->dtype != MSDA_F32) {
+            if (accum == MSDA_ACCUM_FP32_SCRATCH) scratch = true;
+            else if (accum == MSDA_ACCUM_AUTO && p->dtype == MSDA_BF16)
+                scratch = contributions_per_pixel(*p, l) > 4.0;
+        }
+        if (scratch) {
+            p->levels.scratch_off[l] = (int64_t)(total / sizeof(float));
+            total += (size_t)(p->B * (int64_t)p->levels.H[l] * p->levels.W[l] * p->M * p->D) *
+                     sizeof(float);
+        } else {
+            p->levels.scratch_off[l] = -1;
+        }
+    }
+    return total;
+}
+
+int resolved_mode(const msda::Problem &p) {
+    int n = 0;
+    for (int l = 0; l < (int)p.L; ++l) n += p.levels.scratch_off[l] >= 0;
+    if (n == 0) return MSDA_ACCUM_NATIVE;
+    return n == (int)p.L ? MSDA_ACCUM_FP32_SCRATCH : MSDA_ACCUM_PER_LEVEL;
+}
+
+bool valid_accum(int accum) {
+    return accum == MSDA_ACCUM_AUTO || accum == MSDA_ACCUM_NATIVE ||
+           accum == MSDA_ACCUM_FP32_SCRATCH;
+}
+
+// Backward lane mapping: slots of one dword for 16-bit data with even D and
+// 4-byte aligned pointers, else one channel; G = min(16, slots) lanes per
+// query so that one instruction of a group covers one 64-byte segment.
+int choose_bwd_mapping(const msda::Problem &p, bool pairs_aligned, msda::BwdMapping *mp) {
+    const size_t e = elem_size(p.dtype);
+    mp->slot = (e == 2 && p.D % 2 == 0 && pairs_aligned) ? 2 : 1;
+    const int64_t nslots = p.D / mp->slot;
+    const int lg = log2_ceil(nslots) < 4 ? log2_ceil(nslots) : 4;
+    mp->log2_group = lg;
+    const int64_t per_lane = (nslots + (1 << lg) - 1) >> lg;
+    static const int js[] = {1, 2, 3, 4, 8, 16, 32};
+    mp->j = 0;
+    for (int j : js)
+        if (j >= per_lane) {
+            mp->j = j;
+            break;
+        }
+    if (!mp->j || (mp->slot == 2 && mp->j > 16))
+        return fail(MSDA_ERR_UNSUPPORTED, "head_dim %lld too large for the backward (max 512)",
+                    (long long)p.D);
+    const int64_t target_lanes = (int64_t)256 * 8 * 64;
+    const int64_t lanes = p.B * p.M * p.Q * ((int64_t)1 << lg);
+    int ls = 0;
+    while (ls < 2 && p.K % ((int64_t)2 << ls) == 0 && lanes * ((int64_t)1 << ls) < target_lanes &&
+           lg + ls + 1 <= 6)
+        ++ls;
+    mp->log2_split = ls;
+    const int64_t qpb = (int64_t)256 >> (lg + ls);
+    const int64_t qblocks = (p.Q + qpb - 1) / qpb;
+    if (qblocks > INT32_MAX || p.B * p.M * qblocks > (int64_t)INT32_MAX - 8)
+        return fail(MSDA_ERR_UNSUPPORTED, "too many workgroups for one launch");
+    return MSDA_OK;
 }
 
 }  // namespace
@@ -243,11 +307,12 @@ int msda_backward_resolve_accum(int dtype, int64_t batch, int64_t num_keys, int6
     if (make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
                      level_start_index, num_queries, num_points, &p))
         return -1;
-    if (accum != MSDA_ACCUM_AUTO && accum != MSDA_ACCUM_NATIVE && accum != MSDA_ACCUM_FP32_SCRATCH) {
+    if (!valid_accum(accum)) {
         fail(MSDA_ERR_DTYPE, "unknown accumulation mode %d", accum);
         return -1;
     }
-    return resolve_accum(p, accum);
+    plan_scratch(&p, accum);
+    return resolved_mode(p);
 }
 
 size_t msda_backward_workspace_size(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
@@ -259,11 +324,11 @@ size_t msda_backward_workspace_size(int dtype, int64_t batch, int64_t num_keys, 
     if (make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
                      level_start_index, num_queries, num_points, &p))
         return 0;
-    if (accum != MSDA_ACCUM_AUTO && accum != MSDA_ACCUM_NATIVE && accum != MSDA_ACCUM_FP32_SCRATCH) {
+    if (!valid_accum(accum)) {
         fail(MSDA_ERR_DTYPE, "unknown accumulation mode %d", accum);
         return 0;
     }
-    return scratch_bytes(p, resolve_accum(p, accum));
+    return plan_scratch(&p, accum);
 }
 
 int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, int64_t head_dim,
@@ -277,73 +342,58 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
     int st = make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
                           level_start_index, num_queries, num_points, &p);
     if (st) return st;
-    if (accum != MSDA_ACCUM_AUTO && accum != MSDA_ACCUM_NATIVE && accum != MSDA_ACCUM_FP32_SCRATCH)
-        return fail(MSDA_ERR_DTYPE, "unknown accumulation mode %d", accum);
-    if (flags & ~MSDA_FLAG_ACCUMULATE_GRAD_VALUE)
-        return fail(MSDA_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~MSDA_FLAG_ACCUMULATE_GRAD_VALUE);
+    if (!valid_accum(accum)) return fail(MSDA_ERR_DTYPE, "unknown accumulation mode %d", accum);
+    const unsigned known =
+        MSDA_FLAG_ACCUMULATE_GRAD_VALUE | MSDA_FLAG_CONTINUE_SCRATCH | MSDA_FLAG_DEFER_SCRATCH;
+    if (flags & ~known) return fail(MSDA_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~known);
     if (p.B == 0) return ok();
     const bool accumulate = (flags & MSDA_FLAG_ACCUMULATE_GRAD_VALUE) != 0;
-    const int resolved = resolve_accum(p, accum);
-    const size_t need = scratch_bytes(p, resolved);
-    const bool use_scratch = need > 0;
+    const size_t need = plan_scratch(&p, accum);
+    const int mode = resolved_mode(p);
     if ((st = check_ptr(value, "value", dtype))) return st;
     if ((st = check_ptr(grad_value, "grad_value", dtype))) return st;
-    if (use_scratch) {
+    if (need) {
         if (!workspace) return fail(MSDA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
         if (workspace_bytes < need)
             return fail(MSDA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
         if (!aligned(workspace, 16)) return fail(MSDA_ERR_ALIGN, "workspace is not 16-byte aligned");
     }
+    // Native half-precision atomics update aligned 4-byte pairs; every pair
+    // must lie inside grad_value.
+    if (mode != MSDA_ACCUM_FP32_SCRATCH && dtype != MSDA_F32 &&
+        (!aligned(grad_value, 4) || (p.B * p.S * p.M * p.D) % 2 != 0))
+        return fail(MSDA_ERR_ALIGN,
+                    "native half-precision atomics need a 4-byte aligned grad_value with an even "
+                    "element count; use MSDA_ACCUM_FP32_SCRATCH");
+    msda::BwdMapping mp = {1, 1, 0, 0};
     if (p.Q > 0) {
         if ((st = check_ptr(sampling_locations, "sampling_locations", dtype))) return st;
         if ((st = check_ptr(attention_weights, "attention_weights", dtype))) return st;
         if ((st = check_ptr(grad_output, "grad_output", dtype))) return st;
         if ((st = check_ptr(grad_sampling_locations, "grad_sampling_locations", dtype))) return st;
         if ((st = check_ptr(grad_attention_weights, "grad_attention_weights", dtype))) return st;
-    }
-    // Native half-precision atomics update aligned 4-byte pairs; every pair
-    // must lie inside grad_value.
-    if (!use_scratch && dtype != MSDA_F32 &&
-        (!aligned(grad_value, 4) || (p.B * p.S * p.M * p.D) % 2 != 0))
-        return fail(MSDA_ERR_ALIGN,
-                    "native half-precision atomics need a 4-byte aligned grad_value with an even "
-                    "element count; use MSDA_ACCUM_FP32_SCRATCH");
-    msda::Mapping mp = {1, 0, 0};
-    if (p.Q > 0) {
-        // Packed half-precision atomics need 4-byte aligned channel pairs;
-        // an unaligned grad_value falls back to single-element packed adds
-        // through choose_mapping's alignment test on the vector width.
-        const void *vec_ptrs[] = {value, grad_output, grad_value, workspace ? workspace : value};
-        if ((st = choose_mapping(p, vec_ptrs, 4, &mp))) return st;
+        const bool pairs = aligned(value, 4) && aligned(grad_output, 4) && aligned(grad_value, 4);
+        if ((st = choose_bwd_mapping(p, pairs, &mp))) return st;
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t gv_bytes = (size_t)(p.B * p.S * p.M * p.D) * elem_size(dtype);
     hipError_t err;
-    if (use_scratch) {
-        if (p.Q == 0) {
-            if (!accumulate && (err = msda::launch_zero(grad_value, gv_bytes, s)) != hipSuccess)
-                return hip_fail(err, "grad_value zero fill");
-            return ok();
-        }
-        if ((err = msda::launch_zero(workspace, need, s)) != hipSuccess)
-            return hip_fail(err, "scratch zero fill");
-        if ((err = msda::launch_backward(p, mp, value, sampling_locations, attention_weights,
-                                         grad_output, workspace, true, grad_sampling_locations,
-                                         grad_attention_weights, s)) != hipSuccess)
-            return hip_fail(err, "backward launch");
-        if ((err = msda::launch_downcast(dtype, static_cast<const float *>(workspace), grad_value,
-                                         p.B * p.S * p.M * p.D, accumulate, s)) != hipSuccess)
-            return hip_fail(err, "downcast launch");
-        return ok();
-    }
     if (!accumulate && (err = msda::launch_zero(grad_value, gv_bytes, s)) != hipSuccess)
         return hip_fail(err, "grad_value zero fill");
-    if (p.Q == 0) return ok();
-    if ((err = msda::launch_backward(p, mp, value, sampling_locations, attention_weights,
-                                     grad_output, grad_value, dtype == MSDA_F32,
+    const bool keep_sums = (flags & MSDA_FLAG_CONTINUE_SCRATCH) != 0;
+    const bool defer = (flags & MSDA_FLAG_DEFER_SCRATCH) != 0;
+    if (need && !keep_sums && (err = msda::launch_zero(workspace, need, s)) != hipSuccess)
+        return hip_fail(err, "scratch zero fill");
+    if (p.Q > 0 &&
+        (err = msda::launch_backward(p, mp, value, sampling_locations, attention_weights,
+                                     grad_output, grad_value, static_cast<float *>(workspace),
                                      grad_sampling_locations, grad_attention_weights, s)) !=
-        hipSuccess)
+            hipSuccess)
         return hip_fail(err, "backward launch");
+    if (need && !defer &&
+        (err = msda::launch_scratch_add(p, static_cast<const float *>(workspace), grad_value, s)) !=
+            hipSuccess)
+        return hip_fail(err, "scratch add launch");
     return ok();
 }
 

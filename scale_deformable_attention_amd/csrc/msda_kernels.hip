@@ -121,6 +121,100 @@ __device__ __forceinline__ void load_xy(const typename DT::S *p, float &x, float
     y = to_f32(DT{}, p[1]);
 }
 
+// Pin a value in a register at this point of the program: every load it
+// depends on must be issued before here. Used after a chunk's parameter
+// loads so that the compiler cannot sink them next to their first use,
+// which would put one memory round trip per point on the critical path.
+__device__ __forceinline__ void pin(uint32_t &v) { asm volatile("" : "+v"(v)::"memory"); }
+
+// Raw bits of one element, widened to a register.
+template <class DT>
+__device__ __forceinline__ uint32_t load_bits(const typename DT::S *p) {
+    if constexpr (sizeof(typename DT::S) == 4) return __float_as_uint(*p);
+    else return (uint32_t)*p;
+}
+template <class DT>
+__device__ __forceinline__ float bits_to_f32(uint32_t v) {
+    if constexpr (sizeof(typename DT::S) == 4) return __uint_as_float(v);
+    else return to_f32(DT{}, (uint16_t)v);
+}
+
+// ------------------------------------------------------------- gathers
+//
+// Corner rows are read through a raw buffer resource covering one batch's
+// value slice: an offset outside the slice reads as zero and moves no data,
+// so an out-of-bounds corner needs no branch (a branch around a load makes
+// the compiler wait for that load before the branch joins, which would
+// serialise the gathers). Slices above 2 GiB use plain loads from a clamped
+// address followed by a select.
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // >= every buffer size used
+constexpr int kRawBufferConfig = 0x00020000;  // gfx9-family raw buffer descriptor word 3
+
+template <int BYTES>
+__device__ __forceinline__ typename RawVec<BYTES>::type buffer_load_raw(__amdgpu_buffer_rsrc_t r,
+                                                                         uint32_t off);
+template <>
+__device__ __forceinline__ uint16_t buffer_load_raw<2>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ uint32_t buffer_load_raw<4>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ uint2 buffer_load_raw<8>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+template <>
+__device__ __forceinline__ U32x3 buffer_load_raw<12>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    return U32x3{v[0], v[1], v[2]};
+}
+template <>
+__device__ __forceinline__ uint4 buffer_load_raw<16>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <class R>
+__device__ __forceinline__ R zero_raw() {
+    R r;
+    __builtin_memset(&r, 0, sizeof(R));
+    return r;
+}
+
+// One batch's value slice: `base` in bytes and, for BUF, its buffer resource.
+template <bool BUF>
+struct Slice {
+    const char *base;
+    __amdgpu_buffer_rsrc_t rsrc;
+
+    __device__ __forceinline__ Slice(const void *p, int64_t bytes) : base((const char *)p) {
+        if constexpr (BUF)
+            rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                                     kRawBufferConfig);
+    }
+
+    // sizeof(R) bytes at byte offset `off`; zero when !ok.
+    template <class R>
+    __device__ __forceinline__ R gather(int64_t off, bool ok) const {
+        if constexpr (BUF) {
+            return buffer_load_raw<(int)sizeof(R)>(rsrc, ok ? (uint32_t)off : kOutOfRange);
+        } else {
+            const R v = *reinterpret_cast<const R *>(base + (ok ? off : 0));
+            return ok ? v : zero_raw<R>();
+        }
+    }
+};
+
+template <class DT, int N, class R>
+__device__ __forceinline__ void raw_to_f32(const R &r, float (&out)[N]) {
+    typename DT::S e[N];
+    __builtin_memcpy(e, &r, sizeof(R));
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = to_f32(DT{}, e[i]);
+}
+
 // ------------------------------------------------------- cross-lane sums
 
 template <int CTRL>
@@ -166,44 +260,6 @@ __device__ __forceinline__ void atomic_add_pk(BF16T, uint16_t *p, float a, float
     __builtin_amdgcn_global_atomic_fadd_v2bf16(reinterpret_cast<bf16x2_t *>(p), v);
 }
 
-// Add coef * g[0:VEC] into VEC consecutive elements at `t`.
-template <class DT, int VEC, bool FP32ACC>
-struct Scatter;
-
-template <class DT, int VEC>
-struct Scatter<DT, VEC, true> {  // fp32 target
-    __device__ __forceinline__ static void add(void *t, int64_t off, float coef,
-                                               const float (&g)[VEC]) {
-        float *p = static_cast<float *>(t) + off;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) atomic_add_f32(p + i, coef * g[i]);
-    }
-};
-
-template <class DT, int VEC>
-struct Scatter<DT, VEC, false> {  // packed half-precision target
-    __device__ __forceinline__ static void add(void *t, int64_t off, float coef,
-                                               const float (&g)[VEC]) {
-        uint16_t *p = static_cast<uint16_t *>(t) + off;
-        if constexpr (VEC % 2 == 0) {
-            // the host guarantees 4-byte alignment of every pair
-#pragma unroll
-            for (int i = 0; i < VEC; i += 2) atomic_add_pk(DT{}, p + i, coef * g[i], coef * g[i + 1]);
-        } else {
-            // single element: packed add on the enclosing aligned word with
-            // +0 for the neighbouring element (x + 0 == x)
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                uint16_t *e = p + i;
-                const bool hi = (reinterpret_cast<uintptr_t>(e) & 2) != 0;
-                uint16_t *w = reinterpret_cast<uint16_t *>(reinterpret_cast<uintptr_t>(e) & ~uintptr_t(3));
-                const float v = coef * g[i];
-                atomic_add_pk(DT{}, w, hi ? 0.0f : v, hi ? v : 0.0f);
-            }
-        }
-    }
-};
-
 // ------------------------------------------------------------ utilities
 
 // Logical tile for this workgroup; the grid has kXcds * per_xcd workgroups and
@@ -247,15 +303,24 @@ __device__ __forceinline__ Cell map_cell(float loc_x, float loc_y, float Hf, flo
 }
 
 // ------------------------------------------------------------- forward
+//
+// A lane group handles the points p = i * split + s (i = 0, 1, ...) of its
+// query; split divides K, so the level of the i-th point, (i * split) / K, is
+// the same for every lane of the wave and the level table is read with
+// scalar loads. Points are taken CH at a time: the locations and weights of
+// the chunk are loaded first, then all 4 * CH corner gathers are issued, and
+// only then consumed, so a wave waits for two memory round trips per chunk
+// instead of two per point.
 
-template <class DT, int VEC>
-__global__ __launch_bounds__(kBlock) void msda_fwd_kernel(
+template <class DT, int VEC, int CH, bool BUF>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void msda_fwd_kernel(
     const typename DT::S *__restrict__ value, const typename DT::S *__restrict__ loc,
     const typename DT::S *__restrict__ attn, typename DT::S *__restrict__ out,
     const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
     const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
     const int log2s) {
     using E = typename DT::S;
+    using R = typename RawVec<VEC * (int)sizeof(E)>::type;
     const int64_t tile = logical_block();
     if (tile >= ntiles) return;  // whole workgroup leaves together
     const int64_t bm = tile / qblocks;
@@ -273,45 +338,82 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(
     const bool live = q_ok && (c0 < D);
     const int split = 1 << log2s;
     const int LK = L * K;
+    const int per_lane = LK >> log2s;
 
-    const int64_t pq = (b * Q + (q_ok ? q : 0)) * M + m;
+    const int64_t pq = (b * Q + (q_ok ? q : 0)) * M + m;  // clamped: always a valid query
     const E *loc_q = loc + pq * LK * 2;
     const E *attn_q = attn + pq * LK;
     const int64_t MD = (int64_t)M * D;
-    const E *val = value + b * S * MD + (int64_t)m * D + (c0 < D ? c0 : 0);
+    const int64_t row_bytes = MD * (int64_t)sizeof(E);
+    const Slice<BUF> slice(value + b * S * MD, S * row_bytes);
+    const int64_t lane_bytes = ((int64_t)m * D + (c0 < D ? c0 : 0)) * (int64_t)sizeof(E);
 
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
 
-    for (int l = 0; l < L; ++l) {
-        const int H = lt.H[l], W = lt.W[l];
-        const int64_t start = lt.start[l];
-        const float Hf = (float)H, Wf = (float)W;
-#pragma unroll 4
-        for (int k = s; k < K; k += split) {
-            const int p = l * K + k;
-            float lx = 0.0f, ly = 0.0f, a = 0.0f;
-            if (q_ok) {
-                load_xy<DT>(loc_q + 2 * p, lx, ly);
-                a = to_f32(DT{}, attn_q[p]);
-            }
-            const Cell cl = map_cell(lx, ly, Hf, Wf, W, start);
-            const E *p00 = val + cl.row00 * MD;
-            const E *p10 = p00 + (int64_t)W * MD;
-            float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
+    for (int i0 = 0; i0 < per_lane; i0 += CH) {
+        uint32_t bx[CH], by[CH], ba[CH];
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) v00[i] = v01[i] = v10[i] = v11[i] = 0.0f;
-            if (live && cl.v00) load_vec<DT, VEC>(p00, v00);
-            if (live && cl.v01) load_vec<DT, VEC>(p00 + MD, v01);
-            if (live && cl.v10) load_vec<DT, VEC>(p10, v10);
-            if (live && cl.v11) load_vec<DT, VEC>(p10 + MD, v11);
+        for (int t = 0; t < CH; ++t) {
+            const int p = (i0 + t < per_lane ? i0 + t : 0) * split + s;
+            bx[t] = load_bits<DT>(loc_q + 2 * p);
+            by[t] = load_bits<DT>(loc_q + 2 * p + 1);
+            ba[t] = load_bits<DT>(attn_q + p);
+        }
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            pin(bx[t]);
+            pin(by[t]);
+            pin(ba[t]);
+        }
+        float lx[CH], ly[CH], aw[CH];
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            lx[t] = bits_to_f32<DT>(bx[t]);
+            ly[t] = bits_to_f32<DT>(by[t]);
+            aw[t] = (q_ok && i0 + t < per_lane) ? bits_to_f32<DT>(ba[t]) : 0.0f;
+        }
+        int64_t off[CH][4];
+        bool ok[CH][4];
+        float w[CH][4];
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            const bool t_live = live && (i0 + t < per_lane);
+            int l = ((i0 + t) * split) / K;
+            l = l < L ? l : L - 1;
+            const int H = lt.H[l], W = lt.W[l];
+            const Cell cl = map_cell(lx[t], ly[t], (float)H, (float)W, W, lt.start[l]);
+            off[t][0] = cl.row00 * row_bytes + lane_bytes;
+            off[t][1] = off[t][0] + row_bytes;
+            off[t][2] = off[t][0] + (int64_t)W * row_bytes;
+            off[t][3] = off[t][2] + row_bytes;
+            ok[t][0] = t_live && cl.v00;
+            ok[t][1] = t_live && cl.v01;
+            ok[t][2] = t_live && cl.v10;
+            ok[t][3] = t_live && cl.v11;
             const float gx = 1.0f - cl.fx, gy = 1.0f - cl.fy;
-            const float w00 = a * (gx * gy), w01 = a * (cl.fx * gy);
-            const float w10 = a * (gx * cl.fy), w11 = a * (cl.fx * cl.fy);
+            w[t][0] = aw[t] * (gx * gy);
+            w[t][1] = aw[t] * (cl.fx * gy);
+            w[t][2] = aw[t] * (gx * cl.fy);
+            w[t][3] = aw[t] * (cl.fx * cl.fy);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        R raw[CH][4];
 #pragma unroll
-            for (int i = 0; i < VEC; ++i)
-                acc[i] += w00 * v00[i] + w01 * v01[i] + w10 * v10[i] + w11 * v11[i];
+        for (int t = 0; t < CH; ++t)
+#pragma unroll
+            for (int cn = 0; cn < 4; ++cn) raw[t][cn] = slice.template gather<R>(off[t][cn], ok[t][cn]);
+        __builtin_amdgcn_sched_barrier(0);  // all 4 * CH gathers in flight before any use
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+#pragma unroll
+            for (int cn = 0; cn < 4; ++cn) {
+                float v[VEC];
+                raw_to_f32<DT, VEC>(raw[t][cn], v);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) acc[i] += w[t][cn] * v[i];
+            }
         }
     }
     // Sum the split lane groups of one query (all lanes active here).
@@ -323,16 +425,38 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(
 }
 
 // ------------------------------------------------------------ backward
+//
+// Lane layout. MI355X's L2 executes atomics per request, one request covering
+// up to 16 dwords of one 64-byte segment; a request carrying one dword costs
+// about as much as one carrying sixteen. So the backward gives each query a
+// group of G <= 16 lanes and lane c owns the slots c, c + G, ... of a corner
+// row: one instruction of the group touches G consecutive slots, i.e. one
+// contiguous segment, for the gathers and for the atomics alike. A slot is a
+// dword of 16-bit data (two channels, packed atomics) or one fp32 channel.
+// For fp32 targets (fp32 data, or the fp32 scratch of 16-bit data) the
+// upstream gradient is also held in channel layout (channel c + iG) so that
+// every fp32 atomic instruction covers G consecutive dwords.
 
-template <class DT, int VEC, bool FP32ACC>
+// Points per chunk for the backward: about 8 slots of corner data per lane.
+template <int J>
+struct BwdChunk {
+    static constexpr int value = J >= 8 ? 1 : (J >= 3 ? 2 : 8 / J);
+};
+
+template <class DT, int SLOT, int J, bool BUF>
 __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
     const typename DT::S *__restrict__ value, const typename DT::S *__restrict__ loc,
     const typename DT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out,
-    void *__restrict__ acc_target, typename DT::S *__restrict__ grad_loc,
-    typename DT::S *__restrict__ grad_attn, const LevelTable lt, const int64_t S,
-    const int64_t Q, const int M, const int D, const int L, const int K, const int qblocks,
-    const int64_t ntiles, const int log2g, const int log2s) {
+    void *__restrict__ grad_value, float *__restrict__ workspace,
+    typename DT::S *__restrict__ grad_loc, typename DT::S *__restrict__ grad_attn,
+    const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
+    const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
+    const int log2s) {
     using E = typename DT::S;
+    using R = typename RawVec<SLOT * (int)sizeof(E)>::type;  // one slot
+    constexpr bool kF32 = sizeof(E) == 4;
+    constexpr int JC = J * SLOT;  // fp32-channel-layout registers per lane
+    constexpr int CH = BwdChunk<J>::value;
     const int64_t tile = logical_block();
     if (tile >= ntiles) return;
     const int64_t bm = tile / qblocks;
@@ -341,83 +465,171 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
     const int m = (int)(bm - b * M);
 
     const int tid = threadIdx.x;
-    const int c = tid & ((1 << log2g) - 1);
+    const int G = 1 << log2g;
+    const int c = tid & (G - 1);
     const int s = (tid >> log2g) & ((1 << log2s) - 1);
     const int qpb = kBlock >> (log2g + log2s);
     const int64_t q = (int64_t)qb * qpb + (tid >> (log2g + log2s));
     const bool q_ok = q < Q;
-    const int c0 = c * VEC;
-    const bool live = q_ok && (c0 < D);
     const int split = 1 << log2s;
     const int LK = L * K;
+    const int per_lane = LK >> log2s;
+    const int nslots = D / SLOT;
 
-    const int64_t pq = (b * Q + (q_ok ? q : 0)) * M + m;
+    const int64_t pq = (b * Q + (q_ok ? q : 0)) * M + m;  // clamped: always a valid query
     const E *loc_q = loc + pq * LK * 2;
     const E *attn_q = attn + pq * LK;
     const int64_t MD = (int64_t)M * D;
-    const int64_t col = (int64_t)m * D + (c0 < D ? c0 : 0);
-    const E *val = value + b * S * MD + col;
-    const int64_t tgt_base = b * S * MD + col;  // element offset into grad_value / scratch
+    const int64_t row_bytes = MD * (int64_t)sizeof(E);
+    const int64_t bS = b * S;
+    const Slice<BUF> slice(value + bS * MD, S * row_bytes);
+    const int64_t head_bytes = (int64_t)m * D * (int64_t)sizeof(E);
 
-    float g[VEC];
+    // the query's upstream gradient in slot layout (slot c + jG) ...
+    bool slot_ok[J];
+    float g[J][SLOT];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) g[i] = 0.0f;
-    if (live) load_vec<DT, VEC>(grad_out + pq * D + c0, g);
+    for (int j = 0; j < J; ++j) {
+        const int sl = c + j * G;
+        slot_ok[j] = q_ok && sl < nslots;
+        const R r = *reinterpret_cast<const R *>(grad_out + pq * D + (sl < nslots ? sl : 0) * SLOT);
+        raw_to_f32<DT, SLOT>(slot_ok[j] ? r : zero_raw<R>(), g[j]);
+    }
+    // ... and in channel layout (channel c + iG) for fp32 atomics
+    float gc[JC];
+    if constexpr (SLOT == 1) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) gc[j] = g[j][0];
+    } else {
+#pragma unroll
+        for (int i = 0; i < JC; ++i) {
+            const int ch = c + i * G;
+            const float v = to_f32(DT{}, grad_out[pq * D + (ch < D ? ch : 0)]);
+            gc[i] = (q_ok && ch < D) ? v : 0.0f;
+        }
+    }
 
-    for (int l = 0; l < L; ++l) {
-        const int H = lt.H[l], W = lt.W[l];
-        const int64_t start = lt.start[l];
-        const float Hf = (float)H, Wf = (float)W;
-#pragma unroll 2
-        for (int k = s; k < K; k += split) {
-            const int p = l * K + k;
-            float lx = 0.0f, ly = 0.0f, a = 0.0f;
-            if (q_ok) {
-                load_xy<DT>(loc_q + 2 * p, lx, ly);
-                a = to_f32(DT{}, attn_q[p]);
-            }
-            const Cell cl = map_cell(lx, ly, Hf, Wf, W, start);
-            const int64_t r00 = cl.row00 * MD;
-            const int64_t r10 = r00 + (int64_t)W * MD;
-            float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
+    for (int i0 = 0; i0 < per_lane; i0 += CH) {
+        float lx[CH], ly[CH], aw[CH];
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) v00[i] = v01[i] = v10[i] = v11[i] = 0.0f;
-            if (live && cl.v00) load_vec<DT, VEC>(val + r00, v00);
-            if (live && cl.v01) load_vec<DT, VEC>(val + r00 + MD, v01);
-            if (live && cl.v10) load_vec<DT, VEC>(val + r10, v10);
-            if (live && cl.v11) load_vec<DT, VEC>(val + r10 + MD, v11);
-            const float gx = 1.0f - cl.fx, gy = 1.0f - cl.fy;
-            const float w00 = gx * gy, w01 = cl.fx * gy, w10 = gx * cl.fy, w11 = cl.fx * cl.fy;
-            float ds = 0.0f, dx = 0.0f, dy = 0.0f;
+        for (int t = 0; t < CH; ++t) {
+            const bool t_ok = i0 + t < per_lane;  // uniform
+            const int p = (t_ok ? i0 + t : 0) * split + s;
+            load_xy<DT>(loc_q + 2 * p, lx[t], ly[t]);
+            const float a = to_f32(DT{}, attn_q[p]);
+            aw[t] = (q_ok && t_ok) ? a : 0.0f;
+        }
+        Cell cl[CH];
+        int lvl[CH];
+        R raw[CH][4][J];
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                const float smp = w00 * v00[i] + w01 * v01[i] + w10 * v10[i] + w11 * v11[i];
-                const float sx = gy * (v01[i] - v00[i]) + cl.fy * (v11[i] - v10[i]);
-                const float sy = gx * (v10[i] - v00[i]) + cl.fx * (v11[i] - v01[i]);
-                ds += g[i] * smp;
-                dx += g[i] * sx;
-                dy += g[i] * sy;
+        for (int t = 0; t < CH; ++t) {
+            const bool t_ok = i0 + t < per_lane;
+            int l = ((i0 + t) * split) / K;
+            l = l < L ? l : L - 1;
+            lvl[t] = l;
+            const int W = lt.W[l];
+            cl[t] = map_cell(lx[t], ly[t], (float)lt.H[l], (float)W, W, lt.start[l]);
+            if (!t_ok) cl[t].v00 = cl[t].v01 = cl[t].v10 = cl[t].v11 = false;  // uniform
+            const int64_t o00 = cl[t].row00 * row_bytes + head_bytes;
+            const int64_t o10 = o00 + (int64_t)W * row_bytes;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int64_t so = (int64_t)(c + j * G) * SLOT * (int64_t)sizeof(E);
+                raw[t][0][j] = slice.template gather<R>(o00 + so, slot_ok[j] && cl[t].v00);
+                raw[t][1][j] = slice.template gather<R>(o00 + row_bytes + so, slot_ok[j] && cl[t].v01);
+                raw[t][2][j] = slice.template gather<R>(o10 + so, slot_ok[j] && cl[t].v10);
+                raw[t][3][j] = slice.template gather<R>(o10 + row_bytes + so, slot_ok[j] && cl[t].v11);
             }
-            ds = group_sum(ds, log2g);
-            dx = group_sum(dx, log2g);
-            dy = group_sum(dy, log2g);
-            if (q_ok && c == 0) {
+        }
+        float ds[CH], dx[CH], dy[CH];
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            const float fx = cl[t].fx, fy = cl[t].fy, gx = 1.0f - fx, gy = 1.0f - fy;
+            const float w00 = gx * gy, w01 = fx * gy, w10 = gx * fy, w11 = fx * fy;
+            ds[t] = dx[t] = dy[t] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                float a00[SLOT], a01[SLOT], a10[SLOT], a11[SLOT];
+                raw_to_f32<DT, SLOT>(raw[t][0][j], a00);
+                raw_to_f32<DT, SLOT>(raw[t][1][j], a01);
+                raw_to_f32<DT, SLOT>(raw[t][2][j], a10);
+                raw_to_f32<DT, SLOT>(raw[t][3][j], a11);
+#pragma unroll
+                for (int u = 0; u < SLOT; ++u) {
+                    const float smp = w00 * a00[u] + w01 * a01[u] + w10 * a10[u] + w11 * a11[u];
+                    const float sx = gy * (a01[u] - a00[u]) + fy * (a11[u] - a10[u]);
+                    const float sy = gx * (a10[u] - a00[u]) + fx * (a11[u] - a01[u]);
+                    ds[t] += g[j][u] * smp;
+                    dx[t] += g[j][u] * sx;
+                    dy[t] += g[j][u] * sy;
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            ds[t] = group_sum(ds[t], log2g);
+            dx[t] = group_sum(dx[t], log2g);
+            dy[t] = group_sum(dy[t], log2g);
+        }
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            if (!(q_ok && i0 + t < per_lane)) continue;
+            const int l = lvl[t];
+            const int p = (i0 + t) * split + s;
+            const float fx = cl[t].fx, fy = cl[t].fy, gx = 1.0f - fx, gy = 1.0f - fy;
+            if (c == 0) {
                 const int64_t pp = pq * LK + p;
-                grad_attn[pp] = from_f32(DT{}, ds);
-                grad_loc[2 * pp] = from_f32(DT{}, Wf * a * dx);
-                grad_loc[2 * pp + 1] = from_f32(DT{}, Hf * a * dy);
+                grad_attn[pp] = from_f32(DT{}, ds[t]);
+                grad_loc[2 * pp] = from_f32(DT{}, (float)lt.W[l] * aw[t] * dx[t]);
+                grad_loc[2 * pp + 1] = from_f32(DT{}, (float)lt.H[l] * aw[t] * dy[t]);
             }
-            if (live) {
-                if (cl.v00) Scatter<DT, VEC, FP32ACC>::add(acc_target, tgt_base + r00, a * w00, g);
-                if (cl.v01) Scatter<DT, VEC, FP32ACC>::add(acc_target, tgt_base + r00 + MD, a * w01, g);
-                if (cl.v10) Scatter<DT, VEC, FP32ACC>::add(acc_target, tgt_base + r10, a * w10, g);
-                if (cl.v11) Scatter<DT, VEC, FP32ACC>::add(acc_target, tgt_base + r10 + MD, a * w11, g);
+            const int W = lt.W[l];
+            const int64_t start = lt.start[l];
+            const int64_t soff = lt.scratch_off[l];
+            const int64_t HW = (int64_t)lt.H[l] * W;
+            const bool vc[4] = {cl[t].v00, cl[t].v01, cl[t].v10, cl[t].v11};
+            const float coef[4] = {aw[t] * gx * gy, aw[t] * fx * gy, aw[t] * gx * fy, aw[t] * fx * fy};
+            const int64_t drow[4] = {0, 1, W, (int64_t)W + 1};  // pixel rows from row00
+#pragma unroll
+            for (int cn = 0; cn < 4; ++cn) {
+                if (!vc[cn]) continue;
+                const int64_t row = cl[t].row00 + drow[cn];
+                if (kF32 || soff >= 0) {
+                    float *tp = kF32 ? static_cast<float *>(grad_value) + (bS + row) * MD + (int64_t)m * D
+                                     : workspace + soff + ((b * HW + (row - start)) * M + m) * (int64_t)D;
+#pragma unroll
+                    for (int i = 0; i < JC; ++i) {
+                        const int ch = c + i * G;
+                        if (ch < D) atomic_add_f32(tp + ch, coef[cn] * gc[i]);
+                    }
+                } else if constexpr (!kF32) {
+                    uint16_t *tp = static_cast<uint16_t *>(grad_value) + (bS + row) * MD + (int64_t)m * D;
+#pragma unroll
+                    for (int j = 0; j < J; ++j) {
+                        if (!slot_ok[j]) continue;
+                        uint16_t *e = tp + (int64_t)(c + j * G) * SLOT;
+                        if constexpr (SLOT == 2) {
+                            // one dword, 4-byte aligned (host-checked)
+                            atomic_add_pk(DT{}, e, coef[cn] * g[j][0], coef[cn] * g[j][1]);
+                        } else {
+                            // single element: packed add on the enclosing aligned
+                            // word with +0 for the neighbour (x + 0 == x); the
+                            // host guarantees that word lies inside grad_value
+                            const bool hi = (reinterpret_cast<uintptr_t>(e) & 2) != 0;
+                            uint16_t *wd = reinterpret_cast<uint16_t *>(
+                                reinterpret_cast<uintptr_t>(e) & ~uintptr_t(3));
+                            const float v = coef[cn] * g[j][0];
+                            atomic_add_pk(DT{}, wd, hi ? 0.0f : v, hi ? v : 0.0f);
+                        }
+                    }
+                }
             }
         }
     }
 }
 
-// ------------------------------------------------ zero fill and downcast
+// ------------------------------------------------ zero fill and scratch add
 
 __global__ __launch_bounds__(kBlock) void zero_kernel_16(uint4 *__restrict__ dst, int64_t n16) {
     const uint4 z = {0u, 0u, 0u, 0u};
@@ -432,33 +644,37 @@ __global__ __launch_bounds__(kBlock) void zero_kernel_2(uint16_t *__restrict__ d
         dst[i] = 0;
 }
 
-template <class DT>
-__global__ __launch_bounds__(kBlock) void downcast_kernel(const float *__restrict__ src,
-                                                          typename DT::S *__restrict__ dst,
-                                                          int64_t n, int accumulate) {
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * kBlock) {
-        float v = src[i];
-        if (accumulate) v += to_f32(DT{}, dst[i]);
-        dst[i] = from_f32(DT{}, v);
-    }
-}
+// blockIdx.y = scratch level index (into lvl); the level's fp32 block
+// (B, H*W, M, D) is added into grad_value rows [start, start + H*W) of every
+// batch, 4 elements at a time (host-checked alignment and divisibility) or 1.
+struct ScratchLevels {
+    int32_t level[MSDA_MAX_LEVELS];
+    int32_t count;
+};
 
-template <class DT>
-__global__ __launch_bounds__(kBlock) void downcast_kernel_x4(const float4 *__restrict__ src,
-                                                             uint2 *__restrict__ dst, int64_t n4,
-                                                             int accumulate) {
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n4;
-         i += (int64_t)gridDim.x * kBlock) {
-        const float4 v = src[i];
-        float f[4] = {v.x, v.y, v.z, v.w};
-        if (accumulate) {
-            float o[4];
-            load_vec<DT, 4>(reinterpret_cast<const typename DT::S *>(dst + i), o);
+template <class DT, int V>
+__global__ __launch_bounds__(kBlock) void scratch_add_kernel(const float *__restrict__ ws,
+                                                             typename DT::S *__restrict__ gv,
+                                                             const LevelTable lt,
+                                                             const ScratchLevels sl,
+                                                             const int64_t B, const int64_t S,
+                                                             const int64_t MD) {
+    using E = typename DT::S;
+    const int l = sl.level[blockIdx.y];
+    const int64_t n = (int64_t)lt.H[l] * lt.W[l] * MD;  // elements per batch
+    const int64_t total = B * n;
+    const float *src = ws + lt.scratch_off[l];
+    const int64_t start = lt.start[l];
+    for (int64_t i = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * V; i < total;
+         i += (int64_t)gridDim.x * kBlock * V) {
+        const int64_t bb = i / n, off = i - bb * n;
+        E *dst = gv + (bb * S + start) * MD + off;
+        float acc[V], old[V];
+        load_vec<F32T, V>(src + i, acc);
+        load_vec<DT, V>(dst, old);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) f[j] += o[j];
-        }
-        store_vec<DT, 4>(reinterpret_cast<typename DT::S *>(dst + i), f);
+        for (int u = 0; u < V; ++u) acc[u] += old[u];
+        store_vec<DT, V>(dst, acc);
     }
 }
 
@@ -470,37 +686,62 @@ int grid_for(int64_t work_items) {
 
 // ------------------------------------------------------------ dispatch
 
+// Buffer gathers address one batch slice with 32-bit offsets.
+bool slice_fits_buffer(const Problem &p) {
+    const int64_t e = p.dtype == MSDA_F32 ? 4 : 2;
+    return p.S * p.M * p.D * e <= (int64_t)kOutOfRange - 64;
+}
+
 template <class DT, int VEC>
 hipError_t fwd_launch(const Problem &p, const Mapping &mp, const void *value, const void *loc,
                       const void *attn, void *out, hipStream_t stream) {
+    // 4 points per chunk; 16-byte gathers keep 16 x 4 VGPRs of raw data in flight
+    constexpr int CH = 4;
     using E = typename DT::S;
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
     const int qblocks = (int)((p.Q + qpb - 1) / qpb);
     const int64_t ntiles = p.B * p.M * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((msda_fwd_kernel<DT, VEC>), dim3((unsigned)(per_xcd * kXcds)),
-                       dim3(kBlock), 0, stream, static_cast<const E *>(value),
-                       static_cast<const E *>(loc), static_cast<const E *>(attn),
-                       static_cast<E *>(out), p.levels, p.S, p.Q, (int)p.M, (int)p.D, (int)p.L,
-                       (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
+    if (slice_fits_buffer(p))
+        hipLaunchKernelGGL((msda_fwd_kernel<DT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
+                           dim3(kBlock), 0, stream, static_cast<const E *>(value),
+                           static_cast<const E *>(loc), static_cast<const E *>(attn),
+                           static_cast<E *>(out), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
+                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
+    else
+        hipLaunchKernelGGL((msda_fwd_kernel<DT, VEC, CH, false>), dim3((unsigned)(per_xcd * kXcds)),
+                           dim3(kBlock), 0, stream, static_cast<const E *>(value),
+                           static_cast<const E *>(loc), static_cast<const E *>(attn),
+                           static_cast<E *>(out), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
+                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
     return hipGetLastError();
 }
 
-template <class DT, int VEC, bool FP32ACC>
-hipError_t bwd_launch(const Problem &p, const Mapping &mp, const void *value, const void *loc,
-                      const void *attn, const void *grad_out, void *acc_target, void *grad_loc,
-                      void *grad_attn, hipStream_t stream) {
+template <class DT, int SLOT, int J>
+hipError_t bwd_launch(const Problem &p, const BwdMapping &mp, const void *value, const void *loc,
+                      const void *attn, const void *grad_out, void *grad_value, float *workspace,
+                      void *grad_loc, void *grad_attn, hipStream_t stream) {
     using E = typename DT::S;
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
     const int qblocks = (int)((p.Q + qpb - 1) / qpb);
     const int64_t ntiles = p.B * p.M * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((msda_bwd_kernel<DT, VEC, FP32ACC>), dim3((unsigned)(per_xcd * kXcds)),
-                       dim3(kBlock), 0, stream, static_cast<const E *>(value),
-                       static_cast<const E *>(loc), static_cast<const E *>(attn),
-                       static_cast<const E *>(grad_out), acc_target, static_cast<E *>(grad_loc),
-                       static_cast<E *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
-                       (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
+    if (slice_fits_buffer(p))
+        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, true>), dim3((unsigned)(per_xcd * kXcds)),
+                           dim3(kBlock), 0, stream, static_cast<const E *>(value),
+                           static_cast<const E *>(loc), static_cast<const E *>(attn),
+                           static_cast<const E *>(grad_out), grad_value, workspace,
+                           static_cast<E *>(grad_loc), static_cast<E *>(grad_attn), p.levels, p.S,
+                           p.Q, (int)p.M, (int)p.D, (int)p.L, (int)p.K, qblocks, ntiles,
+                           mp.log2_group, mp.log2_split);
+    else
+        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, false>), dim3((unsigned)(per_xcd * kXcds)),
+                           dim3(kBlock), 0, stream, static_cast<const E *>(value),
+                           static_cast<const E *>(loc), static_cast<const E *>(attn),
+                           static_cast<const E *>(grad_out), grad_value, workspace,
+                           static_cast<E *>(grad_loc), static_cast<E *>(grad_attn), p.levels, p.S,
+                           p.Q, (int)p.M, (int)p.D, (int)p.L, (int)p.K, qblocks, ntiles,
+                           mp.log2_group, mp.log2_split);
     return hipGetLastError();
 }
 
@@ -521,22 +762,73 @@ hipError_t fwd_by_vec(const Problem &p, const Mapping &mp, const void *v, const 
     return hipErrorInvalidValue;
 }
 
-template <class DT, bool FP32ACC>
-hipError_t bwd_by_vec(const Problem &p, const Mapping &mp, const void *v, const void *l,
-                      const void *a, const void *go, void *t, void *gl, void *ga,
-                      hipStream_t st) {
-    switch (mp.vec) {
-        case 1: return bwd_launch<DT, 1, FP32ACC>(p, mp, v, l, a, go, t, gl, ga, st);
-        case 2: return bwd_launch<DT, 2, FP32ACC>(p, mp, v, l, a, go, t, gl, ga, st);
-        case 4: return bwd_launch<DT, 4, FP32ACC>(p, mp, v, l, a, go, t, gl, ga, st);
+template <class DT, int SLOT>
+hipError_t bwd_by_j(const Problem &p, const BwdMapping &mp, const void *v, const void *l,
+                    const void *a, const void *go, void *gv, float *ws, void *gl, void *ga,
+                    hipStream_t st) {
+    switch (mp.j) {
+        case 1: return bwd_launch<DT, SLOT, 1>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 2: return bwd_launch<DT, SLOT, 2>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 3: return bwd_launch<DT, SLOT, 3>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 4: return bwd_launch<DT, SLOT, 4>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 8: return bwd_launch<DT, SLOT, 8>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 16: return bwd_launch<DT, SLOT, 16>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
         default: break;
     }
-    if constexpr (sizeof(typename DT::S) == 4) {
-        if (mp.vec == 3) return bwd_launch<DT, 3, FP32ACC>(p, mp, v, l, a, go, t, gl, ga, st);
-    } else {
-        if (mp.vec == 8) return bwd_launch<DT, 8, FP32ACC>(p, mp, v, l, a, go, t, gl, ga, st);
+    if constexpr (SLOT == 1) {
+        if (mp.j == 32) return bwd_launch<DT, SLOT, 32>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
     }
     return hipErrorInvalidValue;
+}
+
+template <class DT>
+hipError_t scratch_add(const Problem &p, const float *ws, void *gv, hipStream_t stream) {
+    using E = typename DT::S;
+    ScratchLevels sl;
+    sl.count = 0;
+    int64_t largest = 0;
+    for (int l = 0; l < (int)p.L; ++l) {
+        if (p.levels.scratch_off[l] < 0) continue;
+        sl.level[sl.count++] = l;
+        const int64_t n = p.B * (int64_t)p.levels.H[l] * p.levels.W[l] * p.M * p.D;
+        if (n > largest) largest = n;
+    }
+    if (sl.count == 0) return hipSuccess;
+    // Levels whose row ranges overlap (a caller-given level_start_index) would
+    // read-modify-write the same grad_value rows from concurrent workgroups:
+    // then add one level per launch, in stream order.
+    bool overlap = false;
+    for (int i = 0; i < sl.count && !overlap; ++i)
+        for (int k = i + 1; k < sl.count && !overlap; ++k) {
+            const int a = sl.level[i], b = sl.level[k];
+            const int64_t a0 = p.levels.start[a], a1 = a0 + (int64_t)p.levels.H[a] * p.levels.W[a];
+            const int64_t b0 = p.levels.start[b], b1 = b0 + (int64_t)p.levels.H[b] * p.levels.W[b];
+            overlap = a0 < b1 && b0 < a1;
+        }
+    if (overlap && sl.count > 1) {
+        for (int i = 0; i < sl.count; ++i) {
+            Problem one = p;
+            for (int l = 0; l < (int)p.L; ++l)
+                if (l != sl.level[i]) one.levels.scratch_off[l] = -1;
+            const hipError_t err = scratch_add<DT>(one, ws, gv, stream);
+            if (err != hipSuccess) return err;
+        }
+        return hipSuccess;
+    }
+    const int64_t MD = p.M * p.D;
+    // 4-wide when a batch block never splits a group of 4 and both sides are aligned
+    const bool v4 = MD % 4 == 0 && reinterpret_cast<uintptr_t>(gv) % 8 == 0 &&
+                    reinterpret_cast<uintptr_t>(ws) % 16 == 0;
+    if (v4) {
+        hipLaunchKernelGGL((scratch_add_kernel<DT, 4>), dim3(grid_for(largest / 4), sl.count),
+                           dim3(kBlock), 0, stream, ws, static_cast<E *>(gv), p.levels, sl, p.B,
+                           p.S, MD);
+    } else {
+        hipLaunchKernelGGL((scratch_add_kernel<DT, 1>), dim3(grid_for(largest), sl.count),
+                           dim3(kBlock), 0, stream, ws, static_cast<E *>(gv), p.levels, sl, p.B,
+                           p.S, MD);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -551,24 +843,24 @@ hipError_t launch_forward(const Problem &p, const Mapping &mp, const void *value
     }
 }
 
-hipError_t launch_backward(const Problem &p, const Mapping &mp, const void *value,
+hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *value,
                            const void *loc, const void *attn, const void *grad_out,
-                           void *acc_target, bool accum_fp32, void *grad_loc, void *grad_attn,
+                           void *grad_value, float *workspace, void *grad_loc, void *grad_attn,
                            hipStream_t stream) {
     switch (p.dtype) {
         case MSDA_F32:
-            return bwd_by_vec<F32T, true>(p, mp, value, loc, attn, grad_out, acc_target, grad_loc,
-                                          grad_attn, stream);
+            return bwd_by_j<F32T, 1>(p, mp, value, loc, attn, grad_out, grad_value, workspace,
+                                     grad_loc, grad_attn, stream);
         case MSDA_F16:
-            return accum_fp32 ? bwd_by_vec<F16T, true>(p, mp, value, loc, attn, grad_out,
-                                                       acc_target, grad_loc, grad_attn, stream)
-                              : bwd_by_vec<F16T, false>(p, mp, value, loc, attn, grad_out,
-                                                        acc_target, grad_loc, grad_attn, stream);
+            return mp.slot == 2 ? bwd_by_j<F16T, 2>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                    workspace, grad_loc, grad_attn, stream)
+                                : bwd_by_j<F16T, 1>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                    workspace, grad_loc, grad_attn, stream);
         case MSDA_BF16:
-            return accum_fp32 ? bwd_by_vec<BF16T, true>(p, mp, value, loc, attn, grad_out,
-                                                        acc_target, grad_loc, grad_attn, stream)
-                              : bwd_by_vec<BF16T, false>(p, mp, value, loc, attn, grad_out,
-                                                         acc_target, grad_loc, grad_attn, stream);
+            return mp.slot == 2 ? bwd_by_j<BF16T, 2>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                     workspace, grad_loc, grad_attn, stream)
+                                : bwd_by_j<BF16T, 1>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                     workspace, grad_loc, grad_attn, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -587,31 +879,13 @@ hipError_t launch_zero(void *dst, size_t bytes, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_downcast(int dtype, const float *scratch, void *grad_value, int64_t n,
-                           bool accumulate, hipStream_t stream) {
-    if (n == 0) return hipSuccess;
-    const bool x4 = (n % 4 == 0) && (reinterpret_cast<uintptr_t>(scratch) % 16 == 0) &&
-                    (reinterpret_cast<uintptr_t>(grad_value) % 8 == 0);
-    if (dtype == MSDA_F16) {
-        if (x4)
-            hipLaunchKernelGGL(downcast_kernel_x4<F16T>, dim3(grid_for(n / 4)), dim3(kBlock), 0,
-                               stream, reinterpret_cast<const float4 *>(scratch),
-                               static_cast<uint2 *>(grad_value), n / 4, (int)accumulate);
-        else
-            hipLaunchKernelGGL(downcast_kernel<F16T>, dim3(grid_for(n)), dim3(kBlock), 0, stream,
-                               scratch, static_cast<uint16_t *>(grad_value), n, (int)accumulate);
-    } else if (dtype == MSDA_BF16) {
-        if (x4)
-            hipLaunchKernelGGL(downcast_kernel_x4<BF16T>, dim3(grid_for(n / 4)), dim3(kBlock), 0,
-                               stream, reinterpret_cast<const float4 *>(scratch),
-                               static_cast<uint2 *>(grad_value), n / 4, (int)accumulate);
-        else
-            hipLaunchKernelGGL(downcast_kernel<BF16T>, dim3(grid_for(n)), dim3(kBlock), 0, stream,
-                               scratch, static_cast<uint16_t *>(grad_value), n, (int)accumulate);
-    } else {
-        return hipErrorInvalidValue;
+hipError_t launch_scratch_add(const Problem &p, const float *workspace, void *grad_value,
+                              hipStream_t stream) {
+    switch (p.dtype) {
+        case MSDA_F16: return scratch_add<F16T>(p, workspace, grad_value, stream);
+        case MSDA_BF16: return scratch_add<BF16T>(p, workspace, grad_value, stream);
+        default: return hipSuccess;  // fp32 data never uses scratch
     }
-    return hipGetLastError();
 }
 
 }  // namespace msda

@@ -11,24 +11,40 @@ namespace msda {
 
 // Level table passed by value in the kernel arguments (no device copy, no
 // host synchronisation). H, W < 2^24 so that they are exact in fp32.
+// scratch_off[l] >= 0: the backward accumulates level l's grad_value rows in
+// fp32 at workspace + scratch_off[l] (elements), laid out (B, H*W, M, D);
+// -1: atomics of the value dtype go straight into grad_value.
 struct LevelTable {
     int32_t H[MSDA_MAX_LEVELS];
     int32_t W[MSDA_MAX_LEVELS];
     int64_t start[MSDA_MAX_LEVELS];
+    int64_t scratch_off[MSDA_MAX_LEVELS];
 };
 
 // Everything a launch needs, validated by the host layer.
 struct Problem {
-    int dtype;          // msda_dtype_t
+    int dtype;  // msda_dtype_t
     int64_t B, S, M, D, L, Q, K;
     LevelTable levels;
 };
 
-// Lane mapping chosen on the host: each query's channels are spread over
-// G = 2^log2_group lanes holding `vec` consecutive channels each; 2^log2_split
-// lane groups share one query and split its L*K points between them.
+// Forward lane mapping: each query's channels are spread over
+// G = 2^log2_group lanes holding `vec` consecutive channels each (16-byte
+// gathers where the pointers allow); 2^log2_split lane groups share one
+// query and split its L*K points.
 struct Mapping {
     int vec;
+    int log2_group;
+    int log2_split;
+};
+
+// Backward lane mapping: G = 2^log2_group lanes per query (at most 16, so one
+// instruction of the group covers one 64-byte segment); lane c owns the
+// "slots" c, c + G, ..., c + (J-1) G of the corner row, a slot being `slot`
+// channels (2 = one dword of 16-bit data, else 1).
+struct BwdMapping {
+    int slot;
+    int j;
     int log2_group;
     int log2_split;
 };
@@ -37,19 +53,20 @@ hipError_t launch_forward(const Problem &p, const Mapping &mp, const void *value
                           const void *loc, const void *attn, void *out,
                           hipStream_t stream);
 
-// accum_fp32: atomics go to `acc_target` as fp32 (the scratch buffer, or
-// grad_value itself for fp32 data); otherwise packed atomics of the value
-// dtype go straight into grad_value.
-hipError_t launch_backward(const Problem &p, const Mapping &mp, const void *value,
+// Scatter kernel: writes grad_loc / grad_attn, adds into grad_value (levels
+// with scratch_off < 0; fp32 adds for fp32 data, packed adds for 16-bit data)
+// and into the fp32 workspace (levels with scratch_off >= 0).
+hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *value,
                            const void *loc, const void *attn, const void *grad_out,
-                           void *acc_target, bool accum_fp32, void *grad_loc,
-                           void *grad_attn, hipStream_t stream);
+                           void *grad_value, float *workspace, void *grad_loc, void *grad_attn,
+                           hipStream_t stream);
 
 // Fill `bytes` bytes (a multiple of 2) at `dst` with zeros.
 hipError_t launch_zero(void *dst, size_t bytes, hipStream_t stream);
 
-// grad_value[i] = (dtype) scratch[i], or += with `accumulate`, for n elements.
-hipError_t launch_downcast(int dtype, const float *scratch, void *grad_value, int64_t n,
-                           bool accumulate, hipStream_t stream);
+// For every level with scratch_off >= 0 and every batch:
+// grad_value rows of that level += (dtype) workspace block.
+hipError_t launch_scratch_add(const Problem &p, const float *workspace, void *grad_value,
+                              hipStream_t stream);
 
 }  // namespace msda

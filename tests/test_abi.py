@@ -105,7 +105,7 @@ def test_forward_given_start_index_may_differ_from_prefix(lib):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(accum=2), 4),
-    (dict(flags=2), 2),
+    (dict(flags=8), 2),
     (dict(gv=None), 1),
     (dict(gout=None), 1),
     (dict(dtype=2, accum=1), 6),  # scratch needed, no workspace
@@ -130,7 +130,11 @@ def test_workspace_size_and_accum_resolution(lib):
     assert lib.msda_backward_resolve_accum(0, *prob, -1) == 0
     assert lib.msda_backward_resolve_accum(2, *prob, 0) == 0
     assert lib.msda_backward_resolve_accum(2, *prob, 1) == 1
-    assert lib.msda_backward_resolve_accum(2, *prob, -1) in (0, 1)
+    # bf16 AUTO: per level by contributions per pixel Q*K*4/(H*W):
+    # (8,10): 16*2*4/80 = 1.6 -> native; (4,5): 128/20 = 6.4 -> scratch
+    assert lib.msda_backward_resolve_accum(2, *prob, -1) == 2
+    assert lib.msda_backward_workspace_size(2, *prob, -1) == 1 * 20 * 2 * 8 * 4
+    assert lib.msda_backward_resolve_accum(1, *prob, -1) == 0  # fp16: native
     assert lib.msda_backward_resolve_accum(2, *prob, 7) == -1
     assert lib.msda_backward_workspace_size(9, *prob, 1) == 0 and lib.msda_last_error()
 
