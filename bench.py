@@ -169,6 +169,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup + timed steps only (for rocprofv3 runs)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="with --profile-only: also run 5 plain device copies of this many MiB "
+                         "(reference dispatches for scaling FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -225,6 +228,15 @@ def main():
     log(f"timed {K} steps: {us_step:.2f} us/step (fwd {fwd_us:.2f}, bwd {bwd_us:.2f}, "
         f"host enqueue {host_us:.2f} us/step)")
     if args.profile_only:
+        if args.calib_copy_mb:
+            n = args.calib_copy_mb * (1 << 20) // 4
+            src = torch.ones(n, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(5):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"calibration: 5 copies of {args.calib_copy_mb} MiB (read {args.calib_copy_mb} MiB, "
+                f"write {args.calib_copy_mb} MiB each)")
         return
 
     # Per-kernel device time, host overhead removed by graph replay.
