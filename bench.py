@@ -5,24 +5,32 @@ One step = one forward call and one backward call of the C ABI on the
 resident, seeded synthetic inputs of a workload (default: the decoder-shaped
 bf16 workload, B=4 Q=300 M=8 D=32 L=4 K=4, levels of an 800x1333 image). The
 backward runs with the library's default accumulation (AUTO) and includes
-every stage: zero-fill, the scatter kernel and the fp32->dtype pass when the
-scratch path is taken.
+every kernel it launches.
+
+Timed region: the step is captured once in a HIP graph and replayed K times
+between two events (host dispatch removed, as with the pages' CUDA-graph
+cross-check); an eager run of the same steps is reported beside it. Per-kernel
+device times come from an instrumented eager pass: the library records a HIP
+event right before and right after each of its launches on the call's stream.
 
 Prints one JSON line:
   value / ms_per_step   microseconds per forward+backward step (lower is better)
-  fwd_us, bwd_us        per-call device time from HIP events in the timed region
+  kernels               per-kernel average device time and algorithmic GB/s
   roofline              the dominant kernel against the 8 TB/s HBM roofline:
                         algorithmic bytes per launch / average launch duration
   cpu_baseline          the CPU oracle (fp64 loops, OpenMP) on the same workload
 
 Algorithmic bytes per launch (e = element size, P = B*Q*M*L*K points,
-U = distinct (b, row, m) value rows with at least one in-bounds corner):
-  forward       3*P*e (locations + weights) + B*Q*M*D*e (output) + U*D*e
-  scatter       3*P*e (params) + B*Q*M*D*e (grad_output) + U*D*e (value)
-                + 2*U*D*e_acc (read-modify-write of touched grad rows; e_acc = 4
-                  for rows of levels accumulated in fp32 scratch)
-                + 3*P*e (grad locations + grad weights)
-  zero fill     B*S*M*D*e (+ scratch rows * 4);  scratch add  rows * D * (4 + 2e)
+U = distinct (b, row, m) value rows with at least one in-bounds corner,
+C = in-bounds corners, N = B*S*M*D grad_value elements):
+  forward          3*P*e (locations + weights) + B*Q*M*D*e (output) + U*D*e
+  backward kernel  3*P*e (params) + B*Q*M*D*e (grad_output) + U*D*e (value)
+                   + 3*P*e (grad locations + grad weights)
+                   + binned: 8*C (records written)
+                   + atomics: 2*U*D*e_acc (read-modify-write of touched rows;
+                     e_acc = 4 for rows of levels accumulated in fp32 scratch)
+  bin count        2*P*e;  bin accumulate  8*C + B*Q*M*D*e + N*e
+  zero fill        bytes written;  scratch add  rows * D * (4 + 2e)
 """
 
 from __future__ import annotations
@@ -54,16 +62,18 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def touched_rows(inp, only_levels=None) -> int:
-    """U: distinct (b, row, m) value rows that at least one in-bounds corner
-    lands on. Host-side accounting of compulsory bytes (single-rounding
-    pixel mapping as in the kernels; products of an fp32 location and an
-    integer width are exact in fp64)."""
+def touched_rows(inp, only_levels=None):
+    """(U, C): distinct (b, row, m) value rows that at least one in-bounds
+    corner lands on, and the number of in-bounds corners. Host-side
+    accounting of compulsory bytes (single-rounding pixel mapping as in the
+    kernels; products of an fp32 location and an integer width are exact in
+    fp64)."""
     value = inp["value"]
     B, S, M, D = value.shape
     loc = inp["sampling_locations"].to(torch.float64).numpy()
     shapes = inp["spatial_shapes"].tolist()
     mark = np.zeros(B * S * M, dtype=bool)
+    corners = 0
     b_idx = np.arange(B).reshape(B, 1, 1, 1)
     m_idx = np.arange(M).reshape(1, 1, M, 1)
     start = 0
@@ -82,8 +92,9 @@ def touched_rows(inp, only_levels=None) -> int:
                 row = start + yy * W + xx
                 key = (b_idx * S + row) * M + m_idx
                 mark[key[ok]] = True
+                corners += int(ok.sum())
         start += H * W
-    return int(mark.sum())
+    return int(mark.sum()), corners
 
 
 def kernel_source_hash() -> str:
@@ -164,7 +175,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decoder_bf16")
-    ap.add_argument("--accum", default="auto", choices=["auto", "native", "fp32_scratch"])
+    ap.add_argument("--accum", default="auto",
+                    choices=["auto", "native", "fp32_scratch", "per_level", "binned"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-only", action="store_true",
@@ -204,30 +216,12 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
-
-    K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    h0 = time.perf_counter()
-    e_start.record()
-    for i in range(K):
-        ev[i][0].record()
-        call.forward()
-        ev[i][1].record()
-        call.backward()
-        ev[i][2].record()
-    e_end.record()
-    h1 = time.perf_counter()
-    torch.cuda.synchronize()
-    total_ms = e_start.elapsed_time(e_end)
-    us_step = total_ms * 1e3 / K
-    fwd_us = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])) * 1e3
-    bwd_us = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])) * 1e3
-    host_us = (h1 - h0) * 1e6 / K
-    log(f"timed {K} steps: {us_step:.2f} us/step (fwd {fwd_us:.2f}, bwd {bwd_us:.2f}, "
-        f"host enqueue {host_us:.2f} us/step)")
     if args.profile_only:
+        K = args.steps
+        for _ in range(K):
+            step()
+        torch.cuda.synchronize()
+        log(f"ran {K} eager steps")
         if args.calib_copy_mb:
             n = args.calib_copy_mb * (1 << 20) // 4
             src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -239,47 +233,114 @@ def main():
                 f"write {args.calib_copy_mb} MiB each)")
         return
 
-    # Per-kernel device time, host overhead removed by graph replay.
-    reps, inner = 20, 20
-    fwd_kernel_us = time_graph(call.forward, reps, inner)
-    # the scatter kernel alone, as the default accumulation runs it: add into
-    # grad_value and keep adding into the scratch levels (no fill, no final add)
-    from scale_deformable_attention_amd._binding import FLAG_CONTINUE_SCRATCH, FLAG_DEFER_SCRATCH
-    call.backward()
-    scatter_us = time_graph(lambda: call.backward(
-        accumulate=True, flags=FLAG_CONTINUE_SCRATCH | FLAG_DEFER_SCRATCH), reps, inner)
-    scatter_native_us = time_graph(lambda: call.backward(accumulate=True, accum="native"), reps,
-                                   inner)
-    graph_step_us = time_graph(step, reps, 5)
-    log(f"graph replay: forward kernel {fwd_kernel_us:.2f} us, scatter kernel ({call.resolved_accum}) "
-        f"{scatter_us:.2f} us, all-native scatter kernel {scatter_native_us:.2f} us, "
-        f"full step {graph_step_us:.2f} us")
+    K = args.steps
+    # Timed region: K replays of one captured step.
+    graph_ok = True
+    try:
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            step()
+        torch.cuda.current_stream().wait_stream(s_cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+    except Exception as exc:  # fall back to eager stepping
+        graph_ok = False
+        log(f"graph capture failed ({exc}); timing eager steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        if graph_ok:
+            graph.replay()
+        else:
+            step()
+    e1.record()
+    torch.cuda.synchronize()
+    us_step = e0.elapsed_time(e1) * 1e3 / K
+    # Eager steps, for context.
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    h1 = time.perf_counter()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / K
+    host_us = (h1 - h0) * 1e6 / K
+    log(f"timed {K} steps: {us_step:.2f} us/step ({'graph replay' if graph_ok else 'eager'}); "
+        f"eager {eager_us:.2f} us/step, host enqueue {host_us:.2f} us/step")
 
-    # Algorithmic bytes.
+    # Per-kernel device times: events right before / after each launch.
+    from scale_deformable_attention_amd._binding import launch_events_recorded, set_launch_events
+    n_inst = min(K, 50)
+    nev = 16
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + nev)] for _ in range(n_inst)]
+    for row in evs:
+        for ev in row:
+            ev.record()
+    torch.cuda.synchronize()
+    n_bwd = None
+    for i in range(n_inst):
+        set_launch_events(evs[i][:2])
+        call.forward()
+        set_launch_events(evs[i][2:])
+        call.backward()
+        n_bwd = launch_events_recorded() // 2
+    torch.cuda.synchronize()
+    bwd_names = {
+        "binned": ["bin_zero", "bin_count", "bin_scan", "msda_bwd_kernel", "bin_accum_kernel"],
+        "native": ["zero_fill", "msda_bwd_kernel"],
+        "per_level": ["zero_fill", "scratch_zero", "msda_bwd_kernel", "scratch_add_kernel"],
+        "fp32_scratch": ["zero_fill", "scratch_zero", "msda_bwd_kernel", "scratch_add_kernel"],
+    }[call.resolved_accum]
+    if n_bwd == len(bwd_names) + 1:  # binned with padding rows: grad_value fill first
+        bwd_names = ["zero_fill"] + bwd_names
+    assert n_bwd == len(bwd_names), (n_bwd, bwd_names)
+    ktimes = {"msda_fwd_kernel": float(np.mean([evs[i][0].elapsed_time(evs[i][1])
+                                                 for i in range(n_inst)])) * 1e3}
+    for j, nm in enumerate(bwd_names):
+        ktimes[nm] = float(np.mean([evs[i][2 + 2 * j].elapsed_time(evs[i][3 + 2 * j])
+                                    for i in range(n_inst)])) * 1e3
+    log("kernels (us): " + ", ".join(f"{k} {v:.2f}" for k, v in ktimes.items()))
+
+    # Algorithmic bytes per launch.
     e = torch.finfo(wl.dtype).bits // 8
     B, S, M, D, L, Kp, Q = wl.B, wl.S, wl.M, wl.D, wl.L, wl.K, wl.num_queries
     P = B * Q * M * L * Kp
-    U = touched_rows(inp)
-    U_scr = touched_rows(inp, only_levels=call.scratch_levels()) if call.scratch_levels() else 0
-    fwd_bytes = 3 * P * e + B * Q * M * D * e + U * D * e
-    # grad rows: read + write once each, 2 bytes per element in bf16/fp16 levels
-    # and 4 in fp32 ones (fp32 data, or the scratch levels of 16-bit data)
-    grad_rows = 2 * ((U - U_scr) * D * e + U_scr * D * 4)
-    scatter_bytes = 3 * P * e + B * Q * M * D * e + U * D * e + grad_rows + 3 * P * e
-    fwd_gbps = fwd_bytes / (fwd_kernel_us * 1e-6) / 1e9
-    scatter_gbps = scatter_bytes / (scatter_us * 1e-6) / 1e9
-    # Dominant kernel: the longer of the two hot kernels.
-    src_hash = kernel_source_hash()
-    if scatter_us >= fwd_kernel_us:
-        kname, kus, kbytes = "msda_bwd_kernel", scatter_us, scatter_bytes
+    N = B * S * M * D
+    U, C = touched_rows(inp)
+    scr_levels = call.scratch_levels()
+    U_scr = touched_rows(inp, only_levels=scr_levels)[0] if scr_levels else 0
+    scratch_rows = sum(B * h * w * M for l, (h, w) in enumerate(wl.levels) if l in scr_levels)
+    common = 3 * P * e + B * Q * M * D * e + U * D * e + 3 * P * e
+    kbytes = {"msda_fwd_kernel": 3 * P * e + B * Q * M * D * e + U * D * e,
+              "bin_count": 2 * P * e, "bin_accum_kernel": 8 * C + B * Q * M * D * e + N * e,
+              "zero_fill": N * e, "scratch_zero": scratch_rows * D * 4,
+              "scratch_add_kernel": scratch_rows * D * (4 + 2 * e)}
+    if call.resolved_accum == "binned":
+        nb = call.bin_count()
+        kbytes.update({"bin_zero": (nb + 1) * 4, "bin_scan": 3 * nb * 4,
+                       "msda_bwd_kernel": common + 8 * C})
     else:
-        kname, kus, kbytes = "msda_fwd_kernel", fwd_kernel_us, fwd_bytes
-    achieved = kbytes / (kus * 1e-6) / 1e9
+        e_acc = 4 if wl.dtype == torch.float32 else e
+        kbytes["msda_bwd_kernel"] = common + 2 * ((U - U_scr) * D * e_acc + U_scr * D * 4)
+    kernels = {k: {"us": round(v, 3), "bytes": int(kbytes[k]),
+                   "GBps": round(kbytes[k] / (v * 1e-6) / 1e9, 1)} for k, v in ktimes.items()}
+    kname = max(ktimes, key=ktimes.get)
+    kus = ktimes[kname]
+    achieved = kbytes[kname] / (kus * 1e-6) / 1e9
+    src_hash = kernel_source_hash()
     traffic = load_traffic(wl.name, kname, src_hash)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic, "kernel": kname, "kernel_us": round(kus, 3),
-                "algorithmic_bytes_per_launch": int(kbytes), "kernel_source_sha": src_hash}
+                "algorithmic_bytes_per_launch": int(kbytes[kname]), "kernel_source_sha": src_hash}
 
     result = {
         "metric": METRIC, "value": round(us_step, 3), "unit": "us/call (fwd+bwd)",
@@ -292,12 +353,11 @@ def main():
         "config": {"workload": wl.name, "B": B, "Q": Q, "S": S, "M": M, "D": D, "L": L, "K": Kp,
                    "levels": [list(x) for x in wl.levels], "accum": call.resolved_accum,
                    "parallelism": "single GPU"},
-        "fwd_us": round(fwd_us, 3), "bwd_us": round(bwd_us, 3), "host_enqueue_us": round(host_us, 3),
-        "graph_step_us": round(graph_step_us, 3),
-        "fwd_kernel_us": round(fwd_kernel_us, 3), "fwd_kernel_GBps": round(fwd_gbps, 1),
-        "scatter_kernel_us": round(scatter_us, 3), "scatter_kernel_GBps": round(scatter_gbps, 1),
-        "scatter_all_native_kernel_us": round(scatter_native_us, 3),
-        "touched_rows_U": U, "points_P": P,
+        "timing": "graph replay" if graph_ok else "eager",
+        "eager_us_per_step": round(eager_us, 3), "host_enqueue_us": round(host_us, 3),
+        "fwd_us": round(ktimes["msda_fwd_kernel"], 3),
+        "bwd_us": round(sum(v for k, v in ktimes.items() if k != "msda_fwd_kernel"), 3),
+        "kernels": kernels, "touched_rows_U": U, "corners_C": C, "points_P": P,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

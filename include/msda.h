@@ -72,25 +72,35 @@ typedef enum msda_dtype {
     MSDA_BF16 = 2
 } msda_dtype_t;
 
-/* Where the backward accumulates grad_value (course page "5. The backward
- * kernel", section "The fix: accumulate in FP32, downcast at the end").
+/* How the backward accumulates grad_value (course page "5. The backward
+ * kernel", sections "Scatter needs atomics" and "The fix: accumulate in FP32,
+ * downcast at the end").
  *   NATIVE        atomics of the value dtype straight into grad_value
  *                 (fp32 atomics, or packed two-wide fp16 / bf16 atomics);
- *   FP32_SCRATCH  fp32 atomics into the caller's workspace, then one
- *                 downcast pass into grad_value (identical to NATIVE for fp32);
- *   AUTO          the library's measured choice: fp32 data -> fp32 atomics;
- *                 fp16 -> packed fp16 atomics; bf16 -> per level: fp32 scratch
- *                 for levels whose pixels receive more than 4 contributions on
- *                 average (Q*K*4 / (H_l*W_l) > 4), packed bf16 atomics for the
- *                 others (bf16 keeps 8 significant bits, so long chains of
- *                 rounded adds drift; see msda_backward).
- * The scratch for a level is laid out (B, H_l*W_l, M, D) in fp32; its rows are
- * added into grad_value once at the end. */
+ *   FP32_SCRATCH  fp32 atomics into the caller's workspace, then one pass
+ *                 adding it into grad_value (identical to NATIVE for fp32);
+ *   PER_LEVEL     16-bit data: fp32 scratch for the levels whose pixels
+ *                 receive more than 4 contributions on average
+ *                 (Q*K*4 / (H_l*W_l) > 4), packed atomics for the others;
+ *   BINNED        no float atomics: every in-bounds corner becomes an 8-byte
+ *                 record in the bin of its destination rows (count, scan,
+ *                 place), and one workgroup per bin sums its records in fp32
+ *                 and writes the bin's grad_value rows once. Needs
+ *                 non-overlapping levels, Q < 2^22 and a batch slice of value
+ *                 below 2 GiB; the workspace holds 8 bytes per point corner;
+ *   AUTO          PER_LEVEL for bf16, NATIVE for fp16 / fp32: the fastest
+ *                 measured paths that hold the parity bars. BINNED rounds
+ *                 every grad_value element once, with no global float
+ *                 atomics, but measures 2-4x slower on MI355X.
+ * A scratch level is laid out (B, H_l*W_l, M, D) in fp32. grad_value is the
+ * fp32 sum rounded once to the value dtype except for levels accumulated with
+ * packed 16-bit atomics, which round every add. */
 typedef enum msda_accum {
     MSDA_ACCUM_AUTO = -1,
     MSDA_ACCUM_NATIVE = 0,
     MSDA_ACCUM_FP32_SCRATCH = 1,
-    MSDA_ACCUM_PER_LEVEL = 2  /* resolution only: scratch for some levels */
+    MSDA_ACCUM_PER_LEVEL = 2,
+    MSDA_ACCUM_BINNED = 3
 } msda_accum_t;
 
 typedef enum msda_status {
@@ -110,7 +120,8 @@ typedef enum msda_status {
 #define MSDA_FLAG_ACCUMULATE_GRAD_VALUE 1u
 /* The workspace already holds this problem's fp32 partial sums from an earlier
  * call made with MSDA_FLAG_DEFER_SCRATCH: keep adding to them instead of
- * zero-filling the workspace first. */
+ * zero-filling the workspace first. CONTINUE_SCRATCH and DEFER_SCRATCH need
+ * an explicit FP32_SCRATCH or PER_LEVEL mode. */
 #define MSDA_FLAG_CONTINUE_SCRATCH 2u
 /* Leave the fp32 sums of the scratch levels in the workspace instead of
  * adding them into grad_value at the end. With CONTINUE_SCRATCH this lets
@@ -145,9 +156,9 @@ size_t msda_backward_workspace_size(int dtype, int64_t batch, int64_t num_keys,
 
 /*
  * The accumulation msda_backward will use for `accum` on this problem:
- * NATIVE (no level uses scratch; always the case for fp32 data),
- * FP32_SCRATCH (every level does), PER_LEVEL (some levels do), or -1 on
- * invalid arguments.
+ * BINNED, NATIVE (no level uses scratch; always the case for fp32 data
+ * outside BINNED), FP32_SCRATCH (every level does), PER_LEVEL (some levels
+ * do), or -1 on invalid arguments (and for BINNED where it cannot apply).
  */
 int msda_backward_resolve_accum(int dtype, int64_t batch, int64_t num_keys,
                                 int64_t num_heads, int64_t head_dim,
@@ -174,6 +185,20 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                   void *grad_value, void *grad_sampling_locations,
                   void *grad_attention_weights, int accum, unsigned flags,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Instrumentation for profilers and benchmarks: the next msda_forward or
+ * msda_backward call made by this thread records events[2i] (hipEvent_t
+ * passed as void*) on its stream right before its i-th kernel launch and
+ * events[2i+1] right after it, while 2i+1 < count (count <= 64); the setting
+ * then clears itself. Kernel i's device time is the time between the two
+ * events. The events are the caller's.
+ */
+int msda_set_launch_events(void *const *events, int count);
+
+/* How many events the last instrumented call of this thread recorded
+ * (twice the number of kernels it launched, up to its count). */
+int msda_launch_events_recorded(void);
 
 /* Static text for a status code. */
 const char *msda_status_string(int status);

@@ -21,8 +21,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmsda_amd.so")
 
 MSDA_F32, MSDA_F16, MSDA_BF16 = 0, 1, 2
-ACCUM_AUTO, ACCUM_NATIVE, ACCUM_FP32_SCRATCH, ACCUM_PER_LEVEL = -1, 0, 1, 2
-_RESOLVED = {ACCUM_NATIVE: "native", ACCUM_FP32_SCRATCH: "fp32_scratch", ACCUM_PER_LEVEL: "per_level"}
+ACCUM_AUTO, ACCUM_NATIVE, ACCUM_FP32_SCRATCH, ACCUM_PER_LEVEL, ACCUM_BINNED = -1, 0, 1, 2, 3
+_RESOLVED = {ACCUM_NATIVE: "native", ACCUM_FP32_SCRATCH: "fp32_scratch", ACCUM_PER_LEVEL: "per_level",
+             ACCUM_BINNED: "binned"}
 FLAG_ACCUMULATE_GRAD_VALUE = 1
 FLAG_CONTINUE_SCRATCH = 2
 FLAG_DEFER_SCRATCH = 4
@@ -30,12 +31,13 @@ MAX_LEVELS = 16
 
 _DTYPE_CODES = {torch.float32: MSDA_F32, torch.float16: MSDA_F16, torch.bfloat16: MSDA_BF16}
 _ACCUM_CODES = {"auto": ACCUM_AUTO, None: ACCUM_AUTO, "native": ACCUM_NATIVE, False: ACCUM_NATIVE,
-                "fp32_scratch": ACCUM_FP32_SCRATCH, True: ACCUM_FP32_SCRATCH}
+                "fp32_scratch": ACCUM_FP32_SCRATCH, True: ACCUM_FP32_SCRATCH,
+                "per_level": ACCUM_PER_LEVEL, "binned": ACCUM_BINNED}
 
 # every symbol include/msda.h declares
 EXPORTED_SYMBOLS = ("msda_forward", "msda_backward", "msda_backward_workspace_size",
                     "msda_backward_resolve_accum", "msda_status_string", "msda_last_error",
-                    "msda_abi_version")
+                    "msda_abi_version", "msda_set_launch_events", "msda_launch_events_recorded")
 
 _lib = None
 
@@ -72,6 +74,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msda_last_error.restype = ctypes.c_char_p
     lib.msda_abi_version.argtypes = []
     lib.msda_abi_version.restype = i32
+    lib.msda_set_launch_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
+    lib.msda_set_launch_events.restype = i32
+    lib.msda_launch_events_recorded.argtypes = []
+    lib.msda_launch_events_recorded.restype = i32
     _lib = lib
     return lib
 
@@ -195,6 +201,19 @@ def msda_backward_resolve_accum(value: torch.Tensor, spatial_shapes, level_start
     return _RESOLVED[r]
 
 
+def set_launch_events(events) -> None:
+    """Instrument the next msda_forward / msda_backward call of this thread:
+    events[i] (torch.cuda.Event, already created) is recorded on the call's
+    stream right after its i-th kernel launch."""
+    lib = load_library()
+    handles = (ctypes.c_void_p * max(1, len(events)))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    _check(lib.msda_set_launch_events(handles, len(events)))
+
+
+def launch_events_recorded() -> int:
+    return int(load_library().msda_launch_events_recorded())
+
+
 class MSDAErrorCodes:
     NULL_ARG, SHAPE, LEVELS, DTYPE, ALIGN, WORKSPACE, HIP, UNSUPPORTED = range(1, 9)
 
@@ -301,10 +320,28 @@ class PreparedCall:
         self.resolved_accum = _RESOLVED.get(
             int(self.lib.msda_backward_resolve_accum(*self.prob, self.accum_code)))
 
+    def bin_count(self) -> int:
+        """Number of grad_value bins of the binned accumulation (its layout
+        rule: about 512 records per bin, at most 32 KiB of fp32 tile)."""
+        B, Q, M, L, K, _ = self.loc.shape
+        D = self.value.shape[3]
+        tp_max = 1
+        while tp_max * 2 <= 1024 and tp_max * 2 * D * 4 <= 32768:
+            tp_max *= 2
+        nbbm = 0
+        for h, w in self.levels.shapes.tolist():
+            c = Q * K * 4 / (h * w)
+            want = 512.0 / c if c > 0 else tp_max
+            tp = 1
+            while tp * 2 <= tp_max and tp * 2 <= want:
+                tp *= 2
+            nbbm += (h * w + tp - 1) // tp
+        return B * M * nbbm
+
     def scratch_levels(self):
         """Levels whose grad_value rows the backward accumulates in fp32 scratch
         under this call's accumulation mode (same rule as the library)."""
-        if self.value.dtype == torch.float32 or self.resolved_accum == "native":
+        if self.value.dtype == torch.float32 or self.resolved_accum in ("native", "binned"):
             return []
         L = self.levels.L
         if self.resolved_accum == "fp32_scratch":

@@ -18,6 +18,39 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Launch events of msda_set_launch_events (this thread's next call only).
+constexpr int kMaxLaunchEvents = 64;
+thread_local hipEvent_t g_launch_events[kMaxLaunchEvents];
+thread_local int g_launch_events_n = 0;
+thread_local int g_launch_events_next = 0;
+
+// Record the "before" event of the next launch (called as an argument of
+// marked(), so it runs right before the launch call itself).
+hipStream_t before(hipStream_t s) {
+    if (g_launch_events_next + 1 < g_launch_events_n)
+        (void)hipEventRecord(g_launch_events[g_launch_events_next], s);
+    return s;
+}
+
+// After a launch: record its "after" event (the pair is consumed only when
+// both fit in the caller's array).
+hipError_t marked(hipError_t err, hipStream_t s) {
+    if (g_launch_events_next + 1 < g_launch_events_n) {
+        if (err == hipSuccess) err = hipEventRecord(g_launch_events[g_launch_events_next + 1], s);
+        g_launch_events_next += 2;
+    }
+    return err;
+}
+
+thread_local int g_launch_events_recorded = 0;
+
+struct LaunchEventsScope {  // clears the instrumentation when a call returns
+    ~LaunchEventsScope() {
+        if (g_launch_events_n) g_launch_events_recorded = g_launch_events_next;
+        g_launch_events_n = g_launch_events_next = 0;
+    }
+};
+
 int fail(int status, const char *fmt, ...) {
     char buf[512];
     va_list ap;
@@ -81,6 +114,7 @@ int make_problem(int dtype, int64_t B, int64_t S, int64_t M, int64_t D, int64_t 
     p->K = K;
     memset(&p->levels, 0, sizeof(p->levels));
     for (int l = 0; l < MSDA_MAX_LEVELS; ++l) p->levels.scratch_off[l] = -1;
+    p->nbbm = 0;
     int64_t acc = 0;
     for (int64_t l = 0; l < L; ++l) {
         const int64_t H = shapes[2 * l], W = shapes[2 * l + 1];
@@ -180,21 +214,28 @@ double contributions_per_pixel(const msda::Problem &p, int l) {
            ((double)p.levels.H[l] * (double)p.levels.W[l]);
 }
 
+int resolved_mode(const msda::Problem &p) {
+    int n = 0;
+    for (int l = 0; l < (int)p.L; ++l) n += p.levels.scratch_off[l] >= 0;
+    if (n == 0) return MSDA_ACCUM_NATIVE;
+    return n == (int)p.L ? MSDA_ACCUM_FP32_SCRATCH : MSDA_ACCUM_PER_LEVEL;
+}
+
+bool valid_accum(int accum) { return accum >= MSDA_ACCUM_AUTO && accum <= MSDA_ACCUM_BINNED; }
+
 // Decide, per level, whether the backward accumulates in fp32 scratch, and
 // lay the scratch blocks out back to back. Returns the workspace bytes.
-// AUTO: fp32 data never needs scratch; fp16 keeps packed fp16 atomics (11
-// significant bits held parity on every tested shape, including ~1300
-// contributions per pixel); bf16 (8 significant bits) uses fp32 scratch for
-// levels above 4 contributions per pixel, where chains of rounded adds drift
-// beyond the 5e-2 parity bar in the tails.
-size_t plan_scratch(msda::Problem *p, int accum) {
+// FP32_SCRATCH: every level of 16-bit data; PER_LEVEL: 16-bit levels above 4
+// contributions per pixel (bf16 keeps 8 significant bits: long chains of
+// rounded packed adds drift beyond the 5e-2 parity bar in the tails, while
+// fp16's 11 bits held parity on every tested shape); NATIVE: none.
+size_t plan_scratch(msda::Problem *p, int mode) {
     size_t total = 0;
     for (int l = 0; l < (int)p->L; ++l) {
         bool scratch = false;
         if (p->dtype != MSDA_F32) {
-            if (accum == MSDA_ACCUM_FP32_SCRATCH) scratch = true;
-            else if (accum == MSDA_ACCUM_AUTO && p->dtype == MSDA_BF16)
-                scratch = contributions_per_pixel(*p, l) > 4.0;
+            if (mode == MSDA_ACCUM_FP32_SCRATCH) scratch = true;
+            else if (mode == MSDA_ACCUM_PER_LEVEL) scratch = contributions_per_pixel(*p, l) > 4.0;
         }
         if (scratch) {
             p->levels.scratch_off[l] = (int64_t)(total / sizeof(float));
@@ -207,16 +248,92 @@ size_t plan_scratch(msda::Problem *p, int accum) {
     return total;
 }
 
-int resolved_mode(const msda::Problem &p) {
-    int n = 0;
-    for (int l = 0; l < (int)p.L; ++l) n += p.levels.scratch_off[l] >= 0;
-    if (n == 0) return MSDA_ACCUM_NATIVE;
-    return n == (int)p.L ? MSDA_ACCUM_FP32_SCRATCH : MSDA_ACCUM_PER_LEVEL;
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool levels_overlap(const msda::Problem &p) {
+    for (int i = 0; i < (int)p.L; ++i)
+        for (int k = i + 1; k < (int)p.L; ++k) {
+            const int64_t a0 = p.levels.start[i], a1 = a0 + (int64_t)p.levels.H[i] * p.levels.W[i];
+            const int64_t b0 = p.levels.start[k], b1 = b0 + (int64_t)p.levels.H[k] * p.levels.W[k];
+            if (a0 < b1 && b0 < a1) return true;
+        }
+    return false;
 }
 
-bool valid_accum(int accum) {
-    return accum == MSDA_ACCUM_AUTO || accum == MSDA_ACCUM_NATIVE ||
-           accum == MSDA_ACCUM_FP32_SCRATCH;
+// Rows of [0, S) outside every level (padding rows) are written by no bin.
+bool levels_leave_gaps(const msda::Problem &p) {
+    int64_t covered = 0;
+    for (int l = 0; l < (int)p.L; ++l) covered += (int64_t)p.levels.H[l] * p.levels.W[l];
+    return covered != p.S;  // levels do not overlap here, so equality covers [0, S)
+}
+
+// Binned grad_value plan: per level a bin height of 2^bin_shift pixel rows so
+// that a bin holds about kBinRecords records if the level's points spread
+// evenly (contributions per pixel Q*K*4 / (H*W)), capped so that the fp32 LDS
+// tile of a bin stays within 32 KiB. Returns false where the path cannot
+// apply; on success fills the level table and the workspace layout.
+constexpr double kBinRecords = 512.0;
+
+struct BinPlan {
+    int64_t nbins = 0, records = 0;
+    int max_rows = 0;
+    size_t starts_off = 0, cursor_off = 0, records_off = 0, bytes = 0;
+};
+
+bool plan_bins(msda::Problem *p, BinPlan *bp) {
+    const int64_t e = p->dtype == MSDA_F32 ? 4 : 2;
+    const int64_t P = p->B * p->Q * p->M * p->L * p->K;
+    if (levels_overlap(*p) || p->Q >= ((int64_t)1 << 22) || 4 * P >= ((int64_t)1 << 32) ||
+        p->S * p->M * p->D * e > ((int64_t)1 << 31) - 64 || p->B * p->Q * p->M >= ((int64_t)1 << 31))
+        return false;
+    int tp_max = 1;
+    while (tp_max * 2 <= 1024 && (int64_t)tp_max * 2 * p->D * 4 <= 32768) tp_max *= 2;
+    int64_t nbbm = 0;
+    int max_rows = 1;
+    for (int l = 0; l < (int)p->L; ++l) {
+        const double c = contributions_per_pixel(*p, l);
+        const double want = c > 0 ? kBinRecords / c : (double)tp_max;
+        int sh = 0;
+        while ((1 << (sh + 1)) <= tp_max && (double)(1 << (sh + 1)) <= want) ++sh;
+        const int64_t HW = (int64_t)p->levels.H[l] * p->levels.W[l];
+        p->levels.bin_shift[l] = sh;
+        p->levels.bin_off[l] = (int32_t)nbbm;
+        nbbm += (HW + (1 << sh) - 1) >> sh;
+        const int rows = (int)(HW < (1 << sh) ? HW : (1 << sh));
+        if (rows > max_rows) max_rows = rows;
+        if (nbbm >= ((int64_t)1 << 31)) return false;
+    }
+    const int64_t nbins = p->B * p->M * nbbm;
+    if (nbins >= ((int64_t)1 << 31) - 1) return false;
+    p->nbbm = nbbm;
+    bp->nbins = nbins;
+    bp->records = 4 * P;
+    bp->max_rows = max_rows;
+    bp->starts_off = 0;
+    bp->cursor_off = align_up((size_t)(nbins + 1) * 4, 256);
+    bp->records_off = bp->cursor_off + align_up((size_t)nbins * 4, 256);
+    bp->bytes = bp->records_off + (size_t)bp->records * 8;
+    return true;
+}
+
+// Resolve `accum` and plan the buffers. Returns the resolved mode, or -1 if
+// an explicit BINNED cannot apply. *bytes = workspace bytes needed.
+// AUTO is PER_LEVEL for bf16 and NATIVE otherwise: measured on MI355X, the
+// binned path's shared per-bin counters serialise (hundreds of increments per
+// address on the decoder workload) and its per-bin accumulation is latency
+// bound, so it is 2-4x slower than the segment-coalesced atomics.
+int plan_accum(msda::Problem *p, int accum, size_t *bytes, BinPlan *bp) {
+    int mode = accum;
+    if (accum == MSDA_ACCUM_BINNED) {
+        if (!plan_bins(p, bp)) return -1;
+        plan_scratch(p, MSDA_ACCUM_NATIVE);
+        *bytes = bp->bytes;
+        return MSDA_ACCUM_BINNED;
+    }
+    if (accum == MSDA_ACCUM_AUTO)
+        mode = p->dtype == MSDA_BF16 ? MSDA_ACCUM_PER_LEVEL : MSDA_ACCUM_NATIVE;
+    *bytes = plan_scratch(p, mode);
+    return resolved_mode(*p);
 }
 
 // Backward lane mapping: slots of one dword for 16-bit data with even D and
@@ -259,6 +376,21 @@ extern "C" {
 
 int msda_abi_version(void) { return MSDA_ABI_VERSION; }
 
+int msda_launch_events_recorded(void) { return g_launch_events_recorded; }
+
+int msda_set_launch_events(void *const *events, int count) {
+    if (count < 0 || count > kMaxLaunchEvents)
+        return fail(MSDA_ERR_SHAPE, "launch event count %d outside [0, %d]", count, kMaxLaunchEvents);
+    if (count > 0 && !events) return fail(MSDA_ERR_NULL_ARG, "events is NULL");
+    for (int i = 0; i < count; ++i) {
+        if (!events[i]) return fail(MSDA_ERR_NULL_ARG, "event %d is NULL", i);
+        g_launch_events[i] = static_cast<hipEvent_t>(events[i]);
+    }
+    g_launch_events_n = count;
+    g_launch_events_next = 0;
+    return ok();
+}
+
 const char *msda_last_error(void) { return g_last_error.c_str(); }
 
 const char *msda_status_string(int status) {
@@ -281,6 +413,7 @@ int msda_forward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, 
                  const int64_t *level_start_index, int64_t num_queries, int64_t num_points,
                  const void *value, const void *sampling_locations, const void *attention_weights,
                  void *output, void *stream) {
+    LaunchEventsScope events_scope;
     msda::Problem p;
     int st = make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
                           level_start_index, num_queries, num_points, &p);
@@ -293,8 +426,10 @@ int msda_forward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, 
     const void *vec_ptrs[] = {value, output};
     msda::Mapping mp;
     if ((st = choose_mapping(p, vec_ptrs, 2, &mp))) return st;
-    hipError_t err = msda::launch_forward(p, mp, value, sampling_locations, attention_weights,
-                                          output, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err = marked(msda::launch_forward(p, mp, value, sampling_locations,
+                                                 attention_weights, output, before(s)),
+                            s);
     if (err != hipSuccess) return hip_fail(err, "forward launch");
     return ok();
 }
@@ -311,8 +446,11 @@ int msda_backward_resolve_accum(int dtype, int64_t batch, int64_t num_keys, int6
         fail(MSDA_ERR_DTYPE, "unknown accumulation mode %d", accum);
         return -1;
     }
-    plan_scratch(&p, accum);
-    return resolved_mode(p);
+    size_t bytes;
+    BinPlan bp;
+    const int mode = plan_accum(&p, accum, &bytes, &bp);
+    if (mode < 0) fail(MSDA_ERR_UNSUPPORTED, "binned accumulation does not apply to this problem");
+    return mode;
 }
 
 size_t msda_backward_workspace_size(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
@@ -328,7 +466,13 @@ size_t msda_backward_workspace_size(int dtype, int64_t batch, int64_t num_keys, 
         fail(MSDA_ERR_DTYPE, "unknown accumulation mode %d", accum);
         return 0;
     }
-    return plan_scratch(&p, accum);
+    size_t bytes = 0;
+    BinPlan bp;
+    if (plan_accum(&p, accum, &bytes, &bp) < 0) {
+        fail(MSDA_ERR_UNSUPPORTED, "binned accumulation does not apply to this problem");
+        return 0;
+    }
+    return bytes;
 }
 
 int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, int64_t head_dim,
@@ -338,6 +482,7 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                   const void *grad_output, void *grad_value, void *grad_sampling_locations,
                   void *grad_attention_weights, int accum, unsigned flags, void *workspace,
                   size_t workspace_bytes, void *stream) {
+    LaunchEventsScope events_scope;
     msda::Problem p;
     int st = make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
                           level_start_index, num_queries, num_points, &p);
@@ -348,8 +493,19 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
     if (flags & ~known) return fail(MSDA_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~known);
     if (p.B == 0) return ok();
     const bool accumulate = (flags & MSDA_FLAG_ACCUMULATE_GRAD_VALUE) != 0;
-    const size_t need = plan_scratch(&p, accum);
-    const int mode = resolved_mode(p);
+    const bool keep_sums = (flags & MSDA_FLAG_CONTINUE_SCRATCH) != 0;
+    const bool defer = (flags & MSDA_FLAG_DEFER_SCRATCH) != 0;
+    if ((keep_sums || defer) && accum != MSDA_ACCUM_FP32_SCRATCH && accum != MSDA_ACCUM_PER_LEVEL &&
+        accum != MSDA_ACCUM_NATIVE)
+        return fail(MSDA_ERR_SHAPE,
+                    "CONTINUE_SCRATCH / DEFER_SCRATCH need an explicit NATIVE, FP32_SCRATCH or "
+                    "PER_LEVEL accumulation");
+    size_t need = 0;
+    BinPlan bp;
+    const int mode = plan_accum(&p, accum, &need, &bp);
+    if (mode < 0)
+        return fail(MSDA_ERR_UNSUPPORTED, "binned accumulation does not apply to this problem");
+    const bool binned = mode == MSDA_ACCUM_BINNED;
     if ((st = check_ptr(value, "value", dtype))) return st;
     if ((st = check_ptr(grad_value, "grad_value", dtype))) return st;
     if (need) {
@@ -360,7 +516,7 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
     }
     // Native half-precision atomics update aligned 4-byte pairs; every pair
     // must lie inside grad_value.
-    if (mode != MSDA_ACCUM_FP32_SCRATCH && dtype != MSDA_F32 &&
+    if (!binned && mode != MSDA_ACCUM_FP32_SCRATCH && dtype != MSDA_F32 &&
         (!aligned(grad_value, 4) || (p.B * p.S * p.M * p.D) % 2 != 0))
         return fail(MSDA_ERR_ALIGN,
                     "native half-precision atomics need a 4-byte aligned grad_value with an even "
@@ -378,21 +534,57 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t gv_bytes = (size_t)(p.B * p.S * p.M * p.D) * elem_size(dtype);
     hipError_t err;
-    if (!accumulate && (err = msda::launch_zero(grad_value, gv_bytes, s)) != hipSuccess)
+    if (binned) {
+        // Rows outside every level are written by no bin: zero all of
+        // grad_value first when there are such rows (or no queries at all).
+        if (!accumulate && (p.Q == 0 || levels_leave_gaps(p)) &&
+            (err = marked(msda::launch_zero(grad_value, gv_bytes, before(s)), s)) != hipSuccess)
+            return hip_fail(err, "grad_value zero fill");
+        if (p.Q == 0) return ok();
+        char *ws = static_cast<char *>(workspace);
+        msda::BinnedBuffers bins;
+        bins.starts = reinterpret_cast<uint32_t *>(ws + bp.starts_off);
+        bins.cursor = reinterpret_cast<uint32_t *>(ws + bp.cursor_off);
+        bins.records = reinterpret_cast<uint2 *>(ws + bp.records_off);
+        bins.nbins = bp.nbins;
+        bins.max_bin_rows = bp.max_rows;
+        // the counts (starts[0:nbins]) start at zero; the fill works in
+        // 2-byte units, so round the byte count up to an even number of them
+        if ((err = marked(msda::launch_zero(bins.starts, align_up((size_t)(bp.nbins + 1) * 4, 16), before(s)), s)) !=
+            hipSuccess)
+            return hip_fail(err, "bin count zero fill");
+        if ((err = marked(msda::launch_bin_count(p, sampling_locations, bins, before(s)), s)) != hipSuccess)
+            return hip_fail(err, "bin count launch");
+        if ((err = marked(msda::launch_bin_scan(bins, before(s)), s)) != hipSuccess)
+            return hip_fail(err, "bin scan launch");
+        if ((err = marked(msda::launch_backward_binned(p, mp, value, sampling_locations,
+                                                       attention_weights, grad_output, bins,
+                                                       grad_sampling_locations,
+                                                       grad_attention_weights, before(s)),
+                          s)) != hipSuccess)
+            return hip_fail(err, "backward launch");
+        if ((err = marked(msda::launch_bin_accumulate(p, mp, grad_output, grad_value, bins,
+                                                      accumulate, before(s)),
+                          s)) != hipSuccess)
+            return hip_fail(err, "bin accumulate launch");
+        return ok();
+    }
+    if (!accumulate && (err = marked(msda::launch_zero(grad_value, gv_bytes, before(s)), s)) != hipSuccess)
         return hip_fail(err, "grad_value zero fill");
-    const bool keep_sums = (flags & MSDA_FLAG_CONTINUE_SCRATCH) != 0;
-    const bool defer = (flags & MSDA_FLAG_DEFER_SCRATCH) != 0;
-    if (need && !keep_sums && (err = msda::launch_zero(workspace, need, s)) != hipSuccess)
+    if (need && !keep_sums && (err = marked(msda::launch_zero(workspace, need, before(s)), s)) != hipSuccess)
         return hip_fail(err, "scratch zero fill");
     if (p.Q > 0 &&
-        (err = msda::launch_backward(p, mp, value, sampling_locations, attention_weights,
-                                     grad_output, grad_value, static_cast<float *>(workspace),
-                                     grad_sampling_locations, grad_attention_weights, s)) !=
-            hipSuccess)
+        (err = marked(msda::launch_backward(p, mp, value, sampling_locations, attention_weights,
+                                            grad_output, grad_value,
+                                            static_cast<float *>(workspace),
+                                            grad_sampling_locations, grad_attention_weights,
+                                            before(s)),
+                      s)) != hipSuccess)
         return hip_fail(err, "backward launch");
     if (need && !defer &&
-        (err = msda::launch_scratch_add(p, static_cast<const float *>(workspace), grad_value, s)) !=
-            hipSuccess)
+        (err = marked(msda::launch_scratch_add(p, static_cast<const float *>(workspace),
+                                               grad_value, before(s)),
+                      s)) != hipSuccess)
         return hip_fail(err, "scratch add launch");
     return ok();
 }

@@ -302,6 +302,53 @@ __device__ __forceinline__ Cell map_cell(float loc_x, float loc_y, float Hf, flo
     return c;
 }
 
+// ------------------------------------------------- wave-aggregated counters
+//
+// Adds 1 to ctr[key] for every lane with `ok`, one atomic per distinct key in
+// the wave (the first pending lane leads; lanes with its key join). With
+// RETURN the lane gets the slot old_value + rank-among-equal-keys. All 64
+// lanes must call it together.
+template <bool RETURN>
+__device__ __forceinline__ uint32_t wave_aggregate(uint32_t *ctr, uint32_t key, bool ok) {
+    uint32_t slot = 0;
+    bool pending = ok;
+    const int lane = (int)(threadIdx.x & 63);
+    while (true) {
+        const uint64_t act = __ballot(pending);
+        if (!act) break;
+        const int leader = (int)__builtin_ctzll(act);
+        const uint32_t lkey = __builtin_amdgcn_readlane(key, leader);
+        const bool mine = pending && key == lkey;
+        const uint64_t same = __ballot(mine);
+        uint32_t base = 0;
+        if (lane == leader) {
+            if constexpr (RETURN)
+                base = __hip_atomic_fetch_add(ctr + lkey, (uint32_t)__popcll(same), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+            else
+                __hip_atomic_fetch_add(ctr + lkey, (uint32_t)__popcll(same), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if constexpr (RETURN) {
+            base = __builtin_amdgcn_readlane(base, leader);
+            const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(same >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)same, 0u));
+            if (mine) slot = base + rank;
+        }
+        if (mine) pending = false;
+    }
+    return slot;
+}
+
+// Bin of pixel row `row` (absolute, within level l) of head m of batch b.
+__device__ __forceinline__ uint32_t bin_of(const LevelTable &lt, int l, int64_t b, int m, int M,
+                                          int64_t nbbm, int64_t row, uint32_t *row_in_bin) {
+    const int64_t rel = row - lt.start[l];
+    const int sh = lt.bin_shift[l];
+    *row_in_bin = (uint32_t)(rel & ((1 << sh) - 1));
+    return (uint32_t)((b * M + m) * nbbm + lt.bin_off[l] + (rel >> sh));
+}
+
 // ------------------------------------------------------------- forward
 //
 // A lane group handles the points p = i * split + s (i = 0, 1, ...) of its
@@ -443,7 +490,7 @@ struct BwdChunk {
     static constexpr int value = J >= 8 ? 1 : (J >= 3 ? 2 : 8 / J);
 };
 
-template <class DT, int SLOT, int J, bool BUF>
+template <class DT, int SLOT, int J, bool BUF, bool BIN>
 __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
     const typename DT::S *__restrict__ value, const typename DT::S *__restrict__ loc,
     const typename DT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out,
@@ -451,7 +498,7 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
     typename DT::S *__restrict__ grad_loc, typename DT::S *__restrict__ grad_attn,
     const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
     const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
-    const int log2s) {
+    const int log2s, const BinnedBuffers bins, const int64_t nbbm) {
     using E = typename DT::S;
     using R = typename RawVec<SLOT * (int)sizeof(E)>::type;  // one slot
     constexpr bool kF32 = sizeof(E) == 4;
@@ -584,6 +631,7 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
                 grad_loc[2 * pp] = from_f32(DT{}, (float)lt.W[l] * aw[t] * dx[t]);
                 grad_loc[2 * pp + 1] = from_f32(DT{}, (float)lt.H[l] * aw[t] * dy[t]);
             }
+            if constexpr (BIN) continue;  // grad_value goes through records below
             const int W = lt.W[l];
             const int64_t start = lt.start[l];
             const int64_t soff = lt.scratch_off[l];
@@ -626,6 +674,180 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
                 }
             }
         }
+        if constexpr (BIN) {
+            // Records: lane c of a group takes corners c, c + G, ... (< 4) of
+            // point t. Wave-uniform loops: the slot allocation aggregates a
+            // whole wave, and every in-bounds corner counted by
+            // bin_count_kernel gets exactly one record.
+#pragma unroll
+            for (int t = 0; t < CH; ++t)
+            for (int cn0 = 0; cn0 < 4; cn0 += G) {
+                const int cn = cn0 + c;
+                const int l = lvl[t];
+                const int W = lt.W[l];
+                const bool vcn = cn == 0 ? cl[t].v00 : cn == 1 ? cl[t].v01 : cn == 2 ? cl[t].v10 : cl[t].v11;
+                const bool ok = q_ok && (i0 + t < per_lane) && cn < 4 && vcn;
+                const float fx = cl[t].fx, fy = cl[t].fy;
+                const float wx = (cn & 1) ? fx : 1.0f - fx, wy = (cn & 2) ? fy : 1.0f - fy;
+                const int64_t row = cl[t].row00 + ((cn & 2) ? W : 0) + (cn & 1);
+                uint32_t rib = 0;
+                const uint32_t key = ok ? bin_of(lt, l, b, m, M, nbbm, row, &rib) : 0u;
+                const uint32_t slot = wave_aggregate<true>(bins.cursor, key, ok);
+                if (ok)
+                    bins.records[slot] = make_uint2(((uint32_t)q << 10) | rib,
+                                                    __float_as_uint(aw[t] * wx * wy));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------ binned grad_value
+//
+// grad_value without float atomics: every in-bounds corner becomes an 8-byte
+// record in the bin of its destination rows (a counting sort: count, scan,
+// place), then one workgroup per bin sums its records in an fp32 LDS tile and
+// writes the bin's rows once. Bins are sized per level so that each holds a
+// few hundred records on average, which keeps heavily shared coarse levels
+// (encoder shapes: ~1300 contributions per pixel) balanced.
+
+// One lane per point: count the in-bounds corners per bin.
+template <class DT>
+__global__ __launch_bounds__(kBlock) void bin_count_kernel(
+    const typename DT::S *__restrict__ loc, const LevelTable lt, uint32_t *__restrict__ counts,
+    const uint32_t P, const uint32_t LK, const uint32_t K, const uint32_t M, const uint32_t QM,
+    const int64_t nbbm, const int64_t iters) {
+    for (int64_t it = 0; it < iters; ++it) {
+        const uint64_t p = ((uint64_t)it * gridDim.x + blockIdx.x) * kBlock + threadIdx.x;
+        const bool pv = p < P;
+        const uint32_t pc = pv ? (uint32_t)p : 0u;
+        const uint32_t pq = pc / LK;
+        const int l = (int)((pc - pq * LK) / K);
+        const uint32_t b = pq / QM, m = pq % M;
+        const float x = to_f32(DT{}, loc[2 * (uint64_t)pc]);
+        const float y = to_f32(DT{}, loc[2 * (uint64_t)pc + 1]);
+        const int W = lt.W[l];
+        const Cell cl = map_cell(x, y, (float)lt.H[l], (float)W, W, lt.start[l]);
+        const bool vc[4] = {cl.v00, cl.v01, cl.v10, cl.v11};
+#pragma unroll
+        for (int cn = 0; cn < 4; ++cn) {
+            const bool ok = pv && vc[cn];
+            const int64_t row = cl.row00 + ((cn & 2) ? W : 0) + (cn & 1);
+            uint32_t rib;
+            const uint32_t key = ok ? bin_of(lt, l, b, (int)m, (int)M, nbbm, row, &rib) : 0u;
+            wave_aggregate<false>(counts, key, ok);
+        }
+    }
+}
+
+// One workgroup: counts[0:nb] -> exclusive starts[0:nb+1], cursor = starts.
+constexpr int kScanBlock = 1024;
+__global__ __launch_bounds__(kScanBlock) void bin_scan_kernel(uint32_t *__restrict__ starts,
+                                                             uint32_t *__restrict__ cursor,
+                                                             const int64_t nb) {
+    __shared__ uint32_t part[kScanBlock];
+    const int tid = threadIdx.x;
+    const int64_t per = (nb + kScanBlock - 1) / kScanBlock;
+    const int64_t i0 = tid * per, i1 = (i0 + per < nb) ? i0 + per : nb;
+    uint32_t sum = 0;
+    for (int64_t i = i0; i < i1; ++i) sum += starts[i];
+    part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kScanBlock; off <<= 1) {
+        const uint32_t v = tid >= off ? part[tid - off] : 0u;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    uint32_t run = part[tid] - sum;
+    for (int64_t i = i0; i < i1; ++i) {
+        const uint32_t cnt = starts[i];
+        starts[i] = run;
+        cursor[i] = run;
+        run += cnt;
+    }
+    if (tid == kScanBlock - 1) starts[nb] = part[kScanBlock - 1];
+}
+
+// One workgroup per bin. Lane groups of G lanes take records (U at a time,
+// loads issued before use), gather the query's upstream-gradient row in slot
+// layout and add coef * g into the LDS tile; then the tile's rows are written
+// (or added, with `accumulate`) to grad_value in the value dtype.
+template <class DT, int SLOT, int J>
+__global__ __launch_bounds__(kBlock) void bin_accum_kernel(
+    const typename DT::S *__restrict__ grad_out, typename DT::S *__restrict__ grad_value,
+    const uint32_t *__restrict__ starts, const uint2 *__restrict__ records, const LevelTable lt,
+    const int64_t S, const int64_t Q, const int M, const int D, const int L, const int64_t nbbm,
+    const int log2g, const int accumulate) {
+    using E = typename DT::S;
+    using R = typename RawVec<SLOT * (int)sizeof(E)>::type;
+    constexpr int U = 4;
+    extern __shared__ float tile[];
+    const int64_t bin = blockIdx.x;
+    const int64_t bm = bin / nbbm;
+    const int lb = (int)(bin - bm * nbbm);
+    const int64_t b = bm / M;
+    const int m = (int)(bm - b * M);
+    int l = 0;
+    for (int i = 1; i < L; ++i)
+        if (lb >= lt.bin_off[i]) l = i;
+    const int sh = lt.bin_shift[l];
+    const int64_t HW = (int64_t)lt.H[l] * lt.W[l];
+    const int64_t r0 = (int64_t)(lb - lt.bin_off[l]) << sh;
+    const int rows = (int)(((int64_t)1 << sh) < HW - r0 ? ((int64_t)1 << sh) : HW - r0);
+    const int n = rows * D;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < n; i += kBlock) tile[i] = 0.0f;
+    __syncthreads();
+
+    const uint32_t rb = starts[bin], re = starts[bin + 1];
+    const int G = 1 << log2g;
+    const int c = tid & (G - 1);
+    const int gid = tid >> log2g;
+    const int ngroups = kBlock >> log2g;
+    const int nslots = D / SLOT;
+    const int64_t MD = (int64_t)M * D;
+    const E *gq = grad_out + (b * Q * M + m) * (int64_t)D;
+    for (uint32_t base = rb + (uint32_t)gid * U; base < re; base += (uint32_t)ngroups * U) {
+        uint2 rec[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) rec[u] = records[base + u < re ? base + u : re - 1];
+        R gr[U][J];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // (clamps keep every access in range whatever a record holds)
+            const uint32_t rq = rec[u].x >> 10;
+            const E *gp = gq + (int64_t)(rq < Q ? rq : 0) * MD;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int sl = c + j * G;
+                gr[u][j] = *reinterpret_cast<const R *>(gp + (sl < nslots ? sl : 0) * SLOT);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (base + u >= re) continue;
+            const float coef = __uint_as_float(rec[u].y);
+            const uint32_t rr = rec[u].x & 1023u;
+            float *trow = tile + (rr < (uint32_t)rows ? rr : 0u) * (uint32_t)D;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int sl = c + j * G;
+                if (sl >= nslots) continue;
+                float gv[SLOT];
+                raw_to_f32<DT, SLOT>(gr[u][j], gv);
+#pragma unroll
+                for (int v = 0; v < SLOT; ++v) atomicAdd(trow + sl * SLOT + v, coef * gv[v]);
+            }
+        }
+    }
+    __syncthreads();
+    E *dst = grad_value + ((b * S + lt.start[l] + r0) * M + m) * (int64_t)D;
+    for (int i = tid; i < n; i += kBlock) {
+        const int rr = i / D, ch = i - rr * D;
+        E *d = dst + (int64_t)rr * MD + ch;
+        float v = tile[i];
+        if (accumulate) v += to_f32(DT{}, *d);
+        *d = from_f32(DT{}, v);
     }
 }
 
@@ -717,31 +939,47 @@ hipError_t fwd_launch(const Problem &p, const Mapping &mp, const void *value, co
     return hipGetLastError();
 }
 
-template <class DT, int SLOT, int J>
+template <class DT, int SLOT, int J, bool BIN>
 hipError_t bwd_launch(const Problem &p, const BwdMapping &mp, const void *value, const void *loc,
                       const void *attn, const void *grad_out, void *grad_value, float *workspace,
-                      void *grad_loc, void *grad_attn, hipStream_t stream) {
+                      void *grad_loc, void *grad_attn, const BinnedBuffers &bins,
+                      hipStream_t stream) {
     using E = typename DT::S;
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
     const int qblocks = (int)((p.Q + qpb - 1) / qpb);
     const int64_t ntiles = p.B * p.M * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
-    if (slice_fits_buffer(p))
-        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, true>), dim3((unsigned)(per_xcd * kXcds)),
-                           dim3(kBlock), 0, stream, static_cast<const E *>(value),
-                           static_cast<const E *>(loc), static_cast<const E *>(attn),
-                           static_cast<const E *>(grad_out), grad_value, workspace,
-                           static_cast<E *>(grad_loc), static_cast<E *>(grad_attn), p.levels, p.S,
-                           p.Q, (int)p.M, (int)p.D, (int)p.L, (int)p.K, qblocks, ntiles,
-                           mp.log2_group, mp.log2_split);
-    else
-        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, false>), dim3((unsigned)(per_xcd * kXcds)),
-                           dim3(kBlock), 0, stream, static_cast<const E *>(value),
-                           static_cast<const E *>(loc), static_cast<const E *>(attn),
-                           static_cast<const E *>(grad_out), grad_value, workspace,
-                           static_cast<E *>(grad_loc), static_cast<E *>(grad_attn), p.levels, p.S,
-                           p.Q, (int)p.M, (int)p.D, (int)p.L, (int)p.K, qblocks, ntiles,
-                           mp.log2_group, mp.log2_split);
+    if (BIN || slice_fits_buffer(p))
+        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, true, BIN>),
+                           dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
+                           static_cast<const E *>(value), static_cast<const E *>(loc),
+                           static_cast<const E *>(attn), static_cast<const E *>(grad_out),
+                           grad_value, workspace, static_cast<E *>(grad_loc),
+                           static_cast<E *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
+                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split, bins,
+                           p.nbbm);
+    else if constexpr (!BIN)
+        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, false, false>),
+                           dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
+                           static_cast<const E *>(value), static_cast<const E *>(loc),
+                           static_cast<const E *>(attn), static_cast<const E *>(grad_out),
+                           grad_value, workspace, static_cast<E *>(grad_loc),
+                           static_cast<E *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
+                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split, bins,
+                           p.nbbm);
+    return hipGetLastError();
+}
+
+template <class DT, int SLOT, int J>
+hipError_t accum_launch(const Problem &p, const BwdMapping &mp, const void *grad_out,
+                        void *grad_value, const BinnedBuffers &bins, bool accumulate,
+                        hipStream_t stream) {
+    using E = typename DT::S;
+    const size_t lds = (size_t)bins.max_bin_rows * (size_t)p.D * sizeof(float);
+    hipLaunchKernelGGL((bin_accum_kernel<DT, SLOT, J>), dim3((unsigned)bins.nbins), dim3(kBlock),
+                       lds, stream, static_cast<const E *>(grad_out), static_cast<E *>(grad_value),
+                       bins.starts, bins.records, p.levels, p.S, p.Q, (int)p.M, (int)p.D, (int)p.L,
+                       p.nbbm, mp.log2_group, (int)accumulate);
     return hipGetLastError();
 }
 
@@ -762,21 +1000,39 @@ hipError_t fwd_by_vec(const Problem &p, const Mapping &mp, const void *v, const 
     return hipErrorInvalidValue;
 }
 
-template <class DT, int SLOT>
+template <class DT, int SLOT, bool BIN>
 hipError_t bwd_by_j(const Problem &p, const BwdMapping &mp, const void *v, const void *l,
                     const void *a, const void *go, void *gv, float *ws, void *gl, void *ga,
-                    hipStream_t st) {
+                    const BinnedBuffers &bn, hipStream_t st) {
     switch (mp.j) {
-        case 1: return bwd_launch<DT, SLOT, 1>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 2: return bwd_launch<DT, SLOT, 2>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 3: return bwd_launch<DT, SLOT, 3>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 4: return bwd_launch<DT, SLOT, 4>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 8: return bwd_launch<DT, SLOT, 8>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 16: return bwd_launch<DT, SLOT, 16>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 1: return bwd_launch<DT, SLOT, 1, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
+        case 2: return bwd_launch<DT, SLOT, 2, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
+        case 3: return bwd_launch<DT, SLOT, 3, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
+        case 4: return bwd_launch<DT, SLOT, 4, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
+        case 8: return bwd_launch<DT, SLOT, 8, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
+        case 16: return bwd_launch<DT, SLOT, 16, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
         default: break;
     }
     if constexpr (SLOT == 1) {
-        if (mp.j == 32) return bwd_launch<DT, SLOT, 32>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        if (mp.j == 32) return bwd_launch<DT, SLOT, 32, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class DT, int SLOT>
+hipError_t accum_by_j(const Problem &p, const BwdMapping &mp, const void *go, void *gv,
+                      const BinnedBuffers &bn, bool acc, hipStream_t st) {
+    switch (mp.j) {
+        case 1: return accum_launch<DT, SLOT, 1>(p, mp, go, gv, bn, acc, st);
+        case 2: return accum_launch<DT, SLOT, 2>(p, mp, go, gv, bn, acc, st);
+        case 3: return accum_launch<DT, SLOT, 3>(p, mp, go, gv, bn, acc, st);
+        case 4: return accum_launch<DT, SLOT, 4>(p, mp, go, gv, bn, acc, st);
+        case 8: return accum_launch<DT, SLOT, 8>(p, mp, go, gv, bn, acc, st);
+        case 16: return accum_launch<DT, SLOT, 16>(p, mp, go, gv, bn, acc, st);
+        default: break;
+    }
+    if constexpr (SLOT == 1) {
+        if (mp.j == 32) return accum_launch<DT, SLOT, 32>(p, mp, go, gv, bn, acc, st);
     }
     return hipErrorInvalidValue;
 }
@@ -847,20 +1103,90 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
                            const void *loc, const void *attn, const void *grad_out,
                            void *grad_value, float *workspace, void *grad_loc, void *grad_attn,
                            hipStream_t stream) {
+    const BinnedBuffers none = {nullptr, nullptr, nullptr, 0, 0};
     switch (p.dtype) {
         case MSDA_F32:
-            return bwd_by_j<F32T, 1>(p, mp, value, loc, attn, grad_out, grad_value, workspace,
-                                     grad_loc, grad_attn, stream);
+            return bwd_by_j<F32T, 1, false>(p, mp, value, loc, attn, grad_out, grad_value,
+                                            workspace, grad_loc, grad_attn, none, stream);
         case MSDA_F16:
-            return mp.slot == 2 ? bwd_by_j<F16T, 2>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                    workspace, grad_loc, grad_attn, stream)
-                                : bwd_by_j<F16T, 1>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                    workspace, grad_loc, grad_attn, stream);
+            return mp.slot == 2
+                       ? bwd_by_j<F16T, 2, false>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                  workspace, grad_loc, grad_attn, none, stream)
+                       : bwd_by_j<F16T, 1, false>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                  workspace, grad_loc, grad_attn, none, stream);
         case MSDA_BF16:
-            return mp.slot == 2 ? bwd_by_j<BF16T, 2>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                     workspace, grad_loc, grad_attn, stream)
-                                : bwd_by_j<BF16T, 1>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                     workspace, grad_loc, grad_attn, stream);
+            return mp.slot == 2
+                       ? bwd_by_j<BF16T, 2, false>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                   workspace, grad_loc, grad_attn, none, stream)
+                       : bwd_by_j<BF16T, 1, false>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                   workspace, grad_loc, grad_attn, none, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_backward_binned(const Problem &p, const BwdMapping &mp, const void *value,
+                                  const void *loc, const void *attn, const void *grad_out,
+                                  const BinnedBuffers &bins, void *grad_loc, void *grad_attn,
+                                  hipStream_t stream) {
+    switch (p.dtype) {
+        case MSDA_F32:
+            return bwd_by_j<F32T, 1, true>(p, mp, value, loc, attn, grad_out, nullptr, nullptr,
+                                           grad_loc, grad_attn, bins, stream);
+        case MSDA_F16:
+            return mp.slot == 2
+                       ? bwd_by_j<F16T, 2, true>(p, mp, value, loc, attn, grad_out, nullptr,
+                                                 nullptr, grad_loc, grad_attn, bins, stream)
+                       : bwd_by_j<F16T, 1, true>(p, mp, value, loc, attn, grad_out, nullptr,
+                                                 nullptr, grad_loc, grad_attn, bins, stream);
+        case MSDA_BF16:
+            return mp.slot == 2
+                       ? bwd_by_j<BF16T, 2, true>(p, mp, value, loc, attn, grad_out, nullptr,
+                                                  nullptr, grad_loc, grad_attn, bins, stream)
+                       : bwd_by_j<BF16T, 1, true>(p, mp, value, loc, attn, grad_out, nullptr,
+                                                  nullptr, grad_loc, grad_attn, bins, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_bin_count(const Problem &p, const void *loc, const BinnedBuffers &bins,
+                            hipStream_t stream) {
+    const int64_t P = p.B * p.Q * p.M * p.L * p.K;
+    if (P == 0) return hipSuccess;
+    const int64_t blocks_needed = (P + kBlock - 1) / kBlock;
+    const int64_t grid = blocks_needed < 256 * 16 ? blocks_needed : 256 * 16;
+    const int64_t iters = (blocks_needed + grid - 1) / grid;
+    const uint32_t LK = (uint32_t)(p.L * p.K), QM = (uint32_t)(p.Q * p.M);
+#define MSDA_COUNT(T)                                                                          \
+    hipLaunchKernelGGL(bin_count_kernel<T>, dim3((unsigned)grid), dim3(kBlock), 0, stream,     \
+                       static_cast<const typename T::S *>(loc), p.levels, bins.starts,          \
+                       (uint32_t)P, LK, (uint32_t)p.K, (uint32_t)p.M, QM, p.nbbm, iters)
+    switch (p.dtype) {
+        case MSDA_F32: MSDA_COUNT(F32T); break;
+        case MSDA_F16: MSDA_COUNT(F16T); break;
+        case MSDA_BF16: MSDA_COUNT(BF16T); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef MSDA_COUNT
+    return hipGetLastError();
+}
+
+hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream) {
+    hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, bins.starts,
+                       bins.cursor, bins.nbins);
+    return hipGetLastError();
+}
+
+hipError_t launch_bin_accumulate(const Problem &p, const BwdMapping &mp, const void *grad_out,
+                                 void *grad_value, const BinnedBuffers &bins, bool accumulate,
+                                 hipStream_t stream) {
+    switch (p.dtype) {
+        case MSDA_F32: return accum_by_j<F32T, 1>(p, mp, grad_out, grad_value, bins, accumulate, stream);
+        case MSDA_F16:
+            return mp.slot == 2 ? accum_by_j<F16T, 2>(p, mp, grad_out, grad_value, bins, accumulate, stream)
+                                : accum_by_j<F16T, 1>(p, mp, grad_out, grad_value, bins, accumulate, stream);
+        case MSDA_BF16:
+            return mp.slot == 2 ? accum_by_j<BF16T, 2>(p, mp, grad_out, grad_value, bins, accumulate, stream)
+                                : accum_by_j<BF16T, 1>(p, mp, grad_out, grad_value, bins, accumulate, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -14,11 +14,17 @@ namespace msda {
 // scratch_off[l] >= 0: the backward accumulates level l's grad_value rows in
 // fp32 at workspace + scratch_off[l] (elements), laid out (B, H*W, M, D);
 // -1: atomics of the value dtype go straight into grad_value.
+//
+// Binned grad_value: the rows of level l of one (b, m) are cut into bins of
+// 2^bin_shift[l] pixel rows; bin_off[l] is the index of level l's first bin
+// among the nbbm bins of one (b, m).
 struct LevelTable {
     int32_t H[MSDA_MAX_LEVELS];
     int32_t W[MSDA_MAX_LEVELS];
     int64_t start[MSDA_MAX_LEVELS];
     int64_t scratch_off[MSDA_MAX_LEVELS];
+    int32_t bin_shift[MSDA_MAX_LEVELS];
+    int32_t bin_off[MSDA_MAX_LEVELS];
 };
 
 // Everything a launch needs, validated by the host layer.
@@ -26,6 +32,18 @@ struct Problem {
     int dtype;  // msda_dtype_t
     int64_t B, S, M, D, L, Q, K;
     LevelTable levels;
+    int64_t nbbm;  // bins per (b, m) of the binned grad_value (0: not planned)
+};
+
+// Workspace of the binned grad_value: starts[nbins + 1] (counts before the
+// scan), cursor[nbins], and one 8-byte record per in-bounds corner:
+// x = query << 10 | row within the bin, y = fp32 bits of A * w_ij.
+struct BinnedBuffers {
+    uint32_t *starts;
+    uint32_t *cursor;
+    uint2 *records;
+    int64_t nbins;
+    int max_bin_rows;  // largest 2^bin_shift, sizes the accumulation tile
 };
 
 // Forward lane mapping: each query's channels are spread over
@@ -60,6 +78,20 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
                            const void *loc, const void *attn, const void *grad_out,
                            void *grad_value, float *workspace, void *grad_loc, void *grad_attn,
                            hipStream_t stream);
+
+// Binned grad_value, in stream order: zero starts (launch_zero), count the
+// in-bounds corners per bin, scan counts into starts and cursors, run
+// launch_backward with `bins` (records instead of atomics), accumulate.
+hipError_t launch_bin_count(const Problem &p, const void *loc, const BinnedBuffers &bins,
+                            hipStream_t stream);
+hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream);
+hipError_t launch_backward_binned(const Problem &p, const BwdMapping &mp, const void *value,
+                                  const void *loc, const void *attn, const void *grad_out,
+                                  const BinnedBuffers &bins, void *grad_loc, void *grad_attn,
+                                  hipStream_t stream);
+hipError_t launch_bin_accumulate(const Problem &p, const BwdMapping &mp, const void *grad_out,
+                                 void *grad_value, const BinnedBuffers &bins, bool accumulate,
+                                 hipStream_t stream);
 
 // Fill `bytes` bytes (a multiple of 2) at `dst` with zeros.
 hipError_t launch_zero(void *dst, size_t bytes, hipStream_t stream);

@@ -104,10 +104,14 @@ def test_forward_given_start_index_may_differ_from_prefix(lib):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(accum=2), 4),
+    (dict(accum=4), 4),
+    (dict(accum=-2), 4),
     (dict(flags=8), 2),
-    (dict(gv=None), 1),
-    (dict(gout=None), 1),
+    (dict(flags=2), 2),  # scratch flags need an explicit scratch-capable mode
+    (dict(gv=None, accum=0), 1),
+    (dict(gout=None, accum=0), 1),
+    (dict(accum=3), 6),  # binned: workspace needed
+    (dict(dtype=2, accum=-1), 6),  # bf16 AUTO: per-level scratch needs a workspace
     (dict(dtype=2, accum=1), 6),  # scratch needed, no workspace
     (dict(dtype=2, accum=1, ws=ctypes.c_void_p(0x10000), ws_bytes=100), 6),
     (dict(dtype=2, accum=1, ws=ctypes.c_void_p(0x10008), ws_bytes=1 << 20), 5),
@@ -127,16 +131,40 @@ def test_workspace_size_and_accum_resolution(lib):
     assert lib.msda_backward_workspace_size(2, *prob, 1) == 1 * 100 * 2 * 8 * 4
     assert lib.msda_backward_workspace_size(2, *prob, 0) == 0
     assert lib.msda_backward_workspace_size(1, *prob, 1) == 1 * 100 * 2 * 8 * 4
-    assert lib.msda_backward_resolve_accum(0, *prob, -1) == 0
     assert lib.msda_backward_resolve_accum(2, *prob, 0) == 0
     assert lib.msda_backward_resolve_accum(2, *prob, 1) == 1
-    # bf16 AUTO: per level by contributions per pixel Q*K*4/(H*W):
-    # (8,10): 16*2*4/80 = 1.6 -> native; (4,5): 128/20 = 6.4 -> scratch
+    # PER_LEVEL: contributions per pixel Q*K*4/(H*W): (8,10): 1.6 -> packed
+    # atomics; (4,5): 6.4 -> fp32 scratch of 20 rows
+    assert lib.msda_backward_resolve_accum(2, *prob, 2) == 2
+    assert lib.msda_backward_workspace_size(2, *prob, 2) == 1 * 20 * 2 * 8 * 4
+    assert lib.msda_backward_resolve_accum(1, *prob, 2) == 2
+    assert lib.msda_backward_resolve_accum(0, *prob, 2) == 0  # fp32: nothing to switch
+    # AUTO: PER_LEVEL for bf16, NATIVE for fp16 and fp32
     assert lib.msda_backward_resolve_accum(2, *prob, -1) == 2
+    assert lib.msda_backward_resolve_accum(1, *prob, -1) == 0
+    assert lib.msda_backward_resolve_accum(0, *prob, -1) == 0
     assert lib.msda_backward_workspace_size(2, *prob, -1) == 1 * 20 * 2 * 8 * 4
-    assert lib.msda_backward_resolve_accum(1, *prob, -1) == 0  # fp16: native
+    # BINNED: 512 records per bin at 1.6 and 6.4 contributions per pixel ->
+    # 256- and 64-row bins -> one bin per level per (b, m): 4 bins; starts
+    # (5 x 4 B) and cursors (4 x 4 B) each padded to 256 B; records: 4 corners
+    # x 128 points x 8 B.
+    for dtype in (0, 1, 2):
+        assert lib.msda_backward_resolve_accum(dtype, *prob, 3) == 3
+        assert lib.msda_backward_workspace_size(dtype, *prob, 3) == 256 + 256 + 4 * 128 * 8
+    # BINNED does not apply to overlapping levels
+    over = (1, 100, 2, 8, 2, SHAPES, (ctypes.c_int64 * 2)(0, 70), 16, 2)
+    assert lib.msda_backward_resolve_accum(2, *over, 3) == -1 and lib.msda_last_error()
+    assert lib.msda_backward_workspace_size(2, *over, 3) == 0
     assert lib.msda_backward_resolve_accum(2, *prob, 7) == -1
     assert lib.msda_backward_workspace_size(9, *prob, 1) == 0 and lib.msda_last_error()
+
+
+def test_launch_event_instrumentation_validation(lib):
+    assert lib.msda_set_launch_events(None, 0) == 0
+    assert lib.msda_set_launch_events(None, 1) == 1
+    assert lib.msda_set_launch_events(None, 65) == 2
+    nulls = (ctypes.c_void_p * 2)(None, None)
+    assert lib.msda_set_launch_events(nulls, 2) == 1
 
 
 def test_python_binding_rejects_bad_tensors_on_cpu():

@@ -85,10 +85,11 @@ def _cached(name):
 
 
 @pytest.mark.parametrize("name,accum", [
-    ("tiny_fp32", "auto"),
+    ("tiny_fp32", "auto"), ("tiny_fp32", "binned"),
     ("decoder_bf16", "auto"), ("decoder_bf16", "native"), ("decoder_bf16", "fp32_scratch"),
-    ("encoder_fp16", "native"), ("encoder_fp16", "fp32_scratch"),
-    ("oddhead_fp32", "auto"),
+    ("decoder_bf16", "binned"),
+    ("encoder_fp16", "auto"), ("encoder_fp16", "fp32_scratch"), ("encoder_fp16", "binned"),
+    ("oddhead_fp32", "auto"), ("oddhead_fp32", "binned"),
 ])
 def test_workload_parity(name, accum):
     wl = workload(name)
@@ -98,13 +99,14 @@ def test_workload_parity(name, accum):
     full_check(inp, wl.dtype, accum, ref=ref)
 
 
-def test_large_encoder_parity():
+@pytest.mark.parametrize("accum", ["auto", "binned"])
+def test_large_encoder_parity(accum):
     name = "large_encoder_bf16"
     wl = workload(name)
-    say(f"case {name} accum=auto: B={wl.B} Q={wl.num_queries} M={wl.M} D={wl.D} "
+    say(f"case {name} accum={accum}: B={wl.B} Q={wl.num_queries} M={wl.M} D={wl.D} "
         f"L={wl.L} K={wl.K} {wl.dtype}")
     inp, ref = _cached(name)
-    full_check(inp, wl.dtype, "auto", ref=ref)
+    full_check(inp, wl.dtype, accum, ref=ref)
 
 
 def test_native_bf16_atomics_error_profile():
@@ -146,6 +148,7 @@ def test_head_dims_and_ragged_queries(dtype, D):
     wl, inp = _small(dtype, D=D)
     say(f"case head_dim D={D} {dtype} Q={wl.Q}")
     full_check(inp, dtype, "native")
+    full_check(inp, dtype, "binned")
     if dtype != torch.float32:
         full_check(inp, dtype, "fp32_scratch")
 
@@ -156,6 +159,7 @@ def test_widest_head_dim(dtype):
     wl, inp = _small(dtype, D=D, Q=9, M=2)
     say(f"case widest head_dim D={D} {dtype}")
     full_check(inp, dtype, "native")
+    full_check(inp, dtype, "binned")
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=str)
@@ -181,6 +185,8 @@ def test_custom_level_start_and_padding_rows(dtype):
     inp["value"] = torch.randn(B, S, M, D, generator=g).to(dtype)
     say(f"case custom level_start_index {starts.tolist()} S={S} {dtype}")
     full_check(inp, dtype, "native", starts=starts)
+    # binned: the padding rows belong to no bin and must come out zero
+    full_check(inp, dtype, "binned", starts=starts)
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=str)
@@ -213,6 +219,10 @@ def test_misaligned_pointers_fall_back_to_narrow_access(dtype):
     check_forward(dtype, out.cpu(), ref_out, touched)
     check_backward(dtype, (gv.cpu(), gl.cpu(), ga.cpu()), ref_grads, inp["spatial_shapes"], None,
                    trows)
+    msda_backward(v, g["spatial_shapes"], None, loc, a, go, accum="binned", **kw)
+    torch.cuda.synchronize()
+    check_backward(dtype, (gv.cpu(), gl.cpu(), ga.cpu()), ref_grads, inp["spatial_shapes"], None,
+                   trows)
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=str)
@@ -239,7 +249,7 @@ def test_empty_batch_and_queries(dtype):
     out = msda_forward(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
                        g["attention_weights"])
     assert out.shape == (wl.B, 0, wl.M * wl.D)
-    for accum in ("native", "fp32_scratch"):
+    for accum in ("native", "fp32_scratch", "auto", "binned"):
         gv = torch.full_like(g["value"], 7.0)
         gv, gl, ga = msda_backward(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
                                    g["attention_weights"], g["grad_output"], grad_value=gv,
@@ -293,7 +303,7 @@ def test_integer_aligned_points_reproduce_rows_exactly(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=str)
-@pytest.mark.parametrize("accum", ["native", "fp32_scratch"])
+@pytest.mark.parametrize("accum", ["native", "fp32_scratch", "binned"])
 def test_accumulate_flag_doubles_grad_value(dtype, accum):
     if dtype == torch.float32 and accum == "fp32_scratch":
         pytest.skip("identical to native for fp32")
@@ -318,13 +328,14 @@ def test_accumulate_flag_doubles_grad_value(dtype, accum):
 def test_deterministic_outputs(dtype):
     wl, inp = _small(dtype, D=32, Q=200)
     say(f"case determinism {dtype}")
-    out1, (gv1, gl1, ga1) = gpu_run(inp, "fp32_scratch" if dtype != torch.float32 else "native")
-    out2, (gv2, gl2, ga2) = gpu_run(inp, "fp32_scratch" if dtype != torch.float32 else "native")
-    assert torch.equal(out1, out2) and torch.equal(gl1, gl2) and torch.equal(ga1, ga2)
-    # grad_value: atomic order may differ; fp32 accumulation keeps runs within rounding
-    d = (gv1.double() - gv2.double()).abs().max().item()
-    scale = gv1.double().abs().max().item()
-    assert d <= 1e-6 * scale + (2.0 ** -8 if dtype != torch.float32 else 0.0) * scale
+    for accum in ("fp32_scratch" if dtype != torch.float32 else "native", "binned"):
+        out1, (gv1, gl1, ga1) = gpu_run(inp, accum)
+        out2, (gv2, gl2, ga2) = gpu_run(inp, accum)
+        assert torch.equal(out1, out2) and torch.equal(gl1, gl2) and torch.equal(ga1, ga2)
+        # grad_value: accumulation order may differ; fp32 sums keep runs within rounding
+        d = (gv1.double() - gv2.double()).abs().max().item()
+        scale = gv1.double().abs().max().item()
+        assert d <= 1e-6 * scale + (2.0 ** -8 if dtype != torch.float32 else 0.0) * scale
 
 
 def test_int64_indexing_beyond_2_pow_31_elements():
@@ -347,31 +358,35 @@ def test_int64_indexing_beyond_2_pow_31_elements():
         rep(last["grad_output"])
     shapes = last["spatial_shapes"]
     out = msda_forward(value, shapes, None, loc, attn)
-    gv, gl, ga = msda_backward(value, shapes, None, loc, attn, gout, accum="native")
     torch.cuda.synchronize()
     out_last = out[B - 1:].cpu()
-    gv_last = gv[B - 1:].cpu()
-    gl_last, ga_last = gl[B - 1:].cpu(), ga[B - 1:].cpu()
-    del value, gv, out
-    torch.cuda.empty_cache()
+    del out
     ref_out, touched, ref_grads, trows = oracle_run(last)
     check_forward(dtype, out_last, ref_out, touched)
-    check_backward(dtype, (gv_last, gl_last, ga_last), ref_grads, shapes, None, trows)
+    for accum in ("native", "binned"):
+        say(f"  backward accum={accum}")
+        gv, gl, ga = msda_backward(value, shapes, None, loc, attn, gout, accum=accum)
+        torch.cuda.synchronize()
+        gv_last = gv[B - 1:].cpu()
+        gl_last, ga_last = gl[B - 1:].cpu(), ga[B - 1:].cpu()
+        del gv, gl, ga
+        torch.cuda.empty_cache()
+        check_backward(dtype, (gv_last, gl_last, ga_last), ref_grads, shapes, None, trows)
 
 
-def test_decoder_bf16_default_accumulates_per_level():
+def test_accumulation_resolution_on_the_decoder_workload():
     from scale_deformable_attention_amd import msda_backward_resolve_accum
     inp = make_inputs(workload("decoder_bf16"), with_grad=False)
     g = to_dev(inp)
     say("case decoder_bf16 accumulation resolution")
-    mode = msda_backward_resolve_accum(g["value"], g["spatial_shapes"], None,
-                                       g["sampling_locations"], g["attention_weights"])
+    args = (g["value"], g["spatial_shapes"], None, g["sampling_locations"], g["attention_weights"])
     # contributions per pixel 300*4*4/(H*W): 0.29, 1.1 (packed bf16), 4.6, 17.6 (fp32 scratch)
-    assert mode == "per_level"
+    assert msda_backward_resolve_accum(*args) == "per_level"
+    assert msda_backward_resolve_accum(*args, accum="binned") == "binned"
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=str)
-@pytest.mark.parametrize("accum", ["auto", "fp32_scratch"])
+@pytest.mark.parametrize("accum", ["per_level", "fp32_scratch"])
 def test_micro_batches_accumulate_in_deferred_scratch(dtype, accum):
     """Two backward calls with different upstream gradients: the first leaves
     its fp32 sums in the workspace, the second continues them and adds once.
