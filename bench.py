@@ -26,10 +26,11 @@ C = in-bounds corners, N = B*S*M*D grad_value elements):
   forward          3*P*e (locations + weights) + B*Q*M*D*e (output) + U*D*e
   backward kernel  3*P*e (params) + B*Q*M*D*e (grad_output) + U*D*e (value)
                    + 3*P*e (grad locations + grad weights)
-                   + binned: 8*C (records written)
-                   + atomics: 2*U*D*e_acc (read-modify-write of touched rows;
-                     e_acc = 4 for rows of levels accumulated in fp32 scratch)
-  bin count        2*P*e;  bin accumulate  8*C + B*Q*M*D*e + N*e
+                   + atomics: 2*U'*D*e_acc (read-modify-write of the touched rows
+                     of levels not binned; e_acc = 4 for fp32 rows)
+  binned levels only (P', C', N' = their points, corners, grad_value elements):
+  bin count        2*P'*e;  bin place  3*P'*e + 8*C' (records written)
+  bin accumulate   8*C' + B*Q*M*D*e + N'*e
   zero fill        bytes written;  scratch add  rows * D * (4 + 2e)
 """
 
@@ -176,7 +177,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decoder_bf16")
     ap.add_argument("--accum", default="auto",
-                    choices=["auto", "native", "fp32_scratch", "per_level", "binned"])
+                    choices=["auto", "native", "fp32_scratch", "per_level", "binned", "mixed"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-only", action="store_true",
@@ -294,7 +295,10 @@ def main():
         n_bwd = launch_events_recorded() // 2
     torch.cuda.synchronize()
     bwd_names = {
-        "binned": ["bin_zero", "bin_count", "bin_scan", "msda_bwd_kernel", "bin_accum_kernel"],
+        "binned": ["bin_zero", "bin_count", "bin_scan", "bin_place", "msda_bwd_kernel",
+                   "bin_accum_kernel"],
+        "mixed": ["zero_fill", "bin_zero", "bin_count", "bin_scan", "bin_place", "msda_bwd_kernel",
+                  "bin_accum_kernel"],
         "native": ["zero_fill", "msda_bwd_kernel"],
         "per_level": ["zero_fill", "scratch_zero", "msda_bwd_kernel", "scratch_add_kernel"],
         "fp32_scratch": ["zero_fill", "scratch_zero", "msda_bwd_kernel", "scratch_add_kernel"],
@@ -315,21 +319,24 @@ def main():
     P = B * Q * M * L * Kp
     N = B * S * M * D
     U, C = touched_rows(inp)
-    scr_levels = call.scratch_levels()
+    level_modes, nb = call.plan()
+    scr_levels = [l for l, m in enumerate(level_modes) if m == "fp32_scratch"]
+    bin_levels = [l for l, m in enumerate(level_modes) if m == "binned"]
     U_scr = touched_rows(inp, only_levels=scr_levels)[0] if scr_levels else 0
+    U_bin, C_bin = touched_rows(inp, only_levels=bin_levels) if bin_levels else (0, 0)
     scratch_rows = sum(B * h * w * M for l, (h, w) in enumerate(wl.levels) if l in scr_levels)
+    bin_rows = sum(B * h * w * M for l, (h, w) in enumerate(wl.levels) if l in bin_levels)
+    P_bin = B * Q * M * Kp * len(bin_levels)
     common = 3 * P * e + B * Q * M * D * e + U * D * e + 3 * P * e
+    e_acc = 4 if wl.dtype == torch.float32 else e
     kbytes = {"msda_fwd_kernel": 3 * P * e + B * Q * M * D * e + U * D * e,
-              "bin_count": 2 * P * e, "bin_accum_kernel": 8 * C + B * Q * M * D * e + N * e,
               "zero_fill": N * e, "scratch_zero": scratch_rows * D * 4,
-              "scratch_add_kernel": scratch_rows * D * (4 + 2 * e)}
-    if call.resolved_accum == "binned":
-        nb = call.bin_count()
-        kbytes.update({"bin_zero": (nb + 1) * 4, "bin_scan": 3 * nb * 4,
-                       "msda_bwd_kernel": common + 8 * C})
-    else:
-        e_acc = 4 if wl.dtype == torch.float32 else e
-        kbytes["msda_bwd_kernel"] = common + 2 * ((U - U_scr) * D * e_acc + U_scr * D * 4)
+              "scratch_add_kernel": scratch_rows * D * (4 + 2 * e),
+              # atomics: read-modify-write of the touched rows of unbinned levels
+              "msda_bwd_kernel": common + 2 * ((U - U_scr - U_bin) * D * e_acc + U_scr * D * 4),
+              "bin_zero": (nb + 1) * 4, "bin_count": 2 * P_bin * e, "bin_scan": 3 * nb * 4,
+              "bin_place": 3 * P_bin * e + 8 * C_bin,
+              "bin_accum_kernel": 8 * C_bin + B * Q * M * D * e + bin_rows * D * e}
     kernels = {k: {"us": round(v, 3), "bytes": int(kbytes[k]),
                    "GBps": round(kbytes[k] / (v * 1e-6) / 1e9, 1)} for k, v in ktimes.items()}
     kname = max(ktimes, key=ktimes.get)

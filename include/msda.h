@@ -85,13 +85,15 @@ typedef enum msda_dtype {
  *   BINNED        no float atomics: every in-bounds corner becomes an 8-byte
  *                 record in the bin of its destination rows (count, scan,
  *                 place), and one workgroup per bin sums its records in fp32
- *                 and writes the bin's grad_value rows once. Needs
- *                 non-overlapping levels, Q < 2^22 and a batch slice of value
- *                 below 2 GiB; the workspace holds 8 bytes per point corner;
- *   AUTO          PER_LEVEL for bf16, NATIVE for fp16 / fp32: the fastest
- *                 measured paths that hold the parity bars. BINNED rounds
- *                 every grad_value element once, with no global float
- *                 atomics, but measures 2-4x slower on MI355X.
+ *                 and writes the bin's grad_value rows once, rounded once.
+ *                 Needs non-overlapping levels and batch slices of value and
+ *                 grad_output below 2 GiB; the workspace holds 8 bytes per
+ *                 corner of every binned level's points;
+ *   MIXED         BINNED for the levels above 4 contributions per pixel,
+ *                 native atomics for the others (same conditions as BINNED);
+ *   AUTO          MIXED where binning applies (which is BINNED when every
+ *                 level is above the threshold, NATIVE when none is), else
+ *                 PER_LEVEL for bf16 and NATIVE for fp16 / fp32.
  * A scratch level is laid out (B, H_l*W_l, M, D) in fp32. grad_value is the
  * fp32 sum rounded once to the value dtype except for levels accumulated with
  * packed 16-bit atomics, which round every add. */
@@ -100,8 +102,16 @@ typedef enum msda_accum {
     MSDA_ACCUM_NATIVE = 0,
     MSDA_ACCUM_FP32_SCRATCH = 1,
     MSDA_ACCUM_PER_LEVEL = 2,
-    MSDA_ACCUM_BINNED = 3
+    MSDA_ACCUM_BINNED = 3,
+    MSDA_ACCUM_MIXED = 4
 } msda_accum_t;
+
+/* How msda_backward accumulates one level's grad_value rows. */
+typedef enum msda_level_mode {
+    MSDA_LEVEL_NATIVE = 0,        /* atomics of the value dtype       */
+    MSDA_LEVEL_FP32_SCRATCH = 1,  /* fp32 atomics into the workspace  */
+    MSDA_LEVEL_BINNED = 2         /* records, summed per bin          */
+} msda_level_mode_t;
 
 typedef enum msda_status {
     MSDA_OK = 0,
@@ -156,9 +166,10 @@ size_t msda_backward_workspace_size(int dtype, int64_t batch, int64_t num_keys,
 
 /*
  * The accumulation msda_backward will use for `accum` on this problem:
- * BINNED, NATIVE (no level uses scratch; always the case for fp32 data
- * outside BINNED), FP32_SCRATCH (every level does), PER_LEVEL (some levels
- * do), or -1 on invalid arguments (and for BINNED where it cannot apply).
+ * BINNED (every level binned), MIXED (some levels), NATIVE (no level uses
+ * scratch or bins; always the case for fp32 data without bins), FP32_SCRATCH
+ * (every level uses scratch), PER_LEVEL (some levels do), or -1 on invalid
+ * arguments (and for BINNED / MIXED where binning cannot apply).
  */
 int msda_backward_resolve_accum(int dtype, int64_t batch, int64_t num_keys,
                                 int64_t num_heads, int64_t head_dim,
@@ -167,13 +178,24 @@ int msda_backward_resolve_accum(int dtype, int64_t batch, int64_t num_keys,
                                 int64_t num_queries, int64_t num_points, int accum);
 
 /*
+ * The per-level plan behind msda_backward_resolve_accum: writes
+ * msda_level_mode_t values to level_modes[0:L] (a host array, or NULL) and
+ * returns the number of grad_value bins (0 when no level is binned), or -1 on
+ * invalid arguments. Host-only, needs no GPU.
+ */
+int64_t msda_backward_plan(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
+                           int64_t head_dim, int64_t num_levels, const int64_t *spatial_shapes,
+                           const int64_t *level_start_index, int64_t num_queries,
+                           int64_t num_points, int accum, int *level_modes);
+
+/*
  * Backward, given grad_output (B, Q, M, D). Writes every element of
  * grad_sampling_locations and grad_attention_weights; grad_value is
  * zero-filled and then accumulated into (or only accumulated into, with
  * MSDA_FLAG_ACCUMULATE_GRAD_VALUE). `workspace` must hold at least
  * msda_backward_workspace_size(...) bytes, 16-byte aligned (NULL if 0).
- * grad_value is bitwise nondeterministic run to run (atomic order); the two
- * other gradients are deterministic.
+ * grad_value is bitwise nondeterministic run to run (the order of atomics,
+ * or of records within a bin); the two other gradients are deterministic.
  * B == 0: returns MSDA_OK. Q == 0: only the grad_value zero-fill runs.
  */
 int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,

@@ -21,9 +21,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmsda_amd.so")
 
 MSDA_F32, MSDA_F16, MSDA_BF16 = 0, 1, 2
-ACCUM_AUTO, ACCUM_NATIVE, ACCUM_FP32_SCRATCH, ACCUM_PER_LEVEL, ACCUM_BINNED = -1, 0, 1, 2, 3
+ACCUM_AUTO, ACCUM_NATIVE, ACCUM_FP32_SCRATCH, ACCUM_PER_LEVEL, ACCUM_BINNED, ACCUM_MIXED = \
+    -1, 0, 1, 2, 3, 4
 _RESOLVED = {ACCUM_NATIVE: "native", ACCUM_FP32_SCRATCH: "fp32_scratch", ACCUM_PER_LEVEL: "per_level",
-             ACCUM_BINNED: "binned"}
+             ACCUM_BINNED: "binned", ACCUM_MIXED: "mixed"}
+LEVEL_MODES = {0: "native", 1: "fp32_scratch", 2: "binned"}
 FLAG_ACCUMULATE_GRAD_VALUE = 1
 FLAG_CONTINUE_SCRATCH = 2
 FLAG_DEFER_SCRATCH = 4
@@ -32,11 +34,12 @@ MAX_LEVELS = 16
 _DTYPE_CODES = {torch.float32: MSDA_F32, torch.float16: MSDA_F16, torch.bfloat16: MSDA_BF16}
 _ACCUM_CODES = {"auto": ACCUM_AUTO, None: ACCUM_AUTO, "native": ACCUM_NATIVE, False: ACCUM_NATIVE,
                 "fp32_scratch": ACCUM_FP32_SCRATCH, True: ACCUM_FP32_SCRATCH,
-                "per_level": ACCUM_PER_LEVEL, "binned": ACCUM_BINNED}
+                "per_level": ACCUM_PER_LEVEL, "binned": ACCUM_BINNED, "mixed": ACCUM_MIXED}
 
 # every symbol include/msda.h declares
 EXPORTED_SYMBOLS = ("msda_forward", "msda_backward", "msda_backward_workspace_size",
-                    "msda_backward_resolve_accum", "msda_status_string", "msda_last_error",
+                    "msda_backward_resolve_accum", "msda_backward_plan", "msda_status_string",
+                    "msda_last_error",
                     "msda_abi_version", "msda_set_launch_events", "msda_launch_events_recorded")
 
 _lib = None
@@ -68,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msda_backward_workspace_size.restype = sz
     lib.msda_backward_resolve_accum.argtypes = prob + [i32]
     lib.msda_backward_resolve_accum.restype = i32
+    lib.msda_backward_plan.argtypes = prob + [i32, ctypes.POINTER(ctypes.c_int)]
+    lib.msda_backward_plan.restype = i64
     lib.msda_status_string.argtypes = [i32]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_last_error.argtypes = []
@@ -320,34 +325,26 @@ class PreparedCall:
         self.resolved_accum = _RESOLVED.get(
             int(self.lib.msda_backward_resolve_accum(*self.prob, self.accum_code)))
 
+    def plan(self):
+        """(per-level accumulation names, number of grad_value bins) of this
+        call's backward, as the library plans it."""
+        modes = (ctypes.c_int * self.levels.L)()
+        nb = int(self.lib.msda_backward_plan(*self.prob, self.accum_code, modes))
+        if nb < 0:
+            raise MSDAError(8, self.lib.msda_last_error().decode())
+        return [LEVEL_MODES[int(m)] for m in modes], nb
+
     def bin_count(self) -> int:
-        """Number of grad_value bins of the binned accumulation (its layout
-        rule: about 512 records per bin, at most 32 KiB of fp32 tile)."""
-        B, Q, M, L, K, _ = self.loc.shape
-        D = self.value.shape[3]
-        tp_max = 1
-        while tp_max * 2 <= 1024 and tp_max * 2 * D * 4 <= 32768:
-            tp_max *= 2
-        nbbm = 0
-        for h, w in self.levels.shapes.tolist():
-            c = Q * K * 4 / (h * w)
-            want = 512.0 / c if c > 0 else tp_max
-            tp = 1
-            while tp * 2 <= tp_max and tp * 2 <= want:
-                tp *= 2
-            nbbm += (h * w + tp - 1) // tp
-        return B * M * nbbm
+        """Number of grad_value bins of the binned levels (0 if none)."""
+        return self.plan()[1]
 
     def scratch_levels(self):
-        """Levels whose grad_value rows the backward accumulates in fp32 scratch
-        under this call's accumulation mode (same rule as the library)."""
-        if self.value.dtype == torch.float32 or self.resolved_accum in ("native", "binned"):
-            return []
-        L = self.levels.L
-        if self.resolved_accum == "fp32_scratch":
-            return list(range(L))
-        B, Q, M, _, K, _ = self.loc.shape
-        return [l for l, (h, w) in enumerate(self.levels.shapes.tolist()) if Q * K * 4 / (h * w) > 4.0]
+        """Levels whose grad_value rows the backward accumulates in fp32 scratch."""
+        return [l for l, m in enumerate(self.plan()[0]) if m == "fp32_scratch"]
+
+    def binned_levels(self):
+        """Levels whose grad_value rows the backward sums through bins."""
+        return [l for l, m in enumerate(self.plan()[0]) if m == "binned"]
 
     def forward(self) -> torch.Tensor:
         _check(self.lib.msda_forward(*self._fwd_args, _stream(self.device, self._stream_arg)))

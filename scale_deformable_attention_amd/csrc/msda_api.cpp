@@ -113,7 +113,10 @@ int make_problem(int dtype, int64_t B, int64_t S, int64_t M, int64_t D, int64_t 
     p->Q = Q;
     p->K = K;
     memset(&p->levels, 0, sizeof(p->levels));
-    for (int l = 0; l < MSDA_MAX_LEVELS; ++l) p->levels.scratch_off[l] = -1;
+    for (int l = 0; l < MSDA_MAX_LEVELS; ++l) {
+        p->levels.scratch_off[l] = -1;
+        p->levels.bin_shift[l] = -1;
+    }
     p->nbbm = 0;
     int64_t acc = 0;
     for (int64_t l = 0; l < L; ++l) {
@@ -214,14 +217,25 @@ double contributions_per_pixel(const msda::Problem &p, int l) {
            ((double)p.levels.H[l] * (double)p.levels.W[l]);
 }
 
+int binned_levels(const msda::Problem &p) {
+    int n = 0;
+    for (int l = 0; l < (int)p.L; ++l) n += p.levels.bin_shift[l] >= 0;
+    return n;
+}
+
 int resolved_mode(const msda::Problem &p) {
+    const int nb = binned_levels(p);
+    if (nb > 0) return nb == (int)p.L ? MSDA_ACCUM_BINNED : MSDA_ACCUM_MIXED;
     int n = 0;
     for (int l = 0; l < (int)p.L; ++l) n += p.levels.scratch_off[l] >= 0;
     if (n == 0) return MSDA_ACCUM_NATIVE;
     return n == (int)p.L ? MSDA_ACCUM_FP32_SCRATCH : MSDA_ACCUM_PER_LEVEL;
 }
 
-bool valid_accum(int accum) { return accum >= MSDA_ACCUM_AUTO && accum <= MSDA_ACCUM_BINNED; }
+bool valid_accum(int accum) { return accum >= MSDA_ACCUM_AUTO && accum <= MSDA_ACCUM_MIXED; }
+
+// A level is "contended" above this many contributions per pixel.
+constexpr double kContended = 4.0;
 
 // Decide, per level, whether the backward accumulates in fp32 scratch, and
 // lay the scratch blocks out back to back. Returns the workspace bytes.
@@ -235,7 +249,7 @@ size_t plan_scratch(msda::Problem *p, int mode) {
         bool scratch = false;
         if (p->dtype != MSDA_F32) {
             if (mode == MSDA_ACCUM_FP32_SCRATCH) scratch = true;
-            else if (mode == MSDA_ACCUM_PER_LEVEL) scratch = contributions_per_pixel(*p, l) > 4.0;
+            else if (mode == MSDA_ACCUM_PER_LEVEL) scratch = contributions_per_pixel(*p, l) > kContended;
         }
         if (scratch) {
             p->levels.scratch_off[l] = (int64_t)(total / sizeof(float));
@@ -267,48 +281,55 @@ bool levels_leave_gaps(const msda::Problem &p) {
     return covered != p.S;  // levels do not overlap here, so equality covers [0, S)
 }
 
-// Binned grad_value plan: per level a bin height of 2^bin_shift pixel rows so
-// that a bin holds about kBinRecords records if the level's points spread
-// evenly (contributions per pixel Q*K*4 / (H*W)), capped so that the fp32 LDS
-// tile of a bin stays within 32 KiB. Returns false where the path cannot
-// apply; on success fills the level table and the workspace layout.
-constexpr double kBinRecords = 512.0;
+// Binned grad_value plan: per level a bin height of 2^bin_shift pixel rows,
+// at most 16, so that a bin holds about kBinRecords records if the level's
+// points spread evenly (contributions per pixel Q*K*4 / (H*W)). Returns false
+// where the path cannot apply; on success fills the level table and the
+// workspace layout.
+constexpr double kBinRecords = 1024.0;
 
 struct BinPlan {
     int64_t nbins = 0, records = 0;
-    int max_rows = 0;
     size_t starts_off = 0, cursor_off = 0, records_off = 0, bytes = 0;
 };
 
-bool plan_bins(msda::Problem *p, BinPlan *bp) {
+// Bins the levels selected by `contended_only` (all levels, or those above
+// kContended contributions per pixel); the other levels keep bin_shift = -1.
+bool plan_bins(msda::Problem *p, BinPlan *bp, bool contended_only) {
     const int64_t e = p->dtype == MSDA_F32 ? 4 : 2;
     const int64_t P = p->B * p->Q * p->M * p->L * p->K;
-    if (levels_overlap(*p) || p->Q >= ((int64_t)1 << 22) || 4 * P >= ((int64_t)1 << 32) ||
-        p->S * p->M * p->D * e > ((int64_t)1 << 31) - 64 || p->B * p->Q * p->M >= ((int64_t)1 << 31))
+    // 28-bit query field; 32-bit record indices; buffer-addressed value and
+    // grad_output slices of one batch
+    if (levels_overlap(*p) || p->Q >= ((int64_t)1 << 28) || 4 * P >= ((int64_t)1 << 32) ||
+        p->S * p->M * p->D * e > ((int64_t)1 << 31) - 64 ||
+        p->Q * p->M * p->D * e > ((int64_t)1 << 31) - 64 || p->B * p->Q * p->M >= ((int64_t)1 << 31))
         return false;
-    int tp_max = 1;
-    while (tp_max * 2 <= 1024 && (int64_t)tp_max * 2 * p->D * 4 <= 32768) tp_max *= 2;
+    // rows per bin: a power of two, at most the 16 lane groups of the
+    // accumulating workgroup (each sums one row, or one replica of a row)
+    const int tp_max = 16;
     int64_t nbbm = 0;
-    int max_rows = 1;
+    int nlev = 0;
     for (int l = 0; l < (int)p->L; ++l) {
         const double c = contributions_per_pixel(*p, l);
+        p->levels.bin_off[l] = (int32_t)nbbm;  // a level without bins shares the next level's offset
+        p->levels.bin_shift[l] = -1;
+        if (contended_only && !(c > kContended)) continue;
         const double want = c > 0 ? kBinRecords / c : (double)tp_max;
-        int sh = 0;
-        while ((1 << (sh + 1)) <= tp_max && (double)(1 << (sh + 1)) <= want) ++sh;
         const int64_t HW = (int64_t)p->levels.H[l] * p->levels.W[l];
+        int sh = 0;  // no taller than the level itself rounded up to a power of two
+        while ((1 << (sh + 1)) <= tp_max && (double)(1 << (sh + 1)) <= want &&
+               ((int64_t)1 << sh) < HW)
+            ++sh;
         p->levels.bin_shift[l] = sh;
-        p->levels.bin_off[l] = (int32_t)nbbm;
         nbbm += (HW + (1 << sh) - 1) >> sh;
-        const int rows = (int)(HW < (1 << sh) ? HW : (1 << sh));
-        if (rows > max_rows) max_rows = rows;
+        ++nlev;
         if (nbbm >= ((int64_t)1 << 31)) return false;
     }
     const int64_t nbins = p->B * p->M * nbbm;
     if (nbins >= ((int64_t)1 << 31) - 1) return false;
     p->nbbm = nbbm;
     bp->nbins = nbins;
-    bp->records = 4 * P;
-    bp->max_rows = max_rows;
+    bp->records = 4 * p->B * p->Q * p->M * p->K * nlev;
     bp->starts_off = 0;
     bp->cursor_off = align_up((size_t)(nbins + 1) * 4, 256);
     bp->records_off = bp->cursor_off + align_up((size_t)nbins * 4, 256);
@@ -316,20 +337,35 @@ bool plan_bins(msda::Problem *p, BinPlan *bp) {
     return true;
 }
 
-// Resolve `accum` and plan the buffers. Returns the resolved mode, or -1 if
-// an explicit BINNED cannot apply. *bytes = workspace bytes needed.
-// AUTO is PER_LEVEL for bf16 and NATIVE otherwise: measured on MI355X, the
-// binned path's shared per-bin counters serialise (hundreds of increments per
-// address on the decoder workload) and its per-bin accumulation is latency
-// bound, so it is 2-4x slower than the segment-coalesced atomics.
-int plan_accum(msda::Problem *p, int accum, size_t *bytes, BinPlan *bp) {
-    int mode = accum;
-    if (accum == MSDA_ACCUM_BINNED) {
-        if (!plan_bins(p, bp)) return -1;
-        plan_scratch(p, MSDA_ACCUM_NATIVE);
-        *bytes = bp->bytes;
-        return MSDA_ACCUM_BINNED;
+void clear_bins(msda::Problem *p) {
+    for (int l = 0; l < MSDA_MAX_LEVELS; ++l) {
+        p->levels.bin_shift[l] = -1;
+        p->levels.bin_off[l] = 0;
     }
+    p->nbbm = 0;
+}
+
+// Resolve `accum` and plan the buffers. Returns the resolved mode, or -1 if
+// an explicit BINNED / MIXED cannot apply. *bytes = workspace bytes needed.
+// AUTO is MIXED where binning applies (BINNED when every level is contended,
+// NATIVE when none is), else PER_LEVEL for bf16 and NATIVE otherwise.
+// Measured on MI355X: native atomics are fastest on levels whose pixels
+// receive a few contributions; on contended levels they serialise on the same
+// addresses (and bf16 adds lose precision), where the binned sum wins.
+int plan_accum(msda::Problem *p, int accum, size_t *bytes, BinPlan *bp) {
+    clear_bins(p);
+    plan_scratch(p, MSDA_ACCUM_NATIVE);
+    *bytes = 0;
+    if (accum == MSDA_ACCUM_BINNED || accum == MSDA_ACCUM_MIXED || accum == MSDA_ACCUM_AUTO) {
+        if (plan_bins(p, bp, accum != MSDA_ACCUM_BINNED)) {
+            if (bp->nbins > 0) *bytes = bp->bytes;
+            else clear_bins(p);
+            return resolved_mode(*p);
+        }
+        clear_bins(p);
+        if (accum != MSDA_ACCUM_AUTO) return -1;
+    }
+    int mode = accum;
     if (accum == MSDA_ACCUM_AUTO)
         mode = p->dtype == MSDA_BF16 ? MSDA_ACCUM_PER_LEVEL : MSDA_ACCUM_NATIVE;
     *bytes = plan_scratch(p, mode);
@@ -453,6 +489,32 @@ int msda_backward_resolve_accum(int dtype, int64_t batch, int64_t num_keys, int6
     return mode;
 }
 
+int64_t msda_backward_plan(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
+                           int64_t head_dim, int64_t num_levels, const int64_t *spatial_shapes,
+                           const int64_t *level_start_index, int64_t num_queries,
+                           int64_t num_points, int accum, int *level_modes) {
+    msda::Problem p;
+    if (make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
+                     level_start_index, num_queries, num_points, &p))
+        return -1;
+    if (!valid_accum(accum)) {
+        fail(MSDA_ERR_DTYPE, "unknown accumulation mode %d", accum);
+        return -1;
+    }
+    size_t bytes;
+    BinPlan bp;
+    if (plan_accum(&p, accum, &bytes, &bp) < 0) {
+        fail(MSDA_ERR_UNSUPPORTED, "binned accumulation does not apply to this problem");
+        return -1;
+    }
+    if (level_modes)
+        for (int l = 0; l < (int)p.L; ++l)
+            level_modes[l] = p.levels.bin_shift[l] >= 0    ? MSDA_LEVEL_BINNED
+                             : p.levels.scratch_off[l] >= 0 ? MSDA_LEVEL_FP32_SCRATCH
+                                                            : MSDA_LEVEL_NATIVE;
+    return binned_levels(p) > 0 ? bp.nbins : 0;
+}
+
 size_t msda_backward_workspace_size(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                                     int64_t head_dim, int64_t num_levels,
                                     const int64_t *spatial_shapes,
@@ -505,7 +567,8 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
     const int mode = plan_accum(&p, accum, &need, &bp);
     if (mode < 0)
         return fail(MSDA_ERR_UNSUPPORTED, "binned accumulation does not apply to this problem");
-    const bool binned = mode == MSDA_ACCUM_BINNED;
+    const bool binned = mode == MSDA_ACCUM_BINNED || mode == MSDA_ACCUM_MIXED;
+    const bool all_binned = mode == MSDA_ACCUM_BINNED;
     if ((st = check_ptr(value, "value", dtype))) return st;
     if ((st = check_ptr(grad_value, "grad_value", dtype))) return st;
     if (need) {
@@ -516,7 +579,7 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
     }
     // Native half-precision atomics update aligned 4-byte pairs; every pair
     // must lie inside grad_value.
-    if (!binned && mode != MSDA_ACCUM_FP32_SCRATCH && dtype != MSDA_F32 &&
+    if (!all_binned && mode != MSDA_ACCUM_FP32_SCRATCH && dtype != MSDA_F32 &&
         (!aligned(grad_value, 4) || (p.B * p.S * p.M * p.D) % 2 != 0))
         return fail(MSDA_ERR_ALIGN,
                     "native half-precision atomics need a 4-byte aligned grad_value with an even "
@@ -535,9 +598,10 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
     const size_t gv_bytes = (size_t)(p.B * p.S * p.M * p.D) * elem_size(dtype);
     hipError_t err;
     if (binned) {
-        // Rows outside every level are written by no bin: zero all of
-        // grad_value first when there are such rows (or no queries at all).
-        if (!accumulate && (p.Q == 0 || levels_leave_gaps(p)) &&
+        // Rows outside every binned level are written by no bin: zero all of
+        // grad_value first when there are such rows (padding rows, levels
+        // left to atomics, or no queries at all).
+        if (!accumulate && (p.Q == 0 || !all_binned || levels_leave_gaps(p)) &&
             (err = marked(msda::launch_zero(grad_value, gv_bytes, before(s)), s)) != hipSuccess)
             return hip_fail(err, "grad_value zero fill");
         if (p.Q == 0) return ok();
@@ -547,20 +611,32 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
         bins.cursor = reinterpret_cast<uint32_t *>(ws + bp.cursor_off);
         bins.records = reinterpret_cast<uint2 *>(ws + bp.records_off);
         bins.nbins = bp.nbins;
-        bins.max_bin_rows = bp.max_rows;
         // the counts (starts[0:nbins]) start at zero; the fill works in
         // 2-byte units, so round the byte count up to an even number of them
         if ((err = marked(msda::launch_zero(bins.starts, align_up((size_t)(bp.nbins + 1) * 4, 16), before(s)), s)) !=
             hipSuccess)
             return hip_fail(err, "bin count zero fill");
-        if ((err = marked(msda::launch_bin_count(p, sampling_locations, bins, before(s)), s)) != hipSuccess)
+        if ((err = marked(msda::launch_bin_sort(p, sampling_locations, attention_weights, bins,
+                                                false, before(s)),
+                          s)) != hipSuccess)
             return hip_fail(err, "bin count launch");
         if ((err = marked(msda::launch_bin_scan(bins, before(s)), s)) != hipSuccess)
             return hip_fail(err, "bin scan launch");
-        if ((err = marked(msda::launch_backward_binned(p, mp, value, sampling_locations,
-                                                       attention_weights, grad_output, bins,
-                                                       grad_sampling_locations,
-                                                       grad_attention_weights, before(s)),
+        if ((err = marked(msda::launch_bin_sort(p, sampling_locations, attention_weights, bins,
+                                                true, before(s)),
+                          s)) != hipSuccess)
+            return hip_fail(err, "bin place launch");
+        // every level binned: the backward writes only grad_loc / grad_attn;
+        // otherwise it adds the unbinned levels' grad_value with atomics
+        if ((err = marked(all_binned
+                              ? msda::launch_backward_binned(p, mp, value, sampling_locations,
+                                                             attention_weights, grad_output,
+                                                             grad_sampling_locations,
+                                                             grad_attention_weights, before(s))
+                              : msda::launch_backward(p, mp, value, sampling_locations,
+                                                      attention_weights, grad_output, grad_value,
+                                                      nullptr, grad_sampling_locations,
+                                                      grad_attention_weights, before(s)),
                           s)) != hipSuccess)
             return hip_fail(err, "backward launch");
         if ((err = marked(msda::launch_bin_accumulate(p, mp, grad_output, grad_value, bins,

@@ -302,53 +302,6 @@ __device__ __forceinline__ Cell map_cell(float loc_x, float loc_y, float Hf, flo
     return c;
 }
 
-// ------------------------------------------------- wave-aggregated counters
-//
-// Adds 1 to ctr[key] for every lane with `ok`, one atomic per distinct key in
-// the wave (the first pending lane leads; lanes with its key join). With
-// RETURN the lane gets the slot old_value + rank-among-equal-keys. All 64
-// lanes must call it together.
-template <bool RETURN>
-__device__ __forceinline__ uint32_t wave_aggregate(uint32_t *ctr, uint32_t key, bool ok) {
-    uint32_t slot = 0;
-    bool pending = ok;
-    const int lane = (int)(threadIdx.x & 63);
-    while (true) {
-        const uint64_t act = __ballot(pending);
-        if (!act) break;
-        const int leader = (int)__builtin_ctzll(act);
-        const uint32_t lkey = __builtin_amdgcn_readlane(key, leader);
-        const bool mine = pending && key == lkey;
-        const uint64_t same = __ballot(mine);
-        uint32_t base = 0;
-        if (lane == leader) {
-            if constexpr (RETURN)
-                base = __hip_atomic_fetch_add(ctr + lkey, (uint32_t)__popcll(same), __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-            else
-                __hip_atomic_fetch_add(ctr + lkey, (uint32_t)__popcll(same), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if constexpr (RETURN) {
-            base = __builtin_amdgcn_readlane(base, leader);
-            const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
-                (uint32_t)(same >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)same, 0u));
-            if (mine) slot = base + rank;
-        }
-        if (mine) pending = false;
-    }
-    return slot;
-}
-
-// Bin of pixel row `row` (absolute, within level l) of head m of batch b.
-__device__ __forceinline__ uint32_t bin_of(const LevelTable &lt, int l, int64_t b, int m, int M,
-                                          int64_t nbbm, int64_t row, uint32_t *row_in_bin) {
-    const int64_t rel = row - lt.start[l];
-    const int sh = lt.bin_shift[l];
-    *row_in_bin = (uint32_t)(rel & ((1 << sh) - 1));
-    return (uint32_t)((b * M + m) * nbbm + lt.bin_off[l] + (rel >> sh));
-}
-
 // ------------------------------------------------------------- forward
 //
 // A lane group handles the points p = i * split + s (i = 0, 1, ...) of its
@@ -498,7 +451,7 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
     typename DT::S *__restrict__ grad_loc, typename DT::S *__restrict__ grad_attn,
     const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
     const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
-    const int log2s, const BinnedBuffers bins, const int64_t nbbm) {
+    const int log2s) {
     using E = typename DT::S;
     using R = typename RawVec<SLOT * (int)sizeof(E)>::type;  // one slot
     constexpr bool kF32 = sizeof(E) == 4;
@@ -631,7 +584,8 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
                 grad_loc[2 * pp] = from_f32(DT{}, (float)lt.W[l] * aw[t] * dx[t]);
                 grad_loc[2 * pp + 1] = from_f32(DT{}, (float)lt.H[l] * aw[t] * dy[t]);
             }
-            if constexpr (BIN) continue;  // grad_value goes through records below
+            if constexpr (BIN) continue;  // grad_value: binned kernels
+            if (lt.bin_shift[l] >= 0) continue;  // this level is binned
             const int W = lt.W[l];
             const int64_t start = lt.start[l];
             const int64_t soff = lt.scratch_off[l];
@@ -674,115 +628,221 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
                 }
             }
         }
-        if constexpr (BIN) {
-            // Records: lane c of a group takes corners c, c + G, ... (< 4) of
-            // point t. Wave-uniform loops: the slot allocation aggregates a
-            // whole wave, and every in-bounds corner counted by
-            // bin_count_kernel gets exactly one record.
-#pragma unroll
-            for (int t = 0; t < CH; ++t)
-            for (int cn0 = 0; cn0 < 4; cn0 += G) {
-                const int cn = cn0 + c;
-                const int l = lvl[t];
-                const int W = lt.W[l];
-                const bool vcn = cn == 0 ? cl[t].v00 : cn == 1 ? cl[t].v01 : cn == 2 ? cl[t].v10 : cl[t].v11;
-                const bool ok = q_ok && (i0 + t < per_lane) && cn < 4 && vcn;
-                const float fx = cl[t].fx, fy = cl[t].fy;
-                const float wx = (cn & 1) ? fx : 1.0f - fx, wy = (cn & 2) ? fy : 1.0f - fy;
-                const int64_t row = cl[t].row00 + ((cn & 2) ? W : 0) + (cn & 1);
-                uint32_t rib = 0;
-                const uint32_t key = ok ? bin_of(lt, l, b, m, M, nbbm, row, &rib) : 0u;
-                const uint32_t slot = wave_aggregate<true>(bins.cursor, key, ok);
-                if (ok)
-                    bins.records[slot] = make_uint2(((uint32_t)q << 10) | rib,
-                                                    __float_as_uint(aw[t] * wx * wy));
-            }
-        }
     }
 }
 
 // ------------------------------------------------------ binned grad_value
 //
-// grad_value without float atomics: every in-bounds corner becomes an 8-byte
-// record in the bin of its destination rows (a counting sort: count, scan,
-// place), then one workgroup per bin sums its records in an fp32 LDS tile and
-// writes the bin's rows once. Bins are sized per level so that each holds a
-// few hundred records on average, which keeps heavily shared coarse levels
-// (encoder shapes: ~1300 contributions per pixel) balanced.
+// grad_value without float atomics on global memory. Every in-bounds corner
+// of every point contributes A * w_ij * g[b, q, m, :] to one destination row.
+// The rows of level l of one (b, m) are cut into bins of 2^bin_shift[l] pixel
+// rows. A counting sort (count, scan, place) groups the contributions by bin
+// as 8-byte records; then one workgroup per bin sums its records into an fp32
+// tile in LDS and writes each row of the bin once, rounded once.
+//
+// Count and place aggregate a workgroup's corners per bin in an LDS hash
+// table before touching the global counters, so a counter receives one
+// atomic per (workgroup, bin) rather than one per corner. Consecutive points
+// of one (b, m) fall into few bins, so counters of heavily shared coarse
+// levels see little contention.
 
-// One lane per point: count the in-bounds corners per bin.
-template <class DT>
-__global__ __launch_bounds__(kBlock) void bin_count_kernel(
-    const typename DT::S *__restrict__ loc, const LevelTable lt, uint32_t *__restrict__ counts,
-    const uint32_t P, const uint32_t LK, const uint32_t K, const uint32_t M, const uint32_t QM,
-    const int64_t nbbm, const int64_t iters) {
-    for (int64_t it = 0; it < iters; ++it) {
-        const uint64_t p = ((uint64_t)it * gridDim.x + blockIdx.x) * kBlock + threadIdx.x;
-        const bool pv = p < P;
-        const uint32_t pc = pv ? (uint32_t)p : 0u;
-        const uint32_t pq = pc / LK;
-        const int l = (int)((pc - pq * LK) / K);
-        const uint32_t b = pq / QM, m = pq % M;
-        const float x = to_f32(DT{}, loc[2 * (uint64_t)pc]);
-        const float y = to_f32(DT{}, loc[2 * (uint64_t)pc + 1]);
-        const int W = lt.W[l];
-        const Cell cl = map_cell(x, y, (float)lt.H[l], (float)W, W, lt.start[l]);
-        const bool vc[4] = {cl.v00, cl.v01, cl.v10, cl.v11};
+constexpr int kHashBits = 11;
+constexpr int kHashSlots = 1 << kHashBits;   // > 4 corners x kBlock points: never full
+constexpr uint32_t kEmptyKey = 0xFFFFFFFFu;  // bin ids stay below 2^31
+
+// One thread per point of one (b, m): workgroup w of pair bm takes the
+// (query, point) indices [w * kBlock, (w + 1) * kBlock) of that pair. Count
+// (PLACE = false) adds the workgroup's per-bin totals to counter[bin]. Place
+// (PLACE = true) reserves a range of each bin with one returning atomic on
+// counter[bin] (the bin's cursor, initialised to its start by the scan) and
+// writes the records: x = query << 4 | row within the bin (bins have at most
+// 16 rows), y = fp32 bits of A * w_ij. Both derive cells with the same map_cell as the backward, so they
+// agree on every in-bounds corner.
+template <class DT, bool PLACE>
+__global__ __launch_bounds__(kBlock) void bin_sort_kernel(
+    const typename DT::S *__restrict__ loc, const typename DT::S *__restrict__ attn,
+    const LevelTable lt, uint32_t *__restrict__ counter, uint2 *__restrict__ records,
+    const int64_t Q, const int M, const int L, const int K, const int64_t nbbm,
+    const int64_t wpb, const int64_t ntiles) {
+    __shared__ uint32_t keys[kHashSlots];
+    __shared__ uint32_t cnt[kHashSlots];
+    __shared__ uint16_t used[4 * kBlock];
+    __shared__ uint32_t nused;
+    const int64_t wg = logical_block();
+    if (wg >= ntiles) return;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kHashSlots; i += kBlock) {
+        keys[i] = kEmptyKey;
+        cnt[i] = 0u;
+    }
+    if (tid == 0) nused = 0u;
+    __syncthreads();
+
+    const int64_t bm = wg / wpb;
+    const int64_t w = wg - bm * wpb;
+    const int64_t b = bm / M;
+    const int m = (int)(bm - b * M);
+    const int LK = L * K;
+    const int64_t i = w * kBlock + tid;
+    const bool ok = i < Q * LK;
+    const int64_t q = ok ? i / LK : 0;
+    const int pp = ok ? (int)(i - q * LK) : 0;
+    const int l = pp / K;
+    const int64_t pt = ((b * Q + q) * M + m) * LK + pp;
+    float x, y;
+    load_xy<DT>(loc + 2 * pt, x, y);
+    const int W = lt.W[l];
+    const int64_t start = lt.start[l];
+    const Cell cl = map_cell(x, y, (float)lt.H[l], (float)W, W, start);
+    const int shl = lt.bin_shift[l];
+    const bool binned = ok && shl >= 0;  // levels left to atomics make no records
+    const int sh = shl >= 0 ? shl : 0;
+    const uint32_t kbase = (uint32_t)(bm * nbbm + lt.bin_off[l]);
+    const bool vc[4] = {binned && cl.v00, binned && cl.v01, binned && cl.v10, binned && cl.v11};
+    uint32_t slot[4], rank[4], rib[4];
+#pragma unroll
+    for (int cn = 0; cn < 4; ++cn) {
+        slot[cn] = rank[cn] = rib[cn] = 0u;
+        if (!vc[cn]) continue;
+        const int64_t rel = cl.row00 + ((cn & 2) ? W : 0) + (cn & 1) - start;
+        rib[cn] = (uint32_t)(rel & ((1 << sh) - 1));
+        const uint32_t key = kbase + (uint32_t)(rel >> sh);
+        uint32_t h = (key * 2654435761u) >> (32 - kHashBits);
+        // linear probing; at most 4 * kBlock keys per workgroup, so an empty
+        // slot always exists and the loop ends
+        while (true) {
+            const uint32_t prev = atomicCAS(&keys[h], kEmptyKey, key);
+            if (prev == kEmptyKey) {
+                used[atomicAdd(&nused, 1u)] = (uint16_t)h;
+                break;
+            }
+            if (prev == key) break;
+            h = (h + 1) & (kHashSlots - 1);
+        }
+        slot[cn] = h;
+        if constexpr (PLACE) rank[cn] = atomicAdd(&cnt[h], 1u);
+        else atomicAdd(&cnt[h], 1u);
+    }
+    __syncthreads();
+    const uint32_t nu = nused;
+    for (uint32_t u = tid; u < nu; u += kBlock) {
+        const uint32_t h = used[u];
+        if constexpr (PLACE)
+            cnt[h] = __hip_atomic_fetch_add(counter + keys[h], cnt[h], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        else
+            __hip_atomic_fetch_add(counter + keys[h], cnt[h], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if constexpr (PLACE) {
+        __syncthreads();
+        const float a = ok ? to_f32(DT{}, attn[pt]) : 0.0f;
+        const uint32_t qx = (uint32_t)q << 4;
 #pragma unroll
         for (int cn = 0; cn < 4; ++cn) {
-            const bool ok = pv && vc[cn];
-            const int64_t row = cl.row00 + ((cn & 2) ? W : 0) + (cn & 1);
-            uint32_t rib;
-            const uint32_t key = ok ? bin_of(lt, l, b, (int)m, (int)M, nbbm, row, &rib) : 0u;
-            wave_aggregate<false>(counts, key, ok);
+            if (!vc[cn]) continue;
+            const float wx = (cn & 1) ? cl.fx : 1.0f - cl.fx;
+            const float wy = (cn & 2) ? cl.fy : 1.0f - cl.fy;
+            records[cnt[slot[cn]] + rank[cn]] = make_uint2(qx | rib[cn], __float_as_uint(a * wx * wy));
         }
     }
 }
 
 // One workgroup: counts[0:nb] -> exclusive starts[0:nb+1], cursor = starts.
+// Tiles of 4 * kScanBlock counts, each thread owning 4 consecutive ones; the
+// next tile's loads are issued before the current tile is scanned (wave
+// shuffles, then the 16 wave totals), and a running carry joins the tiles.
 constexpr int kScanBlock = 1024;
 __global__ __launch_bounds__(kScanBlock) void bin_scan_kernel(uint32_t *__restrict__ starts,
                                                              uint32_t *__restrict__ cursor,
                                                              const int64_t nb) {
-    __shared__ uint32_t part[kScanBlock];
-    const int tid = threadIdx.x;
-    const int64_t per = (nb + kScanBlock - 1) / kScanBlock;
-    const int64_t i0 = tid * per, i1 = (i0 + per < nb) ? i0 + per : nb;
-    uint32_t sum = 0;
-    for (int64_t i = i0; i < i1; ++i) sum += starts[i];
-    part[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < kScanBlock; off <<= 1) {
-        const uint32_t v = tid >= off ? part[tid - off] : 0u;
+    constexpr int kWaves = kScanBlock / 64;
+    constexpr int64_t kTile = 4 * kScanBlock;
+    __shared__ uint32_t wsum[kWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t ntiles = (nb + kTile - 1) / kTile;
+    uint32_t cur[4], nxt[4] = {0u, 0u, 0u, 0u};
+    auto load4 = [&](int64_t t, uint32_t(&v)[4]) {
+        const int64_t i0 = t * kTile + 4 * (int64_t)tid;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = i0 + k < nb ? starts[i0 + k] : 0u;
+    };
+    load4(0, cur);
+    uint32_t carry = 0;
+    for (int64_t t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) load4(t + 1, nxt);
+        const uint32_t s0 = cur[0], s1 = s0 + cur[1], s2 = s1 + cur[2], s3 = s2 + cur[3];
+        uint32_t x = s3;  // inclusive scan over the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wsum[wv] = x;
         __syncthreads();
-        part[tid] += v;
+        if (wv == 0) {
+            uint32_t w = lane < kWaves ? wsum[lane] : 0u;
+#pragma unroll
+            for (int off = 1; off < kWaves; off <<= 1) {
+                const uint32_t y = __shfl_up(w, off);
+                if (lane >= off) w += y;
+            }
+            if (lane < kWaves) wsum[lane] = w;
+        }
         __syncthreads();
+        const uint32_t excl = carry + (wv > 0 ? wsum[wv - 1] : 0u) + x - s3;
+        const uint32_t out[4] = {excl, excl + s0, excl + s1, excl + s2};
+        const int64_t i0 = t * kTile + 4 * (int64_t)tid;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (i0 + k < nb) {
+                starts[i0 + k] = out[k];
+                cursor[i0 + k] = out[k];
+            }
+        carry += wsum[kWaves - 1];
+        __syncthreads();  // wsum is rewritten by the next tile
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cur[k] = nxt[k];
     }
-    uint32_t run = part[tid] - sum;
-    for (int64_t i = i0; i < i1; ++i) {
-        const uint32_t cnt = starts[i];
-        starts[i] = run;
-        cursor[i] = run;
-        run += cnt;
-    }
-    if (tid == kScanBlock - 1) starts[nb] = part[kScanBlock - 1];
+    if (tid == 0) starts[nb] = carry;
 }
 
-// One workgroup per bin. Lane groups of G lanes take records (U at a time,
-// loads issued before use), gather the query's upstream-gradient row in slot
-// layout and add coef * g into the LDS tile; then the tile's rows are written
-// (or added, with `accumulate`) to grad_value in the value dtype.
-template <class DT, int SLOT, int J>
+// One workgroup per bin, no atomics. The workgroup has kAccGroups lane
+// groups of 16 lanes (slot layout as in the backward) and a bin has at most
+// kAccGroups rows; with rep = kAccGroups / rows replicas of each row there
+// are exactly kAccGroups (row, replica) slots, slot s = row * rep + replica
+// belonging to lane group s, which sums its records in registers.
+//
+// Records come in rounds of kBlock, one per thread (the next round's load is
+// issued before the current round is processed), and each round is counting-
+// sorted by slot in LDS: four ballots on the slot bits give every record its
+// rank among the wave's records of the same slot, 16 lanes per wave publish
+// the wave's per-slot counts, one wave scans the 64 counts, and the records
+// are written in slot order. A group then reads its slot's records
+// contiguously, U at a time, with all their upstream-gradient loads (32-bit
+// offsets into a buffer over the batch's grad_output) issued before use. At
+// the end every group stores its sums to an LDS tile, the replicas of each
+// row are added, and the row is written (or added, with `accumulate`) to
+// grad_value, V channels per access.
+constexpr int kAccGroups = kBlock / 16;
+
+template <class DT, int SLOT, int J, int V>
 __global__ __launch_bounds__(kBlock) void bin_accum_kernel(
     const typename DT::S *__restrict__ grad_out, typename DT::S *__restrict__ grad_value,
     const uint32_t *__restrict__ starts, const uint2 *__restrict__ records, const LevelTable lt,
     const int64_t S, const int64_t Q, const int M, const int D, const int L, const int64_t nbbm,
-    const int log2g, const int accumulate) {
+    const int64_t nbins, const int accumulate) {
     using E = typename DT::S;
     using R = typename RawVec<SLOT * (int)sizeof(E)>::type;
-    constexpr int U = 4;
-    extern __shared__ float tile[];
-    const int64_t bin = blockIdx.x;
+    constexpr int G = 16;
+    constexpr int U = J == 1 ? 16 : (J == 2 ? 8 : 4);
+    constexpr int kWaves = kBlock / 64;
+    extern __shared__ float tile[];  // kAccGroups x D
+    __shared__ uint2 sorted[kBlock];
+    __shared__ uint32_t wcount[kAccGroups * kWaves];   // [slot][wave]
+    __shared__ uint32_t woff[kAccGroups * kWaves + 1];  // exclusive prefix, slot-major
+    const int64_t bin = logical_block();  // neighbouring bins share upstream-gradient rows
+    if (bin >= nbins) return;
     const int64_t bm = bin / nbbm;
     const int lb = (int)(bin - bm * nbbm);
     const int64_t b = bm / M;
@@ -790,64 +850,130 @@ __global__ __launch_bounds__(kBlock) void bin_accum_kernel(
     int l = 0;
     for (int i = 1; i < L; ++i)
         if (lb >= lt.bin_off[i]) l = i;
-    const int sh = lt.bin_shift[l];
+    const int sh = lt.bin_shift[l];  // 0..4
+    const int log2rep = 4 - sh;
     const int64_t HW = (int64_t)lt.H[l] * lt.W[l];
     const int64_t r0 = (int64_t)(lb - lt.bin_off[l]) << sh;
     const int rows = (int)(((int64_t)1 << sh) < HW - r0 ? ((int64_t)1 << sh) : HW - r0);
-    const int n = rows * D;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < n; i += kBlock) tile[i] = 0.0f;
-    __syncthreads();
-
-    const uint32_t rb = starts[bin], re = starts[bin + 1];
-    const int G = 1 << log2g;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = tid & (G - 1);
-    const int gid = tid >> log2g;
-    const int ngroups = kBlock >> log2g;
+    const int gid = tid >> 4;
     const int nslots = D / SLOT;
     const int64_t MD = (int64_t)M * D;
+    // grad_output rows of batch b, head m: row q at byte q * MD * e
     const E *gq = grad_out + (b * Q * M + m) * (int64_t)D;
-    for (uint32_t base = rb + (uint32_t)gid * U; base < re; base += (uint32_t)ngroups * U) {
-        uint2 rec[U];
+    const Slice<true> gslice(gq, (Q - 1) * MD * (int64_t)sizeof(E) + D * (int64_t)sizeof(E));
+    const uint32_t row_bytes = (uint32_t)(MD * (int64_t)sizeof(E));
+    uint32_t soff[J];
+    bool slot_ok[J];
 #pragma unroll
-        for (int u = 0; u < U; ++u) rec[u] = records[base + u < re ? base + u : re - 1];
-        R gr[U][J];
+    for (int j = 0; j < J; ++j) {
+        slot_ok[j] = c + j * G < nslots;
+        soff[j] = (uint32_t)((c + j * G) * SLOT * (int)sizeof(E));
+    }
+    float acc[J][SLOT];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            // (clamps keep every access in range whatever a record holds)
-            const uint32_t rq = rec[u].x >> 10;
-            const E *gp = gq + (int64_t)(rq < Q ? rq : 0) * MD;
+    for (int j = 0; j < J; ++j)
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int sl = c + j * G;
-                gr[u][j] = *reinterpret_cast<const R *>(gp + (sl < nslots ? sl : 0) * SLOT);
-            }
+        for (int v = 0; v < SLOT; ++v) acc[j][v] = 0.0f;
+
+    const uint32_t rb = starts[bin], re = starts[bin + 1];
+    uint2 next = make_uint2(0u, 0u);
+    if (rb < re) next = records[rb + tid < re ? rb + tid : re - 1];  // (an empty bin reads nothing)
+    for (uint32_t base = rb; base < re; base += kBlock) {
+        const uint2 rec = next;
+        const bool valid = base + tid < re;
+        {
+            const uint32_t nb = base + kBlock + tid;
+            if (base + kBlock < re) next = records[nb < re ? nb : re - 1];
         }
+        uint32_t rr = rec.x & 15u;
+        rr = rr < (uint32_t)rows ? rr : 0u;  // keeps every access in range
+        const uint32_t slot = (rr << log2rep) | ((base + tid) & ((1u << log2rep) - 1u));
+        // lanes of this wave holding a record of the same slot
+        const uint64_t vb = __ballot(valid);
+        const uint64_t b0 = __ballot(slot & 1u), b1 = __ballot(slot & 2u);
+        const uint64_t b2 = __ballot(slot & 4u), b3 = __ballot(slot & 8u);
+        auto same = [&](uint32_t sl) {
+            return vb & ((sl & 1u) ? b0 : ~b0) & ((sl & 2u) ? b1 : ~b1) & ((sl & 4u) ? b2 : ~b2) &
+                   ((sl & 8u) ? b3 : ~b3);
+        };
+        const uint64_t mine = same(slot);
+        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(mine >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mine, 0u));
+        __syncthreads();  // the previous round's sorted records and offsets consumed
+        if (lane < kAccGroups) wcount[lane * kWaves + wave] = (uint32_t)__popcll(same((uint32_t)lane));
+        __syncthreads();
+        if (wave == 0) {  // exclusive scan of the 64 counts, slot-major
+            const uint32_t x = wcount[lane];
+            uint32_t inc = x;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (base + u >= re) continue;
-            const float coef = __uint_as_float(rec[u].y);
-            const uint32_t rr = rec[u].x & 1023u;
-            float *trow = tile + (rr < (uint32_t)rows ? rr : 0u) * (uint32_t)D;
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int sl = c + j * G;
-                if (sl >= nslots) continue;
-                float gv[SLOT];
-                raw_to_f32<DT, SLOT>(gr[u][j], gv);
-#pragma unroll
-                for (int v = 0; v < SLOT; ++v) atomicAdd(trow + sl * SLOT + v, coef * gv[v]);
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t y = __shfl_up(inc, off);
+                if (lane >= off) inc += y;
             }
+            woff[lane] = inc - x;
+            if (lane == 63) woff[64] = inc;
+        }
+        __syncthreads();
+        if (valid) sorted[woff[slot * kWaves + wave] + rank] = rec;
+        __syncthreads();
+        const uint32_t first = woff[gid * kWaves], n = woff[gid * kWaves + kWaves] - first;
+        for (uint32_t i0 = 0; __ballot(i0 < n); i0 += U) {
+            float coef[U];
+            uint32_t qo[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool ok = i0 + u < n;
+                const uint2 rc = sorted[first + (ok ? i0 + u : 0u)];
+                coef[u] = ok ? __uint_as_float(rc.y) : 0.0f;
+                const uint32_t rq = rc.x >> 4;
+                qo[u] = (rq < (uint64_t)Q ? rq : 0u) * row_bytes;
+            }
+            R gr[U][J];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < J; ++j) gr[u][j] = gslice.template gather<R>(qo[u] + soff[j], slot_ok[j]);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    float gv[SLOT];
+                    raw_to_f32<DT, SLOT>(gr[u][j], gv);
+#pragma unroll
+                    for (int v = 0; v < SLOT; ++v) acc[j][v] = __builtin_fmaf(coef[u], gv[v], acc[j][v]);
+                }
         }
     }
+    // every group's sums (zeros for a group without records) -> tile row gid
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+        if (slot_ok[j])
+#pragma unroll
+            for (int v = 0; v < SLOT; ++v) tile[gid * D + (c + j * G) * SLOT + v] = acc[j][v];
     __syncthreads();
     E *dst = grad_value + ((b * S + lt.start[l] + r0) * M + m) * (int64_t)D;
-    for (int i = tid; i < n; i += kBlock) {
-        const int rr = i / D, ch = i - rr * D;
-        E *d = dst + (int64_t)rr * MD + ch;
-        float v = tile[i];
-        if (accumulate) v += to_f32(DT{}, *d);
-        *d = from_f32(DT{}, v);
+    const int vpr = D / V;
+    const int nrep = 1 << log2rep;
+    for (int i = tid; i < rows * vpr; i += kBlock) {
+        const int rr = i / vpr, cv = i - rr * vpr;
+        E *d = dst + (int64_t)rr * MD + cv * V;
+        float v[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) v[k] = 0.0f;
+        for (int r = 0; r < nrep; ++r) {
+            const float *t = tile + ((rr << log2rep) + r) * D + cv * V;
+#pragma unroll
+            for (int k = 0; k < V; ++k) v[k] += t[k];
+        }
+        if (accumulate) {
+            float o[V];
+            load_vec<DT, V>(d, o);
+#pragma unroll
+            for (int k = 0; k < V; ++k) v[k] += o[k];
+        }
+        store_vec<DT, V>(d, v);
     }
 }
 
@@ -942,45 +1068,59 @@ hipError_t fwd_launch(const Problem &p, const Mapping &mp, const void *value, co
 template <class DT, int SLOT, int J, bool BIN>
 hipError_t bwd_launch(const Problem &p, const BwdMapping &mp, const void *value, const void *loc,
                       const void *attn, const void *grad_out, void *grad_value, float *workspace,
-                      void *grad_loc, void *grad_attn, const BinnedBuffers &bins,
-                      hipStream_t stream) {
+                      void *grad_loc, void *grad_attn, hipStream_t stream) {
     using E = typename DT::S;
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
     const int qblocks = (int)((p.Q + qpb - 1) / qpb);
     const int64_t ntiles = p.B * p.M * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
-    if (BIN || slice_fits_buffer(p))
+    if (slice_fits_buffer(p))
         hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, true, BIN>),
                            dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
                            static_cast<const E *>(value), static_cast<const E *>(loc),
                            static_cast<const E *>(attn), static_cast<const E *>(grad_out),
                            grad_value, workspace, static_cast<E *>(grad_loc),
                            static_cast<E *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
-                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split, bins,
-                           p.nbbm);
-    else if constexpr (!BIN)
-        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, false, false>),
+                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
+    else
+        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, false, BIN>),
                            dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
                            static_cast<const E *>(value), static_cast<const E *>(loc),
                            static_cast<const E *>(attn), static_cast<const E *>(grad_out),
                            grad_value, workspace, static_cast<E *>(grad_loc),
                            static_cast<E *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
-                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split, bins,
-                           p.nbbm);
+                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
     return hipGetLastError();
 }
 
+template <class DT, int SLOT, int J, int V>
+hipError_t accum_launch_v(const Problem &p, const BwdMapping &mp, const void *grad_out,
+                          void *grad_value, const BinnedBuffers &bins, bool accumulate,
+                          hipStream_t stream) {
+    using E = typename DT::S;
+    const size_t lds = (size_t)kAccGroups * (size_t)p.D * sizeof(float);
+    const int64_t per_xcd = (bins.nbins + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL((bin_accum_kernel<DT, SLOT, J, V>), dim3((unsigned)(per_xcd * kXcds)),
+                       dim3(kBlock), lds, stream, static_cast<const E *>(grad_out),
+                       static_cast<E *>(grad_value), bins.starts, bins.records, p.levels, p.S,
+                       p.Q, (int)p.M, (int)p.D, (int)p.L, p.nbbm, bins.nbins, (int)accumulate);
+    return hipGetLastError();
+}
+
+// Write-back width: the widest of 16, 8, 4 bytes (or one element) that
+// divides a row and to which grad_value is aligned.
 template <class DT, int SLOT, int J>
 hipError_t accum_launch(const Problem &p, const BwdMapping &mp, const void *grad_out,
                         void *grad_value, const BinnedBuffers &bins, bool accumulate,
                         hipStream_t stream) {
-    using E = typename DT::S;
-    const size_t lds = (size_t)bins.max_bin_rows * (size_t)p.D * sizeof(float);
-    hipLaunchKernelGGL((bin_accum_kernel<DT, SLOT, J>), dim3((unsigned)bins.nbins), dim3(kBlock),
-                       lds, stream, static_cast<const E *>(grad_out), static_cast<E *>(grad_value),
-                       bins.starts, bins.records, p.levels, p.S, p.Q, (int)p.M, (int)p.D, (int)p.L,
-                       p.nbbm, mp.log2_group, (int)accumulate);
-    return hipGetLastError();
+    constexpr int e = (int)sizeof(typename DT::S);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(grad_value);
+    auto fits = [&](int v) { return p.D % v == 0 && a % (uintptr_t)(v * e) == 0; };
+    if (fits(16 / e)) return accum_launch_v<DT, SLOT, J, 16 / e>(p, mp, grad_out, grad_value, bins, accumulate, stream);
+    if (fits(8 / e)) return accum_launch_v<DT, SLOT, J, 8 / e>(p, mp, grad_out, grad_value, bins, accumulate, stream);
+    if constexpr (e == 2)
+        if (fits(2)) return accum_launch_v<DT, SLOT, J, 2>(p, mp, grad_out, grad_value, bins, accumulate, stream);
+    return accum_launch_v<DT, SLOT, J, 1>(p, mp, grad_out, grad_value, bins, accumulate, stream);
 }
 
 template <class DT>
@@ -1003,18 +1143,18 @@ hipError_t fwd_by_vec(const Problem &p, const Mapping &mp, const void *v, const 
 template <class DT, int SLOT, bool BIN>
 hipError_t bwd_by_j(const Problem &p, const BwdMapping &mp, const void *v, const void *l,
                     const void *a, const void *go, void *gv, float *ws, void *gl, void *ga,
-                    const BinnedBuffers &bn, hipStream_t st) {
+                    hipStream_t st) {
     switch (mp.j) {
-        case 1: return bwd_launch<DT, SLOT, 1, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
-        case 2: return bwd_launch<DT, SLOT, 2, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
-        case 3: return bwd_launch<DT, SLOT, 3, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
-        case 4: return bwd_launch<DT, SLOT, 4, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
-        case 8: return bwd_launch<DT, SLOT, 8, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
-        case 16: return bwd_launch<DT, SLOT, 16, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
+        case 1: return bwd_launch<DT, SLOT, 1, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 2: return bwd_launch<DT, SLOT, 2, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 3: return bwd_launch<DT, SLOT, 3, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 4: return bwd_launch<DT, SLOT, 4, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 8: return bwd_launch<DT, SLOT, 8, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 16: return bwd_launch<DT, SLOT, 16, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
         default: break;
     }
     if constexpr (SLOT == 1) {
-        if (mp.j == 32) return bwd_launch<DT, SLOT, 32, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, bn, st);
+        if (mp.j == 32) return bwd_launch<DT, SLOT, 32, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
     }
     return hipErrorInvalidValue;
 }
@@ -1087,6 +1227,31 @@ hipError_t scratch_add(const Problem &p, const float *ws, void *gv, hipStream_t 
     return hipGetLastError();
 }
 
+template <bool BIN>
+hipError_t backward_dispatch(const Problem &p, const BwdMapping &mp, const void *value,
+                             const void *loc, const void *attn, const void *grad_out,
+                             void *grad_value, float *workspace, void *grad_loc, void *grad_attn,
+                             hipStream_t stream) {
+    switch (p.dtype) {
+        case MSDA_F32:
+            return bwd_by_j<F32T, 1, BIN>(p, mp, value, loc, attn, grad_out, grad_value, workspace,
+                                          grad_loc, grad_attn, stream);
+        case MSDA_F16:
+            return mp.slot == 2
+                       ? bwd_by_j<F16T, 2, BIN>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                workspace, grad_loc, grad_attn, stream)
+                       : bwd_by_j<F16T, 1, BIN>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                workspace, grad_loc, grad_attn, stream);
+        case MSDA_BF16:
+            return mp.slot == 2
+                       ? bwd_by_j<BF16T, 2, BIN>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                 workspace, grad_loc, grad_attn, stream)
+                       : bwd_by_j<BF16T, 1, BIN>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                 workspace, grad_loc, grad_attn, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_forward(const Problem &p, const Mapping &mp, const void *value,
@@ -1103,70 +1268,36 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
                            const void *loc, const void *attn, const void *grad_out,
                            void *grad_value, float *workspace, void *grad_loc, void *grad_attn,
                            hipStream_t stream) {
-    const BinnedBuffers none = {nullptr, nullptr, nullptr, 0, 0};
-    switch (p.dtype) {
-        case MSDA_F32:
-            return bwd_by_j<F32T, 1, false>(p, mp, value, loc, attn, grad_out, grad_value,
-                                            workspace, grad_loc, grad_attn, none, stream);
-        case MSDA_F16:
-            return mp.slot == 2
-                       ? bwd_by_j<F16T, 2, false>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                  workspace, grad_loc, grad_attn, none, stream)
-                       : bwd_by_j<F16T, 1, false>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                  workspace, grad_loc, grad_attn, none, stream);
-        case MSDA_BF16:
-            return mp.slot == 2
-                       ? bwd_by_j<BF16T, 2, false>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                   workspace, grad_loc, grad_attn, none, stream)
-                       : bwd_by_j<BF16T, 1, false>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                   workspace, grad_loc, grad_attn, none, stream);
-        default: return hipErrorInvalidValue;
-    }
+    return backward_dispatch<false>(p, mp, value, loc, attn, grad_out, grad_value, workspace,
+                                    grad_loc, grad_attn, stream);
 }
 
 hipError_t launch_backward_binned(const Problem &p, const BwdMapping &mp, const void *value,
                                   const void *loc, const void *attn, const void *grad_out,
-                                  const BinnedBuffers &bins, void *grad_loc, void *grad_attn,
-                                  hipStream_t stream) {
-    switch (p.dtype) {
-        case MSDA_F32:
-            return bwd_by_j<F32T, 1, true>(p, mp, value, loc, attn, grad_out, nullptr, nullptr,
-                                           grad_loc, grad_attn, bins, stream);
-        case MSDA_F16:
-            return mp.slot == 2
-                       ? bwd_by_j<F16T, 2, true>(p, mp, value, loc, attn, grad_out, nullptr,
-                                                 nullptr, grad_loc, grad_attn, bins, stream)
-                       : bwd_by_j<F16T, 1, true>(p, mp, value, loc, attn, grad_out, nullptr,
-                                                 nullptr, grad_loc, grad_attn, bins, stream);
-        case MSDA_BF16:
-            return mp.slot == 2
-                       ? bwd_by_j<BF16T, 2, true>(p, mp, value, loc, attn, grad_out, nullptr,
-                                                  nullptr, grad_loc, grad_attn, bins, stream)
-                       : bwd_by_j<BF16T, 1, true>(p, mp, value, loc, attn, grad_out, nullptr,
-                                                  nullptr, grad_loc, grad_attn, bins, stream);
-        default: return hipErrorInvalidValue;
-    }
+                                  void *grad_loc, void *grad_attn, hipStream_t stream) {
+    return backward_dispatch<true>(p, mp, value, loc, attn, grad_out, nullptr, nullptr, grad_loc,
+                                   grad_attn, stream);
 }
 
-hipError_t launch_bin_count(const Problem &p, const void *loc, const BinnedBuffers &bins,
-                            hipStream_t stream) {
-    const int64_t P = p.B * p.Q * p.M * p.L * p.K;
-    if (P == 0) return hipSuccess;
-    const int64_t blocks_needed = (P + kBlock - 1) / kBlock;
-    const int64_t grid = blocks_needed < 256 * 16 ? blocks_needed : 256 * 16;
-    const int64_t iters = (blocks_needed + grid - 1) / grid;
-    const uint32_t LK = (uint32_t)(p.L * p.K), QM = (uint32_t)(p.Q * p.M);
-#define MSDA_COUNT(T)                                                                          \
-    hipLaunchKernelGGL(bin_count_kernel<T>, dim3((unsigned)grid), dim3(kBlock), 0, stream,     \
-                       static_cast<const typename T::S *>(loc), p.levels, bins.starts,          \
-                       (uint32_t)P, LK, (uint32_t)p.K, (uint32_t)p.M, QM, p.nbbm, iters)
+hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
+                           const BinnedBuffers &bins, bool place, hipStream_t stream) {
+    const int64_t wpb = (p.Q * p.L * p.K + kBlock - 1) / kBlock;
+    const int64_t ntiles = p.B * p.M * wpb;
+    if (ntiles == 0) return hipSuccess;
+    const int64_t grid = (ntiles + kXcds - 1) / kXcds * kXcds;
+    uint32_t *counter = place ? bins.cursor : bins.starts;
+#define MSDA_SORT(T, PL)                                                                        \
+    hipLaunchKernelGGL((bin_sort_kernel<T, PL>), dim3((unsigned)grid), dim3(kBlock), 0, stream, \
+                       static_cast<const typename T::S *>(loc),                                 \
+                       static_cast<const typename T::S *>(attn), p.levels, counter,             \
+                       bins.records, p.Q, (int)p.M, (int)p.L, (int)p.K, p.nbbm, wpb, ntiles)
     switch (p.dtype) {
-        case MSDA_F32: MSDA_COUNT(F32T); break;
-        case MSDA_F16: MSDA_COUNT(F16T); break;
-        case MSDA_BF16: MSDA_COUNT(BF16T); break;
+        case MSDA_F32: if (place) MSDA_SORT(F32T, true); else MSDA_SORT(F32T, false); break;
+        case MSDA_F16: if (place) MSDA_SORT(F16T, true); else MSDA_SORT(F16T, false); break;
+        case MSDA_BF16: if (place) MSDA_SORT(BF16T, true); else MSDA_SORT(BF16T, false); break;
         default: return hipErrorInvalidValue;
     }
-#undef MSDA_COUNT
+#undef MSDA_SORT
     return hipGetLastError();
 }
 

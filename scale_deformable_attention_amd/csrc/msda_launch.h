@@ -36,14 +36,13 @@ struct Problem {
 };
 
 // Workspace of the binned grad_value: starts[nbins + 1] (counts before the
-// scan), cursor[nbins], and one 8-byte record per in-bounds corner:
-// x = query << 10 | row within the bin, y = fp32 bits of A * w_ij.
+// scan), cursor[nbins], and one 8-byte record per in-bounds corner of a
+// binned level: x = query << 4 | row within the bin, y = fp32 bits of A * w_ij.
 struct BinnedBuffers {
     uint32_t *starts;
     uint32_t *cursor;
     uint2 *records;
     int64_t nbins;
-    int max_bin_rows;  // largest 2^bin_shift, sizes the accumulation tile
 };
 
 // Forward lane mapping: each query's channels are spread over
@@ -79,16 +78,17 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
                            void *grad_value, float *workspace, void *grad_loc, void *grad_attn,
                            hipStream_t stream);
 
-// Binned grad_value, in stream order: zero starts (launch_zero), count the
-// in-bounds corners per bin, scan counts into starts and cursors, run
-// launch_backward with `bins` (records instead of atomics), accumulate.
-hipError_t launch_bin_count(const Problem &p, const void *loc, const BinnedBuffers &bins,
-                            hipStream_t stream);
+// Binned grad_value, in stream order: zero starts[0:nbins] (launch_zero);
+// launch_bin_sort(place = false) counts the in-bounds corners per bin into
+// starts; launch_bin_scan turns the counts into starts and cursors;
+// launch_bin_sort(place = true) writes the records; launch_backward_binned
+// writes grad_loc / grad_attn only; launch_bin_accumulate writes grad_value.
+hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
+                           const BinnedBuffers &bins, bool place, hipStream_t stream);
 hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream);
 hipError_t launch_backward_binned(const Problem &p, const BwdMapping &mp, const void *value,
                                   const void *loc, const void *attn, const void *grad_out,
-                                  const BinnedBuffers &bins, void *grad_loc, void *grad_attn,
-                                  hipStream_t stream);
+                                  void *grad_loc, void *grad_attn, hipStream_t stream);
 hipError_t launch_bin_accumulate(const Problem &p, const BwdMapping &mp, const void *grad_out,
                                  void *grad_value, const BinnedBuffers &bins, bool accumulate,
                                  hipStream_t stream);

@@ -104,7 +104,7 @@ def test_forward_given_start_index_may_differ_from_prefix(lib):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(accum=4), 4),
+    (dict(accum=5), 4),
     (dict(accum=-2), 4),
     (dict(flags=8), 2),
     (dict(flags=2), 2),  # scratch flags need an explicit scratch-capable mode
@@ -139,24 +139,54 @@ def test_workspace_size_and_accum_resolution(lib):
     assert lib.msda_backward_workspace_size(2, *prob, 2) == 1 * 20 * 2 * 8 * 4
     assert lib.msda_backward_resolve_accum(1, *prob, 2) == 2
     assert lib.msda_backward_resolve_accum(0, *prob, 2) == 0  # fp32: nothing to switch
-    # AUTO: PER_LEVEL for bf16, NATIVE for fp16 and fp32
-    assert lib.msda_backward_resolve_accum(2, *prob, -1) == 2
-    assert lib.msda_backward_resolve_accum(1, *prob, -1) == 0
-    assert lib.msda_backward_resolve_accum(0, *prob, -1) == 0
-    assert lib.msda_backward_workspace_size(2, *prob, -1) == 1 * 20 * 2 * 8 * 4
-    # BINNED: 512 records per bin at 1.6 and 6.4 contributions per pixel ->
-    # 256- and 64-row bins -> one bin per level per (b, m): 4 bins; starts
-    # (5 x 4 B) and cursors (4 x 4 B) each padded to 256 B; records: 4 corners
-    # x 128 points x 8 B.
+    # AUTO = MIXED: level (4,5) at 6.4 contributions per pixel is binned, level
+    # (8,10) at 1.6 keeps native atomics. Two 16-row bins per (b, m) for the
+    # binned level: 4 bins; starts (5 x 4 B) and cursors (4 x 4 B) padded to
+    # 256 B each; records: 4 corners x (16 queries x 2 heads x 2 points) x 8 B.
+    for dtype in (0, 1, 2):
+        assert lib.msda_backward_resolve_accum(dtype, *prob, -1) == 4
+        assert lib.msda_backward_resolve_accum(dtype, *prob, 4) == 4
+        assert lib.msda_backward_workspace_size(dtype, *prob, -1) == 256 + 256 + 4 * 64 * 8
+    # BINNED: bins of 16 rows (the cap) at both levels -> 5 + 2 bins per
+    # (b, m): 14 bins; starts (15 x 4 B) and cursors (14 x 4 B) each padded to
+    # 256 B; records: 4 corners x 128 points x 8 B.
     for dtype in (0, 1, 2):
         assert lib.msda_backward_resolve_accum(dtype, *prob, 3) == 3
         assert lib.msda_backward_workspace_size(dtype, *prob, 3) == 256 + 256 + 4 * 128 * 8
-    # BINNED does not apply to overlapping levels
+    # BINNED / MIXED do not apply to overlapping levels; AUTO falls back to
+    # PER_LEVEL for bf16 and NATIVE otherwise
     over = (1, 100, 2, 8, 2, SHAPES, (ctypes.c_int64 * 2)(0, 70), 16, 2)
     assert lib.msda_backward_resolve_accum(2, *over, 3) == -1 and lib.msda_last_error()
+    assert lib.msda_backward_resolve_accum(2, *over, 4) == -1
     assert lib.msda_backward_workspace_size(2, *over, 3) == 0
+    assert lib.msda_backward_resolve_accum(2, *over, -1) == 2
+    assert lib.msda_backward_resolve_accum(1, *over, -1) == 0
+    # no query: nothing is contended, MIXED resolves to NATIVE
+    empty = (1, 100, 2, 8, 2, SHAPES, None, 0, 2)
+    assert lib.msda_backward_resolve_accum(2, *empty, 4) == 0
     assert lib.msda_backward_resolve_accum(2, *prob, 7) == -1
     assert lib.msda_backward_workspace_size(9, *prob, 1) == 0 and lib.msda_last_error()
+
+
+def test_backward_plan_per_level(lib):
+    prob = (1, 100, 2, 8, 2, SHAPES, None, 16, 2)
+    modes = (ctypes.c_int * 2)()
+
+    def plan(dtype, accum, p=prob):
+        nb = lib.msda_backward_plan(dtype, *p, accum, modes)
+        return list(modes), nb
+
+    assert plan(2, -1) == ([0, 2], 4)   # MIXED: native, binned
+    assert plan(2, 3) == ([2, 2], 14)   # BINNED
+    assert plan(2, 2) == ([0, 1], 0)    # PER_LEVEL: native, fp32 scratch
+    assert plan(2, 1) == ([1, 1], 0)    # FP32_SCRATCH
+    assert plan(0, 1) == ([0, 0], 0)    # fp32 data never uses scratch
+    assert plan(1, 0) == ([0, 0], 0)    # NATIVE
+    over = (1, 100, 2, 8, 2, SHAPES, (ctypes.c_int64 * 2)(0, 70), 16, 2)
+    assert plan(2, -1, over) == ([0, 1], 0)
+    assert lib.msda_backward_plan(2, *over, 3, modes) == -1
+    assert lib.msda_backward_plan(2, *prob, 9, None) == -1
+    assert lib.msda_backward_plan(2, *prob, -1, None) == 4
 
 
 def test_launch_event_instrumentation_validation(lib):

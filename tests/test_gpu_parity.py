@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from scale_deformable_attention_amd import MSDAError, msda_backward, msda_forward
+from scale_deformable_attention_amd import MSDAError, PreparedCall, msda_backward, msda_forward
 from scale_deformable_attention_amd.workloads import Workload, make_inputs, workload
 
 from _parity import check_backward, check_forward, level_row_ranges, to_np
@@ -87,8 +87,8 @@ def _cached(name):
 @pytest.mark.parametrize("name,accum", [
     ("tiny_fp32", "auto"), ("tiny_fp32", "binned"),
     ("decoder_bf16", "auto"), ("decoder_bf16", "native"), ("decoder_bf16", "fp32_scratch"),
-    ("decoder_bf16", "binned"),
-    ("encoder_fp16", "auto"), ("encoder_fp16", "fp32_scratch"), ("encoder_fp16", "binned"),
+    ("decoder_bf16", "binned"), ("decoder_bf16", "per_level"), ("oddhead_fp32", "mixed"),
+    ("encoder_fp16", "auto"), ("encoder_fp16", "fp32_scratch"), ("encoder_fp16", "native"),
     ("oddhead_fp32", "auto"), ("oddhead_fp32", "binned"),
 ])
 def test_workload_parity(name, accum):
@@ -99,7 +99,7 @@ def test_workload_parity(name, accum):
     full_check(inp, wl.dtype, accum, ref=ref)
 
 
-@pytest.mark.parametrize("accum", ["auto", "binned"])
+@pytest.mark.parametrize("accum", ["auto", "fp32_scratch"])
 def test_large_encoder_parity(accum):
     name = "large_encoder_bf16"
     wl = workload(name)
@@ -380,9 +380,19 @@ def test_accumulation_resolution_on_the_decoder_workload():
     g = to_dev(inp)
     say("case decoder_bf16 accumulation resolution")
     args = (g["value"], g["spatial_shapes"], None, g["sampling_locations"], g["attention_weights"])
-    # contributions per pixel 300*4*4/(H*W): 0.29, 1.1 (packed bf16), 4.6, 17.6 (fp32 scratch)
-    assert msda_backward_resolve_accum(*args) == "per_level"
+    # contributions per pixel 300*4*4/(H*W): 0.29, 1.1 (native atomics), 4.6, 17.6 (binned)
+    assert msda_backward_resolve_accum(*args) == "mixed"
+    assert msda_backward_resolve_accum(*args, accum="per_level") == "per_level"
     assert msda_backward_resolve_accum(*args, accum="binned") == "binned"
+    call = PreparedCall(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                        g["attention_weights"])
+    modes, nb = call.plan()
+    assert modes == ["native", "native", "binned", "binned"] and nb > 0
+    # the encoder workload is contended at every level: all binned
+    enc = make_inputs(workload("encoder_fp16"), with_grad=False)
+    ge = to_dev(enc)
+    assert msda_backward_resolve_accum(ge["value"], ge["spatial_shapes"], None,
+                                       ge["sampling_locations"], ge["attention_weights"]) == "binned"
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=str)
