@@ -24,7 +24,8 @@ Algorithmic bytes per launch (e = element size, P = B*Q*M*L*K points,
 U = distinct (b, row, m) value rows with at least one in-bounds corner,
 C = in-bounds corners, N = B*S*M*D grad_value elements):
   forward          3*P*e (locations + weights) + B*Q*M*D*e (output) + U*D*e
-  backward kernel  3*P*e (params) + B*Q*M*D*e (grad_output) + U*D*e (value)
+  backward kernel  (msda_bwd_kernel; msda_grad_kernel when every level is binned)
+                   3*P*e (params) + B*Q*M*D*e (grad_output) + U*D*e (value)
                    + 3*P*e (grad locations + grad weights)
                    + atomics: 2*U'*D*e_acc (read-modify-write of the touched rows
                      of levels not binned; e_acc = 4 for fp32 rows)
@@ -295,7 +296,7 @@ def main():
         n_bwd = launch_events_recorded() // 2
     torch.cuda.synchronize()
     bwd_names = {
-        "binned": ["bin_zero", "bin_count", "bin_scan", "bin_place", "msda_bwd_kernel",
+        "binned": ["bin_zero", "bin_count", "bin_scan", "bin_place", "msda_grad_kernel",
                    "bin_accum_kernel"],
         "mixed": ["zero_fill", "bin_zero", "bin_count", "bin_scan", "bin_place", "msda_bwd_kernel",
                   "bin_accum_kernel"],
@@ -334,6 +335,7 @@ def main():
               "scratch_add_kernel": scratch_rows * D * (4 + 2 * e),
               # atomics: read-modify-write of the touched rows of unbinned levels
               "msda_bwd_kernel": common + 2 * ((U - U_scr - U_bin) * D * e_acc + U_scr * D * 4),
+              "msda_grad_kernel": common,
               "bin_zero": (nb + 1) * 4, "bin_count": 2 * P_bin * e, "bin_scan": 3 * nb * 4,
               "bin_place": 3 * P_bin * e + 8 * C_bin,
               "bin_accum_kernel": 8 * C_bin + B * Q * M * D * e + bin_rows * D * e}

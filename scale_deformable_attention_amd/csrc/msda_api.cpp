@@ -585,6 +585,7 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                     "native half-precision atomics need a 4-byte aligned grad_value with an even "
                     "element count; use MSDA_ACCUM_FP32_SCRATCH");
     msda::BwdMapping mp = {1, 1, 0, 0};
+    msda::Mapping gmp = {1, 0, 0};  // gradients-only kernel (every level binned)
     if (p.Q > 0) {
         if ((st = check_ptr(sampling_locations, "sampling_locations", dtype))) return st;
         if ((st = check_ptr(attention_weights, "attention_weights", dtype))) return st;
@@ -593,6 +594,8 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
         if ((st = check_ptr(grad_attention_weights, "grad_attention_weights", dtype))) return st;
         const bool pairs = aligned(value, 4) && aligned(grad_output, 4) && aligned(grad_value, 4);
         if ((st = choose_bwd_mapping(p, pairs, &mp))) return st;
+        const void *vec_ptrs[2] = {value, grad_output};
+        if (all_binned && (st = choose_mapping(p, vec_ptrs, 2, &gmp))) return st;
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t gv_bytes = (size_t)(p.B * p.S * p.M * p.D) * elem_size(dtype);
@@ -629,10 +632,10 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
         // every level binned: the backward writes only grad_loc / grad_attn;
         // otherwise it adds the unbinned levels' grad_value with atomics
         if ((err = marked(all_binned
-                              ? msda::launch_backward_binned(p, mp, value, sampling_locations,
-                                                             attention_weights, grad_output,
-                                                             grad_sampling_locations,
-                                                             grad_attention_weights, before(s))
+                              ? msda::launch_gradients(p, gmp, value, sampling_locations,
+                                                       attention_weights, grad_output,
+                                                       grad_sampling_locations,
+                                                       grad_attention_weights, before(s))
                               : msda::launch_backward(p, mp, value, sampling_locations,
                                                       attention_weights, grad_output, grad_value,
                                                       nullptr, grad_sampling_locations,

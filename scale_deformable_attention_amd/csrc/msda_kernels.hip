@@ -424,6 +424,152 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     if (live && s == 0) store_vec<DT, VEC>(out + pq * D + c0, acc);
 }
 
+// ------------------------------------------------- backward, gradients only
+//
+// grad_attention_weights and grad_sampling_locations when no level's
+// grad_value needs atomics (every level binned): the forward's lane layout
+// (VEC consecutive channels per lane, 16-byte gathers) with the query's
+// upstream gradient held in the same layout. Per point the lane forms its
+// share of g . s, g . ds/dx and g . ds/dy (course page "5. The backward
+// kernel", section "What the backward pass must produce"); the group's
+// shares are summed with DPP moves and lane c stores point t0 + c of the
+// chunk, so a group writes consecutive points with one instruction.
+template <class DT, int VEC, int CH, bool BUF>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void msda_grad_kernel(
+    const typename DT::S *__restrict__ value, const typename DT::S *__restrict__ loc,
+    const typename DT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out,
+    typename DT::S *__restrict__ grad_loc, typename DT::S *__restrict__ grad_attn,
+    const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
+    const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
+    const int log2s) {
+    using E = typename DT::S;
+    using R = typename RawVec<VEC * (int)sizeof(E)>::type;
+    const int64_t tile = logical_block();
+    if (tile >= ntiles) return;  // whole workgroup leaves together
+    const int64_t bm = tile / qblocks;
+    const int qb = (int)(tile - bm * qblocks);
+    const int64_t b = bm / M;
+    const int m = (int)(bm - b * M);
+
+    const int tid = threadIdx.x;
+    const int G = 1 << log2g;
+    const int c = tid & (G - 1);
+    const int s = (tid >> log2g) & ((1 << log2s) - 1);
+    const int qpb = kBlock >> (log2g + log2s);
+    const int64_t q = (int64_t)qb * qpb + (tid >> (log2g + log2s));
+    const bool q_ok = q < Q;
+    const int c0 = c * VEC;
+    const bool live = q_ok && (c0 < D);
+    const int split = 1 << log2s;
+    const int LK = L * K;
+    const int per_lane = LK >> log2s;
+
+    const int64_t pq = (b * Q + (q_ok ? q : 0)) * M + m;  // clamped: always a valid query
+    const E *loc_q = loc + pq * LK * 2;
+    const E *attn_q = attn + pq * LK;
+    const int64_t MD = (int64_t)M * D;
+    const int64_t row_bytes = MD * (int64_t)sizeof(E);
+    const Slice<BUF> slice(value + b * S * MD, S * row_bytes);
+    const int64_t lane_bytes = ((int64_t)m * D + (c0 < D ? c0 : 0)) * (int64_t)sizeof(E);
+    float g[VEC];
+    {
+        const R r = *reinterpret_cast<const R *>(grad_out + pq * D + (c0 < D ? c0 : 0));
+        raw_to_f32<DT, VEC>(live ? r : zero_raw<R>(), g);
+    }
+
+    for (int i0 = 0; i0 < per_lane; i0 += CH) {
+        uint32_t bx[CH], by[CH], ba[CH];
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            const int p = (i0 + t < per_lane ? i0 + t : 0) * split + s;
+            bx[t] = load_bits<DT>(loc_q + 2 * p);
+            by[t] = load_bits<DT>(loc_q + 2 * p + 1);
+            ba[t] = load_bits<DT>(attn_q + p);
+        }
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            pin(bx[t]);
+            pin(by[t]);
+            pin(ba[t]);
+        }
+        int64_t off[CH][4];
+        bool ok[CH][4];
+        float fx[CH], fy[CH], sw[CH], sh[CH];
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            const bool t_live = live && (i0 + t < per_lane);
+            int l = ((i0 + t) * split) / K;
+            l = l < L ? l : L - 1;
+            const int H = lt.H[l], W = lt.W[l];
+            const float aw = (q_ok && i0 + t < per_lane) ? bits_to_f32<DT>(ba[t]) : 0.0f;
+            sw[t] = (float)W * aw;
+            sh[t] = (float)H * aw;
+            const Cell cl = map_cell(bits_to_f32<DT>(bx[t]), bits_to_f32<DT>(by[t]), (float)H,
+                                     (float)W, W, lt.start[l]);
+            fx[t] = cl.fx;
+            fy[t] = cl.fy;
+            off[t][0] = cl.row00 * row_bytes + lane_bytes;
+            off[t][1] = off[t][0] + row_bytes;
+            off[t][2] = off[t][0] + (int64_t)W * row_bytes;
+            off[t][3] = off[t][2] + row_bytes;
+            ok[t][0] = t_live && cl.v00;
+            ok[t][1] = t_live && cl.v01;
+            ok[t][2] = t_live && cl.v10;
+            ok[t][3] = t_live && cl.v11;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        R raw[CH][4];
+#pragma unroll
+        for (int t = 0; t < CH; ++t)
+#pragma unroll
+            for (int cn = 0; cn < 4; ++cn) raw[t][cn] = slice.template gather<R>(off[t][cn], ok[t][cn]);
+        __builtin_amdgcn_sched_barrier(0);  // all 4 * CH gathers in flight before any use
+        float ds[CH], dx[CH], dy[CH];
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
+            raw_to_f32<DT, VEC>(raw[t][0], v00);
+            raw_to_f32<DT, VEC>(raw[t][1], v01);
+            raw_to_f32<DT, VEC>(raw[t][2], v10);
+            raw_to_f32<DT, VEC>(raw[t][3], v11);
+            const float gx = 1.0f - fx[t], gy = 1.0f - fy[t];
+            const float w00 = gx * gy, w01 = fx[t] * gy, w10 = gx * fy[t], w11 = fx[t] * fy[t];
+            ds[t] = dx[t] = dy[t] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                const float smp = w00 * v00[i] + w01 * v01[i] + w10 * v10[i] + w11 * v11[i];
+                const float sx = gy * (v01[i] - v00[i]) + fy[t] * (v11[i] - v10[i]);
+                const float sy = gx * (v10[i] - v00[i]) + fx[t] * (v11[i] - v01[i]);
+                ds[t] += g[i] * smp;
+                dx[t] += g[i] * sx;
+                dy[t] += g[i] * sy;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            ds[t] = group_sum(ds[t], log2g);
+            dx[t] = group_sum(dx[t], log2g) * sw[t];
+            dy[t] = group_sum(dy[t], log2g) * sh[t];
+        }
+        for (int t0 = 0; t0 < CH; t0 += G) {
+            const int t = t0 + c;
+            float vs = ds[0], vx = dx[0], vy = dy[0];
+#pragma unroll
+            for (int k = 1; k < CH; ++k) {
+                vs = t == k ? ds[k] : vs;
+                vx = t == k ? dx[k] : vx;
+                vy = t == k ? dy[k] : vy;
+            }
+            if (q_ok && t < CH && i0 + t < per_lane) {
+                const int64_t pp = pq * LK + (i0 + t) * split + s;
+                grad_attn[pp] = from_f32(DT{}, vs);
+                grad_loc[2 * pp] = from_f32(DT{}, vx);
+                grad_loc[2 * pp + 1] = from_f32(DT{}, vy);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------ backward
 //
 // Lane layout. MI355X's L2 executes atomics per request, one request covering
@@ -443,7 +589,7 @@ struct BwdChunk {
     static constexpr int value = J >= 8 ? 1 : (J >= 3 ? 2 : 8 / J);
 };
 
-template <class DT, int SLOT, int J, bool BUF, bool BIN>
+template <class DT, int SLOT, int J, bool BUF>
 __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
     const typename DT::S *__restrict__ value, const typename DT::S *__restrict__ loc,
     const typename DT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out,
@@ -572,19 +718,36 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
             dx[t] = group_sum(dx[t], log2g);
             dy[t] = group_sum(dy[t], log2g);
         }
+        // Every lane of the group holds the chunk's sums: lane c stores those
+        // of point t0 + c, so one instruction of the group writes up to G
+        // points' grad_attn (and grad_loc x, y) instead of one point each.
+        float gsx[CH], gsy[CH];
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            gsx[t] = (float)lt.W[lvl[t]] * aw[t] * dx[t];
+            gsy[t] = (float)lt.H[lvl[t]] * aw[t] * dy[t];
+        }
+        for (int t0 = 0; t0 < CH; t0 += G) {
+            const int t = t0 + c;
+            float vs = ds[0], vx = gsx[0], vy = gsy[0];
+#pragma unroll
+            for (int k = 1; k < CH; ++k) {
+                vs = t == k ? ds[k] : vs;
+                vx = t == k ? gsx[k] : vx;
+                vy = t == k ? gsy[k] : vy;
+            }
+            if (q_ok && t < CH && i0 + t < per_lane) {
+                const int64_t pp = pq * LK + (i0 + t) * split + s;
+                grad_attn[pp] = from_f32(DT{}, vs);
+                grad_loc[2 * pp] = from_f32(DT{}, vx);
+                grad_loc[2 * pp + 1] = from_f32(DT{}, vy);
+            }
+        }
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
             if (!(q_ok && i0 + t < per_lane)) continue;
             const int l = lvl[t];
-            const int p = (i0 + t) * split + s;
             const float fx = cl[t].fx, fy = cl[t].fy, gx = 1.0f - fx, gy = 1.0f - fy;
-            if (c == 0) {
-                const int64_t pp = pq * LK + p;
-                grad_attn[pp] = from_f32(DT{}, ds[t]);
-                grad_loc[2 * pp] = from_f32(DT{}, (float)lt.W[l] * aw[t] * dx[t]);
-                grad_loc[2 * pp + 1] = from_f32(DT{}, (float)lt.H[l] * aw[t] * dy[t]);
-            }
-            if constexpr (BIN) continue;  // grad_value: binned kernels
             if (lt.bin_shift[l] >= 0) continue;  // this level is binned
             const int W = lt.W[l];
             const int64_t start = lt.start[l];
@@ -1065,7 +1228,27 @@ hipError_t fwd_launch(const Problem &p, const Mapping &mp, const void *value, co
     return hipGetLastError();
 }
 
-template <class DT, int SLOT, int J, bool BIN>
+template <class DT, int VEC>
+hipError_t grad_launch(const Problem &p, const Mapping &mp, const void *value, const void *loc,
+                       const void *attn, const void *grad_out, void *grad_loc, void *grad_attn,
+                       hipStream_t stream) {
+    constexpr int CH = 4;
+    using E = typename DT::S;
+    const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
+    const int qblocks = (int)((p.Q + qpb - 1) / qpb);
+    const int64_t ntiles = p.B * p.M * qblocks;
+    const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
+    if (!slice_fits_buffer(p)) return hipErrorInvalidValue;  // binning requires it
+    hipLaunchKernelGGL((msda_grad_kernel<DT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
+                       dim3(kBlock), 0, stream, static_cast<const E *>(value),
+                       static_cast<const E *>(loc), static_cast<const E *>(attn),
+                       static_cast<const E *>(grad_out), static_cast<E *>(grad_loc),
+                       static_cast<E *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
+                       (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
+    return hipGetLastError();
+}
+
+template <class DT, int SLOT, int J>
 hipError_t bwd_launch(const Problem &p, const BwdMapping &mp, const void *value, const void *loc,
                       const void *attn, const void *grad_out, void *grad_value, float *workspace,
                       void *grad_loc, void *grad_attn, hipStream_t stream) {
@@ -1075,7 +1258,7 @@ hipError_t bwd_launch(const Problem &p, const BwdMapping &mp, const void *value,
     const int64_t ntiles = p.B * p.M * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (slice_fits_buffer(p))
-        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, true, BIN>),
+        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, true>),
                            dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
                            static_cast<const E *>(value), static_cast<const E *>(loc),
                            static_cast<const E *>(attn), static_cast<const E *>(grad_out),
@@ -1083,7 +1266,7 @@ hipError_t bwd_launch(const Problem &p, const BwdMapping &mp, const void *value,
                            static_cast<E *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
                            (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
     else
-        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, false, BIN>),
+        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, false>),
                            dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
                            static_cast<const E *>(value), static_cast<const E *>(loc),
                            static_cast<const E *>(attn), static_cast<const E *>(grad_out),
@@ -1140,21 +1323,38 @@ hipError_t fwd_by_vec(const Problem &p, const Mapping &mp, const void *v, const 
     return hipErrorInvalidValue;
 }
 
-template <class DT, int SLOT, bool BIN>
+template <class DT, int SLOT>
 hipError_t bwd_by_j(const Problem &p, const BwdMapping &mp, const void *v, const void *l,
                     const void *a, const void *go, void *gv, float *ws, void *gl, void *ga,
                     hipStream_t st) {
     switch (mp.j) {
-        case 1: return bwd_launch<DT, SLOT, 1, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 2: return bwd_launch<DT, SLOT, 2, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 3: return bwd_launch<DT, SLOT, 3, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 4: return bwd_launch<DT, SLOT, 4, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 8: return bwd_launch<DT, SLOT, 8, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 16: return bwd_launch<DT, SLOT, 16, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 1: return bwd_launch<DT, SLOT, 1>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 2: return bwd_launch<DT, SLOT, 2>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 3: return bwd_launch<DT, SLOT, 3>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 4: return bwd_launch<DT, SLOT, 4>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 8: return bwd_launch<DT, SLOT, 8>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 16: return bwd_launch<DT, SLOT, 16>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
         default: break;
     }
     if constexpr (SLOT == 1) {
-        if (mp.j == 32) return bwd_launch<DT, SLOT, 32, BIN>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        if (mp.j == 32) return bwd_launch<DT, SLOT, 32>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class DT>
+hipError_t grad_by_vec(const Problem &p, const Mapping &mp, const void *v, const void *l,
+                       const void *a, const void *go, void *gl, void *ga, hipStream_t st) {
+    switch (mp.vec) {
+        case 1: return grad_launch<DT, 1>(p, mp, v, l, a, go, gl, ga, st);
+        case 2: return grad_launch<DT, 2>(p, mp, v, l, a, go, gl, ga, st);
+        case 4: return grad_launch<DT, 4>(p, mp, v, l, a, go, gl, ga, st);
+        default: break;
+    }
+    if constexpr (sizeof(typename DT::S) == 4) {
+        if (mp.vec == 3) return grad_launch<DT, 3>(p, mp, v, l, a, go, gl, ga, st);
+    } else {
+        if (mp.vec == 8) return grad_launch<DT, 8>(p, mp, v, l, a, go, gl, ga, st);
     }
     return hipErrorInvalidValue;
 }
@@ -1227,31 +1427,6 @@ hipError_t scratch_add(const Problem &p, const float *ws, void *gv, hipStream_t 
     return hipGetLastError();
 }
 
-template <bool BIN>
-hipError_t backward_dispatch(const Problem &p, const BwdMapping &mp, const void *value,
-                             const void *loc, const void *attn, const void *grad_out,
-                             void *grad_value, float *workspace, void *grad_loc, void *grad_attn,
-                             hipStream_t stream) {
-    switch (p.dtype) {
-        case MSDA_F32:
-            return bwd_by_j<F32T, 1, BIN>(p, mp, value, loc, attn, grad_out, grad_value, workspace,
-                                          grad_loc, grad_attn, stream);
-        case MSDA_F16:
-            return mp.slot == 2
-                       ? bwd_by_j<F16T, 2, BIN>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                workspace, grad_loc, grad_attn, stream)
-                       : bwd_by_j<F16T, 1, BIN>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                workspace, grad_loc, grad_attn, stream);
-        case MSDA_BF16:
-            return mp.slot == 2
-                       ? bwd_by_j<BF16T, 2, BIN>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                 workspace, grad_loc, grad_attn, stream)
-                       : bwd_by_j<BF16T, 1, BIN>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                 workspace, grad_loc, grad_attn, stream);
-        default: return hipErrorInvalidValue;
-    }
-}
-
 }  // namespace
 
 hipError_t launch_forward(const Problem &p, const Mapping &mp, const void *value,
@@ -1268,15 +1443,33 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
                            const void *loc, const void *attn, const void *grad_out,
                            void *grad_value, float *workspace, void *grad_loc, void *grad_attn,
                            hipStream_t stream) {
-    return backward_dispatch<false>(p, mp, value, loc, attn, grad_out, grad_value, workspace,
-                                    grad_loc, grad_attn, stream);
+    switch (p.dtype) {
+        case MSDA_F32:
+            return bwd_by_j<F32T, 1>(p, mp, value, loc, attn, grad_out, grad_value, workspace,
+                                     grad_loc, grad_attn, stream);
+        case MSDA_F16:
+            return mp.slot == 2 ? bwd_by_j<F16T, 2>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                    workspace, grad_loc, grad_attn, stream)
+                                : bwd_by_j<F16T, 1>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                    workspace, grad_loc, grad_attn, stream);
+        case MSDA_BF16:
+            return mp.slot == 2 ? bwd_by_j<BF16T, 2>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                     workspace, grad_loc, grad_attn, stream)
+                                : bwd_by_j<BF16T, 1>(p, mp, value, loc, attn, grad_out, grad_value,
+                                                     workspace, grad_loc, grad_attn, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
-hipError_t launch_backward_binned(const Problem &p, const BwdMapping &mp, const void *value,
-                                  const void *loc, const void *attn, const void *grad_out,
-                                  void *grad_loc, void *grad_attn, hipStream_t stream) {
-    return backward_dispatch<true>(p, mp, value, loc, attn, grad_out, nullptr, nullptr, grad_loc,
-                                   grad_attn, stream);
+hipError_t launch_gradients(const Problem &p, const Mapping &mp, const void *value,
+                            const void *loc, const void *attn, const void *grad_out,
+                            void *grad_loc, void *grad_attn, hipStream_t stream) {
+    switch (p.dtype) {
+        case MSDA_F32: return grad_by_vec<F32T>(p, mp, value, loc, attn, grad_out, grad_loc, grad_attn, stream);
+        case MSDA_F16: return grad_by_vec<F16T>(p, mp, value, loc, attn, grad_out, grad_loc, grad_attn, stream);
+        case MSDA_BF16: return grad_by_vec<BF16T>(p, mp, value, loc, attn, grad_out, grad_loc, grad_attn, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,

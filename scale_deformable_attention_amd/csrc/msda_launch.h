@@ -72,7 +72,8 @@ hipError_t launch_forward(const Problem &p, const Mapping &mp, const void *value
 
 // Scatter kernel: writes grad_loc / grad_attn, adds into grad_value (levels
 // with scratch_off < 0; fp32 adds for fp32 data, packed adds for 16-bit data)
-// and into the fp32 workspace (levels with scratch_off >= 0).
+// and into the fp32 workspace (levels with scratch_off >= 0); binned levels
+// (bin_shift >= 0) are left to the binned kernels.
 hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *value,
                            const void *loc, const void *attn, const void *grad_out,
                            void *grad_value, float *workspace, void *grad_loc, void *grad_attn,
@@ -81,14 +82,16 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
 // Binned grad_value, in stream order: zero starts[0:nbins] (launch_zero);
 // launch_bin_sort(place = false) counts the in-bounds corners per bin into
 // starts; launch_bin_scan turns the counts into starts and cursors;
-// launch_bin_sort(place = true) writes the records; launch_backward_binned
-// writes grad_loc / grad_attn only; launch_bin_accumulate writes grad_value.
+// launch_bin_sort(place = true) writes the records; launch_gradients (every
+// level binned) or launch_backward (the other levels' atomics) writes
+// grad_loc / grad_attn; launch_bin_accumulate writes grad_value.
 hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
                            const BinnedBuffers &bins, bool place, hipStream_t stream);
 hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream);
-hipError_t launch_backward_binned(const Problem &p, const BwdMapping &mp, const void *value,
-                                  const void *loc, const void *attn, const void *grad_out,
-                                  void *grad_loc, void *grad_attn, hipStream_t stream);
+// grad_loc / grad_attn only, in the forward's lane mapping (every level binned).
+hipError_t launch_gradients(const Problem &p, const Mapping &mp, const void *value,
+                            const void *loc, const void *attn, const void *grad_out,
+                            void *grad_loc, void *grad_attn, hipStream_t stream);
 hipError_t launch_bin_accumulate(const Problem &p, const BwdMapping &mp, const void *grad_out,
                                  void *grad_value, const BinnedBuffers &bins, bool accumulate,
                                  hipStream_t stream);
