@@ -5,7 +5,7 @@ The computation runs in hand-written gfx950 HIP kernels behind a C ABI
 
     msda_forward, msda_backward          the C entry points, with torch tensors
     PreparedCall                         the same calls pre-marshalled for loops
-    multi_scale_deformable_attention     autograd wrapper (added in autograd.py)
+    multi_scale_deformable_attention     autograd wrapper (autograd.py)
     workloads                            seeded synthetic inputs
 
 The library is loaded on first use, so importing the package (for example for
@@ -15,6 +15,8 @@ the input generators) needs neither a GPU nor a built library.
 from ._binding import (ACCUM_AUTO, ACCUM_FP32_SCRATCH, ACCUM_NATIVE, EXPORTED_SYMBOLS,  # noqa: F401
                        MSDAError, PreparedCall, load_library, msda_backward,
                        msda_backward_resolve_accum, msda_backward_workspace_size, msda_forward)
+from .autograd import MultiScaleDeformableAttnFunction, multi_scale_deformable_attention
 
 __all__ = ["msda_forward", "msda_backward", "msda_backward_workspace_size",
-           "msda_backward_resolve_accum", "MSDAError", "PreparedCall", "load_library"]
+           "msda_backward_resolve_accum", "MSDAError", "PreparedCall", "load_library",
+           "multi_scale_deformable_attention", "MultiScaleDeformableAttnFunction"]

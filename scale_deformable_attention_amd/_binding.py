@@ -233,8 +233,9 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index,
                   continue_scratch: bool = False, defer_scratch: bool = False
                   ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Backward of the MSDA core: (grad_value, grad_sampling_locations,
-    grad_attention_weights). `accum` is "auto", "native" or "fp32_scratch"
-    (True/False/None are accepted as in the pages' fp32_grad_accum switch).
+    grad_attention_weights). `accum` is "auto", "native", "fp32_scratch",
+    "per_level", "binned" or "mixed" (True/False/None are accepted as in the
+    pages' fp32_grad_accum switch).
     With `accumulate`, grad_value (given) is added into instead of overwritten.
     `continue_scratch` / `defer_scratch` map to MSDA_FLAG_CONTINUE_SCRATCH /
     MSDA_FLAG_DEFER_SCRATCH (fp32 accumulation across calls in `workspace`)."""
