@@ -24,11 +24,13 @@ Algorithmic bytes per launch (e = element size, P = B*Q*M*L*K points,
 U = distinct (b, row, m) value rows with at least one in-bounds corner,
 C = in-bounds corners, N = B*S*M*D grad_value elements):
   forward          3*P*e (locations + weights) + B*Q*M*D*e (output) + U*D*e
-  backward kernel  (msda_bwd_kernel; msda_grad_kernel when every level is binned)
+  backward kernel  (msda_bwd_kernel; msda_grad_kernel without the atomics term
+                   when some level is binned)
                    3*P*e (params) + B*Q*M*D*e (grad_output) + U*D*e (value)
                    + 3*P*e (grad locations + grad weights)
                    + atomics: 2*U'*D*e_acc (read-modify-write of the touched rows
                      of levels not binned; e_acc = 4 for fp32 rows)
+  scatter          3*(P-P')*e + B*Q*M*D*e + 2*U'*D*e_acc (atomics of the unbinned levels)
   binned levels only (P', C', N' = their points, corners, grad_value elements):
   bin count        2*P'*e;  bin place  3*P'*e + 8*C' (records written)
   bin accumulate   8*C' + B*Q*M*D*e + N'*e
@@ -298,14 +300,17 @@ def main():
     bwd_names = {
         "binned": ["bin_zero", "bin_count", "bin_scan", "bin_place", "msda_grad_kernel",
                    "bin_accum_kernel"],
-        "mixed": ["zero_fill", "bin_zero", "bin_count", "bin_scan", "bin_place", "msda_bwd_kernel",
-                  "bin_accum_kernel"],
+        "mixed": ["zero_fill", "bin_zero", "bin_count", "bin_scan", "bin_place", "msda_grad_kernel",
+                  "msda_scatter_kernel", "bin_accum_kernel"],
         "native": ["zero_fill", "msda_bwd_kernel"],
         "per_level": ["zero_fill", "scratch_zero", "msda_bwd_kernel", "scratch_add_kernel"],
         "fp32_scratch": ["zero_fill", "scratch_zero", "msda_bwd_kernel", "scratch_add_kernel"],
     }[call.resolved_accum]
     if n_bwd == len(bwd_names) + 1:  # binned with padding rows: grad_value fill first
         bwd_names = ["zero_fill"] + bwd_names
+    if call.resolved_accum == "mixed" and wl.dtype == torch.float32:  # one fused kernel
+        bwd_names = [n for n in bwd_names if n != "msda_scatter_kernel"]
+        bwd_names[bwd_names.index("msda_grad_kernel")] = "msda_bwd_kernel"
     assert n_bwd == len(bwd_names), (n_bwd, bwd_names)
     ktimes = {"msda_fwd_kernel": float(np.mean([evs[i][0].elapsed_time(evs[i][1])
                                                  for i in range(n_inst)])) * 1e3}
@@ -336,6 +341,8 @@ def main():
               # atomics: read-modify-write of the touched rows of unbinned levels
               "msda_bwd_kernel": common + 2 * ((U - U_scr - U_bin) * D * e_acc + U_scr * D * 4),
               "msda_grad_kernel": common,
+              "msda_scatter_kernel": 3 * (P - P_bin) * e + B * Q * M * D * e
+              + 2 * (U - U_bin) * D * e_acc,
               "bin_zero": (nb + 1) * 4, "bin_count": 2 * P_bin * e, "bin_scan": 3 * nb * 4,
               "bin_place": 3 * P_bin * e + 8 * C_bin,
               "bin_accum_kernel": 8 * C_bin + B * Q * M * D * e + bin_rows * D * e}

@@ -322,7 +322,8 @@ bool plan_bins(msda::Problem *p, BinPlan *bp, bool contended_only) {
             ++sh;
         p->levels.bin_shift[l] = sh;
         nbbm += (HW + (1 << sh) - 1) >> sh;
-        ++nlev;
+        p->levels.blevel[nlev++] = l;
+        p->levels.nblev = nlev;
         if (nbbm >= ((int64_t)1 << 31)) return false;
     }
     const int64_t nbins = p->B * p->M * nbbm;
@@ -341,7 +342,9 @@ void clear_bins(msda::Problem *p) {
     for (int l = 0; l < MSDA_MAX_LEVELS; ++l) {
         p->levels.bin_shift[l] = -1;
         p->levels.bin_off[l] = 0;
+        p->levels.blevel[l] = 0;
     }
+    p->levels.nblev = 0;
     p->nbbm = 0;
 }
 
@@ -585,7 +588,7 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                     "native half-precision atomics need a 4-byte aligned grad_value with an even "
                     "element count; use MSDA_ACCUM_FP32_SCRATCH");
     msda::BwdMapping mp = {1, 1, 0, 0};
-    msda::Mapping gmp = {1, 0, 0};  // gradients-only kernel (every level binned)
+    msda::Mapping gmp = {1, 0, 0};  // gradients-only kernel (binned modes)
     if (p.Q > 0) {
         if ((st = check_ptr(sampling_locations, "sampling_locations", dtype))) return st;
         if ((st = check_ptr(attention_weights, "attention_weights", dtype))) return st;
@@ -595,7 +598,7 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
         const bool pairs = aligned(value, 4) && aligned(grad_output, 4) && aligned(grad_value, 4);
         if ((st = choose_bwd_mapping(p, pairs, &mp))) return st;
         const void *vec_ptrs[2] = {value, grad_output};
-        if (all_binned && (st = choose_mapping(p, vec_ptrs, 2, &gmp))) return st;
+        if (binned && (st = choose_mapping(p, vec_ptrs, 2, &gmp))) return st;
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t gv_bytes = (size_t)(p.B * p.S * p.M * p.D) * elem_size(dtype);
@@ -629,19 +632,30 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                                                 true, before(s)),
                           s)) != hipSuccess)
             return hip_fail(err, "bin place launch");
-        // every level binned: the backward writes only grad_loc / grad_attn;
-        // otherwise it adds the unbinned levels' grad_value with atomics
-        if ((err = marked(all_binned
-                              ? msda::launch_gradients(p, gmp, value, sampling_locations,
-                                                       attention_weights, grad_output,
-                                                       grad_sampling_locations,
-                                                       grad_attention_weights, before(s))
-                              : msda::launch_backward(p, mp, value, sampling_locations,
-                                                      attention_weights, grad_output, grad_value,
-                                                      nullptr, grad_sampling_locations,
-                                                      grad_attention_weights, before(s)),
-                          s)) != hipSuccess)
+        // grad_loc / grad_attn in the forward's lane mapping, and the unbinned
+        // levels' grad_value (if any) by a gather-free atomic scatter. fp32
+        // rows of unbinned levels span several 64-byte atomic segments; there
+        // the fused kernel, which overlaps those atomics with its gathers,
+        // measures faster than the two separate passes.
+        if (all_binned || dtype != MSDA_F32) {
+            if ((err = marked(msda::launch_gradients(p, gmp, value, sampling_locations,
+                                                     attention_weights, grad_output,
+                                                     grad_sampling_locations,
+                                                     grad_attention_weights, before(s)),
+                              s)) != hipSuccess)
+                return hip_fail(err, "gradient launch");
+            if (!all_binned &&
+                (err = marked(msda::launch_scatter(p, mp, sampling_locations, attention_weights,
+                                                   grad_output, grad_value, nullptr, before(s)),
+                              s)) != hipSuccess)
+                return hip_fail(err, "scatter launch");
+        } else if ((err = marked(msda::launch_backward(p, mp, value, sampling_locations,
+                                                       attention_weights, grad_output, grad_value,
+                                                       nullptr, grad_sampling_locations,
+                                                       grad_attention_weights, before(s)),
+                                 s)) != hipSuccess) {
             return hip_fail(err, "backward launch");
+        }
         if ((err = marked(msda::launch_bin_accumulate(p, mp, grad_output, grad_value, bins,
                                                       accumulate, before(s)),
                           s)) != hipSuccess)

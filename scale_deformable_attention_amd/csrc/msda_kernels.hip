@@ -583,6 +583,92 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
 // upstream gradient is also held in channel layout (channel c + iG) so that
 // every fp32 atomic instruction covers G consecutive dwords.
 
+// grad_value += A * w_ij * g on the in-bounds corners of one point of level l
+// (course page "5. The backward kernel", section "Scatter needs atomics"):
+// fp32 atomics in channel layout (channel c + iG) for fp32 targets (fp32 data,
+// or the level's fp32 scratch), packed 16-bit atomics in slot layout (slot
+// c + jG) otherwise. Levels that are binned are skipped by the callers.
+template <class DT, int SLOT, int J>
+__device__ __forceinline__ void scatter_point(const Cell &cl, float aw, const LevelTable &lt,
+                                              int l, void *grad_value, float *workspace,
+                                              int64_t b, int64_t bS, int m, int M, int D,
+                                              int64_t MD, int c, int G, const bool (&slot_ok)[J],
+                                              const float (&g)[J][SLOT],
+                                              const float (&gc)[J * SLOT]) {
+    constexpr bool kF32 = sizeof(typename DT::S) == 4;
+    constexpr int JC = J * SLOT;
+    const float fx = cl.fx, fy = cl.fy, gx = 1.0f - fx, gy = 1.0f - fy;
+    const int W = lt.W[l];
+    const int64_t start = lt.start[l];
+    const int64_t soff = lt.scratch_off[l];
+    const int64_t HW = (int64_t)lt.H[l] * W;
+    const bool vc[4] = {cl.v00, cl.v01, cl.v10, cl.v11};
+    const float coef[4] = {aw * gx * gy, aw * fx * gy, aw * gx * fy, aw * fx * fy};
+    const int64_t drow[4] = {0, 1, W, (int64_t)W + 1};  // pixel rows from row00
+#pragma unroll
+    for (int cn = 0; cn < 4; ++cn) {
+        if (!vc[cn]) continue;
+        const int64_t row = cl.row00 + drow[cn];
+        if (kF32 || soff >= 0) {
+            float *tp = kF32 ? static_cast<float *>(grad_value) + (bS + row) * MD + (int64_t)m * D
+                             : workspace + soff + ((b * HW + (row - start)) * M + m) * (int64_t)D;
+#pragma unroll
+            for (int i = 0; i < JC; ++i) {
+                const int ch = c + i * G;
+                if (ch < D) atomic_add_f32(tp + ch, coef[cn] * gc[i]);
+            }
+        } else if constexpr (!kF32) {
+            uint16_t *tp = static_cast<uint16_t *>(grad_value) + (bS + row) * MD + (int64_t)m * D;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                if (!slot_ok[j]) continue;
+                uint16_t *e = tp + (int64_t)(c + j * G) * SLOT;
+                if constexpr (SLOT == 2) {
+                    // one dword, 4-byte aligned (host-checked)
+                    atomic_add_pk(DT{}, e, coef[cn] * g[j][0], coef[cn] * g[j][1]);
+                } else {
+                    // single element: packed add on the enclosing aligned word
+                    // with +0 for the neighbour (x + 0 == x); the host
+                    // guarantees that word lies inside grad_value
+                    const bool hi = (reinterpret_cast<uintptr_t>(e) & 2) != 0;
+                    uint16_t *wd = reinterpret_cast<uint16_t *>(reinterpret_cast<uintptr_t>(e) &
+                                                                ~uintptr_t(3));
+                    const float v = coef[cn] * g[j][0];
+                    atomic_add_pk(DT{}, wd, hi ? 0.0f : v, hi ? v : 0.0f);
+                }
+            }
+        }
+    }
+}
+
+// The query's upstream gradient in slot layout (g, slot c + jG) and, for fp32
+// targets, in channel layout (gc, channel c + iG).
+template <class DT, int SLOT, int J>
+__device__ __forceinline__ void load_upstream(const typename DT::S *grad_out, int64_t pq, int D,
+                                              int c, int G, bool q_ok, bool (&slot_ok)[J],
+                                              float (&g)[J][SLOT], float (&gc)[J * SLOT]) {
+    using R = typename RawVec<SLOT * (int)sizeof(typename DT::S)>::type;
+    const int nslots = D / SLOT;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int sl = c + j * G;
+        slot_ok[j] = q_ok && sl < nslots;
+        const R r = *reinterpret_cast<const R *>(grad_out + pq * D + (sl < nslots ? sl : 0) * SLOT);
+        raw_to_f32<DT, SLOT>(slot_ok[j] ? r : zero_raw<R>(), g[j]);
+    }
+    if constexpr (SLOT == 1) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) gc[j] = g[j][0];
+    } else {
+#pragma unroll
+        for (int i = 0; i < J * SLOT; ++i) {
+            const int ch = c + i * G;
+            const float v = to_f32(DT{}, grad_out[pq * D + (ch < D ? ch : 0)]);
+            gc[i] = (q_ok && ch < D) ? v : 0.0f;
+        }
+    }
+}
+
 // Points per chunk for the backward: about 8 slots of corner data per lane.
 template <int J>
 struct BwdChunk {
@@ -600,7 +686,6 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
     const int log2s) {
     using E = typename DT::S;
     using R = typename RawVec<SLOT * (int)sizeof(E)>::type;  // one slot
-    constexpr bool kF32 = sizeof(E) == 4;
     constexpr int JC = J * SLOT;  // fp32-channel-layout registers per lane
     constexpr int CH = BwdChunk<J>::value;
     const int64_t tile = logical_block();
@@ -620,7 +705,6 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
     const int split = 1 << log2s;
     const int LK = L * K;
     const int per_lane = LK >> log2s;
-    const int nslots = D / SLOT;
 
     const int64_t pq = (b * Q + (q_ok ? q : 0)) * M + m;  // clamped: always a valid query
     const E *loc_q = loc + pq * LK * 2;
@@ -631,29 +715,9 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
     const Slice<BUF> slice(value + bS * MD, S * row_bytes);
     const int64_t head_bytes = (int64_t)m * D * (int64_t)sizeof(E);
 
-    // the query's upstream gradient in slot layout (slot c + jG) ...
     bool slot_ok[J];
-    float g[J][SLOT];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int sl = c + j * G;
-        slot_ok[j] = q_ok && sl < nslots;
-        const R r = *reinterpret_cast<const R *>(grad_out + pq * D + (sl < nslots ? sl : 0) * SLOT);
-        raw_to_f32<DT, SLOT>(slot_ok[j] ? r : zero_raw<R>(), g[j]);
-    }
-    // ... and in channel layout (channel c + iG) for fp32 atomics
-    float gc[JC];
-    if constexpr (SLOT == 1) {
-#pragma unroll
-        for (int j = 0; j < J; ++j) gc[j] = g[j][0];
-    } else {
-#pragma unroll
-        for (int i = 0; i < JC; ++i) {
-            const int ch = c + i * G;
-            const float v = to_f32(DT{}, grad_out[pq * D + (ch < D ? ch : 0)]);
-            gc[i] = (q_ok && ch < D) ? v : 0.0f;
-        }
-    }
+    float g[J][SLOT], gc[JC];
+    load_upstream<DT, SLOT, J>(grad_out, pq, D, c, G, q_ok, slot_ok, g, gc);
 
     for (int i0 = 0; i0 < per_lane; i0 += CH) {
         float lx[CH], ly[CH], aw[CH];
@@ -746,49 +810,78 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
             if (!(q_ok && i0 + t < per_lane)) continue;
-            const int l = lvl[t];
-            const float fx = cl[t].fx, fy = cl[t].fy, gx = 1.0f - fx, gy = 1.0f - fy;
-            if (lt.bin_shift[l] >= 0) continue;  // this level is binned
-            const int W = lt.W[l];
-            const int64_t start = lt.start[l];
-            const int64_t soff = lt.scratch_off[l];
-            const int64_t HW = (int64_t)lt.H[l] * W;
-            const bool vc[4] = {cl[t].v00, cl[t].v01, cl[t].v10, cl[t].v11};
-            const float coef[4] = {aw[t] * gx * gy, aw[t] * fx * gy, aw[t] * gx * fy, aw[t] * fx * fy};
-            const int64_t drow[4] = {0, 1, W, (int64_t)W + 1};  // pixel rows from row00
+            if (lt.bin_shift[lvl[t]] >= 0) continue;  // this level is binned
+            scatter_point<DT, SLOT, J>(cl[t], aw[t], lt, lvl[t], grad_value, workspace, b, bS, m,
+                                       M, D, MD, c, G, slot_ok, g, gc);
+        }
+    }
+}
+
+// Atomic scatter only (course page "5. The backward kernel", section
+// "Scatter needs atomics"), for the levels that are not binned when
+// grad_loc / grad_attn come from msda_grad_kernel: no value gathers, no dot
+// products. Same lane mapping as msda_bwd_kernel; a group walks the points of
+// each unbinned level, CH at a time with their parameter loads issued first.
+template <class DT, int SLOT, int J>
+__global__ __launch_bounds__(kBlock) void msda_scatter_kernel(
+    const typename DT::S *__restrict__ loc, const typename DT::S *__restrict__ attn,
+    const typename DT::S *__restrict__ grad_out, void *__restrict__ grad_value,
+    float *__restrict__ workspace, const LevelTable lt, const int64_t S, const int64_t Q,
+    const int M, const int D, const int L, const int K, const int qblocks, const int64_t ntiles,
+    const int log2g, const int log2s) {
+    using E = typename DT::S;
+    constexpr int JC = J * SLOT;
+    constexpr int CH = 8;
+    const int64_t tile = logical_block();
+    if (tile >= ntiles) return;
+    const int64_t bm = tile / qblocks;
+    const int qb = (int)(tile - bm * qblocks);
+    const int64_t b = bm / M;
+    const int m = (int)(bm - b * M);
+    const int tid = threadIdx.x;
+    const int G = 1 << log2g;
+    const int c = tid & (G - 1);
+    const int s = (tid >> log2g) & ((1 << log2s) - 1);
+    const int qpb = kBlock >> (log2g + log2s);
+    const int64_t q = (int64_t)qb * qpb + (tid >> (log2g + log2s));
+    const bool q_ok = q < Q;
+    const int split = 1 << log2s;
+    const int LK = L * K;
+    const int64_t pq = (b * Q + (q_ok ? q : 0)) * M + m;  // clamped: always a valid query
+    const E *loc_q = loc + pq * LK * 2;
+    const E *attn_q = attn + pq * LK;
+    const int64_t MD = (int64_t)M * D;
+    const int64_t bS = b * S;
+    bool slot_ok[J];
+    float g[J][SLOT], gc[JC];
+    load_upstream<DT, SLOT, J>(grad_out, pq, D, c, G, q_ok, slot_ok, g, gc);
+    for (int l = 0; l < L; ++l) {
+        if (lt.bin_shift[l] >= 0) continue;  // binned: handled by the binned kernels
+        const int W = lt.W[l];
+        const float Hf = (float)lt.H[l], Wf = (float)W;
+        for (int k0 = 0; k0 < K; k0 += split * CH) {
+            uint32_t bx[CH], by[CH], ba[CH];
 #pragma unroll
-            for (int cn = 0; cn < 4; ++cn) {
-                if (!vc[cn]) continue;
-                const int64_t row = cl[t].row00 + drow[cn];
-                if (kF32 || soff >= 0) {
-                    float *tp = kF32 ? static_cast<float *>(grad_value) + (bS + row) * MD + (int64_t)m * D
-                                     : workspace + soff + ((b * HW + (row - start)) * M + m) * (int64_t)D;
+            for (int t = 0; t < CH; ++t) {
+                const int k = k0 + t * split;  // + s: the group's own point of this stride
+                const int p = l * K + (k < K ? k + s : s);
+                bx[t] = load_bits<DT>(loc_q + 2 * p);
+                by[t] = load_bits<DT>(loc_q + 2 * p + 1);
+                ba[t] = load_bits<DT>(attn_q + p);
+            }
 #pragma unroll
-                    for (int i = 0; i < JC; ++i) {
-                        const int ch = c + i * G;
-                        if (ch < D) atomic_add_f32(tp + ch, coef[cn] * gc[i]);
-                    }
-                } else if constexpr (!kF32) {
-                    uint16_t *tp = static_cast<uint16_t *>(grad_value) + (bS + row) * MD + (int64_t)m * D;
+            for (int t = 0; t < CH; ++t) {
+                pin(bx[t]);
+                pin(by[t]);
+                pin(ba[t]);
+            }
 #pragma unroll
-                    for (int j = 0; j < J; ++j) {
-                        if (!slot_ok[j]) continue;
-                        uint16_t *e = tp + (int64_t)(c + j * G) * SLOT;
-                        if constexpr (SLOT == 2) {
-                            // one dword, 4-byte aligned (host-checked)
-                            atomic_add_pk(DT{}, e, coef[cn] * g[j][0], coef[cn] * g[j][1]);
-                        } else {
-                            // single element: packed add on the enclosing aligned
-                            // word with +0 for the neighbour (x + 0 == x); the
-                            // host guarantees that word lies inside grad_value
-                            const bool hi = (reinterpret_cast<uintptr_t>(e) & 2) != 0;
-                            uint16_t *wd = reinterpret_cast<uint16_t *>(
-                                reinterpret_cast<uintptr_t>(e) & ~uintptr_t(3));
-                            const float v = coef[cn] * g[j][0];
-                            atomic_add_pk(DT{}, wd, hi ? 0.0f : v, hi ? v : 0.0f);
-                        }
-                    }
-                }
+            for (int t = 0; t < CH; ++t) {
+                if (!(q_ok && k0 + t * split < K)) continue;
+                const Cell cl = map_cell(bits_to_f32<DT>(bx[t]), bits_to_f32<DT>(by[t]), Hf, Wf, W,
+                                         lt.start[l]);
+                scatter_point<DT, SLOT, J>(cl, bits_to_f32<DT>(ba[t]), lt, l, grad_value, workspace,
+                                           b, bS, m, M, D, MD, c, G, slot_ok, g, gc);
             }
         }
     }
@@ -813,8 +906,9 @@ constexpr int kHashBits = 11;
 constexpr int kHashSlots = 1 << kHashBits;   // > 4 corners x kBlock points: never full
 constexpr uint32_t kEmptyKey = 0xFFFFFFFFu;  // bin ids stay below 2^31
 
-// One thread per point of one (b, m): workgroup w of pair bm takes the
-// (query, point) indices [w * kBlock, (w + 1) * kBlock) of that pair. Count
+// One thread per point of a binned level of one (b, m): workgroup w of pair bm
+// takes the (query, binned point) indices [w * kBlock, (w + 1) * kBlock) of
+// that pair. Count
 // (PLACE = false) adds the workgroup's per-bin totals to counter[bin]. Place
 // (PLACE = true) reserves a range of each bin with one returning atomic on
 // counter[bin] (the bin's cursor, initialised to its start by the scan) and
@@ -846,11 +940,13 @@ __global__ __launch_bounds__(kBlock) void bin_sort_kernel(
     const int64_t b = bm / M;
     const int m = (int)(bm - b * M);
     const int LK = L * K;
+    const int LKb = lt.nblev * K;  // points of the binned levels per query
     const int64_t i = w * kBlock + tid;
-    const bool ok = i < Q * LK;
-    const int64_t q = ok ? i / LK : 0;
-    const int pp = ok ? (int)(i - q * LK) : 0;
-    const int l = pp / K;
+    const bool ok = i < Q * LKb;
+    const int64_t q = ok ? i / LKb : 0;
+    const int r = ok ? (int)(i - q * LKb) : 0;
+    const int l = lt.blevel[r / K];
+    const int pp = l * K + (r - (r / K) * K);
     const int64_t pt = ((b * Q + q) * M + m) * LK + pp;
     float x, y;
     load_xy<DT>(loc + 2 * pt, x, y);
@@ -1323,6 +1419,41 @@ hipError_t fwd_by_vec(const Problem &p, const Mapping &mp, const void *v, const 
     return hipErrorInvalidValue;
 }
 
+template <class DT, int SLOT, int J>
+hipError_t scatter_launch(const Problem &p, const BwdMapping &mp, const void *loc, const void *attn,
+                          const void *grad_out, void *grad_value, float *workspace,
+                          hipStream_t stream) {
+    using E = typename DT::S;
+    const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
+    const int qblocks = (int)((p.Q + qpb - 1) / qpb);
+    const int64_t ntiles = p.B * p.M * qblocks;
+    const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL((msda_scatter_kernel<DT, SLOT, J>), dim3((unsigned)(per_xcd * kXcds)),
+                       dim3(kBlock), 0, stream, static_cast<const E *>(loc),
+                       static_cast<const E *>(attn), static_cast<const E *>(grad_out), grad_value,
+                       workspace, p.levels, p.S, p.Q, (int)p.M, (int)p.D, (int)p.L, (int)p.K,
+                       qblocks, ntiles, mp.log2_group, mp.log2_split);
+    return hipGetLastError();
+}
+
+template <class DT, int SLOT>
+hipError_t scatter_by_j(const Problem &p, const BwdMapping &mp, const void *l, const void *a,
+                        const void *go, void *gv, float *ws, hipStream_t st) {
+    switch (mp.j) {
+        case 1: return scatter_launch<DT, SLOT, 1>(p, mp, l, a, go, gv, ws, st);
+        case 2: return scatter_launch<DT, SLOT, 2>(p, mp, l, a, go, gv, ws, st);
+        case 3: return scatter_launch<DT, SLOT, 3>(p, mp, l, a, go, gv, ws, st);
+        case 4: return scatter_launch<DT, SLOT, 4>(p, mp, l, a, go, gv, ws, st);
+        case 8: return scatter_launch<DT, SLOT, 8>(p, mp, l, a, go, gv, ws, st);
+        case 16: return scatter_launch<DT, SLOT, 16>(p, mp, l, a, go, gv, ws, st);
+        default: break;
+    }
+    if constexpr (SLOT == 1) {
+        if (mp.j == 32) return scatter_launch<DT, SLOT, 32>(p, mp, l, a, go, gv, ws, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <class DT, int SLOT>
 hipError_t bwd_by_j(const Problem &p, const BwdMapping &mp, const void *v, const void *l,
                     const void *a, const void *go, void *gv, float *ws, void *gl, void *ga,
@@ -1461,6 +1592,23 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
     }
 }
 
+hipError_t launch_scatter(const Problem &p, const BwdMapping &mp, const void *loc,
+                          const void *attn, const void *grad_out, void *grad_value,
+                          float *workspace, hipStream_t stream) {
+    switch (p.dtype) {
+        case MSDA_F32: return scatter_by_j<F32T, 1>(p, mp, loc, attn, grad_out, grad_value, workspace, stream);
+        case MSDA_F16:
+            return mp.slot == 2
+                       ? scatter_by_j<F16T, 2>(p, mp, loc, attn, grad_out, grad_value, workspace, stream)
+                       : scatter_by_j<F16T, 1>(p, mp, loc, attn, grad_out, grad_value, workspace, stream);
+        case MSDA_BF16:
+            return mp.slot == 2
+                       ? scatter_by_j<BF16T, 2>(p, mp, loc, attn, grad_out, grad_value, workspace, stream)
+                       : scatter_by_j<BF16T, 1>(p, mp, loc, attn, grad_out, grad_value, workspace, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_gradients(const Problem &p, const Mapping &mp, const void *value,
                             const void *loc, const void *attn, const void *grad_out,
                             void *grad_loc, void *grad_attn, hipStream_t stream) {
@@ -1474,7 +1622,7 @@ hipError_t launch_gradients(const Problem &p, const Mapping &mp, const void *val
 
 hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
                            const BinnedBuffers &bins, bool place, hipStream_t stream) {
-    const int64_t wpb = (p.Q * p.L * p.K + kBlock - 1) / kBlock;
+    const int64_t wpb = (p.Q * p.levels.nblev * p.K + kBlock - 1) / kBlock;
     const int64_t ntiles = p.B * p.M * wpb;
     if (ntiles == 0) return hipSuccess;
     const int64_t grid = (ntiles + kXcds - 1) / kXcds * kXcds;

@@ -16,8 +16,8 @@ namespace msda {
 // -1: atomics of the value dtype go straight into grad_value.
 //
 // Binned grad_value: the rows of level l of one (b, m) are cut into bins of
-// 2^bin_shift[l] pixel rows; bin_off[l] is the index of level l's first bin
-// among the nbbm bins of one (b, m).
+// 2^bin_shift[l] pixel rows (bin_shift[l] = -1: level not binned); bin_off[l]
+// is the index of level l's first bin among the nbbm bins of one (b, m).
 struct LevelTable {
     int32_t H[MSDA_MAX_LEVELS];
     int32_t W[MSDA_MAX_LEVELS];
@@ -25,6 +25,8 @@ struct LevelTable {
     int64_t scratch_off[MSDA_MAX_LEVELS];
     int32_t bin_shift[MSDA_MAX_LEVELS];
     int32_t bin_off[MSDA_MAX_LEVELS];
+    int32_t blevel[MSDA_MAX_LEVELS];  // the binned levels, in order
+    int32_t nblev;
 };
 
 // Everything a launch needs, validated by the host layer.
@@ -82,13 +84,19 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
 // Binned grad_value, in stream order: zero starts[0:nbins] (launch_zero);
 // launch_bin_sort(place = false) counts the in-bounds corners per bin into
 // starts; launch_bin_scan turns the counts into starts and cursors;
-// launch_bin_sort(place = true) writes the records; launch_gradients (every
-// level binned) or launch_backward (the other levels' atomics) writes
-// grad_loc / grad_attn; launch_bin_accumulate writes grad_value.
+// launch_bin_sort(place = true) writes the records; launch_gradients writes
+// grad_loc / grad_attn, launch_scatter the unbinned levels' atomics (if any);
+// launch_bin_accumulate writes the binned levels' grad_value rows.
 hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
                            const BinnedBuffers &bins, bool place, hipStream_t stream);
 hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream);
-// grad_loc / grad_attn only, in the forward's lane mapping (every level binned).
+// grad_value atomics only, for the levels that are not binned (no value
+// gathers); used with launch_gradients when some levels are binned.
+hipError_t launch_scatter(const Problem &p, const BwdMapping &mp, const void *loc,
+                          const void *attn, const void *grad_out, void *grad_value,
+                          float *workspace, hipStream_t stream);
+
+// grad_loc / grad_attn only, in the forward's lane mapping.
 hipError_t launch_gradients(const Problem &p, const Mapping &mp, const void *value,
                             const void *loc, const void *attn, const void *grad_out,
                             void *grad_loc, void *grad_attn, hipStream_t stream);
