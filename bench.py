@@ -281,7 +281,8 @@ def main():
         f"eager {eager_us:.2f} us/step, host enqueue {host_us:.2f} us/step")
 
     # Per-kernel device times: events right before / after each launch.
-    from scale_deformable_attention_amd._binding import launch_events_recorded, set_launch_events
+    from scale_deformable_attention_amd._binding import (launch_event_names, launch_events_recorded,
+                                                         set_launch_events)
     n_inst = min(K, 50)
     nev = 16
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + nev)] for _ in range(n_inst)]
@@ -296,21 +297,8 @@ def main():
         set_launch_events(evs[i][2:])
         call.backward()
         n_bwd = launch_events_recorded() // 2
+    bwd_names = launch_event_names()  # the library names each instrumented launch
     torch.cuda.synchronize()
-    bwd_names = {
-        "binned": ["bin_zero", "bin_count", "bin_scan", "bin_place", "msda_grad_kernel",
-                   "bin_accum_kernel"],
-        "mixed": ["zero_fill", "bin_zero", "bin_count", "bin_scan", "bin_place", "msda_grad_kernel",
-                  "msda_scatter_kernel", "bin_accum_kernel"],
-        "native": ["zero_fill", "msda_bwd_kernel"],
-        "per_level": ["zero_fill", "scratch_zero", "msda_bwd_kernel", "scratch_add_kernel"],
-        "fp32_scratch": ["zero_fill", "scratch_zero", "msda_bwd_kernel", "scratch_add_kernel"],
-    }[call.resolved_accum]
-    if n_bwd == len(bwd_names) + 1:  # binned with padding rows: grad_value fill first
-        bwd_names = ["zero_fill"] + bwd_names
-    if call.resolved_accum == "mixed" and wl.dtype == torch.float32:  # one fused kernel
-        bwd_names = [n for n in bwd_names if n != "msda_scatter_kernel"]
-        bwd_names[bwd_names.index("msda_grad_kernel")] = "msda_bwd_kernel"
     assert n_bwd == len(bwd_names), (n_bwd, bwd_names)
     ktimes = {"msda_fwd_kernel": float(np.mean([evs[i][0].elapsed_time(evs[i][1])
                                                  for i in range(n_inst)])) * 1e3}

@@ -40,11 +40,18 @@
  *                      is used as given and only checked for memory safety:
  *                      0 <= start_l and start_l + H_l * W_l <= S.
  *
- * Ownership and threading: the caller owns every buffer. The library keeps no
- * global state apart from a thread-local error string, allocates no device
- * memory, never synchronises, and enqueues all work on the caller's stream
- * (a hipStream_t passed as void*; NULL is the default stream). Calls are
- * reentrant. Device pointers must be aligned to their element size; wider
+ * Ownership and threading: the caller owns every buffer. The library
+ * allocates no device memory and never synchronises. Its only state is
+ * thread-local: an error string and, for backward calls that bin some level,
+ * one side stream (default priority) and three events per device, created by
+ * the first such call of a thread that is not under graph capture and kept
+ * for the thread's lifetime. Work is enqueued on the caller's stream (a
+ * hipStream_t passed as void*; NULL is the default stream); the binned part
+ * of a backward forks onto the side stream after the caller's earlier work
+ * and is joined back before the call returns, so each call is ordered on the
+ * caller's stream as a whole and can be captured in a HIP graph (a call
+ * captured before its thread has a side stream runs entirely on the caller's
+ * stream). Calls are reentrant. Device pointers must be aligned to their element size; wider
  * vector accesses are used automatically when every pointer allows them.
  *
  * Errors: every entry point returns an msda_status_t. All argument checks run
@@ -221,6 +228,11 @@ int msda_set_launch_events(void *const *events, int count);
 /* How many events the last instrumented call of this thread recorded
  * (twice the number of kernels it launched, up to its count). */
 int msda_launch_events_recorded(void);
+
+/* Kernel name of the i-th instrumented launch of that call (the one between
+ * events 2i and 2i+1), e.g. "msda_fwd_kernel" or "bin_accum_kernel"; NULL when
+ * i is out of range. Static storage. */
+const char *msda_launch_events_name(int i);
 
 /* Static text for a status code. */
 const char *msda_status_string(int status);

@@ -40,7 +40,8 @@ _ACCUM_CODES = {"auto": ACCUM_AUTO, None: ACCUM_AUTO, "native": ACCUM_NATIVE, Fa
 EXPORTED_SYMBOLS = ("msda_forward", "msda_backward", "msda_backward_workspace_size",
                     "msda_backward_resolve_accum", "msda_backward_plan", "msda_status_string",
                     "msda_last_error",
-                    "msda_abi_version", "msda_set_launch_events", "msda_launch_events_recorded")
+                    "msda_abi_version", "msda_set_launch_events", "msda_launch_events_recorded",
+                    "msda_launch_events_name")
 
 _lib = None
 
@@ -83,6 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msda_set_launch_events.restype = i32
     lib.msda_launch_events_recorded.argtypes = []
     lib.msda_launch_events_recorded.restype = i32
+    lib.msda_launch_events_name.argtypes = [i32]
+    lib.msda_launch_events_name.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -217,6 +220,13 @@ def set_launch_events(events) -> None:
 
 def launch_events_recorded() -> int:
     return int(load_library().msda_launch_events_recorded())
+
+
+def launch_event_names():
+    """Kernel names of the last instrumented call's launches, in order."""
+    lib = load_library()
+    n = int(lib.msda_launch_events_recorded()) // 2
+    return [lib.msda_launch_events_name(i).decode() for i in range(n)]
 
 
 class MSDAErrorCodes:

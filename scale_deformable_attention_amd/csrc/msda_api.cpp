@@ -32,11 +32,15 @@ hipStream_t before(hipStream_t s) {
     return s;
 }
 
-// After a launch: record its "after" event (the pair is consumed only when
-// both fit in the caller's array).
-hipError_t marked(hipError_t err, hipStream_t s) {
+thread_local const char *g_launch_names[kMaxLaunchEvents / 2];
+thread_local const char *g_recorded_names[kMaxLaunchEvents / 2];
+
+// After a launch: record its "after" event and its name (the pair is
+// consumed only when both fit in the caller's array).
+hipError_t marked(hipError_t err, hipStream_t s, const char *name) {
     if (g_launch_events_next + 1 < g_launch_events_n) {
         if (err == hipSuccess) err = hipEventRecord(g_launch_events[g_launch_events_next + 1], s);
+        g_launch_names[g_launch_events_next / 2] = name;
         g_launch_events_next += 2;
     }
     return err;
@@ -46,10 +50,53 @@ thread_local int g_launch_events_recorded = 0;
 
 struct LaunchEventsScope {  // clears the instrumentation when a call returns
     ~LaunchEventsScope() {
-        if (g_launch_events_n) g_launch_events_recorded = g_launch_events_next;
+        if (g_launch_events_n) {
+            g_launch_events_recorded = g_launch_events_next;
+            for (int i = 0; i < g_launch_events_next / 2; ++i) g_recorded_names[i] = g_launch_names[i];
+        }
         g_launch_events_n = g_launch_events_next = 0;
     }
 };
+
+// Side stream of the binned backward: per thread and device, created on the
+// first binned call (default priority, non-blocking), never destroyed. The
+// binned chain (count, scan, place, accumulate) runs on it while the caller's
+// stream runs the zero fill and the gradient / scatter kernels; two event
+// waits fork it from the caller's stream and one joins it back, so the call
+// stays stream-ordered and capturable in a HIP graph.
+constexpr int kMaxDevices = 64;
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, zeroed = nullptr, join = nullptr;
+};
+thread_local SideStream g_side[kMaxDevices];
+
+// The side stream for the device of `s`, or nullptr to run the chain on `s`
+// itself (no usable device, or `s` is being captured and the side stream
+// does not exist yet: creating one is not done under capture).
+SideStream *side_stream(hipStream_t s) {
+    int dev = -1;
+    if (s ? hipStreamGetDevice(s, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+        return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    SideStream &ss = g_side[dev];
+    if (ss.stream) return &ss;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+        return nullptr;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    SideStream made;
+    bool good = hipStreamCreateWithFlags(&made.stream, hipStreamNonBlocking) == hipSuccess &&
+                hipEventCreateWithFlags(&made.fork, hipEventDisableTiming) == hipSuccess &&
+                hipEventCreateWithFlags(&made.zeroed, hipEventDisableTiming) == hipSuccess &&
+                hipEventCreateWithFlags(&made.join, hipEventDisableTiming) == hipSuccess;
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (!good) return nullptr;  // (partially created handles are kept out of use)
+    ss = made;
+    return &ss;
+}
 
 int fail(int status, const char *fmt, ...) {
     char buf[512];
@@ -417,6 +464,11 @@ int msda_abi_version(void) { return MSDA_ABI_VERSION; }
 
 int msda_launch_events_recorded(void) { return g_launch_events_recorded; }
 
+const char *msda_launch_events_name(int i) {
+    if (i < 0 || i >= g_launch_events_recorded / 2) return nullptr;
+    return g_recorded_names[i];
+}
+
 int msda_set_launch_events(void *const *events, int count) {
     if (count < 0 || count > kMaxLaunchEvents)
         return fail(MSDA_ERR_SHAPE, "launch event count %d outside [0, %d]", count, kMaxLaunchEvents);
@@ -468,7 +520,7 @@ int msda_forward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, 
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err = marked(msda::launch_forward(p, mp, value, sampling_locations,
                                                  attention_weights, output, before(s)),
-                            s);
+                            s, "msda_fwd_kernel");
     if (err != hipSuccess) return hip_fail(err, "forward launch");
     return ok();
 }
@@ -607,64 +659,123 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
         // Rows outside every binned level are written by no bin: zero all of
         // grad_value first when there are such rows (padding rows, levels
         // left to atomics, or no queries at all).
-        if (!accumulate && (p.Q == 0 || !all_binned || levels_leave_gaps(p)) &&
-            (err = marked(msda::launch_zero(grad_value, gv_bytes, before(s)), s)) != hipSuccess)
-            return hip_fail(err, "grad_value zero fill");
-        if (p.Q == 0) return ok();
+        const bool zero_gv = !accumulate && (p.Q == 0 || !all_binned || levels_leave_gaps(p));
+        if (p.Q == 0) {
+            if (zero_gv && (err = marked(msda::launch_zero(grad_value, gv_bytes, before(s)), s,
+                                         "zero_fill")) != hipSuccess)
+                return hip_fail(err, "grad_value zero fill");
+            return ok();
+        }
         char *ws = static_cast<char *>(workspace);
         msda::BinnedBuffers bins;
         bins.starts = reinterpret_cast<uint32_t *>(ws + bp.starts_off);
         bins.cursor = reinterpret_cast<uint32_t *>(ws + bp.cursor_off);
         bins.records = reinterpret_cast<uint2 *>(ws + bp.records_off);
         bins.nbins = bp.nbins;
-        // the counts (starts[0:nbins]) start at zero; the fill works in
-        // 2-byte units, so round the byte count up to an even number of them
-        if ((err = marked(msda::launch_zero(bins.starts, align_up((size_t)(bp.nbins + 1) * 4, 16), before(s)), s)) !=
-            hipSuccess)
-            return hip_fail(err, "bin count zero fill");
-        if ((err = marked(msda::launch_bin_sort(p, sampling_locations, attention_weights, bins,
-                                                false, before(s)),
-                          s)) != hipSuccess)
-            return hip_fail(err, "bin count launch");
-        if ((err = marked(msda::launch_bin_scan(bins, before(s)), s)) != hipSuccess)
-            return hip_fail(err, "bin scan launch");
-        if ((err = marked(msda::launch_bin_sort(p, sampling_locations, attention_weights, bins,
-                                                true, before(s)),
-                          s)) != hipSuccess)
-            return hip_fail(err, "bin place launch");
-        // grad_loc / grad_attn in the forward's lane mapping, and the unbinned
-        // levels' grad_value (if any) by a gather-free atomic scatter. fp32
-        // rows of unbinned levels span several 64-byte atomic segments; there
-        // the fused kernel, which overlaps those atomics with its gathers,
-        // measures faster than the two separate passes.
-        if (all_binned || dtype != MSDA_F32) {
-            if ((err = marked(msda::launch_gradients(p, gmp, value, sampling_locations,
-                                                     attention_weights, grad_output,
-                                                     grad_sampling_locations,
-                                                     grad_attention_weights, before(s)),
-                              s)) != hipSuccess)
-                return hip_fail(err, "gradient launch");
-            if (!all_binned &&
-                (err = marked(msda::launch_scatter(p, mp, sampling_locations, attention_weights,
-                                                   grad_output, grad_value, nullptr, before(s)),
-                              s)) != hipSuccess)
-                return hip_fail(err, "scatter launch");
-        } else if ((err = marked(msda::launch_backward(p, mp, value, sampling_locations,
-                                                       attention_weights, grad_output, grad_value,
-                                                       nullptr, grad_sampling_locations,
-                                                       grad_attention_weights, before(s)),
-                                 s)) != hipSuccess) {
-            return hip_fail(err, "backward launch");
+        // The binned chain (t) overlaps the zero fill and the gradient /
+        // scatter kernels (s); it forks after the caller's earlier work on s
+        // and is joined back on every path below. The fork and join cost
+        // about 20 us per call on MI355X (measured with graph replays), more
+        // than the overlap gains below ~2^19 records (the decoder workload's
+        // 3 * 10^5 lose 20 us; the odd-head workload's 9 * 10^5 gain 24 us).
+        SideStream *side = bp.records >= ((int64_t)1 << 19) ? side_stream(s) : nullptr;
+        const hipStream_t t = side ? side->stream : s;
+        if (side && ((err = hipEventRecord(side->fork, s)) != hipSuccess ||
+                     (err = hipStreamWaitEvent(t, side->fork, 0)) != hipSuccess))
+            return hip_fail(err, "side stream fork");
+        const char *what = nullptr;
+        do {
+            // the counts (starts[0:nbins]) start at zero; the fill works in
+            // 2-byte units, so round the byte count up to an even number of them
+            if ((err = marked(msda::launch_zero(bins.starts, align_up((size_t)(bp.nbins + 1) * 4, 16),
+                                                before(t)),
+                              t, "bin_zero")) != hipSuccess) {
+                what = "bin count zero fill";
+                break;
+            }
+            if ((err = marked(msda::launch_bin_sort(p, sampling_locations, attention_weights, bins,
+                                                    false, before(t)),
+                              t, "bin_count")) != hipSuccess) {
+                what = "bin count launch";
+                break;
+            }
+            if ((err = marked(msda::launch_bin_scan(bins, before(t)), t, "bin_scan")) != hipSuccess) {
+                what = "bin scan launch";
+                break;
+            }
+            if ((err = marked(msda::launch_bin_sort(p, sampling_locations, attention_weights, bins,
+                                                    true, before(t)),
+                              t, "bin_place")) != hipSuccess) {
+                what = "bin place launch";
+                break;
+            }
+            if (zero_gv && (err = marked(msda::launch_zero(grad_value, gv_bytes, before(s)), s,
+                                         "zero_fill")) != hipSuccess) {
+                what = "grad_value zero fill";
+                break;
+            }
+            if (side && (err = hipEventRecord(side->zeroed, s)) != hipSuccess) {
+                what = "side stream event";
+                break;
+            }
+            // grad_loc / grad_attn in the forward's lane mapping, and the
+            // unbinned levels' grad_value (if any) by a gather-free atomic
+            // scatter. fp32 rows of unbinned levels span several 64-byte
+            // atomic segments; there the fused kernel, which overlaps those
+            // atomics with its gathers, measures faster than two passes.
+            if (all_binned || dtype != MSDA_F32) {
+                if ((err = marked(msda::launch_gradients(p, gmp, value, sampling_locations,
+                                                         attention_weights, grad_output,
+                                                         grad_sampling_locations,
+                                                         grad_attention_weights, before(s)),
+                                  s, "msda_grad_kernel")) != hipSuccess) {
+                    what = "gradient launch";
+                    break;
+                }
+                if (!all_binned &&
+                    (err = marked(msda::launch_scatter(p, mp, sampling_locations, attention_weights,
+                                                       grad_output, grad_value, nullptr, before(s)),
+                                  s, "msda_scatter_kernel")) != hipSuccess) {
+                    what = "scatter launch";
+                    break;
+                }
+            } else if ((err = marked(msda::launch_backward(p, mp, value, sampling_locations,
+                                                           attention_weights, grad_output,
+                                                           grad_value, nullptr,
+                                                           grad_sampling_locations,
+                                                           grad_attention_weights, before(s)),
+                                     s, "msda_bwd_kernel")) != hipSuccess) {
+                what = "backward launch";
+                break;
+            }
+            // the accumulation writes whole rows: after the zero fill
+            if (side && (err = hipStreamWaitEvent(t, side->zeroed, 0)) != hipSuccess) {
+                what = "side stream wait";
+                break;
+            }
+            if ((err = marked(msda::launch_bin_accumulate(p, mp, grad_output, grad_value, bins,
+                                                          accumulate, before(t)),
+                              t, "bin_accum_kernel")) != hipSuccess) {
+                what = "bin accumulate launch";
+                break;
+            }
+        } while (false);
+        if (side) {
+            hipError_t je = hipEventRecord(side->join, t);
+            if (je == hipSuccess) je = hipStreamWaitEvent(s, side->join, 0);
+            if (err == hipSuccess && je != hipSuccess) {
+                err = je;
+                what = "side stream join";
+            }
         }
-        if ((err = marked(msda::launch_bin_accumulate(p, mp, grad_output, grad_value, bins,
-                                                      accumulate, before(s)),
-                          s)) != hipSuccess)
-            return hip_fail(err, "bin accumulate launch");
+        if (err != hipSuccess) return hip_fail(err, what);
         return ok();
     }
-    if (!accumulate && (err = marked(msda::launch_zero(grad_value, gv_bytes, before(s)), s)) != hipSuccess)
+    if (!accumulate && (err = marked(msda::launch_zero(grad_value, gv_bytes, before(s)), s,
+                                     "zero_fill")) != hipSuccess)
         return hip_fail(err, "grad_value zero fill");
-    if (need && !keep_sums && (err = marked(msda::launch_zero(workspace, need, before(s)), s)) != hipSuccess)
+    if (need && !keep_sums && (err = marked(msda::launch_zero(workspace, need, before(s)), s,
+                                            "scratch_zero")) != hipSuccess)
         return hip_fail(err, "scratch zero fill");
     if (p.Q > 0 &&
         (err = marked(msda::launch_backward(p, mp, value, sampling_locations, attention_weights,
@@ -672,12 +783,12 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                                             static_cast<float *>(workspace),
                                             grad_sampling_locations, grad_attention_weights,
                                             before(s)),
-                      s)) != hipSuccess)
+                      s, "msda_bwd_kernel")) != hipSuccess)
         return hip_fail(err, "backward launch");
     if (need && !defer &&
         (err = marked(msda::launch_scratch_add(p, static_cast<const float *>(workspace),
                                                grad_value, before(s)),
-                      s)) != hipSuccess)
+                      s, "scratch_add_kernel")) != hipSuccess)
         return hip_fail(err, "scratch add launch");
     return ok();
 }

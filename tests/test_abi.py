@@ -190,6 +190,8 @@ def test_backward_plan_per_level(lib):
 
 
 def test_launch_event_instrumentation_validation(lib):
+    assert lib.msda_launch_events_name(-1) is None
+    assert lib.msda_launch_events_name(10 ** 6) is None
     assert lib.msda_set_launch_events(None, 0) == 0
     assert lib.msda_set_launch_events(None, 1) == 1
     assert lib.msda_set_launch_events(None, 65) == 2

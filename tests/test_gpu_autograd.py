@@ -139,10 +139,13 @@ def test_autograd_empty_query_set():
 
 # ------------------------------------------------------------- HIP graphs
 
-@pytest.mark.parametrize("switch", [None, "binned", "per_level", False])
-def test_graph_capture_replays_match_eager(switch):
-    """Capture forward + backward once, replay with three fresh input sets."""
-    name = "decoder_bf16"
+@pytest.mark.parametrize("name,switch", [("decoder_bf16", None), ("decoder_bf16", "binned"),
+                                         ("decoder_bf16", "per_level"), ("decoder_bf16", False),
+                                         ("oddhead_fp32", None), ("encoder_fp16", None)])
+def test_graph_capture_replays_match_eager(name, switch):
+    """Capture forward + backward once, replay with three fresh input sets.
+    The odd-head and encoder cases bin enough records to run the binned chain
+    on the side stream, captured as a fork and a join."""
     wl = workload(name)
     say(f"case {name} graph capture, fp32_grad_accum={switch!r}")
     inp = make_inputs(wl)
@@ -193,3 +196,68 @@ def test_graph_capture_replays_match_eager(switch):
         check_forward(wl.dtype, static_out.cpu(), ref_out, touched)
         check_backward(wl.dtype, (v.grad.cpu(), loc.grad.cpu(), a.grad.cpu()), ref_grads,
                        fresh["spatial_shapes"], None, trows)
+
+
+def test_capture_on_a_thread_without_side_stream():
+    """A binned backward captured by a thread that never made one before runs
+    on the caller's stream alone (no side stream is created under capture);
+    its replays must still match the oracle. The odd-head workload bins
+    enough records to use a side stream otherwise."""
+    import threading
+    from scale_deformable_attention_amd import PreparedCall
+    wl = workload("oddhead_fp32")
+    inp = make_inputs(wl)
+    g = {k: (t.to(DEV) if k != "spatial_shapes" else t) for k, t in inp.items()}
+    errors = []
+
+    def body():
+        try:
+            torch.cuda.set_device(0)
+            call = PreparedCall(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                                g["attention_weights"], g["grad_output"], accum="mixed")
+            stream = torch.cuda.Stream()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                call.forward()
+                call.backward()
+            for _ in range(2):
+                graph.replay()
+                torch.cuda.synchronize()
+                ref_out, touched, ref_grads, trows = _oracle(inp)
+                check_forward(wl.dtype, call.output.cpu(), ref_out, touched)
+                check_backward(wl.dtype, (call.grad_value.cpu(), call.grad_loc.cpu(),
+                                          call.grad_attn.cpu()), ref_grads,
+                               inp["spatial_shapes"], None, trows)
+        except Exception as e:  # reported in the main thread
+            errors.append(e)
+
+    say("case oddhead_fp32 capture in a fresh thread (mixed)")
+    th = threading.Thread(target=body)
+    th.start()
+    th.join()
+    if errors:
+        raise errors[0]
+
+
+def test_instrumented_launch_names():
+    from scale_deformable_attention_amd import PreparedCall
+    from scale_deformable_attention_amd._binding import (launch_event_names,
+                                                         set_launch_events)
+    inp = make_inputs(workload("decoder_bf16"))
+    g = {k: (t.to(DEV) if k != "spatial_shapes" else t) for k, t in inp.items()}
+    call = PreparedCall(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                        g["attention_weights"], g["grad_output"], accum="mixed")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(20)]
+    for e in evs:
+        e.record()  # torch creates the HIP event on first record
+    torch.cuda.synchronize()
+    set_launch_events(evs[:2])
+    call.forward()
+    assert launch_event_names() == ["msda_fwd_kernel"]
+    set_launch_events(evs)
+    call.backward()
+    torch.cuda.synchronize()
+    assert launch_event_names() == ["bin_zero", "bin_count", "bin_scan", "bin_place", "zero_fill",
+                                    "msda_grad_kernel", "msda_scatter_kernel", "bin_accum_kernel"]
+    for i in range(8):
+        assert evs[2 * i].elapsed_time(evs[2 * i + 1]) >= 0.0
