@@ -173,6 +173,41 @@ def cpu_baseline(inp, min_seconds: float = 10.0, max_reps: int = 200):
     return el / reps * 1e6, reps, oracle.max_threads()
 
 
+def time_foil(g, call, fwd_bytes: int, reps: int = 20) -> dict:
+    """The point-parallel forward foil against the forward kernel, each timed
+    with the library's per-launch event pairs (same bias for both)."""
+    from scale_deformable_attention_amd._binding import (msda_forward_point_parallel,
+                                                         set_launch_events)
+    args = (g["value"], g["spatial_shapes"], None, g["sampling_locations"], g["attention_weights"])
+    fout = msda_forward_point_parallel(*args)
+    out = call.forward()
+    torch.cuda.synchronize()
+    diff = float((fout.float() - out.float()).abs().max())
+
+    def kernel_us(fn):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for pair in evs:
+            for e in pair:
+                e.record()
+        torch.cuda.synchronize()
+        for pair in evs:
+            set_launch_events(pair)
+            fn()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+    foil_us = kernel_us(lambda: msda_forward_point_parallel(*args, output=fout))
+    fwd_us = kernel_us(call.forward)
+    log(f"point-parallel foil {foil_us:.2f} us vs forward kernel {fwd_us:.2f} us "
+        f"(max |difference| {diff:.3g})")
+    gbps = lambda us: fwd_bytes / (us * 1e-6) / 1e9
+    return {"kernel": "msda_foil_kernel", "us": round(foil_us, 3), "GBps": round(gbps(foil_us), 1),
+            "frac": round(gbps(foil_us) / HBM_PEAK_GBPS, 4), "forward_us": round(fwd_us, 3),
+            "forward_GBps": round(gbps(fwd_us), 1),
+            "forward_frac": round(gbps(fwd_us) / HBM_PEAK_GBPS, 4),
+            "max_abs_diff_vs_forward": diff}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +220,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup + timed steps only (for rocprofv3 runs)")
+    ap.add_argument("--foil", action="store_true",
+                    help="also time the point-parallel forward foil against the forward kernel")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="with --profile-only: also run 5 plain device copies of this many MiB "
                          "(reference dispatches for scaling FETCH_SIZE / WRITE_SIZE)")
@@ -226,6 +263,13 @@ def main():
             step()
         torch.cuda.synchronize()
         log(f"ran {K} eager steps")
+        if args.foil:
+            from scale_deformable_attention_amd._binding import msda_forward_point_parallel
+            for _ in range(K):
+                msda_forward_point_parallel(g["value"], g["spatial_shapes"], None,
+                                            g["sampling_locations"], g["attention_weights"])
+            torch.cuda.synchronize()
+            log(f"ran {K} point-parallel foil forwards")
         if args.calib_copy_mb:
             n = args.calib_copy_mb * (1 << 20) // 4
             src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -364,6 +408,8 @@ def main():
         "kernels": kernels, "touched_rows_U": U, "corners_C": C, "points_P": P,
         "roofline": roofline,
     }
+    if args.foil:
+        result["foil"] = time_foil(g, call, kbytes["msda_fwd_kernel"])
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (cpu_baseline)")
         cpu_us, reps_done, threads = cpu_baseline(inp, args.cpu_seconds)

@@ -160,6 +160,22 @@ int msda_forward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                  const void *attention_weights, void *output, void *stream);
 
 /*
+ * Measurement foil, not a forward to use: the point-parallel decomposition
+ * that the forward page contrasts with its own (course page "4. The forward
+ * kernel, line by line", section "The design question: what does one
+ * program own?"), one thread per sampling point reading its corner rows
+ * alone, partial outputs added per query through LDS. Same arguments and
+ * result as msda_forward (summation order aside). MSDA_ERR_UNSUPPORTED unless
+ * num_levels * num_points divides 256 and head_dim <= 64.
+ */
+int msda_forward_point_parallel(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
+                                int64_t head_dim, int64_t num_levels,
+                                const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                int64_t num_queries, int64_t num_points,
+                                const void *value, const void *sampling_locations,
+                                const void *attention_weights, void *output, void *stream);
+
+/*
  * Bytes of device workspace msda_backward needs for `accum` on this problem
  * (0 for NATIVE, and for fp32 data). Returns 0 and sets the last error for
  * invalid arguments; host-only, needs no GPU.

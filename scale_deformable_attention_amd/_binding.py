@@ -37,7 +37,8 @@ _ACCUM_CODES = {"auto": ACCUM_AUTO, None: ACCUM_AUTO, "native": ACCUM_NATIVE, Fa
                 "per_level": ACCUM_PER_LEVEL, "binned": ACCUM_BINNED, "mixed": ACCUM_MIXED}
 
 # every symbol include/msda.h declares
-EXPORTED_SYMBOLS = ("msda_forward", "msda_backward", "msda_backward_workspace_size",
+EXPORTED_SYMBOLS = ("msda_forward", "msda_forward_point_parallel", "msda_backward",
+                    "msda_backward_workspace_size",
                     "msda_backward_resolve_accum", "msda_backward_plan", "msda_status_string",
                     "msda_last_error",
                     "msda_abi_version", "msda_set_launch_events", "msda_launch_events_recorded",
@@ -66,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     prob = [i32, i64, i64, i64, i64, i64, vp, vp, i64, i64]
     lib.msda_forward.argtypes = prob + [vp, vp, vp, vp, vp]
     lib.msda_forward.restype = i32
+    lib.msda_forward_point_parallel.argtypes = prob + [vp, vp, vp, vp, vp]
+    lib.msda_forward_point_parallel.restype = i32
     lib.msda_backward.argtypes = prob + [vp, vp, vp, vp, vp, vp, vp, i32, u32, vp, sz, vp]
     lib.msda_backward.restype = i32
     lib.msda_backward_workspace_size.argtypes = prob + [i32]
@@ -181,6 +184,25 @@ def msda_forward(value: torch.Tensor, spatial_shapes, level_start_index,
         raise ValueError("output must be a contiguous (B, Q, M*D) tensor of the input dtype")
     _check(lib.msda_forward(*_problem(code, B, S, M, D, levels, Q, K), _ptr(value), _ptr(loc),
                             _ptr(attn), _ptr(output), _stream(value.device, stream)))
+    return output
+
+
+def msda_forward_point_parallel(value: torch.Tensor, spatial_shapes, level_start_index,
+                                sampling_locations: torch.Tensor, attention_weights: torch.Tensor,
+                                output: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The point-parallel measurement foil (same result as msda_forward)."""
+    lib = load_library()
+    levels = _Levels(spatial_shapes, level_start_index)
+    code = _dtype_code(value, sampling_locations, attention_weights)
+    value = value.contiguous()
+    loc = sampling_locations.contiguous()
+    attn = attention_weights.contiguous()
+    B, S, M, D, Q, K = _dims(value, levels, loc, attn)
+    if output is None:
+        output = torch.empty((B, Q, M * D), dtype=value.dtype, device=value.device)
+    _check(lib.msda_forward_point_parallel(*_problem(code, B, S, M, D, levels, Q, K), _ptr(value),
+                                           _ptr(loc), _ptr(attn), _ptr(output),
+                                           _stream(value.device, stream)))
     return output
 
 

@@ -525,6 +525,38 @@ int msda_forward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, 
     return ok();
 }
 
+int msda_forward_point_parallel(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
+                                int64_t head_dim, int64_t num_levels,
+                                const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                int64_t num_queries, int64_t num_points, const void *value,
+                                const void *sampling_locations, const void *attention_weights,
+                                void *output, void *stream) {
+    LaunchEventsScope events_scope;
+    msda::Problem p;
+    int st = make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
+                          level_start_index, num_queries, num_points, &p);
+    if (st) return st;
+    const int64_t LK = p.L * p.K;
+    if (LK > 256 || 256 % LK != 0 || p.D > 64)
+        return fail(MSDA_ERR_UNSUPPORTED,
+                    "the point-parallel foil needs num_levels*num_points dividing 256 and "
+                    "head_dim <= 64 (got %lld, %lld)", (long long)LK, (long long)p.D);
+    if (p.B == 0 || p.Q == 0) return ok();
+    if ((st = check_ptr(value, "value", dtype))) return st;
+    if ((st = check_ptr(sampling_locations, "sampling_locations", dtype))) return st;
+    if ((st = check_ptr(attention_weights, "attention_weights", dtype))) return st;
+    if ((st = check_ptr(output, "output", dtype))) return st;
+    const size_t e = elem_size(dtype);
+    const int wide = e == 4 ? 4 : 8;
+    const int vec = (p.D % wide == 0 && aligned(value, (size_t)wide * e)) ? wide : 1;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = marked(msda::launch_forward_foil(p, vec, value, sampling_locations,
+                                                            attention_weights, output, before(s)),
+                                  s, "msda_foil_kernel");
+    if (err != hipSuccess) return hip_fail(err, "foil launch");
+    return ok();
+}
+
 int msda_backward_resolve_accum(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                                 int64_t head_dim, int64_t num_levels,
                                 const int64_t *spatial_shapes, const int64_t *level_start_index,

@@ -424,6 +424,81 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     if (live && s == 0) store_vec<DT, VEC>(out + pq * D + c0, acc);
 }
 
+// ------------------------------------------------ point-parallel foil
+//
+// The decomposition the forward page sets against its own (course page "4.
+// The forward kernel, line by line", section "The design question: what does
+// one program own?"): one thread per sampling point (b, q, m, l, k), points
+// in their memory order, so neighbouring lanes sample unrelated locations and
+// each lane reads its four corner rows alone (VEC channels per load, no
+// coalescing across lanes). A workgroup holds the points of kBlock / (L*K)
+// whole queries; each thread's D partial sums go through LDS and are added
+// per query and channel. Kept for measurement only (occupancy versus
+// bandwidth); the product forward is msda_fwd_kernel.
+template <class DT, int VEC, int MAXD>
+__global__ __launch_bounds__(kBlock) void msda_foil_kernel(
+    const typename DT::S *__restrict__ value, const typename DT::S *__restrict__ loc,
+    const typename DT::S *__restrict__ attn, typename DT::S *__restrict__ out,
+    const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
+    const int L, const int K, const int64_t P) {
+    using E = typename DT::S;
+    extern __shared__ float part[];  // kBlock x D
+    const int tid = threadIdx.x;
+    const int LK = L * K;
+    const int64_t pt = (int64_t)blockIdx.x * kBlock + tid;
+    const bool ok = pt < P;
+    const int64_t pc = ok ? pt : 0;
+    const int64_t bqm = pc / LK;
+    const int pp = (int)(pc - bqm * LK);
+    const int l = pp / K;
+    const int64_t b = bqm / (Q * M);
+    const int m = (int)(bqm % M);
+    const int W = lt.W[l];
+    const Cell cl = map_cell(to_f32(DT{}, loc[2 * pc]), to_f32(DT{}, loc[2 * pc + 1]),
+                             (float)lt.H[l], (float)W, W, lt.start[l]);
+    const float a = ok ? to_f32(DT{}, attn[pc]) : 0.0f;
+    const float gx = 1.0f - cl.fx, gy = 1.0f - cl.fy;
+    const float w[4] = {a * gx * gy, a * cl.fx * gy, a * gx * cl.fy, a * cl.fx * cl.fy};
+    const bool vc[4] = {ok && cl.v00, ok && cl.v01, ok && cl.v10, ok && cl.v11};
+    const int64_t MD = (int64_t)M * D;
+    const E *rows[4];
+    const int64_t r00 = cl.row00;
+    const int64_t drow[4] = {0, 1, W, (int64_t)W + 1};
+#pragma unroll
+    for (int cn = 0; cn < 4; ++cn)
+        rows[cn] = value + ((b * S + (vc[cn] ? r00 + drow[cn] : 0)) * MD + (int64_t)m * D);
+    float acc[MAXD];
+#pragma unroll
+    for (int d = 0; d < MAXD; ++d) acc[d] = 0.0f;
+#pragma unroll
+    for (int d0 = 0; d0 < MAXD; d0 += VEC) {
+        if (d0 < D) {
+#pragma unroll
+            for (int cn = 0; cn < 4; ++cn) {
+                if (!vc[cn]) continue;
+                float v[VEC];
+                load_vec<DT, VEC>(rows[cn] + d0, v);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) acc[d0 + i] += w[cn] * v[i];
+            }
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < MAXD; ++d)
+        if (d < D) part[tid * D + d] = acc[d];
+    __syncthreads();
+    const int qpw = kBlock / LK;
+    const int64_t bqm0 = (int64_t)blockIdx.x * qpw;
+    const int64_t nq = P / LK;
+    for (int i = tid; i < qpw * D; i += kBlock) {
+        const int j = i / D, d = i - j * D;
+        if (bqm0 + j >= nq) continue;
+        float sum = 0.0f;
+        for (int t = 0; t < LK; ++t) sum += part[(j * LK + t) * D + d];
+        out[(bqm0 + j) * D + d] = from_f32(DT{}, sum);
+    }
+}
+
 // ------------------------------------------------- backward, gradients only
 //
 // grad_attention_weights and grad_sampling_locations when no level's
@@ -1661,6 +1736,34 @@ hipError_t launch_bin_accumulate(const Problem &p, const BwdMapping &mp, const v
                                 : accum_by_j<BF16T, 1>(p, mp, grad_out, grad_value, bins, accumulate, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_forward_foil(const Problem &p, int vec, const void *value, const void *loc,
+                               const void *attn, void *out, hipStream_t stream) {
+    const int64_t P = p.B * p.Q * p.M * p.L * p.K;
+    const int64_t grid = (P + kBlock - 1) / kBlock;
+    const size_t lds = (size_t)kBlock * (size_t)p.D * sizeof(float);
+#define MSDA_FOIL(T, V)                                                                         \
+    hipLaunchKernelGGL((msda_foil_kernel<T, V, 64>), dim3((unsigned)grid), dim3(kBlock), lds,    \
+                       stream, static_cast<const typename T::S *>(value),                       \
+                       static_cast<const typename T::S *>(loc),                                 \
+                       static_cast<const typename T::S *>(attn),                                \
+                       static_cast<typename T::S *>(out), p.levels, p.S, p.Q, (int)p.M,         \
+                       (int)p.D, (int)p.L, (int)p.K, P)
+    switch (p.dtype) {
+        case MSDA_F32:
+            if (vec == 4) MSDA_FOIL(F32T, 4); else MSDA_FOIL(F32T, 1);
+            break;
+        case MSDA_F16:
+            if (vec == 8) MSDA_FOIL(F16T, 8); else MSDA_FOIL(F16T, 1);
+            break;
+        case MSDA_BF16:
+            if (vec == 8) MSDA_FOIL(BF16T, 8); else MSDA_FOIL(BF16T, 1);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+#undef MSDA_FOIL
+    return hipGetLastError();
 }
 
 hipError_t launch_zero(void *dst, size_t bytes, hipStream_t stream) {

@@ -104,6 +104,12 @@ hipError_t launch_bin_accumulate(const Problem &p, const BwdMapping &mp, const v
                                  void *grad_value, const BinnedBuffers &bins, bool accumulate,
                                  hipStream_t stream);
 
+// Point-parallel forward foil (measurement only); vec = channels per load
+// (16 bytes when D and the pointers allow, else 1). Needs L*K dividing 256 and
+// D <= 64 (host-checked).
+hipError_t launch_forward_foil(const Problem &p, int vec, const void *value, const void *loc,
+                               const void *attn, void *out, hipStream_t stream);
+
 // Fill `bytes` bytes (a multiple of 2) at `dst` with zeros.
 hipError_t launch_zero(void *dst, size_t bytes, hipStream_t stream);
 

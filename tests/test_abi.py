@@ -92,6 +92,16 @@ def test_forward_rejects(lib, kw, status):
     assert lib.msda_last_error().decode() != ""
 
 
+def test_point_parallel_foil_limits(lib):
+    args = (0, 1, 100, 2, 8, 2, SHAPES, None, 16, 2, FAKE, FAKE, FAKE, FAKE, None)
+    assert lib.msda_forward_point_parallel(*args[:5], 2, SHAPES, None, 0, 2, *args[10:]) == 0
+    # L*K = 2*3 does not divide 256; D = 65 is above 64
+    assert lib.msda_forward_point_parallel(0, 1, 100, 2, 8, 2, SHAPES, None, 16, 3, *args[10:]) == 8
+    assert lib.msda_forward_point_parallel(0, 1, 100, 2, 65, 2, SHAPES, None, 16, 2, *args[10:]) == 8
+    assert lib.msda_forward_point_parallel(0, 1, 100, 2, 8, 2, SHAPES, None, 16, 2, None,
+                                           *args[11:]) == 1
+
+
 def test_forward_empty_batch_or_queries_is_ok_without_launch(lib):
     assert fwd(lib, B=0) == 0
     assert fwd(lib, Q=0) == 0

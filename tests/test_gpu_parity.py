@@ -442,3 +442,17 @@ def test_overlapping_levels(dtype, accum):
                                generator=torch.Generator().manual_seed(4)).to(dtype)
     say(f"case overlapping levels {starts.tolist()} {dtype} {accum}")
     full_check(inp, dtype, accum, starts=starts)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "decoder_bf16", "oddhead_fp32"])
+def test_point_parallel_foil_parity(name):
+    """The point-parallel foil (a measurement study) computes the same forward."""
+    from scale_deformable_attention_amd._binding import msda_forward_point_parallel
+    wl = workload(name)
+    say(f"case {name} point-parallel foil")
+    inp, (ref_out, touched, _, _) = _cached(name)
+    g = to_dev(inp)
+    out = msda_forward_point_parallel(g["value"], g["spatial_shapes"], None,
+                                      g["sampling_locations"], g["attention_weights"])
+    torch.cuda.synchronize()
+    check_forward(wl.dtype, out.cpu(), ref_out, touched)
