@@ -20,19 +20,21 @@ Prints one JSON line:
                         algorithmic bytes per launch / average launch duration
   cpu_baseline          the CPU oracle (fp64 loops, OpenMP) on the same workload
 
-Algorithmic bytes per launch (e = element size, P = B*Q*M*L*K points,
+Algorithmic bytes per launch (e = element size of value / grad rows, pe = of
+locations / weights (fp32 beside 16-bit values in mixed workloads),
+P = B*Q*M*L*K points,
 U = distinct (b, row, m) value rows with at least one in-bounds corner,
 C = in-bounds corners, N = B*S*M*D grad_value elements):
-  forward          3*P*e (locations + weights) + B*Q*M*D*e (output) + U*D*e
+  forward          3*P*pe (locations + weights) + B*Q*M*D*e (output) + U*D*e
   backward kernel  (msda_bwd_kernel; msda_grad_kernel without the atomics term
                    when some level is binned)
-                   3*P*e (params) + B*Q*M*D*e (grad_output) + U*D*e (value)
-                   + 3*P*e (grad locations + grad weights)
+                   3*P*pe (params) + B*Q*M*D*e (grad_output) + U*D*e (value)
+                   + 3*P*pe (grad locations + grad weights)
                    + atomics: 2*U'*D*e_acc (read-modify-write of the touched rows
                      of levels not binned; e_acc = 4 for fp32 rows)
-  scatter          3*(P-P')*e + B*Q*M*D*e + 2*U'*D*e_acc (atomics of the unbinned levels)
+  scatter          3*(P-P')*pe + B*Q*M*D*e + 2*U'*D*e_acc (atomics of the unbinned levels)
   binned levels only (P', C', N' = their points, corners, grad_value elements):
-  bin count        2*P'*e;  bin place  3*P'*e + 8*C' (records written)
+  bin count        2*P'*pe;  bin place  3*P'*pe + 8*C' (records written)
   bin accumulate   8*C' + B*Q*M*D*e + N'*e
   zero fill        bytes written;  scratch add  rows * D * (4 + 2e)
 """
@@ -353,6 +355,7 @@ def main():
 
     # Algorithmic bytes per launch.
     e = torch.finfo(wl.dtype).bits // 8
+    pe = torch.finfo(wl.param_dtype or wl.dtype).bits // 8  # locations / weights
     B, S, M, D, L, Kp, Q = wl.B, wl.S, wl.M, wl.D, wl.L, wl.K, wl.num_queries
     P = B * Q * M * L * Kp
     N = B * S * M * D
@@ -365,18 +368,18 @@ def main():
     scratch_rows = sum(B * h * w * M for l, (h, w) in enumerate(wl.levels) if l in scr_levels)
     bin_rows = sum(B * h * w * M for l, (h, w) in enumerate(wl.levels) if l in bin_levels)
     P_bin = B * Q * M * Kp * len(bin_levels)
-    common = 3 * P * e + B * Q * M * D * e + U * D * e + 3 * P * e
+    common = 3 * P * pe + B * Q * M * D * e + U * D * e + 3 * P * pe
     e_acc = 4 if wl.dtype == torch.float32 else e
-    kbytes = {"msda_fwd_kernel": 3 * P * e + B * Q * M * D * e + U * D * e,
+    kbytes = {"msda_fwd_kernel": 3 * P * pe + B * Q * M * D * e + U * D * e,
               "zero_fill": N * e, "scratch_zero": scratch_rows * D * 4,
               "scratch_add_kernel": scratch_rows * D * (4 + 2 * e),
               # atomics: read-modify-write of the touched rows of unbinned levels
               "msda_bwd_kernel": common + 2 * ((U - U_scr - U_bin) * D * e_acc + U_scr * D * 4),
               "msda_grad_kernel": common,
-              "msda_scatter_kernel": 3 * (P - P_bin) * e + B * Q * M * D * e
+              "msda_scatter_kernel": 3 * (P - P_bin) * pe + B * Q * M * D * e
               + 2 * (U - U_bin) * D * e_acc,
-              "bin_zero": (nb + 1) * 4, "bin_count": 2 * P_bin * e, "bin_scan": 3 * nb * 4,
-              "bin_place": 3 * P_bin * e + 8 * C_bin,
+              "bin_zero": (nb + 1) * 4, "bin_count": 2 * P_bin * pe, "bin_scan": 3 * nb * 4,
+              "bin_place": 3 * P_bin * pe + 8 * C_bin,
               "bin_accum_kernel": 8 * C_bin + B * Q * M * D * e + bin_rows * D * e}
     kernels = {k: {"us": round(v, 3), "bytes": int(kbytes[k]),
                    "GBps": round(kbytes[k] / (v * 1e-6) / 1e9, 1)} for k, v in ktimes.items()}
@@ -400,6 +403,7 @@ def main():
         "data": "synthetic (seeded; stands in for Deformable-DETR COCO inputs)",
         "config": {"workload": wl.name, "B": B, "Q": Q, "S": S, "M": M, "D": D, "L": L, "K": Kp,
                    "levels": [list(x) for x in wl.levels], "accum": call.resolved_accum,
+                   "param_dtype": str(wl.param_dtype or wl.dtype).replace("torch.", ""),
                    "parallelism": "single GPU"},
         "timing": "graph replay" if graph_ok else "eager",
         "eager_us_per_step": round(eager_us, 3), "host_enqueue_us": round(host_us, 3),

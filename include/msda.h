@@ -24,8 +24,9 @@
  * atomics; out-of-bounds corners receive nothing, section "Scatter needs
  * atomics").
  *
- * Tensor layouts (all dense, row-major, on the device, one dtype for every
- * floating tensor of a call):
+ * Tensor layouts (all dense, row-major, on the device; one dtype for every
+ * floating tensor of a call, except in the _ex entry points, where the
+ * locations, weights and their gradients may be fp32 beside 16-bit values):
  *   value                    (B, S, M, D)       S = rows of all levels
  *   sampling_locations       (B, Q, M, L, K, 2) normalised (x, y), not clamped
  *   attention_weights        (B, Q, M, L, K)    used as given (no softmax)
@@ -160,6 +161,21 @@ int msda_forward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                  const void *attention_weights, void *output, void *stream);
 
 /*
+ * Mixed dtypes: msda_forward with a separate dtype for sampling_locations and
+ * attention_weights (param_dtype). param_dtype is value_dtype, or MSDA_F32
+ * beside fp16 / bf16 values (fp32 locations keep sub-pixel precision at large
+ * resolutions, msda-triton README, section "Caveats"); value and output take
+ * value_dtype. MSDA_ERR_DTYPE for any other pair; MSDA_ERR_UNSUPPORTED for a
+ * mixed pair whose per-batch value slice is 2 GiB or more.
+ */
+int msda_forward_ex(int value_dtype, int param_dtype, int64_t batch, int64_t num_keys,
+                    int64_t num_heads, int64_t head_dim, int64_t num_levels,
+                    const int64_t *spatial_shapes, const int64_t *level_start_index,
+                    int64_t num_queries, int64_t num_points, const void *value,
+                    const void *sampling_locations, const void *attention_weights, void *output,
+                    void *stream);
+
+/*
  * Measurement foil, not a forward to use: the point-parallel decomposition
  * that the forward page contrasts with its own (course page "4. The forward
  * kernel, line by line", section "The design question: what does one
@@ -230,6 +246,22 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                   void *grad_value, void *grad_sampling_locations,
                   void *grad_attention_weights, int accum, unsigned flags,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Mixed dtypes for the backward, as msda_forward_ex: sampling_locations,
+ * attention_weights, grad_sampling_locations and grad_attention_weights take
+ * param_dtype; value, grad_output and grad_value take value_dtype. Workspace
+ * sizes and accumulation plans depend on value_dtype only
+ * (msda_backward_workspace_size and friends take it as their dtype).
+ */
+int msda_backward_ex(int value_dtype, int param_dtype, int64_t batch, int64_t num_keys,
+                     int64_t num_heads, int64_t head_dim, int64_t num_levels,
+                     const int64_t *spatial_shapes, const int64_t *level_start_index,
+                     int64_t num_queries, int64_t num_points, const void *value,
+                     const void *sampling_locations, const void *attention_weights,
+                     const void *grad_output, void *grad_value, void *grad_sampling_locations,
+                     void *grad_attention_weights, int accum, unsigned flags, void *workspace,
+                     size_t workspace_bytes, void *stream);
 
 /*
  * Instrumentation for profilers and benchmarks: the next msda_forward or

@@ -37,7 +37,8 @@ _ACCUM_CODES = {"auto": ACCUM_AUTO, None: ACCUM_AUTO, "native": ACCUM_NATIVE, Fa
                 "per_level": ACCUM_PER_LEVEL, "binned": ACCUM_BINNED, "mixed": ACCUM_MIXED}
 
 # every symbol include/msda.h declares
-EXPORTED_SYMBOLS = ("msda_forward", "msda_forward_point_parallel", "msda_backward",
+EXPORTED_SYMBOLS = ("msda_forward", "msda_forward_ex", "msda_forward_point_parallel",
+                    "msda_backward", "msda_backward_ex",
                     "msda_backward_workspace_size",
                     "msda_backward_resolve_accum", "msda_backward_plan", "msda_status_string",
                     "msda_last_error",
@@ -67,6 +68,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     prob = [i32, i64, i64, i64, i64, i64, vp, vp, i64, i64]
     lib.msda_forward.argtypes = prob + [vp, vp, vp, vp, vp]
     lib.msda_forward.restype = i32
+    lib.msda_forward_ex.argtypes = [i32] + prob + [vp, vp, vp, vp, vp]
+    lib.msda_forward_ex.restype = i32
+    lib.msda_backward_ex.argtypes = [i32] + prob + [vp, vp, vp, vp, vp, vp, vp, i32, u32, vp, sz, vp]
+    lib.msda_backward_ex.restype = i32
     lib.msda_forward_point_parallel.argtypes = prob + [vp, vp, vp, vp, vp]
     lib.msda_forward_point_parallel.restype = i32
     lib.msda_backward.argtypes = prob + [vp, vp, vp, vp, vp, vp, vp, i32, u32, vp, sz, vp]
@@ -151,6 +156,30 @@ def _dtype_code(*tensors: torch.Tensor) -> int:
     return _DTYPE_CODES[dt]
 
 
+def _dtype_codes(value: torch.Tensor, loc: torch.Tensor, attn: torch.Tensor,
+                 *value_typed: torch.Tensor) -> Tuple[int, int]:
+    """(value dtype, parameter dtype) codes. Locations and weights share one
+    dtype: the value dtype, or float32 beside float16 / bfloat16 values."""
+    for t in (value, loc, attn) + value_typed:
+        if t.dtype not in _DTYPE_CODES:
+            raise TypeError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16")
+    for t in value_typed:
+        if t.dtype != value.dtype:
+            raise TypeError(f"grad_output must be {value.dtype}, got {t.dtype}")
+    if attn.dtype != loc.dtype:
+        raise TypeError(f"sampling_locations and attention_weights must share one dtype, "
+                        f"got {loc.dtype} and {attn.dtype}")
+    vcode, pcode = _DTYPE_CODES[value.dtype], _DTYPE_CODES[loc.dtype]
+    if pcode != vcode and not (pcode == MSDA_F32 and vcode != MSDA_F32):
+        raise TypeError(f"sampling_locations / attention_weights must be {value.dtype} or "
+                        f"float32 beside 16-bit values, got {loc.dtype}")
+    _dtype_code(value, *value_typed)  # device checks
+    _dtype_code(loc, attn)
+    if loc.device != value.device:
+        raise ValueError(f"all tensors must be on one device, got {value.device} and {loc.device}")
+    return vcode, pcode
+
+
 def _stream(device: torch.device, stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -170,10 +199,11 @@ def _problem(code, B, S, M, D, levels, Q, K):
 def msda_forward(value: torch.Tensor, spatial_shapes, level_start_index,
                  sampling_locations: torch.Tensor, attention_weights: torch.Tensor,
                  output: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Forward of the MSDA core; returns (B, Q, M*D) in the input dtype."""
+    """Forward of the MSDA core; returns (B, Q, M*D) in the value dtype.
+    Locations and weights may be float32 beside float16 / bfloat16 values."""
     lib = load_library()
     levels = _Levels(spatial_shapes, level_start_index)
-    code = _dtype_code(value, sampling_locations, attention_weights)
+    code, pcode = _dtype_codes(value, sampling_locations, attention_weights)
     value = value.contiguous()
     loc = sampling_locations.contiguous()
     attn = attention_weights.contiguous()
@@ -182,8 +212,9 @@ def msda_forward(value: torch.Tensor, spatial_shapes, level_start_index,
         output = torch.empty((B, Q, M * D), dtype=value.dtype, device=value.device)
     elif output.shape != (B, Q, M * D) or output.dtype != value.dtype or not output.is_contiguous():
         raise ValueError("output must be a contiguous (B, Q, M*D) tensor of the input dtype")
-    _check(lib.msda_forward(*_problem(code, B, S, M, D, levels, Q, K), _ptr(value), _ptr(loc),
-                            _ptr(attn), _ptr(output), _stream(value.device, stream)))
+    _check(lib.msda_forward_ex(code, pcode, *_problem(code, B, S, M, D, levels, Q, K)[1:],
+                               _ptr(value), _ptr(loc), _ptr(attn), _ptr(output),
+                               _stream(value.device, stream)))
     return output
 
 
@@ -273,7 +304,7 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index,
     MSDA_FLAG_DEFER_SCRATCH (fp32 accumulation across calls in `workspace`)."""
     lib = load_library()
     levels = _Levels(spatial_shapes, level_start_index)
-    code = _dtype_code(value, sampling_locations, attention_weights, grad_output)
+    code, pcode = _dtype_codes(value, sampling_locations, attention_weights, grad_output)
     value = value.contiguous()
     loc = sampling_locations.contiguous()
     attn = attention_weights.contiguous()
@@ -306,7 +337,7 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index,
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     flags = (FLAG_ACCUMULATE_GRAD_VALUE if accumulate else 0) | \
         (FLAG_CONTINUE_SCRATCH if continue_scratch else 0) | (FLAG_DEFER_SCRATCH if defer_scratch else 0)
-    _check(lib.msda_backward(*prob, _ptr(value), _ptr(loc), _ptr(attn), _ptr(gout),
+    _check(lib.msda_backward_ex(code, pcode, *prob[1:], _ptr(value), _ptr(loc), _ptr(attn), _ptr(gout),
                              _ptr(grad_value), _ptr(grad_loc), _ptr(grad_attn), acode, flags,
                              _ptr(workspace), ws_bytes, _stream(value.device, stream)))
     return grad_value, grad_loc, grad_attn
@@ -325,7 +356,7 @@ class PreparedCall:
                  attention_weights, grad_output=None, accum="auto", stream=None):
         self.lib = load_library()
         levels = _Levels(spatial_shapes, level_start_index)
-        code = _dtype_code(value, sampling_locations, attention_weights)
+        code, pcode = _dtype_codes(value, sampling_locations, attention_weights)
         for t in (value, sampling_locations, attention_weights):
             if not t.is_contiguous():
                 raise ValueError("PreparedCall needs contiguous tensors")
@@ -336,8 +367,9 @@ class PreparedCall:
         self.prob = _problem(code, B, S, M, D, levels, Q, K)
         self.device = value.device
         self._stream_arg = stream  # None: torch's current stream at each call (graph capture)
-        self._fwd_args = self.prob + (_ptr(value), _ptr(sampling_locations),
-                                      _ptr(attention_weights), _ptr(self.output))
+        ex = (code, pcode) + self.prob[1:]  # the _ex entry points' leading arguments
+        self._fwd_args = ex + (_ptr(value), _ptr(sampling_locations),
+                               _ptr(attention_weights), _ptr(self.output))
         self.accum_code = _ACCUM_CODES[accum]
         self.grad_output = grad_output
         if grad_output is not None:
@@ -350,7 +382,7 @@ class PreparedCall:
             need = int(self.lib.msda_backward_workspace_size(*self.prob, self.accum_code))
             self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=value.device) \
                 if need else None
-            self._bwd_head = self.prob + (_ptr(value), _ptr(sampling_locations),
+            self._bwd_head = ex + (_ptr(value), _ptr(sampling_locations),
                                           _ptr(attention_weights), _ptr(grad_output),
                                           _ptr(self.grad_value), _ptr(self.grad_loc),
                                           _ptr(self.grad_attn))
@@ -380,7 +412,7 @@ class PreparedCall:
         return [l for l, m in enumerate(self.plan()[0]) if m == "binned"]
 
     def forward(self) -> torch.Tensor:
-        _check(self.lib.msda_forward(*self._fwd_args, _stream(self.device, self._stream_arg)))
+        _check(self.lib.msda_forward_ex(*self._fwd_args, _stream(self.device, self._stream_arg)))
         return self.output
 
     def backward(self, accumulate: bool = False, accum=None, flags: int = 0):
@@ -388,6 +420,6 @@ class PreparedCall:
         code = self.accum_code if accum is None else _ACCUM_CODES[accum]
         ws = self._ws if accum is None else (self._ws if code == self.accum_code else (None, 0))
         fl = (FLAG_ACCUMULATE_GRAD_VALUE if accumulate else 0) | flags
-        _check(self.lib.msda_backward(*self._bwd_head, code, fl, ws[0], ws[1],
+        _check(self.lib.msda_backward_ex(*self._bwd_head, code, fl, ws[0], ws[1],
                                       _stream(self.device, self._stream_arg)))
         return self.grad_value, self.grad_loc, self.grad_attn

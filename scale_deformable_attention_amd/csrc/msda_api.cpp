@@ -152,6 +152,7 @@ int make_problem(int dtype, int64_t B, int64_t S, int64_t M, int64_t D, int64_t 
         return fail(MSDA_ERR_UNSUPPORTED,
                     "num_heads, head_dim, num_queries or num_levels*num_points too large");
     p->dtype = dtype;
+    p->pdtype = dtype;
     p->B = B;
     p->S = S;
     p->M = M;
@@ -456,6 +457,23 @@ int choose_bwd_mapping(const msda::Problem &p, bool pairs_aligned, msda::BwdMapp
     return MSDA_OK;
 }
 
+// Parameter dtype of a call (sampling locations, attention weights and their
+// gradients): the value dtype, or fp32 beside 16-bit values (msda-triton
+// README, section "Caveats": 16-bit locations quantise coordinates at large
+// resolutions). The mixed kernels address the batch's value slice through a
+// buffer resource, so that slice must stay below 2 GiB.
+int set_param_dtype(msda::Problem *p, int pdtype) {
+    if (pdtype != p->dtype && !(pdtype == MSDA_F32 && p->dtype != MSDA_F32))
+        return fail(MSDA_ERR_DTYPE,
+                    "param_dtype %d must equal value_dtype %d or be MSDA_F32 beside 16-bit values",
+                    pdtype, p->dtype);
+    if (pdtype != p->dtype && p->S * p->M * p->D * (int64_t)elem_size(p->dtype) > ((int64_t)1 << 31) - 64)
+        return fail(MSDA_ERR_UNSUPPORTED,
+                    "mixed dtypes need a value slice of one batch below 2 GiB");
+    p->pdtype = pdtype;
+    return MSDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -499,20 +517,22 @@ const char *msda_status_string(int status) {
     }
 }
 
-int msda_forward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, int64_t head_dim,
-                 int64_t num_levels, const int64_t *spatial_shapes,
-                 const int64_t *level_start_index, int64_t num_queries, int64_t num_points,
-                 const void *value, const void *sampling_locations, const void *attention_weights,
-                 void *output, void *stream) {
+static int forward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
+                        int64_t num_heads, int64_t head_dim, int64_t num_levels,
+                        const int64_t *spatial_shapes, const int64_t *level_start_index,
+                        int64_t num_queries, int64_t num_points, const void *value,
+                        const void *sampling_locations, const void *attention_weights,
+                        void *output, void *stream) {
     LaunchEventsScope events_scope;
     msda::Problem p;
     int st = make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
                           level_start_index, num_queries, num_points, &p);
     if (st) return st;
+    if ((st = set_param_dtype(&p, pdtype))) return st;
     if (p.B == 0 || p.Q == 0) return ok();  // empty tensors may carry NULL pointers
     if ((st = check_ptr(value, "value", dtype))) return st;
-    if ((st = check_ptr(sampling_locations, "sampling_locations", dtype))) return st;
-    if ((st = check_ptr(attention_weights, "attention_weights", dtype))) return st;
+    if ((st = check_ptr(sampling_locations, "sampling_locations", pdtype))) return st;
+    if ((st = check_ptr(attention_weights, "attention_weights", pdtype))) return st;
     if ((st = check_ptr(output, "output", dtype))) return st;
     const void *vec_ptrs[] = {value, output};
     msda::Mapping mp;
@@ -523,6 +543,27 @@ int msda_forward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, 
                             s, "msda_fwd_kernel");
     if (err != hipSuccess) return hip_fail(err, "forward launch");
     return ok();
+}
+
+int msda_forward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, int64_t head_dim,
+                 int64_t num_levels, const int64_t *spatial_shapes,
+                 const int64_t *level_start_index, int64_t num_queries, int64_t num_points,
+                 const void *value, const void *sampling_locations, const void *attention_weights,
+                 void *output, void *stream) {
+    return forward_impl(dtype, dtype, batch, num_keys, num_heads, head_dim, num_levels,
+                        spatial_shapes, level_start_index, num_queries, num_points, value,
+                        sampling_locations, attention_weights, output, stream);
+}
+
+int msda_forward_ex(int value_dtype, int param_dtype, int64_t batch, int64_t num_keys,
+                    int64_t num_heads, int64_t head_dim, int64_t num_levels,
+                    const int64_t *spatial_shapes, const int64_t *level_start_index,
+                    int64_t num_queries, int64_t num_points, const void *value,
+                    const void *sampling_locations, const void *attention_weights, void *output,
+                    void *stream) {
+    return forward_impl(value_dtype, param_dtype, batch, num_keys, num_heads, head_dim,
+                        num_levels, spatial_shapes, level_start_index, num_queries, num_points,
+                        value, sampling_locations, attention_weights, output, stream);
 }
 
 int msda_forward_point_parallel(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
@@ -624,18 +665,20 @@ size_t msda_backward_workspace_size(int dtype, int64_t batch, int64_t num_keys, 
     return bytes;
 }
 
-int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, int64_t head_dim,
-                  int64_t num_levels, const int64_t *spatial_shapes,
-                  const int64_t *level_start_index, int64_t num_queries, int64_t num_points,
-                  const void *value, const void *sampling_locations, const void *attention_weights,
-                  const void *grad_output, void *grad_value, void *grad_sampling_locations,
-                  void *grad_attention_weights, int accum, unsigned flags, void *workspace,
-                  size_t workspace_bytes, void *stream) {
+static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
+                         int64_t num_heads, int64_t head_dim, int64_t num_levels,
+                         const int64_t *spatial_shapes, const int64_t *level_start_index,
+                         int64_t num_queries, int64_t num_points, const void *value,
+                         const void *sampling_locations, const void *attention_weights,
+                         const void *grad_output, void *grad_value, void *grad_sampling_locations,
+                         void *grad_attention_weights, int accum, unsigned flags,
+                         void *workspace, size_t workspace_bytes, void *stream) {
     LaunchEventsScope events_scope;
     msda::Problem p;
     int st = make_problem(dtype, batch, num_keys, num_heads, head_dim, num_levels, spatial_shapes,
                           level_start_index, num_queries, num_points, &p);
     if (st) return st;
+    if ((st = set_param_dtype(&p, pdtype))) return st;
     if (!valid_accum(accum)) return fail(MSDA_ERR_DTYPE, "unknown accumulation mode %d", accum);
     const unsigned known =
         MSDA_FLAG_ACCUMULATE_GRAD_VALUE | MSDA_FLAG_CONTINUE_SCRATCH | MSDA_FLAG_DEFER_SCRATCH;
@@ -674,11 +717,11 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
     msda::BwdMapping mp = {1, 1, 0, 0};
     msda::Mapping gmp = {1, 0, 0};  // gradients-only kernel (binned modes)
     if (p.Q > 0) {
-        if ((st = check_ptr(sampling_locations, "sampling_locations", dtype))) return st;
-        if ((st = check_ptr(attention_weights, "attention_weights", dtype))) return st;
+        if ((st = check_ptr(sampling_locations, "sampling_locations", pdtype))) return st;
+        if ((st = check_ptr(attention_weights, "attention_weights", pdtype))) return st;
         if ((st = check_ptr(grad_output, "grad_output", dtype))) return st;
-        if ((st = check_ptr(grad_sampling_locations, "grad_sampling_locations", dtype))) return st;
-        if ((st = check_ptr(grad_attention_weights, "grad_attention_weights", dtype))) return st;
+        if ((st = check_ptr(grad_sampling_locations, "grad_sampling_locations", pdtype))) return st;
+        if ((st = check_ptr(grad_attention_weights, "grad_attention_weights", pdtype))) return st;
         const bool pairs = aligned(value, 4) && aligned(grad_output, 4) && aligned(grad_value, 4);
         if ((st = choose_bwd_mapping(p, pairs, &mp))) return st;
         const void *vec_ptrs[2] = {value, grad_output};
@@ -823,6 +866,35 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                       s, "scratch_add_kernel")) != hipSuccess)
         return hip_fail(err, "scratch add launch");
     return ok();
+}
+
+int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads, int64_t head_dim,
+                  int64_t num_levels, const int64_t *spatial_shapes,
+                  const int64_t *level_start_index, int64_t num_queries, int64_t num_points,
+                  const void *value, const void *sampling_locations, const void *attention_weights,
+                  const void *grad_output, void *grad_value, void *grad_sampling_locations,
+                  void *grad_attention_weights, int accum, unsigned flags, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    return backward_impl(dtype, dtype, batch, num_keys, num_heads, head_dim, num_levels,
+                         spatial_shapes, level_start_index, num_queries, num_points, value,
+                         sampling_locations, attention_weights, grad_output, grad_value,
+                         grad_sampling_locations, grad_attention_weights, accum, flags, workspace,
+                         workspace_bytes, stream);
+}
+
+int msda_backward_ex(int value_dtype, int param_dtype, int64_t batch, int64_t num_keys,
+                     int64_t num_heads, int64_t head_dim, int64_t num_levels,
+                     const int64_t *spatial_shapes, const int64_t *level_start_index,
+                     int64_t num_queries, int64_t num_points, const void *value,
+                     const void *sampling_locations, const void *attention_weights,
+                     const void *grad_output, void *grad_value, void *grad_sampling_locations,
+                     void *grad_attention_weights, int accum, unsigned flags, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    return backward_impl(value_dtype, param_dtype, batch, num_keys, num_heads, head_dim,
+                         num_levels, spatial_shapes, level_start_index, num_queries, num_points,
+                         value, sampling_locations, attention_weights, grad_output, grad_value,
+                         grad_sampling_locations, grad_attention_weights, accum, flags, workspace,
+                         workspace_bytes, stream);
 }
 
 }  // extern "C"

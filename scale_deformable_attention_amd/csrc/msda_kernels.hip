@@ -29,6 +29,8 @@
 // remapped so that each XCD receives a contiguous range of (batch, head,
 // query-block) tiles, keeping one (b, m) slice of value in one L2.
 
+#include <type_traits>
+
 #include "msda_launch.h"
 
 namespace msda {
@@ -312,10 +314,10 @@ __device__ __forceinline__ Cell map_cell(float loc_x, float loc_y, float Hf, flo
 // only then consumed, so a wave waits for two memory round trips per chunk
 // instead of two per point.
 
-template <class DT, int VEC, int CH, bool BUF>
+template <class DT, class PT, int VEC, int CH, bool BUF>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void msda_fwd_kernel(
-    const typename DT::S *__restrict__ value, const typename DT::S *__restrict__ loc,
-    const typename DT::S *__restrict__ attn, typename DT::S *__restrict__ out,
+    const typename DT::S *__restrict__ value, const typename PT::S *__restrict__ loc,
+    const typename PT::S *__restrict__ attn, typename DT::S *__restrict__ out,
     const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
     const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
     const int log2s) {
@@ -341,8 +343,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const int per_lane = LK >> log2s;
 
     const int64_t pq = (b * Q + (q_ok ? q : 0)) * M + m;  // clamped: always a valid query
-    const E *loc_q = loc + pq * LK * 2;
-    const E *attn_q = attn + pq * LK;
+    const typename PT::S *loc_q = loc + pq * LK * 2;
+    const typename PT::S *attn_q = attn + pq * LK;
     const int64_t MD = (int64_t)M * D;
     const int64_t row_bytes = MD * (int64_t)sizeof(E);
     const Slice<BUF> slice(value + b * S * MD, S * row_bytes);
@@ -357,9 +359,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
             const int p = (i0 + t < per_lane ? i0 + t : 0) * split + s;
-            bx[t] = load_bits<DT>(loc_q + 2 * p);
-            by[t] = load_bits<DT>(loc_q + 2 * p + 1);
-            ba[t] = load_bits<DT>(attn_q + p);
+            bx[t] = load_bits<PT>(loc_q + 2 * p);
+            by[t] = load_bits<PT>(loc_q + 2 * p + 1);
+            ba[t] = load_bits<PT>(attn_q + p);
         }
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
@@ -370,9 +372,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         float lx[CH], ly[CH], aw[CH];
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
-            lx[t] = bits_to_f32<DT>(bx[t]);
-            ly[t] = bits_to_f32<DT>(by[t]);
-            aw[t] = (q_ok && i0 + t < per_lane) ? bits_to_f32<DT>(ba[t]) : 0.0f;
+            lx[t] = bits_to_f32<PT>(bx[t]);
+            ly[t] = bits_to_f32<PT>(by[t]);
+            aw[t] = (q_ok && i0 + t < per_lane) ? bits_to_f32<PT>(ba[t]) : 0.0f;
         }
         int64_t off[CH][4];
         bool ok[CH][4];
@@ -509,11 +511,11 @@ __global__ __launch_bounds__(kBlock) void msda_foil_kernel(
 // kernel", section "What the backward pass must produce"); the group's
 // shares are summed with DPP moves and lane c stores point t0 + c of the
 // chunk, so a group writes consecutive points with one instruction.
-template <class DT, int VEC, int CH, bool BUF>
+template <class DT, class PT, int VEC, int CH, bool BUF>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void msda_grad_kernel(
-    const typename DT::S *__restrict__ value, const typename DT::S *__restrict__ loc,
-    const typename DT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out,
-    typename DT::S *__restrict__ grad_loc, typename DT::S *__restrict__ grad_attn,
+    const typename DT::S *__restrict__ value, const typename PT::S *__restrict__ loc,
+    const typename PT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out,
+    typename PT::S *__restrict__ grad_loc, typename PT::S *__restrict__ grad_attn,
     const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
     const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
     const int log2s) {
@@ -540,8 +542,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const int per_lane = LK >> log2s;
 
     const int64_t pq = (b * Q + (q_ok ? q : 0)) * M + m;  // clamped: always a valid query
-    const E *loc_q = loc + pq * LK * 2;
-    const E *attn_q = attn + pq * LK;
+    const typename PT::S *loc_q = loc + pq * LK * 2;
+    const typename PT::S *attn_q = attn + pq * LK;
     const int64_t MD = (int64_t)M * D;
     const int64_t row_bytes = MD * (int64_t)sizeof(E);
     const Slice<BUF> slice(value + b * S * MD, S * row_bytes);
@@ -557,9 +559,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
             const int p = (i0 + t < per_lane ? i0 + t : 0) * split + s;
-            bx[t] = load_bits<DT>(loc_q + 2 * p);
-            by[t] = load_bits<DT>(loc_q + 2 * p + 1);
-            ba[t] = load_bits<DT>(attn_q + p);
+            bx[t] = load_bits<PT>(loc_q + 2 * p);
+            by[t] = load_bits<PT>(loc_q + 2 * p + 1);
+            ba[t] = load_bits<PT>(attn_q + p);
         }
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
@@ -576,10 +578,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
             int l = ((i0 + t) * split) / K;
             l = l < L ? l : L - 1;
             const int H = lt.H[l], W = lt.W[l];
-            const float aw = (q_ok && i0 + t < per_lane) ? bits_to_f32<DT>(ba[t]) : 0.0f;
+            const float aw = (q_ok && i0 + t < per_lane) ? bits_to_f32<PT>(ba[t]) : 0.0f;
             sw[t] = (float)W * aw;
             sh[t] = (float)H * aw;
-            const Cell cl = map_cell(bits_to_f32<DT>(bx[t]), bits_to_f32<DT>(by[t]), (float)H,
+            const Cell cl = map_cell(bits_to_f32<PT>(bx[t]), bits_to_f32<PT>(by[t]), (float)H,
                                      (float)W, W, lt.start[l]);
             fx[t] = cl.fx;
             fy[t] = cl.fy;
@@ -637,9 +639,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
             }
             if (q_ok && t < CH && i0 + t < per_lane) {
                 const int64_t pp = pq * LK + (i0 + t) * split + s;
-                grad_attn[pp] = from_f32(DT{}, vs);
-                grad_loc[2 * pp] = from_f32(DT{}, vx);
-                grad_loc[2 * pp + 1] = from_f32(DT{}, vy);
+                grad_attn[pp] = from_f32(PT{}, vs);
+                grad_loc[2 * pp] = from_f32(PT{}, vx);
+                grad_loc[2 * pp + 1] = from_f32(PT{}, vy);
             }
         }
     }
@@ -750,12 +752,12 @@ struct BwdChunk {
     static constexpr int value = J >= 8 ? 1 : (J >= 3 ? 2 : 8 / J);
 };
 
-template <class DT, int SLOT, int J, bool BUF>
+template <class DT, class PT, int SLOT, int J, bool BUF>
 __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
-    const typename DT::S *__restrict__ value, const typename DT::S *__restrict__ loc,
-    const typename DT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out,
+    const typename DT::S *__restrict__ value, const typename PT::S *__restrict__ loc,
+    const typename PT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out,
     void *__restrict__ grad_value, float *__restrict__ workspace,
-    typename DT::S *__restrict__ grad_loc, typename DT::S *__restrict__ grad_attn,
+    typename PT::S *__restrict__ grad_loc, typename PT::S *__restrict__ grad_attn,
     const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
     const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
     const int log2s) {
@@ -782,8 +784,8 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
     const int per_lane = LK >> log2s;
 
     const int64_t pq = (b * Q + (q_ok ? q : 0)) * M + m;  // clamped: always a valid query
-    const E *loc_q = loc + pq * LK * 2;
-    const E *attn_q = attn + pq * LK;
+    const typename PT::S *loc_q = loc + pq * LK * 2;
+    const typename PT::S *attn_q = attn + pq * LK;
     const int64_t MD = (int64_t)M * D;
     const int64_t row_bytes = MD * (int64_t)sizeof(E);
     const int64_t bS = b * S;
@@ -800,8 +802,8 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
         for (int t = 0; t < CH; ++t) {
             const bool t_ok = i0 + t < per_lane;  // uniform
             const int p = (t_ok ? i0 + t : 0) * split + s;
-            load_xy<DT>(loc_q + 2 * p, lx[t], ly[t]);
-            const float a = to_f32(DT{}, attn_q[p]);
+            load_xy<PT>(loc_q + 2 * p, lx[t], ly[t]);
+            const float a = to_f32(PT{}, attn_q[p]);
             aw[t] = (q_ok && t_ok) ? a : 0.0f;
         }
         Cell cl[CH];
@@ -877,9 +879,9 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
             }
             if (q_ok && t < CH && i0 + t < per_lane) {
                 const int64_t pp = pq * LK + (i0 + t) * split + s;
-                grad_attn[pp] = from_f32(DT{}, vs);
-                grad_loc[2 * pp] = from_f32(DT{}, vx);
-                grad_loc[2 * pp + 1] = from_f32(DT{}, vy);
+                grad_attn[pp] = from_f32(PT{}, vs);
+                grad_loc[2 * pp] = from_f32(PT{}, vx);
+                grad_loc[2 * pp + 1] = from_f32(PT{}, vy);
             }
         }
 #pragma unroll
@@ -897,14 +899,13 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
 // grad_loc / grad_attn come from msda_grad_kernel: no value gathers, no dot
 // products. Same lane mapping as msda_bwd_kernel; a group walks the points of
 // each unbinned level, CH at a time with their parameter loads issued first.
-template <class DT, int SLOT, int J>
+template <class DT, class PT, int SLOT, int J>
 __global__ __launch_bounds__(kBlock) void msda_scatter_kernel(
-    const typename DT::S *__restrict__ loc, const typename DT::S *__restrict__ attn,
+    const typename PT::S *__restrict__ loc, const typename PT::S *__restrict__ attn,
     const typename DT::S *__restrict__ grad_out, void *__restrict__ grad_value,
     float *__restrict__ workspace, const LevelTable lt, const int64_t S, const int64_t Q,
     const int M, const int D, const int L, const int K, const int qblocks, const int64_t ntiles,
     const int log2g, const int log2s) {
-    using E = typename DT::S;
     constexpr int JC = J * SLOT;
     constexpr int CH = 8;
     const int64_t tile = logical_block();
@@ -923,8 +924,8 @@ __global__ __launch_bounds__(kBlock) void msda_scatter_kernel(
     const int split = 1 << log2s;
     const int LK = L * K;
     const int64_t pq = (b * Q + (q_ok ? q : 0)) * M + m;  // clamped: always a valid query
-    const E *loc_q = loc + pq * LK * 2;
-    const E *attn_q = attn + pq * LK;
+    const typename PT::S *loc_q = loc + pq * LK * 2;
+    const typename PT::S *attn_q = attn + pq * LK;
     const int64_t MD = (int64_t)M * D;
     const int64_t bS = b * S;
     bool slot_ok[J];
@@ -940,9 +941,9 @@ __global__ __launch_bounds__(kBlock) void msda_scatter_kernel(
             for (int t = 0; t < CH; ++t) {
                 const int k = k0 + t * split;  // + s: the group's own point of this stride
                 const int p = l * K + (k < K ? k + s : s);
-                bx[t] = load_bits<DT>(loc_q + 2 * p);
-                by[t] = load_bits<DT>(loc_q + 2 * p + 1);
-                ba[t] = load_bits<DT>(attn_q + p);
+                bx[t] = load_bits<PT>(loc_q + 2 * p);
+                by[t] = load_bits<PT>(loc_q + 2 * p + 1);
+                ba[t] = load_bits<PT>(attn_q + p);
             }
 #pragma unroll
             for (int t = 0; t < CH; ++t) {
@@ -953,9 +954,9 @@ __global__ __launch_bounds__(kBlock) void msda_scatter_kernel(
 #pragma unroll
             for (int t = 0; t < CH; ++t) {
                 if (!(q_ok && k0 + t * split < K)) continue;
-                const Cell cl = map_cell(bits_to_f32<DT>(bx[t]), bits_to_f32<DT>(by[t]), Hf, Wf, W,
+                const Cell cl = map_cell(bits_to_f32<PT>(bx[t]), bits_to_f32<PT>(by[t]), Hf, Wf, W,
                                          lt.start[l]);
-                scatter_point<DT, SLOT, J>(cl, bits_to_f32<DT>(ba[t]), lt, l, grad_value, workspace,
+                scatter_point<DT, SLOT, J>(cl, bits_to_f32<PT>(ba[t]), lt, l, grad_value, workspace,
                                            b, bS, m, M, D, MD, c, G, slot_ok, g, gc);
             }
         }
@@ -1374,76 +1375,83 @@ bool slice_fits_buffer(const Problem &p) {
     return p.S * p.M * p.D * e <= (int64_t)kOutOfRange - 64;
 }
 
-template <class DT, int VEC>
+template <class DT, class PT, int VEC>
 hipError_t fwd_launch(const Problem &p, const Mapping &mp, const void *value, const void *loc,
                       const void *attn, void *out, hipStream_t stream) {
     // 4 points per chunk; 16-byte gathers keep 16 x 4 VGPRs of raw data in flight
     constexpr int CH = 4;
     using E = typename DT::S;
+    using P = typename PT::S;
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
     const int qblocks = (int)((p.Q + qpb - 1) / qpb);
     const int64_t ntiles = p.B * p.M * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (slice_fits_buffer(p))
-        hipLaunchKernelGGL((msda_fwd_kernel<DT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
+        hipLaunchKernelGGL((msda_fwd_kernel<DT, PT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
                            dim3(kBlock), 0, stream, static_cast<const E *>(value),
-                           static_cast<const E *>(loc), static_cast<const E *>(attn),
+                           static_cast<const P *>(loc), static_cast<const P *>(attn),
+                           static_cast<E *>(out), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
+                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
+    else if constexpr (std::is_same<DT, PT>::value)
+        hipLaunchKernelGGL((msda_fwd_kernel<DT, PT, VEC, CH, false>), dim3((unsigned)(per_xcd * kXcds)),
+                           dim3(kBlock), 0, stream, static_cast<const E *>(value),
+                           static_cast<const P *>(loc), static_cast<const P *>(attn),
                            static_cast<E *>(out), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
                            (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
     else
-        hipLaunchKernelGGL((msda_fwd_kernel<DT, VEC, CH, false>), dim3((unsigned)(per_xcd * kXcds)),
-                           dim3(kBlock), 0, stream, static_cast<const E *>(value),
-                           static_cast<const E *>(loc), static_cast<const E *>(attn),
-                           static_cast<E *>(out), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
-                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
+        return hipErrorInvalidValue;  // mixed dtypes need a buffer-addressable slice
     return hipGetLastError();
 }
 
-template <class DT, int VEC>
+template <class DT, class PT, int VEC>
 hipError_t grad_launch(const Problem &p, const Mapping &mp, const void *value, const void *loc,
                        const void *attn, const void *grad_out, void *grad_loc, void *grad_attn,
                        hipStream_t stream) {
     constexpr int CH = 4;
     using E = typename DT::S;
+    using P = typename PT::S;
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
     const int qblocks = (int)((p.Q + qpb - 1) / qpb);
     const int64_t ntiles = p.B * p.M * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (!slice_fits_buffer(p)) return hipErrorInvalidValue;  // binning requires it
-    hipLaunchKernelGGL((msda_grad_kernel<DT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
+    hipLaunchKernelGGL((msda_grad_kernel<DT, PT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
                        dim3(kBlock), 0, stream, static_cast<const E *>(value),
-                       static_cast<const E *>(loc), static_cast<const E *>(attn),
-                       static_cast<const E *>(grad_out), static_cast<E *>(grad_loc),
-                       static_cast<E *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
+                       static_cast<const P *>(loc), static_cast<const P *>(attn),
+                       static_cast<const E *>(grad_out), static_cast<P *>(grad_loc),
+                       static_cast<P *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
                        (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
     return hipGetLastError();
 }
 
-template <class DT, int SLOT, int J>
+template <class DT, class PT, int SLOT, int J>
 hipError_t bwd_launch(const Problem &p, const BwdMapping &mp, const void *value, const void *loc,
                       const void *attn, const void *grad_out, void *grad_value, float *workspace,
                       void *grad_loc, void *grad_attn, hipStream_t stream) {
     using E = typename DT::S;
+    using P = typename PT::S;
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
     const int qblocks = (int)((p.Q + qpb - 1) / qpb);
     const int64_t ntiles = p.B * p.M * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (slice_fits_buffer(p))
-        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, true>),
+        hipLaunchKernelGGL((msda_bwd_kernel<DT, PT, SLOT, J, true>),
                            dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
-                           static_cast<const E *>(value), static_cast<const E *>(loc),
-                           static_cast<const E *>(attn), static_cast<const E *>(grad_out),
-                           grad_value, workspace, static_cast<E *>(grad_loc),
-                           static_cast<E *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
+                           static_cast<const E *>(value), static_cast<const P *>(loc),
+                           static_cast<const P *>(attn), static_cast<const E *>(grad_out),
+                           grad_value, workspace, static_cast<P *>(grad_loc),
+                           static_cast<P *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
+                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
+    else if constexpr (std::is_same<DT, PT>::value)
+        hipLaunchKernelGGL((msda_bwd_kernel<DT, PT, SLOT, J, false>),
+                           dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
+                           static_cast<const E *>(value), static_cast<const P *>(loc),
+                           static_cast<const P *>(attn), static_cast<const E *>(grad_out),
+                           grad_value, workspace, static_cast<P *>(grad_loc),
+                           static_cast<P *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
                            (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
     else
-        hipLaunchKernelGGL((msda_bwd_kernel<DT, SLOT, J, false>),
-                           dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
-                           static_cast<const E *>(value), static_cast<const E *>(loc),
-                           static_cast<const E *>(attn), static_cast<const E *>(grad_out),
-                           grad_value, workspace, static_cast<E *>(grad_loc),
-                           static_cast<E *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
-                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
+        return hipErrorInvalidValue;  // mixed dtypes need a buffer-addressable slice
     return hipGetLastError();
 }
 
@@ -1477,90 +1485,91 @@ hipError_t accum_launch(const Problem &p, const BwdMapping &mp, const void *grad
     return accum_launch_v<DT, SLOT, J, 1>(p, mp, grad_out, grad_value, bins, accumulate, stream);
 }
 
-template <class DT>
+template <class DT, class PT>
 hipError_t fwd_by_vec(const Problem &p, const Mapping &mp, const void *v, const void *l,
                       const void *a, void *o, hipStream_t st) {
     switch (mp.vec) {
-        case 1: return fwd_launch<DT, 1>(p, mp, v, l, a, o, st);
-        case 2: return fwd_launch<DT, 2>(p, mp, v, l, a, o, st);
-        case 4: return fwd_launch<DT, 4>(p, mp, v, l, a, o, st);
+        case 1: return fwd_launch<DT, PT, 1>(p, mp, v, l, a, o, st);
+        case 2: return fwd_launch<DT, PT, 2>(p, mp, v, l, a, o, st);
+        case 4: return fwd_launch<DT, PT, 4>(p, mp, v, l, a, o, st);
         default: break;
     }
     if constexpr (sizeof(typename DT::S) == 4) {
-        if (mp.vec == 3) return fwd_launch<DT, 3>(p, mp, v, l, a, o, st);
+        if (mp.vec == 3) return fwd_launch<DT, PT, 3>(p, mp, v, l, a, o, st);
     } else {
-        if (mp.vec == 8) return fwd_launch<DT, 8>(p, mp, v, l, a, o, st);
+        if (mp.vec == 8) return fwd_launch<DT, PT, 8>(p, mp, v, l, a, o, st);
     }
     return hipErrorInvalidValue;
 }
 
-template <class DT, int SLOT, int J>
+template <class DT, class PT, int SLOT, int J>
 hipError_t scatter_launch(const Problem &p, const BwdMapping &mp, const void *loc, const void *attn,
                           const void *grad_out, void *grad_value, float *workspace,
                           hipStream_t stream) {
     using E = typename DT::S;
+    using P = typename PT::S;
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
     const int qblocks = (int)((p.Q + qpb - 1) / qpb);
     const int64_t ntiles = p.B * p.M * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((msda_scatter_kernel<DT, SLOT, J>), dim3((unsigned)(per_xcd * kXcds)),
-                       dim3(kBlock), 0, stream, static_cast<const E *>(loc),
-                       static_cast<const E *>(attn), static_cast<const E *>(grad_out), grad_value,
+    hipLaunchKernelGGL((msda_scatter_kernel<DT, PT, SLOT, J>), dim3((unsigned)(per_xcd * kXcds)),
+                       dim3(kBlock), 0, stream, static_cast<const P *>(loc),
+                       static_cast<const P *>(attn), static_cast<const E *>(grad_out), grad_value,
                        workspace, p.levels, p.S, p.Q, (int)p.M, (int)p.D, (int)p.L, (int)p.K,
                        qblocks, ntiles, mp.log2_group, mp.log2_split);
     return hipGetLastError();
 }
 
-template <class DT, int SLOT>
+template <class DT, class PT, int SLOT>
 hipError_t scatter_by_j(const Problem &p, const BwdMapping &mp, const void *l, const void *a,
                         const void *go, void *gv, float *ws, hipStream_t st) {
     switch (mp.j) {
-        case 1: return scatter_launch<DT, SLOT, 1>(p, mp, l, a, go, gv, ws, st);
-        case 2: return scatter_launch<DT, SLOT, 2>(p, mp, l, a, go, gv, ws, st);
-        case 3: return scatter_launch<DT, SLOT, 3>(p, mp, l, a, go, gv, ws, st);
-        case 4: return scatter_launch<DT, SLOT, 4>(p, mp, l, a, go, gv, ws, st);
-        case 8: return scatter_launch<DT, SLOT, 8>(p, mp, l, a, go, gv, ws, st);
-        case 16: return scatter_launch<DT, SLOT, 16>(p, mp, l, a, go, gv, ws, st);
+        case 1: return scatter_launch<DT, PT, SLOT, 1>(p, mp, l, a, go, gv, ws, st);
+        case 2: return scatter_launch<DT, PT, SLOT, 2>(p, mp, l, a, go, gv, ws, st);
+        case 3: return scatter_launch<DT, PT, SLOT, 3>(p, mp, l, a, go, gv, ws, st);
+        case 4: return scatter_launch<DT, PT, SLOT, 4>(p, mp, l, a, go, gv, ws, st);
+        case 8: return scatter_launch<DT, PT, SLOT, 8>(p, mp, l, a, go, gv, ws, st);
+        case 16: return scatter_launch<DT, PT, SLOT, 16>(p, mp, l, a, go, gv, ws, st);
         default: break;
     }
     if constexpr (SLOT == 1) {
-        if (mp.j == 32) return scatter_launch<DT, SLOT, 32>(p, mp, l, a, go, gv, ws, st);
+        if (mp.j == 32) return scatter_launch<DT, PT, SLOT, 32>(p, mp, l, a, go, gv, ws, st);
     }
     return hipErrorInvalidValue;
 }
 
-template <class DT, int SLOT>
+template <class DT, class PT, int SLOT>
 hipError_t bwd_by_j(const Problem &p, const BwdMapping &mp, const void *v, const void *l,
                     const void *a, const void *go, void *gv, float *ws, void *gl, void *ga,
                     hipStream_t st) {
     switch (mp.j) {
-        case 1: return bwd_launch<DT, SLOT, 1>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 2: return bwd_launch<DT, SLOT, 2>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 3: return bwd_launch<DT, SLOT, 3>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 4: return bwd_launch<DT, SLOT, 4>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 8: return bwd_launch<DT, SLOT, 8>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
-        case 16: return bwd_launch<DT, SLOT, 16>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 1: return bwd_launch<DT, PT, SLOT, 1>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 2: return bwd_launch<DT, PT, SLOT, 2>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 3: return bwd_launch<DT, PT, SLOT, 3>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 4: return bwd_launch<DT, PT, SLOT, 4>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 8: return bwd_launch<DT, PT, SLOT, 8>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        case 16: return bwd_launch<DT, PT, SLOT, 16>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
         default: break;
     }
     if constexpr (SLOT == 1) {
-        if (mp.j == 32) return bwd_launch<DT, SLOT, 32>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
+        if (mp.j == 32) return bwd_launch<DT, PT, SLOT, 32>(p, mp, v, l, a, go, gv, ws, gl, ga, st);
     }
     return hipErrorInvalidValue;
 }
 
-template <class DT>
+template <class DT, class PT>
 hipError_t grad_by_vec(const Problem &p, const Mapping &mp, const void *v, const void *l,
                        const void *a, const void *go, void *gl, void *ga, hipStream_t st) {
     switch (mp.vec) {
-        case 1: return grad_launch<DT, 1>(p, mp, v, l, a, go, gl, ga, st);
-        case 2: return grad_launch<DT, 2>(p, mp, v, l, a, go, gl, ga, st);
-        case 4: return grad_launch<DT, 4>(p, mp, v, l, a, go, gl, ga, st);
+        case 1: return grad_launch<DT, PT, 1>(p, mp, v, l, a, go, gl, ga, st);
+        case 2: return grad_launch<DT, PT, 2>(p, mp, v, l, a, go, gl, ga, st);
+        case 4: return grad_launch<DT, PT, 4>(p, mp, v, l, a, go, gl, ga, st);
         default: break;
     }
     if constexpr (sizeof(typename DT::S) == 4) {
-        if (mp.vec == 3) return grad_launch<DT, 3>(p, mp, v, l, a, go, gl, ga, st);
+        if (mp.vec == 3) return grad_launch<DT, PT, 3>(p, mp, v, l, a, go, gl, ga, st);
     } else {
-        if (mp.vec == 8) return grad_launch<DT, 8>(p, mp, v, l, a, go, gl, ga, st);
+        if (mp.vec == 8) return grad_launch<DT, PT, 8>(p, mp, v, l, a, go, gl, ga, st);
     }
     return hipErrorInvalidValue;
 }
@@ -1635,64 +1644,64 @@ hipError_t scratch_add(const Problem &p, const float *ws, void *gv, hipStream_t 
 
 }  // namespace
 
+// Parameter type: the value type, or fp32 beside 16-bit values.
+#define MSDA_BY_PT(DTT, CALL)                                        \
+    (p.pdtype == MSDA_F32 ? CALL(DTT, F32T) : CALL(DTT, DTT))
+
 hipError_t launch_forward(const Problem &p, const Mapping &mp, const void *value,
                           const void *loc, const void *attn, void *out, hipStream_t stream) {
+#define MSDA_FWD(T, P) fwd_by_vec<T, P>(p, mp, value, loc, attn, out, stream)
     switch (p.dtype) {
-        case MSDA_F32: return fwd_by_vec<F32T>(p, mp, value, loc, attn, out, stream);
-        case MSDA_F16: return fwd_by_vec<F16T>(p, mp, value, loc, attn, out, stream);
-        case MSDA_BF16: return fwd_by_vec<BF16T>(p, mp, value, loc, attn, out, stream);
+        case MSDA_F32: return MSDA_FWD(F32T, F32T);
+        case MSDA_F16: return MSDA_BY_PT(F16T, MSDA_FWD);
+        case MSDA_BF16: return MSDA_BY_PT(BF16T, MSDA_FWD);
         default: return hipErrorInvalidValue;
     }
+#undef MSDA_FWD
 }
 
 hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *value,
                            const void *loc, const void *attn, const void *grad_out,
                            void *grad_value, float *workspace, void *grad_loc, void *grad_attn,
                            hipStream_t stream) {
+#define MSDA_BWD1(T, P) bwd_by_j<T, P, 1>(p, mp, value, loc, attn, grad_out, grad_value, workspace, grad_loc, grad_attn, stream)
+#define MSDA_BWD2(T, P) bwd_by_j<T, P, 2>(p, mp, value, loc, attn, grad_out, grad_value, workspace, grad_loc, grad_attn, stream)
     switch (p.dtype) {
-        case MSDA_F32:
-            return bwd_by_j<F32T, 1>(p, mp, value, loc, attn, grad_out, grad_value, workspace,
-                                     grad_loc, grad_attn, stream);
-        case MSDA_F16:
-            return mp.slot == 2 ? bwd_by_j<F16T, 2>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                    workspace, grad_loc, grad_attn, stream)
-                                : bwd_by_j<F16T, 1>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                    workspace, grad_loc, grad_attn, stream);
-        case MSDA_BF16:
-            return mp.slot == 2 ? bwd_by_j<BF16T, 2>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                     workspace, grad_loc, grad_attn, stream)
-                                : bwd_by_j<BF16T, 1>(p, mp, value, loc, attn, grad_out, grad_value,
-                                                     workspace, grad_loc, grad_attn, stream);
+        case MSDA_F32: return MSDA_BWD1(F32T, F32T);
+        case MSDA_F16: return mp.slot == 2 ? MSDA_BY_PT(F16T, MSDA_BWD2) : MSDA_BY_PT(F16T, MSDA_BWD1);
+        case MSDA_BF16: return mp.slot == 2 ? MSDA_BY_PT(BF16T, MSDA_BWD2) : MSDA_BY_PT(BF16T, MSDA_BWD1);
         default: return hipErrorInvalidValue;
     }
+#undef MSDA_BWD1
+#undef MSDA_BWD2
 }
 
 hipError_t launch_scatter(const Problem &p, const BwdMapping &mp, const void *loc,
                           const void *attn, const void *grad_out, void *grad_value,
                           float *workspace, hipStream_t stream) {
+#define MSDA_SC1(T, P) scatter_by_j<T, P, 1>(p, mp, loc, attn, grad_out, grad_value, workspace, stream)
+#define MSDA_SC2(T, P) scatter_by_j<T, P, 2>(p, mp, loc, attn, grad_out, grad_value, workspace, stream)
     switch (p.dtype) {
-        case MSDA_F32: return scatter_by_j<F32T, 1>(p, mp, loc, attn, grad_out, grad_value, workspace, stream);
-        case MSDA_F16:
-            return mp.slot == 2
-                       ? scatter_by_j<F16T, 2>(p, mp, loc, attn, grad_out, grad_value, workspace, stream)
-                       : scatter_by_j<F16T, 1>(p, mp, loc, attn, grad_out, grad_value, workspace, stream);
-        case MSDA_BF16:
-            return mp.slot == 2
-                       ? scatter_by_j<BF16T, 2>(p, mp, loc, attn, grad_out, grad_value, workspace, stream)
-                       : scatter_by_j<BF16T, 1>(p, mp, loc, attn, grad_out, grad_value, workspace, stream);
+        case MSDA_F32: return MSDA_SC1(F32T, F32T);
+        case MSDA_F16: return mp.slot == 2 ? MSDA_BY_PT(F16T, MSDA_SC2) : MSDA_BY_PT(F16T, MSDA_SC1);
+        case MSDA_BF16: return mp.slot == 2 ? MSDA_BY_PT(BF16T, MSDA_SC2) : MSDA_BY_PT(BF16T, MSDA_SC1);
         default: return hipErrorInvalidValue;
     }
+#undef MSDA_SC1
+#undef MSDA_SC2
 }
 
 hipError_t launch_gradients(const Problem &p, const Mapping &mp, const void *value,
                             const void *loc, const void *attn, const void *grad_out,
                             void *grad_loc, void *grad_attn, hipStream_t stream) {
+#define MSDA_GR(T, P) grad_by_vec<T, P>(p, mp, value, loc, attn, grad_out, grad_loc, grad_attn, stream)
     switch (p.dtype) {
-        case MSDA_F32: return grad_by_vec<F32T>(p, mp, value, loc, attn, grad_out, grad_loc, grad_attn, stream);
-        case MSDA_F16: return grad_by_vec<F16T>(p, mp, value, loc, attn, grad_out, grad_loc, grad_attn, stream);
-        case MSDA_BF16: return grad_by_vec<BF16T>(p, mp, value, loc, attn, grad_out, grad_loc, grad_attn, stream);
+        case MSDA_F32: return MSDA_GR(F32T, F32T);
+        case MSDA_F16: return MSDA_BY_PT(F16T, MSDA_GR);
+        case MSDA_BF16: return MSDA_BY_PT(BF16T, MSDA_GR);
         default: return hipErrorInvalidValue;
     }
+#undef MSDA_GR
 }
 
 hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
@@ -1707,7 +1716,7 @@ hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
                        static_cast<const typename T::S *>(loc),                                 \
                        static_cast<const typename T::S *>(attn), p.levels, counter,             \
                        bins.records, p.Q, (int)p.M, (int)p.L, (int)p.K, p.nbbm, wpb, ntiles)
-    switch (p.dtype) {
+    switch (p.pdtype) {  // the kernels read only the parameters
         case MSDA_F32: if (place) MSDA_SORT(F32T, true); else MSDA_SORT(F32T, false); break;
         case MSDA_F16: if (place) MSDA_SORT(F16T, true); else MSDA_SORT(F16T, false); break;
         case MSDA_BF16: if (place) MSDA_SORT(BF16T, true); else MSDA_SORT(BF16T, false); break;

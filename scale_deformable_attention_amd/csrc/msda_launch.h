@@ -31,7 +31,9 @@ struct LevelTable {
 
 // Everything a launch needs, validated by the host layer.
 struct Problem {
-    int dtype;  // msda_dtype_t
+    int dtype;   // msda_dtype_t of value, output, grad_output, grad_value
+    int pdtype;  // of sampling_locations, attention_weights and their gradients:
+                 // dtype, or MSDA_F32 beside 16-bit values
     int64_t B, S, M, D, L, Q, K;
     LevelTable levels;
     int64_t nbbm;  // bins per (b, m) of the binned grad_value (0: not planned)

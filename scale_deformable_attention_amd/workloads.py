@@ -59,6 +59,7 @@ class Workload:
     loc_sigma: float = 0.0
     loc_clamp: Optional[Tuple[float, float]] = None
     seed: int = 0
+    param_dtype: Optional[torch.dtype] = None  # locations / weights; None: dtype
 
     @property
     def L(self) -> int:
@@ -98,6 +99,14 @@ WORKLOADS = {
         name="large_encoder_bf16", dtype=torch.bfloat16, B=1, Q=None, M=8,
         D=32, K=4, levels=((512, 896), (256, 448), (128, 224), (64, 112)),
         loc_kind="reference", loc_sigma=0.01, seed=1005),
+    # mixed dtypes: bf16 / fp16 values, fp32 locations and weights
+    "decoder_mixed": Workload(
+        name="decoder_mixed", dtype=torch.bfloat16, B=4, Q=300, M=8, D=32, K=4,
+        levels=_DECODER_LEVELS, loc_kind="uniform", seed=1006, param_dtype=torch.float32),
+    "encoder_mixed": Workload(
+        name="encoder_mixed", dtype=torch.float16, B=4, Q=None, M=8, D=32, K=4,
+        levels=_DECODER_LEVELS, loc_kind="reference", loc_sigma=0.02,
+        loc_clamp=(-0.05, 1.05), seed=1007, param_dtype=torch.float32),
 }
 
 
@@ -121,7 +130,8 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, device="cpu",
 
     Returns a dict of CPU (or `device`) tensors in the workload dtype:
     value, spatial_shapes (int64), sampling_locations, attention_weights and,
-    if `with_grad`, grad_output.
+    if `with_grad`, grad_output. Locations and weights take
+    `wl.param_dtype` when it is set.
     """
     g = torch.Generator(device="cpu")
     g.manual_seed(wl.seed if seed is None else seed)
@@ -148,8 +158,8 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, device="cpu",
     out = {
         "value": value.to(wl.dtype),
         "spatial_shapes": torch.tensor(wl.levels, dtype=torch.int64).reshape(L, 2),
-        "sampling_locations": loc.to(wl.dtype),
-        "attention_weights": attn.to(wl.dtype),
+        "sampling_locations": loc.to(wl.param_dtype or wl.dtype),
+        "attention_weights": attn.to(wl.param_dtype or wl.dtype),
     }
     del value, loc, attn
     if with_grad:

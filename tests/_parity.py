@@ -85,10 +85,16 @@ def check_forward(dtype, out_gpu, out_ref, touched=None) -> list:
 
 
 def check_backward(dtype, gpu, ref, spatial_shapes, level_start_index=None,
-                   touched_rows=None) -> list:
+                   touched_rows=None, param_dtype=None) -> list:
+    """`param_dtype`: dtype of the locations / weights and their gradients
+    when it differs from the value dtype (mixed calls); their tolerances follow
+    it, since those gradients are fp32 sums rounded once to it."""
     gv, gl, ga = (to_np(t) for t in gpu)
     rgv, rgl, rga = ref
-    tol = TOL[dtype]
+    tol = dict(TOL[dtype])
+    if param_dtype is not None:
+        for k in ("grad_attention_weights", "grad_sampling_locations"):
+            tol[k] = TOL[param_dtype][k]
     stats = [check_slice("grad_attention_weights", ga, rga, tol["grad_attention_weights"])]
     for l, (r0, r1) in enumerate(level_row_ranges(spatial_shapes, level_start_index)):
         stats.append(check_slice(f"grad_value[level {l}]", gv[:, r0:r1], rgv[:, r0:r1],

@@ -92,6 +92,21 @@ def test_forward_rejects(lib, kw, status):
     assert lib.msda_last_error().decode() != ""
 
 
+def test_mixed_dtype_pairs(lib):
+    # (value, param): (bf16, fp32) and (fp16, fp32) are accepted; any other
+    # differing pair is a dtype error, checked before any launch
+    for v, pdt, status in [(2, 0, 0), (1, 0, 0), (0, 2, 4), (2, 1, 4), (1, 2, 4), (0, 1, 4)]:
+        got = lib.msda_forward_ex(v, pdt, 1, 100, 2, 8, 2, SHAPES, None, 0, 2, FAKE, FAKE, FAKE,
+                                  FAKE, None)
+        assert got == status, (v, pdt, got)
+        got = lib.msda_backward_ex(v, pdt, 0, 100, 2, 8, 2, SHAPES, None, 16, 2, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, 0, 0, None, 0, None)
+        assert got == status, (v, pdt, got)
+    # fp32 parameters are checked at fp32 alignment
+    assert lib.msda_forward_ex(2, 0, 1, 100, 2, 8, 2, SHAPES, None, 16, 2, FAKE,
+                               ctypes.c_void_p(0x10002), FAKE, FAKE, None) == 5
+
+
 def test_point_parallel_foil_limits(lib):
     args = (0, 1, 100, 2, 8, 2, SHAPES, None, 16, 2, FAKE, FAKE, FAKE, FAKE, None)
     assert lib.msda_forward_point_parallel(*args[:5], 2, SHAPES, None, 0, 2, *args[10:]) == 0

@@ -456,3 +456,34 @@ def test_point_parallel_foil_parity(name):
                                       g["sampling_locations"], g["attention_weights"])
     torch.cuda.synchronize()
     check_forward(wl.dtype, out.cpu(), ref_out, touched)
+
+
+@pytest.mark.parametrize("name,accum", [("decoder_mixed", "auto"), ("decoder_mixed", "native"),
+                                        ("decoder_mixed", "per_level"), ("encoder_mixed", "auto")])
+def test_mixed_dtype_parity(name, accum):
+    """16-bit values with fp32 locations and weights: output and grad_value in
+    the value dtype, grad_loc / grad_attn in fp32 at the fp32 tolerance."""
+    wl = workload(name)
+    say(f"case {name} accum={accum}: value {wl.dtype}, parameters {wl.param_dtype}")
+    inp, ref = _cached(name)
+    assert inp["sampling_locations"].dtype == torch.float32 and inp["value"].dtype == wl.dtype
+    out, grads = gpu_run(inp, accum)
+    assert out.dtype == wl.dtype and grads[0].dtype == wl.dtype
+    assert grads[1].dtype == torch.float32 and grads[2].dtype == torch.float32
+    ref_out, touched, ref_grads, trows = ref
+    check_forward(wl.dtype, out, ref_out, touched)
+    check_backward(wl.dtype, grads, ref_grads, inp["spatial_shapes"], None, trows,
+                   param_dtype=torch.float32)
+
+
+def test_mixed_dtype_rejections():
+    wl = workload("decoder_mixed")
+    inp = make_inputs(wl.replace(Q=8))
+    g = to_dev(inp)
+    v16 = g["value"].to(torch.float16)  # fp16 value with bf16 parameters: not a valid pair
+    with pytest.raises(TypeError):
+        msda_forward(g["value"], g["spatial_shapes"], None, g["sampling_locations"].bfloat16(),
+                     g["attention_weights"])
+    with pytest.raises(TypeError):
+        msda_forward(v16, g["spatial_shapes"], None, g["sampling_locations"].bfloat16(),
+                     g["attention_weights"].bfloat16())
