@@ -59,3 +59,46 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
                         PINS], cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
+
+
+# Mistakes planted in a copy of oracle/module.py (the steps around the core);
+# the copy is loaded as a module object and the module pins must fail on it.
+MODULE_MUTANTS = {
+    "offset_x_scaled_by_H": ("loc[:, :, :, l, :, 0] = r[:, :, None, None, 0] + off[:, :, :, l, :, 0] / W",
+                             "loc[:, :, :, l, :, 0] = r[:, :, None, None, 0] + off[:, :, :, l, :, 0] / H"),
+    "softmax_per_level": ("attn = softmax_lk(logits).reshape(B, Q, M, L, K)",
+                          "attn = softmax_lk(logits.reshape(B, Q, M, L, K))"),
+    "softmax_grad_missing_inner": ("g_logits = af * (gf - inner)", "g_logits = af * gf"),
+    "grad_offset_unscaled": ("g_off[:, :, :, l, :, 1] = gl[:, :, :, l, :, 1] / H",
+                             "g_off[:, :, :, l, :, 1] = gl[:, :, :, l, :, 1]"),
+    "grad_ref_one_level": ("g_ref = per_level if ref_per_level else per_level.sum(axis=2)",
+                           "g_ref = per_level if ref_per_level else per_level[:, :, 0]"),
+    "heads_split_transposed": ("value = value.reshape(B, S, M, D)",
+                               "value = value.reshape(B, S, D, M).transpose(0, 1, 3, 2).copy()"),
+    "per_level_reference_ignored": ("return ref if ref.ndim == 3 else ref[:, :, l, :]",
+                                    "return ref if ref.ndim == 3 else ref[:, :, 0, :]"),
+    "output_proj_grad_transposed": ('grads["output_proj.weight"] = g2.T @ core.reshape(-1, core.shape[-1])',
+                                    'grads["output_proj.weight"] = (g2.T @ core.reshape(-1, core.shape[-1])).T'),
+    "query_grad_drops_logits": ('g_log2 @ p["attention_weights.weight"]).reshape(B, Q, C)',
+                                '0 * g_log2 @ p["attention_weights.weight"]).reshape(B, Q, C)'),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MODULE_MUTANTS))
+def test_module_pins_catch_planted_mistake(name):
+    import importlib.util
+    import test_oracle_module_pins as pins
+    src = open(os.path.join(ROOT, "oracle", "module.py")).read()
+    old, new = MODULE_MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    spec = importlib.util.spec_from_loader(f"oracle._mutant_{name}", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__package__ = "oracle"
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    failed = []
+    for check in pins.CHECKS:
+        try:
+            check(mod)
+        except (AssertionError, ValueError):
+            failed.append(check.__name__)
+    assert failed, f"module pins did not catch mutant {name}"
