@@ -264,6 +264,50 @@ int msda_backward_ex(int value_dtype, int param_dtype, int64_t batch, int64_t nu
                      size_t workspace_bytes, void *stream);
 
 /*
+ * Sampling-parameter preparation: the steps between a deformable-attention
+ * module's linear layers and the core (msda-triton README, section "The
+ * operator": sampling points are the query's reference point mapped to each
+ * level plus learned offsets, weights are softmax-normalised; section
+ * "Quickstart": the softmax runs over the flattened L*K points of each
+ * (b, q, m)). With normalised (x, y) reference points and offsets in pixels of
+ * each level:
+ *   sampling_locations[b,q,m,l,k,:] = ref + (off_x / W_l, off_y / H_l)
+ *   attention_weights[b,q,m,:]      = softmax(attention_logits[b,q,m,:])
+ * Layouts (dense, row-major, device, all in `dtype`):
+ *   reference_points  (B, Q, 2), or (B, Q, L, 2) with ref_per_level = 1
+ *   sampling_offsets  (B, Q, M, L, K, 2)    pixels of level l
+ *   attention_logits  (B, Q, M, L*K)
+ *   outputs as msda_forward's sampling_locations / attention_weights.
+ * Computed in fp32, rounded once at the store. spatial_shapes is the host
+ * (L, 2) table of msda_forward; only the shapes matter here. B == 0 or Q == 0:
+ * MSDA_OK, nothing launched. Rows whose logits are all -inf give NaN weights,
+ * as a softmax does.
+ */
+int msda_sampling_prep(int dtype, int64_t batch, int64_t num_queries, int64_t num_heads,
+                       int64_t num_levels, int64_t num_points, const int64_t *spatial_shapes,
+                       int ref_per_level, const void *reference_points,
+                       const void *sampling_offsets, const void *attention_logits,
+                       void *sampling_locations, void *attention_weights, void *stream);
+
+/*
+ * Backward of msda_sampling_prep, given the core's gradients with respect to
+ * its locations and weights and the weights msda_sampling_prep produced:
+ *   grad_sampling_offsets = grad_sampling_locations / (W_l, H_l)
+ *   grad_attention_logits[j] = A_j * (g_j - sum_i A_i g_i) over the L*K points
+ *   grad_reference_points = sum over heads and points (and levels, unless
+ *                           ref_per_level) of grad_sampling_locations
+ * grad_reference_points may be NULL (not computed). Every element of the
+ * non-NULL outputs is written; deterministic (fixed summation order).
+ */
+int msda_sampling_prep_backward(int dtype, int64_t batch, int64_t num_queries, int64_t num_heads,
+                                int64_t num_levels, int64_t num_points,
+                                const int64_t *spatial_shapes, int ref_per_level,
+                                const void *attention_weights, const void *grad_sampling_locations,
+                                const void *grad_attention_weights, void *grad_reference_points,
+                                void *grad_sampling_offsets, void *grad_attention_logits,
+                                void *stream);
+
+/*
  * Instrumentation for profilers and benchmarks: the next msda_forward or
  * msda_backward call made by this thread records events[2i] (hipEvent_t
  * passed as void*) on its stream right before its i-th kernel launch and

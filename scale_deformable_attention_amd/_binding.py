@@ -43,7 +43,8 @@ EXPORTED_SYMBOLS = ("msda_forward", "msda_forward_ex", "msda_forward_point_paral
                     "msda_backward_resolve_accum", "msda_backward_plan", "msda_status_string",
                     "msda_last_error",
                     "msda_abi_version", "msda_set_launch_events", "msda_launch_events_recorded",
-                    "msda_launch_events_name")
+                    "msda_launch_events_name", "msda_sampling_prep",
+                    "msda_sampling_prep_backward")
 
 _lib = None
 
@@ -82,6 +83,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msda_backward_resolve_accum.restype = i32
     lib.msda_backward_plan.argtypes = prob + [i32, ctypes.POINTER(ctypes.c_int)]
     lib.msda_backward_plan.restype = i64
+    prep = [i32, i64, i64, i64, i64, i64, vp, i32]
+    lib.msda_sampling_prep.argtypes = prep + [vp, vp, vp, vp, vp, vp]
+    lib.msda_sampling_prep.restype = i32
+    lib.msda_sampling_prep_backward.argtypes = prep + [vp, vp, vp, vp, vp, vp, vp]
+    lib.msda_sampling_prep_backward.restype = i32
     lib.msda_status_string.argtypes = [i32]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_last_error.argtypes = []
@@ -423,3 +429,80 @@ class PreparedCall:
         _check(self.lib.msda_backward_ex(*self._bwd_head, code, fl, ws[0], ws[1],
                                       _stream(self.device, self._stream_arg)))
         return self.grad_value, self.grad_loc, self.grad_attn
+
+
+# ------------------------------------------------ sampling-parameter prep
+
+def _prep_dims(reference_points: torch.Tensor, sampling_offsets: torch.Tensor, L: int):
+    if sampling_offsets.dim() != 6 or sampling_offsets.shape[3] != L or \
+            sampling_offsets.shape[5] != 2:
+        raise ValueError(f"sampling_offsets must be (B, Q, M, {L}, K, 2), "
+                         f"got {tuple(sampling_offsets.shape)}")
+    B, Q, M, _, K, _ = sampling_offsets.shape
+    if tuple(reference_points.shape) == (B, Q, 2):
+        per_level = 0
+    elif tuple(reference_points.shape) == (B, Q, L, 2):
+        per_level = 1
+    else:
+        raise ValueError(f"reference_points must be ({B}, {Q}, 2) or ({B}, {Q}, {L}, 2), "
+                         f"got {tuple(reference_points.shape)}")
+    return B, Q, M, K, per_level
+
+
+def msda_sampling_prep(reference_points: torch.Tensor, sampling_offsets: torch.Tensor,
+                       attention_logits: torch.Tensor, spatial_shapes, stream=None):
+    """(sampling_locations (B,Q,M,L,K,2), attention_weights (B,Q,M,L,K)) from
+    normalised reference points (B,Q,2) or (B,Q,L,2), offsets in pixels of
+    each level (B,Q,M,L,K,2) and logits (B,Q,M,L*K) or (B,Q,M,L,K): location =
+    reference + offset / (W_l, H_l), weights = softmax over the L*K points."""
+    lib = load_library()
+    levels = _Levels(spatial_shapes, None)
+    B, Q, M, K, per_level = _prep_dims(reference_points, sampling_offsets, levels.L)
+    L = levels.L
+    if attention_logits.numel() != B * Q * M * L * K or attention_logits.shape[:3] != (B, Q, M):
+        raise ValueError(f"attention_logits must be ({B}, {Q}, {M}, {L * K}), "
+                         f"got {tuple(attention_logits.shape)}")
+    code = _dtype_code(reference_points, sampling_offsets, attention_logits)
+    ref = reference_points.contiguous()
+    off = sampling_offsets.contiguous()
+    logits = attention_logits.contiguous()
+    loc = torch.empty_like(off)
+    attn = torch.empty((B, Q, M, L, K), dtype=off.dtype, device=off.device)
+    _check(lib.msda_sampling_prep(code, B, Q, M, L, K, levels.ptrs()[0], per_level, _ptr(ref),
+                                  _ptr(off), _ptr(logits), _ptr(loc), _ptr(attn),
+                                  _stream(off.device, stream)))
+    return loc, attn
+
+
+def msda_sampling_prep_backward(attention_weights: torch.Tensor,
+                                grad_sampling_locations: torch.Tensor,
+                                grad_attention_weights: torch.Tensor, spatial_shapes,
+                                ref_per_level: bool = False, need_reference_grad: bool = True,
+                                stream=None):
+    """(grad_reference_points or None, grad_sampling_offsets (B,Q,M,L,K,2),
+    grad_attention_logits (B,Q,M,L*K)) of msda_sampling_prep."""
+    lib = load_library()
+    levels = _Levels(spatial_shapes, None)
+    L = levels.L
+    code = _dtype_code(attention_weights, grad_sampling_locations, grad_attention_weights)
+    gl = grad_sampling_locations.contiguous()
+    if gl.dim() != 6 or gl.shape[3] != L or gl.shape[5] != 2:
+        raise ValueError(f"grad_sampling_locations must be (B, Q, M, {L}, K, 2), "
+                         f"got {tuple(gl.shape)}")
+    B, Q, M, _, K, _ = gl.shape
+    a = attention_weights.contiguous()
+    ga = grad_attention_weights.contiguous()
+    for name, t in (("attention_weights", a), ("grad_attention_weights", ga)):
+        if tuple(t.shape) != (B, Q, M, L, K):
+            raise ValueError(f"{name} must be {(B, Q, M, L, K)}, got {tuple(t.shape)}")
+    g_off = torch.empty_like(gl)
+    g_logits = torch.empty((B, Q, M, L * K), dtype=gl.dtype, device=gl.device)
+    g_ref = None
+    if need_reference_grad:
+        shape = (B, Q, L, 2) if ref_per_level else (B, Q, 2)
+        g_ref = torch.empty(shape, dtype=gl.dtype, device=gl.device)
+    _check(lib.msda_sampling_prep_backward(code, B, Q, M, L, K, levels.ptrs()[0],
+                                           1 if ref_per_level else 0, _ptr(a), _ptr(gl), _ptr(ga),
+                                           _ptr(g_ref), _ptr(g_off), _ptr(g_logits),
+                                           _stream(gl.device, stream)))
+    return g_ref, g_off, g_logits

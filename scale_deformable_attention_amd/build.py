@@ -18,7 +18,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libmsda_amd.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = [os.path.join(HERE, "csrc", "msda_kernels.hip"), os.path.join(HERE, "csrc", "msda_api.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", "msda_kernels.hip"),
+           os.path.join(HERE, "csrc", "msda_prep_kernels.hip"),
+           os.path.join(HERE, "csrc", "msda_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "--offload-arch=gfx950",

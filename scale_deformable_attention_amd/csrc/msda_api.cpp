@@ -897,4 +897,109 @@ int msda_backward_ex(int value_dtype, int param_dtype, int64_t batch, int64_t nu
                          workspace_bytes, stream);
 }
 
+// ------------------------------------------------ sampling-parameter prep
+
+static int make_prep(int dtype, int64_t B, int64_t Q, int64_t M, int64_t L, int64_t K,
+                     const int64_t *shapes, int ref_per_level, msda::PrepProblem *p) {
+    if (dtype != MSDA_F32 && dtype != MSDA_F16 && dtype != MSDA_BF16)
+        return fail(MSDA_ERR_DTYPE, "unknown dtype %d (0=f32, 1=f16, 2=bf16)", dtype);
+    if (B < 0 || Q < 0) return fail(MSDA_ERR_SHAPE, "batch (%lld) and num_queries (%lld) must be >= 0",
+                                    (long long)B, (long long)Q);
+    if (M < 1 || K < 1 || L < 1)
+        return fail(MSDA_ERR_SHAPE, "num_heads (%lld), num_levels (%lld), num_points (%lld) must be >= 1",
+                    (long long)M, (long long)L, (long long)K);
+    if (L > MSDA_MAX_LEVELS)
+        return fail(MSDA_ERR_UNSUPPORTED, "num_levels %lld exceeds the limit of %d", (long long)L,
+                    MSDA_MAX_LEVELS);
+    if (K >= ((int64_t)1 << 26)) return fail(MSDA_ERR_UNSUPPORTED, "num_points %lld too large", (long long)K);
+    if (ref_per_level != 0 && ref_per_level != 1)
+        return fail(MSDA_ERR_SHAPE, "ref_per_level must be 0 or 1, got %d", ref_per_level);
+    if (!shapes) return fail(MSDA_ERR_NULL_ARG, "spatial_shapes is NULL");
+    int64_t rows = 0, pts = 0;
+    // rows * 64 lanes and 2 * rows * L * K elements must fit the launch and int64 indexing
+    if (!mul_ok(B, Q, &rows) || !mul_ok(rows, M, &rows) || !mul_ok(rows, L * K * 2, &pts) ||
+        rows >= ((int64_t)1 << 36))
+        return fail(MSDA_ERR_SHAPE, "sampling tensor B*Q*M*L*K overflows");
+    p->dtype = dtype;
+    p->B = B;
+    p->Q = Q;
+    p->M = M;
+    p->L = L;
+    p->K = K;
+    p->ref_levels = ref_per_level ? (int)L : 1;
+    for (int l = 0; l < MSDA_MAX_LEVELS; ++l) p->H[l] = p->W[l] = 1.0f;
+    for (int64_t l = 0; l < L; ++l) {
+        const int64_t H = shapes[2 * l], W = shapes[2 * l + 1];
+        if (H < 1 || W < 1)
+            return fail(MSDA_ERR_LEVELS, "level %lld has shape (%lld, %lld); both must be >= 1",
+                        (long long)l, (long long)H, (long long)W);
+        if (H >= ((int64_t)1 << 24) || W >= ((int64_t)1 << 24))
+            return fail(MSDA_ERR_UNSUPPORTED, "level %lld shape (%lld, %lld) exceeds 2^24",
+                        (long long)l, (long long)H, (long long)W);
+        p->H[l] = (float)H;
+        p->W[l] = (float)W;
+    }
+    return ok();
+}
+
+int msda_sampling_prep(int dtype, int64_t batch, int64_t num_queries, int64_t num_heads,
+                       int64_t num_levels, int64_t num_points, const int64_t *spatial_shapes,
+                       int ref_per_level, const void *reference_points,
+                       const void *sampling_offsets, const void *attention_logits,
+                       void *sampling_locations, void *attention_weights, void *stream) {
+    LaunchEventsScope events_scope;
+    msda::PrepProblem p;
+    int st = make_prep(dtype, batch, num_queries, num_heads, num_levels, num_points, spatial_shapes,
+                       ref_per_level, &p);
+    if (st) return st;
+    if (p.B == 0 || p.Q == 0) return ok();
+    if ((st = check_ptr(reference_points, "reference_points", dtype))) return st;
+    if ((st = check_ptr(sampling_offsets, "sampling_offsets", dtype))) return st;
+    if ((st = check_ptr(attention_logits, "attention_logits", dtype))) return st;
+    if ((st = check_ptr(sampling_locations, "sampling_locations", dtype))) return st;
+    if ((st = check_ptr(attention_weights, "attention_weights", dtype))) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = marked(msda::launch_sampling_prep(p, reference_points, sampling_offsets,
+                                                             attention_logits, sampling_locations,
+                                                             attention_weights, before(s)),
+                                  s, "sampling_prep_kernel");
+    if (err != hipSuccess) return hip_fail(err, "sampling prep launch");
+    return ok();
+}
+
+int msda_sampling_prep_backward(int dtype, int64_t batch, int64_t num_queries, int64_t num_heads,
+                                int64_t num_levels, int64_t num_points,
+                                const int64_t *spatial_shapes, int ref_per_level,
+                                const void *attention_weights, const void *grad_sampling_locations,
+                                const void *grad_attention_weights, void *grad_reference_points,
+                                void *grad_sampling_offsets, void *grad_attention_logits,
+                                void *stream) {
+    LaunchEventsScope events_scope;
+    msda::PrepProblem p;
+    int st = make_prep(dtype, batch, num_queries, num_heads, num_levels, num_points, spatial_shapes,
+                       ref_per_level, &p);
+    if (st) return st;
+    if (p.B == 0 || p.Q == 0) return ok();
+    if ((st = check_ptr(attention_weights, "attention_weights", dtype))) return st;
+    if ((st = check_ptr(grad_sampling_locations, "grad_sampling_locations", dtype))) return st;
+    if ((st = check_ptr(grad_attention_weights, "grad_attention_weights", dtype))) return st;
+    if ((st = check_ptr(grad_sampling_offsets, "grad_sampling_offsets", dtype))) return st;
+    if ((st = check_ptr(grad_attention_logits, "grad_attention_logits", dtype))) return st;
+    if (grad_reference_points &&
+        (st = check_ptr(grad_reference_points, "grad_reference_points", dtype)))
+        return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err = marked(msda::launch_sampling_prep_backward(
+                                p, attention_weights, grad_sampling_locations,
+                                grad_attention_weights, grad_sampling_offsets,
+                                grad_attention_logits, before(s)),
+                            s, "sampling_prep_bwd_kernel");
+    if (err == hipSuccess && grad_reference_points)
+        err = marked(msda::launch_reference_grad(p, grad_sampling_locations, grad_reference_points,
+                                                 before(s)),
+                     s, "reference_grad_kernel");
+    if (err != hipSuccess) return hip_fail(err, "sampling prep backward launch");
+    return ok();
+}
+
 }  // extern "C"

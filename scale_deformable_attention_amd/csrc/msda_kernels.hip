@@ -31,40 +31,11 @@
 
 #include <type_traits>
 
+#include "msda_device.h"
 #include "msda_launch.h"
 
 namespace msda {
 namespace {
-
-constexpr int kBlock = 256;
-constexpr int kXcds = 8;
-
-// ------------------------------------------------------------ element types
-
-struct F32T {
-    using S = float;
-};
-struct F16T {
-    using S = uint16_t;
-};
-struct BF16T {
-    using S = uint16_t;
-};
-
-__device__ __forceinline__ float to_f32(F32T, float v) { return v; }
-__device__ __forceinline__ float to_f32(F16T, uint16_t v) {
-    return (float)__builtin_bit_cast(_Float16, v);
-}
-__device__ __forceinline__ float to_f32(BF16T, uint16_t v) {
-    return __uint_as_float((uint32_t)v << 16);
-}
-__device__ __forceinline__ float from_f32(F32T, float v) { return v; }
-__device__ __forceinline__ uint16_t from_f32(F16T, float v) {
-    return __builtin_bit_cast(uint16_t, (_Float16)v);
-}
-__device__ __forceinline__ uint16_t from_f32(BF16T, float v) {
-    return __builtin_bit_cast(uint16_t, (__bf16)v);
-}
 
 struct alignas(4) U32x3 {
     uint32_t x, y, z;

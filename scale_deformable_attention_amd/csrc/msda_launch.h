@@ -113,6 +113,28 @@ hipError_t launch_forward_foil(const Problem &p, int vec, const void *value, con
                                const void *attn, void *out, hipStream_t stream);
 
 // Fill `bytes` bytes (a multiple of 2) at `dst` with zeros.
+// Sampling-parameter preparation around the core (msda_prep_kernels.hip):
+// locations = reference + offset / (W_l, H_l), weights = softmax over the
+// L*K points of each (b, q, m), and the matching backward. `dtype` is the
+// storage type of every tensor of these calls; `ref_levels` is 1 for one
+// reference point per query, L for one per (query, level).
+struct PrepProblem {
+    int dtype;
+    int64_t B, Q, M, L, K;
+    int ref_levels;
+    float H[MSDA_MAX_LEVELS];
+    float W[MSDA_MAX_LEVELS];
+};
+
+hipError_t launch_sampling_prep(const PrepProblem &p, const void *ref, const void *offsets,
+                                const void *logits, void *loc, void *attn, hipStream_t stream);
+hipError_t launch_sampling_prep_backward(const PrepProblem &p, const void *attn,
+                                         const void *grad_loc, const void *grad_attn,
+                                         void *grad_offsets, void *grad_logits,
+                                         hipStream_t stream);
+hipError_t launch_reference_grad(const PrepProblem &p, const void *grad_loc, void *grad_ref,
+                                 hipStream_t stream);
+
 hipError_t launch_zero(void *dst, size_t bytes, hipStream_t stream);
 
 // For every level with scratch_off >= 0 and every batch:

@@ -236,3 +236,61 @@ def test_python_binding_rejects_bad_tensors_on_cpu():
         msda_forward(v, [[8, 10], [4, 5]], None, loc.double(), a)
     with pytest.raises(ValueError):
         msda_forward(v, [[8, 10], [4, 5], [2, 2]], None, loc, a)
+
+
+def prep(lib, dtype=0, B=1, Q=16, M=2, L=2, K=2, shapes=SHAPES, per_level=0, ref=FAKE, off=FAKE,
+         logits=FAKE, loc=FAKE, attn=FAKE):
+    return lib.msda_sampling_prep(dtype, B, Q, M, L, K, shapes, per_level, ref, off, logits, loc,
+                                  attn, None)
+
+
+def prep_bwd(lib, dtype=0, B=1, Q=16, M=2, L=2, K=2, shapes=SHAPES, per_level=0, attn=FAKE,
+             gl=FAKE, ga=FAKE, gref=FAKE, goff=FAKE, glog=FAKE):
+    return lib.msda_sampling_prep_backward(dtype, B, Q, M, L, K, shapes, per_level, attn, gl, ga,
+                                           gref, goff, glog, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"dtype": 3}, 4), ({"B": -1}, 2), ({"M": 0}, 2), ({"L": 0}, 2), ({"K": 0}, 2),
+    ({"L": 17}, 8), ({"per_level": 2}, 2), ({"shapes": None}, 1),
+    ({"shapes": (ctypes.c_int64 * 4)(8, 0, 4, 5)}, 3),
+    ({"shapes": (ctypes.c_int64 * 4)(8, 1 << 24, 4, 5)}, 8),
+    ({"ref": None}, 1), ({"logits": None}, 1), ({"attn": None}, 1),
+    ({"off": ctypes.c_void_p(0x10002)}, 5), ({"dtype": 1, "loc": ctypes.c_void_p(0x10001)}, 5),
+    ({"B": 1 << 40, "Q": 1 << 30}, 2),
+])
+def test_sampling_prep_rejects(lib, kw, status):
+    assert prep(lib, **kw) == status, lib.msda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"dtype": 7}, 4), ({"Q": -2}, 2), ({"attn": None}, 1), ({"gl": None}, 1), ({"ga": None}, 1),
+    ({"goff": None}, 1), ({"glog": None}, 1), ({"gref": ctypes.c_void_p(0x10002)}, 5),
+    ({"per_level": -1}, 2),
+])
+def test_sampling_prep_backward_rejects(lib, kw, status):
+    assert prep_bwd(lib, **kw) == status, lib.msda_last_error().decode()
+
+
+def test_sampling_prep_empty_is_ok_without_launch(lib):
+    assert prep(lib, B=0) == 0
+    assert prep(lib, Q=0, ref=None, off=None, logits=None, loc=None, attn=None) == 0
+    assert prep_bwd(lib, B=0, gref=None) == 0
+
+
+def test_python_prep_binding_rejects_bad_tensors_on_cpu():
+    import torch
+    from scale_deformable_attention_amd import msda_sampling_prep
+    ref = torch.zeros(1, 16, 2)
+    off = torch.zeros(1, 16, 2, 2, 2, 2)
+    logits = torch.zeros(1, 16, 2, 4)
+    with pytest.raises(ValueError, match="GPU"):
+        msda_sampling_prep(ref, off, logits, [[8, 10], [4, 5]])
+    with pytest.raises(ValueError, match="reference_points"):
+        msda_sampling_prep(torch.zeros(1, 16, 3), off, logits, [[8, 10], [4, 5]])
+    with pytest.raises(ValueError, match="sampling_offsets"):
+        msda_sampling_prep(ref, off, logits, [[8, 10], [4, 5], [2, 2]])
+    with pytest.raises(ValueError, match="attention_logits"):
+        msda_sampling_prep(ref, off, torch.zeros(1, 16, 2, 5), [[8, 10], [4, 5]])
+    with pytest.raises(TypeError):
+        msda_sampling_prep(ref.double(), off, logits, [[8, 10], [4, 5]])
