@@ -35,6 +35,8 @@ C = in-bounds corners, N = B*S*M*D grad_value elements):
   scatter          3*(P-P')*pe + B*Q*M*D*e + 2*U'*D*e_acc (atomics of the unbinned levels)
   binned levels only (P', C', N' = their points, corners, grad_value elements):
   bin count        2*P'*pe;  bin place  3*P'*pe + 8*C' (records written)
+  bin local sort   3*P'*pe + 8*C' + 8*nbins (count and place in one launch,
+                   bin ranges written) + N*e when it also zero-fills grad_value
   bin accumulate   8*C' + B*Q*M*D*e + N'*e
   zero fill        bytes written;  scratch add  rows * D * (4 + 2e)
 """
@@ -370,6 +372,7 @@ def main():
     P_bin = B * Q * M * Kp * len(bin_levels)
     common = 3 * P * pe + B * Q * M * D * e + U * D * e + 3 * P * pe
     e_acc = 4 if wl.dtype == torch.float32 else e
+    zero_fused = int("bin_local_sort" in ktimes and "zero_fill" not in ktimes)
     kbytes = {"msda_fwd_kernel": 3 * P * pe + B * Q * M * D * e + U * D * e,
               "zero_fill": N * e, "scratch_zero": scratch_rows * D * 4,
               "scratch_add_kernel": scratch_rows * D * (4 + 2 * e),
@@ -380,6 +383,7 @@ def main():
               + 2 * (U - U_bin) * D * e_acc,
               "bin_zero": (nb + 1) * 4, "bin_count": 2 * P_bin * pe, "bin_scan": 3 * nb * 4,
               "bin_place": 3 * P_bin * pe + 8 * C_bin,
+              "bin_local_sort": 3 * P_bin * pe + 8 * C_bin + 8 * nb + zero_fused * N * e,
               "bin_accum_kernel": 8 * C_bin + B * Q * M * D * e + bin_rows * D * e}
     kernels = {k: {"us": round(v, 3), "bytes": int(kbytes[k]),
                    "GBps": round(kbytes[k] / (v * 1e-6) / 1e9, 1)} for k, v in ktimes.items()}

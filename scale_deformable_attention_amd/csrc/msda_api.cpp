@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "msda_launch.h"
@@ -339,6 +340,8 @@ constexpr double kBinRecords = 1024.0;
 struct BinPlan {
     int64_t nbins = 0, records = 0;
     size_t starts_off = 0, cursor_off = 0, records_off = 0, bytes = 0;
+    int max_level_bins = 0;    // bins of the binned level with the most
+    bool local_sort = false;   // one-launch count / scan / place applies
 };
 
 // Bins the levels selected by `contended_only` (all levels, or those above
@@ -369,7 +372,9 @@ bool plan_bins(msda::Problem *p, BinPlan *bp, bool contended_only) {
                ((int64_t)1 << sh) < HW)
             ++sh;
         p->levels.bin_shift[l] = sh;
-        nbbm += (HW + (1 << sh) - 1) >> sh;
+        const int64_t nbl = (HW + (1 << sh) - 1) >> sh;
+        nbbm += nbl;
+        if (nbl > bp->max_level_bins) bp->max_level_bins = (int)std::min<int64_t>(nbl, INT32_MAX);
         p->levels.blevel[nlev++] = l;
         p->levels.nblev = nlev;
         if (nbbm >= ((int64_t)1 << 31)) return false;
@@ -379,6 +384,10 @@ bool plan_bins(msda::Problem *p, BinPlan *bp, bool contended_only) {
     p->nbbm = nbbm;
     bp->nbins = nbins;
     bp->records = 4 * p->B * p->Q * p->M * p->K * nlev;
+    // one workgroup per (b, m, binned level) can sort the level's records in
+    // LDS with 16-bit counters
+    bp->local_sort = p->Q * p->K <= msda::local_sort_max_points() &&
+                     bp->max_level_bins <= msda::kMaxLocalSortBins;
     bp->starts_off = 0;
     bp->cursor_off = align_up((size_t)(nbins + 1) * 4, 256);
     bp->records_off = bp->cursor_off + align_up((size_t)nbins * 4, 256);
@@ -747,45 +756,61 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
         bins.cursor = reinterpret_cast<uint32_t *>(ws + bp.cursor_off);
         bins.records = reinterpret_cast<uint2 *>(ws + bp.records_off);
         bins.nbins = bp.nbins;
+        bins.ends = bp.local_sort ? bins.cursor : bins.starts + 1;
         // The binned chain (t) overlaps the zero fill and the gradient /
         // scatter kernels (s); it forks after the caller's earlier work on s
         // and is joined back on every path below. The fork and join cost
         // about 20 us per call on MI355X (measured with graph replays), more
         // than the overlap gains below ~2^19 records (the decoder workload's
         // 3 * 10^5 lose 20 us; the odd-head workload's 9 * 10^5 gain 24 us).
-        SideStream *side = bp.records >= ((int64_t)1 << 19) ? side_stream(s) : nullptr;
+        // (the one-launch local sort serves small problems and runs on s)
+        SideStream *side =
+            !bp.local_sort && bp.records >= ((int64_t)1 << 19) ? side_stream(s) : nullptr;
+        // the local sort's launch also zero-fills grad_value when it can
+        const bool fused_zero = bp.local_sort && zero_gv && aligned(grad_value, 16) &&
+                                gv_bytes % 16 == 0;
         const hipStream_t t = side ? side->stream : s;
         if (side && ((err = hipEventRecord(side->fork, s)) != hipSuccess ||
                      (err = hipStreamWaitEvent(t, side->fork, 0)) != hipSuccess))
             return hip_fail(err, "side stream fork");
         const char *what = nullptr;
         do {
-            // the counts (starts[0:nbins]) start at zero; the fill works in
-            // 2-byte units, so round the byte count up to an even number of them
-            if ((err = marked(msda::launch_zero(bins.starts, align_up((size_t)(bp.nbins + 1) * 4, 16),
+            if (bp.local_sort) {
+                if ((err = marked(msda::launch_bin_local_sort(
+                                      p, sampling_locations, attention_weights, bins,
+                                      bp.max_level_bins, fused_zero ? grad_value : nullptr,
+                                      fused_zero ? gv_bytes : 0, before(t)),
+                                  t, "bin_local_sort")) != hipSuccess) {
+                    what = "bin local sort launch";
+                    break;
+                }
+            } else if ((err = marked(msda::launch_zero(bins.starts, align_up((size_t)(bp.nbins + 1) * 4, 16),
                                                 before(t)),
                               t, "bin_zero")) != hipSuccess) {
+                // (the counts start at zero; the fill works in 2-byte units,
+                // so the byte count is rounded up to an even number of them)
                 what = "bin count zero fill";
                 break;
-            }
-            if ((err = marked(msda::launch_bin_sort(p, sampling_locations, attention_weights, bins,
-                                                    false, before(t)),
-                              t, "bin_count")) != hipSuccess) {
+            } else if ((err = marked(msda::launch_bin_sort(p, sampling_locations,
+                                                           attention_weights, bins, false,
+                                                           before(t)),
+                                     t, "bin_count")) != hipSuccess) {
                 what = "bin count launch";
                 break;
-            }
-            if ((err = marked(msda::launch_bin_scan(bins, before(t)), t, "bin_scan")) != hipSuccess) {
+            } else if ((err = marked(msda::launch_bin_scan(bins, before(t)), t, "bin_scan")) !=
+                       hipSuccess) {
                 what = "bin scan launch";
                 break;
-            }
-            if ((err = marked(msda::launch_bin_sort(p, sampling_locations, attention_weights, bins,
-                                                    true, before(t)),
-                              t, "bin_place")) != hipSuccess) {
+            } else if ((err = marked(msda::launch_bin_sort(p, sampling_locations,
+                                                           attention_weights, bins, true,
+                                                           before(t)),
+                                     t, "bin_place")) != hipSuccess) {
                 what = "bin place launch";
                 break;
             }
-            if (zero_gv && (err = marked(msda::launch_zero(grad_value, gv_bytes, before(s)), s,
-                                         "zero_fill")) != hipSuccess) {
+            if (zero_gv && !fused_zero &&
+                (err = marked(msda::launch_zero(grad_value, gv_bytes, before(s)), s,
+                              "zero_fill")) != hipSuccess) {
                 what = "grad_value zero fill";
                 break;
             }

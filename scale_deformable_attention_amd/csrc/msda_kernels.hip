@@ -29,6 +29,7 @@
 // remapped so that each XCD receives a contiguous range of (batch, head,
 // query-block) tiles, keeping one (b, m) slice of value in one L2.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "msda_device.h"
@@ -1054,6 +1055,135 @@ __global__ __launch_bounds__(kBlock) void bin_sort_kernel(
     }
 }
 
+// One workgroup per (b, m, binned level) does count, scan and place in one
+// launch when the pair has at most kSortBlock * kSortPts points on the level:
+// each thread keeps its points' corners in registers, the level's per-bin
+// counts live in LDS as two 16-bit halves of a word (an LDS integer atomic
+// per corner), a block scan turns them into offsets, the bin's record range
+// [starts, ends) is written, and the cached corners are placed at their
+// bin's LDS cursor. Records of the segment go to its own fixed region of
+// 4 * Q * K records, so no global counter, scan or zero fill is needed.
+// Workgroups past the segments zero-fill grad_value (n16 16-byte stores),
+// which the same launch can do since nothing here reads it.
+constexpr int kSortBlock = 1024;
+constexpr int kSortPts = 2;  // points per thread
+
+template <class DT>
+__global__ __launch_bounds__(kSortBlock) void bin_local_sort_kernel(
+    const typename DT::S *__restrict__ loc, const typename DT::S *__restrict__ attn,
+    const LevelTable lt, uint32_t *__restrict__ starts, uint32_t *__restrict__ ends,
+    uint2 *__restrict__ records, const int64_t Q, const int M, const int L, const int K,
+    const int64_t nbbm, const int64_t nseg, uint4 *__restrict__ zero_dst, const int64_t zero_n16) {
+    constexpr int kWaves = kSortBlock / 64;
+    extern __shared__ uint32_t hist[];  // bin i: half (i & 1) of word i >> 1
+    __shared__ uint32_t wsum[kWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t seg = blockIdx.x;
+    if (seg >= nseg) {
+        const uint4 z = {0u, 0u, 0u, 0u};
+        const int64_t stride = ((int64_t)gridDim.x - nseg) * kSortBlock;
+        for (int64_t i = (seg - nseg) * kSortBlock + tid; i < zero_n16; i += stride) zero_dst[i] = z;
+        return;
+    }
+    const int64_t bm = seg / lt.nblev;
+    const int l = lt.blevel[seg - bm * lt.nblev];
+    const int64_t b = bm / M;
+    const int m = (int)(bm - b * M);
+    const int sh = lt.bin_shift[l];
+    const int W = lt.W[l];
+    const int64_t start = lt.start[l];
+    const int64_t HW = (int64_t)lt.H[l] * W;
+    const int nb = (int)((HW + (1 << sh) - 1) >> sh);
+    const int nw = (nb + 1) >> 1;
+    const int npts = (int)Q * K;
+    const int LK = L * K;
+    const uint32_t rbase = (uint32_t)seg * (uint32_t)(4 * npts);
+    const int64_t gbin0 = bm * nbbm + lt.bin_off[l];
+    for (int w = tid; w < nw; w += kSortBlock) hist[w] = 0u;
+
+    // this thread's points: corner bins (-1: no record), rows in the bin, coefficients
+    int bin[kSortPts][4];
+    uint32_t key[kSortPts][4];
+    float coef[kSortPts][4];
+#pragma unroll
+    for (int r = 0; r < kSortPts; ++r) {
+        const int i = tid + r * kSortBlock;
+        const bool ok = i < npts;
+        const int q = ok ? i / K : 0;
+        const int64_t pt = ((b * Q + q) * M + m) * LK + l * K + (ok ? i - q * K : 0);
+        float x, y;
+        load_xy<DT>(loc + 2 * pt, x, y);
+        const float a = to_f32(DT{}, attn[pt]);
+        const Cell cl = map_cell(x, y, (float)lt.H[l], (float)W, W, start);
+        const bool vc[4] = {ok && cl.v00, ok && cl.v01, ok && cl.v10, ok && cl.v11};
+#pragma unroll
+        for (int cn = 0; cn < 4; ++cn) {
+            const int64_t rel = cl.row00 + ((cn & 2) ? W : 0) + (cn & 1) - start;
+            bin[r][cn] = vc[cn] ? (int)(rel >> sh) : -1;
+            key[r][cn] = ((uint32_t)q << 4) | (uint32_t)(rel & ((1 << sh) - 1));
+            const float wx = (cn & 1) ? cl.fx : 1.0f - cl.fx;
+            const float wy = (cn & 2) ? cl.fy : 1.0f - cl.fy;
+            coef[r][cn] = a * wx * wy;
+        }
+    }
+    __syncthreads();  // hist cleared
+#pragma unroll
+    for (int r = 0; r < kSortPts; ++r)
+#pragma unroll
+        for (int cn = 0; cn < 4; ++cn)
+            if (bin[r][cn] >= 0) atomicAdd(&hist[bin[r][cn] >> 1], 1u << ((bin[r][cn] & 1) << 4));
+    __syncthreads();
+
+    // exclusive scan: thread t owns words [t * per, (t + 1) * per)
+    const int per = (nw + kSortBlock - 1) / kSortBlock;
+    const int w0 = tid * per, w1 = min(nw, w0 + per);
+    uint32_t tot = 0;
+    for (int w = w0; w < w1; ++w) tot += (hist[w] & 0xffffu) + (hist[w] >> 16);
+    uint32_t inc = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t v = lane < kWaves ? wsum[lane] : 0u;
+#pragma unroll
+        for (int off = 1; off < kWaves; off <<= 1) {
+            const uint32_t y = __shfl_up(v, off);
+            if (lane >= off) v += y;
+        }
+        if (lane < kWaves) wsum[lane] = v;
+    }
+    __syncthreads();
+    uint32_t run = inc - tot + (wave > 0 ? wsum[wave - 1] : 0u);
+    for (int w = w0; w < w1; ++w) {
+        const uint32_t v = hist[w];
+        const uint32_t c0 = v & 0xffffu, c1 = v >> 16;
+        const uint32_t o0 = run, o1 = run + c0;
+        run = o1 + c1;
+        hist[w] = o0 | (o1 << 16);  // both <= 4 * Q * K <= 4 * kSortBlock * kSortPts
+        const int64_t g = gbin0 + 2 * w;
+        starts[g] = rbase + o0;
+        ends[g] = rbase + o1;
+        if (2 * w + 1 < nb) {
+            starts[g + 1] = rbase + o1;
+            ends[g + 1] = rbase + o1 + c1;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSortPts; ++r)
+#pragma unroll
+        for (int cn = 0; cn < 4; ++cn) {
+            if (bin[r][cn] < 0) continue;
+            const int hs = (bin[r][cn] & 1) << 4;
+            const uint32_t slot = (atomicAdd(&hist[bin[r][cn] >> 1], 1u << hs) >> hs) & 0xffffu;
+            records[rbase + slot] = make_uint2(key[r][cn], __float_as_uint(coef[r][cn]));
+        }
+}
+
 // One workgroup: counts[0:nb] -> exclusive starts[0:nb+1], cursor = starts.
 // Tiles of 4 * kScanBlock counts, each thread owning 4 consecutive ones; the
 // next tile's loads are issued before the current tile is scanned (wave
@@ -1135,9 +1265,10 @@ constexpr int kAccGroups = kBlock / 16;
 template <class DT, int SLOT, int J, int V>
 __global__ __launch_bounds__(kBlock) void bin_accum_kernel(
     const typename DT::S *__restrict__ grad_out, typename DT::S *__restrict__ grad_value,
-    const uint32_t *__restrict__ starts, const uint2 *__restrict__ records, const LevelTable lt,
-    const int64_t S, const int64_t Q, const int M, const int D, const int L, const int64_t nbbm,
-    const int64_t nbins, const int accumulate) {
+    const uint32_t *__restrict__ starts, const uint32_t *__restrict__ ends,
+    const uint2 *__restrict__ records, const LevelTable lt, const int64_t S, const int64_t Q,
+    const int M, const int D, const int L, const int64_t nbbm, const int64_t nbins,
+    const int accumulate) {
     using E = typename DT::S;
     using R = typename RawVec<SLOT * (int)sizeof(E)>::type;
     constexpr int G = 16;
@@ -1183,7 +1314,7 @@ __global__ __launch_bounds__(kBlock) void bin_accum_kernel(
 #pragma unroll
         for (int v = 0; v < SLOT; ++v) acc[j][v] = 0.0f;
 
-    const uint32_t rb = starts[bin], re = starts[bin + 1];
+    const uint32_t rb = starts[bin], re = ends[bin];
     uint2 next = make_uint2(0u, 0u);
     if (rb < re) next = records[rb + tid < re ? rb + tid : re - 1];  // (an empty bin reads nothing)
     for (uint32_t base = rb; base < re; base += kBlock) {
@@ -1435,7 +1566,7 @@ hipError_t accum_launch_v(const Problem &p, const BwdMapping &mp, const void *gr
     const int64_t per_xcd = (bins.nbins + kXcds - 1) / kXcds;
     hipLaunchKernelGGL((bin_accum_kernel<DT, SLOT, J, V>), dim3((unsigned)(per_xcd * kXcds)),
                        dim3(kBlock), lds, stream, static_cast<const E *>(grad_out),
-                       static_cast<E *>(grad_value), bins.starts, bins.records, p.levels, p.S,
+                       static_cast<E *>(grad_value), bins.starts, bins.ends, bins.records, p.levels, p.S,
                        p.Q, (int)p.M, (int)p.D, (int)p.L, p.nbbm, bins.nbins, (int)accumulate);
     return hipGetLastError();
 }
@@ -1694,6 +1825,32 @@ hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
         default: return hipErrorInvalidValue;
     }
 #undef MSDA_SORT
+    return hipGetLastError();
+}
+
+int local_sort_max_points() { return kSortBlock * kSortPts; }
+
+hipError_t launch_bin_local_sort(const Problem &p, const void *loc, const void *attn,
+                                 const BinnedBuffers &bins, int max_level_bins, void *zero_dst,
+                                 size_t zero_bytes, hipStream_t stream) {
+    const int64_t nseg = p.B * p.M * p.levels.nblev;
+    if (nseg == 0 || p.Q * p.K > kSortBlock * kSortPts) return hipErrorInvalidValue;
+    const size_t lds = (size_t)((max_level_bins + 1) / 2) * 4;
+    const int64_t n16 = (int64_t)(zero_bytes / 16);
+    const int64_t nzero = n16 > 0 ? std::min<int64_t>((n16 + kSortBlock - 1) / kSortBlock, 1024) : 0;
+#define MSDA_LSORT(T)                                                                          \
+    hipLaunchKernelGGL((bin_local_sort_kernel<T>), dim3((unsigned)(nseg + nzero)),             \
+                       dim3(kSortBlock), lds, stream, static_cast<const typename T::S *>(loc),  \
+                       static_cast<const typename T::S *>(attn), p.levels, bins.starts,         \
+                       bins.cursor, bins.records, p.Q, (int)p.M, (int)p.L, (int)p.K, p.nbbm,    \
+                       nseg, static_cast<uint4 *>(zero_dst), n16)
+    switch (p.pdtype) {
+        case MSDA_F32: MSDA_LSORT(F32T); break;
+        case MSDA_F16: MSDA_LSORT(F16T); break;
+        case MSDA_BF16: MSDA_LSORT(BF16T); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef MSDA_LSORT
     return hipGetLastError();
 }
 

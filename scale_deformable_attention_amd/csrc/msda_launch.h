@@ -45,6 +45,7 @@ struct Problem {
 struct BinnedBuffers {
     uint32_t *starts;
     uint32_t *cursor;
+    const uint32_t *ends;  // bin i's records are [starts[i], ends[i])
     uint2 *records;
     int64_t nbins;
 };
@@ -92,6 +93,17 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
 hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
                            const BinnedBuffers &bins, bool place, hipStream_t stream);
 hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream);
+// Count, scan and place in one launch, one workgroup per (b, m, binned level),
+// when Q * K <= local_sort_max_points() and every binned level has at most
+// kMaxLocalSortBins bins: records of segment s at [s * 4QK, (s + 1) * 4QK),
+// bin ranges in [starts[i], cursor[i]) (so bins.ends = bins.cursor). Extra
+// workgroups of the same launch zero-fill zero_bytes (a multiple of 16, at a
+// 16-byte aligned zero_dst) when zero_bytes > 0.
+constexpr int kMaxLocalSortBins = 32000;  // 64000 bytes of LDS counters
+int local_sort_max_points();
+hipError_t launch_bin_local_sort(const Problem &p, const void *loc, const void *attn,
+                                 const BinnedBuffers &bins, int max_level_bins, void *zero_dst,
+                                 size_t zero_bytes, hipStream_t stream);
 // grad_value atomics only, for the levels that are not binned (no value
 // gathers); used with launch_gradients when some levels are binned.
 hipError_t launch_scatter(const Problem &p, const BwdMapping &mp, const void *loc,

@@ -12,6 +12,13 @@ grad_sampling_locations and grad_attention_weights, 5e-2 on grad_value.
 
 Exact parts: a grad_value row no in-bounds corner lands on, and an output
 row none of whose points has an in-bounds corner, must be exactly zero.
+
+Forced packed bf16 atomics (accumulation "native" on bf16 data) round the
+running sum to 8 significant bits on every add; on a level whose pixels take
+more than 4 contributions on average (Q*K*4 / (H*W)) an element whose sum
+nearly cancels can drift past the elementwise bar depending on the order of
+the adds. There grad_value is held to the same 5e-2 normwise (and a cosine
+above 0.998) instead; AUTO never uses bf16 atomics on such levels.
 """
 
 from __future__ import annotations
@@ -84,11 +91,27 @@ def check_forward(dtype, out_gpu, out_ref, touched=None) -> list:
     return stats
 
 
+def contended_levels(spatial_shapes, Q, K, threshold=4.0) -> tuple:
+    """Levels whose pixels receive more than `threshold` contributions on
+    average: Q * K * 4 / (H * W)."""
+    shp = torch.as_tensor(spatial_shapes).tolist()
+    return tuple(l for l, (h, w) in enumerate(shp) if Q * K * 4 / (h * w) > threshold)
+
+
+def native_bf16_levels(dtype, accum, spatial_shapes, Q, K) -> tuple:
+    """Levels checked normwise: contended levels under forced bf16 atomics."""
+    if dtype != torch.bfloat16 or accum not in ("native", False):
+        return ()
+    return contended_levels(spatial_shapes, Q, K)
+
+
 def check_backward(dtype, gpu, ref, spatial_shapes, level_start_index=None,
-                   touched_rows=None, param_dtype=None) -> list:
+                   touched_rows=None, param_dtype=None, normwise_levels=()) -> list:
     """`param_dtype`: dtype of the locations / weights and their gradients
     when it differs from the value dtype (mixed calls); their tolerances follow
-    it, since those gradients are fp32 sums rounded once to it."""
+    it, since those gradients are fp32 sums rounded once to it.
+    `normwise_levels`: levels whose grad_value is held normwise (forced bf16
+    atomics on contended levels, see the module docstring)."""
     gv, gl, ga = (to_np(t) for t in gpu)
     rgv, rgl, rga = ref
     tol = dict(TOL[dtype])
@@ -97,8 +120,17 @@ def check_backward(dtype, gpu, ref, spatial_shapes, level_start_index=None,
             tol[k] = TOL[param_dtype][k]
     stats = [check_slice("grad_attention_weights", ga, rga, tol["grad_attention_weights"])]
     for l, (r0, r1) in enumerate(level_row_ranges(spatial_shapes, level_start_index)):
-        stats.append(check_slice(f"grad_value[level {l}]", gv[:, r0:r1], rgv[:, r0:r1],
-                                 tol["grad_value"]))
+        if l in normwise_levels:
+            got, want = gv[:, r0:r1].ravel(), rgv[:, r0:r1].ravel()
+            nw = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
+            cos = float(np.dot(got, want) / max(np.linalg.norm(got) * np.linalg.norm(want), 1e-300))
+            assert nw <= tol["grad_value"] and cos > 0.998, \
+                f"grad_value[level {l}] (bf16 atomics): normwise {nw:.3e}, cos {cos:.6f}"
+            stats.append({"name": f"grad_value[level {l}] normwise", "n": got.size,
+                          "max_scaled": float("nan"), "normwise": nw})
+        else:
+            stats.append(check_slice(f"grad_value[level {l}]", gv[:, r0:r1], rgv[:, r0:r1],
+                                     tol["grad_value"]))
         stats.append(check_slice(f"grad_sampling_locations[level {l}]", gl[:, :, :, l],
                                  rgl[:, :, :, l], tol["grad_sampling_locations"]))
     if touched_rows is not None:

@@ -16,7 +16,7 @@ import oracle
 from scale_deformable_attention_amd import MSDAError, PreparedCall, msda_backward, msda_forward
 from scale_deformable_attention_amd.workloads import Workload, make_inputs, workload
 
-from _parity import check_backward, check_forward, level_row_ranges, to_np
+from _parity import check_backward, check_forward, level_row_ranges, native_bf16_levels, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -65,7 +65,10 @@ def full_check(inp, dtype, accum="auto", starts=None, ref=None):
     out, grads = gpu_run(inp, accum, starts)
     ref_out, touched, ref_grads, trows = ref if ref is not None else oracle_run(inp, starts)
     stats = check_forward(dtype, out, ref_out, touched)
-    stats += check_backward(dtype, grads, ref_grads, inp["spatial_shapes"], starts, trows)
+    loc = inp["sampling_locations"]
+    stats += check_backward(dtype, grads, ref_grads, inp["spatial_shapes"], starts, trows,
+                            normwise_levels=native_bf16_levels(dtype, accum, inp["spatial_shapes"],
+                                                               loc.shape[1], loc.shape[4]))
     for s in stats:
         if s.get("n"):
             say(f"  {s['name']:34s} max_scaled={s['max_scaled']:.2e} normwise={s['normwise']:.2e}")
