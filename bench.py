@@ -38,6 +38,7 @@ C = in-bounds corners, N = B*S*M*D grad_value elements):
   bin local sort   3*P'*pe + 8*C' + 8*nbins (count and place in one launch,
                    bin ranges written) + N*e when it also zero-fills grad_value
   bin accumulate   8*C' + B*Q*M*D*e + N'*e
+  scatter + accumulate in one launch: the sum of the two
   zero fill        bytes written;  scratch add  rows * D * (4 + 2e)
 """
 
@@ -385,6 +386,7 @@ def main():
               "bin_place": 3 * P_bin * pe + 8 * C_bin,
               "bin_local_sort": 3 * P_bin * pe + 8 * C_bin + 8 * nb + zero_fused * N * e,
               "bin_accum_kernel": 8 * C_bin + B * Q * M * D * e + bin_rows * D * e}
+    kbytes["scatter_accum_kernel"] = kbytes["msda_scatter_kernel"] + kbytes["bin_accum_kernel"]
     kernels = {k: {"us": round(v, 3), "bytes": int(kbytes[k]),
                    "GBps": round(kbytes[k] / (v * 1e-6) / 1e9, 1)} for k, v in ktimes.items()}
     kname = max(ktimes, key=ktimes.get)

@@ -823,6 +823,10 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
             // scatter. fp32 rows of unbinned levels span several 64-byte
             // atomic segments; there the fused kernel, which overlaps those
             // atomics with its gathers, measures faster than two passes.
+            // On one stream, 16-bit data: the scatter and the accumulation
+            // share one launch (they write disjoint rows).
+            const bool fuse_sa = !side && !all_binned && dtype != MSDA_F32 &&
+                                 msda::scatter_accumulate_fits(p, mp, grad_value);
             if (all_binned || dtype != MSDA_F32) {
                 if ((err = marked(msda::launch_gradients(p, gmp, value, sampling_locations,
                                                          attention_weights, grad_output,
@@ -831,6 +835,14 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
                                   s, "msda_grad_kernel")) != hipSuccess) {
                     what = "gradient launch";
                     break;
+                }
+                if (fuse_sa) {
+                    if ((err = marked(msda::launch_scatter_accumulate(
+                                          p, mp, sampling_locations, attention_weights, grad_output,
+                                          grad_value, bins, accumulate, before(s)),
+                                      s, "scatter_accum_kernel")) != hipSuccess)
+                        what = "scatter / accumulate launch";
+                    break;  // done (the accumulation ran too)
                 }
                 if (!all_binned &&
                     (err = marked(msda::launch_scatter(p, mp, sampling_locations, attention_weights,

@@ -871,17 +871,19 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
 // grad_loc / grad_attn come from msda_grad_kernel: no value gathers, no dot
 // products. Same lane mapping as msda_bwd_kernel; a group walks the points of
 // each unbinned level, CH at a time with their parameter loads issued first.
+#define MSDA_SCATTER_PARAMS                                                                   \
+    const typename PT::S *__restrict__ loc, const typename PT::S *__restrict__ attn,          \
+        const typename DT::S *__restrict__ grad_out, void *__restrict__ grad_value,           \
+        float *__restrict__ workspace, const LevelTable &lt, const int64_t S, const int64_t Q, \
+        const int M, const int D, const int L, const int K, const int qblocks,                \
+        const int log2g, const int log2s
+#define MSDA_SCATTER_ARGS loc, attn, grad_out, grad_value, workspace, lt, S, Q, M, D, L, K, qblocks, \
+                          log2g, log2s
+
 template <class DT, class PT, int SLOT, int J>
-__global__ __launch_bounds__(kBlock) void msda_scatter_kernel(
-    const typename PT::S *__restrict__ loc, const typename PT::S *__restrict__ attn,
-    const typename DT::S *__restrict__ grad_out, void *__restrict__ grad_value,
-    float *__restrict__ workspace, const LevelTable lt, const int64_t S, const int64_t Q,
-    const int M, const int D, const int L, const int K, const int qblocks, const int64_t ntiles,
-    const int log2g, const int log2s) {
+__device__ __forceinline__ void scatter_tile(MSDA_SCATTER_PARAMS, const int64_t tile) {
     constexpr int JC = J * SLOT;
     constexpr int CH = 8;
-    const int64_t tile = logical_block();
-    if (tile >= ntiles) return;
     const int64_t bm = tile / qblocks;
     const int qb = (int)(tile - bm * qblocks);
     const int64_t b = bm / M;
@@ -933,6 +935,18 @@ __global__ __launch_bounds__(kBlock) void msda_scatter_kernel(
             }
         }
     }
+}
+
+template <class DT, class PT, int SLOT, int J>
+__global__ __launch_bounds__(kBlock) void msda_scatter_kernel(
+    const typename PT::S *__restrict__ loc, const typename PT::S *__restrict__ attn,
+    const typename DT::S *__restrict__ grad_out, void *__restrict__ grad_value,
+    float *__restrict__ workspace, const LevelTable lt, const int64_t S, const int64_t Q,
+    const int M, const int D, const int L, const int K, const int qblocks, const int64_t ntiles,
+    const int log2g, const int log2s) {
+    const int64_t tile = logical_block();
+    if (tile >= ntiles) return;
+    scatter_tile<DT, PT, SLOT, J>(MSDA_SCATTER_ARGS, tile);
 }
 
 // ------------------------------------------------------ binned grad_value
@@ -1262,24 +1276,25 @@ __global__ __launch_bounds__(kScanBlock) void bin_scan_kernel(uint32_t *__restri
 // grad_value, V channels per access.
 constexpr int kAccGroups = kBlock / 16;
 
+#define MSDA_ACCUM_PARAMS                                                                     \
+    const typename DT::S *__restrict__ grad_out, typename DT::S *__restrict__ grad_value,     \
+        const uint32_t *__restrict__ starts, const uint32_t *__restrict__ ends,               \
+        const uint2 *__restrict__ records, const LevelTable &lt, const int64_t S,             \
+        const int64_t Q, const int M, const int D, const int L, const int64_t nbbm,           \
+        const int accumulate
+#define MSDA_ACCUM_ARGS grad_out, grad_value, starts, ends, records, lt, S, Q, M, D, L, nbbm, accumulate
+
+// `tile`: kAccGroups x D floats of LDS (the kernel's dynamic LDS).
 template <class DT, int SLOT, int J, int V>
-__global__ __launch_bounds__(kBlock) void bin_accum_kernel(
-    const typename DT::S *__restrict__ grad_out, typename DT::S *__restrict__ grad_value,
-    const uint32_t *__restrict__ starts, const uint32_t *__restrict__ ends,
-    const uint2 *__restrict__ records, const LevelTable lt, const int64_t S, const int64_t Q,
-    const int M, const int D, const int L, const int64_t nbbm, const int64_t nbins,
-    const int accumulate) {
+__device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const int64_t bin) {
     using E = typename DT::S;
     using R = typename RawVec<SLOT * (int)sizeof(E)>::type;
     constexpr int G = 16;
     constexpr int U = J == 1 ? 16 : (J == 2 ? 8 : 4);
     constexpr int kWaves = kBlock / 64;
-    extern __shared__ float tile[];  // kAccGroups x D
     __shared__ uint2 sorted[kBlock];
     __shared__ uint32_t wcount[kAccGroups * kWaves];   // [slot][wave]
     __shared__ uint32_t woff[kAccGroups * kWaves + 1];  // exclusive prefix, slot-major
-    const int64_t bin = logical_block();  // neighbouring bins share upstream-gradient rows
-    if (bin >= nbins) return;
     const int64_t bm = bin / nbbm;
     const int lb = (int)(bin - bm * nbbm);
     const int64_t b = bm / M;
@@ -1411,6 +1426,53 @@ __global__ __launch_bounds__(kBlock) void bin_accum_kernel(
             for (int k = 0; k < V; ++k) v[k] += o[k];
         }
         store_vec<DT, V>(d, v);
+    }
+}
+
+template <class DT, int SLOT, int J, int V>
+__global__ __launch_bounds__(kBlock) void bin_accum_kernel(
+    const typename DT::S *__restrict__ grad_out, typename DT::S *__restrict__ grad_value,
+    const uint32_t *__restrict__ starts, const uint32_t *__restrict__ ends,
+    const uint2 *__restrict__ records, const LevelTable lt, const int64_t S, const int64_t Q,
+    const int M, const int D, const int L, const int64_t nbbm, const int64_t nbins,
+    const int accumulate) {
+    extern __shared__ float dyn_tile[];  // kAccGroups x D
+    const int64_t bin = logical_block();  // neighbouring bins share upstream-gradient rows
+    if (bin >= nbins) return;
+    accum_bin<DT, SLOT, J, V>(dyn_tile, MSDA_ACCUM_ARGS, bin);
+}
+
+// The unbinned levels' atomic scatter and the binned levels' accumulation in
+// one launch: they touch disjoint grad_value rows and depend only on work
+// already finished (zero fill, bin sort), so their workgroups share the chip;
+// the accumulation's latency-bound rounds fill the gaps of the scatter's
+// atomic-bound stream. Workgroups [0, nsc) scatter and the rest accumulate,
+// each range with its own XCD-aware order (nsc is a multiple of 8).
+template <class DT, class PT, int SLOT, int J, int V>
+__global__ __launch_bounds__(kBlock) void scatter_accum_kernel(
+    const typename PT::S *__restrict__ loc, const typename PT::S *__restrict__ attn,
+    const typename DT::S *__restrict__ grad_out, void *__restrict__ grad_value,
+    const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D, const int L,
+    const int K, const int qblocks, const int64_t ntiles, const int log2g, const int log2s,
+    const uint32_t nsc, const uint32_t *__restrict__ starts, const uint32_t *__restrict__ ends,
+    const uint2 *__restrict__ records, const int64_t nbbm, const int64_t nbins,
+    const int accumulate) {
+    extern __shared__ float dyn_tile[];
+    const uint32_t bx = blockIdx.x;
+    if (bx < nsc) {
+        const int64_t tile = (int64_t)(bx % kXcds) * (nsc / kXcds) + bx / kXcds;
+        if (tile < ntiles) {
+            float *workspace = nullptr;
+            scatter_tile<DT, PT, SLOT, J>(MSDA_SCATTER_ARGS, tile);
+        }
+    } else {
+        const uint32_t i = bx - nsc;
+        const int64_t bin = (int64_t)(i % kXcds) * ((gridDim.x - nsc) / kXcds) + i / kXcds;
+        if (bin < nbins) {
+            typename DT::S *gv = static_cast<typename DT::S *>(grad_value);
+            accum_bin<DT, SLOT, J, V>(dyn_tile, grad_out, gv, starts, ends, records, lt, S, Q, M,
+                                      D, L, nbbm, accumulate, bin);
+        }
     }
 }
 
@@ -1852,6 +1914,59 @@ hipError_t launch_bin_local_sort(const Problem &p, const void *loc, const void *
     }
 #undef MSDA_LSORT
     return hipGetLastError();
+}
+
+template <class DT, class PT, int J>
+hipError_t scatter_accum_launch(const Problem &p, const BwdMapping &mp, const void *loc,
+                                const void *attn, const void *grad_out, void *grad_value,
+                                const BinnedBuffers &bins, bool accumulate, hipStream_t stream) {
+    using E = typename DT::S;
+    using P = typename PT::S;
+    constexpr int V = 8;  // 16-byte grad_value writes
+    const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
+    const int qblocks = (int)((p.Q + qpb - 1) / qpb);
+    const int64_t ntiles = p.B * p.M * qblocks;
+    const int64_t nsc = (ntiles + kXcds - 1) / kXcds * kXcds;
+    const int64_t nacc = (bins.nbins + kXcds - 1) / kXcds * kXcds;
+    if (nsc + nacc >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const size_t lds = (size_t)kAccGroups * (size_t)p.D * sizeof(float);
+    hipLaunchKernelGGL((scatter_accum_kernel<DT, PT, 2, J, V>), dim3((unsigned)(nsc + nacc)),
+                       dim3(kBlock), lds, stream, static_cast<const P *>(loc),
+                       static_cast<const P *>(attn), static_cast<const E *>(grad_out), grad_value,
+                       p.levels, p.S, p.Q, (int)p.M, (int)p.D, (int)p.L, (int)p.K, qblocks, ntiles,
+                       mp.log2_group, mp.log2_split, (uint32_t)nsc, bins.starts, bins.ends,
+                       bins.records, p.nbbm, bins.nbins, (int)accumulate);
+    return hipGetLastError();
+}
+
+template <class DT, class PT>
+hipError_t scatter_accum_by_j(const Problem &p, const BwdMapping &mp, const void *loc,
+                              const void *attn, const void *grad_out, void *grad_value,
+                              const BinnedBuffers &bins, bool accumulate, hipStream_t stream) {
+    switch (mp.j) {
+        case 1: return scatter_accum_launch<DT, PT, 1>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
+        case 2: return scatter_accum_launch<DT, PT, 2>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
+        case 4: return scatter_accum_launch<DT, PT, 4>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool scatter_accumulate_fits(const Problem &p, const BwdMapping &mp, const void *grad_value) {
+    return p.dtype != MSDA_F32 && mp.slot == 2 && (mp.j == 1 || mp.j == 2 || mp.j == 4) &&
+           p.D % 8 == 0 && reinterpret_cast<uintptr_t>(grad_value) % 16 == 0;
+}
+
+hipError_t launch_scatter_accumulate(const Problem &p, const BwdMapping &mp, const void *loc,
+                                     const void *attn, const void *grad_out, void *grad_value,
+                                     const BinnedBuffers &bins, bool accumulate,
+                                     hipStream_t stream) {
+    if (!scatter_accumulate_fits(p, mp, grad_value)) return hipErrorInvalidValue;
+    const bool f32p = p.pdtype == MSDA_F32;
+    if (p.dtype == MSDA_F16)
+        return f32p ? scatter_accum_by_j<F16T, F32T>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream)
+                    : scatter_accum_by_j<F16T, F16T>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
+    return f32p ? scatter_accum_by_j<BF16T, F32T>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream)
+                : scatter_accum_by_j<BF16T, BF16T>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
 }
 
 hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream) {

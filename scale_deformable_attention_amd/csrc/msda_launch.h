@@ -93,6 +93,13 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
 hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
                            const BinnedBuffers &bins, bool place, hipStream_t stream);
 hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream);
+// launch_scatter and launch_bin_accumulate as one launch (16-bit data, two
+// channels per lane slot, D a multiple of 8, grad_value 16-byte aligned).
+bool scatter_accumulate_fits(const Problem &p, const BwdMapping &mp, const void *grad_value);
+hipError_t launch_scatter_accumulate(const Problem &p, const BwdMapping &mp, const void *loc,
+                                     const void *attn, const void *grad_out, void *grad_value,
+                                     const BinnedBuffers &bins, bool accumulate,
+                                     hipStream_t stream);
 // Count, scan and place in one launch, one workgroup per (b, m, binned level),
 // when Q * K <= local_sort_max_points() and every binned level has at most
 // kMaxLocalSortBins bins: records of segment s at [s * 4QK, (s + 1) * 4QK),
