@@ -38,7 +38,8 @@ C = in-bounds corners, N = B*S*M*D grad_value elements):
   bin local sort   3*P'*pe + 8*C' + 8*nbins (count and place in one launch,
                    bin ranges written) + N*e when it also zero-fills grad_value
   bin accumulate   8*C' + B*Q*M*D*e + N'*e
-  scatter + accumulate in one launch: the sum of the two
+  scatter + accumulate in one launch: the sum of the two; likewise gradients +
+  local sort (+ zero fill) in one launch
   zero fill        bytes written;  scratch add  rows * D * (4 + 2e)
 """
 
@@ -373,7 +374,8 @@ def main():
     P_bin = B * Q * M * Kp * len(bin_levels)
     common = 3 * P * pe + B * Q * M * D * e + U * D * e + 3 * P * pe
     e_acc = 4 if wl.dtype == torch.float32 else e
-    zero_fused = int("bin_local_sort" in ktimes and "zero_fill" not in ktimes)
+    # a zero fill that did not get its own launch ran inside the sort's launch
+    zero_fused = int("zero_fill" not in ktimes and any(m != "binned" for m in level_modes))
     kbytes = {"msda_fwd_kernel": 3 * P * pe + B * Q * M * D * e + U * D * e,
               "zero_fill": N * e, "scratch_zero": scratch_rows * D * 4,
               "scratch_add_kernel": scratch_rows * D * (4 + 2 * e),
@@ -387,6 +389,7 @@ def main():
               "bin_local_sort": 3 * P_bin * pe + 8 * C_bin + 8 * nb + zero_fused * N * e,
               "bin_accum_kernel": 8 * C_bin + B * Q * M * D * e + bin_rows * D * e}
     kbytes["scatter_accum_kernel"] = kbytes["msda_scatter_kernel"] + kbytes["bin_accum_kernel"]
+    kbytes["grad_sort_kernel"] = kbytes["msda_grad_kernel"] + kbytes["bin_local_sort"]
     kernels = {k: {"us": round(v, 3), "bytes": int(kbytes[k]),
                    "GBps": round(kbytes[k] / (v * 1e-6) / 1e9, 1)} for k, v in ktimes.items()}
     kname = max(ktimes, key=ktimes.get)

@@ -773,9 +773,31 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
         if (side && ((err = hipEventRecord(side->fork, s)) != hipSuccess ||
                      (err = hipStreamWaitEvent(t, side->fork, 0)) != hipSuccess))
             return hip_fail(err, "side stream fork");
+        // grad_loc / grad_attn come from msda_grad_kernel (forward lane
+        // mapping) except for fp32 data with unbinned levels: fp32 rows span
+        // several 64-byte atomic segments, and there the fused msda_bwd_kernel,
+        // which overlaps those atomics with its gathers, measures faster.
+        const bool grad_path = all_binned || dtype != MSDA_F32;
+        // Small problems on one stream: the gradients, the local sort and the
+        // zero fill share a launch, then the unbinned levels' scatter and the
+        // accumulation share another (each pair touches disjoint data).
+        const bool fuse_gs = bp.local_sort && !side && grad_path &&
+                             msda::grad_sort_fits(p, gmp, bp.max_level_bins);
+        const bool fuse_sa = !side && !all_binned && dtype != MSDA_F32 &&
+                             msda::scatter_accumulate_fits(p, mp, grad_value);
         const char *what = nullptr;
         do {
-            if (bp.local_sort) {
+            if (fuse_gs) {
+                if ((err = marked(msda::launch_gradients_and_sort(
+                                      p, gmp, value, sampling_locations, attention_weights,
+                                      grad_output, grad_sampling_locations, grad_attention_weights,
+                                      bins, bp.max_level_bins, fused_zero ? grad_value : nullptr,
+                                      fused_zero ? gv_bytes : 0, before(s)),
+                                  s, "grad_sort_kernel")) != hipSuccess) {
+                    what = "gradient / sort launch";
+                    break;
+                }
+            } else if (bp.local_sort) {
                 if ((err = marked(msda::launch_bin_local_sort(
                                       p, sampling_locations, attention_weights, bins,
                                       bp.max_level_bins, fused_zero ? grad_value : nullptr,
@@ -818,17 +840,11 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
                 what = "side stream event";
                 break;
             }
-            // grad_loc / grad_attn in the forward's lane mapping, and the
-            // unbinned levels' grad_value (if any) by a gather-free atomic
-            // scatter. fp32 rows of unbinned levels span several 64-byte
-            // atomic segments; there the fused kernel, which overlaps those
-            // atomics with its gathers, measures faster than two passes.
-            // On one stream, 16-bit data: the scatter and the accumulation
-            // share one launch (they write disjoint rows).
-            const bool fuse_sa = !side && !all_binned && dtype != MSDA_F32 &&
-                                 msda::scatter_accumulate_fits(p, mp, grad_value);
-            if (all_binned || dtype != MSDA_F32) {
-                if ((err = marked(msda::launch_gradients(p, gmp, value, sampling_locations,
+            // the unbinned levels' grad_value (if any) by a gather-free
+            // atomic scatter
+            if (grad_path) {
+                if (!fuse_gs &&
+                    (err = marked(msda::launch_gradients(p, gmp, value, sampling_locations,
                                                          attention_weights, grad_output,
                                                          grad_sampling_locations,
                                                          grad_attention_weights, before(s)),

@@ -483,18 +483,19 @@ __global__ __launch_bounds__(kBlock) void msda_foil_kernel(
 // kernel", section "What the backward pass must produce"); the group's
 // shares are summed with DPP moves and lane c stores point t0 + c of the
 // chunk, so a group writes consecutive points with one instruction.
+#define MSDA_GRAD_PARAMS                                                                      \
+    const typename DT::S *__restrict__ value, const typename PT::S *__restrict__ loc,         \
+        const typename PT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out, \
+        typename PT::S *__restrict__ grad_loc, typename PT::S *__restrict__ grad_attn,        \
+        const LevelTable &lt, const int64_t S, const int64_t Q, const int M, const int D,     \
+        const int L, const int K, const int qblocks, const int log2g, const int log2s
+#define MSDA_GRAD_ARGS value, loc, attn, grad_out, grad_loc, grad_attn, lt, S, Q, M, D, L, K, \
+                       qblocks, log2g, log2s
+
 template <class DT, class PT, int VEC, int CH, bool BUF>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void msda_grad_kernel(
-    const typename DT::S *__restrict__ value, const typename PT::S *__restrict__ loc,
-    const typename PT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out,
-    typename PT::S *__restrict__ grad_loc, typename PT::S *__restrict__ grad_attn,
-    const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
-    const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
-    const int log2s) {
+__device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) {
     using E = typename DT::S;
     using R = typename RawVec<VEC * (int)sizeof(E)>::type;
-    const int64_t tile = logical_block();
-    if (tile >= ntiles) return;  // whole workgroup leaves together
     const int64_t bm = tile / qblocks;
     const int qb = (int)(tile - bm * qblocks);
     const int64_t b = bm / M;
@@ -617,6 +618,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
             }
         }
     }
+}
+
+template <class DT, class PT, int VEC, int CH, bool BUF>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void msda_grad_kernel(
+    const typename DT::S *__restrict__ value, const typename PT::S *__restrict__ loc,
+    const typename PT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out,
+    typename PT::S *__restrict__ grad_loc, typename PT::S *__restrict__ grad_attn,
+    const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
+    const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
+    const int log2s) {
+    const int64_t tile = logical_block();
+    if (tile >= ntiles) return;  // whole workgroup leaves together
+    grad_tile<DT, PT, VEC, CH, BUF>(MSDA_GRAD_ARGS, tile);
 }
 
 // ------------------------------------------------------------ backward
@@ -1082,23 +1096,23 @@ __global__ __launch_bounds__(kBlock) void bin_sort_kernel(
 constexpr int kSortBlock = 1024;
 constexpr int kSortPts = 2;  // points per thread
 
-template <class DT>
-__global__ __launch_bounds__(kSortBlock) void bin_local_sort_kernel(
-    const typename DT::S *__restrict__ loc, const typename DT::S *__restrict__ attn,
-    const LevelTable lt, uint32_t *__restrict__ starts, uint32_t *__restrict__ ends,
-    uint2 *__restrict__ records, const int64_t Q, const int M, const int L, const int K,
-    const int64_t nbbm, const int64_t nseg, uint4 *__restrict__ zero_dst, const int64_t zero_n16) {
+#define MSDA_SORT_PARAMS                                                                      \
+    const typename DT::S *__restrict__ loc, const typename DT::S *__restrict__ attn,          \
+        const LevelTable &lt, uint32_t *__restrict__ starts, uint32_t *__restrict__ ends,     \
+        uint2 *__restrict__ records, const int64_t Q, const int M, const int L, const int K,  \
+        const int64_t nbbm
+#define MSDA_SORT_ARGS loc, attn, lt, starts, ends, records, Q, M, L, K, nbbm
+
+// Workgroups of BLOCK threads, PTS points per thread (Q * K <= BLOCK * PTS);
+// `hist`: the dynamic LDS counters.
+template <class DT, int BLOCK, int PTS>
+__device__ __forceinline__ void local_sort_segment(uint32_t *hist, MSDA_SORT_PARAMS,
+                                                   const int64_t seg) {
+    constexpr int kSortBlock = BLOCK;
+    constexpr int kSortPts = PTS;
     constexpr int kWaves = kSortBlock / 64;
-    extern __shared__ uint32_t hist[];  // bin i: half (i & 1) of word i >> 1
     __shared__ uint32_t wsum[kWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t seg = blockIdx.x;
-    if (seg >= nseg) {
-        const uint4 z = {0u, 0u, 0u, 0u};
-        const int64_t stride = ((int64_t)gridDim.x - nseg) * kSortBlock;
-        for (int64_t i = (seg - nseg) * kSortBlock + tid; i < zero_n16; i += stride) zero_dst[i] = z;
-        return;
-    }
     const int64_t bm = seg / lt.nblev;
     const int l = lt.blevel[seg - bm * lt.nblev];
     const int64_t b = bm / M;
@@ -1196,6 +1210,57 @@ __global__ __launch_bounds__(kSortBlock) void bin_local_sort_kernel(
             const uint32_t slot = (atomicAdd(&hist[bin[r][cn] >> 1], 1u << hs) >> hs) & 0xffffu;
             records[rbase + slot] = make_uint2(key[r][cn], __float_as_uint(coef[r][cn]));
         }
+}
+
+// n16 16-byte zero stores by the workgroups [0, nblocks) of a role
+__device__ __forceinline__ void zero_part(uint4 *__restrict__ dst, const int64_t n16,
+                                          const int64_t block, const int64_t nblocks) {
+    const uint4 z = {0u, 0u, 0u, 0u};
+    const int64_t stride = nblocks * blockDim.x;
+    for (int64_t i = block * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = z;
+}
+
+template <class DT>
+__global__ __launch_bounds__(kSortBlock) void bin_local_sort_kernel(
+    const typename DT::S *__restrict__ loc, const typename DT::S *__restrict__ attn,
+    const LevelTable lt, uint32_t *__restrict__ starts, uint32_t *__restrict__ ends,
+    uint2 *__restrict__ records, const int64_t Q, const int M, const int L, const int K,
+    const int64_t nbbm, const int64_t nseg, uint4 *__restrict__ zero_dst, const int64_t zero_n16) {
+    extern __shared__ uint32_t hist[];  // bin i: half (i & 1) of word i >> 1
+    const int64_t seg = blockIdx.x;
+    if (seg >= nseg) zero_part(zero_dst, zero_n16, seg - nseg, (int64_t)gridDim.x - nseg);
+    else local_sort_segment<DT, kSortBlock, kSortPts>(hist, MSDA_SORT_ARGS, seg);
+}
+
+// The gradients (msda_grad_kernel), the local bin sort and the grad_value zero
+// fill in one launch: none reads what another writes, so the sort's and the
+// fill's short workgroups run beside the gradient tiles. Workgroups
+// [0, ngrad) take gradient tiles (XCD-aware order; ngrad a multiple of 8),
+// [ngrad, ngrad + nseg) sort segments, the rest zero-fill.
+constexpr int kFusedSortPts = 8;  // 256 threads x 8 points: the local sort's 2048 points
+
+template <class DT, class PT, int VEC>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void grad_sort_kernel(
+    const typename DT::S *__restrict__ value, const typename PT::S *__restrict__ loc,
+    const typename PT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out,
+    typename PT::S *__restrict__ grad_loc, typename PT::S *__restrict__ grad_attn,
+    const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
+    const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
+    const int log2s, const uint32_t ngrad, uint32_t *__restrict__ starts,
+    uint32_t *__restrict__ ends, uint2 *__restrict__ records, const int64_t nbbm,
+    const int64_t nseg, uint4 *__restrict__ zero_dst, const int64_t zero_n16) {
+    extern __shared__ uint32_t hist[];
+    const uint32_t bx = blockIdx.x;
+    if (bx < ngrad) {
+        const int64_t tile = (int64_t)(bx % kXcds) * (ngrad / kXcds) + bx / kXcds;
+        if (tile < ntiles) grad_tile<DT, PT, VEC, 4, true>(MSDA_GRAD_ARGS, tile);
+    } else if (bx - ngrad < nseg) {
+        local_sort_segment<PT, kBlock, kFusedSortPts>(hist, loc, attn, lt, starts, ends, records, Q,
+                                                      M, L, K, nbbm, (int64_t)(bx - ngrad));
+    } else {
+        const int64_t first = (int64_t)ngrad + nseg;
+        zero_part(zero_dst, zero_n16, (int64_t)bx - first, (int64_t)gridDim.x - first);
+    }
 }
 
 // One workgroup: counts[0:nb] -> exclusive starts[0:nb+1], cursor = starts.
@@ -1967,6 +2032,67 @@ hipError_t launch_scatter_accumulate(const Problem &p, const BwdMapping &mp, con
                     : scatter_accum_by_j<F16T, F16T>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
     return f32p ? scatter_accum_by_j<BF16T, F32T>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream)
                 : scatter_accum_by_j<BF16T, BF16T>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
+}
+
+template <class DT, class PT, int VEC>
+hipError_t grad_sort_launch(const Problem &p, const Mapping &mp, const void *value, const void *loc,
+                            const void *attn, const void *grad_out, void *grad_loc, void *grad_attn,
+                            const BinnedBuffers &bins, int max_level_bins, void *zero_dst,
+                            size_t zero_bytes, hipStream_t stream) {
+    using E = typename DT::S;
+    using P = typename PT::S;
+    const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
+    const int qblocks = (int)((p.Q + qpb - 1) / qpb);
+    const int64_t ntiles = p.B * p.M * qblocks;
+    const int64_t ngrad = (ntiles + kXcds - 1) / kXcds * kXcds;
+    const int64_t nseg = p.B * p.M * p.levels.nblev;
+    const int64_t n16 = (int64_t)(zero_bytes / 16);
+    const int64_t nzero = n16 > 0 ? std::min<int64_t>((n16 + kBlock - 1) / kBlock, 2048) : 0;
+    if (ngrad + nseg + nzero >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const size_t lds = (size_t)((max_level_bins + 1) / 2) * 4;
+    hipLaunchKernelGGL((grad_sort_kernel<DT, PT, VEC>), dim3((unsigned)(ngrad + nseg + nzero)),
+                       dim3(kBlock), lds, stream, static_cast<const E *>(value),
+                       static_cast<const P *>(loc), static_cast<const P *>(attn),
+                       static_cast<const E *>(grad_out), static_cast<P *>(grad_loc),
+                       static_cast<P *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
+                       (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split,
+                       (uint32_t)ngrad, bins.starts, bins.cursor, bins.records, p.nbbm, nseg,
+                       static_cast<uint4 *>(zero_dst), n16);
+    return hipGetLastError();
+}
+
+template <class DT, class PT>
+hipError_t grad_sort_by_vec(const Problem &p, const Mapping &mp, const void *v, const void *l,
+                            const void *a, const void *go, void *gl, void *ga,
+                            const BinnedBuffers &bins, int mlb, void *zd, size_t zb,
+                            hipStream_t st) {
+    switch (mp.vec) {
+        case 1: return grad_sort_launch<DT, PT, 1>(p, mp, v, l, a, go, gl, ga, bins, mlb, zd, zb, st);
+        case 2: return grad_sort_launch<DT, PT, 2>(p, mp, v, l, a, go, gl, ga, bins, mlb, zd, zb, st);
+        case 4: return grad_sort_launch<DT, PT, 4>(p, mp, v, l, a, go, gl, ga, bins, mlb, zd, zb, st);
+        case 8: return grad_sort_launch<DT, PT, 8>(p, mp, v, l, a, go, gl, ga, bins, mlb, zd, zb, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool grad_sort_fits(const Problem &p, const Mapping &mp, int max_level_bins) {
+    return p.dtype != MSDA_F32 && p.Q * p.K <= kBlock * kFusedSortPts &&
+           max_level_bins <= kMaxFusedSortBins && slice_fits_buffer(p) &&
+           (mp.vec == 1 || mp.vec == 2 || mp.vec == 4 || mp.vec == 8);
+}
+
+hipError_t launch_gradients_and_sort(const Problem &p, const Mapping &mp, const void *value,
+                                     const void *loc, const void *attn, const void *grad_out,
+                                     void *grad_loc, void *grad_attn, const BinnedBuffers &bins,
+                                     int max_level_bins, void *zero_dst, size_t zero_bytes,
+                                     hipStream_t stream) {
+    if (!grad_sort_fits(p, mp, max_level_bins)) return hipErrorInvalidValue;
+    const bool f32p = p.pdtype == MSDA_F32;
+#define MSDA_GS(T, P) grad_sort_by_vec<T, P>(p, mp, value, loc, attn, grad_out, grad_loc, grad_attn, \
+                                             bins, max_level_bins, zero_dst, zero_bytes, stream)
+    if (p.dtype == MSDA_F16) return f32p ? MSDA_GS(F16T, F32T) : MSDA_GS(F16T, F16T);
+    return f32p ? MSDA_GS(BF16T, F32T) : MSDA_GS(BF16T, BF16T);
+#undef MSDA_GS
 }
 
 hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream) {

@@ -93,6 +93,16 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
 hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
                            const BinnedBuffers &bins, bool place, hipStream_t stream);
 hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream);
+// launch_gradients, launch_bin_local_sort and the zero fill as one launch
+// (16-bit data, Q * K <= 2048, every binned level at most kMaxFusedSortBins
+// bins, value slices buffer-addressable).
+constexpr int kMaxFusedSortBins = 4096;  // 8 KB of LDS counters
+bool grad_sort_fits(const Problem &p, const Mapping &mp, int max_level_bins);
+hipError_t launch_gradients_and_sort(const Problem &p, const Mapping &mp, const void *value,
+                                     const void *loc, const void *attn, const void *grad_out,
+                                     void *grad_loc, void *grad_attn, const BinnedBuffers &bins,
+                                     int max_level_bins, void *zero_dst, size_t zero_bytes,
+                                     hipStream_t stream);
 // launch_scatter and launch_bin_accumulate as one launch (16-bit data, two
 // channels per lane slot, D a multiple of 8, grad_value 16-byte aligned).
 bool scatter_accumulate_fits(const Problem &p, const BwdMapping &mp, const void *grad_value);

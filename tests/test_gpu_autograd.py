@@ -259,6 +259,6 @@ def test_instrumented_launch_names():
     set_launch_events(evs)
     call.backward()
     torch.cuda.synchronize()
-    assert launch_event_names() == ["bin_local_sort", "msda_grad_kernel", "scatter_accum_kernel"]
-    for i in range(3):
+    assert launch_event_names() == ["grad_sort_kernel", "scatter_accum_kernel"]
+    for i in range(2):
         assert evs[2 * i].elapsed_time(evs[2 * i + 1]) >= 0.0
