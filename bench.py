@@ -35,6 +35,8 @@ C = in-bounds corners, N = B*S*M*D grad_value elements):
   scatter          3*(P-P')*pe + B*Q*M*D*e + 2*U'*D*e_acc (atomics of the unbinned levels)
   binned levels only (P', C', N' = their points, corners, grad_value elements):
   bin count        2*P'*pe;  bin place  3*P'*pe + 8*C' (records written)
+  bin scan         3*nbins*4 (one workgroup), or tile sums nbins*4, tile offsets
+                   3*ntiles*4, tile scans 3*nbins*4 (large bin counts)
   bin local sort   3*P'*pe + 8*C' + 8*nbins (count and place in one launch,
                    bin ranges written) + N*e when it also zero-fills grad_value
   bin accumulate   8*C' + B*Q*M*D*e + N'*e
@@ -387,6 +389,8 @@ def main():
               "bin_zero": (nb + 1) * 4, "bin_count": 2 * P_bin * pe, "bin_scan": 3 * nb * 4,
               "bin_place": 3 * P_bin * pe + 8 * C_bin,
               "bin_local_sort": 3 * P_bin * pe + 8 * C_bin + 8 * nb + zero_fused * N * e,
+              "bin_tile_sum": nb * 4, "bin_tile_offsets": 3 * (-(-nb // 4096)) * 4,
+              "bin_tile_scan": 3 * nb * 4,
               "bin_accum_kernel": 8 * C_bin + B * Q * M * D * e + bin_rows * D * e}
     kbytes["scatter_accum_kernel"] = kbytes["msda_scatter_kernel"] + kbytes["bin_accum_kernel"]
     kbytes["grad_sort_kernel"] = kbytes["msda_grad_kernel"] + kbytes["bin_local_sort"]

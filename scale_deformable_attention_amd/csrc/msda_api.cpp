@@ -336,10 +336,13 @@ bool levels_leave_gaps(const msda::Problem &p) {
 // where the path cannot apply; on success fills the level table and the
 // workspace layout.
 constexpr double kBinRecords = 1024.0;
+// Up to this many tiles of 4096 bin counts one workgroup scans them (one
+// launch); beyond, the scan runs as three launches over all tiles at once.
+constexpr int64_t kSingleScanTiles = 2;
 
 struct BinPlan {
     int64_t nbins = 0, records = 0;
-    size_t starts_off = 0, cursor_off = 0, records_off = 0, bytes = 0;
+    size_t starts_off = 0, cursor_off = 0, tiles_off = 0, records_off = 0, bytes = 0;
     int max_level_bins = 0;    // bins of the binned level with the most
     bool local_sort = false;   // one-launch count / scan / place applies
 };
@@ -390,7 +393,8 @@ bool plan_bins(msda::Problem *p, BinPlan *bp, bool contended_only) {
                      bp->max_level_bins <= msda::kMaxLocalSortBins;
     bp->starts_off = 0;
     bp->cursor_off = align_up((size_t)(nbins + 1) * 4, 256);
-    bp->records_off = bp->cursor_off + align_up((size_t)nbins * 4, 256);
+    bp->tiles_off = bp->cursor_off + align_up((size_t)nbins * 4, 256);
+    bp->records_off = bp->tiles_off + align_up((size_t)(msda::scan_tiles(nbins) + 1) * 8, 256);
     bp->bytes = bp->records_off + (size_t)bp->records * 8;
     return true;
 }
@@ -754,6 +758,7 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
         msda::BinnedBuffers bins;
         bins.starts = reinterpret_cast<uint32_t *>(ws + bp.starts_off);
         bins.cursor = reinterpret_cast<uint32_t *>(ws + bp.cursor_off);
+        bins.tile_offsets = reinterpret_cast<uint32_t *>(ws + bp.tiles_off);
         bins.records = reinterpret_cast<uint2 *>(ws + bp.records_off);
         bins.nbins = bp.nbins;
         bins.ends = bp.local_sort ? bins.cursor : bins.starts + 1;
@@ -819,8 +824,15 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
                                      t, "bin_count")) != hipSuccess) {
                 what = "bin count launch";
                 break;
-            } else if ((err = marked(msda::launch_bin_scan(bins, before(t)), t, "bin_scan")) !=
-                       hipSuccess) {
+            } else if (msda::scan_tiles(bp.nbins) <= kSingleScanTiles
+                           ? (err = marked(msda::launch_bin_scan(bins, before(t)), t, "bin_scan")) !=
+                                 hipSuccess
+                           : ((err = marked(msda::launch_bin_tile_sums(bins, before(t)), t,
+                                            "bin_tile_sum")) != hipSuccess ||
+                              (err = marked(msda::launch_bin_tile_offsets(bins, before(t)), t,
+                                            "bin_tile_offsets")) != hipSuccess ||
+                              (err = marked(msda::launch_bin_tile_scan(bins, before(t)), t,
+                                            "bin_tile_scan")) != hipSuccess)) {
                 what = "bin scan launch";
                 break;
             } else if ((err = marked(msda::launch_bin_sort(p, sampling_locations,

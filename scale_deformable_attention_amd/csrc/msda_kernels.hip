@@ -1322,6 +1322,76 @@ __global__ __launch_bounds__(kScanBlock) void bin_scan_kernel(uint32_t *__restri
     if (tid == 0) starts[nb] = carry;
 }
 
+// Parallel scan of large count arrays, in tiles of kScanTile counts (each
+// thread of a kScanBlock workgroup owns 4 consecutive ones): tile totals
+// (bin_tile_sum_kernel), an exclusive scan of the totals by bin_scan_kernel
+// over the short totals array, then every tile's exclusive scan plus its
+// offset (bin_tile_scan_kernel), in place over the counts. The single-
+// workgroup scan alone serialises on its barriers (each waits for the
+// tile's loads and stores); these three launches run every tile at once.
+constexpr int64_t kScanTile = 4 * kScanBlock;
+
+__device__ __forceinline__ uint32_t block_sum_1024(uint32_t v, uint32_t *wsum) {
+    constexpr int kWaves = kScanBlock / 64;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) wsum[wv] = v;
+    __syncthreads();
+    uint32_t t = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) t += wsum[i];
+    return t;
+}
+
+__global__ __launch_bounds__(kScanBlock) void bin_tile_sum_kernel(const uint32_t *__restrict__ counts,
+                                                                 uint32_t *__restrict__ tsum,
+                                                                 const int64_t nb) {
+    __shared__ uint32_t wsum[kScanBlock / 64];
+    const int64_t i0 = (int64_t)blockIdx.x * kScanTile + 4 * (int64_t)threadIdx.x;
+    uint32_t v = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v += i0 + k < nb ? counts[i0 + k] : 0u;
+    const uint32_t t = block_sum_1024(v, wsum);
+    if (threadIdx.x == 0) tsum[blockIdx.x] = t;
+}
+
+// starts[0:nb] (counts) -> exclusive starts, cursor = starts; toff = the
+// exclusive scan of the tile totals (toff[ntiles] = total -> starts[nb]).
+__global__ __launch_bounds__(kScanBlock) void bin_tile_scan_kernel(uint32_t *__restrict__ starts,
+                                                                  uint32_t *__restrict__ cursor,
+                                                                  const uint32_t *__restrict__ toff,
+                                                                  const int64_t nb) {
+    constexpr int kWaves = kScanBlock / 64;
+    __shared__ uint32_t wsum[kWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t i0 = (int64_t)blockIdx.x * kScanTile + 4 * (int64_t)tid;
+    uint32_t c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = i0 + k < nb ? starts[i0 + k] : 0u;
+    const uint32_t s3 = c[0] + c[1] + c[2] + c[3];
+    uint32_t x = s3;  // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    uint32_t before = toff[blockIdx.x];
+    for (int i = 0; i < wv; ++i) before += wsum[i];
+    uint32_t o = before + x - s3;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (i0 + k < nb) {
+            starts[i0 + k] = o;
+            cursor[i0 + k] = o;
+        }
+        o += c[k];
+    }
+    if (blockIdx.x == gridDim.x - 1 && tid == 0) starts[nb] = toff[gridDim.x];
+}
+
 // One workgroup per bin, no atomics. The workgroup has kAccGroups lane
 // groups of 16 lanes (slot layout as in the backward) and a bin has at most
 // kAccGroups rows; with rep = kAccGroups / rows replicas of each row there
@@ -2095,9 +2165,34 @@ hipError_t launch_gradients_and_sort(const Problem &p, const Mapping &mp, const 
 #undef MSDA_GS
 }
 
+int64_t scan_tiles(int64_t nbins) { return (nbins + kScanTile - 1) / kScanTile; }
+
 hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream) {
     hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, bins.starts,
                        bins.cursor, bins.nbins);
+    return hipGetLastError();
+}
+
+hipError_t launch_bin_tile_sums(const BinnedBuffers &bins, hipStream_t stream) {
+    const int64_t nt = scan_tiles(bins.nbins);
+    if (nt < 1 || nt >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bin_tile_sum_kernel, dim3((unsigned)nt), dim3(kScanBlock), 0, stream,
+                       bins.starts, bins.tile_offsets, bins.nbins);
+    return hipGetLastError();
+}
+
+hipError_t launch_bin_tile_offsets(const BinnedBuffers &bins, hipStream_t stream) {
+    // the single-workgroup scan over the ntiles totals (toff[ntiles] = total)
+    const int64_t nt = scan_tiles(bins.nbins);  // (the cursor copy goes past the offsets)
+    hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, bins.tile_offsets,
+                       bins.tile_offsets + nt + 1, nt);
+    return hipGetLastError();
+}
+
+hipError_t launch_bin_tile_scan(const BinnedBuffers &bins, hipStream_t stream) {
+    const int64_t nt = scan_tiles(bins.nbins);
+    hipLaunchKernelGGL(bin_tile_scan_kernel, dim3((unsigned)nt), dim3(kScanBlock), 0, stream,
+                       bins.starts, bins.cursor, bins.tile_offsets, bins.nbins);
     return hipGetLastError();
 }
 

@@ -166,18 +166,19 @@ def test_workspace_size_and_accum_resolution(lib):
     assert lib.msda_backward_resolve_accum(0, *prob, 2) == 0  # fp32: nothing to switch
     # AUTO = MIXED: level (4,5) at 6.4 contributions per pixel is binned, level
     # (8,10) at 1.6 keeps native atomics. Two 16-row bins per (b, m) for the
-    # binned level: 4 bins; starts (5 x 4 B) and cursors (4 x 4 B) padded to
-    # 256 B each; records: 4 corners x (16 queries x 2 heads x 2 points) x 8 B.
+    # binned level: 4 bins; starts (5 x 4 B), cursors (4 x 4 B) and the scan's
+    # tile offsets (2 x 2 x 4 B for one tile) padded to 256 B each; records:
+    # 4 corners x (16 queries x 2 heads x 2 points) x 8 B.
     for dtype in (0, 1, 2):
         assert lib.msda_backward_resolve_accum(dtype, *prob, -1) == 4
         assert lib.msda_backward_resolve_accum(dtype, *prob, 4) == 4
-        assert lib.msda_backward_workspace_size(dtype, *prob, -1) == 256 + 256 + 4 * 64 * 8
+        assert lib.msda_backward_workspace_size(dtype, *prob, -1) == 3 * 256 + 4 * 64 * 8
     # BINNED: bins of 16 rows (the cap) at both levels -> 5 + 2 bins per
-    # (b, m): 14 bins; starts (15 x 4 B) and cursors (14 x 4 B) each padded to
-    # 256 B; records: 4 corners x 128 points x 8 B.
+    # (b, m): 14 bins; starts (15 x 4 B), cursors (14 x 4 B) and tile offsets
+    # each padded to 256 B; records: 4 corners x 128 points x 8 B.
     for dtype in (0, 1, 2):
         assert lib.msda_backward_resolve_accum(dtype, *prob, 3) == 3
-        assert lib.msda_backward_workspace_size(dtype, *prob, 3) == 256 + 256 + 4 * 128 * 8
+        assert lib.msda_backward_workspace_size(dtype, *prob, 3) == 3 * 256 + 4 * 128 * 8
     # BINNED / MIXED do not apply to overlapping levels; AUTO falls back to
     # PER_LEVEL for bf16 and NATIVE otherwise
     over = (1, 100, 2, 8, 2, SHAPES, (ctypes.c_int64 * 2)(0, 70), 16, 2)
