@@ -113,7 +113,8 @@ def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in ("scale_deformable_attention_amd/csrc/msda_kernels.hip",
                 "scale_deformable_attention_amd/csrc/msda_api.cpp",
-                "scale_deformable_attention_amd/csrc/msda_launch.h"):
+                "scale_deformable_attention_amd/csrc/msda_launch.h",
+                "scale_deformable_attention_amd/csrc/msda_device.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
