@@ -1234,9 +1234,12 @@ __global__ __launch_bounds__(kSortBlock) void bin_local_sort_kernel(
 
 // The gradients (msda_grad_kernel), the local bin sort and the grad_value zero
 // fill in one launch: none reads what another writes, so the sort's and the
-// fill's short workgroups run beside the gradient tiles. Workgroups
-// [0, ngrad) take gradient tiles (XCD-aware order; ngrad a multiple of 8),
-// [ngrad, ngrad + nseg) sort segments, the rest zero-fill.
+// fill's workgroups run beside the gradient tiles. The fill and the sort come
+// first, so that their streams of stores and their latency chains start with
+// the gathers of the gradient tiles rather than after them: workgroups
+// [0, nzero) zero-fill, [nzero, nzero + nsegp) sort segments (nsegp = nseg
+// rounded up to a multiple of 8), the rest take gradient tiles in XCD-aware
+// order (nzero, nsegp and ngrad are multiples of 8).
 constexpr int kFusedSortPts = 8;  // 256 threads x 8 points: the local sort's 2048 points
 
 template <class DT, class PT, int VEC>
@@ -1248,18 +1251,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
     const int log2s, const uint32_t ngrad, uint32_t *__restrict__ starts,
     uint32_t *__restrict__ ends, uint2 *__restrict__ records, const int64_t nbbm,
-    const int64_t nseg, uint4 *__restrict__ zero_dst, const int64_t zero_n16) {
+    const uint32_t nseg, const uint32_t nsegp, const uint32_t nzero, uint4 *__restrict__ zero_dst,
+    const int64_t zero_n16) {
     extern __shared__ uint32_t hist[];
     const uint32_t bx = blockIdx.x;
-    if (bx < ngrad) {
-        const int64_t tile = (int64_t)(bx % kXcds) * (ngrad / kXcds) + bx / kXcds;
-        if (tile < ntiles) grad_tile<DT, PT, VEC, 4, true>(MSDA_GRAD_ARGS, tile);
-    } else if (bx - ngrad < nseg) {
-        local_sort_segment<PT, kBlock, kFusedSortPts>(hist, loc, attn, lt, starts, ends, records, Q,
-                                                      M, L, K, nbbm, (int64_t)(bx - ngrad));
+    if (bx < nzero) {
+        zero_part(zero_dst, zero_n16, bx, nzero);
+    } else if (bx < nzero + nsegp) {
+        const uint32_t seg = bx - nzero;
+        if (seg < nseg)
+            local_sort_segment<PT, kBlock, kFusedSortPts>(hist, loc, attn, lt, starts, ends, records,
+                                                          Q, M, L, K, nbbm, (int64_t)seg);
     } else {
-        const int64_t first = (int64_t)ngrad + nseg;
-        zero_part(zero_dst, zero_n16, (int64_t)bx - first, (int64_t)gridDim.x - first);
+        const uint32_t g = bx - nzero - nsegp;
+        const int64_t tile = (int64_t)(g % kXcds) * (ngrad / kXcds) + g / kXcds;
+        if (tile < ntiles) grad_tile<DT, PT, VEC, 4, true>(MSDA_GRAD_ARGS, tile);
     }
 }
 
@@ -1581,8 +1587,10 @@ __global__ __launch_bounds__(kBlock) void bin_accum_kernel(
 // one launch: they touch disjoint grad_value rows and depend only on work
 // already finished (zero fill, bin sort), so their workgroups share the chip;
 // the accumulation's latency-bound rounds fill the gaps of the scatter's
-// atomic-bound stream. Workgroups [0, nsc) scatter and the rest accumulate,
-// each range with its own XCD-aware order (nsc is a multiple of 8).
+// atomic-bound stream. Workgroups come in rows of 8 (one per XCD); of the
+// R = gridDim / 8 rows, Rs = nsc / 8 scatter and the others accumulate,
+// spread evenly over the grid so both run from the start; within each role
+// the XCD-aware order is that of its own kernel (nsc is a multiple of 8).
 template <class DT, class PT, int SLOT, int J, int V>
 __global__ __launch_bounds__(kBlock) void scatter_accum_kernel(
     const typename PT::S *__restrict__ loc, const typename PT::S *__restrict__ attn,
@@ -1593,16 +1601,17 @@ __global__ __launch_bounds__(kBlock) void scatter_accum_kernel(
     const uint2 *__restrict__ records, const int64_t nbbm, const int64_t nbins,
     const int accumulate) {
     extern __shared__ float dyn_tile[];
-    const uint32_t bx = blockIdx.x;
-    if (bx < nsc) {
-        const int64_t tile = (int64_t)(bx % kXcds) * (nsc / kXcds) + bx / kXcds;
+    const uint32_t bx = blockIdx.x, xcd = bx % kXcds;
+    const int64_t r = bx / kXcds, R = gridDim.x / kXcds, Rs = nsc / kXcds;
+    const int64_t k = r * Rs / R;  // scatter rows before row r
+    if ((r + 1) * Rs / R > k) {    // row r is scatter row k
+        const int64_t tile = (int64_t)xcd * Rs + k;
         if (tile < ntiles) {
             float *workspace = nullptr;
             scatter_tile<DT, PT, SLOT, J>(MSDA_SCATTER_ARGS, tile);
         }
     } else {
-        const uint32_t i = bx - nsc;
-        const int64_t bin = (int64_t)(i % kXcds) * ((gridDim.x - nsc) / kXcds) + i / kXcds;
+        const int64_t bin = (int64_t)xcd * (R - Rs) + (r - k);
         if (bin < nbins) {
             typename DT::S *gv = static_cast<typename DT::S *>(grad_value);
             accum_bin<DT, SLOT, J, V>(dyn_tile, grad_out, gv, starts, ends, records, lt, S, Q, M,
@@ -2116,17 +2125,21 @@ hipError_t grad_sort_launch(const Problem &p, const Mapping &mp, const void *val
     const int64_t ntiles = p.B * p.M * qblocks;
     const int64_t ngrad = (ntiles + kXcds - 1) / kXcds * kXcds;
     const int64_t nseg = p.B * p.M * p.levels.nblev;
+    const int64_t nsegp = (nseg + kXcds - 1) / kXcds * kXcds;
     const int64_t n16 = (int64_t)(zero_bytes / 16);
-    const int64_t nzero = n16 > 0 ? std::min<int64_t>((n16 + kBlock - 1) / kBlock, 2048) : 0;
-    if (ngrad + nseg + nzero >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    // one long-running fill workgroup per CU, or fewer for a small fill
+    const int64_t nzero =
+        n16 > 0 ? std::min<int64_t>((n16 + kBlock - 1) / kBlock + kXcds - 1, 256) / kXcds * kXcds : 0;
+    if (ngrad + nsegp + nzero >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const size_t lds = (size_t)((max_level_bins + 1) / 2) * 4;
-    hipLaunchKernelGGL((grad_sort_kernel<DT, PT, VEC>), dim3((unsigned)(ngrad + nseg + nzero)),
+    hipLaunchKernelGGL((grad_sort_kernel<DT, PT, VEC>), dim3((unsigned)(nzero + nsegp + ngrad)),
                        dim3(kBlock), lds, stream, static_cast<const E *>(value),
                        static_cast<const P *>(loc), static_cast<const P *>(attn),
                        static_cast<const E *>(grad_out), static_cast<P *>(grad_loc),
                        static_cast<P *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
                        (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split,
-                       (uint32_t)ngrad, bins.starts, bins.cursor, bins.records, p.nbbm, nseg,
+                       (uint32_t)ngrad, bins.starts, bins.cursor, bins.records, p.nbbm,
+                       (uint32_t)nseg, (uint32_t)nsegp, (uint32_t)nzero,
                        static_cast<uint4 *>(zero_dst), n16);
     return hipGetLastError();
 }
