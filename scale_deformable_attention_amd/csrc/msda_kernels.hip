@@ -2127,9 +2127,10 @@ hipError_t grad_sort_launch(const Problem &p, const Mapping &mp, const void *val
     const int64_t nseg = p.B * p.M * p.levels.nblev;
     const int64_t nsegp = (nseg + kXcds - 1) / kXcds * kXcds;
     const int64_t n16 = (int64_t)(zero_bytes / 16);
-    // one long-running fill workgroup per CU, or fewer for a small fill
+    // 128 long-running fill workgroups (measured on the decoder: 64 and 256
+    // are slower), or fewer for a small fill
     const int64_t nzero =
-        n16 > 0 ? std::min<int64_t>((n16 + kBlock - 1) / kBlock + kXcds - 1, 256) / kXcds * kXcds : 0;
+        n16 > 0 ? std::min<int64_t>((n16 + kBlock - 1) / kBlock + kXcds - 1, 128) / kXcds * kXcds : 0;
     if (ngrad + nsegp + nzero >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const size_t lds = (size_t)((max_level_bins + 1) / 2) * 4;
     hipLaunchKernelGGL((grad_sort_kernel<DT, PT, VEC>), dim3((unsigned)(nzero + nsegp + ngrad)),
