@@ -490,3 +490,52 @@ def test_mixed_dtype_rejections():
     with pytest.raises(TypeError):
         msda_forward(v16, g["spatial_shapes"], None, g["sampling_locations"].bfloat16(),
                      g["attention_weights"].bfloat16())
+
+
+# ------------------------------------------- launch paths at their size limits
+
+def _backward_launch_names(inp, accum):
+    """Run the backward with per-launch instrumentation; return the launch
+    names and the gradients."""
+    from scale_deformable_attention_amd._binding import launch_event_names, set_launch_events
+    g = to_dev(inp)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(40)]
+    for e in evs:
+        e.record()  # torch creates the HIP event on first record
+    torch.cuda.synchronize()
+    set_launch_events(evs)
+    grads = msda_backward(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                          g["attention_weights"], g["grad_output"], accum=accum)
+    torch.cuda.synchronize()
+    return launch_event_names(), tuple(t.cpu() for t in grads)
+
+
+# name, dtype, Q, K, M, D, levels, accum, a launch the path must make, launches it must not
+PATH_CASES = [
+    # Q*K = 2048: gradients, one-launch sort and fill share a launch
+    ("fused_sort_at_2048_points", torch.bfloat16, 512, 4, 2, 32, ((64, 64), (32, 32)), "auto",
+     "grad_sort_kernel", ("bin_count", "bin_local_sort")),
+    # Q*K = 2052: count / scan / place
+    ("sort_chain_past_2048_points", torch.bfloat16, 513, 4, 2, 32, ((64, 64), (32, 32)), "auto",
+     "bin_count", ("grad_sort_kernel", "bin_local_sort")),
+    # every level binned; 5625 bins on level 0: the one-launch sort without the
+    # gradients (above 4096 bins)
+    ("local_sort_above_4096_bins", torch.float16, 64, 2, 1, 16, ((300, 300), (8, 8)), "binned",
+     "bin_local_sort", ("grad_sort_kernel", "bin_count")),
+    # 40000 bins on level 0: the chain, with the scan over tiles of 4096
+    ("sort_chain_above_32000_bins", torch.float32, 64, 2, 1, 16, ((800, 800), (8, 8)), "binned",
+     "bin_tile_sum", ("bin_local_sort",)),
+]
+
+
+@pytest.mark.parametrize("case", PATH_CASES, ids=lambda c: c[0])
+def test_sort_paths_at_their_limits(case):
+    name, dtype, Q, K, M, D, levels, accum, must, must_not = case
+    wl = Workload(name=name, dtype=dtype, B=2, Q=Q, M=M, D=D, K=K, levels=levels,
+                  loc_kind="uniform", loc_lo=-0.05, loc_hi=1.05, seed=91)
+    inp = make_inputs(wl)
+    say(f"case {name}: Q={Q} K={K} levels={levels} accum={accum} {dtype}")
+    names, grads = _backward_launch_names(inp, accum)
+    assert must in names and not set(must_not) & set(names), names
+    _, _, ref_grads, trows = oracle_run(inp)
+    check_backward(dtype, grads, ref_grads, inp["spatial_shapes"], None, trows)
