@@ -268,6 +268,28 @@ def msda_backward_resolve_accum(value: torch.Tensor, spatial_shapes, level_start
     return _RESOLVED[r]
 
 
+def msda_backward_level_modes(value: torch.Tensor, spatial_shapes, level_start_index,
+                              sampling_locations: torch.Tensor, attention_weights: torch.Tensor,
+                              accum="auto"):
+    """How msda_backward would accumulate each level's grad_value for this
+    problem: a list of "native" (atomics of the value dtype), "fp32_scratch"
+    or "binned". Host-only (msda_backward_plan)."""
+    lib = load_library()
+    levels = _Levels(spatial_shapes, level_start_index)
+    if value.dtype not in _DTYPE_CODES:
+        raise TypeError(f"unsupported dtype {value.dtype}; use float32, float16 or bfloat16")
+    code = _DTYPE_CODES[value.dtype]  # the plan depends on the value dtype only
+    B, S, M, D, Q, K = _dims(value, levels, sampling_locations, attention_weights)
+    if accum not in _ACCUM_CODES:
+        raise ValueError(f"unknown accumulation mode {accum!r}")
+    modes = (ctypes.c_int * levels.L)()
+    nb = int(lib.msda_backward_plan(*_problem(code, B, S, M, D, levels, Q, K),
+                                    _ACCUM_CODES[accum], modes))
+    if nb < 0:
+        raise MSDAError(8, lib.msda_last_error().decode())
+    return [LEVEL_MODES[int(m)] for m in modes]
+
+
 def set_launch_events(events) -> None:
     """Instrument the next msda_forward / msda_backward call of this thread:
     events[i] (torch.cuda.Event, already created) is recorded on the call's

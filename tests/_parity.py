@@ -13,12 +13,19 @@ grad_sampling_locations and grad_attention_weights, 5e-2 on grad_value.
 Exact parts: a grad_value row no in-bounds corner lands on, and an output
 row none of whose points has an in-bounds corner, must be exactly zero.
 
-Forced packed bf16 atomics (accumulation "native" on bf16 data) round the
-running sum to 8 significant bits on every add; on a level whose pixels take
-more than 4 contributions on average (Q*K*4 / (H*W)) an element whose sum
-nearly cancels can drift past the elementwise bar depending on the order of
-the adds. There grad_value is held to the same 5e-2 normwise (and a cosine
-above 0.998) instead; AUTO never uses bf16 atomics on such levels.
+Packed 16-bit atomics round the running sum to the value dtype on every add
+(8 significant bits for bf16, 11 for fp16). Where contributions of one
+element nearly cancel, the rounding of the large partial sums leaves an
+absolute error of up to about one 16-bit ulp of the largest partial sum,
+which for such an element can exceed the elementwise bar whatever the order
+of the adds (seen: one element in 4.3 M on the decoder's level 1, bf16, at
+1.1 contributions per pixel). So on levels accumulated with 16-bit atomics
+grad_value may have a few such elements (at most 1e-5 of the level, and at
+least one allowed) provided the level's normwise error stays within the same
+bar and the cosine above 0.998; on bf16 levels above 4 contributions per
+pixel (Q*K*4 / (H*W)), which only forced NATIVE accumulation sends to bf16
+atomics, the level is held normwise only. Every level summed in fp32 (fp32
+data, fp32 scratch, binned) is held element by element.
 """
 
 from __future__ import annotations
@@ -98,20 +105,39 @@ def contended_levels(spatial_shapes, Q, K, threshold=4.0) -> tuple:
     return tuple(l for l, (h, w) in enumerate(shp) if Q * K * 4 / (h * w) > threshold)
 
 
-def native_bf16_levels(dtype, accum, spatial_shapes, Q, K) -> tuple:
-    """Levels checked normwise: contended levels under forced bf16 atomics."""
-    if dtype != torch.bfloat16 or accum not in ("native", False):
-        return ()
-    return contended_levels(spatial_shapes, Q, K)
+def atomic_level_rules(dtype, accum, inp, level_start_index=None) -> dict:
+    """check_backward's keyword arguments for the levels that the library
+    accumulates with 16-bit atomics on this problem (see the module
+    docstring): normwise_levels (bf16, contended) and outlier_levels."""
+    if dtype not in (torch.float16, torch.bfloat16):
+        return {}
+    from scale_deformable_attention_amd._binding import msda_backward_level_modes
+    accum = {None: "auto", False: "native", True: "fp32_scratch"}.get(accum, accum)
+    modes = msda_backward_level_modes(inp["value"], inp["spatial_shapes"], level_start_index,
+                                      inp["sampling_locations"], inp["attention_weights"], accum)
+    loc = inp["sampling_locations"]
+    hot = contended_levels(inp["spatial_shapes"], loc.shape[1], loc.shape[4])
+    native = [l for l, m in enumerate(modes) if m == "native"]
+    normwise = tuple(l for l in native if dtype == torch.bfloat16 and l in hot)
+    return {"normwise_levels": normwise,
+            "outlier_levels": tuple(l for l in native if l not in normwise)}
+
+
+def _normwise(name, got, want, tol):
+    nw = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
+    cos = float(np.dot(got, want) / max(np.linalg.norm(got) * np.linalg.norm(want), 1e-300))
+    assert nw <= tol and cos > 0.998, f"{name} (16-bit atomics): normwise {nw:.3e}, cos {cos:.6f}"
+    return nw
 
 
 def check_backward(dtype, gpu, ref, spatial_shapes, level_start_index=None,
-                   touched_rows=None, param_dtype=None, normwise_levels=()) -> list:
+                   touched_rows=None, param_dtype=None, normwise_levels=(),
+                   outlier_levels=()) -> list:
     """`param_dtype`: dtype of the locations / weights and their gradients
     when it differs from the value dtype (mixed calls); their tolerances follow
     it, since those gradients are fp32 sums rounded once to it.
-    `normwise_levels`: levels whose grad_value is held normwise (forced bf16
-    atomics on contended levels, see the module docstring)."""
+    `normwise_levels` / `outlier_levels`: levels accumulated with 16-bit
+    atomics (see the module docstring; atomic_level_rules gives both)."""
     gv, gl, ga = (to_np(t) for t in gpu)
     rgv, rgl, rga = ref
     tol = dict(TOL[dtype])
@@ -120,14 +146,23 @@ def check_backward(dtype, gpu, ref, spatial_shapes, level_start_index=None,
             tol[k] = TOL[param_dtype][k]
     stats = [check_slice("grad_attention_weights", ga, rga, tol["grad_attention_weights"])]
     for l, (r0, r1) in enumerate(level_row_ranges(spatial_shapes, level_start_index)):
+        name = f"grad_value[level {l}]"
+        got, want = gv[:, r0:r1].ravel(), rgv[:, r0:r1].ravel()
         if l in normwise_levels:
-            got, want = gv[:, r0:r1].ravel(), rgv[:, r0:r1].ravel()
-            nw = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
-            cos = float(np.dot(got, want) / max(np.linalg.norm(got) * np.linalg.norm(want), 1e-300))
-            assert nw <= tol["grad_value"] and cos > 0.998, \
-                f"grad_value[level {l}] (bf16 atomics): normwise {nw:.3e}, cos {cos:.6f}"
-            stats.append({"name": f"grad_value[level {l}] normwise", "n": got.size,
+            nw = _normwise(name, got, want, tol["grad_value"])
+            stats.append({"name": name + " normwise", "n": got.size,
                           "max_scaled": float("nan"), "normwise": nw})
+        elif l in outlier_levels and want.size:
+            rms = float(np.sqrt(np.mean(want * want)))
+            bad = ~(np.abs(got - want) <= tol["grad_value"] * (np.abs(want) + rms))
+            if bad.any():
+                assert bad.sum() <= max(1, int(1e-5 * want.size)), \
+                    f"{name}: {int(bad.sum())}/{want.size} elements outside tol (16-bit atomics)"
+                nw = _normwise(name, got, want, tol["grad_value"])
+                stats.append({"name": name + f" ({int(bad.sum())} rounding outliers)",
+                              "n": got.size, "max_scaled": float("nan"), "normwise": nw})
+            else:
+                stats.append(check_slice(name, got, want, tol["grad_value"]))
         else:
             stats.append(check_slice(f"grad_value[level {l}]", gv[:, r0:r1], rgv[:, r0:r1],
                                      tol["grad_value"]))

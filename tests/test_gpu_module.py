@@ -241,3 +241,29 @@ def test_module_mixed_param_dtype_runs_fp32_locations():
     assert out.dtype == torch.bfloat16 and torch.isfinite(out).all()
     assert torch.isfinite(x.grad).all() and torch.isfinite(inp.grad).all()
     assert mod.sampling_offsets.weight.grad is not None
+
+
+def test_module_padding_mask_zeroes_value_rows():
+    """input_padding_mask zeroes the value rows of padded input positions: the
+    output does not change when those inputs change, and their input
+    gradients are zero."""
+    from scale_deformable_attention_amd import MSDeformAttn
+    say("case module padding mask")
+    torch.manual_seed(9)
+    mod = MSDeformAttn(d_model=32, n_levels=3, n_heads=4, n_points=2).to(DEV)
+    S = sum(h * w for h, w in MODULE_LEVELS)
+    g = torch.Generator().manual_seed(10)
+    x = torch.randn(2, 12, 32, generator=g).to(DEV)
+    ref = (0.1 + 0.8 * torch.rand(2, 12, 2, generator=g)).to(DEV)
+    inp = torch.randn(2, S, 32, generator=g).to(DEV)
+    mask = torch.rand(2, S, generator=g).to(DEV) < 0.3
+    other = inp.clone()
+    other[mask] = torch.randn(int(mask.sum()), 32, device=DEV) * 5.0
+    a = mod(x, ref, inp, MODULE_LEVELS, input_padding_mask=mask)
+    inp_b = other.clone().requires_grad_(True)
+    b = mod(x, ref, inp_b, MODULE_LEVELS, input_padding_mask=mask)
+    b.sum().backward()
+    torch.cuda.synchronize()
+    assert torch.allclose(a, b, rtol=0, atol=0), "padded inputs changed the output"
+    assert not inp_b.grad[mask].any(), "padded inputs received gradient"
+    assert inp_b.grad[~mask].abs().sum() > 0

@@ -16,7 +16,7 @@ import oracle
 from scale_deformable_attention_amd import MSDAError, PreparedCall, msda_backward, msda_forward
 from scale_deformable_attention_amd.workloads import Workload, make_inputs, workload
 
-from _parity import check_backward, check_forward, level_row_ranges, native_bf16_levels, to_np
+from _parity import atomic_level_rules, check_backward, check_forward, level_row_ranges, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -65,10 +65,8 @@ def full_check(inp, dtype, accum="auto", starts=None, ref=None):
     out, grads = gpu_run(inp, accum, starts)
     ref_out, touched, ref_grads, trows = ref if ref is not None else oracle_run(inp, starts)
     stats = check_forward(dtype, out, ref_out, touched)
-    loc = inp["sampling_locations"]
     stats += check_backward(dtype, grads, ref_grads, inp["spatial_shapes"], starts, trows,
-                            normwise_levels=native_bf16_levels(dtype, accum, inp["spatial_shapes"],
-                                                               loc.shape[1], loc.shape[4]))
+                            **atomic_level_rules(dtype, accum, inp, starts))
     for s in stats:
         if s.get("n"):
             say(f"  {s['name']:34s} max_scaled={s['max_scaled']:.2e} normwise={s['normwise']:.2e}")
@@ -374,7 +372,8 @@ def test_int64_indexing_beyond_2_pow_31_elements():
         gl_last, ga_last = gl[B - 1:].cpu(), ga[B - 1:].cpu()
         del gv, gl, ga
         torch.cuda.empty_cache()
-        check_backward(dtype, (gv_last, gl_last, ga_last), ref_grads, shapes, None, trows)
+        check_backward(dtype, (gv_last, gl_last, ga_last), ref_grads, shapes, None, trows,
+                       **atomic_level_rules(dtype, accum, last))
 
 
 def test_accumulation_resolution_on_the_decoder_workload():
@@ -476,7 +475,7 @@ def test_mixed_dtype_parity(name, accum):
     ref_out, touched, ref_grads, trows = ref
     check_forward(wl.dtype, out, ref_out, touched)
     check_backward(wl.dtype, grads, ref_grads, inp["spatial_shapes"], None, trows,
-                   param_dtype=torch.float32)
+                   param_dtype=torch.float32, **atomic_level_rules(wl.dtype, accum, inp))
 
 
 def test_mixed_dtype_rejections():
@@ -538,4 +537,5 @@ def test_sort_paths_at_their_limits(case):
     names, grads = _backward_launch_names(inp, accum)
     assert must in names and not set(must_not) & set(names), names
     _, _, ref_grads, trows = oracle_run(inp)
-    check_backward(dtype, grads, ref_grads, inp["spatial_shapes"], None, trows)
+    check_backward(dtype, grads, ref_grads, inp["spatial_shapes"], None, trows,
+                   **atomic_level_rules(dtype, accum, inp))
