@@ -237,7 +237,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     if not torch.cuda.is_available():

@@ -130,7 +130,7 @@ typedef enum msda_status {
     MSDA_ERR_ALIGN = 5,       /* pointer not aligned to its element size */
     MSDA_ERR_WORKSPACE = 6,   /* workspace missing or too small          */
     MSDA_ERR_HIP = 7,         /* a HIP launch failed                     */
-    MSDA_ERR_UNSUPPORTED = 8  /* valid but outside this build's limits   */
+    MSDA_ERR_UNSUPPORTED = 8  /* valid but outside the library's limits  */
 } msda_status_t;
 
 /* Add into grad_value instead of overwriting it (training-style gradient

@@ -334,8 +334,9 @@ bool levels_leave_gaps(const msda::Problem &p) {
 // at most 16, so that a bin holds about kBinRecords records if the level's
 // points spread evenly (contributions per pixel Q*K*4 / (H*W)). Returns false
 // where the path cannot apply; on success fills the level table and the
-// workspace layout.
-constexpr double kBinRecords = 1024.0;
+// workspace layout. Measured on MI355X (encoder workload step): 256 records
+// per bin 1439 us, 1024 1275 us, 4096 1239 us, 16384 1303 us.
+constexpr double kBinRecords = 4096.0;
 // Up to this many tiles of 4096 bin counts one workgroup scans them (one
 // launch); beyond, the scan runs as three launches over all tiles at once.
 constexpr int64_t kSingleScanTiles = 2;
