@@ -18,6 +18,9 @@ Prints one JSON line:
   kernels               per-kernel average device time and algorithmic GB/s
   roofline              the dominant kernel against the 8 TB/s HBM roofline:
                         algorithmic bytes per launch / average launch duration
+  cold_us_per_step      context: one step timed alone after 1 GiB is written
+                        (L2 and the 256 MB MALL evicted)
+  device_copy_GBps      context: a 1 GiB device copy, bytes read + written / time
   cpu_baseline          the CPU oracle (fp64 loops, OpenMP) on the same workload
 
 Algorithmic bytes per launch (e = element size of value / grad rows, pe = of
@@ -333,6 +336,37 @@ def main():
     log(f"timed {K} steps: {us_step:.2f} us/step ({'graph replay' if graph_ok else 'eager'}); "
         f"eager {eager_us:.2f} us/step, host enqueue {host_us:.2f} us/step")
 
+    # Cold caches, for context: a 1 GiB write between steps evicts L2 and the
+    # 256 MB MALL; each step is timed alone (one launch of the captured step).
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    n_cold = min(K, 50)
+    c_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n_cold)]
+    for c0, c1 in c_evs:
+        flush.fill_(1.0)
+        c0.record()
+        if graph_ok:
+            graph.replay()
+        else:
+            step()
+        c1.record()
+    torch.cuda.synchronize()
+    cold_us = float(np.mean([c0.elapsed_time(c1) for c0, c1 in c_evs])) * 1e3
+    # Device copy bandwidth, for context: 10 copies of 1 GiB (read + write).
+    cp_src = flush
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        cp_dst.copy_(cp_src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 10 * 2 * cp_src.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del flush, cp_src, cp_dst
+    log(f"cold-cache step {cold_us:.2f} us (1 GiB written between steps); "
+        f"device copy {copy_gbps:.0f} GB/s")
+
     # Per-kernel device times: events right before / after each launch.
     from scale_deformable_attention_amd._binding import (launch_event_names, launch_events_recorded,
                                                          set_launch_events)
@@ -421,6 +455,8 @@ def main():
                    "parallelism": "single GPU"},
         "timing": "graph replay" if graph_ok else "eager",
         "eager_us_per_step": round(eager_us, 3), "host_enqueue_us": round(host_us, 3),
+        "cold_us_per_step": round(cold_us, 3), "cold_flush_bytes": 1 << 30,
+        "device_copy_GBps": round(copy_gbps, 1),
         "fwd_us": round(ktimes["msda_fwd_kernel"], 3),
         "bwd_us": round(sum(v for k, v in ktimes.items() if k != "msda_fwd_kernel"), 3),
         "kernels": kernels, "touched_rows_U": U, "corners_C": C, "points_P": P,
