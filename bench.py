@@ -18,6 +18,8 @@ Prints one JSON line:
   kernels               per-kernel average device time and algorithmic GB/s
   roofline              the dominant kernel against the 8 TB/s HBM roofline:
                         algorithmic bytes per launch / average launch duration
+  phases                the forward and the backward call as wholes: their
+                        kernels' algorithmic bytes / summed launch times
   cold_us_per_step      context: one step timed alone after 1 GiB is written
                         (L2 and the 256 MB MALL evicted)
   device_copy_GBps      context: a 1 GiB device copy, bytes read + written / time
@@ -431,6 +433,17 @@ def main():
     kbytes["grad_sort_kernel"] = kbytes["msda_grad_kernel"] + kbytes["bin_local_sort"]
     kernels = {k: {"us": round(v, 3), "bytes": int(kbytes[k]),
                    "GBps": round(kbytes[k] / (v * 1e-6) / 1e9, 1)} for k, v in ktimes.items()}
+    # The forward call and the backward call as wholes: algorithmic bytes of
+    # their kernels over the sum of their launch times (event pairs), against
+    # the 8 TB/s peak.
+    phases = {}
+    for ph, names in (("forward", ["msda_fwd_kernel"]),
+                      ("backward", [k for k in ktimes if k != "msda_fwd_kernel"])):
+        t = sum(ktimes[k] for k in names)
+        by = sum(kbytes[k] for k in names)
+        phases[ph] = {"us": round(t, 3), "bytes": int(by),
+                      "GBps": round(by / (t * 1e-6) / 1e9, 1),
+                      "frac": round(by / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     kname = max(ktimes, key=ktimes.get)
     kus = ktimes[kname]
     achieved = kbytes[kname] / (kus * 1e-6) / 1e9
@@ -459,7 +472,7 @@ def main():
         "device_copy_GBps": round(copy_gbps, 1),
         "fwd_us": round(ktimes["msda_fwd_kernel"], 3),
         "bwd_us": round(sum(v for k, v in ktimes.items() if k != "msda_fwd_kernel"), 3),
-        "kernels": kernels, "touched_rows_U": U, "corners_C": C, "points_P": P,
+        "kernels": kernels, "phases": phases, "touched_rows_U": U, "corners_C": C, "points_P": P,
         "roofline": roofline,
     }
     if args.foil:

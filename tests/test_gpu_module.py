@@ -339,3 +339,35 @@ def test_module_graph_capture_replays_match_eager():
             assert torch.allclose(got[k], want[k], rtol=1e-5, atol=1e-6), (trial, k)
         for n, p in params.items():
             p.grad = static_grads[n]
+
+
+def test_sampling_prep_encoder_size_and_strided_inputs():
+    """The prep kernels at the encoder workload's size (711 K rows of L*K = 16
+    points, per-level reference points) against the oracle, with
+    non-contiguous inputs (the binding copies them to dense tensors)."""
+    from scale_deformable_attention_amd import msda_sampling_prep, msda_sampling_prep_backward
+    say("case prep encoder size, strided inputs")
+    levels = ((100, 167), (50, 84), (25, 42), (13, 21))
+    B, Q, M, K, L = 4, 22223, 8, 4, 4
+    g = torch.Generator().manual_seed(23)
+    ref = torch.rand(B, Q, L, 2, generator=g)
+    off = torch.randn(B, Q, M, L, K, 2, generator=g) * 2.0
+    logits = torch.randn(B, Q, M, L * K, generator=g)
+    gl = torch.randn(B, Q, M, L, K, 2, generator=g)
+    ga = torch.randn(B, Q, M, L, K, generator=g)
+    a = torch.softmax(torch.randn(B, Q, M, L * K, generator=g), -1).view(B, Q, M, L, K)
+    shapes = torch.tensor(levels)
+    # offsets as a transposed view: same values, non-contiguous on the device
+    off_t = off.to(DEV).transpose(0, 1).contiguous().transpose(0, 1)
+    assert not off_t.is_contiguous()
+    loc_g, attn_g = msda_sampling_prep(ref.to(DEV), off_t, logits.to(DEV), shapes)
+    g_ref, g_off, g_log = msda_sampling_prep_backward(a.to(DEV), gl.to(DEV), ga.to(DEV), shapes,
+                                                      ref_per_level=True)
+    torch.cuda.synchronize()
+    loc_o, attn_o = om.sampling_prep(ref, off, logits, shapes)
+    r_ref, r_off, r_log = om.sampling_prep_backward(a, gl, ga, shapes, ref_per_level=True)
+    check_slice("sampling_locations", to_np(loc_g), loc_o, 1e-5)
+    check_slice("attention_weights", to_np(attn_g), attn_o, 1e-5)
+    check_slice("grad_sampling_offsets", to_np(g_off), r_off, 1e-5)
+    check_slice("grad_attention_logits", to_np(g_log), r_log, 1e-5)
+    check_slice("grad_reference_points", to_np(g_ref), r_ref, 1e-5)
