@@ -982,10 +982,12 @@ static int make_prep(int dtype, int64_t B, int64_t Q, int64_t M, int64_t L, int6
         return fail(MSDA_ERR_SHAPE, "ref_per_level must be 0 or 1, got %d", ref_per_level);
     if (!shapes) return fail(MSDA_ERR_NULL_ARG, "spatial_shapes is NULL");
     int64_t rows = 0, pts = 0;
-    // rows * 64 lanes and 2 * rows * L * K elements must fit the launch and int64 indexing
-    if (!mul_ok(B, Q, &rows) || !mul_ok(rows, M, &rows) || !mul_ok(rows, L * K * 2, &pts) ||
-        rows >= ((int64_t)1 << 36))
+    // 2 * rows * L * K elements must fit int64 indexing, and rows * 64 lanes
+    // one launch (at most 2^31 - 1 workgroups of 256 threads)
+    if (!mul_ok(B, Q, &rows) || !mul_ok(rows, M, &rows) || !mul_ok(rows, L * K * 2, &pts))
         return fail(MSDA_ERR_SHAPE, "sampling tensor B*Q*M*L*K overflows");
+    if (rows >= ((int64_t)1 << 33))
+        return fail(MSDA_ERR_UNSUPPORTED, "B*Q*M = %lld rows exceed one launch", (long long)rows);
     p->dtype = dtype;
     p->B = B;
     p->Q = Q;

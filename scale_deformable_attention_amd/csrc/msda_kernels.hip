@@ -2044,6 +2044,7 @@ hipError_t launch_bin_local_sort(const Problem &p, const void *loc, const void *
     const size_t lds = (size_t)((max_level_bins + 1) / 2) * 4;
     const int64_t n16 = (int64_t)(zero_bytes / 16);
     const int64_t nzero = n16 > 0 ? std::min<int64_t>((n16 + kSortBlock - 1) / kSortBlock, 1024) : 0;
+    if (nseg + nzero >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
 #define MSDA_LSORT(T)                                                                          \
     hipLaunchKernelGGL((bin_local_sort_kernel<T>), dim3((unsigned)(nseg + nzero)),             \
                        dim3(kSortBlock), lds, stream, static_cast<const typename T::S *>(loc),  \

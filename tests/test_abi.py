@@ -258,7 +258,7 @@ def prep_bwd(lib, dtype=0, B=1, Q=16, M=2, L=2, K=2, shapes=SHAPES, per_level=0,
     ({"shapes": (ctypes.c_int64 * 4)(8, 1 << 24, 4, 5)}, 8),
     ({"ref": None}, 1), ({"logits": None}, 1), ({"attn": None}, 1),
     ({"off": ctypes.c_void_p(0x10002)}, 5), ({"dtype": 1, "loc": ctypes.c_void_p(0x10001)}, 5),
-    ({"B": 1 << 40, "Q": 1 << 30}, 2),
+    ({"B": 1 << 40, "Q": 1 << 30}, 2), ({"B": 1 << 20, "Q": 1 << 12, "M": 2048}, 8),
 ])
 def test_sampling_prep_rejects(lib, kw, status):
     assert prep(lib, **kw) == status, lib.msda_last_error().decode()
