@@ -1404,18 +1404,21 @@ __global__ __launch_bounds__(kScanBlock) void bin_tile_scan_kernel(uint32_t *__r
 // are exactly kAccGroups (row, replica) slots, slot s = row * rep + replica
 // belonging to lane group s, which sums its records in registers.
 //
-// Records come in rounds of kBlock, one per thread (the next round's load is
-// issued before the current round is processed), and each round is counting-
-// sorted by slot in LDS: four ballots on the slot bits give every record its
-// rank among the wave's records of the same slot, 16 lanes per wave publish
-// the wave's per-slot counts, one wave scans the 64 counts, and the records
-// are written in slot order. A group then reads its slot's records
+// Records come in rounds of kAccRPT * kBlock, kAccRPT per thread (the next
+// round's loads are issued before the current round is processed), and each
+// round is counting-sorted by slot in LDS: four ballots on the slot bits per
+// record index give every record its rank among the wave's records of the
+// same slot, 16 lanes per wave publish the wave's per-slot counts, one wave
+// scans the 64 counts, and the records are written in slot order. Two
+// records per thread halve the rounds, and with them the barriers and the
+// scan, per record; the sums per slot grow to twice the length. A group then reads its slot's records
 // contiguously, U at a time, with all their upstream-gradient loads (32-bit
 // offsets into a buffer over the batch's grad_output) issued before use. At
 // the end every group stores its sums to an LDS tile, the replicas of each
 // row are added, and the row is written (or added, with `accumulate`) to
 // grad_value, V channels per access.
 constexpr int kAccGroups = kBlock / 16;
+constexpr int kAccRPT = 2;  // records per thread in one counting-sort round
 
 #define MSDA_ACCUM_PARAMS                                                                     \
     const typename DT::S *__restrict__ grad_out, typename DT::S *__restrict__ grad_value,     \
@@ -1433,7 +1436,7 @@ __device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const 
     constexpr int G = 16;
     constexpr int U = J == 1 ? 16 : (J == 2 ? 8 : 4);
     constexpr int kWaves = kBlock / 64;
-    __shared__ uint2 sorted[kBlock];
+    __shared__ uint2 sorted[kAccRPT * kBlock];
     __shared__ uint32_t wcount[kAccGroups * kWaves];   // [slot][wave]
     __shared__ uint32_t woff[kAccGroups * kWaves + 1];  // exclusive prefix, slot-major
     const int64_t bm = bin / nbbm;
@@ -1471,31 +1474,62 @@ __device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const 
         for (int v = 0; v < SLOT; ++v) acc[j][v] = 0.0f;
 
     const uint32_t rb = starts[bin], re = ends[bin];
-    uint2 next = make_uint2(0u, 0u);
-    if (rb < re) next = records[rb + tid < re ? rb + tid : re - 1];  // (an empty bin reads nothing)
-    for (uint32_t base = rb; base < re; base += kBlock) {
-        const uint2 rec = next;
-        const bool valid = base + tid < re;
-        {
-            const uint32_t nb = base + kBlock + tid;
-            if (base + kBlock < re) next = records[nb < re ? nb : re - 1];
+    // kAccRPT records per thread per round; record k of a round is
+    // base + k * kBlock + tid (the next round's are loaded before this one is
+    // processed; an empty bin reads nothing)
+    uint2 next[kAccRPT];
+#pragma unroll
+    for (int k = 0; k < kAccRPT; ++k) {
+        const uint32_t i = rb + k * kBlock + tid;
+        next[k] = rb < re ? records[i < re ? i : re - 1] : make_uint2(0u, 0u);
+    }
+    for (uint32_t base = rb; base < re; base += kAccRPT * kBlock) {
+        uint2 rec[kAccRPT];
+        bool valid[kAccRPT];
+        uint32_t slot[kAccRPT];
+#pragma unroll
+        for (int k = 0; k < kAccRPT; ++k) {
+            rec[k] = next[k];
+            const uint32_t i = base + k * kBlock + tid;
+            valid[k] = i < re;
+            const uint32_t ni = i + kAccRPT * kBlock;
+            if (base + kAccRPT * kBlock < re) next[k] = records[ni < re ? ni : re - 1];
+            uint32_t rr = rec[k].x & 15u;
+            rr = rr < (uint32_t)rows ? rr : 0u;  // keeps every access in range
+            slot[k] = (rr << log2rep) | (i & ((1u << log2rep) - 1u));
         }
-        uint32_t rr = rec.x & 15u;
-        rr = rr < (uint32_t)rows ? rr : 0u;  // keeps every access in range
-        const uint32_t slot = (rr << log2rep) | ((base + tid) & ((1u << log2rep) - 1u));
-        // lanes of this wave holding a record of the same slot
-        const uint64_t vb = __ballot(valid);
-        const uint64_t b0 = __ballot(slot & 1u), b1 = __ballot(slot & 2u);
-        const uint64_t b2 = __ballot(slot & 4u), b3 = __ballot(slot & 8u);
-        auto same = [&](uint32_t sl) {
-            return vb & ((sl & 1u) ? b0 : ~b0) & ((sl & 2u) ? b1 : ~b1) & ((sl & 4u) ? b2 : ~b2) &
-                   ((sl & 8u) ? b3 : ~b3);
+        // lanes of this wave holding a record of the same slot, per record
+        // index k; records k' < k of a slot come first in the slot's run
+        uint64_t vb[kAccRPT], sb[kAccRPT][4];
+#pragma unroll
+        for (int k = 0; k < kAccRPT; ++k) {
+            vb[k] = __ballot(valid[k]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sb[k][t] = __ballot((slot[k] >> t) & 1u);
+        }
+        auto same = [&](int k, uint32_t sl) {
+            uint64_t mk = vb[k];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) mk &= ((sl >> t) & 1u) ? sb[k][t] : ~sb[k][t];
+            return mk;
         };
-        const uint64_t mine = same(slot);
-        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
-            (uint32_t)(mine >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mine, 0u));
+        uint32_t rank[kAccRPT];
+#pragma unroll
+        for (int k = 0; k < kAccRPT; ++k) {
+            const uint64_t mine = same(k, slot[k]);
+            uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(mine >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mine, 0u));
+#pragma unroll
+            for (int k2 = 0; k2 < k; ++k2) r += (uint32_t)__popcll(same(k2, slot[k]));
+            rank[k] = r;
+        }
         __syncthreads();  // the previous round's sorted records and offsets consumed
-        if (lane < kAccGroups) wcount[lane * kWaves + wave] = (uint32_t)__popcll(same((uint32_t)lane));
+        if (lane < kAccGroups) {
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int k = 0; k < kAccRPT; ++k) cnt += (uint32_t)__popcll(same(k, (uint32_t)lane));
+            wcount[lane * kWaves + wave] = cnt;
+        }
         __syncthreads();
         if (wave == 0) {  // exclusive scan of the 64 counts, slot-major
             const uint32_t x = wcount[lane];
@@ -1509,7 +1543,9 @@ __device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const 
             if (lane == 63) woff[64] = inc;
         }
         __syncthreads();
-        if (valid) sorted[woff[slot * kWaves + wave] + rank] = rec;
+#pragma unroll
+        for (int k = 0; k < kAccRPT; ++k)
+            if (valid[k]) sorted[woff[slot[k] * kWaves + wave] + rank[k]] = rec[k];
         __syncthreads();
         const uint32_t first = woff[gid * kWaves], n = woff[gid * kWaves + kWaves] - first;
         for (uint32_t i0 = 0; __ballot(i0 < n); i0 += U) {
