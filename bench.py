@@ -171,7 +171,7 @@ def time_graph(fn, reps: int, inner: int) -> float:
     return e0.elapsed_time(e1) * 1e3 / (reps * inner)  # us
 
 
-def cpu_baseline(inp, min_seconds: float = 10.0, max_reps: int = 200):
+def cpu_baseline(inp, min_seconds: float = 10.0, max_reps: int = 2000):
     import oracle  # the CPU-baseline leg is the only product-side user of the oracle
     args = (inp["value"], inp["spatial_shapes"], None, inp["sampling_locations"],
             inp["attention_weights"])

@@ -1428,13 +1428,23 @@ constexpr int kAccRPT = 2;  // records per thread in one counting-sort round
         const int accumulate
 #define MSDA_ACCUM_ARGS grad_out, grad_value, starts, ends, records, lt, S, Q, M, D, L, nbbm, accumulate
 
+// With WIDE (rows of exactly 64 bytes, J == 1) a group reads four records at
+// a time instead of one: its lanes form four sub-groups of 4, sub-group r
+// takes records r, r + 4, ... of the slot and each lane gathers 16 bytes of
+// the row, as the forward does, so one load instruction of a wave covers 16
+// records rather than 4; the sub-groups' sums are added with two cross-lane
+// steps once per bin.
+//
 // `tile`: kAccGroups x D floats of LDS (the kernel's dynamic LDS).
-template <class DT, int SLOT, int J, int V>
+template <class DT, int SLOT, int J, int V, bool WIDE>
 __device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const int64_t bin) {
     using E = typename DT::S;
     using R = typename RawVec<SLOT * (int)sizeof(E)>::type;
+    static_assert(!WIDE || (J == 1 && SLOT * sizeof(E) == 4), "wide mode: 64-byte rows");
     constexpr int G = 16;
     constexpr int U = J == 1 ? 16 : (J == 2 ? 8 : 4);
+    constexpr int VW = 16 / (int)sizeof(E);  // elements per 16-byte gather (wide mode)
+    constexpr int UW = 4;                    // records per sub-group in flight (wide mode)
     constexpr int kWaves = kBlock / 64;
     __shared__ uint2 sorted[kAccRPT * kBlock];
     __shared__ uint32_t wcount[kAccGroups * kWaves];   // [slot][wave]
@@ -1472,6 +1482,11 @@ __device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const 
     for (int j = 0; j < J; ++j)
 #pragma unroll
         for (int v = 0; v < SLOT; ++v) acc[j][v] = 0.0f;
+    float accw[VW];
+#pragma unroll
+    for (int v = 0; v < VW; ++v) accw[v] = 0.0f;
+    const int sub = c >> 2;                     // wide mode: record of four
+    const uint32_t lbytes = (uint32_t)(c & 3) * 16u;  // wide mode: 16-byte chunk of the row
 
     const uint32_t rb = starts[bin], re = ends[bin];
     // kAccRPT records per thread per round; record k of a round is
@@ -1548,14 +1563,54 @@ __device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const 
             if (valid[k]) sorted[woff[slot[k] * kWaves + wave] + rank[k]] = rec[k];
         __syncthreads();
         const uint32_t first = woff[gid * kWaves], n = woff[gid * kWaves + kWaves] - first;
+        // a record past the slot's end reads neither LDS past the round nor
+        // its row: coefficient 0 and a zero row, whatever grad_output holds
+        if constexpr (WIDE) {
+            for (uint32_t i0 = 0; __ballot(i0 < n); i0 += 4 * UW) {
+                float coef[UW];
+                uint32_t qo[UW];
+                bool okr[UW];
+#pragma unroll
+                for (int u = 0; u < UW; ++u) {
+                    const uint32_t idx = i0 + 4 * u + sub;
+                    okr[u] = idx < n;
+                    const uint2 rc = sorted[okr[u] ? first + idx : 0u];
+                    coef[u] = __uint_as_float(rc.y & (0u - (uint32_t)okr[u]));
+                    const uint32_t rq = rc.x >> 4;
+                    qo[u] = (rq < (uint64_t)Q ? rq : 0u) * row_bytes + lbytes;
+                }
+                uint4 gr[UW];
+#pragma unroll
+                for (int u = 0; u < UW; ++u) gr[u] = gslice.template gather<uint4>(qo[u], okr[u]);
+                __builtin_amdgcn_sched_barrier(0);  // every gather issued before any use
+#pragma unroll
+                for (int u = 0; u < UW; ++u) {
+                    float gv[VW];
+                    if constexpr (std::is_same<DT, BF16T>::value) {
+                        const uint32_t w4[4] = {gr[u].x, gr[u].y, gr[u].z, gr[u].w};
+#pragma unroll
+                        for (int h = 0; h < 4; ++h) {  // bf16 pair -> two floats
+                            gv[2 * h] = __uint_as_float(w4[h] << 16);
+                            gv[2 * h + 1] = __uint_as_float(w4[h] & 0xFFFF0000u);
+                        }
+                    } else {
+                        raw_to_f32<DT, VW>(gr[u], gv);
+                    }
+#pragma unroll
+                    for (int v = 0; v < VW; ++v) accw[v] = __builtin_fmaf(coef[u], gv[v], accw[v]);
+                }
+            }
+            continue;
+        }
         for (uint32_t i0 = 0; __ballot(i0 < n); i0 += U) {
             float coef[U];
             uint32_t qo[U];
+            bool okr[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const bool ok = i0 + u < n;
-                const uint2 rc = sorted[first + (ok ? i0 + u : 0u)];
-                coef[u] = ok ? __uint_as_float(rc.y) : 0.0f;
+                okr[u] = i0 + u < n;
+                const uint2 rc = sorted[okr[u] ? first + i0 + u : 0u];
+                coef[u] = okr[u] ? __uint_as_float(rc.y) : 0.0f;
                 const uint32_t rq = rc.x >> 4;
                 qo[u] = (rq < (uint64_t)Q ? rq : 0u) * row_bytes;
             }
@@ -1563,7 +1618,8 @@ __device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const 
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int j = 0; j < J; ++j) gr[u][j] = gslice.template gather<R>(qo[u] + soff[j], slot_ok[j]);
+                for (int j = 0; j < J; ++j)
+                    gr[u][j] = gslice.template gather<R>(qo[u] + soff[j], slot_ok[j] && okr[u]);
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -1576,11 +1632,22 @@ __device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const 
         }
     }
     // every group's sums (zeros for a group without records) -> tile row gid
+    if constexpr (WIDE) {
 #pragma unroll
-    for (int j = 0; j < J; ++j)
-        if (slot_ok[j])
+        for (int v = 0; v < VW; ++v) {
+            accw[v] += __shfl_xor(accw[v], 4);
+            accw[v] += __shfl_xor(accw[v], 8);
+        }
+        if (sub == 0)
 #pragma unroll
-            for (int v = 0; v < SLOT; ++v) tile[gid * D + (c + j * G) * SLOT + v] = acc[j][v];
+            for (int v = 0; v < VW; ++v) tile[gid * D + (c & 3) * VW + v] = accw[v];
+    } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (slot_ok[j])
+#pragma unroll
+                for (int v = 0; v < SLOT; ++v) tile[gid * D + (c + j * G) * SLOT + v] = acc[j][v];
+    }
     __syncthreads();
     E *dst = grad_value + ((b * S + lt.start[l] + r0) * M + m) * (int64_t)D;
     const int vpr = D / V;
@@ -1606,7 +1673,7 @@ __device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const 
     }
 }
 
-template <class DT, int SLOT, int J, int V>
+template <class DT, int SLOT, int J, int V, bool WIDE>
 __global__ __launch_bounds__(kBlock) void bin_accum_kernel(
     const typename DT::S *__restrict__ grad_out, typename DT::S *__restrict__ grad_value,
     const uint32_t *__restrict__ starts, const uint32_t *__restrict__ ends,
@@ -1616,7 +1683,7 @@ __global__ __launch_bounds__(kBlock) void bin_accum_kernel(
     extern __shared__ float dyn_tile[];  // kAccGroups x D
     const int64_t bin = logical_block();  // neighbouring bins share upstream-gradient rows
     if (bin >= nbins) return;
-    accum_bin<DT, SLOT, J, V>(dyn_tile, MSDA_ACCUM_ARGS, bin);
+    accum_bin<DT, SLOT, J, V, WIDE>(dyn_tile, MSDA_ACCUM_ARGS, bin);
 }
 
 // The unbinned levels' atomic scatter and the binned levels' accumulation in
@@ -1627,7 +1694,7 @@ __global__ __launch_bounds__(kBlock) void bin_accum_kernel(
 // R = gridDim / 8 rows, Rs = nsc / 8 scatter and the others accumulate,
 // spread evenly over the grid so both run from the start; within each role
 // the XCD-aware order is that of its own kernel (nsc is a multiple of 8).
-template <class DT, class PT, int SLOT, int J, int V>
+template <class DT, class PT, int SLOT, int J, int V, bool WIDE>
 __global__ __launch_bounds__(kBlock) void scatter_accum_kernel(
     const typename PT::S *__restrict__ loc, const typename PT::S *__restrict__ attn,
     const typename DT::S *__restrict__ grad_out, void *__restrict__ grad_value,
@@ -1650,7 +1717,7 @@ __global__ __launch_bounds__(kBlock) void scatter_accum_kernel(
         const int64_t bin = (int64_t)xcd * (R - Rs) + (r - k);
         if (bin < nbins) {
             typename DT::S *gv = static_cast<typename DT::S *>(grad_value);
-            accum_bin<DT, SLOT, J, V>(dyn_tile, grad_out, gv, starts, ends, records, lt, S, Q, M,
+            accum_bin<DT, SLOT, J, V, WIDE>(dyn_tile, grad_out, gv, starts, ends, records, lt, S, Q, M,
                                       D, L, nbbm, accumulate, bin);
         }
     }
@@ -1799,18 +1866,39 @@ hipError_t bwd_launch(const Problem &p, const BwdMapping &mp, const void *value,
     return hipGetLastError();
 }
 
-template <class DT, int SLOT, int J, int V>
-hipError_t accum_launch_v(const Problem &p, const BwdMapping &mp, const void *grad_out,
+// The accumulation reads 16 bytes per lane when a row is exactly 64 bytes
+// (J == 1) and grad_output is 16-byte aligned.
+template <class DT, int SLOT, int J>
+bool accum_wide(const Problem &p, const void *grad_out) {
+    constexpr int e = (int)sizeof(typename DT::S);
+    return J == 1 && SLOT * e == 4 && p.D * e == 64 &&
+           reinterpret_cast<uintptr_t>(grad_out) % 16 == 0;
+}
+
+template <class DT, int SLOT, int J, int V, bool WIDE>
+hipError_t accum_launch_w(const Problem &p, const BwdMapping &mp, const void *grad_out,
                           void *grad_value, const BinnedBuffers &bins, bool accumulate,
                           hipStream_t stream) {
     using E = typename DT::S;
     const size_t lds = (size_t)kAccGroups * (size_t)p.D * sizeof(float);
     const int64_t per_xcd = (bins.nbins + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((bin_accum_kernel<DT, SLOT, J, V>), dim3((unsigned)(per_xcd * kXcds)),
+    hipLaunchKernelGGL((bin_accum_kernel<DT, SLOT, J, V, WIDE>), dim3((unsigned)(per_xcd * kXcds)),
                        dim3(kBlock), lds, stream, static_cast<const E *>(grad_out),
                        static_cast<E *>(grad_value), bins.starts, bins.ends, bins.records, p.levels, p.S,
                        p.Q, (int)p.M, (int)p.D, (int)p.L, p.nbbm, bins.nbins, (int)accumulate);
     return hipGetLastError();
+}
+
+template <class DT, int SLOT, int J, int V>
+hipError_t accum_launch_v(const Problem &p, const BwdMapping &mp, const void *grad_out,
+                          void *grad_value, const BinnedBuffers &bins, bool accumulate,
+                          hipStream_t stream) {
+    if constexpr (J == 1 && SLOT * sizeof(typename DT::S) == 4)
+        if (accum_wide<DT, SLOT, J>(p, grad_out))
+            return accum_launch_w<DT, SLOT, J, V, true>(p, mp, grad_out, grad_value, bins,
+                                                        accumulate, stream);
+    return accum_launch_w<DT, SLOT, J, V, false>(p, mp, grad_out, grad_value, bins, accumulate,
+                                                 stream);
 }
 
 // Write-back width: the widest of 16, 8, 4 bytes (or one element) that
@@ -2097,7 +2185,7 @@ hipError_t launch_bin_local_sort(const Problem &p, const void *loc, const void *
     return hipGetLastError();
 }
 
-template <class DT, class PT, int J>
+template <class DT, class PT, int J, bool WIDE>
 hipError_t scatter_accum_launch(const Problem &p, const BwdMapping &mp, const void *loc,
                                 const void *attn, const void *grad_out, void *grad_value,
                                 const BinnedBuffers &bins, bool accumulate, hipStream_t stream) {
@@ -2111,7 +2199,7 @@ hipError_t scatter_accum_launch(const Problem &p, const BwdMapping &mp, const vo
     const int64_t nacc = (bins.nbins + kXcds - 1) / kXcds * kXcds;
     if (nsc + nacc >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const size_t lds = (size_t)kAccGroups * (size_t)p.D * sizeof(float);
-    hipLaunchKernelGGL((scatter_accum_kernel<DT, PT, 2, J, V>), dim3((unsigned)(nsc + nacc)),
+    hipLaunchKernelGGL((scatter_accum_kernel<DT, PT, 2, J, V, WIDE>), dim3((unsigned)(nsc + nacc)),
                        dim3(kBlock), lds, stream, static_cast<const P *>(loc),
                        static_cast<const P *>(attn), static_cast<const E *>(grad_out), grad_value,
                        p.levels, p.S, p.Q, (int)p.M, (int)p.D, (int)p.L, (int)p.K, qblocks, ntiles,
@@ -2125,9 +2213,12 @@ hipError_t scatter_accum_by_j(const Problem &p, const BwdMapping &mp, const void
                               const void *attn, const void *grad_out, void *grad_value,
                               const BinnedBuffers &bins, bool accumulate, hipStream_t stream) {
     switch (mp.j) {
-        case 1: return scatter_accum_launch<DT, PT, 1>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
-        case 2: return scatter_accum_launch<DT, PT, 2>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
-        case 4: return scatter_accum_launch<DT, PT, 4>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
+        case 1:
+            if (accum_wide<DT, 2, 1>(p, grad_out))
+                return scatter_accum_launch<DT, PT, 1, true>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
+            return scatter_accum_launch<DT, PT, 1, false>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
+        case 2: return scatter_accum_launch<DT, PT, 2, false>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
+        case 4: return scatter_accum_launch<DT, PT, 4, false>(p, mp, loc, attn, grad_out, grad_value, bins, accumulate, stream);
         default: return hipErrorInvalidValue;
     }
 }
