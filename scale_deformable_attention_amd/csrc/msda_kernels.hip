@@ -981,6 +981,7 @@ __global__ __launch_bounds__(kBlock) void msda_scatter_kernel(
 constexpr int kHashBits = 11;
 constexpr int kHashSlots = 1 << kHashBits;   // > 4 corners x kBlock points: never full
 constexpr uint32_t kEmptyKey = 0xFFFFFFFFu;  // bin ids stay below 2^31
+constexpr int kRankedKeys = 256;             // bins per workgroup visited in key order
 
 // One thread per point of a binned level of one (b, m): workgroup w of pair bm
 // takes the (query, binned point) indices [w * kBlock, (w + 1) * kBlock) of
@@ -1001,6 +1002,8 @@ __global__ __launch_bounds__(kBlock) void bin_sort_kernel(
     __shared__ uint32_t cnt[kHashSlots];
     __shared__ uint16_t used[4 * kBlock];
     __shared__ uint32_t nused;
+    __shared__ uint32_t ukey[kRankedKeys];
+    __shared__ uint16_t order[kRankedKeys];
     const int64_t wg = logical_block();
     if (wg >= ntiles) return;
     const int tid = threadIdx.x;
@@ -1060,8 +1063,26 @@ __global__ __launch_bounds__(kBlock) void bin_sort_kernel(
     }
     __syncthreads();
     const uint32_t nu = nused;
+    // One atomic request covers every lane of an instruction that falls in
+    // the same 64-byte segment, i.e. 16 neighbouring bin counters. Visiting
+    // the workgroup's bins in key order lets lanes with neighbouring bins
+    // share requests; keys are ranked by counting when there are at most
+    // kRankedKeys of them (local sampling patterns give a few dozen),
+    // otherwise the insertion order stands.
+    const bool ranked = nu <= (uint32_t)kRankedKeys;  // uniform over the workgroup
+    if (ranked) {
+        if (tid < nu) ukey[tid] = keys[used[tid]];
+        __syncthreads();
+        if (tid < nu) {
+            const uint32_t k = ukey[tid];
+            uint32_t rk = 0u;
+            for (uint32_t j = 0; j < nu; ++j) rk += ukey[j] < k ? 1u : 0u;
+            order[rk] = used[tid];  // keys are distinct: ranks are a permutation
+        }
+        __syncthreads();
+    }
     for (uint32_t u = tid; u < nu; u += kBlock) {
-        const uint32_t h = used[u];
+        const uint32_t h = ranked ? order[u] : used[u];
         if constexpr (PLACE)
             cnt[h] = __hip_atomic_fetch_add(counter + keys[h], cnt[h], __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
