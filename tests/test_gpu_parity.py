@@ -539,3 +539,45 @@ def test_sort_paths_at_their_limits(case):
     _, _, ref_grads, trows = oracle_run(inp)
     check_backward(dtype, grads, ref_grads, inp["spatial_shapes"], None, trows,
                    **atomic_level_rules(dtype, accum, inp))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=str)
+@pytest.mark.parametrize("accum", ["auto", "binned", "native"])
+def test_non_finite_upstream_gradient_stays_local(dtype, accum):
+    """An infinite upstream gradient at one (batch, query, head) makes
+    non-finite exactly the grad_value entries that the oracle makes
+    non-finite (the rows that query's in-bounds corners of that head land
+    on) and that query's own location and weight gradients; every other
+    entry is finite and matches the oracle. Guards the lanes of the binned
+    accumulation that hold no record: they must read no upstream-gradient
+    row, whatever it holds. Q*K = 2400 takes the count / scan / place chain."""
+    wl = workload("decoder_bf16").replace(name="decoder_q600", dtype=dtype, B=1, Q=600, seed=23)
+    inp = make_inputs(wl)
+    D, m_bad, q_bad = wl.D, 3, 7
+    go = inp["grad_output"].clone()
+    go[0, q_bad, m_bad * D:(m_bad + 1) * D] = float("inf")
+    inp["grad_output"] = go
+    say(f"case non-finite grad_output {dtype} accum={accum}")
+    _, _, (gv_ref, gl_ref, ga_ref), _ = oracle_run(inp)
+    g = to_dev(inp)
+    got = msda_backward(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                        g["attention_weights"], g["grad_output"], accum=accum)
+    torch.cuda.synchronize()
+    tol = 1e-5 if dtype == torch.float32 else 2e-2
+    for name, t, ref in zip(("grad_value", "grad_sampling_locations",
+                             "grad_attention_weights"), got, (gv_ref, gl_ref, ga_ref)):
+        a = t.detach().float().cpu().numpy().astype(np.float64)
+        ref = np.asarray(ref, dtype=np.float64).reshape(a.shape)
+        fin, fin_ref = np.isfinite(a), np.isfinite(ref)
+        assert (~fin_ref).any(), f"{name}: the oracle has no non-finite entry"
+        assert np.array_equal(fin, fin_ref), \
+            f"{name}: {int((fin != fin_ref).sum())} entries differ in finiteness"
+        if name == "grad_value":  # only head m_bad is touched (B = 1)
+            assert not np.delete(~fin, m_bad, axis=2).any()
+        else:  # only query q_bad, head m_bad
+            bad = ~fin.reshape(1, wl.num_queries, wl.M, -1)
+            assert bad[0, q_bad, m_bad].any()
+            bad[0, q_bad, m_bad] = False
+            assert not bad.any()
+        err = np.linalg.norm(a[fin] - ref[fin]) / max(np.linalg.norm(ref[fin]), 1e-300)
+        assert err <= tol, f"{name}: normwise error {err:.3e} on the finite entries"
