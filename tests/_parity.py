@@ -130,6 +130,28 @@ def _normwise(name, got, want, tol):
     return nw
 
 
+def check_grad_value_level(name, got, want, tol, normwise=False, outliers=False) -> dict:
+    """One level's grad_value rows: elementwise within `tol`; for a level
+    accumulated with 16-bit atomics, normwise only (`normwise`: bf16 on a
+    contended level), or at most max(1, 1e-5 n) rounding outliers with the
+    normwise bound (`outliers`)."""
+    got, want = np.asarray(got).ravel(), np.asarray(want).ravel()
+    if normwise:
+        nw = _normwise(name, got, want, tol)
+        return {"name": name + " normwise", "n": got.size, "max_scaled": float("nan"),
+                "normwise": nw}
+    if outliers and want.size:
+        rms = float(np.sqrt(np.mean(want * want)))
+        bad = ~(np.abs(got - want) <= tol * (np.abs(want) + rms))
+        if bad.any():
+            assert bad.sum() <= max(1, int(1e-5 * want.size)), \
+                f"{name}: {int(bad.sum())}/{want.size} elements outside tol (16-bit atomics)"
+            nw = _normwise(name, got, want, tol)
+            return {"name": name + f" ({int(bad.sum())} rounding outliers)", "n": got.size,
+                    "max_scaled": float("nan"), "normwise": nw}
+    return check_slice(name, got, want, tol)
+
+
 def check_backward(dtype, gpu, ref, spatial_shapes, level_start_index=None,
                    touched_rows=None, param_dtype=None, normwise_levels=(),
                    outlier_levels=()) -> list:
@@ -146,26 +168,10 @@ def check_backward(dtype, gpu, ref, spatial_shapes, level_start_index=None,
             tol[k] = TOL[param_dtype][k]
     stats = [check_slice("grad_attention_weights", ga, rga, tol["grad_attention_weights"])]
     for l, (r0, r1) in enumerate(level_row_ranges(spatial_shapes, level_start_index)):
-        name = f"grad_value[level {l}]"
-        got, want = gv[:, r0:r1].ravel(), rgv[:, r0:r1].ravel()
-        if l in normwise_levels:
-            nw = _normwise(name, got, want, tol["grad_value"])
-            stats.append({"name": name + " normwise", "n": got.size,
-                          "max_scaled": float("nan"), "normwise": nw})
-        elif l in outlier_levels and want.size:
-            rms = float(np.sqrt(np.mean(want * want)))
-            bad = ~(np.abs(got - want) <= tol["grad_value"] * (np.abs(want) + rms))
-            if bad.any():
-                assert bad.sum() <= max(1, int(1e-5 * want.size)), \
-                    f"{name}: {int(bad.sum())}/{want.size} elements outside tol (16-bit atomics)"
-                nw = _normwise(name, got, want, tol["grad_value"])
-                stats.append({"name": name + f" ({int(bad.sum())} rounding outliers)",
-                              "n": got.size, "max_scaled": float("nan"), "normwise": nw})
-            else:
-                stats.append(check_slice(name, got, want, tol["grad_value"]))
-        else:
-            stats.append(check_slice(f"grad_value[level {l}]", gv[:, r0:r1], rgv[:, r0:r1],
-                                     tol["grad_value"]))
+        stats.append(check_grad_value_level(f"grad_value[level {l}]", gv[:, r0:r1],
+                                            rgv[:, r0:r1], tol["grad_value"],
+                                            normwise=l in normwise_levels,
+                                            outliers=l in outlier_levels))
         stats.append(check_slice(f"grad_sampling_locations[level {l}]", gl[:, :, :, l],
                                  rgl[:, :, :, l], tol["grad_sampling_locations"]))
     if touched_rows is not None:
