@@ -144,7 +144,7 @@ DTYPES = [torch.float32, torch.float16, torch.bfloat16]
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=str)
-@pytest.mark.parametrize("D", [1, 3, 8, 24, 32, 48, 64, 128, 256])
+@pytest.mark.parametrize("D", [1, 3, 8, 16, 24, 32, 48, 64, 128, 256])
 def test_head_dims_and_ragged_queries(dtype, D):
     wl, inp = _small(dtype, D=D)
     say(f"case head_dim D={D} {dtype} Q={wl.Q}")
@@ -224,6 +224,27 @@ def test_misaligned_pointers_fall_back_to_narrow_access(dtype):
     torch.cuda.synchronize()
     check_backward(dtype, (gv.cpu(), gl.cpu(), ga.cpu()), ref_grads, inp["spatial_shapes"], None,
                    trows)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("accum", ["auto", "mixed", "binned"])
+def test_grad_output_off_16_byte_alignment(dtype, accum):
+    """grad_output two elements into a buffer (4-byte aligned, not 16): the
+    accumulation reads it 4 bytes per lane instead of 16 (64-byte rows), in
+    the launch shared with the atomic scatter and in the standalone one."""
+    wl, inp = _small(dtype, D=32, Q=150, M=2, K=4, levels=((20, 30), (6, 9), (3, 4)))
+    say(f"case grad_output 4-byte aligned {dtype} {accum}")
+    _, _, ref_grads, trows = oracle_run(inp)
+    g = to_dev(inp)
+    buf = torch.empty(g["grad_output"].numel() + 2, dtype=dtype, device=DEV)
+    go = buf[2:].view(g["grad_output"].shape)
+    go.copy_(g["grad_output"])
+    assert go.data_ptr() % 16 != 0 and go.data_ptr() % 4 == 0
+    grads = msda_backward(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                          g["attention_weights"], go, accum=accum)
+    torch.cuda.synchronize()
+    check_backward(dtype, tuple(t.cpu() for t in grads), ref_grads, inp["spatial_shapes"], None,
+                   trows, **atomic_level_rules(dtype, accum, inp))
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=str)
