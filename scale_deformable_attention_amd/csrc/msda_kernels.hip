@@ -254,6 +254,14 @@ struct Cell {
 __device__ __forceinline__ Cell map_cell(float loc_x, float loc_y, float Hf, float Wf, int W,
                                          int64_t start) {
     Cell c;
+    // A non-finite coordinate, or one beyond 1e30 in magnitude (whose product
+    // with the level size could overflow), becomes -4 (normalised), outside
+    // the level in that dimension like the coordinate it replaces: the point
+    // then has no in-bounds corner and finite weights, so it adds exactly 0
+    // to every result (left as it is, its NaN weights would make NaN of the
+    // zero corners they multiply). Other coordinates pass unchanged.
+    loc_x = __builtin_fabsf(loc_x) <= 1.0e30f ? loc_x : -4.0f;
+    loc_y = __builtin_fabsf(loc_y) <= 1.0e30f ? loc_y : -4.0f;
     // x = loc_x * W - 0.5 with a single rounding (README "Kernel design").
     const float xf = __builtin_fmaf(loc_x, Wf, -0.5f);
     const float yf = __builtin_fmaf(loc_y, Hf, -0.5f);

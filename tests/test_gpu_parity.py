@@ -610,3 +610,38 @@ def test_non_finite_upstream_gradient_stays_local(dtype, accum):
             assert not bad.any()
         err = np.linalg.norm(a[fin] - ref[fin]) / max(np.linalg.norm(ref[fin]), 1e-300)
         assert err <= tol, f"{name}: normwise error {err:.3e} on the finite entries"
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("accum", ["auto", "binned", "native"])
+def test_non_finite_locations_are_out_of_bounds(dtype, accum):
+    """A NaN, infinite or huge sampling coordinate puts its point outside the level:
+    every result equals the oracle's with that coordinate moved far out of
+    bounds (-10), i.e. the point adds exactly 0 to the output and to
+    grad_value, and its own location and weight gradients are 0. (The oracle
+    itself refuses non-finite locations; the substitution pins the reading
+    that they count as out of bounds.)"""
+    wl, inp = _small(dtype, D=32, Q=40, M=2, K=4, levels=((12, 16), (6, 8), (3, 4)))
+    nan, inf = float("nan"), float("inf")
+    bad = [((0, 3, 1, 0, 2, 0), nan), ((0, 5, 0, 1, 1, 1), inf), ((1, 7, 1, 2, 3, 0), -inf),
+           ((1, 9, 0, 0, 0, 0), nan), ((1, 9, 0, 0, 0, 1), nan), ((0, 11, 1, 2, 0, 1), -inf),
+           ((0, 13, 0, 1, 2, 0), 1e38)]  # finite, but its product with W overflows fp32
+    loc, sub = inp["sampling_locations"].clone(), inp["sampling_locations"].clone()
+    for idx, v in bad:
+        loc[idx] = v
+        sub[idx] = -10.0
+    ref_inp = dict(inp, sampling_locations=sub)
+    say(f"case non-finite locations {dtype} accum={accum}")
+    ref_out, touched, ref_grads, trows = oracle_run(ref_inp)
+    g = to_dev(dict(inp, sampling_locations=loc))
+    out = msda_forward(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                       g["attention_weights"])
+    grads = msda_backward(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                          g["attention_weights"], g["grad_output"], accum=accum)
+    torch.cuda.synchronize()
+    check_forward(dtype, out.cpu(), ref_out, touched)
+    grads = tuple(t.cpu() for t in grads)
+    check_backward(dtype, grads, ref_grads, inp["spatial_shapes"], None, trows,
+                   **atomic_level_rules(dtype, accum, ref_inp))
+    for idx, _ in bad:
+        assert float(grads[1][idx[:5]].abs().max()) == 0.0 and float(grads[2][idx[:5]]) == 0.0
