@@ -986,14 +986,16 @@ __global__ __launch_bounds__(kBlock) void msda_scatter_kernel(
 // of one (b, m) fall into few bins, so counters of heavily shared coarse
 // levels see little contention.
 
-constexpr int kHashBits = 11;
-constexpr int kHashSlots = 1 << kHashBits;   // > 4 corners x kBlock points: never full
+constexpr int kBinBlock = 512;  // threads (one point each) of the count / place workgroups
+constexpr int kHashBits = 12;
+constexpr int kHashSlots = 1 << kHashBits;   // > 4 corners x kBinBlock points: never full
 constexpr uint32_t kEmptyKey = 0xFFFFFFFFu;  // bin ids stay below 2^31
 constexpr int kRankedKeys = 256;             // bins per workgroup visited in key order
 
 // One thread per point of a binned level of one (b, m): workgroup w of pair bm
-// takes the (query, binned point) indices [w * kBlock, (w + 1) * kBlock) of
-// that pair. Count
+// takes the (query, binned point) indices [w * kBinBlock, (w + 1) * kBinBlock)
+// of that pair (512 points: more corners share each (workgroup, bin) atomic,
+// at the 32 waves per CU that the 37.5 KB of LDS leaves). Count
 // (PLACE = false) adds the workgroup's per-bin totals to counter[bin]. Place
 // (PLACE = true) reserves a range of each bin with one returning atomic on
 // counter[bin] (the bin's cursor, initialised to its start by the scan) and
@@ -1001,21 +1003,21 @@ constexpr int kRankedKeys = 256;             // bins per workgroup visited in ke
 // 16 rows), y = fp32 bits of A * w_ij. Both derive cells with the same map_cell as the backward, so they
 // agree on every in-bounds corner.
 template <class DT, bool PLACE>
-__global__ __launch_bounds__(kBlock) void bin_sort_kernel(
+__global__ __launch_bounds__(kBinBlock) void bin_sort_kernel(
     const typename DT::S *__restrict__ loc, const typename DT::S *__restrict__ attn,
     const LevelTable lt, uint32_t *__restrict__ counter, uint2 *__restrict__ records,
     const int64_t Q, const int M, const int L, const int K, const int64_t nbbm,
     const int64_t wpb, const int64_t ntiles) {
     __shared__ uint32_t keys[kHashSlots];
     __shared__ uint32_t cnt[kHashSlots];
-    __shared__ uint16_t used[4 * kBlock];
+    __shared__ uint16_t used[4 * kBinBlock];
     __shared__ uint32_t nused;
     __shared__ uint32_t ukey[kRankedKeys];
     __shared__ uint16_t order[kRankedKeys];
     const int64_t wg = logical_block();
     if (wg >= ntiles) return;
     const int tid = threadIdx.x;
-    for (int i = tid; i < kHashSlots; i += kBlock) {
+    for (int i = tid; i < kHashSlots; i += kBinBlock) {
         keys[i] = kEmptyKey;
         cnt[i] = 0u;
     }
@@ -1028,7 +1030,7 @@ __global__ __launch_bounds__(kBlock) void bin_sort_kernel(
     const int m = (int)(bm - b * M);
     const int LK = L * K;
     const int LKb = lt.nblev * K;  // points of the binned levels per query
-    const int64_t i = w * kBlock + tid;
+    const int64_t i = w * kBinBlock + tid;
     const bool ok = i < Q * LKb;
     const int64_t q = ok ? i / LKb : 0;
     const int r = ok ? (int)(i - q * LKb) : 0;
@@ -1054,7 +1056,7 @@ __global__ __launch_bounds__(kBlock) void bin_sort_kernel(
         rib[cn] = (uint32_t)(rel & ((1 << sh) - 1));
         const uint32_t key = kbase + (uint32_t)(rel >> sh);
         uint32_t h = (key * 2654435761u) >> (32 - kHashBits);
-        // linear probing; at most 4 * kBlock keys per workgroup, so an empty
+        // linear probing; at most 4 * kBinBlock keys per workgroup, so an empty
         // slot always exists and the loop ends
         while (true) {
             const uint32_t prev = atomicCAS(&keys[h], kEmptyKey, key);
@@ -1089,7 +1091,7 @@ __global__ __launch_bounds__(kBlock) void bin_sort_kernel(
         }
         __syncthreads();
     }
-    for (uint32_t u = tid; u < nu; u += kBlock) {
+    for (uint32_t u = tid; u < nu; u += kBinBlock) {
         const uint32_t h = ranked ? order[u] : used[u];
         if constexpr (PLACE)
             cnt[h] = __hip_atomic_fetch_add(counter + keys[h], cnt[h], __ATOMIC_RELAXED,
@@ -2167,13 +2169,13 @@ hipError_t launch_gradients(const Problem &p, const Mapping &mp, const void *val
 
 hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
                            const BinnedBuffers &bins, bool place, hipStream_t stream) {
-    const int64_t wpb = (p.Q * p.levels.nblev * p.K + kBlock - 1) / kBlock;
+    const int64_t wpb = (p.Q * p.levels.nblev * p.K + kBinBlock - 1) / kBinBlock;
     const int64_t ntiles = p.B * p.M * wpb;
     if (ntiles == 0) return hipSuccess;
     const int64_t grid = (ntiles + kXcds - 1) / kXcds * kXcds;
     uint32_t *counter = place ? bins.cursor : bins.starts;
 #define MSDA_SORT(T, PL)                                                                        \
-    hipLaunchKernelGGL((bin_sort_kernel<T, PL>), dim3((unsigned)grid), dim3(kBlock), 0, stream, \
+    hipLaunchKernelGGL((bin_sort_kernel<T, PL>), dim3((unsigned)grid), dim3(kBinBlock), 0, stream, \
                        static_cast<const typename T::S *>(loc),                                 \
                        static_cast<const typename T::S *>(attn), p.levels, counter,             \
                        bins.records, p.Q, (int)p.M, (int)p.L, (int)p.K, p.nbbm, wpb, ntiles)
