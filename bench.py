@@ -73,6 +73,10 @@ HBM_PEAK_GBPS = 8000.0
 # machine (H100, Triton, bf16: forward 8 us + backward 56 us; msda-triton
 # README, section "Benchmarks"). Context for vs_baseline, not a target.
 PAGES_DECODER_BF16_US = 8.0 + 56.0
+# Device-scope atomic adds on MI355X are request-bound: about 21 G requests/s
+# measured for requests of 1 to 16 dwords inside one 64-byte segment.
+ATOMIC_CEILING_GREQ = 21.0
+ATOMIC_KERNELS = ("msda_bwd_kernel", "msda_scatter_kernel", "scatter_accum_kernel")
 
 
 def log(msg):
@@ -454,6 +458,21 @@ def main():
                 "traffic": traffic, "kernel": kname, "kernel_us": round(kus, 3),
                 "algorithmic_bytes_per_launch": int(kbytes[kname]), "kernel_source_sha": src_hash}
 
+    # Context for a kernel bound by atomics rather than HBM: its requests (one
+    # per in-bounds corner per 64-byte segment of the target row: packed
+    # 16-bit rows of D*e bytes, fp32 rows of D*4) per second of launch time,
+    # against the measured request ceiling.
+    atomic_rate = None
+    if kname in ATOMIC_KERNELS:
+        seg = {"native": -(-D * (4 if wl.dtype == torch.float32 else e) // 64),
+               "fp32_scratch": -(-D * 4 // 64)}
+        reqs = sum(touched_rows(inp, only_levels=[l])[1] * seg[m]
+                   for l, m in enumerate(level_modes) if m in seg)
+        rate = reqs / (kus * 1e-6) / 1e9
+        atomic_rate = {"kernel": kname, "requests": int(reqs), "achieved": round(rate, 2),
+                       "ceiling": ATOMIC_CEILING_GREQ, "unit": "G requests/s",
+                       "frac": round(rate / ATOMIC_CEILING_GREQ, 4)}
+
     result = {
         "metric": METRIC, "value": round(us_step, 3), "unit": "us/call (fwd+bwd)",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(us_step / 1e3, 6),
@@ -473,7 +492,7 @@ def main():
         "fwd_us": round(ktimes["msda_fwd_kernel"], 3),
         "bwd_us": round(sum(v for k, v in ktimes.items() if k != "msda_fwd_kernel"), 3),
         "kernels": kernels, "phases": phases, "touched_rows_U": U, "corners_C": C, "points_P": P,
-        "roofline": roofline,
+        "roofline": roofline, "atomic_rate": atomic_rate,
     }
     if args.foil:
         result["foil"] = time_foil(g, call, kbytes["msda_fwd_kernel"])
