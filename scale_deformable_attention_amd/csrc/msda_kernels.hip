@@ -500,21 +500,34 @@ __global__ __launch_bounds__(kBlock) void msda_foil_kernel(
 #define MSDA_GRAD_ARGS value, loc, attn, grad_out, grad_loc, grad_attn, lt, S, Q, M, D, L, K, \
                        qblocks, log2g, log2s
 
+// Heads per workgroup of the gradients-only kernel: the query slots of a
+// workgroup hold HG heads of each of its queries, head fastest, so that one
+// store instruction writes a query's gradients for HG neighbouring heads,
+// which share memory lines (one head per workgroup would leave each line to
+// be filled by workgroups on different XCDs, written back in parts). The
+// largest of 4, 2, 1 that divides M and is at most the slots per workgroup.
+__host__ __device__ inline int grad_heads(int M, int slots) {
+    return (M % 4 == 0 && slots >= 4) ? 4 : (M % 2 == 0 && slots >= 2) ? 2 : 1;
+}
+
 template <class DT, class PT, int VEC, int CH, bool BUF>
 __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) {
     using E = typename DT::S;
     using R = typename RawVec<VEC * (int)sizeof(E)>::type;
-    const int64_t bm = tile / qblocks;
-    const int qb = (int)(tile - bm * qblocks);
-    const int64_t b = bm / M;
-    const int m = (int)(bm - b * M);
-
     const int tid = threadIdx.x;
     const int G = 1 << log2g;
     const int c = tid & (G - 1);
     const int s = (tid >> log2g) & ((1 << log2s) - 1);
-    const int qpb = kBlock >> (log2g + log2s);
-    const int64_t q = (int64_t)qb * qpb + (tid >> (log2g + log2s));
+    const int qpb = kBlock >> (log2g + log2s);  // query slots
+    const int HG = grad_heads(M, qpb);
+    const int slot = tid >> (log2g + log2s);
+    // tile = (b, head group, query block), query block fastest
+    const int64_t bg = tile / qblocks;
+    const int qb = (int)(tile - bg * qblocks);
+    const int64_t ngroups = M / HG;
+    const int64_t b = bg / ngroups;
+    const int m = (int)(bg - b * ngroups) * HG + slot % HG;
+    const int64_t q = (int64_t)qb * (qpb / HG) + slot / HG;
     const bool q_ok = q < Q;
     const int c0 = c * VEC;
     const bool live = q_ok && (c0 < D);
@@ -1853,8 +1866,9 @@ hipError_t grad_launch(const Problem &p, const Mapping &mp, const void *value, c
     using E = typename DT::S;
     using P = typename PT::S;
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
-    const int qblocks = (int)((p.Q + qpb - 1) / qpb);
-    const int64_t ntiles = p.B * p.M * qblocks;
+    const int hg = grad_heads((int)p.M, qpb);
+    const int qblocks = (int)((p.Q + qpb / hg - 1) / (qpb / hg));
+    const int64_t ntiles = p.B * (p.M / hg) * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (!slice_fits_buffer(p)) return hipErrorInvalidValue;  // binning requires it
     hipLaunchKernelGGL((msda_grad_kernel<DT, PT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
@@ -2280,8 +2294,9 @@ hipError_t grad_sort_launch(const Problem &p, const Mapping &mp, const void *val
     using E = typename DT::S;
     using P = typename PT::S;
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
-    const int qblocks = (int)((p.Q + qpb - 1) / qpb);
-    const int64_t ntiles = p.B * p.M * qblocks;
+    const int hg = grad_heads((int)p.M, qpb);
+    const int qblocks = (int)((p.Q + qpb / hg - 1) / (qpb / hg));
+    const int64_t ntiles = p.B * (p.M / hg) * qblocks;
     const int64_t ngrad = (ntiles + kXcds - 1) / kXcds * kXcds;
     const int64_t nseg = p.B * p.M * p.levels.nblev;
     const int64_t nsegp = (nseg + kXcds - 1) / kXcds * kXcds;
