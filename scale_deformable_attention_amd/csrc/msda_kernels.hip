@@ -294,6 +294,24 @@ __device__ __forceinline__ Cell map_cell(float loc_x, float loc_y, float Hf, flo
 // only then consumed, so a wave waits for two memory round trips per chunk
 // instead of two per point.
 
+// Heads per workgroup of the forward and gradients-only kernels: the query
+// slots of a workgroup hold HG heads of each of its queries, head fastest,
+// so that one store instruction writes a query's results for HG neighbouring
+// heads, which share memory lines (one head per workgroup would leave each
+// line to be filled by workgroups on different XCDs, written back in parts),
+// and heads that sample near the same pixels share L1 / L2 lines. The
+// largest of 4, 2, 1 that divides M and is at most the slots per workgroup.
+__host__ __device__ inline int grad_heads(int M, int slots) {
+    return (M % 4 == 0 && slots >= 4) ? 4 : (M % 2 == 0 && slots >= 2) ? 2 : 1;
+}
+
+// The forward groups heads only for rows of at most 64 bytes (measured: the
+// encoder workloads' forward 204 -> 177 us and 2147 -> 1794 us with 64-byte
+// rows, the odd-head workload's 192-byte fp32 rows 52 -> 57 us).
+__host__ __device__ inline int fwd_heads(int M, int slots, int row_bytes) {
+    return row_bytes <= 64 ? grad_heads(M, slots) : 1;
+}
+
 template <class DT, class PT, int VEC, int CH, bool BUF>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void msda_fwd_kernel(
     const typename DT::S *__restrict__ value, const typename PT::S *__restrict__ loc,
@@ -305,16 +323,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     using R = typename RawVec<VEC * (int)sizeof(E)>::type;
     const int64_t tile = logical_block();
     if (tile >= ntiles) return;  // whole workgroup leaves together
-    const int64_t bm = tile / qblocks;
-    const int qb = (int)(tile - bm * qblocks);
-    const int64_t b = bm / M;
-    const int m = (int)(bm - b * M);
-
     const int tid = threadIdx.x;
     const int c = tid & ((1 << log2g) - 1);
     const int s = (tid >> log2g) & ((1 << log2s) - 1);
-    const int qpb = kBlock >> (log2g + log2s);
-    const int64_t q = (int64_t)qb * qpb + (tid >> (log2g + log2s));
+    const int qpb = kBlock >> (log2g + log2s);  // query slots
+    const int HG = fwd_heads(M, qpb, D * (int)sizeof(E));
+    const int slot = tid >> (log2g + log2s);
+    // tile = (b, head group, query block), query block fastest
+    const int64_t bg = tile / qblocks;
+    const int qb = (int)(tile - bg * qblocks);
+    const int64_t ngroups = M / HG;
+    const int64_t b = bg / ngroups;
+    const int m = (int)(bg - b * ngroups) * HG + slot % HG;
+    const int64_t q = (int64_t)qb * (qpb / HG) + slot / HG;
     const bool q_ok = q < Q;
     const int c0 = c * VEC;
     const bool live = q_ok && (c0 < D);
@@ -499,16 +520,6 @@ __global__ __launch_bounds__(kBlock) void msda_foil_kernel(
         const int L, const int K, const int qblocks, const int log2g, const int log2s
 #define MSDA_GRAD_ARGS value, loc, attn, grad_out, grad_loc, grad_attn, lt, S, Q, M, D, L, K, \
                        qblocks, log2g, log2s
-
-// Heads per workgroup of the gradients-only kernel: the query slots of a
-// workgroup hold HG heads of each of its queries, head fastest, so that one
-// store instruction writes a query's gradients for HG neighbouring heads,
-// which share memory lines (one head per workgroup would leave each line to
-// be filled by workgroups on different XCDs, written back in parts). The
-// largest of 4, 2, 1 that divides M and is at most the slots per workgroup.
-__host__ __device__ inline int grad_heads(int M, int slots) {
-    return (M % 4 == 0 && slots >= 4) ? 4 : (M % 2 == 0 && slots >= 2) ? 2 : 1;
-}
 
 template <class DT, class PT, int VEC, int CH, bool BUF>
 __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) {
@@ -1838,8 +1849,9 @@ hipError_t fwd_launch(const Problem &p, const Mapping &mp, const void *value, co
     using E = typename DT::S;
     using P = typename PT::S;
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
-    const int qblocks = (int)((p.Q + qpb - 1) / qpb);
-    const int64_t ntiles = p.B * p.M * qblocks;
+    const int hg = fwd_heads((int)p.M, qpb, (int)(p.D * (int64_t)sizeof(typename DT::S)));
+    const int qblocks = (int)((p.Q + qpb / hg - 1) / (qpb / hg));
+    const int64_t ntiles = p.B * (p.M / hg) * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (slice_fits_buffer(p))
         hipLaunchKernelGGL((msda_fwd_kernel<DT, PT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
