@@ -63,6 +63,8 @@ def _load():
     lib.msda_oracle_forward.restype = i32
     lib.msda_oracle_backward.argtypes = common + [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32]
     lib.msda_oracle_backward.restype = i32
+    lib.msda_oracle_scatter_stats.argtypes = common + [vp, vp, vp, vp, vp, i32, i32]
+    lib.msda_oracle_scatter_stats.restype = i32
     lib.msda_oracle_max_threads.argtypes = []
     lib.msda_oracle_max_threads.restype = i32
     _lib = lib
@@ -145,3 +147,37 @@ def backward(value, spatial_shapes, level_start_index, sampling_locations,
         raise ValueError(f"oracle backward: {_ERRORS.get(rc, rc)}")
     res = (gv, gl, ga)
     return res + (touched.astype(bool),) if return_touched else res
+
+
+def scatter_stats(spatial_shapes, level_start_index, sampling_locations, attention_weights,
+                  grad_output, num_keys: int, head_dim: int, mode: str = "pinned_f32",
+                  num_threads: int = 0):
+    """Per grad_value element, the sum of the absolute values of the terms
+    A * w_ij * g[d] that the scatter adds into it, and per (b, row, m) row the
+    number of those terms (in-bounds corners landing on the row).
+
+    Returns (abs_sum (B, S, M, D) fp64, count (B, S, M) int64). With them a
+    sum of `count` terms, each rounded once to a type with unit roundoff u and
+    added with one rounding per add in any order, is within
+    gamma(count) * abs_sum of the exact sum, gamma(n) = n*u / (1 - n*u)
+    (course page "5. The backward kernel", section "Atomics make gradients
+    nondeterministic", for why half-precision atomics round on each add)."""
+    lib = _load()
+    loc, a, g = _f64(sampling_locations), _f64(attention_weights), _f64(grad_output)
+    shp = _i64(spatial_shapes).reshape(-1, 2)
+    st = None if level_start_index is None else _i64(level_start_index)
+    if loc.ndim != 6 or loc.shape[3] != shp.shape[0] or loc.shape[5] != 2:
+        raise ValueError(f"sampling_locations shape {loc.shape} does not match "
+                         f"{shp.shape[0]} levels")
+    B, Q, M, L, K, _ = loc.shape
+    S, D = int(num_keys), int(head_dim)
+    if g.size != B * Q * M * D:
+        raise ValueError(f"grad_output has {g.size} elements, expected {B * Q * M * D}")
+    abs_sum = np.empty((B, S, M, D), dtype=np.float64)
+    count = np.empty((B, S, M), dtype=np.int64)
+    rc = lib.msda_oracle_scatter_stats(B, S, M, D, L, _ptr(shp), _ptr(st), Q, K, _ptr(loc),
+                                       _ptr(a), _ptr(g), _ptr(abs_sum), _ptr(count),
+                                       MODES[mode], num_threads)
+    if rc:
+        raise ValueError(f"oracle scatter_stats: {_ERRORS.get(rc, rc)}")
+    return abs_sum, count

@@ -397,3 +397,87 @@ int msda_oracle_backward(int64_t B, int64_t S, int64_t M, int64_t D, int64_t L,
         return ORACLE_ERR_NONFINITE;
     return ORACLE_OK;
 }
+
+/*
+ * Rounding statistics of the grad_value scatter, for judging a sum whose
+ * every add is rounded to a 16-bit type (course page "5. The backward
+ * kernel", section "Atomics make gradients nondeterministic": native
+ * half-precision atomics round on each add, so the result depends on the
+ * order and carries the rounding of every partial sum).
+ *
+ * For each grad_value element (b, row, m, d) this returns
+ *   abs_sum[b,row,m,d] = sum over the in-bounds corners that land on row of
+ *                        |A * w_ij * g[d]|  (the same terms whose signed sum
+ *                        msda_oracle_backward returns as grad_value)
+ *   count[b,row,m]     = the number of those corners (the same for every d).
+ * With these, the recursive-summation bound of numerical analysis gives
+ * |fl(sum) - sum| <= gamma_n * abs_sum, gamma_n = n*u / (1 - n*u), for n
+ * terms each rounded once to the 16-bit type and added one by one with
+ * rounding, in any order; the test suite applies that bound.
+ *
+ * Same loops, same order and same ownership as the grad_value part of
+ * msda_oracle_backward (parallel over (b, m)); value is not needed.
+ */
+int msda_oracle_scatter_stats(int64_t B, int64_t S, int64_t M, int64_t D, int64_t L,
+                              const int64_t *spatial_shapes,
+                              const int64_t *level_start_index, int64_t Q, int64_t K,
+                              const double *loc, const double *attn,
+                              const double *grad_out, double *abs_sum, int64_t *count,
+                              int mode, int num_threads)
+{
+    int status = check_sizes(B, S, M, D, L, Q, K);
+    if (status)
+        return status;
+    int64_t *starts = (int64_t *)malloc(sizeof(int64_t) * (size_t)L);
+    if (!starts)
+        return ORACLE_ERR_NOMEM;
+    status = level_table(S, L, spatial_shapes, level_start_index, starts);
+    if (status) {
+        free(starts);
+        return status;
+    }
+    set_threads(num_threads);
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t s = 0; s < S; ++s) {
+                double *as = abs_sum + ((b * S + s) * M + m) * D;
+                for (int64_t d = 0; d < D; ++d)
+                    as[d] = 0.0;
+                count[(b * S + s) * M + m] = 0;
+            }
+            for (int64_t q = 0; q < Q; ++q) {
+                const double *g = grad_out + ((b * Q + q) * M + m) * D;
+                for (int64_t l = 0; l < L; ++l) {
+                    int64_t H = spatial_shapes[2 * l], W = spatial_shapes[2 * l + 1];
+                    for (int64_t k = 0; k < K; ++k) {
+                        int64_t p = ((b * Q + q) * M + m) * L * K + l * K + k;
+                        cell_t c;
+                        if (map_point(loc[2 * p], loc[2 * p + 1], H, W, mode, &c)) {
+                            bad |= 2;
+                            continue;
+                        }
+                        double a = attn[p];
+                        for (int i = 0; i < 2; ++i) {
+                            for (int j = 0; j < 2; ++j) {
+                                if (!corner_valid(&c, i, j, H, W))
+                                    continue;
+                                int64_t row = starts[l] + (c.y0 + i) * W + (c.x0 + j);
+                                double *as = abs_sum + ((b * S + row) * M + m) * D;
+                                double term = a * corner_weight(&c, i, j);
+                                for (int64_t d = 0; d < D; ++d)
+                                    as[d] += fabs(term * g[d]);
+                                count[(b * S + row) * M + m] += 1;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+    free(starts);
+    if (bad & 2)
+        return ORACLE_ERR_NONFINITE;
+    return ORACLE_OK;
+}

@@ -44,6 +44,13 @@ MUTANTS = {
     "forward_missing_A": ("o[d] += a * sample[d];", "o[d] += sample[d];"),
     "y_weight_from_wrong_corner": ("double sy = (1.0 - c.lx) * (a10 - a00) + c.lx * (a11 - a01);",
                                    "double sy = (1.0 - c.lx) * (a10 - a00) + c.lx * (a11 - a10);"),
+    # the rounding statistics of the grad_value scatter
+    "stats_abs_of_upstream_only": ("as[d] += fabs(term * g[d]);", "as[d] += term * fabs(g[d]);"),
+    "stats_signed_terms": ("as[d] += fabs(term * g[d]);", "as[d] += term * g[d];"),
+    "stats_count_is_a_flag": ("count[(b * S + row) * M + m] += 1;",
+                              "count[(b * S + row) * M + m] = 1;"),
+    "stats_corner_weight_dropped": ("double term = a * corner_weight(&c, i, j);",
+                                    "double term = a;"),
 }
 
 

@@ -443,3 +443,77 @@ def test_bad_levels_are_rejected():
     loc2[0, 0, 0, 0, 0, 0] = float("nan")
     with pytest.raises(ValueError):
         oracle.forward(value, shapes, None, loc2, attn)
+
+
+# ------------------------------------------- grad_value rounding statistics
+#
+# oracle.scatter_stats gives, per grad_value element, the sum of the absolute
+# values of its terms A * w_ij * g[d] and, per row, their number; the GPU
+# parity rule for sums made with 16-bit atomics is built on them (backward
+# course page, section "Atomics make gradients nondeterministic").
+
+def test_scatter_stats_golden():
+    d = json.load(open(os.path.join(GOLDEN, "rounding", "scatter_rounding_stats.json")))
+    shapes = np.array(d["spatial_shapes"], np.int64)
+    loc = np.array(d["sampling_locations"], np.float64)
+    attn = np.array(d["attention_weights"], np.float64)
+    g = np.array(d["grad_output"], np.float64)
+    S, D = d["num_keys"], d["head_dim"]
+    ex = d["expected"]
+    for mode in ("pinned_f32", "exact_f64"):
+        abs_sum, count = oracle.scatter_stats(shapes, None, loc, attn, g, S, D, mode=mode)
+        np.testing.assert_array_equal(abs_sum, np.array(ex["abs_sum"]))
+        np.testing.assert_array_equal(count, np.array(ex["count"]))
+        value = np.zeros((1, S, 1, D))
+        gv = oracle.backward(value, shapes, None, loc, attn, g, mode=mode)[0]
+        np.testing.assert_array_equal(gv, np.array(ex["grad_value"]))
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_scatter_stats_equal_signed_sum_when_terms_share_a_sign(sign):
+    """With non-negative weights A and an upstream gradient of one sign, every
+    term A * w_ij * g[d] has that sign, so the sum of absolute values equals
+    the absolute value of the sum: abs_sum == |grad_value| exactly (the same
+    terms added in the same order)."""
+    value, shapes, st, loc, attn, gout = _rand_case(21, starts=(30, 0, 13))
+    gpos = sign * gout.abs()
+    gv = oracle.backward(value, shapes, st, loc, attn, gpos)[0]
+    abs_sum, count = oracle.scatter_stats(shapes, st, loc, attn, gpos, value.shape[1],
+                                          value.shape[3])
+    np.testing.assert_array_equal(abs_sum, np.abs(gv))
+    assert (count > 0).sum() > 0
+
+
+def test_scatter_stats_bound_the_signed_sum_and_count_corners():
+    """Mixed signs: |grad_value| <= abs_sum elementwise (triangle inequality),
+    equality on rows that receive one term; the upstream gradient's sign does
+    not change abs_sum; doubling it doubles abs_sum exactly; count > 0
+    exactly on the rows the backward reports as touched, and the counts add
+    up to the in-bounds corners counted point by point in numpy."""
+    value, shapes, st, loc, attn, gout = _rand_case(22, Q=11, starts=(30, 0, 13))
+    attn = attn - 0.5  # weights of both signs
+    S, D = value.shape[1], value.shape[3]
+    gv, _, _, touched = oracle.backward(value, shapes, st, loc, attn, gout, return_touched=True)
+    abs_sum, count = oracle.scatter_stats(shapes, st, loc, attn, gout, S, D)
+    assert np.all(np.abs(gv) <= abs_sum * (1 + 1e-15))
+    one = count == 1
+    np.testing.assert_allclose(np.abs(gv)[one], abs_sum[one], rtol=1e-15, atol=0)
+    assert np.all(abs_sum[count >= 2] >= np.abs(gv)[count >= 2])
+    assert (np.abs(gv)[count >= 2] < abs_sum[count >= 2] * (1 - 1e-12)).any()
+    np.testing.assert_array_equal(oracle.scatter_stats(shapes, st, loc, attn, -gout, S, D)[0],
+                                  abs_sum)
+    np.testing.assert_array_equal(oracle.scatter_stats(shapes, st, loc, attn, 2 * gout, S, D)[0],
+                                  2 * abs_sum)
+    np.testing.assert_array_equal(count > 0, touched)
+    # in-bounds corners point by point (single-rounding fp32 mapping)
+    corners = 0
+    for l, (H, W) in enumerate(shapes.tolist()):
+        lx = loc[:, :, :, l, :, 0].numpy().astype(np.float32)
+        ly = loc[:, :, :, l, :, 1].numpy().astype(np.float32)
+        x0 = np.floor((lx.astype(np.float64) * W - 0.5).astype(np.float32)).astype(np.int64)
+        y0 = np.floor((ly.astype(np.float64) * H - 0.5).astype(np.float32)).astype(np.int64)
+        for dy in (0, 1):
+            for dx in (0, 1):
+                corners += int((((x0 + dx) >= 0) & ((x0 + dx) < W) &
+                                ((y0 + dy) >= 0) & ((y0 + dy) < H)).sum())
+    assert int(count.sum()) == corners
