@@ -131,7 +131,7 @@ def test_forward_given_start_index_may_differ_from_prefix(lib):
 @pytest.mark.parametrize("kw,status", [
     (dict(accum=5), 4),
     (dict(accum=-2), 4),
-    (dict(flags=8), 2),
+    (dict(flags=16), 2),
     (dict(flags=2), 2),  # scratch flags need an explicit scratch-capable mode
     (dict(gv=None, accum=0), 1),
     (dict(gout=None, accum=0), 1),
@@ -295,3 +295,42 @@ def test_python_prep_binding_rejects_bad_tensors_on_cpu():
         msda_sampling_prep(ref, off, torch.zeros(1, 16, 2, 5), [[8, 10], [4, 5]])
     with pytest.raises(TypeError):
         msda_sampling_prep(ref.double(), off, logits, [[8, 10], [4, 5]])
+
+
+def test_workload_plans_match_the_documented_policy(lib):
+    """For every named workload and accumulation mode, the library's per-level
+    plan (msda_backward_plan, host-only) equals the table the GPU parity
+    tests hard-code, and the test-side reading of include/msda.h's policy."""
+    import sys
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from _parity import WORKLOAD_PLANS, expected_level_modes
+    from scale_deformable_attention_amd.workloads import workload
+    for name, plans in WORKLOAD_PLANS.items():
+        wl = workload(name)
+        L = len(wl.levels)
+        v = torch.empty((wl.B, wl.S, wl.M, wl.D), dtype=wl.dtype, device="meta")
+        pdt = wl.param_dtype or wl.dtype
+        loc = torch.empty((wl.B, wl.num_queries, wl.M, L, wl.K, 2), dtype=pdt, device="meta")
+        attn = torch.empty((wl.B, wl.num_queries, wl.M, L, wl.K), dtype=pdt, device="meta")
+        for accum, table in plans.items():
+            got = bind.msda_backward_level_modes(v, torch.tensor(wl.levels), None, loc, attn,
+                                                 accum)
+            want = expected_level_modes(wl.dtype, accum, torch.tensor(wl.levels), wl.B, wl.S,
+                                        wl.M, wl.D, wl.num_queries, wl.K)
+            assert got == table == want, (name, accum, got, table, want)
+
+
+def test_release_thread_resources_without_any_is_ok(lib):
+    """No binned backward ran on this thread: nothing to release, no HIP call,
+    MSDA_OK (twice in a row too)."""
+    assert lib.msda_release_thread_resources() == 0
+    assert lib.msda_release_thread_resources() == 0
+    bind.release_thread_resources()
+
+
+def test_single_stream_flag_is_known(lib):
+    """MSDA_FLAG_SINGLE_STREAM (8) passes flag validation; an unknown bit does
+    not (both stop before any launch: B = 0 returns after validation)."""
+    assert bwd(lib, B=0, flags=8) == 0
+    assert bwd(lib, B=0, flags=16) == 2

@@ -19,7 +19,7 @@ from scale_deformable_attention_amd import (msda_backward, msda_backward_resolve
                                             msda_forward, multi_scale_deformable_attention)
 from scale_deformable_attention_amd.workloads import Workload, make_inputs, workload
 
-from _parity import atomic_level_rules, check_backward, check_forward, check_slice, to_np
+from _parity import check_backward, check_forward, check_slice, parity_kwargs, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -78,7 +78,8 @@ def _autograd_check(name, switch, device_shapes=False):
     torch.cuda.synchronize()
     check_forward(dtype, out.detach().cpu(), ref_out, touched)
     check_backward(dtype, (v.grad.cpu(), loc.grad.cpu(), a.grad.cpu()), ref_grads,
-                   inp["spatial_shapes"], None, trows, **atomic_level_rules(dtype, switch, inp))
+                   inp["spatial_shapes"], None, trows,
+                   **parity_kwargs(dtype, switch, inp, workload_name=name))
 
 
 def test_autograd_matches_oracle_tiny():
@@ -196,7 +197,7 @@ def test_graph_capture_replays_match_eager(name, switch):
         check_forward(wl.dtype, static_out.cpu(), ref_out, touched)
         check_backward(wl.dtype, (v.grad.cpu(), loc.grad.cpu(), a.grad.cpu()), ref_grads,
                        fresh["spatial_shapes"], None, trows,
-                       **atomic_level_rules(wl.dtype, switch, fresh))
+                       **parity_kwargs(wl.dtype, switch, fresh, workload_name=name))
 
 
 def test_capture_on_a_thread_without_side_stream():
