@@ -46,14 +46,16 @@
  * thread-local: an error string and, for backward calls that bin some level,
  * one side stream (default priority) and three events per device, created by
  * the first such call of a thread that is not under graph capture and kept
- * for the thread's lifetime. Work is enqueued on the caller's stream (a
- * hipStream_t passed as void*; NULL is the default stream); the binned part
- * of a backward forks onto the side stream after the caller's earlier work
- * and is joined back before the call returns, so each call is ordered on the
- * caller's stream as a whole and can be captured in a HIP graph (a call
- * captured before its thread has a side stream runs entirely on the caller's
- * stream). Calls are reentrant. Device pointers must be aligned to their element size; wider
- * vector accesses are used automatically when every pointer allows them.
+ * until msda_release_thread_resources() (or the thread's end); a call with
+ * MSDA_FLAG_SINGLE_STREAM neither uses nor creates them. Work is enqueued on
+ * the caller's stream (a hipStream_t passed as void*; NULL is the default
+ * stream); the binned part of a backward forks onto the side stream after the
+ * caller's earlier work and is joined back before the call returns, so each
+ * call is ordered on the caller's stream as a whole and can be captured in a
+ * HIP graph (a call captured before its thread has a side stream runs
+ * entirely on the caller's stream). Calls are reentrant. Device pointers must
+ * be aligned to their element size; wider vector accesses are used
+ * automatically when every pointer allows them.
  *
  * Errors: every entry point returns an msda_status_t. All argument checks run
  * before any HIP call, so a rejected call has no side effect and needs no GPU.
@@ -146,6 +148,10 @@ typedef enum msda_status {
  * several backward calls (micro-batches) accumulate in fp32 and round into
  * grad_value once, by a last call without DEFER_SCRATCH. */
 #define MSDA_FLAG_DEFER_SCRATCH 4u
+/* Run the whole backward on the caller's stream: no side stream is used or
+ * created (by default a backward binning at least 2^19 records runs its
+ * binned chain on this thread's side stream, see "Ownership and threading"). */
+#define MSDA_FLAG_SINGLE_STREAM 8u
 
 /*
  * Forward. Writes every element of `output` (B, Q, M, D).
@@ -331,6 +337,16 @@ const char *msda_status_string(int status);
 
 /* Thread-local detail for the last non-OK status of this thread ("" if none). */
 const char *msda_last_error(void);
+
+/*
+ * Destroys this thread's side streams and their events on every device (the
+ * only resources the library keeps, see "Ownership and threading"). Work
+ * already queued on them still completes, and HIP graphs captured earlier keep
+ * working (they hold nodes, not the streams). A later binned backward on this
+ * thread creates them again. Returns MSDA_OK when there is nothing to release
+ * (no HIP call is made then), MSDA_ERR_HIP if a destroy fails.
+ */
+int msda_release_thread_resources(void);
 
 /* MSDA_ABI_VERSION of the built library. */
 int msda_abi_version(void);

@@ -29,6 +29,7 @@ LEVEL_MODES = {0: "native", 1: "fp32_scratch", 2: "binned"}
 FLAG_ACCUMULATE_GRAD_VALUE = 1
 FLAG_CONTINUE_SCRATCH = 2
 FLAG_DEFER_SCRATCH = 4
+FLAG_SINGLE_STREAM = 8
 MAX_LEVELS = 16
 
 _DTYPE_CODES = {torch.float32: MSDA_F32, torch.float16: MSDA_F16, torch.bfloat16: MSDA_BF16}
@@ -44,7 +45,7 @@ EXPORTED_SYMBOLS = ("msda_forward", "msda_forward_ex", "msda_forward_point_paral
                     "msda_last_error",
                     "msda_abi_version", "msda_set_launch_events", "msda_launch_events_recorded",
                     "msda_launch_events_name", "msda_sampling_prep",
-                    "msda_sampling_prep_backward")
+                    "msda_sampling_prep_backward", "msda_release_thread_resources")
 
 _lib = None
 
@@ -100,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msda_launch_events_recorded.restype = i32
     lib.msda_launch_events_name.argtypes = [i32]
     lib.msda_launch_events_name.restype = ctypes.c_char_p
+    lib.msda_release_thread_resources.argtypes = []
+    lib.msda_release_thread_resources.restype = i32
     _lib = lib
     return lib
 
@@ -290,6 +293,11 @@ def msda_backward_level_modes(value: torch.Tensor, spatial_shapes, level_start_i
     return [LEVEL_MODES[int(m)] for m in modes]
 
 
+def release_thread_resources() -> None:
+    """Destroy this thread's side streams and events (msda_release_thread_resources)."""
+    _check(load_library().msda_release_thread_resources())
+
+
 def set_launch_events(events) -> None:
     """Instrument the next msda_forward / msda_backward call of this thread:
     events[i] (torch.cuda.Event, already created) is recorded on the call's
@@ -321,7 +329,8 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index,
                   grad_attention_weights: Optional[torch.Tensor] = None,
                   accum: Union[str, bool, None] = "auto", accumulate: bool = False,
                   workspace: Optional[torch.Tensor] = None, stream=None,
-                  continue_scratch: bool = False, defer_scratch: bool = False
+                  continue_scratch: bool = False, defer_scratch: bool = False,
+                  single_stream: bool = False
                   ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Backward of the MSDA core: (grad_value, grad_sampling_locations,
     grad_attention_weights). `accum` is "auto", "native", "fp32_scratch",
@@ -329,7 +338,8 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index,
     pages' fp32_grad_accum switch).
     With `accumulate`, grad_value (given) is added into instead of overwritten.
     `continue_scratch` / `defer_scratch` map to MSDA_FLAG_CONTINUE_SCRATCH /
-    MSDA_FLAG_DEFER_SCRATCH (fp32 accumulation across calls in `workspace`)."""
+    MSDA_FLAG_DEFER_SCRATCH (fp32 accumulation across calls in `workspace`);
+    `single_stream` to MSDA_FLAG_SINGLE_STREAM (no side stream)."""
     lib = load_library()
     levels = _Levels(spatial_shapes, level_start_index)
     code, pcode = _dtype_codes(value, sampling_locations, attention_weights, grad_output)
@@ -364,7 +374,8 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index,
         workspace = torch.empty(need, dtype=torch.uint8, device=value.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     flags = (FLAG_ACCUMULATE_GRAD_VALUE if accumulate else 0) | \
-        (FLAG_CONTINUE_SCRATCH if continue_scratch else 0) | (FLAG_DEFER_SCRATCH if defer_scratch else 0)
+        (FLAG_CONTINUE_SCRATCH if continue_scratch else 0) | \
+        (FLAG_DEFER_SCRATCH if defer_scratch else 0) | (FLAG_SINGLE_STREAM if single_stream else 0)
     _check(lib.msda_backward_ex(code, pcode, *prob[1:], _ptr(value), _ptr(loc), _ptr(attn), _ptr(gout),
                              _ptr(grad_value), _ptr(grad_loc), _ptr(grad_attn), acode, flags,
                              _ptr(workspace), ws_bytes, _stream(value.device, stream)))

@@ -31,14 +31,17 @@ COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "--offload-arch=gfx950",
 def build(verbose: bool = False, asm_dir: str = None) -> str:
     """Compile and link the library; optionally also write device assembly
     of the kernels to `asm_dir` (used to check which atomic forms are emitted)."""
-    objs = []
-    for src in SOURCES:
+    objs, procs = [], []
+    for src in SOURCES:  # the sources compile in parallel
         obj = os.path.join(HERE, "csrc", os.path.basename(src) + ".o")
         cmd = [HIPCC, "-c", "-x", "hip", src, "-o", obj] + COMMON_FLAGS
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        procs.append((subprocess.Popen(cmd), cmd))
         objs.append(obj)
+    for proc, cmd in procs:
+        if proc.wait() != 0:
+            raise subprocess.CalledProcessError(proc.returncode, cmd)
     tmp = LIB_PATH + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
     if verbose:

@@ -99,6 +99,29 @@ SideStream *side_stream(hipStream_t s) {
     return &ss;
 }
 
+// Destroy this thread's side streams and events on every device.
+hipError_t release_side_streams() {
+    hipError_t first = hipSuccess;
+    int cur = -1;
+    bool have_cur = false;
+    for (int dev = 0; dev < kMaxDevices; ++dev) {
+        SideStream &ss = g_side[dev];
+        if (!ss.stream) continue;
+        if (!have_cur) have_cur = hipGetDevice(&cur) == hipSuccess;
+        hipError_t e = hipSetDevice(dev);
+        // (destroying a stream with work still queued lets that work finish first)
+        if (e == hipSuccess) e = hipStreamDestroy(ss.stream);
+        for (hipEvent_t ev : {ss.fork, ss.zeroed, ss.join}) {
+            const hipError_t ee = hipEventDestroy(ev);
+            if (e == hipSuccess) e = ee;
+        }
+        if (first == hipSuccess) first = e;
+        ss = SideStream();
+    }
+    if (have_cur) (void)hipSetDevice(cur);
+    return first;
+}
+
 int fail(int status, const char *fmt, ...) {
     char buf[512];
     va_list ap;
@@ -516,6 +539,12 @@ int msda_set_launch_events(void *const *events, int count) {
 
 const char *msda_last_error(void) { return g_last_error.c_str(); }
 
+int msda_release_thread_resources(void) {
+    const hipError_t err = release_side_streams();
+    if (err != hipSuccess) return hip_fail(err, "releasing the side stream");
+    return ok();
+}
+
 const char *msda_status_string(int status) {
     switch (status) {
         case MSDA_OK: return "ok";
@@ -694,8 +723,8 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
     if (st) return st;
     if ((st = set_param_dtype(&p, pdtype))) return st;
     if (!valid_accum(accum)) return fail(MSDA_ERR_DTYPE, "unknown accumulation mode %d", accum);
-    const unsigned known =
-        MSDA_FLAG_ACCUMULATE_GRAD_VALUE | MSDA_FLAG_CONTINUE_SCRATCH | MSDA_FLAG_DEFER_SCRATCH;
+    const unsigned known = MSDA_FLAG_ACCUMULATE_GRAD_VALUE | MSDA_FLAG_CONTINUE_SCRATCH |
+                           MSDA_FLAG_DEFER_SCRATCH | MSDA_FLAG_SINGLE_STREAM;
     if (flags & ~known) return fail(MSDA_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~known);
     if (p.B == 0) return ok();
     const bool accumulate = (flags & MSDA_FLAG_ACCUMULATE_GRAD_VALUE) != 0;
@@ -770,8 +799,10 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
         // than the overlap gains below ~2^19 records (the decoder workload's
         // 3 * 10^5 lose 20 us; the odd-head workload's 9 * 10^5 gain 24 us).
         // (the one-launch local sort serves small problems and runs on s)
-        SideStream *side =
-            !bp.local_sort && bp.records >= ((int64_t)1 << 19) ? side_stream(s) : nullptr;
+        SideStream *side = !bp.local_sort && bp.records >= ((int64_t)1 << 19) &&
+                                   !(flags & MSDA_FLAG_SINGLE_STREAM)
+                               ? side_stream(s)
+                               : nullptr;
         // the local sort's launch also zero-fills grad_value when it can
         const bool fused_zero = bp.local_sort && zero_gv && aligned(grad_value, 16) &&
                                 gv_bytes % 16 == 0;
