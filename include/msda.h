@@ -254,6 +254,31 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * msda_backward for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments and results without the workspace, which comes from a static
+ * scratch array of 32 MiB inside the library instead (device memory each
+ * GPU the library runs on holds until the process ends). No device memory is
+ * allocated or freed, and the whole backward runs on the caller's stream (as
+ * with MSDA_FLAG_SINGLE_STREAM). Every call on one GPU shares that GPU's
+ * scratch: each call clears what must start at zero itself, and calls that
+ * overlap in time on one GPU race (order them on one stream, or use
+ * msda_backward with separate workspaces). MSDA_ERR_WORKSPACE when the
+ * problem needs more than 32 MiB of workspace for `accum`
+ * (msda_backward_workspace_size), before any HIP call; MSDA_ERR_SHAPE for the
+ * CONTINUE_SCRATCH / DEFER_SCRATCH flags, which would rely on the shared
+ * scratch's earlier contents.
+ */
+int msda_backward_noalloc(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
+                          int64_t head_dim, int64_t num_levels, const int64_t *spatial_shapes,
+                          const int64_t *level_start_index, int64_t num_queries,
+                          int64_t num_points, const void *value, const void *sampling_locations,
+                          const void *attention_weights, const void *grad_output,
+                          void *grad_value, void *grad_sampling_locations,
+                          void *grad_attention_weights, int accum, unsigned flags,
+                          void *stream);
+
+/*
  * Mixed dtypes for the backward, as msda_forward_ex: sampling_locations,
  * attention_weights, grad_sampling_locations and grad_attention_weights take
  * param_dtype; value, grad_output and grad_value take value_dtype. Workspace

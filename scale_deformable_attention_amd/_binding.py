@@ -45,7 +45,8 @@ EXPORTED_SYMBOLS = ("msda_forward", "msda_forward_ex", "msda_forward_point_paral
                     "msda_last_error",
                     "msda_abi_version", "msda_set_launch_events", "msda_launch_events_recorded",
                     "msda_launch_events_name", "msda_sampling_prep",
-                    "msda_sampling_prep_backward", "msda_release_thread_resources")
+                    "msda_sampling_prep_backward", "msda_release_thread_resources",
+                    "msda_backward_noalloc")
 
 _lib = None
 
@@ -101,6 +102,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msda_launch_events_recorded.restype = i32
     lib.msda_launch_events_name.argtypes = [i32]
     lib.msda_launch_events_name.restype = ctypes.c_char_p
+    lib.msda_backward_noalloc.argtypes = prob + [vp, vp, vp, vp, vp, vp, vp, i32, u32, vp]
+    lib.msda_backward_noalloc.restype = i32
     lib.msda_release_thread_resources.argtypes = []
     lib.msda_release_thread_resources.restype = i32
     _lib = lib
@@ -380,6 +383,37 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index,
                              _ptr(grad_value), _ptr(grad_loc), _ptr(grad_attn), acode, flags,
                              _ptr(workspace), ws_bytes, _stream(value.device, stream)))
     return grad_value, grad_loc, grad_attn
+
+
+def msda_backward_noalloc(value: torch.Tensor, spatial_shapes, level_start_index,
+                          sampling_locations: torch.Tensor, attention_weights: torch.Tensor,
+                          grad_output: torch.Tensor, grad_value: torch.Tensor,
+                          grad_sampling_locations: torch.Tensor,
+                          grad_attention_weights: torch.Tensor, accum="auto",
+                          accumulate: bool = False, stream=None) -> None:
+    """msda_backward into caller-given outputs with the library's static
+    scratch as workspace (msda_backward_noalloc): allocates nothing, so the
+    inputs must already be contiguous and in one dtype."""
+    lib = load_library()
+    levels = _Levels(spatial_shapes, level_start_index)
+    code = _dtype_code(value, sampling_locations, attention_weights, grad_output, grad_value,
+                       grad_sampling_locations, grad_attention_weights)
+    for t in (value, sampling_locations, attention_weights, grad_output, grad_value,
+              grad_sampling_locations, grad_attention_weights):
+        if not t.is_contiguous():
+            raise ValueError("msda_backward_noalloc needs contiguous tensors")
+    B, S, M, D, Q, K = _dims(value, levels, sampling_locations, attention_weights)
+    if grad_output.numel() != B * Q * M * D or grad_value.shape != value.shape or \
+            grad_sampling_locations.shape != sampling_locations.shape or \
+            grad_attention_weights.shape != attention_weights.shape:
+        raise ValueError("gradient tensors must match their inputs' shapes")
+    _check(lib.msda_backward_noalloc(*_problem(code, B, S, M, D, levels, Q, K), _ptr(value),
+                                     _ptr(sampling_locations), _ptr(attention_weights),
+                                     _ptr(grad_output), _ptr(grad_value),
+                                     _ptr(grad_sampling_locations), _ptr(grad_attention_weights),
+                                     _ACCUM_CODES[accum],
+                                     FLAG_ACCUMULATE_GRAD_VALUE if accumulate else 0,
+                                     _stream(value.device, stream)))
 
 
 class PreparedCall:

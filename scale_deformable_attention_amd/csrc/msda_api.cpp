@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "msda_launch.h"
@@ -977,6 +978,93 @@ int msda_backward(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
                          sampling_locations, attention_weights, grad_output, grad_value,
                          grad_sampling_locations, grad_attention_weights, accum, flags, workspace,
                          workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ allocation-free backward
+//
+// msda_backward_noalloc runs msda_backward with a workspace taken from this
+// file-scope device array instead of the caller's memory, for callers that
+// cannot allocate. Each GPU the library runs on holds its own copy until the
+// process ends; in host code the array's name only stands for it, so its
+// device address is looked up once per device (with that device current) and
+// only that address is handed to kernels. Every call on one GPU shares the
+// array: the backward clears what must start at zero (bin counters, fp32
+// sums) itself, and calls that overlap on one GPU race.
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on device `dev` (looked up on first use).
+int scratch_address(int dev, void **out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        hipError_t err = hipGetDevice(&cur);
+        if (err == hipSuccess && cur != dev) err = hipSetDevice(dev);
+        void *ptr = nullptr;
+        if (err == hipSuccess) err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+        if (err != hipSuccess) return hip_fail(err, "looking up the static scratch address");
+        if (!ptr) return fail(MSDA_ERR_HIP, "the static scratch has no device address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MSDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msda_backward_noalloc(int dtype, int64_t batch, int64_t num_keys, int64_t num_heads,
+                          int64_t head_dim, int64_t num_levels, const int64_t *spatial_shapes,
+                          const int64_t *level_start_index, int64_t num_queries,
+                          int64_t num_points, const void *value, const void *sampling_locations,
+                          const void *attention_weights, const void *grad_output,
+                          void *grad_value, void *grad_sampling_locations,
+                          void *grad_attention_weights, int accum, unsigned flags,
+                          void *stream) {
+    if (flags & (MSDA_FLAG_CONTINUE_SCRATCH | MSDA_FLAG_DEFER_SCRATCH))
+        return fail(MSDA_ERR_SHAPE,
+                    "msda_backward_noalloc takes no CONTINUE_SCRATCH / DEFER_SCRATCH: its "
+                    "scratch is shared by every call on the GPU");
+    // Size the workspace first (host only), so an oversized problem is
+    // rejected before any HIP call.
+    const size_t need = msda_backward_workspace_size(dtype, batch, num_keys, num_heads, head_dim,
+                                                     num_levels, spatial_shapes,
+                                                     level_start_index, num_queries, num_points,
+                                                     accum);
+    // (need == 0 for invalid arguments too: msda_backward's own validation
+    // below then returns their status)
+    if (need > kNoAllocScratchBytes)
+        return fail(MSDA_ERR_WORKSPACE,
+                    "this backward needs %zu bytes of workspace, above the %zu bytes of "
+                    "msda_backward_noalloc's static scratch; call msda_backward with a "
+                    "workspace instead",
+                    need, kNoAllocScratchBytes);
+    void *ws = nullptr;
+    if (need && batch > 0) {
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        int dev = -1;
+        const hipError_t err = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+        if (err != hipSuccess) return hip_fail(err, "finding the stream's device");
+        if (dev < 0 || dev >= kMaxDevices)
+            return fail(MSDA_ERR_UNSUPPORTED, "device %d outside [0, %d)", dev, kMaxDevices);
+        const int st = scratch_address(dev, &ws);
+        if (st) return st;
+    }
+    return backward_impl(dtype, dtype, batch, num_keys, num_heads, head_dim, num_levels,
+                         spatial_shapes, level_start_index, num_queries, num_points, value,
+                         sampling_locations, attention_weights, grad_output, grad_value,
+                         grad_sampling_locations, grad_attention_weights, accum,
+                         flags | MSDA_FLAG_SINGLE_STREAM, ws, ws ? kNoAllocScratchBytes : 0,
+                         stream);
 }
 
 int msda_backward_ex(int value_dtype, int param_dtype, int64_t batch, int64_t num_keys,

@@ -334,3 +334,19 @@ def test_single_stream_flag_is_known(lib):
     not (both stop before any launch: B = 0 returns after validation)."""
     assert bwd(lib, B=0, flags=8) == 0
     assert bwd(lib, B=0, flags=16) == 2
+
+
+def test_noalloc_backward_rejects_before_any_hip_call(lib):
+    """msda_backward_noalloc: a problem whose workspace exceeds the 32 MiB
+    static scratch is refused with MSDA_ERR_WORKSPACE, the scratch-continuing
+    flags with MSDA_ERR_SHAPE, invalid sizes with their own status; an empty
+    batch is OK. None of these reaches a HIP call."""
+    def nb(dtype=2, B=1, S=100, M=2, D=8, Q=16, K=2, accum=-1, flags=0, shapes=SHAPES):
+        return lib.msda_backward_noalloc(dtype, B, S, M, D, 2, shapes, None, Q, K, FAKE, FAKE,
+                                         FAKE, FAKE, FAKE, FAKE, FAKE, accum, flags, None)
+    # fp32 scratch of B*S*M*D fp32 = 16384 * 100 * 2 * 8 * 4 bytes = 100 MiB > 32 MiB
+    assert nb(B=16384, accum=1) == 6
+    assert "static scratch" in lib.msda_last_error().decode()
+    assert nb(flags=2) == 2 and nb(flags=4) == 2
+    assert nb(M=0) == 2
+    assert nb(B=0) == 0
