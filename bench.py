@@ -2,52 +2,57 @@
 """Benchmark of the MSDA core (forward + backward) on one MI355X.
 
 One step = one forward call and one backward call of the C ABI on the
-resident, seeded synthetic inputs of a workload (default: the decoder-shaped
-bf16 workload, B=4 Q=300 M=8 D=32 L=4 K=4, levels of an 800x1333 image). The
+resident, seeded synthetic inputs of a workload. The headline workload is the
+decoder-shaped bf16 one (B=4 Q=300 M=8 D=32 L=4 K=4, levels of an 800x1333
+image); the encoder-shaped workloads (fp16 encoder, odd-head fp32, large bf16
+encoder) are measured the same way in the line's `configs` object. The
 backward runs with the library's default accumulation (AUTO) and includes
 every kernel it launches.
 
-Timed region: the step is captured once in a HIP graph and replayed K times
-between two events (host dispatch removed, as with the pages' CUDA-graph
-cross-check); an eager run of the same steps is reported beside it. Per-kernel
-device times come from an instrumented eager pass: the library records a HIP
-event right before and right after each of its launches on the call's stream.
+Timing. The step is captured once in a HIP graph and replayed K times between
+two events (host dispatch removed, as with the pages' CUDA-graph cross-check);
+per-kernel device times and the phases' device spans come from an
+instrumented eager pass: the library launches each kernel with a pair of HIP
+events that the launch itself stamps at the kernel's start and end
+(hipExtLaunchKernel), the same interval rocprofv3's kernel trace reports.
+
+Algorithmic bytes (the method's own traffic; e = element size of value /
+output / grad rows, pe = of locations / weights, P = B*Q*M*L*K points,
+U = distinct (b, row, m) value rows with at least one in-bounds corner,
+N = B*S*M*D grad_value elements; U is computed exactly on the host):
+  forward    3*P*pe + B*Q*M*D*e + U*D*e
+  backward   3*P*pe + B*Q*M*D*e + U*D*e + 3*P*pe + N*e
+             (parameters, upstream gradient and touched value rows read;
+             grad_loc / grad_attn written; grad_value written once in full)
+Each term belongs to exactly one kernel, so the kernels' shares add up to the
+phase: parameters, upstream gradient, value rows and the per-point gradients
+to the kernel that writes grad_loc / grad_attn; of grad_value, the rows of
+levels summed with atomics that some corner touches to the kernel issuing
+those atomics, their untouched rows to the zero fill, the rows of binned
+levels to the accumulation, the rows of fp32-scratch levels to the scratch
+add. Everything else a kernel moves is reported apart as `overhead_bytes`
+(modelled, not measured): the zero fill's rows that atomics or bins later
+overwrite, the read of each atomically updated row (U_a*D*e_acc, e_acc = 4
+for fp32 rows), the scatter kernel's second read of parameters and upstream
+gradient, bin records (8 bytes per in-bounds corner of a binned level,
+written by the place / sort step and read by the accumulation), the count
+and sort steps' parameter reads, the accumulation's reads of upstream
+gradient rows, and the fp32 scratch's fill, read-modify-writes and read.
 
 Prints one JSON line:
-  value / ms_per_step   microseconds per forward+backward step (lower is better)
-  kernels               per-kernel average device time and algorithmic GB/s
-  roofline              the dominant kernel against the 8 TB/s HBM roofline:
-                        algorithmic bytes per launch / average launch duration
-  phases                the forward and the backward call as wholes: their
-                        kernels' algorithmic bytes / summed launch times
-  cold_us_per_step      context: one step timed alone after 1 GiB is written
-                        (L2 and the 256 MB MALL evicted)
-  device_copy_GBps      context: a 1 GiB device copy, bytes read + written / time
-  cpu_baseline          the CPU oracle (fp64 loops, OpenMP) on the same workload
-
-Algorithmic bytes per launch (e = element size of value / grad rows, pe = of
-locations / weights (fp32 beside 16-bit values in mixed workloads),
-P = B*Q*M*L*K points,
-U = distinct (b, row, m) value rows with at least one in-bounds corner,
-C = in-bounds corners, N = B*S*M*D grad_value elements):
-  forward          3*P*pe (locations + weights) + B*Q*M*D*e (output) + U*D*e
-  backward kernel  (msda_bwd_kernel; msda_grad_kernel without the atomics term
-                   when some level is binned)
-                   3*P*pe (params) + B*Q*M*D*e (grad_output) + U*D*e (value)
-                   + 3*P*pe (grad locations + grad weights)
-                   + atomics: 2*U'*D*e_acc (read-modify-write of the touched rows
-                     of levels not binned; e_acc = 4 for fp32 rows)
-  scatter          3*(P-P')*pe + B*Q*M*D*e + 2*U'*D*e_acc (atomics of the unbinned levels)
-  binned levels only (P', C', N' = their points, corners, grad_value elements):
-  bin count        2*P'*pe;  bin place  3*P'*pe + 8*C' (records written)
-  bin scan         3*nbins*4 (one workgroup), or tile sums nbins*4, tile offsets
-                   3*ntiles*4, tile scans 3*nbins*4 (large bin counts)
-  bin local sort   3*P'*pe + 8*C' + 8*nbins (count and place in one launch,
-                   bin ranges written) + N*e when it also zero-fills grad_value
-  bin accumulate   8*C' + B*Q*M*D*e + N'*e
-  scatter + accumulate in one launch: the sum of the two; likewise gradients +
-  local sort (+ zero fill) in one launch
-  zero fill        bytes written;  scratch add  rows * D * (4 + 2e)
+  value / ms_per_step   microseconds per forward+backward step of the headline
+                        workload (lower is better)
+  phases                forward and backward as wholes: algorithmic bytes / device
+                        span (first kernel's start to last kernel's end, from
+                        the launch-stamped events) against the 8 TB/s peak;
+                        each phase alone as a graph replay beside it (a
+                        replay adds ROCm's graph launch cost, ~10 us)
+  kernels               per kernel: time, algorithmic share, overhead bytes
+  roofline              the kernel with the largest time, its algorithmic share
+                        per launch / its average launch time
+  configs               the same figures for the encoder-shaped workloads
+  cpu_baseline          the CPU oracle (fp64 loops, OpenMP) on a bounded sample
+                        of the same workload, scaled to one call
 """
 
 from __future__ import annotations
@@ -73,9 +78,13 @@ HBM_PEAK_GBPS = 8000.0
 # machine (H100, Triton, bf16: forward 8 us + backward 56 us; msda-triton
 # README, section "Benchmarks"). Context for vs_baseline, not a target.
 PAGES_DECODER_BF16_US = 8.0 + 56.0
-# Device-scope atomic adds on MI355X are request-bound: about 21 G requests/s
-# measured for requests of 1 to 16 dwords inside one 64-byte segment.
-ATOMIC_CEILING_GREQ = 21.0
+HEADLINE = "decoder_bf16"
+DEFAULT_CONFIGS = ("encoder_fp16", "oddhead_fp32", "large_encoder_bf16")
+GRADIENT_KERNELS = ("msda_grad_kernel", "grad_sort_kernel", "msda_bwd_kernel")
+# Device-scope no-return atomic adds: about 21.3 G requests/s, one request
+# covering up to 16 dwords of one 64-byte segment (atomic_probe_kernel,
+# `bench.py --atomic-probe`; profiles/atomic_probe_kernel_request_ceiling.md).
+ATOMIC_CEILING_GREQ = 21.3
 ATOMIC_KERNELS = ("msda_bwd_kernel", "msda_scatter_kernel", "scatter_accum_kernel")
 
 
@@ -83,39 +92,172 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def touched_rows(inp, only_levels=None):
-    """(U, C): distinct (b, row, m) value rows that at least one in-bounds
-    corner lands on, and the number of in-bounds corners. Host-side
-    accounting of compulsory bytes (single-rounding pixel mapping as in the
-    kernels; products of an fp32 location and an integer width are exact in
-    fp64)."""
+# ---------------------------------------------------------- byte accounting
+
+def touched_rows_per_level(inp):
+    """Per level l: (U_l, C_l), the distinct (b, row, m) value rows of level l
+    that at least one in-bounds corner lands on, and the number of in-bounds
+    corners. Host-side accounting of compulsory bytes with the single-rounding
+    pixel mapping of the kernels (the product of an fp32 location and an
+    integer size is exact in fp64). Levels here never overlap (default level
+    starts), so counts over several levels are sums of these."""
     value = inp["value"]
     B, S, M, D = value.shape
-    loc = inp["sampling_locations"].to(torch.float64).numpy()
-    shapes = inp["spatial_shapes"].tolist()
-    mark = np.zeros(B * S * M, dtype=bool)
-    corners = 0
-    b_idx = np.arange(B).reshape(B, 1, 1, 1)
-    m_idx = np.arange(M).reshape(1, 1, M, 1)
-    start = 0
-    for l, (H, W) in enumerate(shapes):
-        if only_levels is not None and l not in only_levels:
-            start += H * W
-            continue
-        x = (loc[:, :, :, l, :, 0] * W - 0.5).astype(np.float32)
-        y = (loc[:, :, :, l, :, 1] * H - 0.5).astype(np.float32)
-        x0 = np.floor(x).astype(np.int64)
-        y0 = np.floor(y).astype(np.int64)
-        for dy in (0, 1):
-            for dx in (0, 1):
-                xx, yy = x0 + dx, y0 + dy
-                ok = (xx >= 0) & (xx < W) & (yy >= 0) & (yy < H)
-                row = start + yy * W + xx
-                key = (b_idx * S + row) * M + m_idx
-                mark[key[ok]] = True
-                corners += int(ok.sum())
-        start += H * W
-    return int(mark.sum()), corners
+    loc_t = inp["sampling_locations"]
+    out = []
+    m_idx = np.arange(M, dtype=np.int64).reshape(1, M, 1)
+    for l, (H, W) in enumerate(inp["spatial_shapes"].tolist()):
+        mark = np.zeros(B * H * W * M, dtype=bool)
+        corners = 0
+        for b in range(B):  # one batch at a time bounds host memory
+            lxy = loc_t[b, :, :, l].to(torch.float64).numpy()  # (Q, M, K, 2)
+            x0 = np.floor((lxy[..., 0] * W - 0.5).astype(np.float32)).astype(np.int64)
+            y0 = np.floor((lxy[..., 1] * H - 0.5).astype(np.float32)).astype(np.int64)
+            del lxy
+            for dy in (0, 1):
+                for dx in (0, 1):
+                    xx, yy = x0 + dx, y0 + dy
+                    ok = (xx >= 0) & (xx < W) & (yy >= 0) & (yy < H)
+                    mark[((b * H * W + yy * W + xx) * M + m_idx)[ok]] = True
+                    corners += int(ok.sum())
+        out.append((int(mark.sum()), corners))
+    return out
+
+
+class ByteModel:
+    """Algorithmic bytes of one forward and one backward call, their split
+    over the kernels, and the modelled overhead traffic (module docstring)."""
+
+    def __init__(self, wl, inp, level_modes, nbins):
+        e = torch.finfo(wl.dtype).bits // 8
+        pe = torch.finfo(wl.param_dtype or wl.dtype).bits // 8
+        B, S, M, D, L, K, Q = wl.B, wl.S, wl.M, wl.D, wl.L, wl.K, wl.num_queries
+        self.P = P = B * Q * M * L * K
+        self.N = N = B * S * M * D
+        t0 = time.perf_counter()
+        per = touched_rows_per_level(inp)
+        atomic = [l for l, m in enumerate(level_modes) if m == "native"]
+        scratch = [l for l, m in enumerate(level_modes) if m == "fp32_scratch"]
+        binned = [l for l, m in enumerate(level_modes) if m == "binned"]
+        self.U, self.C = sum(u for u, _ in per), sum(c for _, c in per)
+        U_a = sum(per[l][0] for l in atomic)
+        U_s = sum(per[l][0] for l in scratch)
+        C_b = sum(per[l][1] for l in binned)
+        log(f"byte model: U={self.U} rows, C={self.C} corners, {time.perf_counter() - t0:.1f} s")
+        rows = lambda lv: sum(B * wl.levels[l][0] * wl.levels[l][1] * M for l in lv)
+        N_a, N_s, N_b = rows(atomic) * D, rows(scratch) * D, rows(binned) * D
+        e_acc = 4 if wl.dtype == torch.float32 else e
+        P_a, P_b = B * Q * M * K * len(atomic), B * Q * M * K * len(binned)
+        go = B * Q * M * D * e
+        self.fwd = 3 * P * pe + go + self.U * D * e
+        self.bwd = 3 * P * pe + go + self.U * D * e + 3 * P * pe + N * e
+        grad = 3 * P * pe + go + self.U * D * e + 3 * P * pe
+        sh = {  # algorithmic share of each kernel
+            "msda_fwd_kernel": self.fwd,
+            "msda_grad_kernel": grad,
+            "msda_bwd_kernel": grad + U_a * D * e + U_s * D * e,
+            "msda_scatter_kernel": U_a * D * e + U_s * D * e,
+            "zero_fill": (N_a - U_a * D) * e,
+            "bin_accum_kernel": N_b * e,
+            "scratch_add_kernel": N_s * e,
+        }
+        sh["scatter_accum_kernel"] = sh["msda_scatter_kernel"] + sh["bin_accum_kernel"]
+        sh["grad_sort_kernel"] = grad + sh["zero_fill"]
+        rec = 8 * C_b
+        ov = {  # modelled traffic beyond the share
+            "zero_fill": N * e - sh["zero_fill"],
+            "msda_bwd_kernel": U_a * D * e_acc + 2 * U_s * D * 4,
+            "msda_scatter_kernel": 3 * P_a * pe + go + U_a * D * e_acc + 2 * U_s * D * 4,
+            "scratch_zero": N_s * 4, "scratch_add_kernel": N_s * 4,
+            "bin_zero": (nbins + 1) * 4, "bin_count": 2 * P_b * pe,
+            "bin_scan": 3 * nbins * 4, "bin_tile_sum": nbins * 4,
+            "bin_tile_offsets": 3 * (-(-nbins // 4096)) * 4, "bin_tile_scan": 3 * nbins * 4,
+            "bin_place": 3 * P_b * pe + rec,
+            "bin_local_sort": 3 * P_b * pe + rec + 8 * nbins,
+            "bin_accum_kernel": rec + go,
+        }
+        ov["scatter_accum_kernel"] = ov["msda_scatter_kernel"] + ov["bin_accum_kernel"]
+        # the gradient launch that also sorts and fills
+        ov["grad_sort_kernel"] = ov["bin_local_sort"] + ov["zero_fill"]
+        self.share, self.overhead = sh, ov
+        # atomic requests: one per in-bounds corner per 64-byte segment of
+        # its target row (16-bit rows of D*e bytes, fp32 rows of D*4)
+        seg16, seg32 = -(-D * e_acc // 64), -(-D * 4 // 64)
+        self.atomic_requests = (sum(per[l][1] for l in atomic) * seg16
+                                + sum(per[l][1] for l in scratch) * seg32)
+
+    def kernel(self, name):
+        return self.share.get(name, 0), self.overhead.get(name, 0)
+
+
+# ------------------------------------------------------------------- timing
+
+def capture(fn):
+    """A HIP graph of one call of `fn` (after two warm calls on the capture stream)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(g, reps):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps  # us
+
+
+def kernel_times(call, n_inst):
+    """Average device time of every kernel of the forward and of the backward,
+    from the library's per-launch events (stamped at kernel start and end),
+    and each call's device span: from its first kernel's start to its last
+    kernel's end, whichever streams they ran on (averages over n_inst calls).
+    Returns (per-kernel us, forward span us, backward span us)."""
+    from scale_deformable_attention_amd._binding import (launch_event_names,
+                                                         launch_events_recorded,
+                                                         set_launch_events)
+    nev = 32
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + nev)] for _ in range(n_inst)]
+    for row in evs:
+        for ev in row:
+            ev.record()  # torch creates the HIP event on first record
+    torch.cuda.synchronize()
+    names = None
+    for i in range(n_inst):
+        set_launch_events(evs[i][:2])
+        call.forward()
+        set_launch_events(evs[i][2:])
+        call.backward()
+        n_bwd = launch_events_recorded() // 2
+        names = launch_event_names()
+        assert n_bwd == len(names), (n_bwd, names)
+    torch.cuda.synchronize()
+    kt = {"msda_fwd_kernel": float(np.mean([r[0].elapsed_time(r[1]) for r in evs])) * 1e3}
+    for j, nm in enumerate(names):
+        key = nm if nm not in kt else f"{nm}#{j}"
+        kt[key] = float(np.mean([r[2 + 2 * j].elapsed_time(r[3 + 2 * j]) for r in evs])) * 1e3
+    n = len(names)
+
+    def span(r):  # relative to the first launch's start event
+        starts = [r[2].elapsed_time(r[2 + 2 * j]) for j in range(n)]
+        stops = [r[2].elapsed_time(r[3 + 2 * j]) for j in range(n)]
+        return max(stops) - min(0.0, min(starts))
+    bwd_span = float(np.mean([span(r) for r in evs])) * 1e3
+    return kt, kt["msda_fwd_kernel"], bwd_span
 
 
 def kernel_source_hash() -> str:
@@ -149,81 +291,162 @@ def load_traffic(workload: str, kernel: str, src_hash: str):
         return None
 
 
-def time_graph(fn, reps: int, inner: int) -> float:
-    """Average device time of `fn` per call: `inner` calls captured in one HIP
-    graph, replayed `reps` times between events on the capture stream."""
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for _ in range(3):
-            fn()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(inner):
-            fn()
-    torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * inner)  # us
+def frac(nbytes, us):
+    gbps = nbytes / (us * 1e-6) / 1e9 if us > 0 else 0.0
+    return round(gbps, 1), round(gbps / HBM_PEAK_GBPS, 4)
 
 
-def cpu_baseline(inp, min_seconds: float = 10.0, max_reps: int = 2000):
+# --------------------------------------------------------------- cpu oracle
+
+def cpu_baseline(inp, seconds: float):
+    """The oracle's forward + backward on a bounded sample of the workload,
+    scaled to one call. The sample is the first Q' queries of every batch
+    (all of them when a whole call fits the time budget); the per-call fixed
+    cost (fp64 conversion of value, the grad_value fill) is timed with zero
+    queries and counted once, the rest scaled by Q / Q'."""
     import oracle  # the CPU-baseline leg is the only product-side user of the oracle
-    args = (inp["value"], inp["spatial_shapes"], None, inp["sampling_locations"],
-            inp["attention_weights"])
-    oracle.forward(*args)  # warm (page-in, thread pool)
-    reps, t0 = 0, time.perf_counter()
-    while True:
+    Q = inp["sampling_locations"].shape[1]
+
+    def sub(qn):
+        return {k: (v[:, :qn].contiguous() if k in ("sampling_locations", "attention_weights",
+                                                    "grad_output") else v)
+                for k, v in inp.items()}
+
+    def call(d):
+        args = (d["value"], d["spatial_shapes"], None, d["sampling_locations"],
+                d["attention_weights"])
+        t0 = time.perf_counter()
         oracle.forward(*args)
-        oracle.backward(*args, inp["grad_output"])
-        reps += 1
-        el = time.perf_counter() - t0
-        if (el >= min_seconds and reps >= 3) or reps >= max_reps:
+        oracle.backward(*args, d["grad_output"])
+        return time.perf_counter() - t0
+
+    fixed = min(call(sub(0)) for _ in range(2))
+    q_probe = min(Q, 64)
+    per_q = max(call(sub(q_probe)) - fixed, 1e-9) / q_probe
+    q_s = int(min(Q, max(q_probe, (seconds / 2) / per_q)))
+    d = sub(q_s)
+    times, t_start = [], time.perf_counter()
+    while True:
+        times.append(call(d))
+        if len(times) >= 3 or time.perf_counter() - t_start >= seconds / 2:
             break
-    return el / reps * 1e6, reps, oracle.max_threads()
+    t = float(np.median(times))
+    est = t if q_s == Q else fixed + max(t - fixed, 0.0) * Q / q_s
+    sample = (f"all {Q} queries" if q_s == Q else f"queries [0, {q_s}) of {Q} per batch, "
+              f"scaled by Q/Q' (fixed per-call cost {fixed * 1e3:.0f} ms counted once)")
+    return est * 1e6, len(times), oracle.max_threads(), sample
 
 
-def time_foil(g, call, fwd_bytes: int, reps: int = 20) -> dict:
-    """The point-parallel forward foil against the forward kernel, each timed
-    with the library's per-launch event pairs (same bias for both)."""
-    from scale_deformable_attention_amd._binding import (msda_forward_point_parallel,
-                                                         set_launch_events)
-    args = (g["value"], g["spatial_shapes"], None, g["sampling_locations"], g["attention_weights"])
-    fout = msda_forward_point_parallel(*args)
-    out = call.forward()
+# ------------------------------------------------------------- measurement
+
+def measure(name, accum, steps, warmup, n_inst, headline=False):
+    from scale_deformable_attention_amd import PreparedCall
+    from scale_deformable_attention_amd.workloads import make_inputs, workload
+
+    wl = workload(name)
+    dev = torch.device("cuda:0")
+    log(f"workload {wl.name}: B={wl.B} Q={wl.num_queries} S={wl.S} M={wl.M} D={wl.D} "
+        f"L={wl.L} K={wl.K} {wl.dtype}")
+    inp = make_inputs(wl)
+    g = {k: (v.to(dev) if k != "spatial_shapes" else v) for k, v in inp.items()}
+    call = PreparedCall(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                        g["attention_weights"], g["grad_output"], accum=accum)
+    log(f"backward accumulation: {accum} -> {call.resolved_accum}")
+
+    def step():
+        call.forward()
+        call.backward()
+
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
-    diff = float((fout.float() - out.float()).abs().max())
+    g_step, g_fwd, g_bwd = capture(step), capture(call.forward), capture(call.backward)
+    us_step = time_replays(g_step, steps)
+    fwd_graph_us = time_replays(g_fwd, steps)
+    bwd_graph_us = time_replays(g_bwd, steps)
+    kt, fwd_us, bwd_us = kernel_times(call, n_inst)
+    log(f"{name}: {us_step:.2f} us/step (graph replay, {steps} steps); forward {fwd_us:.2f} us, "
+        f"backward {bwd_us:.2f} us (device spans; alone as graph replays {fwd_graph_us:.2f} / "
+        f"{bwd_graph_us:.2f} us)")
+    log("kernels (us): " + ", ".join(f"{k} {v:.2f}" for k, v in kt.items()))
+    modes, nbins = call.plan()
+    bm = ByteModel(wl, inp, modes, nbins)
+    kernels = {}
+    for k, us in kt.items():
+        share, over = bm.kernel(k.split("#")[0])
+        gbps, fr = frac(share, us)
+        kernels[k] = {"us": round(us, 3), "bytes": int(share), "overhead_bytes": int(over),
+                      "GBps": gbps, "frac": fr}
+    fg, ff = frac(bm.fwd, fwd_us)
+    bg, bf = frac(bm.bwd, bwd_us)
+    phases = {"forward": {"us": round(fwd_us, 3), "bytes": int(bm.fwd), "GBps": fg, "frac": ff,
+                          "graph_replay_us": round(fwd_graph_us, 3)},
+              "backward": {"us": round(bwd_us, 3), "bytes": int(bm.bwd), "GBps": bg, "frac": bf,
+                           "graph_replay_us": round(bwd_graph_us, 3),
+                           "overhead_bytes": int(sum(kernels[k]["overhead_bytes"]
+                                                     for k in kernels
+                                                     if k != "msda_fwd_kernel")),
+                           "kernel_sum_us": round(sum(v for k, v in kt.items()
+                                                      if k != "msda_fwd_kernel"), 3)}}
+    kname = max(kt, key=kt.get)
+    src_hash = kernel_source_hash()
+    kshare = kernels[kname]["bytes"]
+    roofline = {"bound": "hbm", "achieved": kernels[kname]["GBps"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": kernels[kname]["frac"],
+                "traffic": load_traffic(wl.name, kname.split("#")[0], src_hash),
+                "kernel": kname, "kernel_us": kernels[kname]["us"],
+                "algorithmic_bytes_per_launch": int(kshare),
+                "kernel_source_sha": src_hash}
+    atomic_rate = None
+    if kname.split("#")[0] in ATOMIC_KERNELS and bm.atomic_requests:
+        rate = bm.atomic_requests / (kt[kname] * 1e-6) / 1e9
+        atomic_rate = {"kernel": kname, "requests": int(bm.atomic_requests),
+                       "achieved": round(rate, 2), "ceiling": ATOMIC_CEILING_GREQ,
+                       "unit": "G requests/s", "frac": round(rate / ATOMIC_CEILING_GREQ, 4)}
+    res = {"workload": wl.name, "dtype": str(wl.dtype).replace("torch.", ""),
+           "param_dtype": str(wl.param_dtype or wl.dtype).replace("torch.", ""),
+           "B": wl.B, "Q": wl.num_queries, "S": wl.S, "M": wl.M, "D": wl.D, "L": wl.L,
+           "K": wl.K, "levels": [list(x) for x in wl.levels], "accum": call.resolved_accum,
+           "level_modes": modes, "us_per_step": round(us_step, 3), "steps": steps,
+           "phases": phases, "kernels": kernels, "roofline": roofline, "atomic_rate": atomic_rate,
+           "touched_rows_U": bm.U, "corners_C": bm.C, "points_P": bm.P}
+    extra = {"inp": inp, "g": g, "call": call, "step": step, "g_step": g_step, "wl": wl}
+    return res, extra
 
-    def kernel_us(fn):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-        for pair in evs:
-            for e in pair:
-                e.record()
-        torch.cuda.synchronize()
-        for pair in evs:
-            set_launch_events(pair)
-            fn()
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
 
-    foil_us = kernel_us(lambda: msda_forward_point_parallel(*args, output=fout))
-    fwd_us = kernel_us(call.forward)
-    log(f"point-parallel foil {foil_us:.2f} us vs forward kernel {fwd_us:.2f} us "
-        f"(max |difference| {diff:.3g})")
-    gbps = lambda us: fwd_bytes / (us * 1e-6) / 1e9
-    return {"kernel": "msda_foil_kernel", "us": round(foil_us, 3), "GBps": round(gbps(foil_us), 1),
-            "frac": round(gbps(foil_us) / HBM_PEAK_GBPS, 4), "forward_us": round(fwd_us, 3),
-            "forward_GBps": round(gbps(fwd_us), 1),
-            "forward_frac": round(gbps(fwd_us) / HBM_PEAK_GBPS, 4),
-            "max_abs_diff_vs_forward": diff}
+def atomic_probe(reps=20):
+    """Request rate of no-return atomic adds (fp32 and packed bf16) for runs of
+    1, 4 and 16 dwords per 64-byte segment, on an L2-sized and an HBM-sized
+    target; kernel times from the launch-stamped events."""
+    from scale_deformable_attention_amd._binding import probe_atomic_requests, set_launch_events
+    out = []
+    for mib in (4, 64):
+        buf = torch.zeros(mib << 18, dtype=torch.float32, device="cuda:0")
+        for bf16 in (False, True):
+            for run in (1, 4, 16):
+                wgs, iters = 4096, 64 if run == 1 else 256
+                evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                       for _ in range(reps)]
+                for pair in evs:
+                    for e in pair:
+                        e.record()
+                probe_atomic_requests(buf, bf16, run, wgs, iters)  # warm
+                torch.cuda.synchronize()
+                req = 0
+                for pair in evs:
+                    set_launch_events(pair)
+                    req = probe_atomic_requests(buf, bf16, run, wgs, iters)
+                torch.cuda.synchronize()
+                us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+                rate = req / (us * 1e-6) / 1e9
+                out.append({"target_MiB": mib, "type": "pk_bf16" if bf16 else "f32",
+                            "dwords_per_request": run, "requests": req, "us": round(us, 2),
+                            "G_requests_per_s": round(rate, 2),
+                            "G_dwords_per_s": round(rate * run, 1)})
+                log(f"atomic probe {mib} MiB {'pk_bf16' if bf16 else 'f32'} run={run}: "
+                    f"{req} requests in {us:.1f} us = {rate:.2f} G requests/s")
+        del buf
+    return out
 
 
 def main():
@@ -231,23 +454,28 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decoder_bf16")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--accum", default="auto",
                     choices=["auto", "native", "fp32_scratch", "per_level", "binned", "mixed"])
+    ap.add_argument("--configs", default=",".join(DEFAULT_CONFIGS),
+                    help="comma-separated workloads measured besides the headline ('none': skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU budget of the headline's oracle sample (each config gets half)")
     ap.add_argument("--profile-only", action="store_true",
-                    help="run warmup + timed steps only (for rocprofv3 runs)")
+                    help="run warmup + timed steps of --workload only (for rocprofv3 runs)")
     ap.add_argument("--foil", action="store_true",
-                    help="also time the point-parallel forward foil against the forward kernel")
+                    help="with --profile-only: also run the point-parallel forward foil")
+    ap.add_argument("--atomic-probe", action="store_true",
+                    help="measure the atomic request rate instead (measurement kernel)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="with --profile-only: also run 5 plain device copies of this many MiB "
                          "(reference dispatches for scaling FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1",
-                          "n_gpus": args.gpus}), flush=True)
+        print(json.dumps({"error": "bench.py measures one GPU; every box here has one, so "
+                                   "--gpus must be 1", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
@@ -257,37 +485,32 @@ def main():
     from scale_deformable_attention_amd.workloads import make_inputs, workload
 
     load_library()  # raises if the HIP library is missing
-    wl = workload(args.workload)
     dev = torch.device("cuda:0")
-    log(f"workload {wl.name}: B={wl.B} Q={wl.num_queries} S={wl.S} M={wl.M} D={wl.D} "
-        f"L={wl.L} K={wl.K} {wl.dtype}")
-    inp = make_inputs(wl)
-    g = {k: (v.to(dev) if k != "spatial_shapes" else v) for k, v in inp.items()}
-    call = PreparedCall(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
-                        g["attention_weights"], g["grad_output"], accum=args.accum)
-    log(f"backward accumulation: {args.accum} -> {call.resolved_accum}")
 
-    def step():
-        call.forward()
-        call.backward()
+    if args.atomic_probe:
+        rows = atomic_probe()
+        print(json.dumps({"atomic_probe": rows}), flush=True)
+        return
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
     if args.profile_only:
-        K = args.steps
-        for _ in range(K):
-            step()
+        wl = workload(args.workload)
+        inp = make_inputs(wl)
+        g = {k: (v.to(dev) if k != "spatial_shapes" else v) for k, v in inp.items()}
+        call = PreparedCall(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                            g["attention_weights"], g["grad_output"], accum=args.accum)
+        log(f"workload {wl.name}, backward accumulation {args.accum} -> {call.resolved_accum}")
+        for _ in range(args.warmup + args.steps):
+            call.forward()
+            call.backward()
         torch.cuda.synchronize()
-        log(f"ran {K} eager steps")
+        log(f"ran {args.warmup} + {args.steps} eager steps")
         if args.foil:
             from scale_deformable_attention_amd._binding import msda_forward_point_parallel
-            for _ in range(K):
+            for _ in range(args.steps):
                 msda_forward_point_parallel(g["value"], g["spatial_shapes"], None,
                                             g["sampling_locations"], g["attention_weights"])
             torch.cuda.synchronize()
-            log(f"ran {K} point-parallel foil forwards")
+            log(f"ran {args.steps} point-parallel foil forwards")
         if args.calib_copy_mb:
             n = args.calib_copy_mb * (1 << 20) // 4
             src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -295,40 +518,17 @@ def main():
             for _ in range(5):
                 dst.copy_(src)
             torch.cuda.synchronize()
-            log(f"calibration: 5 copies of {args.calib_copy_mb} MiB (read {args.calib_copy_mb} MiB, "
-                f"write {args.calib_copy_mb} MiB each)")
+            log(f"calibration: 5 copies of {args.calib_copy_mb} MiB (read {args.calib_copy_mb} "
+                f"MiB, write {args.calib_copy_mb} MiB each)")
         return
 
     K = args.steps
-    # Timed region: K replays of one captured step.
-    graph_ok = True
-    try:
-        s_cap = torch.cuda.Stream()
-        s_cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s_cap):
-            step()
-        torch.cuda.current_stream().wait_stream(s_cap)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        graph.replay()
-        torch.cuda.synchronize()
-    except Exception as exc:  # fall back to eager stepping
-        graph_ok = False
-        log(f"graph capture failed ({exc}); timing eager steps")
+    head, ex = measure(args.workload, args.accum, K, args.warmup, n_inst=min(K, 50),
+                       headline=True)
+    wl, call, step, g_step = ex["wl"], ex["call"], ex["step"], ex["g_step"]
+
+    # Context for the headline: eager steps, host enqueue, cold caches, copy bandwidth.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(K):
-        if graph_ok:
-            graph.replay()
-        else:
-            step()
-    e1.record()
-    torch.cuda.synchronize()
-    us_step = e0.elapsed_time(e1) * 1e3 / K
-    # Eager steps, for context.
     torch.cuda.synchronize()
     h0 = time.perf_counter()
     e0.record()
@@ -339,171 +539,82 @@ def main():
     torch.cuda.synchronize()
     eager_us = e0.elapsed_time(e1) * 1e3 / K
     host_us = (h1 - h0) * 1e6 / K
-    log(f"timed {K} steps: {us_step:.2f} us/step ({'graph replay' if graph_ok else 'eager'}); "
-        f"eager {eager_us:.2f} us/step, host enqueue {host_us:.2f} us/step")
-
-    # Cold caches, for context: a 1 GiB write between steps evicts L2 and the
-    # 256 MB MALL; each step is timed alone (one launch of the captured step).
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     n_cold = min(K, 50)
     c_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(n_cold)]
     for c0, c1 in c_evs:
-        flush.fill_(1.0)
+        flush.fill_(1.0)  # 1 GiB written: L2 and the 256 MB MALL evicted
         c0.record()
-        if graph_ok:
-            graph.replay()
-        else:
-            step()
+        g_step.replay()
         c1.record()
     torch.cuda.synchronize()
     cold_us = float(np.mean([c0.elapsed_time(c1) for c0, c1 in c_evs])) * 1e3
-    # Device copy bandwidth, for context: 10 copies of 1 GiB (read + write).
-    cp_src = flush
-    cp_dst = torch.empty_like(cp_src)
-    cp_dst.copy_(cp_src)
+    cp_dst = torch.empty_like(flush)
+    cp_dst.copy_(flush)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(10):
-        cp_dst.copy_(cp_src)
+        cp_dst.copy_(flush)
     e1.record()
     torch.cuda.synchronize()
-    copy_gbps = 10 * 2 * cp_src.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del flush, cp_src, cp_dst
-    log(f"cold-cache step {cold_us:.2f} us (1 GiB written between steps); "
-        f"device copy {copy_gbps:.0f} GB/s")
+    copy_gbps = 10 * 2 * flush.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del flush, cp_dst
+    log(f"eager {eager_us:.2f} us/step, host enqueue {host_us:.2f} us/step, cold {cold_us:.2f} "
+        f"us, device copy {copy_gbps:.0f} GB/s")
 
-    # Per-kernel device times: events right before / after each launch.
-    from scale_deformable_attention_amd._binding import (launch_event_names, launch_events_recorded,
-                                                         set_launch_events)
-    n_inst = min(K, 50)
-    nev = 16
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + nev)] for _ in range(n_inst)]
-    for row in evs:
-        for ev in row:
-            ev.record()
-    torch.cuda.synchronize()
-    n_bwd = None
-    for i in range(n_inst):
-        set_launch_events(evs[i][:2])
-        call.forward()
-        set_launch_events(evs[i][2:])
-        call.backward()
-        n_bwd = launch_events_recorded() // 2
-    bwd_names = launch_event_names()  # the library names each instrumented launch
-    torch.cuda.synchronize()
-    assert n_bwd == len(bwd_names), (n_bwd, bwd_names)
-    ktimes = {"msda_fwd_kernel": float(np.mean([evs[i][0].elapsed_time(evs[i][1])
-                                                 for i in range(n_inst)])) * 1e3}
-    for j, nm in enumerate(bwd_names):
-        ktimes[nm] = float(np.mean([evs[i][2 + 2 * j].elapsed_time(evs[i][3 + 2 * j])
-                                    for i in range(n_inst)])) * 1e3
-    log("kernels (us): " + ", ".join(f"{k} {v:.2f}" for k, v in ktimes.items()))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {wl.name}")
+        cpu_us, reps, threads, sample = cpu_baseline(ex["inp"], args.cpu_seconds)
+        cpu = {"value": round(cpu_us, 1), "unit": "us/call (fwd+bwd)", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{wl.name}: {sample}; {reps} timed calls; "
+                         f"{platform.processor() or platform.machine()}"}
+    del ex
 
-    # Algorithmic bytes per launch.
-    e = torch.finfo(wl.dtype).bits // 8
-    pe = torch.finfo(wl.param_dtype or wl.dtype).bits // 8  # locations / weights
-    B, S, M, D, L, Kp, Q = wl.B, wl.S, wl.M, wl.D, wl.L, wl.K, wl.num_queries
-    P = B * Q * M * L * Kp
-    N = B * S * M * D
-    U, C = touched_rows(inp)
-    level_modes, nb = call.plan()
-    scr_levels = [l for l, m in enumerate(level_modes) if m == "fp32_scratch"]
-    bin_levels = [l for l, m in enumerate(level_modes) if m == "binned"]
-    U_scr = touched_rows(inp, only_levels=scr_levels)[0] if scr_levels else 0
-    U_bin, C_bin = touched_rows(inp, only_levels=bin_levels) if bin_levels else (0, 0)
-    scratch_rows = sum(B * h * w * M for l, (h, w) in enumerate(wl.levels) if l in scr_levels)
-    bin_rows = sum(B * h * w * M for l, (h, w) in enumerate(wl.levels) if l in bin_levels)
-    P_bin = B * Q * M * Kp * len(bin_levels)
-    common = 3 * P * pe + B * Q * M * D * e + U * D * e + 3 * P * pe
-    e_acc = 4 if wl.dtype == torch.float32 else e
-    # a zero fill that did not get its own launch ran inside the sort's launch
-    zero_fused = int("zero_fill" not in ktimes and any(m != "binned" for m in level_modes))
-    kbytes = {"msda_fwd_kernel": 3 * P * pe + B * Q * M * D * e + U * D * e,
-              "zero_fill": N * e, "scratch_zero": scratch_rows * D * 4,
-              "scratch_add_kernel": scratch_rows * D * (4 + 2 * e),
-              # atomics: read-modify-write of the touched rows of unbinned levels
-              "msda_bwd_kernel": common + 2 * ((U - U_scr - U_bin) * D * e_acc + U_scr * D * 4),
-              "msda_grad_kernel": common,
-              "msda_scatter_kernel": 3 * (P - P_bin) * pe + B * Q * M * D * e
-              + 2 * (U - U_bin) * D * e_acc,
-              "bin_zero": (nb + 1) * 4, "bin_count": 2 * P_bin * pe, "bin_scan": 3 * nb * 4,
-              "bin_place": 3 * P_bin * pe + 8 * C_bin,
-              "bin_local_sort": 3 * P_bin * pe + 8 * C_bin + 8 * nb + zero_fused * N * e,
-              "bin_tile_sum": nb * 4, "bin_tile_offsets": 3 * (-(-nb // 4096)) * 4,
-              "bin_tile_scan": 3 * nb * 4,
-              "bin_accum_kernel": 8 * C_bin + B * Q * M * D * e + bin_rows * D * e}
-    kbytes["scatter_accum_kernel"] = kbytes["msda_scatter_kernel"] + kbytes["bin_accum_kernel"]
-    kbytes["grad_sort_kernel"] = kbytes["msda_grad_kernel"] + kbytes["bin_local_sort"]
-    kernels = {k: {"us": round(v, 3), "bytes": int(kbytes[k]),
-                   "GBps": round(kbytes[k] / (v * 1e-6) / 1e9, 1)} for k, v in ktimes.items()}
-    # The forward call and the backward call as wholes: algorithmic bytes of
-    # their kernels over the sum of their launch times (event pairs), against
-    # the 8 TB/s peak.
-    phases = {}
-    for ph, names in (("forward", ["msda_fwd_kernel"]),
-                      ("backward", [k for k in ktimes if k != "msda_fwd_kernel"])):
-        t = sum(ktimes[k] for k in names)
-        by = sum(kbytes[k] for k in names)
-        phases[ph] = {"us": round(t, 3), "bytes": int(by),
-                      "GBps": round(by / (t * 1e-6) / 1e9, 1),
-                      "frac": round(by / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
-    kname = max(ktimes, key=ktimes.get)
-    kus = ktimes[kname]
-    achieved = kbytes[kname] / (kus * 1e-6) / 1e9
-    src_hash = kernel_source_hash()
-    traffic = load_traffic(wl.name, kname, src_hash)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "kernel": kname, "kernel_us": round(kus, 3),
-                "algorithmic_bytes_per_launch": int(kbytes[kname]), "kernel_source_sha": src_hash}
-
-    # Context for a kernel bound by atomics rather than HBM: its requests (one
-    # per in-bounds corner per 64-byte segment of the target row: packed
-    # 16-bit rows of D*e bytes, fp32 rows of D*4) per second of launch time,
-    # against the measured request ceiling.
-    atomic_rate = None
-    if kname in ATOMIC_KERNELS:
-        seg = {"native": -(-D * (4 if wl.dtype == torch.float32 else e) // 64),
-               "fp32_scratch": -(-D * 4 // 64)}
-        reqs = sum(touched_rows(inp, only_levels=[l])[1] * seg[m]
-                   for l, m in enumerate(level_modes) if m in seg)
-        rate = reqs / (kus * 1e-6) / 1e9
-        atomic_rate = {"kernel": kname, "requests": int(reqs), "achieved": round(rate, 2),
-                       "ceiling": ATOMIC_CEILING_GREQ, "unit": "G requests/s",
-                       "frac": round(rate / ATOMIC_CEILING_GREQ, 4)}
+    configs = {}
+    names = [] if args.configs in ("", "none") else args.configs.split(",")
+    for name in names:
+        if name == args.workload:
+            continue
+        res, cex = measure(name, args.accum, max(10, min(K, 50)), min(args.warmup, 5),
+                           n_inst=10)
+        if not args.no_cpu_baseline:
+            log(f"timing the CPU oracle on {name}")
+            cpu_us, reps, threads, sample = cpu_baseline(cex["inp"], args.cpu_seconds / 2)
+            res["cpu_baseline"] = {"value": round(cpu_us, 1), "unit": "us/call (fwd+bwd)",
+                                   "cores": threads, "kind": "oracle",
+                                   "sample": f"{name}: {sample}; {reps} timed calls"}
+        del cex
+        torch.cuda.empty_cache()
+        configs[name] = res
 
     result = {
-        "metric": METRIC, "value": round(us_step, 3), "unit": "us/call (fwd+bwd)",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(us_step / 1e3, 6),
+        "metric": METRIC, "value": head["us_per_step"], "unit": "us/call (fwd+bwd)",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(head["us_per_step"] / 1e3, 6),
         "higher_is_better": False, "scaling": "weak",
-        "vs_baseline": round(us_step / PAGES_DECODER_BF16_US, 4)
-        if wl.name == "decoder_bf16" else None,
+        "vs_baseline": round(head["us_per_step"] / PAGES_DECODER_BF16_US, 4)
+        if wl.name == HEADLINE else None,
         "dtype": {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[wl.dtype],
         "data": "synthetic (seeded; stands in for Deformable-DETR COCO inputs)",
-        "config": {"workload": wl.name, "B": B, "Q": Q, "S": S, "M": M, "D": D, "L": L, "K": Kp,
-                   "levels": [list(x) for x in wl.levels], "accum": call.resolved_accum,
-                   "param_dtype": str(wl.param_dtype or wl.dtype).replace("torch.", ""),
-                   "parallelism": "single GPU"},
-        "timing": "graph replay" if graph_ok else "eager",
+        "config": {k: head[k] for k in ("workload", "B", "Q", "S", "M", "D", "L", "K", "levels",
+                                        "accum", "param_dtype")} | {"parallelism": "single GPU"},
+        "timing": "graph replay; kernels: launch-stamped events",
+        "fwd_us": head["phases"]["forward"]["us"], "bwd_us": head["phases"]["backward"]["us"],
+        "phases": head["phases"], "kernels": head["kernels"], "roofline": head["roofline"],
+        "atomic_rate": head["atomic_rate"],
+        "level_modes": head["level_modes"],
+        "touched_rows_U": head["touched_rows_U"], "corners_C": head["corners_C"],
+        "points_P": head["points_P"],
         "eager_us_per_step": round(eager_us, 3), "host_enqueue_us": round(host_us, 3),
         "cold_us_per_step": round(cold_us, 3), "cold_flush_bytes": 1 << 30,
         "device_copy_GBps": round(copy_gbps, 1),
-        "fwd_us": round(ktimes["msda_fwd_kernel"], 3),
-        "bwd_us": round(sum(v for k, v in ktimes.items() if k != "msda_fwd_kernel"), 3),
-        "kernels": kernels, "phases": phases, "touched_rows_U": U, "corners_C": C, "points_P": P,
-        "roofline": roofline, "atomic_rate": atomic_rate,
+        "configs": configs,
     }
-    if args.foil:
-        result["foil"] = time_foil(g, call, kbytes["msda_fwd_kernel"])
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle (cpu_baseline)")
-        cpu_us, reps_done, threads = cpu_baseline(inp, args.cpu_seconds)
-        result["cpu_baseline"] = {
-            "value": round(cpu_us, 1), "unit": "us/call (fwd+bwd)", "cores": threads,
-            "kind": "oracle",
-            "sample": f"full {wl.name} workload, {reps_done} forward+backward calls, "
-                      f"{platform.processor() or platform.machine()}"}
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

@@ -198,6 +198,25 @@ int msda_forward_point_parallel(int dtype, int64_t batch, int64_t num_keys, int6
                                 const void *attention_weights, void *output, void *stream);
 
 /*
+ * Measurement kernel, not part of the MSDA computation: the request rate of
+ * device-scope no-return atomic adds, which bounds the backward's grad_value
+ * scatter on atomically accumulated levels (course page "5. The backward
+ * kernel", section "Scatter needs atomics"). Launches `workgroups` x 256
+ * threads; every thread makes `iters` adds of 1 (fp32, or packed bf16 pairs
+ * when bf16 != 0) into `buffer` (device, 64-byte aligned; the largest power
+ * of two of whole 64-byte segments in buffer_bytes is used, up to 2^30;
+ * contents overwritten), in runs of dwords_per_request
+ * (1, 2, 4, 8 or 16) consecutive lanes that each address one 64-byte
+ * segment, lane i of a run its dword i, and no two runs in flight the same
+ * segment. *requests receives the number of atomic requests the launch makes
+ * (threads / dwords_per_request * iters); time the launch with
+ * msda_set_launch_events. workgroups in [1, 2^24], iters >= 1.
+ */
+int msda_probe_atomic_requests(void *buffer, size_t buffer_bytes, int bf16,
+                               int dwords_per_request, int64_t workgroups, int iters,
+                               int64_t *requests, void *stream);
+
+/*
  * Bytes of device workspace msda_backward needs for `accum` on this problem
  * (0 for NATIVE, and for fp32 data). Returns 0 and sets the last error for
  * invalid arguments; host-only, needs no GPU.
@@ -341,10 +360,11 @@ int msda_sampling_prep_backward(int dtype, int64_t batch, int64_t num_queries, i
 /*
  * Instrumentation for profilers and benchmarks: the next msda_forward or
  * msda_backward call made by this thread records events[2i] (hipEvent_t
- * passed as void*) on its stream right before its i-th kernel launch and
- * events[2i+1] right after it, while 2i+1 < count (count <= 64); the setting
- * then clears itself. Kernel i's device time is the time between the two
- * events. The events are the caller's.
+ * passed as void*) when its i-th kernel starts on the device and events[2i+1]
+ * when it ends (hipExtLaunchKernel's launch-packet timestamps), while
+ * 2i+1 < count (count <= 64); the setting then clears itself. Kernel i's
+ * device time is the time between the two events (a launch step that ran no
+ * kernel records both back to back). The events are the caller's.
  */
 int msda_set_launch_events(void *const *events, int count);
 

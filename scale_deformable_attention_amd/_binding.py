@@ -46,7 +46,7 @@ EXPORTED_SYMBOLS = ("msda_forward", "msda_forward_ex", "msda_forward_point_paral
                     "msda_abi_version", "msda_set_launch_events", "msda_launch_events_recorded",
                     "msda_launch_events_name", "msda_sampling_prep",
                     "msda_sampling_prep_backward", "msda_release_thread_resources",
-                    "msda_backward_noalloc")
+                    "msda_backward_noalloc", "msda_probe_atomic_requests")
 
 _lib = None
 
@@ -104,6 +104,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msda_launch_events_name.restype = ctypes.c_char_p
     lib.msda_backward_noalloc.argtypes = prob + [vp, vp, vp, vp, vp, vp, vp, i32, u32, vp]
     lib.msda_backward_noalloc.restype = i32
+    lib.msda_probe_atomic_requests.argtypes = [vp, sz, i32, i32, i64, i32,
+                                               ctypes.POINTER(ctypes.c_int64), vp]
+    lib.msda_probe_atomic_requests.restype = i32
     lib.msda_release_thread_resources.argtypes = []
     lib.msda_release_thread_resources.restype = i32
     _lib = lib
@@ -294,6 +297,21 @@ def msda_backward_level_modes(value: torch.Tensor, spatial_shapes, level_start_i
     if nb < 0:
         raise MSDAError(8, lib.msda_last_error().decode())
     return [LEVEL_MODES[int(m)] for m in modes]
+
+
+def probe_atomic_requests(buffer: torch.Tensor, bf16: bool, dwords_per_request: int,
+                          workgroups: int, iters: int, stream=None) -> int:
+    """Launch the atomic request-rate probe (msda_probe_atomic_requests) on
+    `buffer` (a device tensor, overwritten); returns the requests it makes."""
+    lib = load_library()
+    if buffer.device.type != "cuda" or not buffer.is_contiguous():
+        raise ValueError("buffer must be a contiguous device tensor")
+    req = ctypes.c_int64(0)
+    _check(lib.msda_probe_atomic_requests(_ptr(buffer), buffer.numel() * buffer.element_size(),
+                                          1 if bf16 else 0, dwords_per_request, workgroups,
+                                          iters, ctypes.byref(req),
+                                          _stream(buffer.device, stream)))
+    return int(req.value)
 
 
 def release_thread_resources() -> None:

@@ -26,22 +26,31 @@ thread_local hipEvent_t g_launch_events[kMaxLaunchEvents];
 thread_local int g_launch_events_n = 0;
 thread_local int g_launch_events_next = 0;
 
-// Record the "before" event of the next launch (called as an argument of
-// marked(), so it runs right before the launch call itself).
+thread_local msda::TimedLaunch g_timed_launch;
+
+// Arm the next launch's event pair (called as an argument of marked(), so it
+// runs right before the launch call itself): the launch records them at its
+// kernel's start and end.
 hipStream_t before(hipStream_t s) {
     if (g_launch_events_next + 1 < g_launch_events_n)
-        (void)hipEventRecord(g_launch_events[g_launch_events_next], s);
+        g_timed_launch = {g_launch_events[g_launch_events_next],
+                          g_launch_events[g_launch_events_next + 1]};
     return s;
 }
 
 thread_local const char *g_launch_names[kMaxLaunchEvents / 2];
 thread_local const char *g_recorded_names[kMaxLaunchEvents / 2];
 
-// After a launch: record its "after" event and its name (the pair is
-// consumed only when both fit in the caller's array).
+// After a launch: disarm the pair and keep its name (the pair is consumed
+// only when both fit in the caller's array). A helper that launched nothing
+// (an empty fill) gets both events recorded here, back to back.
 hipError_t marked(hipError_t err, hipStream_t s, const char *name) {
     if (g_launch_events_next + 1 < g_launch_events_n) {
-        if (err == hipSuccess) err = hipEventRecord(g_launch_events[g_launch_events_next + 1], s);
+        if (err == hipSuccess && g_timed_launch.start) {
+            err = hipEventRecord(g_timed_launch.start, s);
+            if (err == hipSuccess) err = hipEventRecord(g_timed_launch.stop, s);
+        }
+        g_timed_launch = {};
         g_launch_names[g_launch_events_next / 2] = name;
         g_launch_events_next += 2;
     }
@@ -57,6 +66,7 @@ struct LaunchEventsScope {  // clears the instrumentation when a call returns
             for (int i = 0; i < g_launch_events_next / 2; ++i) g_recorded_names[i] = g_launch_names[i];
         }
         g_launch_events_n = g_launch_events_next = 0;
+        g_timed_launch = {};
     }
 };
 
@@ -514,6 +524,10 @@ int set_param_dtype(msda::Problem *p, int pdtype) {
 
 }  // namespace
 
+namespace msda {
+TimedLaunch &timed_launch() { return g_timed_launch; }
+}  // namespace msda
+
 extern "C" {
 
 int msda_abi_version(void) { return MSDA_ABI_VERSION; }
@@ -539,6 +553,35 @@ int msda_set_launch_events(void *const *events, int count) {
 }
 
 const char *msda_last_error(void) { return g_last_error.c_str(); }
+
+int msda_probe_atomic_requests(void *buffer, size_t buffer_bytes, int bf16,
+                               int dwords_per_request, int64_t workgroups, int iters,
+                               int64_t *requests, void *stream) {
+    LaunchEventsScope events_scope;
+    if (!buffer || !requests) return fail(MSDA_ERR_NULL_ARG, "buffer or requests is NULL");
+    if (!aligned(buffer, 64)) return fail(MSDA_ERR_ALIGN, "buffer must be 64-byte aligned");
+    int log2run = -1;
+    for (int r = 0; r <= 4; ++r)
+        if (dwords_per_request == (1 << r)) log2run = r;
+    if (log2run < 0)
+        return fail(MSDA_ERR_SHAPE, "dwords_per_request must be 1, 2, 4, 8 or 16, got %d",
+                    dwords_per_request);
+    // the largest power of two of whole 64-byte segments that fits
+    int64_t nseg = 1;
+    while (nseg * 2 <= (int64_t)(buffer_bytes / 64) && nseg < ((int64_t)1 << 30)) nseg *= 2;
+    if ((int64_t)(buffer_bytes / 64) < 1)
+        return fail(MSDA_ERR_SHAPE, "buffer must hold at least one 64-byte segment");
+    if (workgroups < 1 || workgroups > ((int64_t)1 << 24) || iters < 1)
+        return fail(MSDA_ERR_SHAPE, "workgroups must be in [1, 2^24] and iters >= 1");
+    *requests = (workgroups * 256 >> log2run) * (int64_t)iters;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err =
+        marked(msda::launch_atomic_probe(buffer, nseg, bf16 ? 1 : 0, log2run, workgroups, iters,
+                                         before(s)),
+               s, "atomic_probe_kernel");
+    if (err != hipSuccess) return hip_fail(err, "probe launch");
+    return ok();
+}
 
 int msda_release_thread_resources(void) {
     const hipError_t err = release_side_streams();

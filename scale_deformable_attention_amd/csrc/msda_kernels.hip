@@ -1854,13 +1854,13 @@ hipError_t fwd_launch(const Problem &p, const Mapping &mp, const void *value, co
     const int64_t ntiles = p.B * (p.M / hg) * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (slice_fits_buffer(p))
-        hipLaunchKernelGGL((msda_fwd_kernel<DT, PT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
+        MSDA_LAUNCH((msda_fwd_kernel<DT, PT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
                            dim3(kBlock), 0, stream, static_cast<const E *>(value),
                            static_cast<const P *>(loc), static_cast<const P *>(attn),
                            static_cast<E *>(out), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
                            (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
     else if constexpr (std::is_same<DT, PT>::value)
-        hipLaunchKernelGGL((msda_fwd_kernel<DT, PT, VEC, CH, false>), dim3((unsigned)(per_xcd * kXcds)),
+        MSDA_LAUNCH((msda_fwd_kernel<DT, PT, VEC, CH, false>), dim3((unsigned)(per_xcd * kXcds)),
                            dim3(kBlock), 0, stream, static_cast<const E *>(value),
                            static_cast<const P *>(loc), static_cast<const P *>(attn),
                            static_cast<E *>(out), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
@@ -1883,7 +1883,7 @@ hipError_t grad_launch(const Problem &p, const Mapping &mp, const void *value, c
     const int64_t ntiles = p.B * (p.M / hg) * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (!slice_fits_buffer(p)) return hipErrorInvalidValue;  // binning requires it
-    hipLaunchKernelGGL((msda_grad_kernel<DT, PT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
+    MSDA_LAUNCH((msda_grad_kernel<DT, PT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
                        dim3(kBlock), 0, stream, static_cast<const E *>(value),
                        static_cast<const P *>(loc), static_cast<const P *>(attn),
                        static_cast<const E *>(grad_out), static_cast<P *>(grad_loc),
@@ -1903,7 +1903,7 @@ hipError_t bwd_launch(const Problem &p, const BwdMapping &mp, const void *value,
     const int64_t ntiles = p.B * p.M * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (slice_fits_buffer(p))
-        hipLaunchKernelGGL((msda_bwd_kernel<DT, PT, SLOT, J, true>),
+        MSDA_LAUNCH((msda_bwd_kernel<DT, PT, SLOT, J, true>),
                            dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
                            static_cast<const E *>(value), static_cast<const P *>(loc),
                            static_cast<const P *>(attn), static_cast<const E *>(grad_out),
@@ -1911,7 +1911,7 @@ hipError_t bwd_launch(const Problem &p, const BwdMapping &mp, const void *value,
                            static_cast<P *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
                            (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
     else if constexpr (std::is_same<DT, PT>::value)
-        hipLaunchKernelGGL((msda_bwd_kernel<DT, PT, SLOT, J, false>),
+        MSDA_LAUNCH((msda_bwd_kernel<DT, PT, SLOT, J, false>),
                            dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
                            static_cast<const E *>(value), static_cast<const P *>(loc),
                            static_cast<const P *>(attn), static_cast<const E *>(grad_out),
@@ -1939,7 +1939,7 @@ hipError_t accum_launch_w(const Problem &p, const BwdMapping &mp, const void *gr
     using E = typename DT::S;
     const size_t lds = (size_t)kAccGroups * (size_t)p.D * sizeof(float);
     const int64_t per_xcd = (bins.nbins + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((bin_accum_kernel<DT, SLOT, J, V, WIDE>), dim3((unsigned)(per_xcd * kXcds)),
+    MSDA_LAUNCH((bin_accum_kernel<DT, SLOT, J, V, WIDE>), dim3((unsigned)(per_xcd * kXcds)),
                        dim3(kBlock), lds, stream, static_cast<const E *>(grad_out),
                        static_cast<E *>(grad_value), bins.starts, bins.ends, bins.records, p.levels, p.S,
                        p.Q, (int)p.M, (int)p.D, (int)p.L, p.nbbm, bins.nbins, (int)accumulate);
@@ -2001,7 +2001,7 @@ hipError_t scatter_launch(const Problem &p, const BwdMapping &mp, const void *lo
     const int qblocks = (int)((p.Q + qpb - 1) / qpb);
     const int64_t ntiles = p.B * p.M * qblocks;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((msda_scatter_kernel<DT, PT, SLOT, J>), dim3((unsigned)(per_xcd * kXcds)),
+    MSDA_LAUNCH((msda_scatter_kernel<DT, PT, SLOT, J>), dim3((unsigned)(per_xcd * kXcds)),
                        dim3(kBlock), 0, stream, static_cast<const P *>(loc),
                        static_cast<const P *>(attn), static_cast<const E *>(grad_out), grad_value,
                        workspace, p.levels, p.S, p.Q, (int)p.M, (int)p.D, (int)p.L, (int)p.K,
@@ -2120,11 +2120,11 @@ hipError_t scratch_add(const Problem &p, const float *ws, void *gv, hipStream_t 
     const bool v4 = MD % 4 == 0 && reinterpret_cast<uintptr_t>(gv) % 8 == 0 &&
                     reinterpret_cast<uintptr_t>(ws) % 16 == 0;
     if (v4) {
-        hipLaunchKernelGGL((scratch_add_kernel<DT, 4>), dim3(grid_for(largest / 4), sl.count),
+        MSDA_LAUNCH((scratch_add_kernel<DT, 4>), dim3(grid_for(largest / 4), sl.count),
                            dim3(kBlock), 0, stream, ws, static_cast<E *>(gv), p.levels, sl, p.B,
                            p.S, MD);
     } else {
-        hipLaunchKernelGGL((scratch_add_kernel<DT, 1>), dim3(grid_for(largest), sl.count),
+        MSDA_LAUNCH((scratch_add_kernel<DT, 1>), dim3(grid_for(largest), sl.count),
                            dim3(kBlock), 0, stream, ws, static_cast<E *>(gv), p.levels, sl, p.B,
                            p.S, MD);
     }
@@ -2201,7 +2201,7 @@ hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
     const int64_t grid = (ntiles + kXcds - 1) / kXcds * kXcds;
     uint32_t *counter = place ? bins.cursor : bins.starts;
 #define MSDA_SORT(T, PL)                                                                        \
-    hipLaunchKernelGGL((bin_sort_kernel<T, PL>), dim3((unsigned)grid), dim3(kBinBlock), 0, stream, \
+    MSDA_LAUNCH((bin_sort_kernel<T, PL>), dim3((unsigned)grid), dim3(kBinBlock), 0, stream, \
                        static_cast<const typename T::S *>(loc),                                 \
                        static_cast<const typename T::S *>(attn), p.levels, counter,             \
                        bins.records, p.Q, (int)p.M, (int)p.L, (int)p.K, p.nbbm, wpb, ntiles)
@@ -2227,7 +2227,7 @@ hipError_t launch_bin_local_sort(const Problem &p, const void *loc, const void *
     const int64_t nzero = n16 > 0 ? std::min<int64_t>((n16 + kSortBlock - 1) / kSortBlock, 1024) : 0;
     if (nseg + nzero >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
 #define MSDA_LSORT(T)                                                                          \
-    hipLaunchKernelGGL((bin_local_sort_kernel<T>), dim3((unsigned)(nseg + nzero)),             \
+    MSDA_LAUNCH((bin_local_sort_kernel<T>), dim3((unsigned)(nseg + nzero)),             \
                        dim3(kSortBlock), lds, stream, static_cast<const typename T::S *>(loc),  \
                        static_cast<const typename T::S *>(attn), p.levels, bins.starts,         \
                        bins.cursor, bins.records, p.Q, (int)p.M, (int)p.L, (int)p.K, p.nbbm,    \
@@ -2256,7 +2256,7 @@ hipError_t scatter_accum_launch(const Problem &p, const BwdMapping &mp, const vo
     const int64_t nacc = (bins.nbins + kXcds - 1) / kXcds * kXcds;
     if (nsc + nacc >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const size_t lds = (size_t)kAccGroups * (size_t)p.D * sizeof(float);
-    hipLaunchKernelGGL((scatter_accum_kernel<DT, PT, 2, J, V, WIDE>), dim3((unsigned)(nsc + nacc)),
+    MSDA_LAUNCH((scatter_accum_kernel<DT, PT, 2, J, V, WIDE>), dim3((unsigned)(nsc + nacc)),
                        dim3(kBlock), lds, stream, static_cast<const P *>(loc),
                        static_cast<const P *>(attn), static_cast<const E *>(grad_out), grad_value,
                        p.levels, p.S, p.Q, (int)p.M, (int)p.D, (int)p.L, (int)p.K, qblocks, ntiles,
@@ -2319,7 +2319,7 @@ hipError_t grad_sort_launch(const Problem &p, const Mapping &mp, const void *val
         n16 > 0 ? std::min<int64_t>((n16 + kBlock - 1) / kBlock + kXcds - 1, 128) / kXcds * kXcds : 0;
     if (ngrad + nsegp + nzero >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const size_t lds = (size_t)((max_level_bins + 1) / 2) * 4;
-    hipLaunchKernelGGL((grad_sort_kernel<DT, PT, VEC>), dim3((unsigned)(nzero + nsegp + ngrad)),
+    MSDA_LAUNCH((grad_sort_kernel<DT, PT, VEC>), dim3((unsigned)(nzero + nsegp + ngrad)),
                        dim3(kBlock), lds, stream, static_cast<const E *>(value),
                        static_cast<const P *>(loc), static_cast<const P *>(attn),
                        static_cast<const E *>(grad_out), static_cast<P *>(grad_loc),
@@ -2368,7 +2368,7 @@ hipError_t launch_gradients_and_sort(const Problem &p, const Mapping &mp, const 
 int64_t scan_tiles(int64_t nbins) { return (nbins + kScanTile - 1) / kScanTile; }
 
 hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream) {
-    hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, bins.starts,
+    MSDA_LAUNCH(bin_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, bins.starts,
                        bins.cursor, bins.nbins);
     return hipGetLastError();
 }
@@ -2376,7 +2376,7 @@ hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream) {
 hipError_t launch_bin_tile_sums(const BinnedBuffers &bins, hipStream_t stream) {
     const int64_t nt = scan_tiles(bins.nbins);
     if (nt < 1 || nt >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bin_tile_sum_kernel, dim3((unsigned)nt), dim3(kScanBlock), 0, stream,
+    MSDA_LAUNCH(bin_tile_sum_kernel, dim3((unsigned)nt), dim3(kScanBlock), 0, stream,
                        bins.starts, bins.tile_offsets, bins.nbins);
     return hipGetLastError();
 }
@@ -2384,14 +2384,14 @@ hipError_t launch_bin_tile_sums(const BinnedBuffers &bins, hipStream_t stream) {
 hipError_t launch_bin_tile_offsets(const BinnedBuffers &bins, hipStream_t stream) {
     // the single-workgroup scan over the ntiles totals (toff[ntiles] = total)
     const int64_t nt = scan_tiles(bins.nbins);  // (the cursor copy goes past the offsets)
-    hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, bins.tile_offsets,
+    MSDA_LAUNCH(bin_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, bins.tile_offsets,
                        bins.tile_offsets + nt + 1, nt);
     return hipGetLastError();
 }
 
 hipError_t launch_bin_tile_scan(const BinnedBuffers &bins, hipStream_t stream) {
     const int64_t nt = scan_tiles(bins.nbins);
-    hipLaunchKernelGGL(bin_tile_scan_kernel, dim3((unsigned)nt), dim3(kScanBlock), 0, stream,
+    MSDA_LAUNCH(bin_tile_scan_kernel, dim3((unsigned)nt), dim3(kScanBlock), 0, stream,
                        bins.starts, bins.cursor, bins.tile_offsets, bins.nbins);
     return hipGetLastError();
 }
@@ -2417,7 +2417,7 @@ hipError_t launch_forward_foil(const Problem &p, int vec, const void *value, con
     const int64_t grid = (P + kBlock - 1) / kBlock;
     const size_t lds = (size_t)kBlock * (size_t)p.D * sizeof(float);
 #define MSDA_FOIL(T, V)                                                                         \
-    hipLaunchKernelGGL((msda_foil_kernel<T, V, 64>), dim3((unsigned)grid), dim3(kBlock), lds,    \
+    MSDA_LAUNCH((msda_foil_kernel<T, V, 64>), dim3((unsigned)grid), dim3(kBlock), lds,    \
                        stream, static_cast<const typename T::S *>(value),                       \
                        static_cast<const typename T::S *>(loc),                                 \
                        static_cast<const typename T::S *>(attn),                                \
@@ -2443,11 +2443,11 @@ hipError_t launch_zero(void *dst, size_t bytes, hipStream_t stream) {
     if (bytes == 0) return hipSuccess;
     if ((reinterpret_cast<uintptr_t>(dst) % 16 == 0) && (bytes % 16 == 0)) {
         const int64_t n16 = (int64_t)(bytes / 16);
-        hipLaunchKernelGGL(zero_kernel_16, dim3(grid_for(n16)), dim3(kBlock), 0, stream,
+        MSDA_LAUNCH(zero_kernel_16, dim3(grid_for(n16)), dim3(kBlock), 0, stream,
                            static_cast<uint4 *>(dst), n16);
     } else {
         const int64_t n2 = (int64_t)(bytes / 2);
-        hipLaunchKernelGGL(zero_kernel_2, dim3(grid_for(n2)), dim3(kBlock), 0, stream,
+        MSDA_LAUNCH(zero_kernel_2, dim3(grid_for(n2)), dim3(kBlock), 0, stream,
                            static_cast<uint16_t *>(dst), n2);
     }
     return hipGetLastError();

@@ -2,12 +2,36 @@
 // gfx950 kernels (msda_kernels.hip). Not installed, not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "msda.h"
 
 namespace msda {
+
+// Launch instrumentation (msda_set_launch_events): when `stop` is set, the next
+// kernel launch of this thread records `start` when that kernel starts and
+// `stop` when it ends (the launch packet's own timestamps); a helper that
+// launches several kernels records `start` at its first and `stop` at its last.
+struct TimedLaunch {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+TimedLaunch &timed_launch();  // this thread's pending events (msda_api.cpp)
+
+// Every kernel launch of the library goes through this macro.
+#define MSDA_LAUNCH(kernel, grid, block, lds, stream, ...)                                     \
+    do {                                                                                        \
+        ::msda::TimedLaunch &tl_ = ::msda::timed_launch();                                     \
+        if (tl_.stop) {                                                                         \
+            hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, tl_.start, tl_.stop, 0,     \
+                                  __VA_ARGS__);                                                 \
+            tl_.start = nullptr;                                                                \
+        } else {                                                                                \
+            hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                  \
+        }                                                                                       \
+    } while (0)
 
 // Level table passed by value in the kernel arguments (no device copy, no
 // host synchronisation). H, W < 2^24 so that they are exact in fp32.
@@ -172,6 +196,12 @@ hipError_t launch_reference_grad(const PrepProblem &p, const void *grad_loc, voi
                                  hipStream_t stream);
 
 hipError_t launch_zero(void *dst, size_t bytes, hipStream_t stream);
+
+// Atomic request-rate probe (msda_probe.hip, measurement only): workgroups of
+// 256 threads, each lane `iters` no-return adds (fp32, or packed bf16 pairs)
+// in runs of 2^log2run lanes per 64-byte segment of `buf` (nseg segments).
+hipError_t launch_atomic_probe(void *buf, int64_t nseg, int bf16, int log2run, int64_t workgroups,
+                               int iters, hipStream_t stream);
 
 // For every level with scratch_off >= 0 and every batch:
 // grad_value rows of that level += (dtype) workspace block.

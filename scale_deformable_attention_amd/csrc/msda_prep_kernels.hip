@@ -136,7 +136,7 @@ hipError_t prep_launch(const PrepProblem &p, const void *ref, const void *off, c
     const int64_t rows = p.B * p.Q * p.M;
     const int lg = lanes_log2(p.L * p.K);
     const int64_t grid = ((rows << lg) + kBlock - 1) / kBlock;
-    hipLaunchKernelGGL(sampling_prep_kernel<T>, dim3((unsigned)grid), dim3(kBlock), 0, stream,
+    MSDA_LAUNCH(sampling_prep_kernel<T>, dim3((unsigned)grid), dim3(kBlock), 0, stream,
                        static_cast<const S *>(ref), static_cast<const S *>(off),
                        static_cast<const S *>(logits), static_cast<S *>(loc),
                        static_cast<S *>(attn), p, rows, lg);
@@ -151,7 +151,7 @@ hipError_t prep_bwd_launch(const PrepProblem &p, const void *attn, const void *g
     const int64_t rows = p.B * p.Q * p.M;
     const int lg = lanes_log2(p.L * p.K);
     const int64_t grid = ((rows << lg) + kBlock - 1) / kBlock;
-    hipLaunchKernelGGL(sampling_prep_bwd_kernel<T>, dim3((unsigned)grid), dim3(kBlock), 0, stream,
+    MSDA_LAUNCH(sampling_prep_bwd_kernel<T>, dim3((unsigned)grid), dim3(kBlock), 0, stream,
                        static_cast<const S *>(attn), static_cast<const S *>(grad_loc),
                        static_cast<const S *>(grad_attn), static_cast<S *>(grad_off),
                        static_cast<S *>(grad_logits), p, rows, lg);
@@ -164,7 +164,7 @@ hipError_t ref_grad_launch(const PrepProblem &p, const void *grad_loc, void *gra
     using S = typename T::S;
     const int64_t nbq = p.B * p.Q;
     const int64_t grid = (nbq + kBlock / 64 - 1) / (kBlock / 64);
-    hipLaunchKernelGGL(reference_grad_kernel<T>, dim3((unsigned)grid), dim3(kBlock), 0, stream,
+    MSDA_LAUNCH(reference_grad_kernel<T>, dim3((unsigned)grid), dim3(kBlock), 0, stream,
                        static_cast<const S *>(grad_loc), static_cast<S *>(grad_ref), p, nbq);
     return hipGetLastError();
 }
