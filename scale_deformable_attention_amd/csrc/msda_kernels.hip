@@ -243,6 +243,83 @@ __device__ __forceinline__ int64_t logical_block() {
     return (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
 }
 
+// Order of the query tiles of the forward and gradient kernels.
+//
+// Linear (nc == 0): tile = (b, head group, block of qs consecutive queries),
+// query block fastest; XCD x takes a contiguous range of tiles, i.e. whole
+// (b, head group) pairs when there are at least 8 of them.
+//
+// Column groups (nc > 1), for pixel queries when there are fewer (b, head
+// group) pairs than XCDs: when the queries are the pyramid's own pixels in S
+// order (Q == S and the levels tile [0, S) without overlap, as in a
+// deformable-attention encoder), every query samples near its own pixel, and
+// a linear range of queries is a few full-width rows whose sampled
+// neighbourhoods, for 4 heads of 64-byte rows, exceed one XCD's 4 MB L2. The
+// pixels of every level are then cut into nc column groups, and region
+// (b, head group, column group) takes per_region consecutive logical tiles
+// (one region per XCD): its column group of level 0 row by row, then level
+// 1's, and so on, each row's part cut into tiles of qs = 2^log2qs queries
+// (the last one ragged; the tail of a smaller region is empty). Any order
+// gives the same results: only the assignment of queries to workgroups
+// changes. All tile arithmetic is 32-bit (the host checks the ranges).
+struct TileOrder {
+    int32_t nc;          // column groups (0: linear order)
+    int32_t per_region;  // logical tiles per region
+};
+
+struct TileQueries {
+    int64_t b;   // batch
+    int hg;      // head group
+    int64_t q0;  // first query of the tile
+    int qn;      // queries in the tile (<= qs)
+};
+
+// Columns [x0, x1) of column group c of a level of width W, and its tiles per row.
+__host__ __device__ __forceinline__ uint32_t group_columns(uint32_t W, uint32_t c, uint32_t nc,
+                                                          int log2qs, uint32_t *x0,
+                                                          uint32_t *x1) {
+    *x0 = (c * W) / nc;
+    *x1 = ((c + 1) * W) / nc;
+    return (*x1 - *x0 + (1u << log2qs) - 1) >> log2qs;
+}
+
+// The queries of logical tile `tile`; false for an empty tile (the padded
+// tail of a region). Uniform over the workgroup.
+__device__ __forceinline__ bool tile_queries(int64_t tile, const TileOrder &to,
+                                             const LevelTable &lt, int L, int64_t Q, int log2qs,
+                                             int ngroups, int qblocks, TileQueries &tq) {
+    const int qs = 1 << log2qs;
+    if (to.nc == 0) {
+        const int64_t bg = tile / qblocks;
+        const int qb = (int)(tile - bg * qblocks);
+        tq.b = bg / ngroups;
+        tq.hg = (int)(bg - tq.b * ngroups);
+        tq.q0 = (int64_t)qb * qs;
+        tq.qn = (int)(Q - tq.q0 < qs ? Q - tq.q0 : qs);
+        return true;
+    }
+    const uint32_t t32 = (uint32_t)tile, per = (uint32_t)to.per_region, nc = (uint32_t)to.nc;
+    const uint32_t region = t32 / per;
+    uint32_t idx = t32 - region * per;
+    const uint32_t c = region % nc, bg = region / nc;
+    tq.b = bg / (uint32_t)ngroups;
+    tq.hg = (int)(bg - (uint32_t)tq.b * (uint32_t)ngroups);
+    for (int l = 0; l < L; ++l) {
+        uint32_t x0, x1;
+        const uint32_t tpr = group_columns((uint32_t)lt.W[l], c, nc, log2qs, &x0, &x1);
+        const uint32_t n = (uint32_t)lt.H[l] * tpr;
+        if (idx < n) {
+            const uint32_t row = idx / tpr;
+            const uint32_t xs = x0 + ((idx - row * tpr) << log2qs);
+            tq.q0 = lt.start[l] + (int64_t)row * lt.W[l] + xs;
+            tq.qn = (int)(x1 - xs < (uint32_t)qs ? x1 - xs : (uint32_t)qs);
+            return true;
+        }
+        idx -= n;
+    }
+    return false;  // the padded tail of the region
+}
+
 // Everything that depends only on the point's location: cell, weights (times
 // the attention weight for the forward), masks and corner row offsets.
 struct Cell {
@@ -284,6 +361,111 @@ __device__ __forceinline__ Cell map_cell(float loc_x, float loc_y, float Hf, flo
     return c;
 }
 
+// -------------------------------------------------- sampling parameters
+//
+// The G lanes of a group share every point (they hold different channels), so
+// loading a point's location and weight in every lane would cost G load
+// instructions per parameter, each as expensive for the vector memory path as
+// a corner gather. Instead lane k of the group loads the parameters of chunk
+// k (points kCH .. kCH + CH - 1 of the group's list) once, before the chunk
+// loop, and chunk k's parameters are shuffled from lane k when its turn comes
+// (needs at most G chunks). Parameters are kept as raw dwords: 16-bit types
+// hold a point's (x, y) in one dword and two points' weights in another;
+// fp32 types one value per dword.
+template <class PT, int CH>
+struct ChunkParams {
+    static constexpr int kE = (int)sizeof(typename PT::S);
+    static constexpr int kLocW = CH * 2 * kE / 4;    // 16-bit: CH; fp32: 2 CH
+    static constexpr int kAttW = (CH * kE + 3) / 4;  // 16-bit: CH / 2; fp32: CH
+    uint32_t loc[kLocW];
+    uint32_t att[kAttW];
+};
+
+// Lane k's own chunk: points i = k * CH + t (t < CH) of the group's list,
+// i < per_lane, point index i * split + s. `vec`: the chunk is whole and its
+// dwords are aligned for 16-byte (locations) and 8- or 16-byte (weights)
+// loads (split == 1, checked on the host), else element loads.
+template <class PT, int CH>
+__device__ __forceinline__ void own_chunk_params(const typename PT::S *loc_q,
+                                                 const typename PT::S *attn_q, int k,
+                                                 int per_lane, int split, int s, bool vec,
+                                                 ChunkParams<PT, CH> &cp) {
+    using C = ChunkParams<PT, CH>;
+    static_assert(C::kLocW % 4 == 0 && (C::kAttW == 2 || C::kAttW % 4 == 0), "chunk layout");
+#pragma unroll
+    for (int w = 0; w < C::kLocW; ++w) cp.loc[w] = 0;
+#pragma unroll
+    for (int w = 0; w < C::kAttW; ++w) cp.att[w] = 0;
+    const int i0 = k * CH;
+    if (i0 >= per_lane) return;
+    if (vec) {
+        const uint4 *lp = reinterpret_cast<const uint4 *>(loc_q + 2 * i0);
+#pragma unroll
+        for (int w = 0; w < C::kLocW / 4; ++w) {
+            const uint4 v = lp[w];
+            cp.loc[4 * w] = v.x;
+            cp.loc[4 * w + 1] = v.y;
+            cp.loc[4 * w + 2] = v.z;
+            cp.loc[4 * w + 3] = v.w;
+        }
+        if constexpr (C::kAttW == 2) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(attn_q + i0);
+            cp.att[0] = v.x;
+            cp.att[1] = v.y;
+        } else {
+            const uint4 *ap = reinterpret_cast<const uint4 *>(attn_q + i0);
+#pragma unroll
+            for (int w = 0; w < C::kAttW / 4; ++w) {
+                const uint4 v = ap[w];
+                cp.att[4 * w] = v.x;
+                cp.att[4 * w + 1] = v.y;
+                cp.att[4 * w + 2] = v.z;
+                cp.att[4 * w + 3] = v.w;
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+        const int i = i0 + t;
+        const int p = (i < per_lane ? i : i0) * split + s;  // in-bounds address
+        const uint32_t x = load_bits<PT>(loc_q + 2 * p), y = load_bits<PT>(loc_q + 2 * p + 1);
+        const uint32_t a = i < per_lane ? load_bits<PT>(attn_q + p) : 0u;
+        if constexpr (C::kE == 2) {
+            cp.loc[t] = (x & 0xFFFFu) | (y << 16);
+            cp.att[t / 2] |= (a & 0xFFFFu) << (16 * (t & 1));
+        } else {
+            cp.loc[2 * t] = x;
+            cp.loc[2 * t + 1] = y;
+            cp.att[t] = a;
+        }
+    }
+}
+
+// Chunk parameters from lane `src` (absolute lane of the wave), unpacked.
+template <class PT, int CH>
+__device__ __forceinline__ void chunk_params(const ChunkParams<PT, CH> &own, int src,
+                                             float (&lx)[CH], float (&ly)[CH], float (&aw)[CH]) {
+    using C = ChunkParams<PT, CH>;
+    uint32_t lw[C::kLocW], aw_[C::kAttW];
+#pragma unroll
+    for (int w = 0; w < C::kLocW; ++w) lw[w] = (uint32_t)__shfl((int)own.loc[w], src, 64);
+#pragma unroll
+    for (int w = 0; w < C::kAttW; ++w) aw_[w] = (uint32_t)__shfl((int)own.att[w], src, 64);
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+        if constexpr (C::kE == 2) {
+            lx[t] = bits_to_f32<PT>(lw[t] & 0xFFFFu);
+            ly[t] = bits_to_f32<PT>(lw[t] >> 16);
+            aw[t] = bits_to_f32<PT>((aw_[t / 2] >> (16 * (t & 1))) & 0xFFFFu);
+        } else {
+            lx[t] = __uint_as_float(lw[2 * t]);
+            ly[t] = __uint_as_float(lw[2 * t + 1]);
+            aw[t] = __uint_as_float(aw_[t]);
+        }
+    }
+}
+
 // ------------------------------------------------------------- forward
 //
 // A lane group handles the points p = i * split + s (i = 0, 1, ...) of its
@@ -318,7 +500,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const typename PT::S *__restrict__ attn, typename DT::S *__restrict__ out,
     const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
     const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
-    const int log2s) {
+    const int log2s, const TileOrder to, const bool pvec) {
     using E = typename DT::S;
     using R = typename RawVec<VEC * (int)sizeof(E)>::type;
     const int64_t tile = logical_block();
@@ -329,14 +511,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const int qpb = kBlock >> (log2g + log2s);  // query slots
     const int HG = fwd_heads(M, qpb, D * (int)sizeof(E));
     const int slot = tid >> (log2g + log2s);
-    // tile = (b, head group, query block), query block fastest
-    const int64_t bg = tile / qblocks;
-    const int qb = (int)(tile - bg * qblocks);
-    const int64_t ngroups = M / HG;
-    const int64_t b = bg / ngroups;
-    const int m = (int)(bg - b * ngroups) * HG + slot % HG;
-    const int64_t q = (int64_t)qb * (qpb / HG) + slot / HG;
-    const bool q_ok = q < Q;
+    TileQueries tq;
+    const int log2qs = 8 - log2g - log2s - (HG == 4 ? 2 : HG == 2 ? 1 : 0);  // queries per tile
+    if (!tile_queries(tile, to, lt, L, Q, log2qs, M / HG, qblocks, tq)) return;
+    const int64_t b = tq.b;
+    const int m = tq.hg * HG + slot % HG;
+    const int64_t q = tq.q0 + slot / HG;
+    const bool q_ok = slot / HG < tq.qn;
     const int c0 = c * VEC;
     const bool live = q_ok && (c0 < D);
     const int split = 1 << log2s;
@@ -355,28 +536,40 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
 
+    // chunk k's parameters live in lane k of the group (at most G chunks)
+    const bool owned = per_lane <= (CH << log2g);
+    ChunkParams<PT, CH> own;
+    if (owned) own_chunk_params<PT, CH>(loc_q, attn_q, c, per_lane, split, s, pvec, own);
+    const int group_base = (tid & 63) & ~((1 << log2g) - 1);
+
     for (int i0 = 0; i0 < per_lane; i0 += CH) {
-        uint32_t bx[CH], by[CH], ba[CH];
-#pragma unroll
-        for (int t = 0; t < CH; ++t) {
-            const int p = (i0 + t < per_lane ? i0 + t : 0) * split + s;
-            bx[t] = load_bits<PT>(loc_q + 2 * p);
-            by[t] = load_bits<PT>(loc_q + 2 * p + 1);
-            ba[t] = load_bits<PT>(attn_q + p);
-        }
-#pragma unroll
-        for (int t = 0; t < CH; ++t) {
-            pin(bx[t]);
-            pin(by[t]);
-            pin(ba[t]);
-        }
         float lx[CH], ly[CH], aw[CH];
+        if (owned) {
+            chunk_params<PT, CH>(own, group_base + i0 / CH, lx, ly, aw);
+        } else {
+            uint32_t bx[CH], by[CH], ba[CH];
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-            lx[t] = bits_to_f32<PT>(bx[t]);
-            ly[t] = bits_to_f32<PT>(by[t]);
-            aw[t] = (q_ok && i0 + t < per_lane) ? bits_to_f32<PT>(ba[t]) : 0.0f;
+            for (int t = 0; t < CH; ++t) {
+                const int p = (i0 + t < per_lane ? i0 + t : 0) * split + s;
+                bx[t] = load_bits<PT>(loc_q + 2 * p);
+                by[t] = load_bits<PT>(loc_q + 2 * p + 1);
+                ba[t] = load_bits<PT>(attn_q + p);
+            }
+#pragma unroll
+            for (int t = 0; t < CH; ++t) {
+                pin(bx[t]);
+                pin(by[t]);
+                pin(ba[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < CH; ++t) {
+                lx[t] = bits_to_f32<PT>(bx[t]);
+                ly[t] = bits_to_f32<PT>(by[t]);
+                aw[t] = bits_to_f32<PT>(ba[t]);
+            }
         }
+#pragma unroll
+        for (int t = 0; t < CH; ++t) aw[t] = (q_ok && i0 + t < per_lane) ? aw[t] : 0.0f;
         int64_t off[CH][4];
         bool ok[CH][4];
         float w[CH][4];
@@ -517,9 +710,10 @@ __global__ __launch_bounds__(kBlock) void msda_foil_kernel(
         const typename PT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out, \
         typename PT::S *__restrict__ grad_loc, typename PT::S *__restrict__ grad_attn,        \
         const LevelTable &lt, const int64_t S, const int64_t Q, const int M, const int D,     \
-        const int L, const int K, const int qblocks, const int log2g, const int log2s
+        const int L, const int K, const int qblocks, const int log2g, const int log2s,        \
+        const TileOrder &to, const bool pvec
 #define MSDA_GRAD_ARGS value, loc, attn, grad_out, grad_loc, grad_attn, lt, S, Q, M, D, L, K, \
-                       qblocks, log2g, log2s
+                       qblocks, log2g, log2s, to, pvec
 
 template <class DT, class PT, int VEC, int CH, bool BUF>
 __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) {
@@ -532,14 +726,13 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
     const int qpb = kBlock >> (log2g + log2s);  // query slots
     const int HG = grad_heads(M, qpb);
     const int slot = tid >> (log2g + log2s);
-    // tile = (b, head group, query block), query block fastest
-    const int64_t bg = tile / qblocks;
-    const int qb = (int)(tile - bg * qblocks);
-    const int64_t ngroups = M / HG;
-    const int64_t b = bg / ngroups;
-    const int m = (int)(bg - b * ngroups) * HG + slot % HG;
-    const int64_t q = (int64_t)qb * (qpb / HG) + slot / HG;
-    const bool q_ok = q < Q;
+    TileQueries tq;
+    const int log2qs = 8 - log2g - log2s - (HG == 4 ? 2 : HG == 2 ? 1 : 0);  // queries per tile
+    if (!tile_queries(tile, to, lt, L, Q, log2qs, M / HG, qblocks, tq)) return;
+    const int64_t b = tq.b;
+    const int m = tq.hg * HG + slot % HG;
+    const int64_t q = tq.q0 + slot / HG;
+    const bool q_ok = slot / HG < tq.qn;
     const int c0 = c * VEC;
     const bool live = q_ok && (c0 < D);
     const int split = 1 << log2s;
@@ -559,20 +752,37 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
         raw_to_f32<DT, VEC>(live ? r : zero_raw<R>(), g);
     }
 
+    // chunk k's parameters live in lane k of the group (at most G chunks)
+    const bool owned = per_lane <= (CH << log2g);
+    ChunkParams<PT, CH> own;
+    if (owned) own_chunk_params<PT, CH>(loc_q, attn_q, c, per_lane, split, s, pvec, own);
+    const int group_base = (tid & 63) & ~(G - 1);
+
     for (int i0 = 0; i0 < per_lane; i0 += CH) {
-        uint32_t bx[CH], by[CH], ba[CH];
+        float lx[CH], ly[CH], la[CH];
+        if (owned) {
+            chunk_params<PT, CH>(own, group_base + i0 / CH, lx, ly, la);
+        } else {
+            uint32_t bx[CH], by[CH], ba[CH];
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-            const int p = (i0 + t < per_lane ? i0 + t : 0) * split + s;
-            bx[t] = load_bits<PT>(loc_q + 2 * p);
-            by[t] = load_bits<PT>(loc_q + 2 * p + 1);
-            ba[t] = load_bits<PT>(attn_q + p);
-        }
+            for (int t = 0; t < CH; ++t) {
+                const int p = (i0 + t < per_lane ? i0 + t : 0) * split + s;
+                bx[t] = load_bits<PT>(loc_q + 2 * p);
+                by[t] = load_bits<PT>(loc_q + 2 * p + 1);
+                ba[t] = load_bits<PT>(attn_q + p);
+            }
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-            pin(bx[t]);
-            pin(by[t]);
-            pin(ba[t]);
+            for (int t = 0; t < CH; ++t) {
+                pin(bx[t]);
+                pin(by[t]);
+                pin(ba[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < CH; ++t) {
+                lx[t] = bits_to_f32<PT>(bx[t]);
+                ly[t] = bits_to_f32<PT>(by[t]);
+                la[t] = bits_to_f32<PT>(ba[t]);
+            }
         }
         int64_t off[CH][4];
         bool ok[CH][4];
@@ -583,11 +793,10 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
             int l = ((i0 + t) * split) / K;
             l = l < L ? l : L - 1;
             const int H = lt.H[l], W = lt.W[l];
-            const float aw = (q_ok && i0 + t < per_lane) ? bits_to_f32<PT>(ba[t]) : 0.0f;
+            const float aw = (q_ok && i0 + t < per_lane) ? la[t] : 0.0f;
             sw[t] = (float)W * aw;
             sh[t] = (float)H * aw;
-            const Cell cl = map_cell(bits_to_f32<PT>(bx[t]), bits_to_f32<PT>(by[t]), (float)H,
-                                     (float)W, W, lt.start[l]);
+            const Cell cl = map_cell(lx[t], ly[t], (float)H, (float)W, W, lt.start[l]);
             fx[t] = cl.fx;
             fy[t] = cl.fy;
             off[t][0] = cl.row00 * row_bytes + lane_bytes;
@@ -659,7 +868,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     typename PT::S *__restrict__ grad_loc, typename PT::S *__restrict__ grad_attn,
     const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
     const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
-    const int log2s) {
+    const int log2s, const TileOrder to, const bool pvec) {
     const int64_t tile = logical_block();
     if (tile >= ntiles) return;  // whole workgroup leaves together
     grad_tile<DT, PT, VEC, CH, BUF>(MSDA_GRAD_ARGS, tile);
@@ -1304,7 +1513,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     typename PT::S *__restrict__ grad_loc, typename PT::S *__restrict__ grad_attn,
     const LevelTable lt, const int64_t S, const int64_t Q, const int M, const int D,
     const int L, const int K, const int qblocks, const int64_t ntiles, const int log2g,
-    const int log2s, const uint32_t ngrad, uint32_t *__restrict__ starts,
+    const int log2s, const bool pvec, const uint32_t ngrad, uint32_t *__restrict__ starts,
     uint32_t *__restrict__ ends, uint2 *__restrict__ records, const int64_t nbbm,
     const uint32_t nseg, const uint32_t nsegp, const uint32_t nzero, uint4 *__restrict__ zero_dst,
     const int64_t zero_n16) {
@@ -1320,6 +1529,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     } else {
         const uint32_t g = bx - nzero - nsegp;
         const int64_t tile = (int64_t)(g % kXcds) * (ngrad / kXcds) + g / kXcds;
+        const TileOrder to = {0, 0};  // linear
         if (tile < ntiles) grad_tile<DT, PT, VEC, 4, true>(MSDA_GRAD_ARGS, tile);
     }
 }
@@ -1835,6 +2045,59 @@ int grid_for(int64_t work_items) {
 
 // ------------------------------------------------------------ dispatch
 
+// The queries are the pyramid's own pixels in S order: Q == S and the levels
+// tile [0, S) without overlap.
+bool pixel_queries(const Problem &p) {
+    if (p.Q != p.S) return false;
+    int64_t covered = 0;
+    for (int i = 0; i < (int)p.L; ++i) {
+        const int64_t a0 = p.levels.start[i], a1 = a0 + (int64_t)p.levels.H[i] * p.levels.W[i];
+        covered += a1 - a0;
+        for (int k = i + 1; k < (int)p.L; ++k) {
+            const int64_t b0 = p.levels.start[k], b1 = b0 + (int64_t)p.levels.H[k] * p.levels.W[k];
+            if (a0 < b1 && b0 < a1) return false;
+        }
+    }
+    return covered == p.S;
+}
+
+// Tile order and tile count of the forward / gradient kernels (TileOrder):
+// column groups for pixel queries with fewer (b, head group) pairs than XCDs
+// (as many groups as give every XCD one region), else linear.
+TileOrder tile_order(const Problem &p, int log2qs, int ngroups, int64_t *ntiles) {
+    TileOrder to = {0, 0};
+    const int qs = 1 << log2qs;
+    const int64_t qblocks = (p.Q + qs - 1) / qs;
+    *ntiles = p.B * ngroups * qblocks;
+    const int64_t bg = p.B * ngroups;
+    if (!pixel_queries(p) || bg >= kXcds || kXcds % bg != 0)
+        return to;
+    const int nc = (int)(kXcds / bg);
+    int64_t per_region = 0;
+    for (int c = 0; c < nc; ++c) {
+        int64_t n = 0;
+        for (int l = 0; l < (int)p.L; ++l) {
+            uint32_t x0, x1;
+            n += (int64_t)p.levels.H[l] *
+                 group_columns((uint32_t)p.levels.W[l], (uint32_t)c, (uint32_t)nc, log2qs, &x0, &x1);
+        }
+        per_region = std::max(per_region, n);
+    }
+    if (bg * nc * per_region >= ((int64_t)1 << 31)) return to;  // 32-bit tile arithmetic
+    to = {nc, (int32_t)per_region};
+    *ntiles = bg * nc * per_region;
+    return to;
+}
+
+// Chunk-owner parameter loads may use vector loads: no point split, whole
+// chunks of `ch` points, and the chunk's locations / weights aligned for 16-
+// and 8- (16-bit) or 16-byte (fp32) loads.
+bool params_vectorizable(const Problem &p, int log2s, int ch, const void *loc, const void *attn) {
+    const uintptr_t e = p.pdtype == MSDA_F32 ? 4 : 2;
+    return log2s == 0 && (p.L * p.K) % ch == 0 && reinterpret_cast<uintptr_t>(loc) % 16 == 0 &&
+           reinterpret_cast<uintptr_t>(attn) % (e == 2 ? 8 : 16) == 0;
+}
+
 // Buffer gathers address one batch slice with 32-bit offsets.
 bool slice_fits_buffer(const Problem &p) {
     const int64_t e = p.dtype == MSDA_F32 ? 4 : 2;
@@ -1851,20 +2114,24 @@ hipError_t fwd_launch(const Problem &p, const Mapping &mp, const void *value, co
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
     const int hg = fwd_heads((int)p.M, qpb, (int)(p.D * (int64_t)sizeof(typename DT::S)));
     const int qblocks = (int)((p.Q + qpb / hg - 1) / (qpb / hg));
-    const int64_t ntiles = p.B * (p.M / hg) * qblocks;
+    int64_t ntiles;
+    const int log2qs = 8 - mp.log2_group - mp.log2_split - (hg == 4 ? 2 : hg == 2 ? 1 : 0);
+    const TileOrder to = tile_order(p, log2qs, (int)(p.M / hg), &ntiles);
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (slice_fits_buffer(p))
         MSDA_LAUNCH((msda_fwd_kernel<DT, PT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
                            dim3(kBlock), 0, stream, static_cast<const E *>(value),
                            static_cast<const P *>(loc), static_cast<const P *>(attn),
                            static_cast<E *>(out), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
-                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
+                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split, to,
+                           params_vectorizable(p, mp.log2_split, CH, loc, attn));
     else if constexpr (std::is_same<DT, PT>::value)
         MSDA_LAUNCH((msda_fwd_kernel<DT, PT, VEC, CH, false>), dim3((unsigned)(per_xcd * kXcds)),
                            dim3(kBlock), 0, stream, static_cast<const E *>(value),
                            static_cast<const P *>(loc), static_cast<const P *>(attn),
                            static_cast<E *>(out), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
-                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
+                           (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split, to,
+                           params_vectorizable(p, mp.log2_split, CH, loc, attn));
     else
         return hipErrorInvalidValue;  // mixed dtypes need a buffer-addressable slice
     return hipGetLastError();
@@ -1880,7 +2147,9 @@ hipError_t grad_launch(const Problem &p, const Mapping &mp, const void *value, c
     const int qpb = kBlock >> (mp.log2_group + mp.log2_split);
     const int hg = grad_heads((int)p.M, qpb);
     const int qblocks = (int)((p.Q + qpb / hg - 1) / (qpb / hg));
-    const int64_t ntiles = p.B * (p.M / hg) * qblocks;
+    int64_t ntiles;
+    const int log2qs = 8 - mp.log2_group - mp.log2_split - (hg == 4 ? 2 : hg == 2 ? 1 : 0);
+    const TileOrder to = tile_order(p, log2qs, (int)(p.M / hg), &ntiles);
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (!slice_fits_buffer(p)) return hipErrorInvalidValue;  // binning requires it
     MSDA_LAUNCH((msda_grad_kernel<DT, PT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
@@ -1888,7 +2157,8 @@ hipError_t grad_launch(const Problem &p, const Mapping &mp, const void *value, c
                        static_cast<const P *>(loc), static_cast<const P *>(attn),
                        static_cast<const E *>(grad_out), static_cast<P *>(grad_loc),
                        static_cast<P *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
-                       (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split);
+                       (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split, to,
+                       params_vectorizable(p, mp.log2_split, CH, loc, attn));
     return hipGetLastError();
 }
 
@@ -2325,7 +2595,8 @@ hipError_t grad_sort_launch(const Problem &p, const Mapping &mp, const void *val
                        static_cast<const E *>(grad_out), static_cast<P *>(grad_loc),
                        static_cast<P *>(grad_attn), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
                        (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split,
-                       (uint32_t)ngrad, bins.starts, bins.cursor, bins.records, p.nbbm,
+                       params_vectorizable(p, mp.log2_split, 4, loc, attn), (uint32_t)ngrad,
+                       bins.starts, bins.cursor, bins.records, p.nbbm,
                        (uint32_t)nseg, (uint32_t)nsegp, (uint32_t)nzero,
                        static_cast<uint4 *>(zero_dst), n16);
     return hipGetLastError();

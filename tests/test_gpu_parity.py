@@ -685,3 +685,36 @@ def test_single_stream_flag_and_side_stream_release():
                               inp["spatial_shapes"], None, trows, **kw))
         if release:
             release_thread_resources()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("reordered", [False, True])
+def test_pixel_queries_in_column_groups(dtype, reordered):
+    """Encoder-style queries (every pyramid pixel, sampling near its own
+    pixel) with fewer (batch, head group) pairs than XCDs: the forward and
+    gradient kernels visit the queries in column groups of every level.
+    Odd level widths give ragged tiles at every group edge; `reordered`
+    stores the levels in another order along S (a given level_start_index
+    that still tiles [0, S)). Results must match the oracle as in any order."""
+    levels = ((24, 37), (12, 19), (6, 10), (3, 5))
+    wl = Workload(name="pixels", dtype=dtype, B=1, Q=None, M=4, D=32, K=4, levels=levels,
+                  loc_kind="reference", loc_sigma=0.05, seed=31)
+    inp = make_inputs(wl)
+    starts = None
+    if reordered:
+        # level 2, then 0, then 3, then 1 along S: value rows and queries move together
+        order = [2, 0, 3, 1]
+        sizes = [h * w for h, w in levels]
+        st, acc = [0] * 4, 0
+        for l in order:
+            st[l] = acc
+            acc += sizes[l]
+        starts = torch.tensor(st)
+        dflt = np.cumsum([0] + sizes[:-1])
+        perm = np.concatenate([np.arange(dflt[l], dflt[l] + sizes[l]) for l in order])
+        inp["value"] = inp["value"][:, perm].contiguous()
+        for k in ("sampling_locations", "attention_weights", "grad_output"):
+            inp[k] = inp[k][:, perm].contiguous()
+    say(f"case pixel queries in column groups {dtype} reordered={reordered}")
+    for accum in ("auto", "native"):
+        full_check(inp, dtype, accum, starts=starts)
