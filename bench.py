@@ -30,14 +30,19 @@ to the kernel that writes grad_loc / grad_attn; of grad_value, the rows of
 levels summed with atomics that some corner touches to the kernel issuing
 those atomics, their untouched rows to the zero fill, the rows of binned
 levels to the accumulation, the rows of fp32-scratch levels to the scratch
-add. Everything else a kernel moves is reported apart as `overhead_bytes`
+add (fp32-scratch and pre-reduced levels). Everything else a kernel moves is
+reported apart as `overhead_bytes`
 (modelled, not measured): the zero fill's rows that atomics or bins later
 overwrite, the read of each atomically updated row (U_a*D*e_acc, e_acc = 4
 for fp32 rows), the scatter kernel's second read of parameters and upstream
 gradient, bin records (8 bytes per in-bounds corner of a binned level,
 written by the place / sort step and read by the accumulation), the count
 and sort steps' parameter reads, the accumulation's reads of upstream
-gradient rows, and the fp32 scratch's fill, read-modify-writes and read.
+gradient rows, the pre-reduction's reads of its levels' parameters (the
+locations three times: window placement, count, place; the weights once) and
+of the upstream gradient, and its read-modify-write of touched fp32 rows
+(counted once per row: a lower bound, as chunks and overlapping windows add
+more), and the fp32 scratch's fill, read-modify-writes and read.
 
 Prints one JSON line:
   value / ms_per_step   microseconds per forward+backward step of the headline
@@ -139,13 +144,16 @@ class ByteModel:
         atomic = [l for l, m in enumerate(level_modes) if m == "native"]
         scratch = [l for l, m in enumerate(level_modes) if m == "fp32_scratch"]
         binned = [l for l, m in enumerate(level_modes) if m == "binned"]
+        prered = [l for l, m in enumerate(level_modes) if m == "prereduce"]
         self.U, self.C = sum(u for u, _ in per), sum(c for _, c in per)
         U_a = sum(per[l][0] for l in atomic)
         U_s = sum(per[l][0] for l in scratch)
         C_b = sum(per[l][1] for l in binned)
         log(f"byte model: U={self.U} rows, C={self.C} corners, {time.perf_counter() - t0:.1f} s")
+        U_p = sum(per[l][0] for l in prered)
         rows = lambda lv: sum(B * wl.levels[l][0] * wl.levels[l][1] * M for l in lv)
-        N_a, N_s, N_b = rows(atomic) * D, rows(scratch) * D, rows(binned) * D
+        N_a, N_s, N_b = rows(atomic) * D, rows(scratch + prered) * D, rows(binned) * D
+        P_p = B * Q * M * K * len(prered)
         e_acc = 4 if wl.dtype == torch.float32 else e
         P_a, P_b = B * Q * M * K * len(atomic), B * Q * M * K * len(binned)
         go = B * Q * M * D * e
@@ -175,6 +183,10 @@ class ByteModel:
             "bin_place": 3 * P_b * pe + rec,
             "bin_local_sort": 3 * P_b * pe + rec + 8 * nbins,
             "bin_accum_kernel": rec + go,
+            # pre-reduction: its levels' locations read three times and weights
+            # once, the upstream gradient, one read-modify-write of every
+            # touched fp32 row
+            "prereduce_kernel": 7 * P_p * pe + go + 2 * U_p * D * 4,
         }
         ov["scatter_accum_kernel"] = ov["msda_scatter_kernel"] + ov["bin_accum_kernel"]
         # the gradient launch that also sorts and fills
@@ -456,7 +468,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--accum", default="auto",
-                    choices=["auto", "native", "fp32_scratch", "per_level", "binned", "mixed"])
+                    choices=["auto", "native", "fp32_scratch", "per_level", "binned", "mixed",
+                             "prereduce"])
     ap.add_argument("--configs", default=",".join(DEFAULT_CONFIGS),
                     help="comma-separated workloads measured besides the headline ('none': skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

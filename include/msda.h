@@ -101,6 +101,20 @@ typedef enum msda_dtype {
  *                 corner of every binned level's points;
  *   MIXED         BINNED for the levels above 4 contributions per pixel,
  *                 native atomics for the others (same conditions as BINNED);
+ *   PREREDUCE     the levels above 256 contributions per pixel are summed
+ *                 in LDS first (msda-triton README, section "Benchmarks": a
+ *                 shared-memory pre-reduction): one workgroup per head and
+ *                 block of queries (a 2-D tile of pixels and the matching
+ *                 pixels of the other levels when the queries are the
+ *                 pyramid's pixels in S order, else consecutive queries)
+ *                 counting-sorts its corners on such a level by pixel of a
+ *                 window placed at the mean of its samples there, sums each
+ *                 pixel's records in fp32 and adds the sums into the level's
+ *                 fp32 workspace rows (corners outside the window add there
+ *                 directly); the workspace is rounded once into grad_value.
+ *                 The levels above 4 are BINNED, the others native (same
+ *                 conditions as BINNED, and D up to 256). Measured slower
+ *                 than MIXED on the encoder shapes; AUTO does not pick it;
  *   AUTO          MIXED where binning applies (which is BINNED when every
  *                 level is above the threshold, NATIVE when none is), else
  *                 PER_LEVEL for bf16 and NATIVE for fp16 / fp32.
@@ -113,14 +127,16 @@ typedef enum msda_accum {
     MSDA_ACCUM_FP32_SCRATCH = 1,
     MSDA_ACCUM_PER_LEVEL = 2,
     MSDA_ACCUM_BINNED = 3,
-    MSDA_ACCUM_MIXED = 4
+    MSDA_ACCUM_MIXED = 4,
+    MSDA_ACCUM_PREREDUCE = 5
 } msda_accum_t;
 
 /* How msda_backward accumulates one level's grad_value rows. */
 typedef enum msda_level_mode {
     MSDA_LEVEL_NATIVE = 0,        /* atomics of the value dtype       */
     MSDA_LEVEL_FP32_SCRATCH = 1,  /* fp32 atomics into the workspace  */
-    MSDA_LEVEL_BINNED = 2         /* records, summed per bin          */
+    MSDA_LEVEL_BINNED = 2,        /* records, summed per bin          */
+    MSDA_LEVEL_PREREDUCE = 3      /* LDS sums, then fp32 scratch      */
 } msda_level_mode_t;
 
 typedef enum msda_status {

@@ -21,11 +21,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmsda_amd.so")
 
 MSDA_F32, MSDA_F16, MSDA_BF16 = 0, 1, 2
-ACCUM_AUTO, ACCUM_NATIVE, ACCUM_FP32_SCRATCH, ACCUM_PER_LEVEL, ACCUM_BINNED, ACCUM_MIXED = \
-    -1, 0, 1, 2, 3, 4
+ACCUM_AUTO, ACCUM_NATIVE, ACCUM_FP32_SCRATCH, ACCUM_PER_LEVEL, ACCUM_BINNED, ACCUM_MIXED, \
+    ACCUM_PREREDUCE = -1, 0, 1, 2, 3, 4, 5
 _RESOLVED = {ACCUM_NATIVE: "native", ACCUM_FP32_SCRATCH: "fp32_scratch", ACCUM_PER_LEVEL: "per_level",
-             ACCUM_BINNED: "binned", ACCUM_MIXED: "mixed"}
-LEVEL_MODES = {0: "native", 1: "fp32_scratch", 2: "binned"}
+             ACCUM_BINNED: "binned", ACCUM_MIXED: "mixed", ACCUM_PREREDUCE: "prereduce"}
+LEVEL_MODES = {0: "native", 1: "fp32_scratch", 2: "binned", 3: "prereduce"}
 FLAG_ACCUMULATE_GRAD_VALUE = 1
 FLAG_CONTINUE_SCRATCH = 2
 FLAG_DEFER_SCRATCH = 4
@@ -35,7 +35,8 @@ MAX_LEVELS = 16
 _DTYPE_CODES = {torch.float32: MSDA_F32, torch.float16: MSDA_F16, torch.bfloat16: MSDA_BF16}
 _ACCUM_CODES = {"auto": ACCUM_AUTO, None: ACCUM_AUTO, "native": ACCUM_NATIVE, False: ACCUM_NATIVE,
                 "fp32_scratch": ACCUM_FP32_SCRATCH, True: ACCUM_FP32_SCRATCH,
-                "per_level": ACCUM_PER_LEVEL, "binned": ACCUM_BINNED, "mixed": ACCUM_MIXED}
+                "per_level": ACCUM_PER_LEVEL, "binned": ACCUM_BINNED, "mixed": ACCUM_MIXED,
+                "prereduce": ACCUM_PREREDUCE}
 
 # every symbol include/msda.h declares
 EXPORTED_SYMBOLS = ("msda_forward", "msda_forward_ex", "msda_forward_point_parallel",

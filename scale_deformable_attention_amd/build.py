@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = [os.path.join(HERE, "csrc", "msda_kernels.hip"),
            os.path.join(HERE, "csrc", "msda_prep_kernels.hip"),
            os.path.join(HERE, "csrc", "msda_probe.hip"),
+           os.path.join(HERE, "csrc", "msda_prereduce.hip"),
            os.path.join(HERE, "csrc", "msda_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -7,10 +7,12 @@
 // "Quickstart"; course page "4. The forward kernel", section "The wrapper").
 
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <string>
 
@@ -307,6 +309,7 @@ int binned_levels(const msda::Problem &p) {
 }
 
 int resolved_mode(const msda::Problem &p) {
+    if (p.levels.prered) return MSDA_ACCUM_PREREDUCE;
     const int nb = binned_levels(p);
     if (nb > 0) return nb == (int)p.L ? MSDA_ACCUM_BINNED : MSDA_ACCUM_MIXED;
     int n = 0;
@@ -315,7 +318,7 @@ int resolved_mode(const msda::Problem &p) {
     return n == (int)p.L ? MSDA_ACCUM_FP32_SCRATCH : MSDA_ACCUM_PER_LEVEL;
 }
 
-bool valid_accum(int accum) { return accum >= MSDA_ACCUM_AUTO && accum <= MSDA_ACCUM_MIXED; }
+bool valid_accum(int accum) { return accum >= MSDA_ACCUM_AUTO && accum <= MSDA_ACCUM_PREREDUCE; }
 
 // A level is "contended" above this many contributions per pixel.
 constexpr double kContended = 4.0;
@@ -384,7 +387,8 @@ struct BinPlan {
 
 // Bins the levels selected by `contended_only` (all levels, or those above
 // kContended contributions per pixel); the other levels keep bin_shift = -1.
-bool plan_bins(msda::Problem *p, BinPlan *bp, bool contended_only) {
+bool plan_bins(msda::Problem *p, BinPlan *bp, bool contended_only,
+               double max_contributions = 1e300) {
     const int64_t e = p->dtype == MSDA_F32 ? 4 : 2;
     const int64_t P = p->B * p->Q * p->M * p->L * p->K;
     // 28-bit query field; 32-bit record indices; buffer-addressed value and
@@ -403,6 +407,7 @@ bool plan_bins(msda::Problem *p, BinPlan *bp, bool contended_only) {
         p->levels.bin_off[l] = (int32_t)nbbm;  // a level without bins shares the next level's offset
         p->levels.bin_shift[l] = -1;
         if (contended_only && !(c > kContended)) continue;
+        if (!(c <= max_contributions)) continue;  // pre-reduced instead
         const double want = c > 0 ? kBinRecords / c : (double)tp_max;
         const int64_t HW = (int64_t)p->levels.H[l] * p->levels.W[l];
         int sh = 0;  // no taller than the level itself rounded up to a power of two
@@ -434,6 +439,94 @@ bool plan_bins(msda::Problem *p, BinPlan *bp, bool contended_only) {
     return true;
 }
 
+// Pre-reduced levels (PREREDUCE): those above kPreReduce contributions per
+// pixel. Their fp32 scratch follows the bins in the workspace (256-byte
+// aligned at `offset`); returns its bytes and fills the launch layout.
+constexpr double kPreReduce = 256.0;
+constexpr int64_t kPreWindowPixels = 1024;       // per level, shaped like the level
+constexpr int64_t kPreMaxLdsBytes = 152 * 1024;  // at most, beside the static LDS
+
+bool pixel_queries(const msda::Problem &p) {
+    if (p.Q != p.S || levels_overlap(p)) return false;
+    int64_t covered = 0;
+    for (int l = 0; l < (int)p.L; ++l) covered += (int64_t)p.levels.H[l] * p.levels.W[l];
+    return covered == p.S;
+}
+
+// Returns false when the LDS a workgroup needs does not fit.
+bool plan_prereduce(msda::Problem *p, size_t offset, msda::PreTiles *pt, size_t *bytes) {
+    memset(pt, 0, sizeof(*pt));
+    *bytes = 0;
+    p->levels.prered = 0;
+    size_t total = 0;
+    for (int l = 0; l < (int)p->L; ++l) {
+        if (!(contributions_per_pixel(*p, l) > kPreReduce)) continue;
+        p->levels.prered |= 1u << l;
+        p->levels.scratch_off[l] = (int64_t)((offset + total) / sizeof(float));
+        total += (size_t)(p->B * (int64_t)p->levels.H[l] * p->levels.W[l] * p->M * p->D) *
+                 sizeof(float);
+        pt->lev[pt->nlev++] = l;
+    }
+    *bytes = total;
+    if (!pt->nlev) return true;
+    pt->pixel = pixel_queries(*p) ? 1 : 0;
+    // windows of about kPreWindowPixels, shaped like their level
+    for (int li = 0; li < pt->nlev; ++li) {
+        const int l = pt->lev[li];
+        const double H = p->levels.H[l], W = p->levels.W[l];
+        int64_t wy = std::max<int64_t>(1, (int64_t)std::sqrt((double)kPreWindowPixels * H / W));
+        wy = std::min<int64_t>(wy, p->levels.H[l]);
+        const int64_t wx =
+            std::min<int64_t>(std::max<int64_t>(1, kPreWindowPixels / wy), p->levels.W[l]);
+        pt->wx[li] = (int32_t)wx;
+        pt->wy[li] = (int32_t)wy;
+        pt->max_px = std::max<int32_t>(pt->max_px, (int32_t)(wx * wy));
+    }
+    const msda::LevelTable &lt = p->levels;
+    if (pt->pixel)
+        for (int l = 1; l < (int)p->L; ++l)
+            if ((int64_t)lt.H[l] * lt.W[l] > (int64_t)lt.H[pt->ref] * lt.W[pt->ref]) pt->ref = l;
+    // blocks: the largest whose working set fits in LDS (pixel tiles of 16 x
+    // 16 pixels of the reference level, or 256 consecutive queries, halved
+    // until it fits)
+    for (int side = pt->pixel ? 16 : 256; side >= 1; side /= 2) {
+        int64_t maxq = side;
+        if (pt->pixel) {  // the largest merged tile
+            pt->tile = side;
+            const int32_t H0 = lt.H[pt->ref], W0 = lt.W[pt->ref];
+            const int64_t ny = (H0 + side - 1) / side, nx = (W0 + side - 1) / side;
+            maxq = 0;
+            for (int64_t ty = 0; ty < ny; ++ty)
+                for (int64_t tx = 0; tx < nx; ++tx) {
+                    int64_t n = 0;
+                    for (int l = 0; l < (int)p->L; ++l)
+                        n += (int64_t)(msda::pre_tile_span(ty + 1, side, lt.H[l], H0, ny) -
+                                       msda::pre_tile_span(ty, side, lt.H[l], H0, ny)) *
+                             (msda::pre_tile_span(tx + 1, side, lt.W[l], W0, nx) -
+                              msda::pre_tile_span(tx, side, lt.W[l], W0, nx));
+                    maxq = std::max(maxq, n);
+                }
+        } else {
+            pt->lin_queries = side;
+        }
+        if (4 * maxq * p->K >= INT32_MAX) continue;
+        pt->max_queries = (int32_t)maxq;
+        pt->max_records = (int32_t)(4 * maxq * p->K);
+        pt->max_chunks = pt->max_records / msda::kPreChunk + pt->max_px;
+        if (msda::pre_lds_bytes(*pt, p->D, p->dtype == MSDA_F32 ? 4 : 2) <= kPreMaxLdsBytes)
+            return true;
+    }
+    return false;
+}
+
+// Why an explicit BINNED / MIXED / PREREDUCE request was refused.
+const char *inapplicable_mode(int accum) {
+    return accum == MSDA_ACCUM_PREREDUCE
+               ? "pre-reduced accumulation does not apply to this problem (it needs the binned "
+                 "conditions, head_dim <= 256 and room in LDS)"
+               : "binned accumulation does not apply to this problem";
+}
+
 void clear_bins(msda::Problem *p) {
     for (int l = 0; l < MSDA_MAX_LEVELS; ++l) {
         p->levels.bin_shift[l] = -1;
@@ -451,10 +544,33 @@ void clear_bins(msda::Problem *p) {
 // Measured on MI355X: native atomics are fastest on levels whose pixels
 // receive a few contributions; on contended levels they serialise on the same
 // addresses (and bf16 adds lose precision), where the binned sum wins.
-int plan_accum(msda::Problem *p, int accum, size_t *bytes, BinPlan *bp) {
+int plan_accum(msda::Problem *p, int accum, size_t *bytes, BinPlan *bp,
+               msda::PreTiles *pt = nullptr) {
     clear_bins(p);
     plan_scratch(p, MSDA_ACCUM_NATIVE);
+    p->levels.prered = 0;
     *bytes = 0;
+    if (accum == MSDA_ACCUM_PREREDUCE) {
+        msda::PreTiles tmp;
+        if (!pt) pt = &tmp;
+        // (D <= 256: a block's upstream-gradient rows leave room for windows
+        // in LDS)
+        if (p->D > 256 || !plan_bins(p, bp, true, kPreReduce)) {
+            clear_bins(p);
+            return -1;
+        }
+        if (bp->nbins == 0) clear_bins(p);
+        const size_t off = bp->nbins > 0 ? align_up(bp->bytes, 256) : 0;
+        size_t scr = 0;
+        if (!plan_prereduce(p, off, pt, &scr)) {
+            clear_bins(p);
+            plan_scratch(p, MSDA_ACCUM_NATIVE);
+            p->levels.prered = 0;
+            return -1;
+        }
+        *bytes = scr ? off + scr : (bp->nbins > 0 ? bp->bytes : 0);
+        return resolved_mode(*p);
+    }
     if (accum == MSDA_ACCUM_BINNED || accum == MSDA_ACCUM_MIXED || accum == MSDA_ACCUM_AUTO) {
         if (plan_bins(p, bp, accum != MSDA_ACCUM_BINNED)) {
             if (bp->nbins > 0) *bytes = bp->bytes;
@@ -700,7 +816,7 @@ int msda_backward_resolve_accum(int dtype, int64_t batch, int64_t num_keys, int6
     size_t bytes;
     BinPlan bp;
     const int mode = plan_accum(&p, accum, &bytes, &bp);
-    if (mode < 0) fail(MSDA_ERR_UNSUPPORTED, "binned accumulation does not apply to this problem");
+    if (mode < 0) fail(MSDA_ERR_UNSUPPORTED, "%s", inapplicable_mode(accum));
     return mode;
 }
 
@@ -719,12 +835,13 @@ int64_t msda_backward_plan(int dtype, int64_t batch, int64_t num_keys, int64_t n
     size_t bytes;
     BinPlan bp;
     if (plan_accum(&p, accum, &bytes, &bp) < 0) {
-        fail(MSDA_ERR_UNSUPPORTED, "binned accumulation does not apply to this problem");
+        fail(MSDA_ERR_UNSUPPORTED, "%s", inapplicable_mode(accum));
         return -1;
     }
     if (level_modes)
         for (int l = 0; l < (int)p.L; ++l)
-            level_modes[l] = p.levels.bin_shift[l] >= 0    ? MSDA_LEVEL_BINNED
+            level_modes[l] = (p.levels.prered >> l) & 1u   ? MSDA_LEVEL_PREREDUCE
+                             : p.levels.bin_shift[l] >= 0    ? MSDA_LEVEL_BINNED
                              : p.levels.scratch_off[l] >= 0 ? MSDA_LEVEL_FP32_SCRATCH
                                                             : MSDA_LEVEL_NATIVE;
     return binned_levels(p) > 0 ? bp.nbins : 0;
@@ -746,7 +863,7 @@ size_t msda_backward_workspace_size(int dtype, int64_t batch, int64_t num_keys, 
     size_t bytes = 0;
     BinPlan bp;
     if (plan_accum(&p, accum, &bytes, &bp) < 0) {
-        fail(MSDA_ERR_UNSUPPORTED, "binned accumulation does not apply to this problem");
+        fail(MSDA_ERR_UNSUPPORTED, "%s", inapplicable_mode(accum));
         return 0;
     }
     return bytes;
@@ -781,10 +898,12 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
                     "PER_LEVEL accumulation");
     size_t need = 0;
     BinPlan bp;
-    const int mode = plan_accum(&p, accum, &need, &bp);
+    msda::PreTiles pt;
+    const int mode = plan_accum(&p, accum, &need, &bp, &pt);
     if (mode < 0)
-        return fail(MSDA_ERR_UNSUPPORTED, "binned accumulation does not apply to this problem");
-    const bool binned = mode == MSDA_ACCUM_BINNED || mode == MSDA_ACCUM_MIXED;
+        return fail(MSDA_ERR_UNSUPPORTED, "%s", inapplicable_mode(accum));
+    const bool binned = mode == MSDA_ACCUM_BINNED || mode == MSDA_ACCUM_MIXED ||
+                        (p.levels.prered && bp.nbins > 0);
     const bool all_binned = mode == MSDA_ACCUM_BINNED;
     if ((st = check_ptr(value, "value", dtype))) return st;
     if ((st = check_ptr(grad_value, "grad_value", dtype))) return st;
@@ -976,6 +1095,26 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
                 break;
             }
         } while (false);
+        // pre-reduced levels: their fp32 rows (after the bins in the
+        // workspace) summed in LDS windows, then rounded into grad_value
+        // after the zero fill; disjoint from the binned rows
+        if (err == hipSuccess && p.levels.prered) {
+            char *scr0 = ws + align_up(bp.bytes, 256);
+            const size_t scr_bytes = need - align_up(bp.bytes, 256);
+            if ((err = marked(msda::launch_zero(scr0, scr_bytes, before(s)), s, "scratch_zero")) !=
+                hipSuccess)
+                what = "scratch zero fill";
+            else if ((err = marked(msda::launch_prereduce(p, pt, sampling_locations,
+                                                          attention_weights, grad_output,
+                                                          reinterpret_cast<float *>(ws),
+                                                          before(s)),
+                                   s, "prereduce_kernel")) != hipSuccess)
+                what = "pre-reduce launch";
+            else if ((err = marked(msda::launch_scratch_add(p, reinterpret_cast<float *>(ws),
+                                                            grad_value, before(s)),
+                                   s, "scratch_add_kernel")) != hipSuccess)
+                what = "scratch add launch";
+        }
         if (side) {
             hipError_t je = hipEventRecord(side->join, t);
             if (je == hipSuccess) je = hipStreamWaitEvent(s, side->join, 0);
@@ -1001,6 +1140,12 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
                                             before(s)),
                       s, "msda_bwd_kernel")) != hipSuccess)
         return hip_fail(err, "backward launch");
+    if (p.Q > 0 && p.levels.prered &&
+        (err = marked(msda::launch_prereduce(p, pt, sampling_locations, attention_weights,
+                                             grad_output, static_cast<float *>(workspace),
+                                             before(s)),
+                      s, "prereduce_kernel")) != hipSuccess)
+        return hip_fail(err, "pre-reduce launch");
     if (need && !defer &&
         (err = marked(msda::launch_scratch_add(p, static_cast<const float *>(workspace),
                                                grad_value, before(s)),

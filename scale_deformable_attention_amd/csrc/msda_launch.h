@@ -51,7 +51,51 @@ struct LevelTable {
     int32_t bin_off[MSDA_MAX_LEVELS];
     int32_t blevel[MSDA_MAX_LEVELS];  // the binned levels, in order
     int32_t nblev;
+    uint32_t prered;  // bit l: level l is pre-reduced in LDS (launch_prereduce)
 };
+
+// Pre-reduced levels (launch_prereduce): their fp32 scratch rows receive the
+// per-window sums of one workgroup. One workgroup per (b, m, block of
+// queries): for pixel queries a tile of `tile` x `tile` pixels of the largest
+// level (ref) together with the rows and columns of every other level in the
+// same normalised area (pre_tile_span), else lin_queries consecutive queries.
+// Window li (of level lev[li]) is wx[li] x wy[li] pixels.
+struct PreTiles {
+    int32_t pixel;
+    int32_t ref;          // pixel tiles: the level with the most pixels
+    int32_t tile;         // pixel tiles: side, in pixels of the reference level
+    int32_t lin_queries;  // linear blocks: queries per block
+    int32_t nlev;
+    int32_t lev[MSDA_MAX_LEVELS];
+    int32_t wx[MSDA_MAX_LEVELS];
+    int32_t wy[MSDA_MAX_LEVELS];
+    int32_t max_px;       // pixels of the largest window
+    int32_t max_queries;  // queries of the largest block
+    int32_t max_records;  // 4 corners of every point of the largest block on one level
+    int32_t max_chunks;   // record chunks of one level: max_records / kPreChunk + max_px
+};
+
+constexpr int kPreBlock = 256;  // threads of a pre-reduction workgroup
+constexpr int kPreChunk = 32;   // records a lane sums before it adds into the scratch
+
+// First row (column) on a level of n rows (columns) of tile i of `tiles`
+// tiles of `side` rows over the reference level's n0 rows: the rows whose
+// normalised position falls in the tile's, rounded to the nearest row
+// boundary; the last tile ends at n.
+__host__ __device__ inline int32_t pre_tile_span(int64_t i, int32_t side, int32_t n, int32_t n0,
+                                                 int64_t tiles) {
+    return i >= tiles ? n : (int32_t)((i * side * n + n0 / 2) / n0);
+}
+
+// Dynamic LDS bytes of one pre-reduction workgroup: record weights and
+// record queries, window row starts, cursors and chunk starts, chunk pixels,
+// query indexes (4 bytes each), then the upstream-gradient rows (D + 1
+// elements of `esize` bytes).
+inline size_t pre_lds_bytes(const PreTiles &pt, int64_t D, int esize) {
+    return (2 * (size_t)pt.max_records + 3 * (size_t)pt.max_px + 2 + (size_t)pt.max_chunks +
+            (size_t)pt.max_queries) * 4 +
+           (size_t)pt.max_queries * (size_t)(D + 1) * (size_t)esize;
+}
 
 // Everything a launch needs, validated by the host layer.
 struct Problem {
@@ -196,6 +240,11 @@ hipError_t launch_reference_grad(const PrepProblem &p, const void *grad_loc, voi
                                  hipStream_t stream);
 
 hipError_t launch_zero(void *dst, size_t bytes, hipStream_t stream);
+
+// The pre-reduced levels' contributions into their fp32 scratch rows (the
+// scratch must be zero-filled first; scratch_add rounds it into grad_value).
+hipError_t launch_prereduce(const Problem &p, const PreTiles &pt, const void *loc, const void *attn,
+                            const void *grad_out, float *workspace, hipStream_t stream);
 
 // Atomic request-rate probe (msda_probe.hip, measurement only): workgroups of
 // 256 threads, each lane `iters` no-return adds (fp32, or packed bf16 pairs)

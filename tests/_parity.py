@@ -27,7 +27,7 @@ fp16 (11), and each rounding may also err by half the spacing of the
 type's subnormals (2^-25 for fp16, 2^-134 for bf16), so an element's
 rounding term is gamma(n) * sum|c_i| + 2 n * that. It is added to the bar
 above on those levels only; every level summed in fp32 (fp32 data, fp32
-scratch, binned) is held to the bar alone. Which levels a call accumulates
+scratch, binned, pre-reduced) is held to the bar alone. Which levels a call accumulates
 with 16-bit atomics is derived here from the documented policy
 (expected_level_modes) and the library's own report must equal it, so a
 wrong plan fails the test instead of loosening it.
@@ -52,8 +52,10 @@ UNIT_ROUNDOFF = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
 SUBNORMAL_HALF_SPACING = {torch.bfloat16: 2.0 ** -134, torch.float16: 2.0 ** -25}
 
 # Contributions per pixel (Q * K * 4 / (H * W)) above which a level counts as
-# contended (include/msda.h, msda_accum_t).
+# contended, and above which PREREDUCE sums it in LDS (include/msda.h,
+# msda_accum_t).
 CONTENDED = 4.0
+PREREDUCED = 256.0
 
 # The per-level plan of every named workload under each accumulation mode, as
 # include/msda.h's policy gives it (contributions per pixel in comments).
@@ -61,27 +63,32 @@ WORKLOAD_PLANS = {
     # 1.6, 6.4
     "tiny_fp32": {"auto": ["native", "binned"], "mixed": ["native", "binned"],
                   "binned": ["binned", "binned"], "native": ["native", "native"],
-                  "fp32_scratch": ["native", "native"], "per_level": ["native", "native"]},
+                  "fp32_scratch": ["native", "native"], "per_level": ["native", "native"],
+                  "prereduce": ["native", "binned"]},
     # 0.29, 1.14, 4.57, 17.6
     "decoder_bf16": {"auto": ["native", "native", "binned", "binned"],
                      "mixed": ["native", "native", "binned", "binned"],
                      "binned": ["binned"] * 4, "native": ["native"] * 4,
                      "fp32_scratch": ["fp32_scratch"] * 4,
-                     "per_level": ["native", "native", "fp32_scratch", "fp32_scratch"]},
+                     "per_level": ["native", "native", "fp32_scratch", "fp32_scratch"],
+                     "prereduce": ["native", "native", "binned", "binned"]},
     # 21.3, 84.7, 339, 1302
     "encoder_fp16": {"auto": ["binned"] * 4, "mixed": ["binned"] * 4, "binned": ["binned"] * 4,
                      "native": ["native"] * 4, "fp32_scratch": ["fp32_scratch"] * 4,
-                     "per_level": ["fp32_scratch"] * 4},
+                     "per_level": ["fp32_scratch"] * 4,
+                     "prereduce": ["binned", "binned", "prereduce", "prereduce"]},
     # 0.43, 1.72, 6.86, 27.4
     "oddhead_fp32": {"auto": ["native", "native", "binned", "binned"],
                      "mixed": ["native", "native", "binned", "binned"],
                      "binned": ["binned"] * 4, "native": ["native"] * 4,
-                     "fp32_scratch": ["native"] * 4, "per_level": ["native"] * 4},
+                     "fp32_scratch": ["native"] * 4, "per_level": ["native"] * 4,
+                     "prereduce": ["native", "native", "binned", "binned"]},
     # 21.2, 85.0, 340, 1360
     "large_encoder_bf16": {"auto": ["binned"] * 4, "mixed": ["binned"] * 4,
                            "binned": ["binned"] * 4, "native": ["native"] * 4,
                            "fp32_scratch": ["fp32_scratch"] * 4,
-                           "per_level": ["fp32_scratch"] * 4},
+                           "per_level": ["fp32_scratch"] * 4,
+                           "prereduce": ["binned", "binned", "prereduce", "prereduce"]},
 }
 WORKLOAD_PLANS["decoder_mixed"] = WORKLOAD_PLANS["decoder_bf16"]
 WORKLOAD_PLANS["encoder_mixed"] = WORKLOAD_PLANS["encoder_fp16"]
@@ -130,13 +137,18 @@ def binning_applies(dtype, B, S, M, D, Q, K, L, spatial_shapes, level_start_inde
 
 def expected_level_modes(dtype, accum, spatial_shapes, B, S, M, D, Q, K,
                          level_start_index=None) -> list:
-    """Per-level accumulation ("native", "fp32_scratch" or "binned") that
-    include/msda.h's policy gives for this call."""
+    """Per-level accumulation ("native", "fp32_scratch", "binned" or
+    "prereduce") that include/msda.h's policy gives for this call."""
     accum = accum_name(accum)
     L = len(torch.as_tensor(spatial_shapes).tolist())
     hot = set(contended_levels(spatial_shapes, Q, K))
     bins = binning_applies(dtype, B, S, M, D, Q, K, L, spatial_shapes, level_start_index)
     half = dtype != torch.float32
+    if accum == "prereduce":
+        assert bins and D <= 256, "PREREDUCE does not apply to this problem"
+        very = set(contended_levels(spatial_shapes, Q, K, PREREDUCED))
+        return ["prereduce" if l in very else "binned" if l in hot else "native"
+                for l in range(L)]
     if accum in ("auto", "mixed") and bins:
         return ["binned" if l in hot else "native" for l in range(L)]
     if accum == "binned":

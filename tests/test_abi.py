@@ -129,8 +129,9 @@ def test_forward_given_start_index_may_differ_from_prefix(lib):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(accum=5), 4),
+    (dict(accum=6), 4),
     (dict(accum=-2), 4),
+    (dict(accum=5, D=300), 8),  # PREREDUCE: head_dim above 256
     (dict(flags=16), 2),
     (dict(flags=2), 2),  # scratch flags need an explicit scratch-capable mode
     (dict(gv=None, accum=0), 1),

@@ -17,7 +17,7 @@ from scale_deformable_attention_amd import MSDAError, PreparedCall, msda_backwar
 from scale_deformable_attention_amd.workloads import Workload, make_inputs, workload
 
 from _parity import (check_backward, check_forward, check_grad_value, level_row_ranges,
-                     parity_kwargs, to_np)
+                     parity_kwargs, plan_for, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -97,7 +97,7 @@ def _cached(name):
     ("decoder_bf16", "auto"), ("decoder_bf16", "native"), ("decoder_bf16", "fp32_scratch"),
     ("decoder_bf16", "binned"), ("decoder_bf16", "per_level"), ("oddhead_fp32", "mixed"),
     ("encoder_fp16", "auto"), ("encoder_fp16", "fp32_scratch"), ("encoder_fp16", "native"),
-    ("oddhead_fp32", "auto"), ("oddhead_fp32", "binned"),
+    ("oddhead_fp32", "auto"), ("oddhead_fp32", "binned"), ("encoder_fp16", "prereduce"),
 ])
 def test_workload_parity(name, accum):
     wl = workload(name)
@@ -107,7 +107,7 @@ def test_workload_parity(name, accum):
     full_check(inp, wl.dtype, accum, ref=ref, workload_name=name)
 
 
-@pytest.mark.parametrize("accum", ["auto", "fp32_scratch"])
+@pytest.mark.parametrize("accum", ["auto", "fp32_scratch", "prereduce"])
 def test_large_encoder_parity(accum):
     name = "large_encoder_bf16"
     wl = workload(name)
@@ -294,7 +294,7 @@ def test_empty_batch_and_queries(dtype):
     assert out.shape[0] == 0
 
 
-ALL_MODES = ["native", "fp32_scratch", "binned", "mixed", "auto"]
+ALL_MODES = ["native", "fp32_scratch", "binned", "mixed", "auto", "prereduce"]
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=str)
@@ -687,6 +687,23 @@ def test_single_stream_flag_and_side_stream_release():
             release_thread_resources()
 
 
+def _reorder_levels(inp, levels, order):
+    """Store the levels along S in `order` (value rows and, for pixel queries,
+    the queries move together); returns the level_start_index that still
+    tiles [0, S)."""
+    sizes = [h * w for h, w in levels]
+    st, acc = [0] * len(levels), 0
+    for l in order:
+        st[l] = acc
+        acc += sizes[l]
+    dflt = np.cumsum([0] + sizes[:-1])
+    perm = np.concatenate([np.arange(dflt[l], dflt[l] + sizes[l]) for l in order])
+    inp["value"] = inp["value"][:, perm].contiguous()
+    for k in ("sampling_locations", "attention_weights", "grad_output"):
+        inp[k] = inp[k][:, perm].contiguous()
+    return torch.tensor(st)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
 @pytest.mark.parametrize("reordered", [False, True])
 def test_pixel_queries_in_column_groups(dtype, reordered):
@@ -700,21 +717,74 @@ def test_pixel_queries_in_column_groups(dtype, reordered):
     wl = Workload(name="pixels", dtype=dtype, B=1, Q=None, M=4, D=32, K=4, levels=levels,
                   loc_kind="reference", loc_sigma=0.05, seed=31)
     inp = make_inputs(wl)
-    starts = None
-    if reordered:
-        # level 2, then 0, then 3, then 1 along S: value rows and queries move together
-        order = [2, 0, 3, 1]
-        sizes = [h * w for h, w in levels]
-        st, acc = [0] * 4, 0
-        for l in order:
-            st[l] = acc
-            acc += sizes[l]
-        starts = torch.tensor(st)
-        dflt = np.cumsum([0] + sizes[:-1])
-        perm = np.concatenate([np.arange(dflt[l], dflt[l] + sizes[l]) for l in order])
-        inp["value"] = inp["value"][:, perm].contiguous()
-        for k in ("sampling_locations", "attention_weights", "grad_output"):
-            inp[k] = inp[k][:, perm].contiguous()
+    starts = _reorder_levels(inp, levels, [2, 0, 3, 1]) if reordered else None
     say(f"case pixel queries in column groups {dtype} reordered={reordered}")
     for accum in ("auto", "native"):
         full_check(inp, dtype, accum, starts=starts)
+
+
+# Levels above 256 contributions per pixel, summed by PREREDUCE's in-LDS sort:
+# pixel queries (merged tiles; levels stored out of order; a wide head whose
+# tiles shrink to fit LDS), consecutive-query blocks, a level larger than the
+# window (corners outside it add straight into the scratch) and a wide head
+# with 8 points whose blocks shrink.
+PRE_CASES = {
+    "pixels": dict(B=2, Q=None, M=4, D=32, K=4, levels=((24, 37), (12, 19), (6, 10), (3, 5)),
+                   loc_kind="reference", loc_sigma=0.05, seed=41),
+    "pixels_reordered": dict(B=2, Q=None, M=4, D=32, K=4,
+                             levels=((24, 37), (12, 19), (6, 10), (3, 5)),
+                             loc_kind="reference", loc_sigma=0.05, seed=42),
+    "pixels_wide_head": dict(B=1, Q=None, M=1, D=128, K=4,
+                             levels=((24, 37), (12, 19), (6, 10), (3, 5)),
+                             loc_kind="reference", loc_sigma=0.05, seed=43),
+    "linear": dict(B=2, Q=600, M=2, D=16, K=4, levels=((9, 11), (4, 5), (2, 3)),
+                   loc_kind="uniform", loc_lo=-0.1, loc_hi=1.1, seed=44),
+    "beyond_window": dict(B=1, Q=30000, M=1, D=8, K=4, levels=((40, 40),),
+                          loc_kind="uniform", loc_lo=-0.1, loc_hi=1.1, seed=45),
+    "linear_wide_head": dict(B=1, Q=700, M=2, D=256, K=8, levels=((6, 7), (3, 4)),
+                             loc_kind="uniform", loc_lo=-0.1, loc_hi=1.1, seed=46),
+}
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+@pytest.mark.parametrize("case", list(PRE_CASES))
+def test_prereduce_cases(dtype, case):
+    """PREREDUCE against the oracle; the plan (which levels are pre-reduced)
+    is checked against the documented policy inside parity_kwargs."""
+    wl = Workload(name=case, dtype=dtype, **PRE_CASES[case])
+    inp = make_inputs(wl)
+    starts = _reorder_levels(inp, wl.levels, [2, 0, 3, 1]) if case == "pixels_reordered" else None
+    modes = plan_for(dtype, "prereduce", inp, starts)
+    assert "prereduce" in modes, modes
+    say(f"case prereduce {case} {dtype}: Q={wl.num_queries} D={wl.D} K={wl.K} plan={modes}")
+    full_check(inp, dtype, "prereduce", starts=starts)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+def test_prereduce_accumulates_and_ignores_out_of_bounds_points(dtype):
+    """PREREDUCE with MSDA_FLAG_ACCUMULATE_GRAD_VALUE adds the pre-reduced sums
+    into the existing grad_value; with every point outside its level the
+    gradients are exactly zero."""
+    wl = Workload(name="linear", dtype=dtype, **PRE_CASES["linear"])
+    inp = make_inputs(wl)
+    g = to_dev(inp)
+    say(f"case prereduce accumulate twice {dtype}")
+    args = (g["value"], g["spatial_shapes"], None, g["sampling_locations"], g["attention_weights"],
+            g["grad_output"])
+    gv1, _, _ = msda_backward(*args, accum="prereduce")
+    once = gv1.clone()
+    msda_backward(*args, grad_value=gv1, accum="prereduce", accumulate=True)
+    torch.cuda.synchronize()
+    ref = oracle.backward(inp["value"], inp["spatial_shapes"], None, inp["sampling_locations"],
+                          inp["attention_weights"], inp["grad_output"])[0]
+    kw = parity_kwargs(dtype, "prereduce", inp)
+    report(check_grad_value(dtype, to_np(once), ref, inp["spatial_shapes"], **kw))
+    report(check_grad_value(dtype, to_np(gv1), 2 * ref, inp["spatial_shapes"], passes=2, **kw))
+
+    loc = inp["sampling_locations"].float()
+    sel = torch.rand(loc.shape[:-1], generator=torch.Generator().manual_seed(2)) < 0.5
+    loc[..., 1] = torch.where(sel, torch.tensor(1.7), torch.tensor(-0.9))
+    inp["sampling_locations"] = loc.to(dtype)
+    say(f"case prereduce all points out of bounds {dtype}")
+    out, (gv, gl, ga) = gpu_run(inp, "prereduce")
+    assert torch.all(out == 0) and torch.all(gv == 0) and torch.all(gl == 0) and torch.all(ga == 0)
