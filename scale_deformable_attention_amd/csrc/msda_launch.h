@@ -87,6 +87,33 @@ __host__ __device__ inline int32_t pre_tile_span(int64_t i, int32_t side, int32_
     return i >= tiles ? n : (int32_t)((i * side * n + n0 / 2) / n0);
 }
 
+// The queries of merged tile r of pixel queries (those of the pyramid's own
+// pixels in S order): tile (ty, tx) of `side` x `side` pixels of level ref,
+// and on every level l the rows and columns pre_tile_span assigns it, level
+// by level, row-major within each. Writes their indexes to qidx (threads
+// tid, tid + nthreads, ... of the workgroup share the work) and returns
+// their count; every thread walks the same levels.
+__device__ inline int merged_tile_queries(const LevelTable &lt, int L, int ref, int side,
+                                          int64_t r, int32_t *qidx, int tid, int nthreads) {
+    const int32_t H0 = lt.H[ref], W0 = lt.W[ref];
+    const int64_t ny = (H0 + side - 1) / side, nx = (W0 + side - 1) / side;
+    const int64_t ty = r / nx, tx = r - ty * nx;
+    int n = 0;
+    for (int l = 0; l < L; ++l) {
+        const int32_t y0 = pre_tile_span(ty, side, lt.H[l], H0, ny);
+        const int32_t y1 = pre_tile_span(ty + 1, side, lt.H[l], H0, ny);
+        const int32_t x0 = pre_tile_span(tx, side, lt.W[l], W0, nx);
+        const int32_t w = pre_tile_span(tx + 1, side, lt.W[l], W0, nx) - x0;
+        const int cnt = (y1 - y0) * w;
+        for (int i = tid; i < cnt; i += nthreads) {
+            const int dy = i / w;
+            qidx[n + i] = (int32_t)(lt.start[l] + (int64_t)(y0 + dy) * lt.W[l] + x0 + (i - dy * w));
+        }
+        n += cnt;
+    }
+    return n;
+}
+
 // Dynamic LDS bytes of one pre-reduction workgroup: record weights and
 // record queries, window row starts, cursors and chunk starts, chunk pixels,
 // query indexes (4 bytes each), then the upstream-gradient rows (D + 1
@@ -143,6 +170,7 @@ struct BwdMapping {
 hipError_t launch_forward(const Problem &p, const Mapping &mp, const void *value,
                           const void *loc, const void *attn, void *out,
                           hipStream_t stream);
+
 
 // Scatter kernel: writes grad_loc / grad_attn, adds into grad_value (levels
 // with scratch_off < 0; fp32 adds for fp32 data, packed adds for 16-bit data)

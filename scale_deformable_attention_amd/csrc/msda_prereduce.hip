@@ -47,23 +47,7 @@ __device__ __forceinline__ int block_queries(const PreTiles &pt, const LevelTabl
         for (int j = tid; j < n; j += kPreBlock) qidx[j] = (int32_t)(q0 + j);
         return n;
     }
-    const int32_t H0 = lt.H[pt.ref], W0 = lt.W[pt.ref], side = pt.tile;
-    const int64_t ny = (H0 + side - 1) / side, nx = (W0 + side - 1) / side;
-    const int64_t ty = r / nx, tx = r - ty * nx;
-    int n = 0;
-    for (int l = 0; l < L; ++l) {  // uniform: every lane walks the same levels
-        const int32_t y0 = pre_tile_span(ty, side, lt.H[l], H0, ny);
-        const int32_t y1 = pre_tile_span(ty + 1, side, lt.H[l], H0, ny);
-        const int32_t x0 = pre_tile_span(tx, side, lt.W[l], W0, nx);
-        const int32_t w = pre_tile_span(tx + 1, side, lt.W[l], W0, nx) - x0;
-        const int cnt = (y1 - y0) * w;
-        for (int i = tid; i < cnt; i += kPreBlock) {
-            const int dy = i / w;
-            qidx[n + i] = (int32_t)(lt.start[l] + (int64_t)(y0 + dy) * lt.W[l] + x0 + (i - dy * w));
-        }
-        n += cnt;
-    }
-    return n;
+    return merged_tile_queries(lt, L, pt.ref, pt.tile, r, qidx, tid, kPreBlock);
 }
 
 template <class DT, class PT>
