@@ -46,7 +46,10 @@ more), and the fp32 scratch's fill, read-modify-writes and read.
 
 Prints one JSON line:
   value / ms_per_step   microseconds per forward+backward step of the headline
-                        workload (lower is better)
+                        workload (lower is better): exactly `--steps` steps
+                        replayed from HIP graphs of 10 steps each (one-step
+                        graphs for a remainder), so each replay's own launch
+                        cost is spread over 10 steps
   phases                forward and backward as wholes: algorithmic bytes / device
                         span (first kernel's start to last kernel's end, from
                         the launch-stamped events) against the 8 TB/s peak;
@@ -204,8 +207,11 @@ class ByteModel:
 
 # ------------------------------------------------------------------- timing
 
-def capture(fn):
-    """A HIP graph of one call of `fn` (after two warm calls on the capture stream)."""
+STEPS_PER_GRAPH = 10  # calls captured in one graph: amortises the replay's own launch cost
+
+
+def capture(fn, calls=1):
+    """A HIP graph of `calls` calls of `fn` (after two warm calls on the capture stream)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -215,18 +221,26 @@ def capture(fn):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        fn()
+        for _ in range(calls):
+            fn()
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
     return g
 
 
-def time_replays(g, reps):
+def time_replays(g, reps, g_many=None, many=STEPS_PER_GRAPH):
+    """Microseconds per call over exactly `reps` calls: replays of `g_many`
+    (a graph of `many` calls) while at least `many` calls remain, then of `g`
+    (one call)."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(reps):
+    left = reps
+    while g_many is not None and left >= many:
+        g_many.replay()
+        left -= many
+    for _ in range(left):
         g.replay()
     e1.record()
     torch.cuda.synchronize()
@@ -373,11 +387,13 @@ def measure(name, accum, steps, warmup, n_inst, headline=False):
         step()
     torch.cuda.synchronize()
     g_step, g_fwd, g_bwd = capture(step), capture(call.forward), capture(call.backward)
-    us_step = time_replays(g_step, steps)
+    g_steps = capture(step, STEPS_PER_GRAPH)
+    us_step = time_replays(g_step, steps, g_steps)
+    del g_steps
     fwd_graph_us = time_replays(g_fwd, steps)
     bwd_graph_us = time_replays(g_bwd, steps)
     kt, fwd_us, bwd_us = kernel_times(call, n_inst)
-    log(f"{name}: {us_step:.2f} us/step (graph replay, {steps} steps); forward {fwd_us:.2f} us, "
+    log(f"{name}: {us_step:.2f} us/step ({steps} steps, graphs of {STEPS_PER_GRAPH}); forward {fwd_us:.2f} us, "
         f"backward {bwd_us:.2f} us (device spans; alone as graph replays {fwd_graph_us:.2f} / "
         f"{bwd_graph_us:.2f} us)")
     log("kernels (us): " + ", ".join(f"{k} {v:.2f}" for k, v in kt.items()))
@@ -614,7 +630,7 @@ def main():
         "data": "synthetic (seeded; stands in for Deformable-DETR COCO inputs)",
         "config": {k: head[k] for k in ("workload", "B", "Q", "S", "M", "D", "L", "K", "levels",
                                         "accum", "param_dtype")} | {"parallelism": "single GPU"},
-        "timing": "graph replay; kernels: launch-stamped events",
+        "timing": f"graph replay, {STEPS_PER_GRAPH} steps per graph; kernels: launch-stamped events",
         "fwd_us": head["phases"]["forward"]["us"], "bwd_us": head["phases"]["backward"]["us"],
         "phases": head["phases"], "kernels": head["kernels"], "roofline": head["roofline"],
         "atomic_rate": head["atomic_rate"],

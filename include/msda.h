@@ -409,6 +409,17 @@ const char *msda_last_error(void);
  */
 int msda_release_thread_resources(void);
 
+/*
+ * Testing hook, for tests only: with enable != 0, every later call addresses
+ * the value slice with plain loads from clamped addresses, the path the
+ * library otherwise takes only for batch slices of 2 GiB or more, and plans
+ * as it does for such slices (no binned or pre-reduced accumulation, no
+ * mixed dtypes). Results are the same up to fp32 summation order. The
+ * setting is process-wide and not synchronised with calls in flight on other
+ * threads. Returns the previous setting (0 or 1); host-only, no HIP call.
+ */
+int msda_debug_force_flat_gathers(int enable);
+
 /* MSDA_ABI_VERSION of the built library. */
 int msda_abi_version(void);
 

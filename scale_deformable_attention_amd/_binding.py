@@ -47,7 +47,8 @@ EXPORTED_SYMBOLS = ("msda_forward", "msda_forward_ex", "msda_forward_point_paral
                     "msda_abi_version", "msda_set_launch_events", "msda_launch_events_recorded",
                     "msda_launch_events_name", "msda_sampling_prep",
                     "msda_sampling_prep_backward", "msda_release_thread_resources",
-                    "msda_backward_noalloc", "msda_probe_atomic_requests")
+                    "msda_backward_noalloc", "msda_probe_atomic_requests",
+                    "msda_debug_force_flat_gathers")
 
 _lib = None
 
@@ -110,6 +111,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msda_probe_atomic_requests.restype = i32
     lib.msda_release_thread_resources.argtypes = []
     lib.msda_release_thread_resources.restype = i32
+    lib.msda_debug_force_flat_gathers.argtypes = [i32]
+    lib.msda_debug_force_flat_gathers.restype = i32
     _lib = lib
     return lib
 
@@ -318,6 +321,20 @@ def probe_atomic_requests(buffer: torch.Tensor, bf16: bool, dwords_per_request: 
 def release_thread_resources() -> None:
     """Destroy this thread's side streams and events (msda_release_thread_resources)."""
     _check(load_library().msda_release_thread_resources())
+
+
+class force_flat_gathers:
+    """Context manager (tests only): within it, calls address the value slice
+    with plain loads, as for batch slices of 2 GiB or more
+    (msda_debug_force_flat_gathers); the previous setting comes back on exit."""
+
+    def __enter__(self):
+        self._prev = load_library().msda_debug_force_flat_gathers(1)
+        return self
+
+    def __exit__(self, *exc):
+        load_library().msda_debug_force_flat_gathers(self._prev)
+        return False
 
 
 def set_launch_events(events) -> None:

@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <mutex>
 #include <string>
@@ -227,6 +228,9 @@ int make_problem(int dtype, int64_t B, int64_t S, int64_t M, int64_t D, int64_t 
 
 bool aligned(const void *ptr, size_t a) { return reinterpret_cast<uintptr_t>(ptr) % a == 0; }
 
+// msda_debug_force_flat_gathers: process-wide, read at planning and launch.
+std::atomic<int> g_flat_gathers{0};
+
 int log2_ceil(int64_t x) {
     int r = 0;
     while (((int64_t)1 << r) < x) ++r;
@@ -394,7 +398,7 @@ bool plan_bins(msda::Problem *p, BinPlan *bp, bool contended_only,
     // 28-bit query field; 32-bit record indices; buffer-addressed value and
     // grad_output slices of one batch
     if (levels_overlap(*p) || p->Q >= ((int64_t)1 << 28) || 4 * P >= ((int64_t)1 << 32) ||
-        p->S * p->M * p->D * e > ((int64_t)1 << 31) - 64 ||
+        !msda::slice_fits_buffer(*p) ||
         p->Q * p->M * p->D * e > ((int64_t)1 << 31) - 64 || p->B * p->Q * p->M >= ((int64_t)1 << 31))
         return false;
     // rows per bin: a power of two, at most the 16 lane groups of the
@@ -631,7 +635,7 @@ int set_param_dtype(msda::Problem *p, int pdtype) {
         return fail(MSDA_ERR_DTYPE,
                     "param_dtype %d must equal value_dtype %d or be MSDA_F32 beside 16-bit values",
                     pdtype, p->dtype);
-    if (pdtype != p->dtype && p->S * p->M * p->D * (int64_t)elem_size(p->dtype) > ((int64_t)1 << 31) - 64)
+    if (pdtype != p->dtype && !msda::slice_fits_buffer(*p))
         return fail(MSDA_ERR_UNSUPPORTED,
                     "mixed dtypes need a value slice of one batch below 2 GiB");
     p->pdtype = pdtype;
@@ -642,6 +646,7 @@ int set_param_dtype(msda::Problem *p, int pdtype) {
 
 namespace msda {
 TimedLaunch &timed_launch() { return g_timed_launch; }
+bool flat_gathers_forced() { return g_flat_gathers.load(std::memory_order_relaxed) != 0; }
 }  // namespace msda
 
 extern "C" {
@@ -703,6 +708,10 @@ int msda_release_thread_resources(void) {
     const hipError_t err = release_side_streams();
     if (err != hipSuccess) return hip_fail(err, "releasing the side stream");
     return ok();
+}
+
+int msda_debug_force_flat_gathers(int enable) {
+    return g_flat_gathers.exchange(enable ? 1 : 0) ? 1 : 0;
 }
 
 const char *msda_status_string(int status) {

@@ -1931,11 +1931,16 @@ bool params_vectorizable(const Problem &p, int log2s, int ch, const void *loc, c
            reinterpret_cast<uintptr_t>(attn) % (e == 2 ? 8 : 16) == 0;
 }
 
-// Buffer gathers address one batch slice with 32-bit offsets.
+}  // namespace
+
+// Buffer gathers address one batch slice with 32-bit offsets (unless a test
+// forces the plain-load path, msda_debug_force_flat_gathers).
 bool slice_fits_buffer(const Problem &p) {
     const int64_t e = p.dtype == MSDA_F32 ? 4 : 2;
-    return p.S * p.M * p.D * e <= (int64_t)kOutOfRange - 64;
+    return p.S * p.M * p.D * e <= (int64_t)kOutOfRange - 64 && !flat_gathers_forced();
 }
+
+namespace {
 
 template <class DT, class PT, int VEC>
 hipError_t fwd_launch(const Problem &p, const Mapping &mp, const void *value, const void *loc,

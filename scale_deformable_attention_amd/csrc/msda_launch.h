@@ -167,6 +167,11 @@ struct BwdMapping {
     int log2_split;
 };
 
+// The value slice of one batch can be addressed by a buffer resource (32-bit
+// offsets), and no test forces plain loads (msda_debug_force_flat_gathers).
+bool slice_fits_buffer(const Problem &p);
+bool flat_gathers_forced();
+
 hipError_t launch_forward(const Problem &p, const Mapping &mp, const void *value,
                           const void *loc, const void *attn, void *out,
                           hipStream_t stream);

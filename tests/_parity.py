@@ -136,13 +136,16 @@ def binning_applies(dtype, B, S, M, D, Q, K, L, spatial_shapes, level_start_inde
 
 
 def expected_level_modes(dtype, accum, spatial_shapes, B, S, M, D, Q, K,
-                         level_start_index=None) -> list:
+                         level_start_index=None, flat=False) -> list:
     """Per-level accumulation ("native", "fp32_scratch", "binned" or
     "prereduce") that include/msda.h's policy gives for this call."""
     accum = accum_name(accum)
     L = len(torch.as_tensor(spatial_shapes).tolist())
     hot = set(contended_levels(spatial_shapes, Q, K))
-    bins = binning_applies(dtype, B, S, M, D, Q, K, L, spatial_shapes, level_start_index)
+    # flat: the plain-load path is forced (msda_debug_force_flat_gathers), which
+    # plans as for a value slice of 2 GiB or more: no binning
+    bins = not flat and binning_applies(dtype, B, S, M, D, Q, K, L, spatial_shapes,
+                                        level_start_index)
     half = dtype != torch.float32
     if accum == "prereduce":
         assert bins and D <= 256, "PREREDUCE does not apply to this problem"
@@ -164,14 +167,14 @@ def expected_level_modes(dtype, accum, spatial_shapes, B, S, M, D, Q, K,
     return ["native"] * L
 
 
-def plan_for(dtype, accum, inp, level_start_index=None, workload_name=None) -> list:
+def plan_for(dtype, accum, inp, level_start_index=None, workload_name=None, flat=False) -> list:
     """The expected per-level plan of a call on `inp`; for a named workload
     also the hard-coded table entry, which must agree."""
     v, loc = inp["value"], inp["sampling_locations"]
     B, S, M, D = v.shape
     Q, K = loc.shape[1], loc.shape[4]
     modes = expected_level_modes(dtype, accum, inp["spatial_shapes"], B, S, M, D, Q, K,
-                                 level_start_index)
+                                 level_start_index, flat)
     if workload_name is not None:
         table = WORKLOAD_PLANS[workload_name][accum_name(accum)]
         assert modes == table, (workload_name, accum, modes, table)
@@ -303,11 +306,11 @@ def check_backward(dtype, gpu, ref, spatial_shapes, level_start_index=None,
 
 
 def parity_kwargs(dtype, accum, inp, level_start_index=None, workload_name=None,
-                  check_library=True, grad_output=None) -> dict:
+                  check_library=True, grad_output=None, flat=False) -> dict:
     """check_backward's `modes` and `stats` for a call on `inp`: the expected
     plan (checked against the library's report) and, when some level is
     accumulated with 16-bit atomics, the oracle's rounding statistics."""
-    modes = plan_for(dtype, accum, inp, level_start_index, workload_name)
+    modes = plan_for(dtype, accum, inp, level_start_index, workload_name, flat)
     if check_library:
         assert_library_plan(modes, inp, accum, level_start_index)
     stats = rounding_stats(inp, level_start_index, grad_output) \

@@ -351,3 +351,39 @@ def test_noalloc_backward_rejects_before_any_hip_call(lib):
     assert nb(flags=2) == 2 and nb(flags=4) == 2
     assert nb(M=0) == 2
     assert nb(B=0) == 0
+
+
+def test_flat_gathers_hook_plans_as_for_large_slices(lib):
+    """msda_debug_force_flat_gathers (a testing hook): returns the previous
+    setting; while set, binned accumulation no longer applies (as for a batch
+    value slice of 2 GiB or more), AUTO falls back to PER_LEVEL for bf16, and
+    mixed dtypes are refused; all host-only."""
+    import sys
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from _parity import WORKLOAD_PLANS
+    from scale_deformable_attention_amd.workloads import workload
+    wl = workload("decoder_bf16")
+    L = len(wl.levels)
+    v = torch.empty((wl.B, wl.S, wl.M, wl.D), dtype=wl.dtype, device="meta")
+    loc = torch.empty((wl.B, wl.num_queries, wl.M, L, wl.K, 2), dtype=wl.dtype, device="meta")
+    attn = torch.empty((wl.B, wl.num_queries, wl.M, L, wl.K), dtype=wl.dtype, device="meta")
+    shapes = torch.tensor(wl.levels)
+    assert lib.msda_debug_force_flat_gathers(0) == 0
+    try:
+        assert lib.msda_debug_force_flat_gathers(1) == 0
+        assert bind.msda_backward_level_modes(v, shapes, None, loc, attn, "auto") == \
+            WORKLOAD_PLANS["decoder_bf16"]["per_level"]
+        for accum in ("binned", "mixed", "prereduce"):
+            with pytest.raises(bind.MSDAError) as err:
+                bind.msda_backward_level_modes(v, shapes, None, loc, attn, accum)
+            assert err.value.status == 8
+        # mixed dtypes (fp32 parameters beside bf16 values) need the buffer path
+        st = lib.msda_forward_ex(2, 0, 1, 100, 2, 8, 2, SHAPES, None, 16, 2, FAKE, FAKE, FAKE,
+                                 FAKE, None)
+        assert st == 8, lib.msda_last_error()
+        assert lib.msda_debug_force_flat_gathers(0) == 1
+    finally:
+        lib.msda_debug_force_flat_gathers(0)
+    assert bind.msda_backward_level_modes(v, shapes, None, loc, attn, "auto") == \
+        WORKLOAD_PLANS["decoder_bf16"]["auto"]

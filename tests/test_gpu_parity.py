@@ -70,8 +70,8 @@ def report(stats):
                 f"normwise={s['normwise']:.2e}{extra}")
 
 
-def full_check(inp, dtype, accum="auto", starts=None, ref=None, workload_name=None):
-    kw = parity_kwargs(dtype, accum, inp, starts, workload_name)
+def full_check(inp, dtype, accum="auto", starts=None, ref=None, workload_name=None, flat=False):
+    kw = parity_kwargs(dtype, accum, inp, starts, workload_name, flat=flat)
     out, grads = gpu_run(inp, accum, starts)
     ref_out, touched, ref_grads, trows = ref if ref is not None else oracle_run(inp, starts)
     stats = check_forward(dtype, out, ref_out, touched)
@@ -788,3 +788,20 @@ def test_prereduce_accumulates_and_ignores_out_of_bounds_points(dtype):
     say(f"case prereduce all points out of bounds {dtype}")
     out, (gv, gl, ga) = gpu_run(inp, "prereduce")
     assert torch.all(out == 0) and torch.all(gv == 0) and torch.all(gl == 0) and torch.all(ga == 0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+@pytest.mark.parametrize("accum", ["auto", "native", "fp32_scratch"])
+def test_plain_load_path_for_large_slices(dtype, accum):
+    """The gathers' fallback for batch value slices of 2 GiB or more (plain
+    loads from clamped addresses instead of a buffer resource), forced on a
+    small problem with out-of-bounds corners on every side: forward and
+    backward against the oracle, planned as for such slices (no binning)."""
+    from scale_deformable_attention_amd._binding import force_flat_gathers
+    wl, inp = _small(dtype, D=16, Q=97, K=4, levels=((6, 9), (3, 5), (2, 2)), lo=-0.2, hi=1.2,
+                     seed=81)
+    say(f"case plain-load gathers {dtype} {accum}")
+    with force_flat_gathers():
+        modes = plan_for(dtype, accum, inp, flat=True)
+        assert "binned" not in modes and "prereduce" not in modes, modes
+        full_check(inp, dtype, accum, flat=True)
