@@ -287,13 +287,14 @@ def kernel_times(call, n_inst):
 
 
 def kernel_source_hash() -> str:
+    """Hash of every source the library is built from (csrc/), by name order."""
     h = hashlib.sha256()
-    for rel in ("scale_deformable_attention_amd/csrc/msda_kernels.hip",
-                "scale_deformable_attention_amd/csrc/msda_api.cpp",
-                "scale_deformable_attention_amd/csrc/msda_launch.h",
-                "scale_deformable_attention_amd/csrc/msda_device.h"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "scale_deformable_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -1113,29 +1113,42 @@ __global__ __launch_bounds__(kBinBlock) void bin_sort_kernel(
     const int sh = shl >= 0 ? shl : 0;
     const uint32_t kbase = (uint32_t)(bm * nbbm + lt.bin_off[l]);
     const bool vc[4] = {binned && cl.v00, binned && cl.v01, binned && cl.v10, binned && cl.v11};
-    uint32_t slot[4], rank[4], rib[4];
+    uint32_t slot[4], rank[4], rib[4], key[4];
 #pragma unroll
     for (int cn = 0; cn < 4; ++cn) {
-        slot[cn] = rank[cn] = rib[cn] = 0u;
+        slot[cn] = rank[cn] = rib[cn] = key[cn] = 0u;
         if (!vc[cn]) continue;
         const int64_t rel = cl.row00 + ((cn & 2) ? W : 0) + (cn & 1) - start;
         rib[cn] = (uint32_t)(rel & ((1 << sh) - 1));
-        const uint32_t key = kbase + (uint32_t)(rel >> sh);
-        uint32_t h = (key * 2654435761u) >> (32 - kHashBits);
+        key[cn] = kbase + (uint32_t)(rel >> sh);
+    }
+    // The two corners of a pair (00-01, 10-11: neighbouring rows) mostly
+    // share a bin; then one hash access and one counter add of 2 serve both,
+    // and the second corner takes the rank after the first's.
+#pragma unroll
+    for (int cn = 0; cn < 4; ++cn) {
+        if (!vc[cn]) continue;
+        if ((cn & 1) && vc[cn - 1] && key[cn] == key[cn - 1]) {
+            slot[cn] = slot[cn - 1];
+            rank[cn] = rank[cn - 1] + 1u;
+            continue;
+        }
+        const uint32_t n = (!(cn & 1) && vc[cn + 1] && key[cn + 1] == key[cn]) ? 2u : 1u;
+        uint32_t h = (key[cn] * 2654435761u) >> (32 - kHashBits);
         // linear probing; at most 4 * kBinBlock keys per workgroup, so an empty
         // slot always exists and the loop ends
         while (true) {
-            const uint32_t prev = atomicCAS(&keys[h], kEmptyKey, key);
+            const uint32_t prev = atomicCAS(&keys[h], kEmptyKey, key[cn]);
             if (prev == kEmptyKey) {
                 used[atomicAdd(&nused, 1u)] = (uint16_t)h;
                 break;
             }
-            if (prev == key) break;
+            if (prev == key[cn]) break;
             h = (h + 1) & (kHashSlots - 1);
         }
         slot[cn] = h;
-        if constexpr (PLACE) rank[cn] = atomicAdd(&cnt[h], 1u);
-        else atomicAdd(&cnt[h], 1u);
+        if constexpr (PLACE) rank[cn] = atomicAdd(&cnt[h], n);
+        else atomicAdd(&cnt[h], n);
     }
     __syncthreads();
     const uint32_t nu = nused;
