@@ -166,8 +166,10 @@ class ByteModel:
         sh = {  # algorithmic share of each kernel
             "msda_fwd_kernel": self.fwd,
             "msda_grad_kernel": grad,
-            "msda_bwd_kernel": grad + U_a * D * e + U_s * D * e,
-            "msda_scatter_kernel": U_a * D * e + U_s * D * e,
+            # (rows of fp32-scratch levels: their grad_value write is the
+            # scratch add's; the atomics into the scratch are overhead)
+            "msda_bwd_kernel": grad + U_a * D * e,
+            "msda_scatter_kernel": U_a * D * e,
             "zero_fill": (N_a - U_a * D) * e,
             "bin_accum_kernel": N_b * e,
             "scratch_add_kernel": N_s * e,
