@@ -723,6 +723,30 @@ def test_pixel_queries_in_column_groups(dtype, reordered):
         full_check(inp, dtype, accum, starts=starts)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("K", [2, 4])
+def test_pixel_query_points_sharing_pixels(dtype, K):
+    """Pixel queries whose K points lie within a fraction of a pixel of one
+    another on the coarse levels, so two, three or all K of one query's points
+    put a corner on the same pixel; the binned chain's count and place merge
+    such corners into one record. A tenth of the points is pushed outside
+    its level (some corners or all of them out of bounds). grad_value must
+    match the oracle exactly as without merging."""
+    levels = ((30, 44), (15, 22), (8, 11), (4, 6))
+    wl = Workload(name="shared", dtype=dtype, B=2, Q=None, M=2, D=16, K=K, levels=levels,
+                  loc_kind="reference", loc_sigma=0.01, seed=41)
+    inp = make_inputs(wl)
+    loc = inp["sampling_locations"]
+    far = torch.rand(loc.shape[:-1], generator=torch.Generator().manual_seed(7)) < 0.1
+    loc[far] = (loc[far].float() * 1.6 - 0.3).to(loc.dtype)
+    say(f"case pixel queries sharing pixels K={K} {dtype}")
+    names, grads = _backward_launch_names(inp, "binned")
+    assert "bin_count" in names and "bin_place" in names, names  # the chain that merges
+    _, _, ref_grads, trows = oracle_run(inp)
+    check_backward(dtype, grads, ref_grads, inp["spatial_shapes"], None, trows,
+                   **parity_kwargs(dtype, "binned", inp))
+
+
 # Levels above 256 contributions per pixel, summed by PREREDUCE's in-LDS sort:
 # pixel queries (merged tiles; levels stored out of order; a wide head whose
 # tiles shrink to fit LDS), consecutive-query blocks, a level larger than the
