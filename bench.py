@@ -35,8 +35,10 @@ reported apart as `overhead_bytes`
 (modelled, not measured): the zero fill's rows that atomics or bins later
 overwrite, the read of each atomically updated row (U_a*D*e_acc, e_acc = 4
 for fp32 rows), the scatter kernel's second read of parameters and upstream
-gradient, bin records (8 bytes per in-bounds corner of a binned level,
-written by the place / sort step and read by the accumulation), the count
+gradient, bin records (8 bytes per in-bounds corner of a binned level, or
+per distinct (query, pixel) where the library merges a query's corners on
+one pixel, for pixel queries with K = 2 or 4; written by the place / sort
+step and read by the accumulation), the count
 and sort steps' parameter reads, the accumulation's reads of upstream
 gradient rows, the pre-reduction's reads of its levels' parameters (the
 locations three times: window placement, count, place; the weights once) and
@@ -132,6 +134,37 @@ def touched_rows_per_level(inp):
     return out
 
 
+def merged_records_per_level(inp):
+    """Per level: the bin records when the corners of one query's points
+    that fall on one pixel share a record, i.e. the distinct (b, q, m, pixel)
+    among the in-bounds corners. A corner (cx, cy) of point k is at
+    (x0_k + cx, y0_k + cy); it repeats a corner of an earlier point k' of the
+    same (b, q, m) exactly when cx + x0_k - x0_k' and cy + y0_k - y0_k' are
+    both 0 or 1."""
+    loc_t = inp["sampling_locations"]
+    B, Q, M, L, K, _ = loc_t.shape
+    out = []
+    for l, (H, W) in enumerate(inp["spatial_shapes"].tolist()):
+        n = 0
+        for b in range(B):
+            lxy = loc_t[b, :, :, l].to(torch.float64).numpy()  # (Q, M, K, 2)
+            x0 = np.floor((lxy[..., 0] * W - 0.5).astype(np.float32)).astype(np.int64)
+            y0 = np.floor((lxy[..., 1] * H - 0.5).astype(np.float32)).astype(np.int64)
+            del lxy
+            for k in range(K):
+                for cy in (0, 1):
+                    for cx in (0, 1):
+                        xx, yy = x0[..., k] + cx, y0[..., k] + cy
+                        keep = (xx >= 0) & (xx < W) & (yy >= 0) & (yy < H)
+                        for k2 in range(k):
+                            px = cx + x0[..., k] - x0[..., k2]
+                            py = cy + y0[..., k] - y0[..., k2]
+                            keep &= ~((px >= 0) & (px <= 1) & (py >= 0) & (py <= 1))
+                        n += int(keep.sum())
+        out.append(n)
+    return out
+
+
 class ByteModel:
     """Algorithmic bytes of one forward and one backward call, their split
     over the kernels, and the modelled overhead traffic (module docstring)."""
@@ -152,7 +185,16 @@ class ByteModel:
         U_a = sum(per[l][0] for l in atomic)
         U_s = sum(per[l][0] for l in scratch)
         C_b = sum(per[l][1] for l in binned)
-        log(f"byte model: U={self.U} rows, C={self.C} corners, {time.perf_counter() - t0:.1f} s")
+        # records of the binned levels: one per in-bounds corner, or one per
+        # distinct (query, pixel) where the library merges (pixel queries,
+        # K = 2 or 4, sorted by the count / place chain: above 2048 points
+        # per (b, m, level); the one-launch local sort below that keeps all)
+        if wl.Q is None and K in (2, 4) and Q * K > 2048 and binned:
+            merged = merged_records_per_level(inp)
+            C_b = sum(merged[l] for l in binned)
+        self.records = C_b
+        log(f"byte model: U={self.U} rows, C={self.C} corners, {C_b} binned records, "
+            f"{time.perf_counter() - t0:.1f} s")
         U_p = sum(per[l][0] for l in prered)
         rows = lambda lv: sum(B * wl.levels[l][0] * wl.levels[l][1] * M for l in lv)
         N_a, N_s, N_b = rows(atomic) * D, rows(scratch + prered) * D, rows(binned) * D

@@ -124,3 +124,36 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "--gpus must be 1" in r.stdout
+
+
+def brute_records(inp):
+    """Distinct (b, q, m, pixel) among the in-bounds corners, per level."""
+    loc = inp["sampling_locations"].to(torch.float64).numpy()
+    B, Q, M, L, K, _ = loc.shape
+    out = []
+    for l, (H, W) in enumerate(inp["spatial_shapes"].tolist()):
+        seen = set()
+        for b in range(B):
+            for q in range(Q):
+                for m in range(M):
+                    for k in range(K):
+                        x = int(np.floor(np.float32(loc[b, q, m, l, k, 0] * W - 0.5)))
+                        y = int(np.floor(np.float32(loc[b, q, m, l, k, 1] * H - 0.5)))
+                        for dy in (0, 1):
+                            for dx in (0, 1):
+                                if 0 <= x + dx < W and 0 <= y + dy < H:
+                                    seen.add((b, q, m, (y + dy) * W + x + dx))
+        out.append(len(seen))
+    return out
+
+
+def test_merged_records_match_brute_force():
+    """Pixel queries sampling within a pixel of their own position: many
+    points of one query share pixels (and some lie outside the level)."""
+    wl = Workload(name="host_px", dtype=torch.float32, B=2, Q=None, M=2, D=8, K=4,
+                  levels=((6, 9), (3, 4)), loc_kind="reference", loc_sigma=0.08, seed=3)
+    inp = make_inputs(wl)
+    got = bench.merged_records_per_level(inp)
+    assert got == brute_records(inp)
+    counts = brute_counts(inp)
+    assert all(r < c for r, (_, c) in zip(got, counts))  # merging happened on every level
