@@ -177,6 +177,40 @@ __device__ __forceinline__ void raw_to_f32(const R &r, float (&out)[N]) {
     for (int i = 0; i < N; ++i) out[i] = to_f32(DT{}, e[i]);
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + sum over the N channels a lane holds of g[i] * v[i], with `graw` /
+// `vraw` the raw channels and `g` the upstream gradient in fp32. 16-bit data
+// with whole channel pairs uses the two-channel dot-product instructions
+// (v_dot2c_f32_f16 / _bf16: no conversions, products exact in fp32); other
+// data converts and multiply-adds.
+template <class DT, int N, class R>
+__device__ __forceinline__ float lane_dot(const R &graw, const float (&g)[N], const R &vraw,
+                                          float acc) {
+    if constexpr (sizeof(typename DT::S) == 2 && N % 2 == 0) {
+        uint32_t gw[N / 2], vw[N / 2];
+        __builtin_memcpy(gw, &graw, sizeof(R));
+        __builtin_memcpy(vw, &vraw, sizeof(R));
+#pragma unroll
+        for (int p = 0; p < N / 2; ++p) {
+            if constexpr (std::is_same<DT, F16T>::value)
+                acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, gw[p]),
+                                             __builtin_bit_cast(f16x2_t, vw[p]), acc, false);
+            else
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, gw[p]),
+                                                      __builtin_bit_cast(bf16x2_t, vw[p]), acc,
+                                                      false);
+        }
+    } else {
+        float v[N];
+        raw_to_f32<DT, N>(vraw, v);
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc = __builtin_fmaf(g[i], v[i], acc);
+    }
+    return acc;
+}
+
 // ------------------------------------------------------- cross-lane sums
 
 template <int CTRL>
@@ -202,9 +236,6 @@ __device__ __forceinline__ float group_sum(float v, int log2g) {
 
 // -------------------------------------------------------------- atomics
 
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ void atomic_add_pk(F16T, uint16_t *p, float a, float b) {
     f16x2_t v;
     v.x = (_Float16)a;
@@ -219,6 +250,20 @@ __device__ __forceinline__ void atomic_add_pk(BF16T, uint16_t *p, float a, float
 }
 
 // ------------------------------------------------------------ utilities
+
+// A point's contributions to grad_attn (before A) and to grad_loc (before
+// A * W, A * H) from the dot products d[cn] of its corner rows 00, 01, 10, 11
+// with the upstream gradient: the bilinear sample and the sample's slopes
+// along x and y (course page "5. The backward kernel", section "What the
+// backward pass must produce", items 1 and 2).
+__device__ __forceinline__ void point_sums(const float (&d)[4], float fx, float fy, float &ds,
+                                           float &dx, float &dy) {
+    const float gx = 1.0f - fx, gy = 1.0f - fy;
+    ds = gx * gy * d[0] + fx * gy * d[1] + gx * fy * d[2] + fx * fy * d[3];
+    dx = gy * (d[1] - d[0]) + fy * (d[3] - d[2]);
+    dy = gx * (d[2] - d[0]) + fx * (d[3] - d[1]);
+}
+
 
 // Order of the query tiles of the forward and gradient kernels.
 //
@@ -578,9 +623,11 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
     const Slice<BUF> slice(value + b * S * MD, S * row_bytes);
     const int64_t lane_bytes = ((int64_t)m * D + (c0 < D ? c0 : 0)) * (int64_t)sizeof(E);
     float g[VEC];
+    R graw;
     {
         const R r = *reinterpret_cast<const R *>(grad_out + pq * D + (c0 < D ? c0 : 0));
-        raw_to_f32<DT, VEC>(live ? r : zero_raw<R>(), g);
+        graw = live ? r : zero_raw<R>();
+        raw_to_f32<DT, VEC>(graw, g);
     }
 
     // chunk k's parameters live in lane k of the group (at most G chunks)
@@ -649,23 +696,13 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
         float ds[CH], dx[CH], dy[CH];
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
-            float v00[VEC], v01[VEC], v10[VEC], v11[VEC];
-            raw_to_f32<DT, VEC>(raw[t][0], v00);
-            raw_to_f32<DT, VEC>(raw[t][1], v01);
-            raw_to_f32<DT, VEC>(raw[t][2], v10);
-            raw_to_f32<DT, VEC>(raw[t][3], v11);
-            const float gx = 1.0f - fx[t], gy = 1.0f - fy[t];
-            const float w00 = gx * gy, w01 = fx[t] * gy, w10 = gx * fy[t], w11 = fx[t] * fy[t];
-            ds[t] = dx[t] = dy[t] = 0.0f;
+            // The sample and its two slopes are linear in the corner rows, so
+            // their dot products with the upstream gradient follow from the
+            // four rows' own dot products.
+            float d[4];
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                const float smp = w00 * v00[i] + w01 * v01[i] + w10 * v10[i] + w11 * v11[i];
-                const float sx = gy * (v01[i] - v00[i]) + fy[t] * (v11[i] - v10[i]);
-                const float sy = gx * (v10[i] - v00[i]) + fx[t] * (v11[i] - v01[i]);
-                ds[t] += g[i] * smp;
-                dx[t] += g[i] * sx;
-                dy[t] += g[i] * sy;
-            }
+            for (int cn = 0; cn < 4; ++cn) d[cn] = lane_dot<DT, VEC>(graw, g, raw[t][cn], 0.0f);
+            point_sums(d, fx[t], fy[t], ds[t], dx[t], dy[t]);
         }
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
@@ -779,9 +816,10 @@ __device__ __forceinline__ void scatter_point(const Cell &cl, float aw, const Le
 // The query's upstream gradient in slot layout (g, slot c + jG) and, for fp32
 // targets, in channel layout (gc, channel c + iG).
 template <class DT, int SLOT, int J>
-__device__ __forceinline__ void load_upstream(const typename DT::S *grad_out, int64_t pq, int D,
-                                              int c, int G, bool q_ok, bool (&slot_ok)[J],
-                                              float (&g)[J][SLOT], float (&gc)[J * SLOT]) {
+__device__ __forceinline__ void load_upstream(
+    const typename DT::S *grad_out, int64_t pq, int D, int c, int G, bool q_ok, bool (&slot_ok)[J],
+    float (&g)[J][SLOT], float (&gc)[J * SLOT],
+    typename RawVec<SLOT * (int)sizeof(typename DT::S)>::type (&graw)[J]) {
     using R = typename RawVec<SLOT * (int)sizeof(typename DT::S)>::type;
     const int nslots = D / SLOT;
 #pragma unroll
@@ -789,7 +827,8 @@ __device__ __forceinline__ void load_upstream(const typename DT::S *grad_out, in
         const int sl = c + j * G;
         slot_ok[j] = q_ok && sl < nslots;
         const R r = *reinterpret_cast<const R *>(grad_out + pq * D + (sl < nslots ? sl : 0) * SLOT);
-        raw_to_f32<DT, SLOT>(slot_ok[j] ? r : zero_raw<R>(), g[j]);
+        graw[j] = slot_ok[j] ? r : zero_raw<R>();
+        raw_to_f32<DT, SLOT>(graw[j], g[j]);
     }
     if constexpr (SLOT == 1) {
 #pragma unroll
@@ -852,7 +891,8 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
 
     bool slot_ok[J];
     float g[J][SLOT], gc[JC];
-    load_upstream<DT, SLOT, J>(grad_out, pq, D, c, G, q_ok, slot_ok, g, gc);
+    R graw[J];
+    load_upstream<DT, SLOT, J>(grad_out, pq, D, c, G, q_ok, slot_ok, g, gc, graw);
 
     for (int i0 = 0; i0 < per_lane; i0 += CH) {
         float lx[CH], ly[CH], aw[CH];
@@ -890,26 +930,13 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(
         float ds[CH], dx[CH], dy[CH];
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
-            const float fx = cl[t].fx, fy = cl[t].fy, gx = 1.0f - fx, gy = 1.0f - fy;
-            const float w00 = gx * gy, w01 = fx * gy, w10 = gx * fy, w11 = fx * fy;
-            ds[t] = dx[t] = dy[t] = 0.0f;
+            // the four corner rows' dot products with the upstream gradient
+            float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                float a00[SLOT], a01[SLOT], a10[SLOT], a11[SLOT];
-                raw_to_f32<DT, SLOT>(raw[t][0][j], a00);
-                raw_to_f32<DT, SLOT>(raw[t][1][j], a01);
-                raw_to_f32<DT, SLOT>(raw[t][2][j], a10);
-                raw_to_f32<DT, SLOT>(raw[t][3][j], a11);
+            for (int j = 0; j < J; ++j)
 #pragma unroll
-                for (int u = 0; u < SLOT; ++u) {
-                    const float smp = w00 * a00[u] + w01 * a01[u] + w10 * a10[u] + w11 * a11[u];
-                    const float sx = gy * (a01[u] - a00[u]) + fy * (a11[u] - a10[u]);
-                    const float sy = gx * (a10[u] - a00[u]) + fx * (a11[u] - a01[u]);
-                    ds[t] += g[j][u] * smp;
-                    dx[t] += g[j][u] * sx;
-                    dy[t] += g[j][u] * sy;
-                }
-            }
+                for (int cn = 0; cn < 4; ++cn) d[cn] = lane_dot<DT, SLOT>(graw[j], g[j], raw[t][cn][j], d[cn]);
+            point_sums(d, cl[t].fx, cl[t].fy, ds[t], dx[t], dy[t]);
         }
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
@@ -991,7 +1018,8 @@ __device__ __forceinline__ void scatter_tile(MSDA_SCATTER_PARAMS, const int64_t 
     const int64_t bS = b * S;
     bool slot_ok[J];
     float g[J][SLOT], gc[JC];
-    load_upstream<DT, SLOT, J>(grad_out, pq, D, c, G, q_ok, slot_ok, g, gc);
+    typename RawVec<SLOT * (int)sizeof(typename DT::S)>::type graw[J];  // unused here
+    load_upstream<DT, SLOT, J>(grad_out, pq, D, c, G, q_ok, slot_ok, g, gc, graw);
     for (int l = 0; l < L; ++l) {
         // binned or pre-reduced: summed by their own kernels
         if (lt.bin_shift[l] >= 0 || ((lt.prered >> l) & 1u)) continue;
