@@ -1598,10 +1598,10 @@ __global__ __launch_bounds__(kScanBlock) void bin_tile_scan_kernel(uint32_t *__r
 //
 // Records come in rounds of kAccRPT * kBlock, kAccRPT per thread (the next
 // round's loads are issued before the current round is processed), and each
-// round is counting-sorted by slot in LDS: four ballots on the slot bits per
-// record index give every record its rank among the wave's records of the
-// same slot, 16 lanes per wave publish the wave's per-slot counts, one wave
-// scans the 64 counts, and the records are written in slot order. Two
+// round is counting-sorted by slot in LDS: a returning add on the wave's own
+// counter of the slot gives every record its rank among the wave's records of
+// the same slot, one wave scans the 64 counters (and clears them for the
+// next round), and the records are written in slot order. Two
 // records per thread halve the rounds, and with them the barriers and the
 // scan, per record; the sums per slot grow to twice the length. A group then reads its slot's records
 // contiguously, U at a time, with all their upstream-gradient loads (32-bit
@@ -1690,6 +1690,9 @@ __device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const 
         const uint32_t i = rb + k * kBlock + tid;
         next[k] = rb < re ? records[i < re ? i : re - 1] : make_uint2(0u, 0u);
     }
+    static_assert(kAccGroups * kWaves == 64, "one counter per lane of wave 0");
+    if (tid < 64) wcount[tid] = 0u;
+    __syncthreads();
     for (uint32_t base = rb; base < re; base += kAccRPT * kBlock) {
         uint2 rec[kAccRPT];
         bool valid[kAccRPT];
@@ -1705,41 +1708,17 @@ __device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const 
             rr = rr < (uint32_t)rows ? rr : 0u;  // keeps every access in range
             slot[k] = (rr << log2rep) | (i & ((1u << log2rep) - 1u));
         }
-        // lanes of this wave holding a record of the same slot, per record
-        // index k; records k' < k of a slot come first in the slot's run
-        uint64_t vb[kAccRPT], sb[kAccRPT][4];
-#pragma unroll
-        for (int k = 0; k < kAccRPT; ++k) {
-            vb[k] = __ballot(valid[k]);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) sb[k][t] = __ballot((slot[k] >> t) & 1u);
-        }
-        auto same = [&](int k, uint32_t sl) {
-            uint64_t mk = vb[k];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) mk &= ((sl >> t) & 1u) ? sb[k][t] : ~sb[k][t];
-            return mk;
-        };
+        // each record's rank among this wave's records of its slot: a
+        // returning add on the wave's own counter of the slot (record index
+        // k = 0 first, so records k' < k of a slot come first in its run)
         uint32_t rank[kAccRPT];
 #pragma unroll
-        for (int k = 0; k < kAccRPT; ++k) {
-            const uint64_t mine = same(k, slot[k]);
-            uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(mine >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mine, 0u));
-#pragma unroll
-            for (int k2 = 0; k2 < k; ++k2) r += (uint32_t)__popcll(same(k2, slot[k]));
-            rank[k] = r;
-        }
-        __syncthreads();  // the previous round's sorted records and offsets consumed
-        if (lane < kAccGroups) {
-            uint32_t cnt = 0;
-#pragma unroll
-            for (int k = 0; k < kAccRPT; ++k) cnt += (uint32_t)__popcll(same(k, (uint32_t)lane));
-            wcount[lane * kWaves + wave] = cnt;
-        }
-        __syncthreads();
-        if (wave == 0) {  // exclusive scan of the 64 counts, slot-major
+        for (int k = 0; k < kAccRPT; ++k)
+            rank[k] = valid[k] ? atomicAdd(&wcount[slot[k] * kWaves + wave], 1u) : 0u;
+        __syncthreads();  // every wave's counts in; the previous round's records and offsets consumed
+        if (wave == 0) {  // exclusive scan of the 64 counts, slot-major; counts cleared for the next round
             const uint32_t x = wcount[lane];
+            wcount[lane] = 0u;
             uint32_t inc = x;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
