@@ -219,6 +219,7 @@ class ByteModel:
         sh["scatter_accum_kernel"] = sh["msda_scatter_kernel"] + sh["bin_accum_kernel"]
         sh["grad_sort_kernel"] = grad + sh["zero_fill"]
         rec = 8 * C_b
+        nt = -(-nbins // 4096)  # scan tiles of 4096 counts
         ov = {  # modelled traffic beyond the share
             "zero_fill": N * e - sh["zero_fill"],
             "msda_bwd_kernel": U_a * D * e_acc + 2 * U_s * D * 4,
@@ -226,7 +227,7 @@ class ByteModel:
             "scratch_zero": N_s * 4, "scratch_add_kernel": N_s * 4,
             "bin_zero": (nbins + 1) * 4, "bin_count": 2 * P_b * pe,
             "bin_scan": 3 * nbins * 4, "bin_tile_sum": nbins * 4,
-            "bin_tile_offsets": 3 * (-(-nbins // 4096)) * 4, "bin_tile_scan": 3 * nbins * 4,
+            "bin_tile_scan": 3 * nbins * 4 + 2 * nt * (nt - 1),  # + the earlier tiles' totals
             "bin_place": 3 * P_b * pe + rec,
             "bin_local_sort": 3 * P_b * pe + rec + 8 * nbins,
             "bin_accum_kernel": rec + go,

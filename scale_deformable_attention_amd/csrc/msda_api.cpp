@@ -1033,8 +1033,6 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
                                  hipSuccess
                            : ((err = marked(msda::launch_bin_tile_sums(bins, before(t)), t,
                                             "bin_tile_sum")) != hipSuccess ||
-                              (err = marked(msda::launch_bin_tile_offsets(bins, before(t)), t,
-                                            "bin_tile_offsets")) != hipSuccess ||
                               (err = marked(msda::launch_bin_tile_scan(bins, before(t)), t,
                                             "bin_tile_scan")) != hipSuccess)) {
                 what = "bin scan launch";

@@ -1556,17 +1556,29 @@ __global__ __launch_bounds__(kScanBlock) void bin_tile_sum_kernel(const uint32_t
 
 // starts[0:nb] (counts) -> exclusive starts, cursor = starts; toff = the
 // exclusive scan of the tile totals (toff[ntiles] = total -> starts[nb]).
+// Every tile's exclusive scan plus its offset, the sum of the earlier tiles'
+// totals (`tsum`, from bin_tile_sum_kernel), which wave 0 adds up itself:
+// there are few tiles (4096 counts each), so no separate scan of the totals
+// is launched. The last tile also writes starts[nb], the total.
 __global__ __launch_bounds__(kScanBlock) void bin_tile_scan_kernel(uint32_t *__restrict__ starts,
                                                                   uint32_t *__restrict__ cursor,
-                                                                  const uint32_t *__restrict__ toff,
+                                                                  const uint32_t *__restrict__ tsum,
                                                                   const int64_t nb) {
     constexpr int kWaves = kScanBlock / 64;
     __shared__ uint32_t wsum[kWaves];
+    __shared__ uint32_t tile_before;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t i0 = (int64_t)blockIdx.x * kScanTile + 4 * (int64_t)tid;
     uint32_t c[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) c[k] = i0 + k < nb ? starts[i0 + k] : 0u;
+    if (wv == 0) {
+        uint32_t t = 0;
+        for (uint32_t j = lane; j < blockIdx.x; j += 64) t += tsum[j];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+        if (lane == 0) tile_before = t;
+    }
     const uint32_t s3 = c[0] + c[1] + c[2] + c[3];
     uint32_t x = s3;  // inclusive scan over the wave
 #pragma unroll
@@ -1576,7 +1588,7 @@ __global__ __launch_bounds__(kScanBlock) void bin_tile_scan_kernel(uint32_t *__r
     }
     if (lane == 63) wsum[wv] = x;
     __syncthreads();
-    uint32_t before = toff[blockIdx.x];
+    uint32_t before = tile_before;
     for (int i = 0; i < wv; ++i) before += wsum[i];
     uint32_t o = before + x - s3;
 #pragma unroll
@@ -1587,7 +1599,7 @@ __global__ __launch_bounds__(kScanBlock) void bin_tile_scan_kernel(uint32_t *__r
         }
         o += c[k];
     }
-    if (blockIdx.x == gridDim.x - 1 && tid == 0) starts[nb] = toff[gridDim.x];
+    if (blockIdx.x == gridDim.x - 1 && tid == kScanBlock - 1) starts[nb] = o;
 }
 
 // One workgroup per bin, no atomics. The workgroup has kAccGroups lane
@@ -2565,14 +2577,6 @@ hipError_t launch_bin_tile_sums(const BinnedBuffers &bins, hipStream_t stream) {
     if (nt < 1 || nt >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     MSDA_LAUNCH(bin_tile_sum_kernel, dim3((unsigned)nt), dim3(kScanBlock), 0, stream,
                        bins.starts, bins.tile_offsets, bins.nbins);
-    return hipGetLastError();
-}
-
-hipError_t launch_bin_tile_offsets(const BinnedBuffers &bins, hipStream_t stream) {
-    // the single-workgroup scan over the ntiles totals (toff[ntiles] = total)
-    const int64_t nt = scan_tiles(bins.nbins);  // (the cursor copy goes past the offsets)
-    MSDA_LAUNCH(bin_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, bins.tile_offsets,
-                       bins.tile_offsets + nt + 1, nt);
     return hipGetLastError();
 }
 

@@ -141,7 +141,7 @@ struct BinnedBuffers {
     uint32_t *starts;
     uint32_t *cursor;
     const uint32_t *ends;  // bin i's records are [starts[i], ends[i])
-    uint32_t *tile_offsets;  // 2 * (scan_tiles(nbins) + 1): tile totals / offsets of the scan
+    uint32_t *tile_offsets;  // scan_tiles(nbins) tile totals of the scan (2 * (scan_tiles + 1) reserved)
     uint2 *records;
     int64_t nbins;
 };
@@ -195,11 +195,10 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
 hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
                            const BinnedBuffers &bins, bool place, hipStream_t stream);
 hipError_t launch_bin_scan(const BinnedBuffers &bins, hipStream_t stream);
-// The same scan in three launches over tiles of 4096 counts (tile totals,
-// their scan, every tile's scan plus its offset), for large bin counts.
+// The same scan in two launches over tiles of 4096 counts (tile totals;
+// every tile's scan plus the sum of the earlier totals), for large bin counts.
 int64_t scan_tiles(int64_t nbins);
 hipError_t launch_bin_tile_sums(const BinnedBuffers &bins, hipStream_t stream);
-hipError_t launch_bin_tile_offsets(const BinnedBuffers &bins, hipStream_t stream);
 hipError_t launch_bin_tile_scan(const BinnedBuffers &bins, hipStream_t stream);
 // launch_gradients, launch_bin_local_sort and the zero fill as one launch
 // (16-bit data, Q * K <= 2048, every binned level at most kMaxFusedSortBins
