@@ -1875,8 +1875,13 @@ __global__ __launch_bounds__(kBlock) void bin_accum_kernel(
 // the accumulation's latency-bound rounds fill the gaps of the scatter's
 // atomic-bound stream. Workgroups come in rows of 8 (one per XCD); of the
 // R = gridDim / 8 rows, Rs = nsc / 8 scatter and the others accumulate,
-// spread evenly over the grid so both run from the start; within each role
-// the XCD-aware order is that of its own kernel (nsc is a multiple of 8).
+// spread evenly over the grid so both run from the start. The accumulation
+// keeps its own kernel's XCD-aware order (neighbouring bins on one XCD);
+// scatter tiles are dealt to the XCDs in turn, so every XCD's atomics cover
+// all heads and batches rather than a block of 4 heads of one batch, whose
+// rows would fill only half of each pixel's 8 heads' rows (measured:
+// scatter launch 21.7-22.3 -> 21.4-21.8 us on the decoder; nsc is a multiple
+// of 8).
 template <class DT, class PT, int SLOT, int J, int V, bool WIDE>
 __global__ __launch_bounds__(kBlock) void scatter_accum_kernel(
     const typename PT::S *__restrict__ loc, const typename PT::S *__restrict__ attn,
@@ -1891,7 +1896,7 @@ __global__ __launch_bounds__(kBlock) void scatter_accum_kernel(
     const int64_t r = bx / kXcds, R = gridDim.x / kXcds, Rs = nsc / kXcds;
     const int64_t k = r * Rs / R;  // scatter rows before row r
     if ((r + 1) * Rs / R > k) {    // row r is scatter row k
-        const int64_t tile = (int64_t)xcd * Rs + k;
+        const int64_t tile = k * kXcds + xcd;
         if (tile < ntiles) {
             float *workspace = nullptr;
             scatter_tile<DT, PT, SLOT, J>(MSDA_SCATTER_ARGS, tile);
