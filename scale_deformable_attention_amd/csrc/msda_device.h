@@ -217,5 +217,39 @@ __device__ __forceinline__ void chunk_params(const ChunkParams<PT, CH> &own, int
     }
 }
 
+// Point k (< CH) of the chunk owned by lane `src`, unpacked: the chunk's
+// dwords are shuffled as in chunk_params and point k's are kept.
+template <class PT, int CH>
+__device__ __forceinline__ void point_params(const ChunkParams<PT, CH> &own, int src, int k,
+                                             float &x, float &y, float &a) {
+    using C = ChunkParams<PT, CH>;
+    uint32_t lw[C::kLocW], aw_[C::kAttW];
+#pragma unroll
+    for (int w = 0; w < C::kLocW; ++w) lw[w] = (uint32_t)__shfl((int)own.loc[w], src, 64);
+#pragma unroll
+    for (int w = 0; w < C::kAttW; ++w) aw_[w] = (uint32_t)__shfl((int)own.att[w], src, 64);
+    if constexpr (C::kE == 2) {
+        uint32_t l = lw[0], at = aw_[0];
+#pragma unroll
+        for (int t = 1; t < CH; ++t) l = k == t ? lw[t] : l;
+#pragma unroll
+        for (int w = 1; w < C::kAttW; ++w) at = (k >> 1) == w ? aw_[w] : at;
+        x = bits_to_f32<PT>(l & 0xFFFFu);
+        y = bits_to_f32<PT>(l >> 16);
+        a = bits_to_f32<PT>((at >> (16 * (k & 1))) & 0xFFFFu);
+    } else {
+        uint32_t lx = lw[0], ly = lw[1], at = aw_[0];
+#pragma unroll
+        for (int t = 1; t < CH; ++t) {
+            lx = k == t ? lw[2 * t] : lx;
+            ly = k == t ? lw[2 * t + 1] : ly;
+            at = k == t ? aw_[t] : at;
+        }
+        x = __uint_as_float(lx);
+        y = __uint_as_float(ly);
+        a = __uint_as_float(at);
+    }
+}
+
 }  // namespace
 }  // namespace msda

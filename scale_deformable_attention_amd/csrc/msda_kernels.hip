@@ -234,6 +234,16 @@ __device__ __forceinline__ float group_sum(float v, int log2g) {
     return v;
 }
 
+// Lane t's value in every lane of its quad (DPP quad_perm [t, t, t, t]).
+template <int T>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, T * 0x55, 0xF, 0xF, true);
+}
+template <int T>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __uint_as_float(quad_bcast<T>(__float_as_uint(v)));
+}
+
 // -------------------------------------------------------------- atomics
 
 __device__ __forceinline__ void atomic_add_pk(F16T, uint16_t *p, float a, float b) {
@@ -370,7 +380,7 @@ __host__ __device__ inline int fwd_heads(int M, int slots, int row_bytes) {
     return row_bytes <= 64 ? grad_heads(M, slots) : 1;
 }
 
-template <class DT, class PT, int VEC, int CH, bool BUF>
+template <class DT, class PT, int VEC, int CH, bool BUF, bool QUAD>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void msda_fwd_kernel(
     const typename DT::S *__restrict__ value, const typename PT::S *__restrict__ loc,
     const typename PT::S *__restrict__ attn, typename DT::S *__restrict__ out,
@@ -418,7 +428,51 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     if (owned) own_chunk_params<PT, CH>(loc_q, attn_q, c, per_lane, split, s, pvec, own);
     const int group_base = (tid & 63) & ~((1 << log2g) - 1);
 
+    // QUAD (4-lane groups that hold exactly D channels, chunks inside one
+    // level, parameters owned, buffer gathers; chosen on the host): lane k of
+    // a group works out point k of the chunk (cell, weights, corner offsets,
+    // out-of-range for out-of-bounds corners) and the quad broadcasts each
+    // point's 8 values, instead of every lane working out all CH points (the
+    // same arithmetic, so the same results).
+    static_assert(!QUAD || (BUF && CH == 4), "quad setup: buffer gathers, 4-point chunks");
+    // QUAD: 32-bit offsets, kOutOfRange for out-of-bounds corners (ok unused)
+    using Off = typename std::conditional<QUAD, uint32_t, int64_t>::type;
     for (int i0 = 0; i0 < per_lane; i0 += CH) {
+        Off off[CH][4];
+        bool ok[CH][4];
+        float w[CH][4];
+        if constexpr (QUAD) {
+            float px, py, pa;
+            point_params<PT, CH>(own, group_base + i0 / CH, c, px, py, pa);
+            const bool p_live = live && (i0 + c < per_lane);
+            const float a = (q_ok && i0 + c < per_lane) ? pa : 0.0f;
+            int l = (i0 * split) / K;  // the chunk's level
+            l = l < L ? l : L - 1;
+            const int H = lt.H[l], W = lt.W[l];
+            const Cell cl = map_cell(px, py, (float)H, (float)W, W, lt.start[l]);
+            // 32-bit offsets without the lane's channels (the slice is buffer-addressable)
+            const uint32_t rb = (uint32_t)row_bytes;
+            const uint32_t o00 = (uint32_t)cl.row00 * rb, o10 = o00 + (uint32_t)W * rb;
+            uint32_t po[4] = {p_live && cl.v00 ? o00 : kOutOfRange,
+                              p_live && cl.v01 ? o00 + rb : kOutOfRange,
+                              p_live && cl.v10 ? o10 : kOutOfRange,
+                              p_live && cl.v11 ? o10 + rb : kOutOfRange};
+            const float gx = 1.0f - cl.fx, gy = 1.0f - cl.fy;
+            float pw[4] = {a * (gx * gy), a * (cl.fx * gy), a * (gx * cl.fy), a * (cl.fx * cl.fy)};
+            auto take = [&](auto tc) {
+                constexpr int T = decltype(tc)::value;
+#pragma unroll
+                for (int cn = 0; cn < 4; ++cn) {
+                    // kOutOfRange plus the lane's bytes is still past the slice
+                    off[T][cn] = quad_bcast<T>(po[cn]) + (uint32_t)lane_bytes;
+                    w[T][cn] = quad_bcast<T>(pw[cn]);
+                }
+            };
+            take(std::integral_constant<int, 0>{});
+            take(std::integral_constant<int, 1>{});
+            take(std::integral_constant<int, 2>{});
+            take(std::integral_constant<int, 3>{});
+        } else {
         float lx[CH], ly[CH], aw[CH];
         if (owned) {
             chunk_params<PT, CH>(own, group_base + i0 / CH, lx, ly, aw);
@@ -446,9 +500,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         }
 #pragma unroll
         for (int t = 0; t < CH; ++t) aw[t] = (q_ok && i0 + t < per_lane) ? aw[t] : 0.0f;
-        int64_t off[CH][4];
-        bool ok[CH][4];
-        float w[CH][4];
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
             const bool t_live = live && (i0 + t < per_lane);
@@ -470,12 +521,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
             w[t][2] = aw[t] * (gx * cl.fy);
             w[t][3] = aw[t] * (cl.fx * cl.fy);
         }
+        }
         __builtin_amdgcn_sched_barrier(0);
         R raw[CH][4];
 #pragma unroll
         for (int t = 0; t < CH; ++t)
 #pragma unroll
-            for (int cn = 0; cn < 4; ++cn) raw[t][cn] = slice.template gather<R>(off[t][cn], ok[t][cn]);
+            for (int cn = 0; cn < 4; ++cn) {
+                if constexpr (QUAD)
+                    raw[t][cn] = buffer_load_raw<(int)sizeof(R)>(slice.rsrc, off[t][cn]);
+                else
+                    raw[t][cn] = slice.template gather<R>(off[t][cn], ok[t][cn]);
+            }
         __builtin_amdgcn_sched_barrier(0);  // all 4 * CH gathers in flight before any use
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
@@ -2046,15 +2103,30 @@ hipError_t fwd_launch(const Problem &p, const Mapping &mp, const void *value, co
     const int log2qs = 8 - mp.log2_group - mp.log2_split - (hg == 4 ? 2 : hg == 2 ? 1 : 0);
     const TileOrder to = tile_order(p, log2qs, (int)(p.M / hg), &ntiles);
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
+    // the quad setup (see msda_fwd_kernel)
+    const int64_t per_lane = (p.L * p.K) >> mp.log2_split;
+    const bool quad = mp.log2_group == 2 && p.D == 4 * VEC && per_lane <= (CH << 2) &&
+                      p.K % ((int64_t)CH << mp.log2_split) == 0;
+    if constexpr (VEC * sizeof(E) == 16) {  // 16-byte lane vectors: 64-byte fp16 / bf16 or fp32 rows
+        if (slice_fits_buffer(p) && quad) {
+            MSDA_LAUNCH((msda_fwd_kernel<DT, PT, VEC, CH, true, true>),
+                        dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
+                        static_cast<const E *>(value), static_cast<const P *>(loc),
+                        static_cast<const P *>(attn), static_cast<E *>(out), p.levels, p.S, p.Q,
+                        (int)p.M, (int)p.D, (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group,
+                        mp.log2_split, to, params_vectorizable(p, mp.log2_split, CH, loc, attn));
+            return hipGetLastError();
+        }
+    }
     if (slice_fits_buffer(p))
-        MSDA_LAUNCH((msda_fwd_kernel<DT, PT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
+        MSDA_LAUNCH((msda_fwd_kernel<DT, PT, VEC, CH, true, false>), dim3((unsigned)(per_xcd * kXcds)),
                            dim3(kBlock), 0, stream, static_cast<const E *>(value),
                            static_cast<const P *>(loc), static_cast<const P *>(attn),
                            static_cast<E *>(out), p.levels, p.S, p.Q, (int)p.M, (int)p.D,
                            (int)p.L, (int)p.K, qblocks, ntiles, mp.log2_group, mp.log2_split, to,
                            params_vectorizable(p, mp.log2_split, CH, loc, attn));
     else if constexpr (std::is_same<DT, PT>::value)
-        MSDA_LAUNCH((msda_fwd_kernel<DT, PT, VEC, CH, false>), dim3((unsigned)(per_xcd * kXcds)),
+        MSDA_LAUNCH((msda_fwd_kernel<DT, PT, VEC, CH, false, false>), dim3((unsigned)(per_xcd * kXcds)),
                            dim3(kBlock), 0, stream, static_cast<const E *>(value),
                            static_cast<const P *>(loc), static_cast<const P *>(attn),
                            static_cast<E *>(out), p.levels, p.S, p.Q, (int)p.M, (int)p.D,

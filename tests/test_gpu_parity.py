@@ -747,6 +747,46 @@ def test_pixel_query_points_sharing_pixels(dtype, K):
                    **parity_kwargs(dtype, "binned", inp))
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+@pytest.mark.parametrize("case", ["pixels", "uniform_k8"])
+def test_quad_setup_matches_plain_forward(dtype, case):
+    """Four-lane groups holding exactly D channels (D = 32 in 16-bit types,
+    D = 16 in fp32), one lane group per query and chunks inside one level:
+    the forward works out each point's cell, weights and offsets once per
+    quad and broadcasts them. The forced plain-load path works every point
+    out in every lane; the two must agree bit for bit (the same arithmetic),
+    and both must match the oracle. 'pixels': encoder-style queries with a
+    tenth of the points pushed outside their level; 'uniform_k8': 2048
+    queries with uniform locations (some out of bounds), K = 8 on 2 levels."""
+    from scale_deformable_attention_amd._binding import force_flat_gathers
+    D = 16 if dtype == torch.float32 else 32
+    if case == "pixels":
+        wl = Workload(name="quad", dtype=dtype, B=2, Q=None, M=8, D=D, K=4,
+                      levels=((40, 56), (20, 28), (10, 14), (5, 7)), loc_kind="reference",
+                      loc_sigma=0.05, seed=61)
+    else:
+        wl = Workload(name="quad", dtype=dtype, B=2, Q=2048, M=8, D=D, K=8,
+                      levels=((30, 41), (15, 21)), loc_kind="uniform", loc_lo=-0.1, loc_hi=1.1,
+                      seed=62)
+    inp = make_inputs(wl)
+    if case == "pixels":
+        loc = inp["sampling_locations"]
+        far = torch.rand(loc.shape[:-1], generator=torch.Generator().manual_seed(9)) < 0.1
+        loc[far] = (loc[far].float() * 1.6 - 0.3).to(loc.dtype)
+    say(f"case quad setup {dtype} {case}")
+    g = to_dev(inp)
+    args = (g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+            g["attention_weights"])
+    out = msda_forward(*args).cpu()
+    with force_flat_gathers():
+        out_plain = msda_forward(*args).cpu()
+    assert torch.equal(out, out_plain), (out.float() - out_plain.float()).abs().max()
+    ref_out, touched = oracle.forward(inp["value"], inp["spatial_shapes"], None,
+                                      inp["sampling_locations"], inp["attention_weights"],
+                                      return_touched=True)
+    report(check_forward(dtype, out, ref_out, touched))
+
+
 # Levels above 256 contributions per pixel, summed by PREREDUCE's in-LDS sort:
 # pixel queries (merged tiles; levels stored out of order; a wide head whose
 # tiles shrink to fit LDS), consecutive-query blocks, a level larger than the
