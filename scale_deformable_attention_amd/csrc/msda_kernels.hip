@@ -648,7 +648,7 @@ __global__ __launch_bounds__(kBlock) void msda_foil_kernel(
 #define MSDA_GRAD_ARGS value, loc, attn, grad_out, grad_loc, grad_attn, lt, S, Q, M, D, L, K, \
                        qblocks, log2g, log2s, to, pvec
 
-template <class DT, class PT, int VEC, int CH, bool BUF>
+template <class DT, class PT, int VEC, int CH, bool BUF, bool QUAD = false>
 __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) {
     using E = typename DT::S;
     using R = typename RawVec<VEC * (int)sizeof(E)>::type;
@@ -693,7 +693,45 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
     if (owned) own_chunk_params<PT, CH>(loc_q, attn_q, c, per_lane, split, s, pvec, own);
     const int group_base = (tid & 63) & ~(G - 1);
 
+    // QUAD: as in the forward, lane k of a 4-lane group works out point k of
+    // the chunk and the quad broadcasts its corner offsets and fractions; the
+    // slope scales stay in lane k, which stores point k (the same arithmetic)
+    static_assert(!QUAD || (BUF && CH == 4), "quad setup: buffer gathers, 4-point chunks");
+    using Off = typename std::conditional<QUAD, uint32_t, int64_t>::type;
     for (int i0 = 0; i0 < per_lane; i0 += CH) {
+        Off off[CH][4];
+        bool ok[CH][4];
+        float fx[CH], fy[CH], sw[CH], sh[CH];
+        if constexpr (QUAD) {
+            float px, py, pa;
+            point_params<PT, CH>(own, group_base + i0 / CH, c, px, py, pa);
+            const bool p_live = live && (i0 + c < per_lane);
+            const float aw = (q_ok && i0 + c < per_lane) ? pa : 0.0f;
+            int l = (i0 * split) / K;  // the chunk's level
+            l = l < L ? l : L - 1;
+            const int H = lt.H[l], W = lt.W[l];
+            sw[0] = (float)W * aw;  // lane k's own point's scales
+            sh[0] = (float)H * aw;
+            const Cell cl = map_cell(px, py, (float)H, (float)W, W, lt.start[l]);
+            const uint32_t rb = (uint32_t)row_bytes;
+            const uint32_t o00 = (uint32_t)cl.row00 * rb, o10 = o00 + (uint32_t)W * rb;
+            const uint32_t po[4] = {p_live && cl.v00 ? o00 : kOutOfRange,
+                                    p_live && cl.v01 ? o00 + rb : kOutOfRange,
+                                    p_live && cl.v10 ? o10 : kOutOfRange,
+                                    p_live && cl.v11 ? o10 + rb : kOutOfRange};
+            auto take = [&](auto tc) {
+                constexpr int T = decltype(tc)::value;
+#pragma unroll
+                for (int cn = 0; cn < 4; ++cn)
+                    off[T][cn] = quad_bcast<T>(po[cn]) + (uint32_t)lane_bytes;
+                fx[T] = quad_bcast<T>(cl.fx);
+                fy[T] = quad_bcast<T>(cl.fy);
+            };
+            take(std::integral_constant<int, 0>{});
+            take(std::integral_constant<int, 1>{});
+            take(std::integral_constant<int, 2>{});
+            take(std::integral_constant<int, 3>{});
+        } else {
         float lx[CH], ly[CH], la[CH];
         if (owned) {
             chunk_params<PT, CH>(own, group_base + i0 / CH, lx, ly, la);
@@ -719,9 +757,6 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
                 la[t] = bits_to_f32<PT>(ba[t]);
             }
         }
-        int64_t off[CH][4];
-        bool ok[CH][4];
-        float fx[CH], fy[CH], sw[CH], sh[CH];
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
             const bool t_live = live && (i0 + t < per_lane);
@@ -743,12 +778,18 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
             ok[t][2] = t_live && cl.v10;
             ok[t][3] = t_live && cl.v11;
         }
+        }
         __builtin_amdgcn_sched_barrier(0);
         R raw[CH][4];
 #pragma unroll
         for (int t = 0; t < CH; ++t)
 #pragma unroll
-            for (int cn = 0; cn < 4; ++cn) raw[t][cn] = slice.template gather<R>(off[t][cn], ok[t][cn]);
+            for (int cn = 0; cn < 4; ++cn) {
+                if constexpr (QUAD)
+                    raw[t][cn] = buffer_load_raw<(int)sizeof(R)>(slice.rsrc, off[t][cn]);
+                else
+                    raw[t][cn] = slice.template gather<R>(off[t][cn], ok[t][cn]);
+            }
         __builtin_amdgcn_sched_barrier(0);  // all 4 * CH gathers in flight before any use
         float ds[CH], dx[CH], dy[CH];
 #pragma unroll
@@ -764,8 +805,8 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
             ds[t] = group_sum(ds[t], log2g);
-            dx[t] = group_sum(dx[t], log2g) * sw[t];
-            dy[t] = group_sum(dy[t], log2g) * sh[t];
+            dx[t] = group_sum(dx[t], log2g) * (QUAD ? 1.0f : sw[t]);
+            dy[t] = group_sum(dy[t], log2g) * (QUAD ? 1.0f : sh[t]);
         }
         for (int t0 = 0; t0 < CH; t0 += G) {
             const int t = t0 + c;
@@ -775,6 +816,10 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
                 vs = t == k ? ds[k] : vs;
                 vx = t == k ? dx[k] : vx;
                 vy = t == k ? dy[k] : vy;
+            }
+            if constexpr (QUAD) {  // lane k's scales are point k's
+                vx *= sw[0];
+                vy *= sh[0];
             }
             if (q_ok && t < CH && i0 + t < per_lane) {
                 const int64_t pp = pq * LK + (i0 + t) * split + s;
@@ -786,7 +831,7 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
     }
 }
 
-template <class DT, class PT, int VEC, int CH, bool BUF>
+template <class DT, class PT, int VEC, int CH, bool BUF, bool QUAD>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void msda_grad_kernel(
     const typename DT::S *__restrict__ value, const typename PT::S *__restrict__ loc,
     const typename PT::S *__restrict__ attn, const typename DT::S *__restrict__ grad_out,
@@ -796,7 +841,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const int log2s, const TileOrder to, const bool pvec) {
     const int64_t tile = logical_block();
     if (tile >= ntiles) return;  // whole workgroup leaves together
-    grad_tile<DT, PT, VEC, CH, BUF>(MSDA_GRAD_ARGS, tile);
+    grad_tile<DT, PT, VEC, CH, BUF, QUAD>(MSDA_GRAD_ARGS, tile);
 }
 
 // ------------------------------------------------------------ backward
@@ -2152,7 +2197,22 @@ hipError_t grad_launch(const Problem &p, const Mapping &mp, const void *value, c
     const TileOrder to = tile_order(p, log2qs, (int)(p.M / hg), &ntiles);
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (!slice_fits_buffer(p)) return hipErrorInvalidValue;  // binning requires it
-    MSDA_LAUNCH((msda_grad_kernel<DT, PT, VEC, CH, true>), dim3((unsigned)(per_xcd * kXcds)),
+    if constexpr (VEC * sizeof(E) == 16) {  // the quad setup (see grad_tile)
+        const int64_t per_lane = (p.L * p.K) >> mp.log2_split;
+        if (mp.log2_group == 2 && p.D == 4 * VEC && per_lane <= (CH << 2) &&
+            p.K % ((int64_t)CH << mp.log2_split) == 0) {
+            MSDA_LAUNCH((msda_grad_kernel<DT, PT, VEC, CH, true, true>),
+                        dim3((unsigned)(per_xcd * kXcds)), dim3(kBlock), 0, stream,
+                        static_cast<const E *>(value), static_cast<const P *>(loc),
+                        static_cast<const P *>(attn), static_cast<const E *>(grad_out),
+                        static_cast<P *>(grad_loc), static_cast<P *>(grad_attn), p.levels, p.S,
+                        p.Q, (int)p.M, (int)p.D, (int)p.L, (int)p.K, qblocks, ntiles,
+                        mp.log2_group, mp.log2_split, to,
+                        params_vectorizable(p, mp.log2_split, CH, loc, attn));
+            return hipGetLastError();
+        }
+    }
+    MSDA_LAUNCH((msda_grad_kernel<DT, PT, VEC, CH, true, false>), dim3((unsigned)(per_xcd * kXcds)),
                        dim3(kBlock), 0, stream, static_cast<const E *>(value),
                        static_cast<const P *>(loc), static_cast<const P *>(attn),
                        static_cast<const E *>(grad_out), static_cast<P *>(grad_loc),

@@ -752,12 +752,14 @@ def test_pixel_query_points_sharing_pixels(dtype, K):
 def test_quad_setup_matches_plain_forward(dtype, case):
     """Four-lane groups holding exactly D channels (D = 32 in 16-bit types,
     D = 16 in fp32), one lane group per query and chunks inside one level:
-    the forward works out each point's cell, weights and offsets once per
-    quad and broadcasts them. The forced plain-load path works every point
-    out in every lane; the two must agree bit for bit (the same arithmetic),
-    and both must match the oracle. 'pixels': encoder-style queries with a
-    tenth of the points pushed outside their level; 'uniform_k8': 2048
-    queries with uniform locations (some out of bounds), K = 8 on 2 levels."""
+    the forward and the gradients-only kernel work out each point's cell,
+    weights and offsets once per quad and broadcast them. The forced
+    plain-load path works every point out in every lane; the two forwards
+    must agree bit for bit (the same arithmetic), and the forward and the
+    binned backward (whose gradients come from the gradients-only kernel)
+    must match the oracle. 'pixels': encoder-style queries with a tenth of
+    the points pushed outside their level; 'uniform_k8': 2048 queries with
+    uniform locations (some out of bounds), K = 8 on 2 levels."""
     from scale_deformable_attention_amd._binding import force_flat_gathers
     D = 16 if dtype == torch.float32 else 32
     if case == "pixels":
@@ -781,10 +783,9 @@ def test_quad_setup_matches_plain_forward(dtype, case):
     with force_flat_gathers():
         out_plain = msda_forward(*args).cpu()
     assert torch.equal(out, out_plain), (out.float() - out_plain.float()).abs().max()
-    ref_out, touched = oracle.forward(inp["value"], inp["spatial_shapes"], None,
-                                      inp["sampling_locations"], inp["attention_weights"],
-                                      return_touched=True)
-    report(check_forward(dtype, out, ref_out, touched))
+    names, _ = _backward_launch_names(inp, "binned")
+    assert "msda_grad_kernel" in names, names
+    full_check(inp, dtype, "binned")
 
 
 # Levels above 256 contributions per pixel, summed by PREREDUCE's in-LDS sort:
