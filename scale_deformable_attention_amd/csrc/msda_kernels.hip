@@ -1851,22 +1851,25 @@ __device__ __forceinline__ void accum_bin(float *tile, MSDA_ACCUM_PARAMS, const 
         // a record past the slot's end reads neither LDS past the round nor
         // its row: coefficient 0 and a zero row, whatever grad_output holds
         if constexpr (WIDE) {
+            static_assert(UW == 4, "one record per lane of a sub-group");
             for (uint32_t i0 = 0; __ballot(i0 < n); i0 += 4 * UW) {
-                float coef[UW];
-                uint32_t qo[UW];
-                bool okr[UW];
-#pragma unroll
-                for (int u = 0; u < UW; ++u) {
-                    const uint32_t idx = i0 + 4 * u + sub;
-                    okr[u] = idx < n;
-                    const uint2 rc = sorted[okr[u] ? first + idx : 0u];
-                    coef[u] = __uint_as_float(rc.y & (0u - (uint32_t)okr[u]));
-                    const uint32_t rq = rc.x >> 4;
-                    qo[u] = (rq < (uint64_t)Q ? rq : 0u) * row_bytes + lbytes;
-                }
+                // lane k of the sub-group (an aligned quad) decodes its record
+                // u = k, out-of-range offset past the slot's end, and the quad
+                // broadcasts each record's coefficient and row offset
+                const uint32_t idx = i0 + 4 * (c & 3) + sub;
+                const bool okk = idx < n;
+                const uint2 rc = sorted[okk ? first + idx : 0u];
+                const float ck = __uint_as_float(rc.y & (0u - (uint32_t)okk));
+                const uint32_t rq = rc.x >> 4;
+                const uint32_t ok_off = okk ? (rq < (uint64_t)Q ? rq : 0u) * row_bytes : kOutOfRange;
+                const float coef[UW] = {quad_bcast<0>(ck), quad_bcast<1>(ck), quad_bcast<2>(ck),
+                                        quad_bcast<3>(ck)};
+                // kOutOfRange plus the chunk's bytes is still past the slice
+                const uint32_t qo[UW] = {quad_bcast<0>(ok_off) + lbytes, quad_bcast<1>(ok_off) + lbytes,
+                                         quad_bcast<2>(ok_off) + lbytes, quad_bcast<3>(ok_off) + lbytes};
                 uint4 gr[UW];
 #pragma unroll
-                for (int u = 0; u < UW; ++u) gr[u] = gslice.template gather<uint4>(qo[u], okr[u]);
+                for (int u = 0; u < UW; ++u) gr[u] = buffer_load_raw<16>(gslice.rsrc, qo[u]);
                 __builtin_amdgcn_sched_barrier(0);  // every gather issued before any use
 #pragma unroll
                 for (int u = 0; u < UW; ++u) {
