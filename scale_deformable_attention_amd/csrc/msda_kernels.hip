@@ -694,14 +694,15 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
     const int group_base = (tid & 63) & ~(G - 1);
 
     // QUAD: as in the forward, lane k of a 4-lane group works out point k of
-    // the chunk and the quad broadcasts its corner offsets and fractions; the
-    // slope scales stay in lane k, which stores point k (the same arithmetic)
+    // the chunk and the quad broadcasts its corner offsets; its fractions and
+    // slope scales stay in lane k, which sums and stores point k
     static_assert(!QUAD || (BUF && CH == 4), "quad setup: buffer gathers, 4-point chunks");
     using Off = typename std::conditional<QUAD, uint32_t, int64_t>::type;
     for (int i0 = 0; i0 < per_lane; i0 += CH) {
         Off off[CH][4];
         bool ok[CH][4];
         float fx[CH], fy[CH], sw[CH], sh[CH];
+        float fx_own = 0.0f, fy_own = 0.0f;  // QUAD: lane k's own point's fractions
         if constexpr (QUAD) {
             float px, py, pa;
             point_params<PT, CH>(own, group_base + i0 / CH, c, px, py, pa);
@@ -713,6 +714,8 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
             sw[0] = (float)W * aw;  // lane k's own point's scales
             sh[0] = (float)H * aw;
             const Cell cl = map_cell(px, py, (float)H, (float)W, W, lt.start[l]);
+            fx_own = cl.fx;
+            fy_own = cl.fy;
             const uint32_t rb = (uint32_t)row_bytes;
             const uint32_t o00 = (uint32_t)cl.row00 * rb, o10 = o00 + (uint32_t)W * rb;
             const uint32_t po[4] = {p_live && cl.v00 ? o00 : kOutOfRange,
@@ -724,8 +727,6 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
 #pragma unroll
                 for (int cn = 0; cn < 4; ++cn)
                     off[T][cn] = quad_bcast<T>(po[cn]) + (uint32_t)lane_bytes;
-                fx[T] = quad_bcast<T>(cl.fx);
-                fy[T] = quad_bcast<T>(cl.fy);
             };
             take(std::integral_constant<int, 0>{});
             take(std::integral_constant<int, 1>{});
@@ -791,12 +792,51 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
                     raw[t][cn] = slice.template gather<R>(off[t][cn], ok[t][cn]);
             }
         __builtin_amdgcn_sched_barrier(0);  // all 4 * CH gathers in flight before any use
+        // The sample and its two slopes are linear in the corner rows, so
+        // their dot products with the upstream gradient follow from the four
+        // rows' own dot products.
+        if constexpr (QUAD) {
+            // Reduce-scatter of the lanes' 16 partial dot products over the
+            // quad: lanes k and k ^ 2 swap the halves of the chunk the other
+            // keeps (points with bit 1 of t equal to its own), then lanes k
+            // and k ^ 1 do so for one point, so lane k ends with point k's
+            // four sums and combines them once, for the point it stores.
+            float d[CH][4];
+#pragma unroll
+            for (int t = 0; t < CH; ++t)
+#pragma unroll
+                for (int cn = 0; cn < 4; ++cn) d[t][cn] = lane_dot<DT, VEC>(graw, g, raw[t][cn], 0.0f);
+            const bool hi2 = (c & 2) != 0, hi1 = (c & 1) != 0;
+            float e[2][4], f[4];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int cn = 0; cn < 4; ++cn) {
+                    const float keep = hi2 ? d[j + 2][cn] : d[j][cn];
+                    const float give = hi2 ? d[j][cn] : d[j + 2][cn];
+                    e[j][cn] = keep + dpp_move<0x4E>(give);  // quad_perm [2, 3, 0, 1]
+                }
+#pragma unroll
+            for (int cn = 0; cn < 4; ++cn) {
+                const float keep = hi1 ? e[1][cn] : e[0][cn];
+                const float give = hi1 ? e[0][cn] : e[1][cn];
+                f[cn] = keep + dpp_move<0xB1>(give);  // quad_perm [1, 0, 3, 2]
+            }
+            float vs, vx, vy;
+            point_sums(f, fx_own, fy_own, vs, vx, vy);
+            vx *= sw[0];  // lane k's scales are point k's
+            vy *= sh[0];
+            if (q_ok && i0 + c < per_lane) {
+                const int64_t pp = pq * LK + (i0 + c) * split + s;
+                grad_attn[pp] = from_f32(PT{}, vs);
+                grad_loc[2 * pp] = from_f32(PT{}, vx);
+                grad_loc[2 * pp + 1] = from_f32(PT{}, vy);
+            }
+            continue;
+        }
         float ds[CH], dx[CH], dy[CH];
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
-            // The sample and its two slopes are linear in the corner rows, so
-            // their dot products with the upstream gradient follow from the
-            // four rows' own dot products.
             float d[4];
 #pragma unroll
             for (int cn = 0; cn < 4; ++cn) d[cn] = lane_dot<DT, VEC>(graw, g, raw[t][cn], 0.0f);
@@ -805,8 +845,8 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
             ds[t] = group_sum(ds[t], log2g);
-            dx[t] = group_sum(dx[t], log2g) * (QUAD ? 1.0f : sw[t]);
-            dy[t] = group_sum(dy[t], log2g) * (QUAD ? 1.0f : sh[t]);
+            dx[t] = group_sum(dx[t], log2g) * sw[t];
+            dy[t] = group_sum(dy[t], log2g) * sh[t];
         }
         for (int t0 = 0; t0 < CH; t0 += G) {
             const int t = t0 + c;
@@ -816,10 +856,6 @@ __device__ __forceinline__ void grad_tile(MSDA_GRAD_PARAMS, const int64_t tile) 
                 vs = t == k ? ds[k] : vs;
                 vx = t == k ? dx[k] : vx;
                 vy = t == k ? dy[k] : vy;
-            }
-            if constexpr (QUAD) {  // lane k's scales are point k's
-                vx *= sw[0];
-                vy *= sh[0];
             }
             if (q_ok && t < CH && i0 + t < per_lane) {
                 const int64_t pp = pq * LK + (i0 + t) * split + s;
