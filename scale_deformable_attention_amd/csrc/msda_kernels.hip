@@ -1263,12 +1263,17 @@ __global__ __launch_bounds__(kBinBlock) void bin_sort_kernel(
     const int m = (int)(bm - b * M);
     const int LK = L * K;
     const int LKb = lt.nblev * K;  // points of the binned levels per query
-    const int64_t i = w * kBinBlock + tid;
-    const bool ok = i < Q * LKb;
-    const int64_t q = ok ? i / LKb : 0;
-    const int r = ok ? (int)(i - q * LKb) : 0;
-    const int l = lt.blevel[r / K];
-    const int pp = l * K + (r - (r / K) * K);
+    // 32-bit index arithmetic: the host keeps 4 * B * Q * M * L * K below
+    // 2^32; shifts for power-of-two divisors (the choice is uniform)
+    const uint32_t i = (uint32_t)(w * kBinBlock) + (uint32_t)tid;
+    const bool ok = i < (uint32_t)(Q * LKb);
+    const uint32_t q = !ok ? 0u
+                           : ((LKb & (LKb - 1)) == 0 ? i >> __builtin_ctz((unsigned)LKb)
+                                                     : i / (uint32_t)LKb);
+    const int r = ok ? (int)(i - q * (uint32_t)LKb) : 0;
+    const int rk = (K & (K - 1)) == 0 ? r >> __builtin_ctz((unsigned)K) : r / K;
+    const int l = lt.blevel[rk];
+    const int pp = l * K + (r - rk * K);
     const int64_t pt = ((b * Q + q) * M + m) * LK + pp;
     float x, y;
     load_xy<DT>(loc + 2 * pt, x, y);
