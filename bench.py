@@ -543,6 +543,9 @@ def main():
                     help="with --profile-only: also run the point-parallel forward foil")
     ap.add_argument("--atomic-probe", action="store_true",
                     help="measure the atomic request rate instead (measurement kernel)")
+    ap.add_argument("--single-stream", action="store_true",
+                    help="with --profile-only: backward on the caller's stream only "
+                         "(MSDA_FLAG_SINGLE_STREAM), so per-kernel times have no overlap")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="with --profile-only: also run 5 plain device copies of this many MiB "
                          "(reference dispatches for scaling FETCH_SIZE / WRITE_SIZE)")
@@ -574,9 +577,16 @@ def main():
         call = PreparedCall(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
                             g["attention_weights"], g["grad_output"], accum=args.accum)
         log(f"workload {wl.name}, backward accumulation {args.accum} -> {call.resolved_accum}")
+        if args.single_stream:
+            from scale_deformable_attention_amd._binding import msda_backward
+            bargs = (g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                     g["attention_weights"], g["grad_output"])
         for _ in range(args.warmup + args.steps):
             call.forward()
-            call.backward()
+            if args.single_stream:
+                msda_backward(*bargs, accum=args.accum, single_stream=True)
+            else:
+                call.backward()
         torch.cuda.synchronize()
         log(f"ran {args.warmup} + {args.steps} eager steps")
         if args.foil:
