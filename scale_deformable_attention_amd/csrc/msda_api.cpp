@@ -963,7 +963,9 @@ static int backward_impl(int dtype, int pdtype, int64_t batch, int64_t num_keys,
         bins.tile_offsets = reinterpret_cast<uint32_t *>(ws + bp.tiles_off);
         bins.records = reinterpret_cast<uint2 *>(ws + bp.records_off);
         bins.nbins = bp.nbins;
-        bins.ends = bp.local_sort ? bins.cursor : bins.starts + 1;
+        // a bin's records end at its cursor after place (count's totals are
+        // upper bounds where place merges records)
+        bins.ends = bins.cursor;
         // The binned chain (t) overlaps the zero fill and the gradient /
         // scatter kernels (s); it forks after the caller's earlier work on s
         // and is joined back on every path below. The fork and join cost

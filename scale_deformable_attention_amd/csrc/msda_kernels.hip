@@ -1311,8 +1311,8 @@ __global__ __launch_bounds__(kBinBlock) void bin_sort_kernel(
     // add to the same grad_value row with the same upstream gradient, so they
     // make one record: the lowest point k holding the pixel keeps its corner
     // and adds the other points' own coefficients, the others drop theirs.
-    // Count and place take the same decisions. The quad's values rotate by
-    // DPP quad permutes (no LDS traffic).
+    // Only place merges (count counts every in-bounds corner, an upper
+    // bound). The quad's values rotate by DPP quad permutes (no LDS traffic).
     float sum[4];  // coefficient of this point's record per corner
 #pragma unroll
     for (int cn = 0; cn < 4; ++cn) sum[cn] = coef[cn];
@@ -2585,7 +2585,10 @@ hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
     // near their own pixel, so on coarse levels several points of one query
     // share pixels (encoder workload: 32% fewer records, accumulation 298 ->
     // 231 us); elsewhere the comparisons would cost without merging anything.
-    const bool merge = (p.K == 2 || p.K == 4) && pixel_queries(p);
+    // Only place merges: count's totals then bound each bin's records from
+    // above, the bin's range keeps an unused tail, and the accumulation ends
+    // each bin at its cursor after place.
+    const bool merge = place && (p.K == 2 || p.K == 4) && pixel_queries(p);
 #define MSDA_SORT(T, PL)                                                                        \
     MSDA_LAUNCH((bin_sort_kernel<T, PL>), dim3((unsigned)grid), dim3(kBinBlock), 0, stream, \
                        static_cast<const typename T::S *>(loc),                                 \
