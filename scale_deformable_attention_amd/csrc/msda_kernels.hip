@@ -1233,8 +1233,9 @@ constexpr int kRankedKeys = 256;             // bins per workgroup visited in ke
 // counter[bin] (the bin's cursor, initialised to its start by the scan) and
 // writes the records: x = query << 4 | row within the bin (bins have at most
 // 16 rows), y = fp32 bits of A * w_ij (summed over the query's points that
-// share the pixel, when merging). Both derive cells with the same map_cell as
-// the backward, so they agree on every in-bounds corner.
+// share the pixel, when merging; count counts every in-bounds corner, so a
+// bin's count bounds its records from above). Both derive cells with the
+// same map_cell as the backward, so they agree on every in-bounds corner.
 template <class DT, bool PLACE>
 __global__ __launch_bounds__(kBinBlock) void bin_sort_kernel(
     const typename DT::S *__restrict__ loc, const typename DT::S *__restrict__ attn,

@@ -140,7 +140,7 @@ struct Problem {
 struct BinnedBuffers {
     uint32_t *starts;
     uint32_t *cursor;
-    const uint32_t *ends;  // bin i's records are [starts[i], ends[i])
+    const uint32_t *ends;  // bin i's records are [starts[i], ends[i]): the cursors after place
     uint32_t *tile_offsets;  // scan_tiles(nbins) tile totals of the scan (2 * (scan_tiles + 1) reserved)
     uint2 *records;
     int64_t nbins;
@@ -189,7 +189,9 @@ hipError_t launch_backward(const Problem &p, const BwdMapping &mp, const void *v
 // Binned grad_value, in stream order: zero starts[0:nbins] (launch_zero);
 // launch_bin_sort(place = false) counts the in-bounds corners per bin into
 // starts; launch_bin_scan turns the counts into starts and cursors;
-// launch_bin_sort(place = true) writes the records; launch_gradients writes
+// launch_bin_sort(place = true) writes the records, each bin's from its start
+// up to its cursor (fewer than counted where place merges records, so a bin
+// ends at its cursor, not at the next start); launch_gradients writes
 // grad_loc / grad_attn, launch_scatter the unbinned levels' atomics (if any);
 // launch_bin_accumulate writes the binned levels' grad_value rows.
 hipError_t launch_bin_sort(const Problem &p, const void *loc, const void *attn,
