@@ -663,6 +663,44 @@ def test_non_finite_locations_are_out_of_bounds(dtype, accum):
         assert float(grads[1][idx[:5]].abs().max()) == 0.0 and float(grads[2][idx[:5]]) == 0.0
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+def test_non_finite_locations_under_the_quad_setup(dtype):
+    """The same reading as above on shapes that take the quad setup (4-lane
+    groups holding a whole head row, one lane group per query) in the
+    forward and the gradients-only kernel, and the binned chain with merged
+    records (pixel queries, K = 4): NaN, infinite and overflowing coordinates,
+    among them all four points of one (query, level) and a point whose x
+    alone is NaN, count as out of bounds."""
+    D = 16 if dtype == torch.float32 else 32
+    wl = Workload(name="quad_nonfinite", dtype=dtype, B=2, Q=None, M=8, D=D, K=4,
+                  levels=((40, 56), (20, 28), (10, 14), (5, 7)), loc_kind="reference",
+                  loc_sigma=0.03, seed=81)
+    inp = make_inputs(wl)
+    nan, inf = float("nan"), float("inf")
+    bad = [((0, 100, 3, 0, 2, 0), nan), ((1, 2300, 5, 1, 1, 1), inf),
+           ((1, 2900, 7, 3, 3, 0), -inf), ((0, 17, 0, 2, 0, 1), 1e38)]
+    bad += [((1, 2950, 2, 3, k, c), nan) for k in range(4) for c in range(2)]  # a whole quad
+    loc, sub = inp["sampling_locations"].clone(), inp["sampling_locations"].clone()
+    for idx, v in bad:
+        loc[idx] = v
+        sub[idx] = -10.0
+    ref_inp = dict(inp, sampling_locations=sub)
+    say(f"case non-finite locations, quad setup {dtype}")
+    ref_out, touched, ref_grads, trows = oracle_run(ref_inp)
+    g = to_dev(dict(inp, sampling_locations=loc))
+    out = msda_forward(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                       g["attention_weights"])
+    grads = msda_backward(g["value"], g["spatial_shapes"], None, g["sampling_locations"],
+                          g["attention_weights"], g["grad_output"], accum="binned")
+    torch.cuda.synchronize()
+    check_forward(dtype, out.cpu(), ref_out, touched)
+    grads = tuple(t.cpu() for t in grads)
+    check_backward(dtype, grads, ref_grads, inp["spatial_shapes"], None, trows,
+                   **parity_kwargs(dtype, "binned", ref_inp))
+    for idx, _ in bad:
+        assert float(grads[1][idx[:5]].abs().max()) == 0.0 and float(grads[2][idx[:5]]) == 0.0
+
+
 def test_single_stream_flag_and_side_stream_release():
     """The odd-head workload bins about 9 * 10^5 records, so by default its
     binned chain runs on the thread's side stream. With single_stream the
