@@ -826,6 +826,45 @@ def test_quad_setup_matches_plain_forward(dtype, case):
     full_check(inp, dtype, "binned")
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
+def test_quad_setup_with_element_aligned_parameters(dtype):
+    """The quad setup when the locations and weights (and their gradients)
+    start one element into their buffers: value rows stay 16-byte aligned, so
+    the forward and the gradients-only kernel keep the quad setup, but each
+    lane loads its chunk's parameters element by element instead of with
+    vector loads. Forward bit for bit against the plain-load path; forward and
+    binned backward against the oracle."""
+    from scale_deformable_attention_amd._binding import force_flat_gathers
+    D = 16 if dtype == torch.float32 else 32
+    wl = Workload(name="quad_align", dtype=dtype, B=2, Q=None, M=8, D=D, K=4,
+                  levels=((40, 56), (20, 28), (10, 14), (5, 7)), loc_kind="reference",
+                  loc_sigma=0.04, seed=91)
+    inp = make_inputs(wl)
+    g = to_dev(inp)
+    say(f"case quad setup, element-aligned parameters {dtype}")
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+    loc, a = shifted(g["sampling_locations"]), shifted(g["attention_weights"])
+    args = (g["value"], g["spatial_shapes"], None, loc, a)
+    out = msda_forward(*args).cpu()
+    with force_flat_gathers():
+        out_plain = msda_forward(*args).cpu()
+    assert torch.equal(out, out_plain), (out.float() - out_plain.float()).abs().max()
+    ref_out, touched, ref_grads, trows = oracle_run(inp)
+    check_forward(dtype, out, ref_out, touched)
+    gl = shifted(torch.empty_like(g["sampling_locations"]))
+    ga = shifted(torch.empty_like(g["attention_weights"]))
+    grads = msda_backward(*args, g["grad_output"], grad_sampling_locations=gl,
+                          grad_attention_weights=ga, accum="binned")
+    torch.cuda.synchronize()
+    check_backward(dtype, tuple(t.cpu() for t in grads), ref_grads, inp["spatial_shapes"], None,
+                   trows, **parity_kwargs(dtype, "binned", inp))
+
+
 # Levels above 256 contributions per pixel, summed by PREREDUCE's in-LDS sort:
 # pixel queries (merged tiles; levels stored out of order; a wide head whose
 # tiles shrink to fit LDS), consecutive-query blocks, a level larger than the
