@@ -351,12 +351,16 @@ def test_integer_aligned_points_reproduce_rows_exactly(dtype, accum):
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=str)
 @pytest.mark.parametrize("accum", ["native", "fp32_scratch", "binned"])
-def test_accumulate_flag_doubles_grad_value(dtype, accum):
+@pytest.mark.parametrize("D", [16, 32])
+def test_accumulate_flag_doubles_grad_value(dtype, accum, D):
+    """A second backward with `accumulate` adds to the first one's grad_value.
+    D = 32 gives 16-bit dtypes 64-byte rows (the binned accumulation's wide
+    mode) and fp32 two 64-byte slot groups per row."""
     if dtype == torch.float32 and accum == "fp32_scratch":
         pytest.skip("identical to native for fp32")
-    wl, inp = _small(dtype, D=16)
+    wl, inp = _small(dtype, D=D)
     g = to_dev(inp)
-    say(f"case accumulate twice {dtype} {accum}")
+    say(f"case accumulate twice {dtype} {accum} D={D}")
     args = (g["value"], g["spatial_shapes"], None, g["sampling_locations"], g["attention_weights"],
             g["grad_output"])
     gv1, _, _ = msda_backward(*args, accum=accum)
