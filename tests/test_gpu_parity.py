@@ -177,6 +177,21 @@ def test_points_and_levels(dtype, K, L):
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=str)
+@pytest.mark.parametrize("accum", ["native", "fp32_scratch", "binned"])
+def test_degenerate_level_shapes(dtype, accum):
+    """Levels of one pixel, one row and one column beside a small 2-D level:
+    a corner off the single row or column is out of bounds, and every
+    in-bounds corner of a 1 x 1 level is that one pixel. Points spread past
+    the map on all sides."""
+    if dtype == torch.float32 and accum == "fp32_scratch":
+        pytest.skip("identical to native for fp32")
+    levels = ((1, 1), (1, 7), (7, 1), (2, 3))
+    wl, inp = _small(dtype, D=32, K=4, levels=levels, Q=50, M=4, lo=-0.3, hi=1.3, seed=97)
+    say(f"case degenerate level shapes {dtype} {accum}")
+    full_check(inp, dtype, accum)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
 def test_custom_level_start_and_padding_rows(dtype):
     levels = ((6, 9), (3, 5), (2, 2))
     wl, inp = _small(dtype, levels=levels)
