@@ -922,6 +922,23 @@ def test_prereduce_cases(dtype, case):
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=str)
+@pytest.mark.parametrize("accum", ["binned", "prereduce"])
+def test_degenerate_levels_with_pixel_queries(dtype, accum):
+    """Pixel queries over levels of one pixel, one row and one column, points
+    spread well past the map: binned with merged records (K = 4), and with
+    the 1 x 1 level pre-reduced (every in-bounds corner of all its points is
+    the one pixel)."""
+    wl = Workload(name="pixels_degenerate", dtype=dtype, B=2, Q=None, M=4, D=32, K=4,
+                  levels=((1, 1), (1, 7), (7, 1), (2, 3)), loc_kind="reference",
+                  loc_sigma=0.3, seed=47)
+    inp = make_inputs(wl)
+    modes = plan_for(dtype, accum, inp)
+    assert accum in modes, modes
+    say(f"case degenerate levels, pixel queries {dtype} {accum}: plan={modes}")
+    full_check(inp, dtype, accum)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=str)
 def test_prereduce_accumulates_and_ignores_out_of_bounds_points(dtype):
     """PREREDUCE with MSDA_FLAG_ACCUMULATE_GRAD_VALUE adds the pre-reduced sums
     into the existing grad_value; with every point outside its level the
