@@ -6,7 +6,8 @@ what msda_backward gives on the same inputs: grad_sampling_locations and
 grad_attention_weights bit for bit (no atomics behind them), grad_value
 within the oracle parity rule (its summation order may differ between runs).
 Each mode that needs a workspace runs: AUTO (bins for two levels), BINNED
-(bins for all levels), PER_LEVEL (fp32 sums for two levels).
+(bins for all levels), PER_LEVEL (fp32 sums for two levels), and on pixel
+queries PREREDUCE (two levels pre-reduced in LDS, two binned).
 """
 
 import os
@@ -65,7 +66,7 @@ def test_noalloc_matches_backward_on_two_calls(accum):
                            inp["spatial_shapes"], None, ref_grads[3], **kw)
 
 
-@pytest.mark.parametrize("accum", ["auto", "binned"])
+@pytest.mark.parametrize("accum", ["auto", "binned", "prereduce"])
 def test_noalloc_pixel_queries_on_two_calls(accum):
     """Pixel queries (every pyramid pixel a query, K = 4) take the count /
     scan / place chain, whose records merge a query's corners that share a
